@@ -1,0 +1,207 @@
+#!/usr/bin/env python
+"""Benchmark of the affine-Q4 MoE hot path on one MI355X.
+
+Headline (`value`): HBM GB/s of the batch-1 decode MoE layer over a 40-layer
+decode loop (hidden 2048, 256 routed + 1 shared expert, top-8, Q4 g64; about
+18 GB of weights, far beyond the caches).  A step is one decode token through
+all 40 layers, each a dependent router -> top-k -> experts chain; `--steps`
+steps are timed after `--warmup` untimed ones.  Bytes per layer are the
+algorithmic ones: the 9 touched experts at 4.5 bits per weight, the bf16
+router, the bf16 input and the fp32 output.
+
+Also reported: the 2,048-token prefill chunk through one layer (grouped-GEMM
+TFLOP/s against the bf16 MFMA peak), the LM-head GEMV + argmax
+(151,936 x 2048, two weight copies alternated so the 175 MB matrix is not
+cache-resident), and the CPU oracle timed on a bounded sample of the decode
+workload.  All inputs are seeded and synthetic.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "decode MoE-layer GEMV HBM GB/s (% of peak) + prefill grouped-GEMM TFLOP/s"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(stack_host, seed, budget_s=12.0):
+    """The oracle (as it stands) on (step, layer) pairs of the decode workload until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import q4moe_oracle as orc
+    from quantized_moe_decode_affine_amd import synth, workloads
+
+    pairs = [(s, l) for s in range(64) for l in sorted(stack_host)]
+    done, t0 = 0, time.perf_counter()
+    for s, l in pairs:
+        orc.moe_ffn_token(stack_host[l], synth.hidden_vector(seed, s, l))
+        done += 1
+        if time.perf_counter() - t0 > budget_s and done >= 2:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    bytes_per = workloads.decode_layer_bytes()
+    return {"value": round(bytes_per * done / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} (step, layer) decode MoE layers of the 40-layer workload, layers "
+                      f"{sorted(stack_host)}, steps from 0; {dt:.1f} s wall; numpy fp64 oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=40)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and LM-head legs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_moe_decode_affine_amd import binding as B
+    from quantized_moe_decode_affine_amd import synth, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.load_library()
+    dev = "cuda"
+
+    # ---------------------------------------------------------- decode loop
+    log(f"building {args.layers} decode layers")
+    t0 = time.perf_counter()
+    stack = workloads.DecodeStack(seed=2, n_layers=args.layers, n_steps=64, device=dev,
+                                  keep_host=(0, 1) if not args.no_cpu else (),
+                                  progress=lambda l: log(f"layer {l} uploaded") if l % 10 == 9 else None)
+    torch.cuda.synchronize()
+    log(f"decode stack ready: {stack.weight_bytes / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
+
+    for s in range(args.warmup):
+        stack.step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    h0 = time.perf_counter()
+    for s in range(args.steps):
+        stack.step(s)
+    host_s = time.perf_counter() - h0
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / args.steps
+    layer_bytes = workloads.decode_layer_bytes()
+    step_bytes = layer_bytes * args.layers
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    layer_us = ms_step * 1e3 / args.layers
+    log(f"decode: {ms_step * 1e3:.1f} us/step, {layer_us:.2f} us/layer, {gbs:.1f} GB/s; host enqueue "
+        f"{host_s / args.steps * 1e6:.1f} us/step")
+
+    # determinism: the same step twice gives the same expert ids
+    stack.step(0, record_ids=True)
+    torch.cuda.synchronize()
+    ids_a = stack.ids.cpu().numpy().copy()
+    stack.step(0, record_ids=True)
+    torch.cuda.synchronize()
+    digest_ok = bool(np.array_equal(ids_a, stack.ids.cpu().numpy()))
+
+    result = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.layers}-layer MoE decode loop, batch 1 (hidden 2048, 256 routed + 1 shared "
+                               f"experts, top-8, SwiGLU, affine Q4 g64 weights, bf16 router); per-step seeded "
+                               f"random layer inputs",
+                   "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
+                   "weights_gb": round(stack.weight_bytes / 1e9, 2), "bytes_per_layer": layer_bytes,
+                   "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                   "us_per_layer": round(layer_us, 3),
+                   "host_enqueue_us_per_step": round(host_s / args.steps * 1e6, 1),
+                   "ids_repeat": digest_ok},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "moe_ffn_decode (one layer call)",
+                     "unit_bytes": layer_bytes, "avg_us": round(layer_us, 3)},
+    }
+    host_layers = dict(stack.host)
+    del stack
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        # ------------------------------------------------------- prefill chunk
+        log("building the prefill layer")
+        layer = synth.moe_layer(1)
+        dl = B.DeviceLayer(layer, dev)
+        del layer
+        X = B.bf16_tensor(synth.token_rows(3, 2048, synth.HIDDEN), dev)
+        ws = B.workspace(B.workspace_bytes(B.OP_FFN_PREFILL, dl, rows=2048), dev)
+        Y = torch.empty((2048, synth.HIDDEN), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
+        torch.cuda.synchronize()
+        reps = 10
+        ev0.record()
+        for _ in range(reps):
+            B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        p_us = ev0.elapsed_time(ev1) * 1e3 / reps
+        flops = workloads.prefill_expert_flops()
+        tfl = flops / (p_us * 1e-6) / 1e12
+        result["prefill"] = {"workload": "2,048-token chunk through one MoE layer (route, permute, grouped Q4 "
+                                         "GEMMs with SwiGLU, combine)",
+                             "us_per_layer": round(p_us, 2), "tokens_per_s": round(2048 / (p_us * 1e-6), 1),
+                             "expert_gflop": round(flops / 1e9, 3),
+                             "tflops_whole_layer": round(tfl, 2),
+                             "pct_of_bf16_peak_whole_layer": round(100 * tfl / BF16_PEAK_TFLOPS, 2)}
+        log(f"prefill: {p_us:.1f} us/layer, {tfl:.1f} TFLOP/s over the whole layer")
+        del dl, X, ws, Y
+        torch.cuda.empty_cache()
+
+        # ------------------------------------------------------------ LM head
+        log("building the LM head (two copies)")
+        mat = synth.lm_head()
+        Ws = [B.DeviceQ4(*mat, device=dev), B.DeviceQ4(*mat, device=dev)]
+        del mat
+        lm = {}
+        for batch in (1, 4):
+            Xh = B.bf16_tensor(synth.token_rows(4, batch, synth.HIDDEN, index=batch), dev)
+            wsl = B.workspace(B.workspace_bytes(B.OP_LMHEAD, W=Ws[0], rows=batch), dev)
+            for i in range(4):
+                B.lmhead_argmax(Ws[i % 2], Xh, ws=wsl)
+            torch.cuda.synchronize()
+            reps = 20
+            ev0.record()
+            for i in range(reps):
+                B.lmhead_argmax(Ws[i % 2], Xh, ws=wsl)
+            ev1.record()
+            torch.cuda.synchronize()
+            us = ev0.elapsed_time(ev1) * 1e3 / reps
+            nbytes = workloads.q4_matrix_bytes(synth.VOCAB, synth.HIDDEN) + batch * synth.HIDDEN * 2
+            lm[f"B{batch}"] = {"us": round(us, 2), "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                               "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        result["lmhead"] = dict(workload="LM-head Q4 GEMV + greedy argmax, 151,936 x 2048", **lm)
+        log(f"lmhead: {lm}")
+        del Ws
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(host_layers, seed=2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * q4moe — affine 4-bit mixture-of-experts feed-forward on AMD MI355X (gfx950).
+ *
+ * Weight format (lily README, introduction and "Requirements": MLX affine
+ * 4-bit weights, group size 64).  A Q4 matrix of n rows and k columns is
+ *   codes  uint32 [n][k/8]   eight 4-bit codes per word; column j of a row is
+ *                             in word j/8 at bits [4*(j%8), 4*(j%8)+4)
+ *   scales bf16   [n][k/64]  one scale per 64 consecutive columns of a row
+ *   biases bf16   [n][k/64]  one bias per 64 consecutive columns of a row
+ * and stands for w[r][j] = scale[r][j/64] * code[r][j] + bias[r][j/64].
+ * All arrays are row-major and contiguous.  Stacked matrices (count > 1) are
+ * laid out [count][n][...].  Activations are bfloat16 bit patterns.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named in the argument lists are DEVICE pointers owned by the
+ *    caller, except the descriptor structs, which are host memory read during
+ *    the call only.  The library allocates nothing and keeps no state between
+ *    calls; scratch comes from the caller's workspace (size from
+ *    q4moe_workspace_bytes, 256-byte aligned).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *    the call returns without synchronising.  Inputs must stay unmodified and
+ *    the workspace untouched until the stream reaches the end of the call.
+ *  - Arguments are validated on the host before any HIP call.  Invalid shapes,
+ *    null pointers or misaligned buffers return Q4MOE_EINVAL (or
+ *    Q4MOE_EUNSUPPORTED for valid shapes outside what the kernels handle) and
+ *    enqueue nothing.  A HIP launch error returns Q4MOE_EHIP.  There is no
+ *    fallback path.  No C++ exception crosses this interface.
+ *  - Alignment: codes, activations and outputs 16-byte aligned; scale and bias
+ *    arrays 2-byte aligned; workspaces 256-byte aligned.
+ */
+#ifndef Q4MOE_H
+#define Q4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t q4moe_bf16;   /* raw bfloat16 bits */
+typedef void* q4moe_stream;    /* hipStream_t */
+
+enum {
+  Q4MOE_OK = 0,
+  Q4MOE_EINVAL = 1,        /* null pointer, bad shape, misaligned buffer */
+  Q4MOE_EUNSUPPORTED = 2,  /* valid but outside the kernels' limits */
+  Q4MOE_EWORKSPACE = 3,    /* workspace missing or smaller than required */
+  Q4MOE_EHIP = 4           /* a HIP runtime or launch error */
+};
+
+enum { Q4MOE_OUT_F32 = 0, Q4MOE_OUT_BF16 = 1 };
+
+/* Operation ids for q4moe_workspace_bytes. */
+enum {
+  Q4MOE_OP_GEMV = 0,
+  Q4MOE_OP_GEMM = 1,
+  Q4MOE_OP_ROUTE = 2,
+  Q4MOE_OP_PERMUTE = 3,
+  Q4MOE_OP_FFN_DECODE = 4,
+  Q4MOE_OP_FFN_PREFILL = 5,
+  Q4MOE_OP_LMHEAD = 6
+};
+
+/* A Q4 matrix, or `count` stacked matrices of the same shape. */
+typedef struct {
+  const uint32_t* codes;
+  const q4moe_bf16* scales;
+  const q4moe_bf16* biases;
+  int64_t count;  /* >= 1 */
+  int64_t n;      /* rows per matrix */
+  int64_t k;      /* columns, a multiple of 64 */
+} q4moe_matrix;
+
+/*
+ * One MoE feed-forward layer.  Routed expert e has gate and up matrices of
+ * `inter` rows by `hidden` columns and a down matrix of `hidden` rows by
+ * `inter` columns (gate/up/down stacked with count = n_experts).  The shared
+ * expert, when sh_gate.codes is non-null, has the same shapes with count 1
+ * and is added with weight 1.  The router is bf16 [n_experts][hidden].
+ */
+typedef struct {
+  int32_t hidden;
+  int32_t inter;
+  int32_t n_experts;
+  int32_t top_k;
+  const q4moe_bf16* router;
+  q4moe_matrix gate, up, down;
+  q4moe_matrix sh_gate, sh_up, sh_down;
+} q4moe_layer;
+
+/*
+ * y = W x, one bf16 vector x[k] against every row of W (count*n rows), fp32
+ * accumulation, y written as fp32 or bf16 [count*n].  The decode form of the
+ * 4-bit weight stream (lily-qwen3.8-flash-next README, "How the speed was
+ * achieved": decode reads every weight once and is bandwidth-bound).
+ */
+int q4_gemv(const q4moe_matrix* W, const q4moe_bf16* x, void* y, int out_dtype,
+            q4moe_stream stream);
+
+/*
+ * Y[m][r] = sum_j X[m][j] W[r][j] for bf16 rows X[m][k], Y [m][count*n] fp32 or
+ * bf16.  The prefill form, run on bf16 matrix cores with exact dequantization
+ * (lily-qwen3.8-flash-next README, "How the speed was achieved": prefill GEMMs
+ * on the tensor units).  Needs Q4MOE_OP_GEMM workspace (m).
+ */
+int q4_gemm(const q4moe_matrix* W, const q4moe_bf16* X, int64_t m, void* Y, int out_dtype,
+            void* workspace, size_t workspace_bytes, q4moe_stream stream);
+
+/*
+ * Router: logits[t][e] = router[e] . X[t] (fp32 accumulation), softmax over
+ * all n_experts, the top_k largest kept in descending order (equal logits:
+ * lower expert id first), their probabilities renormalised to sum to 1.
+ * Writes ids int32 [T][top_k] and weights fp32 [T][top_k].  1 <= top_k <= 32,
+ * top_k <= n_experts <= 1024, hidden a multiple of 64.  Needs
+ * Q4MOE_OP_ROUTE workspace (T).
+ */
+int moe_route_topk(const q4moe_bf16* router, int32_t n_experts, int32_t hidden,
+                   const q4moe_bf16* X, int64_t T, int32_t top_k, int32_t* ids, float* weights,
+                   void* workspace, size_t workspace_bytes, q4moe_stream stream);
+
+/*
+ * Stable counting sort of the T*top_k rows r = t*top_k + slot by expert id
+ * (token-to-expert grouping for the prefill expert GEMM; lily-qwen3.8-flash-next
+ * README, "How the speed was achieved").  Writes offsets int32 [n_experts+1]
+ * (offsets[e]..offsets[e+1] is expert e's segment), sorted_rows int32 [T*top_k]
+ * (rows of each segment in increasing r) and inv_rows int32 [T*top_k] with
+ * inv_rows[sorted_rows[p]] = p.  ids must lie in [0, n_experts); an
+ * out-of-range id is skipped by the kernels and leaves the outputs
+ * inconsistent.  Needs Q4MOE_OP_PERMUTE workspace (T*top_k).
+ */
+int moe_permute(const int32_t* ids, int64_t T, int32_t top_k, int32_t n_experts,
+                int32_t* offsets, int32_t* sorted_rows, int32_t* inv_rows,
+                void* workspace, size_t workspace_bytes, q4moe_stream stream);
+
+/*
+ * One token through the MoE layer (batch-1 greedy decode step):
+ *   y = sum_i w_i down_{e_i}(silu(gate_{e_i} x) * up_{e_i} x) + shared(x)
+ * with (e_i, w_i) from the router as in moe_route_topk.  x bf16 [hidden]; y fp32
+ * or bf16 [hidden].  ids_out int32 [top_k] and w_out fp32 [top_k] may be null.
+ * Intermediates stay fp32.  Needs Q4MOE_OP_FFN_DECODE workspace.
+ */
+int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int out_dtype,
+                   int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
+                   q4moe_stream stream);
+
+/*
+ * T tokens through the MoE layer (a prefill chunk, 2,048 tokens in the
+ * "Measurement contract" of "2026-09-02: Lily vs MLX 0.32.2"): route, permute
+ * by expert, grouped bf16-MFMA GEMMs for gate/up with SwiGLU and for down with
+ * the routing weight, then combine back in token order.  Row t of Y equals
+ * moe_ffn_decode on X[t] up to rounding; the SwiGLU output is rounded to bf16
+ * once before the down GEMM.  Y fp32 or bf16 [T][hidden].  Needs
+ * Q4MOE_OP_FFN_PREFILL workspace (T).
+ */
+int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, void* Y,
+                    int out_dtype, void* workspace, size_t workspace_bytes, q4moe_stream stream);
+
+/*
+ * Greedy LM head: logits[b][r] = W[r] . X[b] in fp32 for b < B (1 <= B <= 8),
+ * ids[b] = the lowest index of the largest logit (Lily decodes greedily: lily
+ * README, introduction).  max_logit fp32 [B] may be null.  Needs
+ * Q4MOE_OP_LMHEAD workspace (B).
+ */
+int lmhead_argmax(const q4moe_matrix* W, const q4moe_bf16* X, int64_t B, int32_t* ids,
+                  float* max_logit, void* workspace, size_t workspace_bytes, q4moe_stream stream);
+
+/*
+ * Workspace bytes for an operation.  `layer` is read for the FFN and ROUTE
+ * ops (ROUTE uses layer->n_experts), `W` for GEMM and LMHEAD; `rows` is T, m
+ * or B.  Returns 0 when no workspace is needed or the arguments are invalid.
+ */
+size_t q4moe_workspace_bytes(int op, const q4moe_layer* layer, const q4moe_matrix* W, int64_t rows);
+
+/* Static text for a status code. */
+const char* q4moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4MOE_H */

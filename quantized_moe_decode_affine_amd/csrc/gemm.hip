@@ -1,0 +1,527 @@
+// Grouped affine-Q4 GEMM on bf16 matrix cores, and the prefill MoE layer
+// built on it (lily-qwen3.8-flash-next README, "How the speed was achieved":
+// prefill is compute-bound and runs the expert GEMM over token-to-expert
+// groups; "2026-09-02: Lily vs MLX 0.32.2", "Measurement contract": prompts go
+// through in 2,048-token chunks).
+//
+// Exact dequantization on MFMA: the B operand holds the codes as bfloat16
+// (128 + q) (common.h), so one 64-column group yields
+//   P'[m][n] = sum_j x[m][j] (128 + q[n][j])        (exact products, fp32 sum)
+// and the output accumulates scale[n][g] * P'[m][n] per group (one VALU FMA
+// per element per group).  The remaining term
+//   sum_g (bias - 128*scale)[n][g] * rowsum_g(x)[m]
+// is itself a small product over the group index; both factors are split
+// exactly into bfloat16 parts (3 for the fp32 row sums, 2 for the offset
+// bias, which needs at most 16 significant bits) and fed to the same MFMA
+// after the main loop.  No weight is rounded.
+//
+// Tiling: a workgroup (4 waves) owns 128 rows of one group (expert) and 256
+// output columns (or 128 gate + 128 up columns for the SwiGLU epilogue); each
+// wave computes 4 x 2 MFMA 32x32 blocks.  The row tile is staged through LDS
+// (permuted into the nibble-pair order) with one group of look-ahead; each
+// lane loads its own 16 code bytes per group for its column.  Workgroups of
+// the same row tile are placed on the same XCD so the row tile stays in that
+// XCD's L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace q4moe {
+
+namespace {
+
+constexpr int BM = 128;          // rows per tile
+constexpr int BN = 256;          // output columns per tile (store/scale)
+constexpr int A_ROW_BYTES = 144; // 128 bytes of one row's group + 16 bytes pad
+constexpr int kXcd = 8;
+
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SCALE = 2 };
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct GemmParams {
+  const uint16_t* A;          // bf16 rows [*][K]
+  const uint16_t* xs;         // bf16 [*][3][Gp] row group-sum parts, same row indexing as A
+  const int32_t* sorted_rows; // gather mode: positions p < P read row sorted_rows[p] / topk
+  int gather;                 // 1: gather rows as above (p >= P read row p - P); 0: row p
+  int topk;
+  int64_t P;                  // positions of the routed segments
+  int K, G, Gp;
+  int N;                      // output columns (store/scale) or intermediate width (swiglu)
+  Q4Mat W, W2;                // routed experts (W2 = up for swiglu), stacked
+  int64_t w_codes_stride, w_groups_stride;
+  Q4Mat X, X2;                // the extra segment's matrix (shared expert / single matrix)
+  int n_routed;
+  const int32_t* offsets;     // [n_routed+1]
+  const int32_t* tile_offsets;// [n_routed+1]
+  int64_t extra_rows;
+  int extra_tiles;
+  int n_slices;
+  int epi;
+  void* out;
+  int out_bf16;
+  int64_t ldo;
+  const float* route_w;       // [P] by original row (scale epilogue)
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint4 codes_to_operand(uint32_t w) {
+  return make_uint4(nib_pair(w, 0), nib_pair(w, 4), nib_pair(w, 8), nib_pair(w, 12));
+}
+
+__global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
+  __shared__ __align__(16) uint8_t s_a[2][BM * A_ROW_BYTES];
+  __shared__ int32_t s_src[BM];
+  __shared__ int64_t s_row0;
+  __shared__ int32_t s_rows, s_seg;
+
+  // ---- tile of this workgroup (XCD-aware: all slices of a tile share an XCD)
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcd;
+  const int q = bid / kXcd;
+  const int slice = q % p.n_slices;
+  const int tile = (q / p.n_slices) * kXcd + xcd;
+  if (threadIdx.x == 0) {
+    const int routed_tiles = p.n_routed ? p.tile_offsets[p.n_routed] : 0;
+    int seg = -2;
+    int64_t row0 = 0;
+    int rows = 0;
+    if (tile < routed_tiles) {
+      int lo = 0, hi = p.n_routed;  // find e with tile_offsets[e] <= tile < tile_offsets[e+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.tile_offsets[mid] <= tile) lo = mid; else hi = mid;
+      }
+      const int mt = tile - p.tile_offsets[lo];
+      row0 = (int64_t)p.offsets[lo] + (int64_t)mt * BM;
+      rows = (int)min<int64_t>(BM, (int64_t)p.offsets[lo + 1] - row0);
+      seg = lo;
+    } else if (tile - routed_tiles < p.extra_tiles) {
+      const int mt = tile - routed_tiles;
+      row0 = p.P + (int64_t)mt * BM;
+      rows = (int)min<int64_t>(BM, p.P + p.extra_rows - row0);
+      seg = -1;
+    }
+    s_seg = seg;
+    s_row0 = row0;
+    s_rows = rows;
+  }
+  __syncthreads();
+  const int seg = s_seg;
+  if (seg == -2) return;
+  const int64_t row0 = s_row0;
+  const int rows = s_rows;
+
+  // ---- source row of each tile row (clamped to a valid row for padding rows)
+  for (int r = threadIdx.x; r < BM; r += blockDim.x) {
+    const int64_t pos = row0 + min(r, rows - 1);
+    int64_t src = pos;
+    if (p.gather) src = pos < p.P ? (int64_t)(p.sorted_rows[pos] / p.topk) : pos - p.P;
+    s_src[r] = (int32_t)src;
+  }
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int ln = lane & 31, lh = lane >> 5;
+  const bool swiglu = p.epi == EPI_SWIGLU;
+
+  // ---- weight rows (B columns) of this lane: nb = 0, 1
+  const Q4Mat& M0 = seg >= 0 ? p.W : p.X;
+  const Q4Mat& M1 = seg >= 0 ? (swiglu ? p.W2 : p.W) : (swiglu ? p.X2 : p.X);
+  const int64_t oc = seg >= 0 ? seg * p.w_codes_stride : 0;
+  const int64_t og = seg >= 0 ? seg * p.w_groups_stride : 0;
+  int col[2];
+  const uint32_t* bcodes[2];
+  const uint16_t* bscale[2];
+  const uint16_t* bbias[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    col[nb] = swiglu ? slice * 128 + wave * 32 + ln : slice * BN + wave * 64 + nb * 32 + ln;
+    const int64_t wrow = min(col[nb], p.N - 1);
+    const Q4Mat& Mx = nb == 0 ? M0 : M1;
+    bcodes[nb] = Mx.codes + oc + wrow * (p.K >> 3);
+    bscale[nb] = Mx.scales + og + wrow * p.G;
+    bbias[nb] = Mx.biases + og + wrow * p.G;
+  }
+
+  // ---- A staging: thread -> (row, half group)
+  const int a_row = threadIdx.x >> 1, a_half = threadIdx.x & 1;
+  __syncthreads();  // s_src ready
+  const uint4* a_src = reinterpret_cast<const uint4*>(p.A + (int64_t)s_src[a_row] * p.K) + a_half * 4;
+  const bool a_live = a_row < rows;
+  auto load_a = [&](int g, uint4 (&ra)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = a_live ? a_src[g * 8 + j] : make_uint4(0, 0, 0, 0);
+  };
+  auto store_a = [&](int buf, const uint4 (&ra)[4]) {
+    uint8_t* dst = s_a[buf] + a_row * A_ROW_BYTES + a_half * 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(dst + 16 * j) = permute_block(ra[j]);
+  };
+  auto load_b = [&](int g, uint4 (&rb)[2], uint32_t (&sc)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      rb[nb] = reinterpret_cast<const uint4*>(bcodes[nb])[2 * g + lh];
+      sc[nb] = bscale[nb][g];
+    }
+  };
+
+  const int mblocks = (rows + 31) >> 5;  // active 32-row blocks (wave-uniform)
+  const f32x16_t zero16 = {};
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16;
+
+  uint4 ra[4];
+  uint4 rb[2], rb_next[2];
+  uint32_t sc[2], sc_next[2];
+  load_a(0, ra);
+  load_b(0, rb, sc);
+  store_a(0, ra);
+  __syncthreads();
+
+  for (int g = 0; g < p.G; ++g) {
+    const int buf = g & 1;
+    const bool more = g + 1 < p.G;
+    if (more) {
+      load_a(g + 1, ra);
+      load_b(g + 1, rb_next, sc_next);
+    }
+    f32x16_t part[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t bop[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t w = s == 0 ? rb[nb].x : s == 1 ? rb[nb].y : s == 2 ? rb[nb].z : rb[nb].w;
+        bop[nb] = as_bf16x8(codes_to_operand(w));
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb < mblocks) {
+          const uint4 av = *reinterpret_cast<const uint4*>(s_a[buf] + (mb * 32 + ln) * A_ROW_BYTES + (4 * lh + s) * 16);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            part[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), bop[nb],
+                                                                   s == 0 ? zero16 : part[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float scale = bf16_bits_to_f32(sc[nb]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        if (mb < mblocks)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[mb][nb][i] = fmaf(scale, part[mb][nb][i], acc[mb][nb][i]);
+    }
+    if (more) {
+      store_a(buf ^ 1, ra);
+      rb[0] = rb_next[0]; rb[1] = rb_next[1];
+      sc[0] = sc_next[0]; sc[1] = sc_next[1];
+    }
+    __syncthreads();
+  }
+
+  // ---- offset/bias term: sum_g (bias - 128 scale)[n][g] * rowsum_g[m], on MFMA with exact bf16 parts
+  for (int t = 0; t * 16 < p.Gp; ++t) {
+    const int gbase = t * 16 + 8 * lh;
+    uint4 bc[2][2];  // [nb][hi/lo]
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int g = gbase + j;
+        float c = 0.f;
+        if (g < p.G) c = bf16_bits_to_f32(bbias[nb][g]) - 128.0f * bf16_bits_to_f32(bscale[nb][g]);
+        hi[j] = f32_to_bf16_bits(c);
+        lo[j] = f32_to_bf16_bits(c - bf16_bits_to_f32(hi[j]));
+      }
+      bc[nb][0] = make_uint4(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16);
+      bc[nb][1] = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb >= mblocks) continue;
+      const uint16_t* xr = p.xs + (int64_t)s_src[mb * 32 + ln] * 3 * p.Gp + gbase;
+#pragma unroll
+      for (int part_i = 0; part_i < 3; ++part_i) {
+        const uint4 xa = *reinterpret_cast<const uint4*>(xr + part_i * p.Gp);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xa), as_bf16x8(bc[nb][hl]), acc[mb][nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue.  D layout: column = lane % 32, row = 8*(i/4) + 4*(lane/32) + i%4.
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if (mb >= mblocks) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = mb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+      if (r >= rows) continue;
+      const int64_t pos = row0 + r;
+      if (swiglu) {
+        if (col[0] < p.N) {
+          const float a = silu(acc[mb][0][i]) * acc[mb][1][i];
+          reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + col[0]] = (uint16_t)f32_to_bf16_bits(a);
+        }
+      } else {
+        float wgt = 1.0f;
+        if (p.epi == EPI_SCALE && pos < p.P) wgt = p.route_w[p.sorted_rows[pos]];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          if (col[nb] >= p.N) continue;
+          const float v = wgt * acc[mb][nb][i];
+          if (p.out_bf16)
+            reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + col[nb]] = (uint16_t)f32_to_bf16_bits(v);
+          else
+            reinterpret_cast<float*>(p.out)[pos * p.ldo + col[nb]] = v;
+        }
+      }
+    }
+  }
+}
+
+// Per-row, per-64-column-group sums of a bf16 matrix, split exactly into three
+// bfloat16 parts: out[r][part][g] (groups padded with zeros to Gp).
+__global__ void row_group_sums_kernel(const uint16_t* __restrict__ A, int64_t rows, int K, int Gp,
+                                      uint16_t* __restrict__ out) {
+  const int G = K >> 6;
+  const int64_t total = rows * Gp;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / Gp;
+    const int g = (int)(i - r * Gp);
+    float s = 0.f;
+    if (g < G) {
+      const uint4* src = reinterpret_cast<const uint4*>(A + r * K + g * 64);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint4 v = src[j];
+        s += (bf16_bits_to_f32(v.x & 0xFFFFu) + bf16_bits_to_f32(v.x >> 16)) +
+             (bf16_bits_to_f32(v.y & 0xFFFFu) + bf16_bits_to_f32(v.y >> 16)) +
+             (bf16_bits_to_f32(v.z & 0xFFFFu) + bf16_bits_to_f32(v.z >> 16)) +
+             (bf16_bits_to_f32(v.w & 0xFFFFu) + bf16_bits_to_f32(v.w >> 16));
+      }
+    }
+    const uint32_t h = f32_to_bf16_bits(s);
+    const float r1 = s - bf16_bits_to_f32(h);
+    const uint32_t m = f32_to_bf16_bits(r1);
+    const uint32_t l = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));
+    uint16_t* o = out + r * 3 * Gp + g;
+    o[0] = (uint16_t)h;
+    o[Gp] = (uint16_t)m;
+    o[2 * Gp] = (uint16_t)l;
+  }
+}
+
+// Y[t] = Ys[P + t] (shared expert, weight already 1) + sum_slot Ys[inv[t*k + slot]], fixed slot order.
+__global__ void combine_kernel(const float* __restrict__ Ys, const int32_t* __restrict__ inv, int64_t T, int k,
+                               int H, int has_shared, int64_t P, void* __restrict__ Y, int out_bf16) {
+  const int H4 = H >> 2;
+  const int64_t total = T * H4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / H4;
+    const int c = (int)(i - t * H4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (has_shared) acc = reinterpret_cast<const float4*>(Ys + (P + t) * H)[c];
+    for (int j = 0; j < k; ++j) {
+      const float4 v = reinterpret_cast<const float4*>(Ys + (int64_t)inv[t * k + j] * H)[c];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (out_bf16) {
+      uint2 o;
+      o.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+      o.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + t * H)[c] = o;
+    } else {
+      reinterpret_cast<float4*>(static_cast<float*>(Y) + t * H)[c] = acc;
+    }
+  }
+}
+
+int grid_for(int64_t n, int block) {
+  int64_t b = (n + block - 1) / block;
+  if (b > 65536) b = 65536;
+  return (int)(b < 1 ? 1 : b);
+}
+
+int pad16(int g) { return (g + 15) & ~15; }
+
+hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream) {
+  const int64_t tiles_rounded = (max_tiles + kXcd - 1) / kXcd * kXcd;
+  const int64_t blocks = tiles_rounded * p.n_slices;
+  hipLaunchKernelGGL(grouped_q4_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_sums(const uint16_t* A, int64_t rows, int K, uint16_t* out, hipStream_t stream) {
+  const int Gp = pad16(K >> 6);
+  hipLaunchKernelGGL(row_group_sums_kernel, dim3(grid_for(rows * Gp, 256)), dim3(256), 0, stream, A, rows, K, Gp,
+                     out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int64_t m, int k) { return align256((size_t)m * 3 * pad16(k / 64) * 2); }
+
+hipError_t run_q4_gemm(const Q4Mat& W, int64_t n, int k, const uint16_t* X, int64_t m, void* Y, int out_bf16,
+                       void* ws, hipStream_t stream) {
+  uint16_t* xs = static_cast<uint16_t*>(ws);
+  hipError_t e = launch_row_sums(X, m, k, xs, stream);
+  if (e != hipSuccess) return e;
+  GemmParams p{};
+  p.A = X;
+  p.xs = xs;
+  p.gather = 0;
+  p.P = 0;
+  p.K = k;
+  p.G = k / 64;
+  p.Gp = pad16(p.G);
+  p.N = (int)n;
+  p.X = W;
+  p.X2 = W;
+  p.n_routed = 0;
+  p.extra_rows = m;
+  p.extra_tiles = (int)((m + BM - 1) / BM);
+  p.n_slices = (int)((n + BN - 1) / BN);
+  p.epi = EPI_STORE;
+  p.out = Y;
+  p.out_bf16 = out_bf16;
+  p.ldo = n;
+  return launch_grouped(p, p.extra_tiles, stream);
+}
+
+namespace {
+struct PrefillWs {
+  float* logits;
+  int32_t* ids;
+  float* weights;
+  int32_t* offsets;
+  int32_t* tile_offsets;
+  int32_t* sorted_rows;
+  int32_t* inv;
+  void* perm_ws;
+  uint16_t* xs_x;
+  uint16_t* act;
+  uint16_t* xs_act;
+  float* ys;
+  size_t total;
+};
+
+PrefillWs carve(void* base, int64_t T, int H, int I, int E, int k, int has_shared) {
+  PrefillWs w{};
+  char* c = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* r = c ? c + off : nullptr; off += align256(bytes); return r; };
+  const int64_t P = T * k, R = P + (has_shared ? T : 0);
+  w.logits = reinterpret_cast<float*>(take(route_workspace_bytes(T, E)));
+  w.ids = reinterpret_cast<int32_t*>(take(P * 4));
+  w.weights = reinterpret_cast<float*>(take(P * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+  w.tile_offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+  w.sorted_rows = reinterpret_cast<int32_t*>(take(P * 4));
+  w.inv = reinterpret_cast<int32_t*>(take(P * 4));
+  w.perm_ws = take(permute_workspace_bytes(P, E));
+  w.xs_x = reinterpret_cast<uint16_t*>(take((size_t)T * 3 * pad16(H / 64) * 2));
+  w.act = reinterpret_cast<uint16_t*>(take((size_t)R * I * 2));
+  w.xs_act = reinterpret_cast<uint16_t*>(take((size_t)R * 3 * pad16(I / 64) * 2));
+  w.ys = reinterpret_cast<float*>(take((size_t)R * H * 4));
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t prefill_workspace_bytes(int64_t T, int hidden, int inter, int n_experts, int top_k, int has_shared) {
+  return carve(nullptr, T, hidden, inter, n_experts, top_k, has_shared).total;
+}
+
+hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t T, void* Y, int out_bf16, void* ws,
+                               hipStream_t stream) {
+  const int H = L.hidden, I = L.inter, E = L.n_experts, k = L.top_k;
+  PrefillWs w = carve(ws, T, H, I, E, k, L.has_shared);
+  const int64_t P = T * k;
+  hipError_t e = run_route_topk(L.router, E, H, X, T, k, w.ids, w.weights, w.logits, stream);
+  if (e != hipSuccess) return e;
+  e = run_permute(w.ids, P, E, w.offsets, w.sorted_rows, w.inv, w.perm_ws, BM, w.tile_offsets, stream);
+  if (e != hipSuccess) return e;
+  e = launch_row_sums(X, T, H, w.xs_x, stream);
+  if (e != hipSuccess) return e;
+
+  const int64_t max_routed_tiles = (P + BM - 1) / BM + E;
+  const int shared_tiles = L.has_shared ? (int)((T + BM - 1) / BM) : 0;
+
+  // gate/up with SwiGLU -> act (bf16, sorted positions; shared rows appended)
+  GemmParams p{};
+  p.A = X;
+  p.xs = w.xs_x;
+  p.sorted_rows = w.sorted_rows;
+  p.gather = 1;
+  p.topk = k;
+  p.P = P;
+  p.K = H;
+  p.G = H / 64;
+  p.Gp = pad16(p.G);
+  p.N = I;
+  p.W = L.gate;
+  p.W2 = L.up;
+  p.w_codes_stride = (int64_t)I * (H / 8);
+  p.w_groups_stride = (int64_t)I * (H / 64);
+  p.X = L.sh_gate;
+  p.X2 = L.sh_up;
+  p.n_routed = E;
+  p.offsets = w.offsets;
+  p.tile_offsets = w.tile_offsets;
+  p.extra_rows = L.has_shared ? T : 0;
+  p.extra_tiles = shared_tiles;
+  p.n_slices = (I + 127) / 128;
+  p.epi = EPI_SWIGLU;
+  p.out = w.act;
+  p.out_bf16 = 1;
+  p.ldo = I;
+  e = launch_grouped(p, max_routed_tiles + shared_tiles, stream);
+  if (e != hipSuccess) return e;
+
+  const int64_t R = P + (L.has_shared ? T : 0);
+  e = launch_row_sums(w.act, R, I, w.xs_act, stream);
+  if (e != hipSuccess) return e;
+
+  // down with the routing weight -> ys (fp32, sorted positions)
+  GemmParams d = p;
+  d.A = w.act;
+  d.xs = w.xs_act;
+  d.gather = 0;
+  d.K = I;
+  d.G = I / 64;
+  d.Gp = pad16(d.G);
+  d.N = H;
+  d.W = L.down;
+  d.W2 = L.down;
+  d.w_codes_stride = (int64_t)H * (I / 8);
+  d.w_groups_stride = (int64_t)H * (I / 64);
+  d.X = L.sh_down;
+  d.X2 = L.sh_down;
+  d.n_slices = (H + BN - 1) / BN;
+  d.epi = EPI_SCALE;
+  d.out = w.ys;
+  d.out_bf16 = 0;
+  d.ldo = H;
+  d.route_w = w.weights;
+  e = launch_grouped(d, max_routed_tiles + shared_tiles, stream);
+  if (e != hipSuccess) return e;
+
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * (H / 4), 256)), dim3(256), 0, stream, w.ys, w.inv, T, k, H,
+                     L.has_shared, P, Y, out_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace q4moe

@@ -1,0 +1,60 @@
+// Internal launchers behind the C ABI (abi.cpp validates every argument
+// before calling any of these).  All launch on the given stream and return
+// the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4moe {
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// ---- GEMV family (gemv.hip)
+size_t gemv_lds_bytes(int k, int B);
+int lmhead_partial_blocks(int64_t rows, int k, int B);
+hipError_t run_q4_gemv(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t rows,
+                       int k, const uint16_t* x, void* y, int out_bf16, hipStream_t stream);
+hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                             int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
+                             float* part_val, int32_t* part_idx, hipStream_t stream);
+
+// ---- Q4 matrices as seen by the kernels
+struct Q4Mat {
+  const uint32_t* codes;   // [count][n][k/8]
+  const uint16_t* scales;  // [count][n][k/64]
+  const uint16_t* biases;
+};
+
+// ---- decode MoE layer (decode.hip)
+struct DecodeLayer {
+  int hidden, inter, n_experts, top_k, has_shared;
+  const uint16_t* router;                // [E][H]
+  Q4Mat gate, up, down;                  // routed, stacked by expert
+  Q4Mat sh_gate, sh_up, sh_down;         // shared (count 1) when has_shared
+};
+size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k);
+hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_bf16, int32_t* ids_out,
+                              float* w_out, void* ws, hipStream_t stream);
+
+// ---- routing and permutation (route.hip)
+size_t route_workspace_bytes(int64_t T, int n_experts);
+hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* X, int64_t T, int k,
+                          int32_t* ids, float* weights, void* ws, hipStream_t stream);
+size_t permute_workspace_bytes(int64_t rows, int n_experts);
+// Stable counting sort of `rows` ids by expert.  When tile_offsets is non-null,
+// it receives E+1 prefix sums of ceil(count_e / tile_rows).
+hipError_t run_permute(const int32_t* ids, int64_t rows, int n_experts, int32_t* offsets, int32_t* sorted_rows,
+                       int32_t* inv_rows, void* ws, int tile_rows, int32_t* tile_offsets, hipStream_t stream);
+
+// ---- grouped MFMA GEMM and the prefill layer (gemm.hip)
+size_t gemm_workspace_bytes(int64_t m, int k);
+hipError_t run_q4_gemm(const Q4Mat& W, int64_t n, int k, const uint16_t* X, int64_t m, void* Y, int out_bf16,
+                       void* ws, hipStream_t stream);
+size_t prefill_workspace_bytes(int64_t T, int hidden, int inter, int n_experts, int top_k, int has_shared);
+hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t T, void* Y, int out_bf16,
+                               void* ws, hipStream_t stream);
+
+}  // namespace q4moe

@@ -1,0 +1,82 @@
+"""Device-resident workloads driven through the C ABI (used by bench.py and the
+full-size tests).
+
+* :class:`DecodeStack`: ``n_layers`` independent MoE layers (hidden 2048, 256
+  routed + 1 shared expert, top-8, Q4 g64; about 455 MB each) and a batch-1
+  decode loop.  Step s feeds layer l a seeded hidden vector x[s][l]; layers
+  run in order on one stream, each a full router -> top-k -> experts chain.
+* Byte and FLOP counts of the algorithmic work of each workload.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import binding as B
+from . import synth
+
+GROUP = 64
+
+
+def q4_matrix_bytes(n: int, k: int) -> int:
+    """Bytes of one Q4 matrix: 4 bits per weight plus a bf16 scale and bias per 64 weights."""
+    return n * k // 2 + 2 * 2 * n * (k // GROUP)
+
+
+def decode_layer_bytes(hidden=synth.HIDDEN, inter=synth.INTER, n_experts=synth.N_EXPERTS, top_k=synth.TOP_K,
+                       shared=True, out_bytes=4) -> int:
+    """Algorithmic bytes of one decode MoE layer: the selected experts' weights (and the shared
+    expert's), the bf16 router, the bf16 input and the output vector."""
+    expert = 2 * q4_matrix_bytes(inter, hidden) + q4_matrix_bytes(hidden, inter)
+    return (top_k + (1 if shared else 0)) * expert + n_experts * hidden * 2 + hidden * 2 + hidden * out_bytes
+
+
+def prefill_expert_flops(T=2048, hidden=synth.HIDDEN, inter=synth.INTER, top_k=synth.TOP_K, shared=True) -> int:
+    """FLOPs of the expert GEMMs of one prefill chunk (gate, up and down; 2 per multiply-add)."""
+    return 2 * T * (top_k + (1 if shared else 0)) * 3 * hidden * inter
+
+
+class DecodeStack:
+    """n_layers MoE layers on the device plus the per-(step, layer) decode inputs."""
+
+    def __init__(self, seed: int = 2, n_layers: int = 40, n_steps: int = 64, device="cuda", keep_host=(),
+                 progress=None, **shape):
+        self.seed, self.n_layers, self.n_steps = seed, n_layers, n_steps
+        self.layers, self.host = [], {}
+        for l in range(n_layers):
+            lay = synth.moe_layer(seed, l, **shape)
+            self.layers.append(B.DeviceLayer(lay, device))
+            if l in keep_host:
+                self.host[l] = lay
+            del lay
+            if progress:
+                progress(l)
+        H = self.layers[0].hidden
+        xs = [[synth.hidden_vector(seed, s, l, H) for l in range(n_layers)] for s in range(n_steps)]
+        import numpy as np
+        self.x = B.bf16_tensor(np.asarray(xs, dtype=np.uint16), device)          # [steps][layers][H]
+        self.y = torch.empty((n_layers, H), dtype=torch.float32, device=device)
+        self.ids = torch.empty((n_layers, self.layers[0].top_k), dtype=torch.int32, device=device)
+        self.ws = B.workspace(B.workspace_bytes(B.OP_FFN_DECODE, self.layers[0]), device)
+        lib = B.load_library()
+        self._fn = lib.moe_ffn_decode
+        self._refs = [ctypes.byref(d.struct) for d in self.layers]
+
+    @property
+    def weight_bytes(self) -> int:
+        return sum(d.nbytes for d in self.layers)
+
+    def step(self, s: int, record_ids: bool = False) -> None:
+        """Enqueue one decode step (all layers, in order) on the current stream."""
+        stream = torch.cuda.current_stream().cuda_stream
+        xs = self.x[s % self.n_steps]
+        H = self.y.shape[1]
+        x0, y0 = xs.data_ptr(), self.y.data_ptr()
+        ids0, kk = self.ids.data_ptr(), self.ids.shape[1]
+        ws, wsn = self.ws.data_ptr(), self.ws.numel()
+        for l in range(self.n_layers):
+            st = self._fn(self._refs[l], x0 + 2 * H * l, y0 + 4 * H * l, B.OUT_F32,
+                          (ids0 + 4 * kk * l) if record_ids else None, None, ws, wsn, stream)
+            if st != B.OK:
+                B._check("moe_ffn_decode", st)

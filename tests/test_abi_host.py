@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, and rejects invalid arguments with the
+documented status before any HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_decode_affine_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4moe.h")
+
+A = 0x10000          # fake, well-aligned device addresses: never dereferenced on these paths
+A2 = 0x20000
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B._LIB_PATH):
+        from quantized_moe_decode_affine_amd import build
+        build.build()
+    return B.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _header_functions()
+    assert set(declared) == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_strerror(lib):
+    for code in range(5):
+        assert lib.q4moe_strerror(code)
+    assert b"unknown" in lib.q4moe_strerror(99)
+
+
+def _mat(count=1, n=64, k=128, codes=A, scales=A2, biases=A2 + 0x1000):
+    return B.q4moe_matrix(codes, scales, biases, count, n, k)
+
+
+def _layer(H=128, I=64, E=4, k=2, shared=True, **over):
+    L = B.q4moe_layer(H, I, E, k, A, _mat(E, I, H), _mat(E, I, H), _mat(E, H, I),
+                      *( [_mat(1, I, H), _mat(1, I, H), _mat(1, H, I)] if shared else [B.q4moe_matrix()] * 3))
+    for key, v in over.items():
+        setattr(L, key, v)
+    return L
+
+
+def test_gemv_rejects(lib):
+    s = None
+    assert lib.q4_gemv(None, A, A, 0, s) == B.EINVAL
+    assert lib.q4_gemv(ctypes.byref(_mat(k=100)), A, A, 0, s) == B.EINVAL        # k % 64
+    assert lib.q4_gemv(ctypes.byref(_mat(codes=A + 4)), A, A, 0, s) == B.EINVAL  # codes misaligned
+    assert lib.q4_gemv(ctypes.byref(_mat(n=0)), A, A, 0, s) == B.EINVAL
+    assert lib.q4_gemv(ctypes.byref(_mat()), None, A, 0, s) == B.EINVAL
+    assert lib.q4_gemv(ctypes.byref(_mat()), A + 2, A, 0, s) == B.EINVAL         # x misaligned
+    assert lib.q4_gemv(ctypes.byref(_mat()), A, A, 7, s) == B.EINVAL             # out dtype
+    assert lib.q4_gemv(ctypes.byref(_mat(k=32768)), A, A, 0, s) == B.EUNSUPPORTED
+
+
+def test_gemm_rejects(lib):
+    W = ctypes.byref(_mat())
+    need = lib.q4moe_workspace_bytes(B.OP_GEMM, None, W, 100)
+    assert need > 0
+    assert lib.q4_gemm(W, A, -1, A, 0, A, need, None) == B.EINVAL
+    assert lib.q4_gemm(W, A, 100, A, 0, None, need, None) == B.EWORKSPACE
+    assert lib.q4_gemm(W, A, 100, A, 0, A, need - 1, None) == B.EWORKSPACE
+    assert lib.q4_gemm(W, A, 100, A, 0, A + 16, need, None) == B.EWORKSPACE      # workspace alignment
+    assert lib.q4_gemm(W, A, 0, A, 0, None, 0, None) == B.OK                     # empty: nothing enqueued
+
+
+def test_route_and_permute_reject(lib):
+    need = lib.q4moe_workspace_bytes(B.OP_ROUTE, ctypes.byref(_layer(E=256, k=8)), None, 10)
+    assert need >= 10 * 256 * 4
+    f = lib.moe_route_topk
+    assert f(A, 256, 2048, A, 10, 0, A, A, A, need, None) == B.EINVAL            # top_k 0
+    assert f(A, 4, 2048, A, 10, 5, A, A, A, need, None) == B.EINVAL              # top_k > E
+    assert f(A, 2048, 2048, A, 10, 8, A, A, A, need, None) == B.EUNSUPPORTED     # E > 1024
+    assert f(A, 256, 2048, A, 10, 33, A, A, A, need, None) == B.EUNSUPPORTED     # top_k > 32
+    assert f(A, 256, 100, A, 10, 8, A, A, A, need, None) == B.EINVAL             # hidden % 64
+    assert f(A, 256, 2048, A, 10, 8, None, A, A, need, None) == B.EINVAL
+    assert f(A, 256, 2048, A, 10, 8, A, A, A, 16, None) == B.EWORKSPACE
+    assert f(A, 256, 2048, A, 0, 8, A, A, None, 0, None) == B.OK                 # T = 0
+    pneed = lib.q4moe_workspace_bytes(B.OP_PERMUTE, ctypes.byref(_layer(E=256, k=8)), None, 2048)
+    assert pneed > 0
+    g = lib.moe_permute
+    assert g(None, 10, 8, 256, A, A, A, A, pneed, None) == B.EINVAL
+    assert g(A, 10, 0, 256, A, A, A, A, pneed, None) == B.EINVAL
+    assert g(A, 10, 8, 4096, A, A, A, A, pneed, None) == B.EUNSUPPORTED
+    assert g(A, 2048, 8, 256, A, A, A, A, 64, None) == B.EWORKSPACE
+
+
+def test_ffn_rejects(lib):
+    good = _layer()
+    need_d = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE, ctypes.byref(good), None, 1)
+    need_p = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(good), None, 50)
+    assert need_d > 0 and need_p > need_d
+    d, p = lib.moe_ffn_decode, lib.moe_ffn_prefill
+    bad_shapes = [
+        _layer(hidden=100), _layer(inter=96), _layer(top_k=0), _layer(top_k=5),
+        _layer(router=None), _layer(router=A + 8),
+    ]
+    for L in bad_shapes:
+        assert d(ctypes.byref(L), A, A, 0, None, None, A, need_d, None) == B.EINVAL
+        assert p(ctypes.byref(L), A, 50, A, 0, A, need_p, None) == B.EINVAL
+    L = _layer()
+    L.down = _mat(4, 64, 128)            # down must be hidden x inter
+    assert d(ctypes.byref(L), A, A, 0, None, None, A, need_d, None) == B.EINVAL
+    L = _layer()
+    L.sh_up = _mat(2, 64, 128)           # shared expert must have count 1
+    assert d(ctypes.byref(L), A, A, 0, None, None, A, need_d, None) == B.EINVAL
+    assert d(ctypes.byref(_layer(n_experts=2048, gate=_mat(2048, 64, 128), up=_mat(2048, 64, 128),
+                                 down=_mat(2048, 128, 64))), A, A, 0, None, None, A, need_d, None) == B.EUNSUPPORTED
+    assert d(ctypes.byref(good), A, A, 0, None, None, A, need_d - 1, None) == B.EWORKSPACE
+    assert d(ctypes.byref(good), A + 8, A, 0, None, None, A, need_d, None) == B.EINVAL
+    assert p(ctypes.byref(good), A, -3, A, 0, A, need_p, None) == B.EINVAL
+    assert p(ctypes.byref(good), A, 50, A, 0, A, need_p - 256, None) == B.EWORKSPACE
+    assert p(ctypes.byref(good), A, 0, A, 0, None, 0, None) == B.OK
+    # a layer without a shared expert is valid and needs no more workspace
+    noshared = _layer(shared=False)
+    assert lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(noshared), None, 50) < need_p
+
+
+def test_lmhead_rejects(lib):
+    W = ctypes.byref(_mat(1, 1000, 2048))
+    need = lib.q4moe_workspace_bytes(B.OP_LMHEAD, None, W, 4)
+    assert need > 0
+    f = lib.lmhead_argmax
+    assert f(W, A, 0, A, None, A, need, None) == B.EINVAL
+    assert f(W, A, 9, A, None, A, need, None) == B.EUNSUPPORTED
+    assert f(W, A, 4, None, None, A, need, None) == B.EINVAL
+    assert f(W, A, 4, A, None, A, need - 8, None) == B.EWORKSPACE
+    assert f(ctypes.byref(_mat(1, 1000, 8192)), A, 4, A, None, A, need, None) == B.EUNSUPPORTED
+
+
+def test_workspace_queries(lib):
+    assert lib.q4moe_workspace_bytes(B.OP_GEMV, None, None, 1) == 0
+    assert lib.q4moe_workspace_bytes(99, None, None, 1) == 0
+    assert lib.q4moe_workspace_bytes(B.OP_FFN_DECODE, ctypes.byref(_layer(hidden=100)), None, 1) == 0
+    assert lib.q4moe_workspace_bytes(B.OP_GEMM, None, None, 5) == 0
+    small = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(_layer()), None, 10)
+    big = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(_layer()), None, 1000)
+    assert 0 < small < big

@@ -1,0 +1,46 @@
+"""The 40-layer decode loop at full size (about 18 GB of Q4 weights), driven
+exactly as bench.py drives it, with sampled (step, layer) outputs checked
+against the oracle and the expert ids repeating bit for bit across rounds."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import q4moe_oracle as orc
+from quantized_moe_decode_affine_amd import synth
+from tests.parity_util import REL_L2_TOL, rel_l2, routing_ok, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_loop_full_size_sampled():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_moe_decode_affine_amd import binding as B, workloads
+
+    B.load_library()
+    sampled_layers = (0, 17, 39)
+    say("decode loop: building 40 layers")
+    stack = workloads.DecodeStack(seed=2, n_layers=40, n_steps=64, keep_host=sampled_layers,
+                                  progress=lambda l: say(f"  layer {l}") if l % 10 == 9 else None)
+    digests = []
+    for rnd in range(2):
+        for s in (0, 1, 63):
+            say(f"decode loop round {rnd} step {s}")
+            stack.step(s, record_ids=True)
+            torch.cuda.synchronize()
+            ids = stack.ids.cpu().numpy().copy()
+            digests.append(synth.fnv1a64(ids))
+            if rnd == 0 and s in (0, 63):
+                y = stack.y.double().cpu().numpy()
+                for l in sampled_layers:
+                    lay = stack.host[l]
+                    x = synth.hidden_vector(2, s, l)
+                    ref, rids, _, logits = orc.moe_ffn_token(lay, x)
+                    ok, exact = routing_ok(ids[l], logits, lay.top_k)
+                    assert ok, (s, l, ids[l], rids)
+                    if not exact:
+                        ref, _, _, _ = orc.moe_ffn_token(lay, x, ids=ids[l])
+                    err = rel_l2(y[l], ref)
+                    say(f"  step {s} layer {l}: rel_l2 {err:.2e}")
+                    assert err <= REL_L2_TOL and err <= 1e-5
+    assert digests[:3] == digests[3:]

@@ -181,7 +181,7 @@ def lm_head(seed: int = 4, rows: int = VOCAB, hidden: int = HIDDEN):
 def fnv1a64(values) -> int:
     """64-bit FNV-1a over the little-endian bytes of an int32 array (a determinism digest)."""
     h = 0xCBF29CE484222325
-    for byte in np.ascontiguousarray(np.asarray(values, dtype=np.int32)).view(np.uint8).tolist():
+    for byte in np.ascontiguousarray(np.asarray(values, dtype=np.int32).ravel()).view(np.uint8).tolist():
         h ^= byte
         h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
     return h

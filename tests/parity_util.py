@@ -22,6 +22,28 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
+# bfloat16 keeps 8 significant bits: rounding alone moves a value by up to 2^-8 of itself.
+BF16_HALF_ULP_REL = 2.0 ** -8
+
+
+def bf16_bits_of_f32(t) -> np.ndarray:
+    """Round-to-nearest-even of float32 values to bfloat16 bit patterns (finite inputs)."""
+    u = np.ascontiguousarray(t.detach().cpu().numpy().astype(np.float32)).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def bf16_bits(t) -> np.ndarray:
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_bf16_output(got_bf16, got_f32, ref) -> None:
+    """A bf16 output must be exactly the rounding of the same call's fp32 output, and lie
+    within bfloat16's own rounding bound of the oracle."""
+    np.testing.assert_array_equal(bf16_bits(got_bf16), bf16_bits_of_f32(got_f32))
+    assert rel_l2(to_f64(got_bf16), ref) <= BF16_HALF_ULP_REL
+
+
 def to_f64(t) -> np.ndarray:
     """A torch tensor (float32 or bfloat16, any device) -> float64 numpy (exact)."""
     import torch

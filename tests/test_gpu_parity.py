@@ -12,7 +12,7 @@ import torch
 
 from oracle import q4moe_oracle as orc
 from quantized_moe_decode_affine_amd import synth
-from tests.parity_util import REL_L2_TOL, TIE_BAND, rel_l2, routing_ok, say, to_f64
+from tests.parity_util import REL_L2_TOL, TIE_BAND, check_bf16_output, rel_l2, routing_ok, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -68,18 +68,18 @@ def test_gemv_one_hot_columns_exact(B):
 
 @pytest.mark.parametrize("n,k,seed", [(512, 2048, 0), (1, 64, 1), (3, 128, 2), (777, 192, 3), (1000, 4096, 4),
                                       (64, 16384, 5), (257, 512, 6)])
-@pytest.mark.parametrize("out_dtype", [0, 1])
-def test_gemv_parity(B, n, k, seed, out_dtype):
-    say(f"gemv n={n} k={k} out={out_dtype}")
+def test_gemv_parity(B, n, k, seed):
+    say(f"gemv n={n} k={k}")
     mat = synth.q4_matrix(seed, 0, 0, 0, n, k)
     xb = synth.hidden_vector(seed, 0, 0, k)
-    y = B.q4_gemv(_q4(B, mat), B.bf16_tensor(xb), out_dtype)
+    W, x = _q4(B, mat), B.bf16_tensor(xb)
+    y = B.q4_gemv(W, x, 0)
+    yb = B.q4_gemv(W, x, 1)
     _sync()
     ref = orc.q4_gemv(*mat, xb)
     err = rel_l2(to_f64(y), ref)
-    assert err <= REL_L2_TOL
-    if out_dtype == 0:
-        assert err <= 1e-5
+    assert err <= REL_L2_TOL and err <= 1e-5
+    check_bf16_output(yb, y, ref)
 
 
 # ---------------------------------------------------------------- LM head --
@@ -202,30 +202,32 @@ def test_permute_skewed(B):
 
 @pytest.mark.parametrize("m,n,k,seed", [(1, 32, 64, 0), (300, 777, 640, 1), (128, 256, 2048, 2),
                                         (2048, 512, 2048, 3), (129, 2048, 512, 4), (40, 100, 192, 5)])
-@pytest.mark.parametrize("out_dtype", [0, 1])
-def test_gemm_parity(B, m, n, k, seed, out_dtype):
-    say(f"gemm m={m} n={n} k={k} out={out_dtype}")
+def test_gemm_parity(B, m, n, k, seed):
+    say(f"gemm m={m} n={n} k={k}")
     mat = synth.q4_matrix(70 + seed, 0, 0, 0, n, k)
     X = synth.token_rows(70 + seed, m, k)
-    Y = B.q4_gemm(_q4(B, mat), B.bf16_tensor(X), out_dtype)
+    W, Xd = _q4(B, mat), B.bf16_tensor(X)
+    Y = B.q4_gemm(W, Xd, 0)
+    Yb = B.q4_gemm(W, Xd, 1)
     _sync()
     ref = orc.q4_gemm(*mat, X)
-    err = rel_l2(to_f64(Y), ref)
-    assert err <= REL_L2_TOL
-    if out_dtype == 0:
-        assert err <= 1e-5
-        # row by row as well: no row may be off (a wrong tile would hide in the global norm)
-        got = to_f64(Y)
-        for r in range(0, m, max(1, m // 17)):
-            assert rel_l2(got[r], ref[r]) <= 1e-4
+    got = to_f64(Y)
+    err = rel_l2(got, ref)
+    assert err <= REL_L2_TOL and err <= 1e-5
+    # row by row as well: no row may be off (a wrong tile would hide in the global norm)
+    for r in range(0, m, max(1, m // 17)):
+        assert rel_l2(got[r], ref[r]) <= 1e-4
+    check_bf16_output(Yb, Y, ref)
 
 
 # ------------------------------------------------------------ MoE decode --
 
-def _decode_check(B, layer, dl, x_bits, out_dtype=0, tol=None):
+def _decode_check(B, layer, dl, x_bits, with_bf16=False):
     ids = torch.empty(layer.top_k, dtype=torch.int32, device=DEV)
     w = torch.empty(layer.top_k, dtype=torch.float32, device=DEV)
-    y = B.moe_ffn_decode(dl, B.bf16_tensor(x_bits), out_dtype, ids_out=ids, w_out=w)
+    xd = B.bf16_tensor(x_bits)
+    y = B.moe_ffn_decode(dl, xd, 0, ids_out=ids, w_out=w)
+    yb = B.moe_ffn_decode(dl, xd, 1) if with_bf16 else None
     _sync()
     gids = ids.cpu().numpy()
     ref, rids, rw, logits = orc.moe_ffn_token(layer, x_bits)
@@ -235,7 +237,9 @@ def _decode_check(B, layer, dl, x_bits, out_dtype=0, tol=None):
         ref, _, rw, _ = orc.moe_ffn_token(layer, x_bits, ids=gids)
     np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-4, atol=1e-6)
     err = rel_l2(to_f64(y), ref)
-    assert err <= (tol if tol is not None else REL_L2_TOL), err
+    assert err <= REL_L2_TOL, err
+    if with_bf16:
+        check_bf16_output(yb, y, ref)
     return err, exact
 
 
@@ -247,10 +251,9 @@ def test_decode_small(B, H, I, E, k, shared):
     layer = synth.moe_layer(80, 0, H, I, E, k, shared=shared)
     dl = B.DeviceLayer(layer)
     for step in range(3):
-        for out_dtype in (0, 1):
-            x = synth.hidden_vector(80, step, 0, H)
-            err, _ = _decode_check(B, layer, dl, x, out_dtype)
-            assert err <= (1e-5 if out_dtype == 0 else REL_L2_TOL)
+        x = synth.hidden_vector(80, step, 0, H)
+        err, _ = _decode_check(B, layer, dl, x, with_bf16=True)
+        assert err <= 1e-5
 
 
 def test_decode_config1(B):
@@ -269,10 +272,12 @@ def test_decode_config1(B):
 
 # ----------------------------------------------------------- MoE prefill --
 
-def _prefill_check(B, layer, dl, X, out_dtype=0):
+def _prefill_check(B, layer, dl, X, with_bf16=True):
     """Whole-chunk comparison; tokens whose routing differs within the tie band are
     evaluated by the oracle on the GPU's expert choice."""
-    Y = B.moe_ffn_prefill(dl, B.bf16_tensor(X), out_dtype)
+    Xd = B.bf16_tensor(X)
+    Y = B.moe_ffn_prefill(dl, Xd, 0)
+    Yb = B.moe_ffn_prefill(dl, Xd, 1) if with_bf16 else None
     ids, _ = B.moe_route_topk(dl.router, B.bf16_tensor(X), layer.top_k)
     _sync()
     got = to_f64(Y)
@@ -287,6 +292,8 @@ def _prefill_check(B, layer, dl, X, out_dtype=0):
             use[t] = gids[t]
     ref, _, _, _ = orc.moe_ffn_prefill(layer, X, ids=use)
     worst = max(rel_l2(got[t], ref[t]) for t in range(X.shape[0]))
+    if with_bf16:
+        check_bf16_output(Yb, Y, ref)
     return rel_l2(got, ref), worst
 
 

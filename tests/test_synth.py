@@ -45,3 +45,5 @@ def test_fnv1a64_known_values():
     for _ in range(4):
         h = ((h ^ 0) * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
     assert synth.fnv1a64(np.array([0], dtype=np.int32)) == h
+    a = np.arange(12, dtype=np.int32).reshape(3, 4)
+    assert synth.fnv1a64(a) == synth.fnv1a64(a.ravel())

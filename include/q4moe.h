@@ -138,7 +138,14 @@ int moe_permute(const int32_t* ids, int64_t T, int32_t top_k, int32_t n_experts,
  *   y = sum_i w_i down_{e_i}(silu(gate_{e_i} x) * up_{e_i} x) + shared(x)
  * with (e_i, w_i) from the router as in moe_route_topk.  x bf16 [hidden]; y fp32
  * or bf16 [hidden].  ids_out int32 [top_k] and w_out fp32 [top_k] may be null.
- * Intermediates stay fp32.  Needs Q4MOE_OP_FFN_DECODE workspace.
+ * Intermediates stay fp32.  Runs as one launch of one workgroup per compute
+ * unit; values passed between workgroups carry a per-launch tag kept in the
+ * workspace, so the Q4MOE_OP_FFN_DECODE workspace must be zero-filled before
+ * its first use and must stay with one device; each call leaves it ready for
+ * the next.  Calls that share a workspace must not overlap.  Every wait inside
+ * the kernel is bounded (about a quarter second): if one ever gives up, the
+ * result is wrong and the 32-bit word at byte offset 2048 of the workspace is
+ * incremented (it stays 0 in correct use).
  */
 int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int out_dtype,
                    int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,

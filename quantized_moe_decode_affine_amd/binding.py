@@ -162,8 +162,11 @@ def workspace_bytes(op: int, layer: Optional[DeviceLayer] = None, W: Optional[De
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A device byte buffer (torch's allocator returns 256-byte aligned blocks)."""
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """A zero-filled device byte buffer (torch's allocator returns 256-byte aligned blocks).
+
+    Zero-filled because the decode workspace holds a grid-barrier state that must
+    be zero before its first use; the other operations do not care."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def _out(shape, out_dtype, device, out=None):

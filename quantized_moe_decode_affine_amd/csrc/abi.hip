@@ -81,11 +81,6 @@ int layer_check(const q4moe_layer* L, q4moe::DecodeLayer* d) {
   return Q4MOE_OK;
 }
 
-size_t decode_lds_c(const q4moe::DecodeLayer& d) {
-  const int nslot = d.top_k + (d.has_shared ? 1 : 0);
-  return (size_t)nslot * (d.inter / 32) * (36 * 4 + 4);
-}
-
 int hip_status(hipError_t e) { return e == hipSuccess ? Q4MOE_OK : Q4MOE_EHIP; }
 
 size_t lmhead_ws(int64_t rows, int64_t k, int64_t B) {
@@ -207,7 +202,7 @@ int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int o
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!x || !aligned(x, 16) || !out_ok(y, out_dtype)) return Q4MOE_EINVAL;
-    if (decode_lds_c(d) > kMaxDynLds) return Q4MOE_EUNSUPPORTED;
+    if (q4moe::decode_lds_bytes(d) > kMaxDynLds) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_workspace_bytes(d.hidden, d.inter, d.n_experts, d.top_k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
     return hip_status(q4moe::run_moe_ffn_decode(d, x, y, out_dtype == Q4MOE_OUT_BF16, ids_out, w_out, workspace,

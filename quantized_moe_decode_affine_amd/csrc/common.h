@@ -75,20 +75,68 @@ __device__ __forceinline__ uint4 permute_block(uint4 v) {
   return r;
 }
 
-// Butterfly sum over groups of W consecutive lanes (W a power of two <= 64);
-// every lane of a group ends with the group's total.
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m, kWave);
+// ---- cross-lane steps without LDS traffic: DPP inside 16-lane rows, the gfx950
+// permlane swaps across rows and halves.
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Exchange across the two 16-lane rows of each 32-lane half (row r <-> r^1) and
+// across the two 32-lane halves.  Each swap returns the pair {own, other} in an
+// order that depends on the lane, so callers combine the pair symmetrically
+// (sum, max).
+__device__ __forceinline__ void swap_rows16(uint32_t v, uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap_halves32(uint32_t v, uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// Sum over aligned groups of 2^lshift consecutive lanes (lshift 0..6, uniform);
+// every lane of a group ends with the group total.  The mirror steps are sums
+// once both mirrored halves already hold equal partial totals.
+__device__ __forceinline__ float group_sum_rt(float v, int lshift) {
+  if (lshift >= 1) v += dpp_f32<kDppQuadXor1>(v);
+  if (lshift >= 2) v += dpp_f32<kDppQuadXor2>(v);
+  if (lshift >= 3) v += dpp_f32<kDppRowHalfMirror>(v);
+  if (lshift >= 4) v += dpp_f32<kDppRowMirror>(v);
+  uint32_t a, b;
+  if (lshift >= 5) { swap_rows16(__float_as_uint(v), a, b); v = __uint_as_float(a) + __uint_as_float(b); }
+  if (lshift >= 6) { swap_halves32(__float_as_uint(v), a, b); v = __uint_as_float(a) + __uint_as_float(b); }
   return v;
 }
 
 template <int W>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+__device__ __forceinline__ float group_sum(float v) {
+  constexpr int sh = W >= 64 ? 6 : W >= 32 ? 5 : W >= 16 ? 4 : W >= 8 ? 3 : W >= 4 ? 2 : W >= 2 ? 1 : 0;
+  return group_sum_rt(v, sh);
+}
+
+// Maximum over the whole wave (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuadXor1>(v));
+  v = max(v, dpp_u32<kDppQuadXor2>(v));
+  v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = max(v, dpp_u32<kDppRowMirror>(v));
+  uint32_t a, b;
+  swap_rows16(v, a, b);
+  v = max(a, b);
+  swap_halves32(v, a, b);
+  return max(a, b);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -99,7 +147,64 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// ---- device-coherent data exchange between workgroups of one grid.
+// The XCDs' L2 caches are not coherent with each other.  Values handed from one
+// workgroup to another inside a kernel are stored and loaded with agent-scope
+// atomics (write-through / L2-bypassing accesses), so no L2 writeback or
+// invalidation of the whole cache is needed to publish or observe them.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Grid-wide barrier over `nblocks` co-resident workgroups.  State {count, gen}
+// lives in caller memory that is zero when first used; count returns to zero
+// after every barrier.  Every thread first waits for its own outstanding
+// stores, so agent-scope stores issued before the barrier are visible after it.
+struct GridBarrier {
+  unsigned count;
+  unsigned gen;
+  unsigned timeouts;  // waits abandoned after kBarrierSpinLimit polls (a misuse: should stay 0)
+};
+
+// Each poll is a device-coherent load (about a microsecond), so this bounds a
+// wait to roughly a quarter of a second; a corrupted barrier state then costs a
+// wrong result and a recorded timeout, not a hang.
+constexpr unsigned kBarrierSpinLimit = 1u << 18;
+
+__device__ __forceinline__ void grid_barrier(GridBarrier* bar, unsigned nblocks) {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned g = __hip_atomic_load(&bar->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmem();  // the generation is read before this workgroup is counted
+    const unsigned arrived = __hip_atomic_fetch_add(&bar->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrived == nblocks - 1) {
+      __hip_atomic_store(&bar->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_vmem();  // the reset lands before the release
+      __hip_atomic_fetch_add(&bar->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      unsigned spins = 0;
+      while (__hip_atomic_load(&bar->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == kBarrierSpinLimit) {
+          __hip_atomic_fetch_add(&bar->timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    wait_vmem();
+  }
+  __syncthreads();
+}
 
 }  // namespace q4moe

@@ -36,6 +36,7 @@ struct DecodeLayer {
   Q4Mat sh_gate, sh_up, sh_down;         // shared (count 1) when has_shared
 };
 size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k);
+size_t decode_lds_bytes(const DecodeLayer& L);
 hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_bf16, int32_t* ids_out,
                               float* w_out, void* ws, hipStream_t stream);
 

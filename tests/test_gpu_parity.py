@@ -222,12 +222,12 @@ def test_gemm_parity(B, m, n, k, seed):
 
 # ------------------------------------------------------------ MoE decode --
 
-def _decode_check(B, layer, dl, x_bits, with_bf16=False):
+def _decode_check(B, layer, dl, x_bits, with_bf16=False, ws=None):
     ids = torch.empty(layer.top_k, dtype=torch.int32, device=DEV)
     w = torch.empty(layer.top_k, dtype=torch.float32, device=DEV)
     xd = B.bf16_tensor(x_bits)
-    y = B.moe_ffn_decode(dl, xd, 0, ids_out=ids, w_out=w)
-    yb = B.moe_ffn_decode(dl, xd, 1) if with_bf16 else None
+    y = B.moe_ffn_decode(dl, xd, 0, ids_out=ids, w_out=w, ws=ws)
+    yb = B.moe_ffn_decode(dl, xd, 1, ws=ws) if with_bf16 else None
     _sync()
     gids = ids.cpu().numpy()
     ref, rids, rw, logits = orc.moe_ffn_token(layer, x_bits)
@@ -245,7 +245,7 @@ def _decode_check(B, layer, dl, x_bits, with_bf16=False):
 
 @pytest.mark.parametrize("H,I,E,k,shared", [(128, 64, 8, 2, True), (384, 192, 16, 4, True),
                                             (256, 128, 32, 8, False), (2048, 512, 64, 8, True),
-                                            (64, 64, 1, 1, True)])
+                                            (64, 64, 1, 1, True), (4096, 2048, 16, 4, True)])
 def test_decode_small(B, H, I, E, k, shared):
     say(f"decode H={H} I={I} E={E} k={k} shared={shared}")
     layer = synth.moe_layer(80, 0, H, I, E, k, shared=shared)
@@ -257,17 +257,20 @@ def test_decode_small(B, H, I, E, k, shared):
 
 
 def test_decode_config1(B):
-    """One MoE layer at decode: hidden 2048, 256 experts + 1 shared, top-8."""
+    """One MoE layer at decode: hidden 2048, 256 experts + 1 shared, top-8, one reused workspace."""
     say("decode full layer: generating")
     layer = synth.moe_layer(1)
     dl = B.DeviceLayer(layer)
+    ws = B.workspace(B.workspace_bytes(B.OP_FFN_DECODE, dl))
     n_exact = 0
     for step in range(8):
         say(f"decode full layer step {step}")
-        err, exact = _decode_check(B, layer, dl, synth.hidden_vector(1, step, 0))
+        err, exact = _decode_check(B, layer, dl, synth.hidden_vector(1, step, 0), ws=ws)
         assert err <= 1e-5
         n_exact += exact
     assert n_exact >= 6
+    # no abandoned waits inside the kernel (the counter at byte offset 2048 of the workspace)
+    assert int(ws[2048:2052].cpu().view(torch.int32)[0]) == 0
 
 
 # ----------------------------------------------------------- MoE prefill --

@@ -25,6 +25,8 @@ CFLAGS = [
     "-Wno-unused-command-line-argument",
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs (the per-group scale fold reads them with VALU ops)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

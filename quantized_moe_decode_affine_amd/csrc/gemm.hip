@@ -29,9 +29,9 @@ namespace q4moe {
 
 namespace {
 
-constexpr int BM = 128;          // rows per tile
+constexpr int BM = 96;           // rows per tile (3 MFMA row blocks; experts hold ~40-90 rows)
+constexpr int MB = BM / 32;
 constexpr int BN = 256;          // output columns per tile (store/scale)
-constexpr int A_ROW_BYTES = 144; // 128 bytes of one row's group + 16 bytes pad
 constexpr int kXcd = 8;
 
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SCALE = 2 };
@@ -69,8 +69,26 @@ __device__ __forceinline__ uint4 codes_to_operand(uint32_t w) {
   return make_uint4(nib_pair(w, 0), nib_pair(w, 4), nib_pair(w, 8), nib_pair(w, 12));
 }
 
-__global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
-  __shared__ __align__(16) uint8_t s_a[2][BM * A_ROW_BYTES];
+// s_waitcnt immediate for "at most n vector-memory ops outstanding" (gfx9 encoding,
+// expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Pipeline depth (K groups in flight) and per-stage vector-memory ops per thread:
+// MB A-tile LDS loads, 2 B-code LDS loads, 2 scale loads.
+constexpr int kStages = 3;
+constexpr int kOpsPerStage = MB + 4;
+constexpr int A_STAGE_BYTES = BM * 128;           // BM rows x one 64-column group of bf16
+constexpr int B_STAGE_BYTES = 4 * 2 * 64 * 16;    // 4 waves x 2 column blocks x 64 lanes x 16 bytes
+
+// Swizzled slot of (row r, 16-byte word w) in an A stage: the words of a row
+// are XOR-rotated by the row's low bits so that 8 consecutive rows reading the
+// same word hit 8 different LDS bank groups.
+__device__ __forceinline__ int a_slot(int r, int w) { return r * 8 + (w ^ (r & 7)); }
+
+__global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* s_a = smem;                                   // [kStages][A_STAGE_BYTES]
+  uint8_t* s_b = smem + kStages * A_STAGE_BYTES;         // [kStages][B_STAGE_BYTES]
   __shared__ int32_t s_src[BM];
   __shared__ int64_t s_row0;
   __shared__ int32_t s_rows, s_seg;
@@ -112,7 +130,7 @@ __global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
   const int64_t row0 = s_row0;
   const int rows = s_rows;
 
-  // ---- source row of each tile row (clamped to a valid row for padding rows)
+  // ---- source row of each tile row (padding rows repeat the last real row; their outputs are dropped)
   for (int r = threadIdx.x; r < BM; r += blockDim.x) {
     const int64_t pos = row0 + min(r, rows - 1);
     int64_t src = pos;
@@ -131,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
   const int64_t oc = seg >= 0 ? seg * p.w_codes_stride : 0;
   const int64_t og = seg >= 0 ? seg * p.w_groups_stride : 0;
   int col[2];
-  const uint32_t* bcodes[2];
+  const uint4* bcodes[2];
   const uint16_t* bscale[2];
   const uint16_t* bbias[2];
 #pragma unroll
@@ -139,92 +157,89 @@ __global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
     col[nb] = swiglu ? slice * 128 + wave * 32 + ln : slice * BN + wave * 64 + nb * 32 + ln;
     const int64_t wrow = min(col[nb], p.N - 1);
     const Q4Mat& Mx = nb == 0 ? M0 : M1;
-    bcodes[nb] = Mx.codes + oc + wrow * (p.K >> 3);
+    bcodes[nb] = reinterpret_cast<const uint4*>(Mx.codes + oc + wrow * (p.K >> 3)) + lh;
     bscale[nb] = Mx.scales + og + wrow * p.G;
     bbias[nb] = Mx.biases + og + wrow * p.G;
   }
-
-  // ---- A staging: thread -> (row, half group)
-  const int a_row = threadIdx.x >> 1, a_half = threadIdx.x & 1;
   __syncthreads();  // s_src ready
-  const uint4* a_src = reinterpret_cast<const uint4*>(p.A + (int64_t)s_src[a_row] * p.K) + a_half * 4;
-  const bool a_live = a_row < rows;
-  auto load_a = [&](int g, uint4 (&ra)[4]) {
+
+  // ---- A-tile loads of this thread: MB instructions, rows (wave*MB+i)*8 + lane/8, swizzled word
+  const uint16_t* a_ptr[MB];
+  int a_word[MB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ra[j] = a_live ? a_src[g * 8 + j] : make_uint4(0, 0, 0, 0);
-  };
-  auto store_a = [&](int buf, const uint4 (&ra)[4]) {
-    uint8_t* dst = s_a[buf] + a_row * A_ROW_BYTES + a_half * 64;
+  for (int i = 0; i < MB; ++i) {
+    const int r = (wave * MB + i) * 8 + (lane >> 3);
+    a_word[i] = (lane & 7) ^ (r & 7);
+    a_ptr[i] = p.A + (int64_t)s_src[r] * p.K + a_word[i] * 8;
+  }
+
+  // Issue all loads of K group g into stage `st` (groups past the end repeat the last one).
+  auto issue = [&](int g, int st, uint32_t (&sc)[2]) {
+    g = min(g, p.G - 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(dst + 16 * j) = permute_block(ra[j]);
-  };
-  auto load_b = [&](int g, uint4 (&rb)[2], uint32_t (&sc)[2]) {
+    for (int i = 0; i < MB; ++i)
+      __builtin_amdgcn_global_load_lds(a_ptr[i] + g * 64, s_a + st * A_STAGE_BYTES + (wave * MB + i) * 1024, 16, 0, 0);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      rb[nb] = reinterpret_cast<const uint4*>(bcodes[nb])[2 * g + lh];
-      sc[nb] = bscale[nb][g];
-    }
+    for (int nb = 0; nb < 2; ++nb)
+      __builtin_amdgcn_global_load_lds(bcodes[nb] + 2 * g, s_b + st * B_STAGE_BYTES + (wave * 2 + nb) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) sc[nb] = bscale[nb][g];
   };
 
   const int mblocks = (rows + 31) >> 5;  // active 32-row blocks (wave-uniform)
   const f32x16_t zero16 = {};
-  f32x16_t acc[4][2];
+  f32x16_t acc[MB][2];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16;
 
-  uint4 ra[4];
-  uint4 rb[2], rb_next[2];
-  uint32_t sc[2], sc_next[2];
-  load_a(0, ra);
-  load_b(0, rb, sc);
-  store_a(0, ra);
-  __syncthreads();
+  uint32_t sc[kStages][2];
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st) issue(st, st, sc[st]);
 
-  for (int g = 0; g < p.G; ++g) {
-    const int buf = g & 1;
-    const bool more = g + 1 < p.G;
-    if (more) {
-      load_a(g + 1, ra);
-      load_b(g + 1, rb_next, sc_next);
-    }
-    f32x16_t part[4][2];
+  for (int g0 = 0; g0 < p.G; g0 += kStages) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t bop[2];
+    for (int st = 0; st < kStages; ++st) {
+      const int g = g0 + st;
+      if (g < p.G) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOpsPerStage * (kStages - 2)));  // group g has landed
+        __syncthreads();                                                    // ... for every wave
+        issue(g + kStages - 1, (st + kStages - 1) % kStages, sc[(st + kStages - 1) % kStages]);
+
+        const uint8_t* sa = s_a + st * A_STAGE_BYTES;
+        const uint8_t* sb = s_b + st * B_STAGE_BYTES + wave * 2 * 1024 + lane * 16;
+        const uint4 rb0 = *reinterpret_cast<const uint4*>(sb);
+        const uint4 rb1 = *reinterpret_cast<const uint4*>(sb + 1024);
+        bf16x8_t bop[2][4];  // this group's B operands, converted once, used by every row block
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const uint32_t w = s == 0 ? rb[nb].x : s == 1 ? rb[nb].y : s == 2 ? rb[nb].z : rb[nb].w;
-        bop[nb] = as_bf16x8(codes_to_operand(w));
-      }
+        for (int s4 = 0; s4 < 4; ++s4) {
+          bop[0][s4] = as_bf16x8(codes_to_operand(s4 == 0 ? rb0.x : s4 == 1 ? rb0.y : s4 == 2 ? rb0.z : rb0.w));
+          bop[1][s4] = as_bf16x8(codes_to_operand(s4 == 0 ? rb1.x : s4 == 1 ? rb1.y : s4 == 2 ? rb1.z : rb1.w));
+        }
+        const float scale0 = bf16_bits_to_f32(sc[st][0]), scale1 = bf16_bits_to_f32(sc[st][1]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        if (mb < mblocks) {
-          const uint4 av = *reinterpret_cast<const uint4*>(s_a[buf] + (mb * 32 + ln) * A_ROW_BYTES + (4 * lh + s) * 16);
+        for (int mb = 0; mb < MB; ++mb) {
+          if (mb < mblocks) {
+            // two independent chains (one per column block) over the group's 4 K-steps, then the fold
+            f32x16_t p0 = zero16, p1 = zero16;
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            part[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), bop[nb],
-                                                                   s == 0 ? zero16 : part[mb][nb], 0, 0, 0);
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const uint4 av = *reinterpret_cast<const uint4*>(sa + a_slot(mb * 32 + ln, 4 * lh + s4) * 16);
+              p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), bop[0][s4], p0, 0, 0, 0);
+              p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), bop[1][s4], p1, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              acc[mb][0][i] = fmaf(scale0, p0[i], acc[mb][0][i]);
+              acc[mb][1][i] = fmaf(scale1, p1[i], acc[mb][1][i]);
+            }
+          }
         }
       }
     }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float scale = bf16_bits_to_f32(sc[nb]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        if (mb < mblocks)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[mb][nb][i] = fmaf(scale, part[mb][nb][i], acc[mb][nb][i]);
-    }
-    if (more) {
-      store_a(buf ^ 1, ra);
-      rb[0] = rb_next[0]; rb[1] = rb_next[1];
-      sc[0] = sc_next[0]; sc[1] = sc_next[1];
-    }
-    __syncthreads();
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing (unused) loads before LDS is released
 
   // ---- offset/bias term: sum_g (bias - 128 scale)[n][g] * rowsum_g[m], on MFMA with exact bf16 parts
   for (int t = 0; t * 16 < p.Gp; ++t) {
@@ -245,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
       bc[nb][1] = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16);
     }
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       if (mb >= mblocks) continue;
       const uint16_t* xr = p.xs + (int64_t)s_src[mb * 32 + ln] * 3 * p.Gp + gbase;
 #pragma unroll
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
 
   // ---- epilogue.  D layout: column = lane % 32, row = 8*(i/4) + 4*(lane/32) + i%4.
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     if (mb >= mblocks) continue;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -271,8 +286,11 @@ __global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
       const int64_t pos = row0 + r;
       if (swiglu) {
         if (col[0] < p.N) {
+          // activations are written in the permuted 8-column order the next GEMM's A operand uses
+          const int c = col[0], j = c & 7;
+          const int pc = (c & ~7) | (j < 4 ? 2 * j : 2 * (j - 4) + 1);
           const float a = silu(acc[mb][0][i]) * acc[mb][1][i];
-          reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + col[0]] = (uint16_t)f32_to_bf16_bits(a);
+          reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + pc] = (uint16_t)f32_to_bf16_bits(a);
         }
       } else {
         float wgt = 1.0f;
@@ -292,9 +310,11 @@ __global__ __launch_bounds__(256, 1) void grouped_q4_gemm_kernel(GemmParams p) {
 }
 
 // Per-row, per-64-column-group sums of a bf16 matrix, split exactly into three
-// bfloat16 parts: out[r][part][g] (groups padded with zeros to Gp).
-__global__ void row_group_sums_kernel(const uint16_t* __restrict__ A, int64_t rows, int K, int Gp,
-                                      uint16_t* __restrict__ out) {
+// bfloat16 parts: sums[r][part][g] (groups padded with zeros to Gp).  When `ap`
+// is given, also writes the rows with each 8-column block permuted into the
+// (x0,x4),(x1,x5),(x2,x6),(x3,x7) pair order the MFMA A operand uses.
+__global__ void prep_rows_kernel(const uint16_t* __restrict__ A, int64_t rows, int K, int Gp,
+                                 uint16_t* __restrict__ sums, uint16_t* __restrict__ ap) {
   const int G = K >> 6;
   const int64_t total = rows * Gp;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -303,6 +323,7 @@ __global__ void row_group_sums_kernel(const uint16_t* __restrict__ A, int64_t ro
     float s = 0.f;
     if (g < G) {
       const uint4* src = reinterpret_cast<const uint4*>(A + r * K + g * 64);
+      uint4* dst = ap ? reinterpret_cast<uint4*>(ap + r * K + g * 64) : nullptr;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint4 v = src[j];
@@ -310,13 +331,14 @@ __global__ void row_group_sums_kernel(const uint16_t* __restrict__ A, int64_t ro
              (bf16_bits_to_f32(v.y & 0xFFFFu) + bf16_bits_to_f32(v.y >> 16)) +
              (bf16_bits_to_f32(v.z & 0xFFFFu) + bf16_bits_to_f32(v.z >> 16)) +
              (bf16_bits_to_f32(v.w & 0xFFFFu) + bf16_bits_to_f32(v.w >> 16));
+        if (dst) dst[j] = permute_block(v);
       }
     }
     const uint32_t h = f32_to_bf16_bits(s);
     const float r1 = s - bf16_bits_to_f32(h);
     const uint32_t m = f32_to_bf16_bits(r1);
     const uint32_t l = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));
-    uint16_t* o = out + r * 3 * Gp + g;
+    uint16_t* o = sums + r * 3 * Gp + g;
     o[0] = (uint16_t)h;
     o[Gp] = (uint16_t)m;
     o[2 * Gp] = (uint16_t)l;
@@ -356,31 +378,45 @@ int grid_for(int64_t n, int block) {
 
 int pad16(int g) { return (g + 15) & ~15; }
 
+constexpr size_t kGemmLds = (size_t)kStages * (A_STAGE_BYTES + B_STAGE_BYTES);
+
 hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_q4_gemm_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   const int64_t tiles_rounded = (max_tiles + kXcd - 1) / kXcd * kXcd;
   const int64_t blocks = tiles_rounded * p.n_slices;
-  hipLaunchKernelGGL(grouped_q4_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(grouped_q4_gemm_kernel, dim3((unsigned)blocks), dim3(256), kGemmLds, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_row_sums(const uint16_t* A, int64_t rows, int K, uint16_t* out, hipStream_t stream) {
+// Row sums (and, with ap, the permuted copy) of `rows` bf16 rows of length K.
+hipError_t launch_prep_rows(const uint16_t* A, int64_t rows, int K, uint16_t* sums, uint16_t* ap,
+                            hipStream_t stream) {
   const int Gp = pad16(K >> 6);
-  hipLaunchKernelGGL(row_group_sums_kernel, dim3(grid_for(rows * Gp, 256)), dim3(256), 0, stream, A, rows, K, Gp,
-                     out);
+  hipLaunchKernelGGL(prep_rows_kernel, dim3(grid_for(rows * Gp, 256)), dim3(256), 0, stream, A, rows, K, Gp, sums,
+                     ap);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t m, int k) { return align256((size_t)m * 3 * pad16(k / 64) * 2); }
+size_t gemm_workspace_bytes(int64_t m, int k) {
+  return align256((size_t)m * 3 * pad16(k / 64) * 2) + align256((size_t)m * k * 2);
+}
 
 hipError_t run_q4_gemm(const Q4Mat& W, int64_t n, int k, const uint16_t* X, int64_t m, void* Y, int out_bf16,
                        void* ws, hipStream_t stream) {
   uint16_t* xs = static_cast<uint16_t*>(ws);
-  hipError_t e = launch_row_sums(X, m, k, xs, stream);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align256((size_t)m * 3 * pad16(k / 64) * 2));
+  hipError_t e = launch_prep_rows(X, m, k, xs, xp, stream);
   if (e != hipSuccess) return e;
   GemmParams p{};
-  p.A = X;
+  p.A = xp;
   p.xs = xs;
   p.gather = 0;
   p.P = 0;
@@ -412,6 +448,7 @@ struct PrefillWs {
   int32_t* inv;
   void* perm_ws;
   uint16_t* xs_x;
+  uint16_t* xp;
   uint16_t* act;
   uint16_t* xs_act;
   float* ys;
@@ -433,6 +470,7 @@ PrefillWs carve(void* base, int64_t T, int H, int I, int E, int k, int has_share
   w.inv = reinterpret_cast<int32_t*>(take(P * 4));
   w.perm_ws = take(permute_workspace_bytes(P, E));
   w.xs_x = reinterpret_cast<uint16_t*>(take((size_t)T * 3 * pad16(H / 64) * 2));
+  w.xp = reinterpret_cast<uint16_t*>(take((size_t)T * H * 2));
   w.act = reinterpret_cast<uint16_t*>(take((size_t)R * I * 2));
   w.xs_act = reinterpret_cast<uint16_t*>(take((size_t)R * 3 * pad16(I / 64) * 2));
   w.ys = reinterpret_cast<float*>(take((size_t)R * H * 4));
@@ -454,7 +492,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   if (e != hipSuccess) return e;
   e = run_permute(w.ids, P, E, w.offsets, w.sorted_rows, w.inv, w.perm_ws, BM, w.tile_offsets, stream);
   if (e != hipSuccess) return e;
-  e = launch_row_sums(X, T, H, w.xs_x, stream);
+  e = launch_prep_rows(X, T, H, w.xs_x, w.xp, stream);
   if (e != hipSuccess) return e;
 
   const int64_t max_routed_tiles = (P + BM - 1) / BM + E;
@@ -462,7 +500,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
 
   // gate/up with SwiGLU -> act (bf16, sorted positions; shared rows appended)
   GemmParams p{};
-  p.A = X;
+  p.A = w.xp;
   p.xs = w.xs_x;
   p.sorted_rows = w.sorted_rows;
   p.gather = 1;
@@ -492,7 +530,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   if (e != hipSuccess) return e;
 
   const int64_t R = P + (L.has_shared ? T : 0);
-  e = launch_row_sums(w.act, R, I, w.xs_act, stream);
+  e = launch_prep_rows(w.act, R, I, w.xs_act, nullptr, stream);
   if (e != hipSuccess) return e;
 
   // down with the routing weight -> ys (fp32, sorted positions)

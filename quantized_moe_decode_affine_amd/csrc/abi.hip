@@ -188,8 +188,8 @@ int moe_permute(const int32_t* ids, int64_t T, int32_t top_k, int32_t n_experts,
     const int64_t rows = T * top_k;
     if (!workspace || workspace_bytes < q4moe::permute_workspace_bytes(rows, n_experts) || !aligned(workspace, 256))
       return Q4MOE_EWORKSPACE;
-    return hip_status(q4moe::run_permute(ids, rows, n_experts, offsets, sorted_rows, inv_rows, workspace, 0,
-                                         nullptr, (hipStream_t)stream));
+    return hip_status(q4moe::run_permute(ids, rows, n_experts, offsets, sorted_rows, inv_rows, workspace, nullptr,
+                                         (hipStream_t)stream));
   } catch (...) {
     return Q4MOE_EHIP;
   }

@@ -22,6 +22,8 @@
 // lane loads its own 16 code bytes per group for its column.  Workgroups of
 // the same row tile are placed on the same XCD so the row tile stays in that
 // XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -41,29 +43,32 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct GemmParams {
   const uint16_t* A;          // bf16 rows [*][K]
   const uint16_t* xs;         // bf16 [*][3][Gp] row group-sum parts, same row indexing as A
-  const int32_t* sorted_rows; // gather mode: positions p < P read row sorted_rows[p] / topk
-  int gather;                 // 1: gather rows as above (p >= P read row p - P); 0: row p
-  int topk;
+  const int4* tiles;          // per tile {segment (expert; -1 extra; -2 none), first position, rows, 0};
+                              // null: tile t covers positions t*BM.. of the extra segment
+  int n_tiles;                // table length (the grid may hold a few more tiles)
+  const int32_t* row_src;     // gather mode: A row (token) of each routed position; positions >= P read row pos - P
+  const float* route_w;       // scale epilogue: routing weight of each routed position
+  int gather;
   int64_t P;                  // positions of the routed segments
   int K, G, Gp;
   int N;                      // output columns (store/scale) or intermediate width (swiglu)
   Q4Mat W, W2;                // routed experts (W2 = up for swiglu), stacked
   int64_t w_codes_stride, w_groups_stride;
   Q4Mat X, X2;                // the extra segment's matrix (shared expert / single matrix)
-  int n_routed;
-  const int32_t* offsets;     // [n_routed+1]
-  const int32_t* tile_offsets;// [n_routed+1]
-  int64_t extra_rows;
-  int extra_tiles;
+  int64_t extra_rows;         // positions of the extra segment (uniform tiling when tiles is null)
   int n_slices;
   int epi;
   void* out;
   int out_bf16;
   int64_t ldo;
-  const float* route_w;       // [P] by original row (scale epilogue)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Global-address-space view of a pointer: a generic (flat) load could touch
+// LDS, so it would have to wait for every LDS DMA still in flight.
+typedef const uint16_t __attribute__((address_space(1)))* gu16_ptr;
+__device__ __forceinline__ uint32_t ld_global_u16(const uint16_t* ptr) { return *(gu16_ptr)ptr; }
 
 __device__ __forceinline__ uint4 codes_to_operand(uint32_t w) {
   return make_uint4(nib_pair(w, 0), nib_pair(w, 4), nib_pair(w, 8), nib_pair(w, 12));
@@ -72,10 +77,12 @@ __device__ __forceinline__ uint4 codes_to_operand(uint32_t w) {
 // s_waitcnt immediate for "at most n vector-memory ops outstanding" (gfx9 encoding,
 // expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// The same with lgkmcnt(0) (all of this wave's LDS reads done).
+constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xF << 8); }
 
 // Pipeline depth (K groups in flight) and per-stage vector-memory ops per thread:
 // MB A-tile LDS loads, 2 B-code LDS loads, 2 scale loads.
-constexpr int kStages = 3;
+constexpr int kStages = 3;  // the stage arrays below are written out for exactly 3
 constexpr int kOpsPerStage = MB + 4;
 constexpr int A_STAGE_BYTES = BM * 128;           // BM rows x one 64-column group of bf16
 constexpr int B_STAGE_BYTES = 4 * 2 * 64 * 16;    // 4 waves x 2 column blocks x 64 lanes x 16 bytes
@@ -86,12 +93,16 @@ constexpr int B_STAGE_BYTES = 4 * 2 * 64 * 16;    // 4 waves x 2 column blocks x
 __device__ __forceinline__ int a_slot(int r, int w) { return r * 8 + (w ^ (r & 7)); }
 
 __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* s_a = smem;                                   // [kStages][A_STAGE_BYTES]
-  uint8_t* s_b = smem + kStages * A_STAGE_BYTES;         // [kStages][B_STAGE_BYTES]
+  // One LDS array per pipeline stage: distinct variables let the compiler see
+  // that reading one stage does not depend on the DMA still filling another,
+  // so it does not wait for every outstanding load before each LDS read.
+  // (The compiler tracks only a few distinct DMA targets, so A and B of a stage share one array.)
+  __shared__ __align__(16) uint8_t s_st0[A_STAGE_BYTES + B_STAGE_BYTES], s_st1[A_STAGE_BYTES + B_STAGE_BYTES],
+      s_st2[A_STAGE_BYTES + B_STAGE_BYTES];
+  auto stage_a = [&](int st) -> uint8_t* { return st == 0 ? s_st0 : st == 1 ? s_st1 : s_st2; };
+  auto stage_b = [&](int st) -> uint8_t* { return stage_a(st) + A_STAGE_BYTES; };
   __shared__ int32_t s_src[BM];
-  __shared__ int64_t s_row0;
-  __shared__ int32_t s_rows, s_seg;
+  __shared__ float s_wgt[BM];  // routing weight of each tile row (scale epilogue)
 
   // ---- tile of this workgroup (XCD-aware: all slices of a tile share an XCD)
   const int bid = blockIdx.x;
@@ -99,43 +110,28 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
   const int q = bid / kXcd;
   const int slice = q % p.n_slices;
   const int tile = (q / p.n_slices) * kXcd + xcd;
-  if (threadIdx.x == 0) {
-    const int routed_tiles = p.n_routed ? p.tile_offsets[p.n_routed] : 0;
-    int seg = -2;
-    int64_t row0 = 0;
-    int rows = 0;
-    if (tile < routed_tiles) {
-      int lo = 0, hi = p.n_routed;  // find e with tile_offsets[e] <= tile < tile_offsets[e+1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.tile_offsets[mid] <= tile) lo = mid; else hi = mid;
-      }
-      const int mt = tile - p.tile_offsets[lo];
-      row0 = (int64_t)p.offsets[lo] + (int64_t)mt * BM;
-      rows = (int)min<int64_t>(BM, (int64_t)p.offsets[lo + 1] - row0);
-      seg = lo;
-    } else if (tile - routed_tiles < p.extra_tiles) {
-      const int mt = tile - routed_tiles;
-      row0 = p.P + (int64_t)mt * BM;
-      rows = (int)min<int64_t>(BM, p.P + p.extra_rows - row0);
-      seg = -1;
-    }
-    s_seg = seg;
-    s_row0 = row0;
-    s_rows = rows;
+  int seg, rows;
+  int64_t row0;
+  if (tile >= p.n_tiles) return;
+  if (p.tiles) {
+    const int4 ti = p.tiles[tile];
+    seg = ti.x;
+    row0 = ti.y;
+    rows = ti.z;
+  } else {
+    row0 = (int64_t)tile * BM;
+    seg = row0 < p.extra_rows ? -1 : -2;
+    rows = (int)min<int64_t>(BM, p.extra_rows - row0);
   }
-  __syncthreads();
-  const int seg = s_seg;
   if (seg == -2) return;
-  const int64_t row0 = s_row0;
-  const int rows = s_rows;
 
-  // ---- source row of each tile row (padding rows repeat the last real row; their outputs are dropped)
+  // ---- source row and routing weight of each tile row (padding rows repeat the
+  // last real row; their outputs are dropped)
   for (int r = threadIdx.x; r < BM; r += blockDim.x) {
     const int64_t pos = row0 + min(r, rows - 1);
-    int64_t src = pos;
-    if (p.gather) src = pos < p.P ? (int64_t)(p.sorted_rows[pos] / p.topk) : pos - p.P;
-    s_src[r] = (int32_t)src;
+    const bool routed = pos < p.P;
+    s_src[r] = p.gather ? (routed ? p.row_src[pos] : (int32_t)(pos - p.P)) : (int32_t)pos;
+    s_wgt[r] = p.epi == EPI_SCALE && routed ? p.route_w[pos] : 1.0f;
   }
 
   const int lane = lane_id();
@@ -178,12 +174,12 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
     g = min(g, p.G - 1);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
-      __builtin_amdgcn_global_load_lds(a_ptr[i] + g * 64, s_a + st * A_STAGE_BYTES + (wave * MB + i) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a_ptr[i] + g * 64, stage_a(st) + (wave * MB + i) * 1024, 16, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
-      __builtin_amdgcn_global_load_lds(bcodes[nb] + 2 * g, s_b + st * B_STAGE_BYTES + (wave * 2 + nb) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bcodes[nb] + 2 * g, stage_b(st) + (wave * 2 + nb) * 1024, 16, 0, 0);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) sc[nb] = bscale[nb][g];
+    for (int nb = 0; nb < 2; ++nb) sc[nb] = ld_global_u16(bscale[nb] + g);
   };
 
   const int mblocks = (rows + 31) >> 5;  // active 32-row blocks (wave-uniform)
@@ -194,51 +190,86 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16;
 
+  // Raw bf16 scale bits of the groups in flight, converted where they are used
+  // (a conversion next to the load would make the wave wait for it there).
   uint32_t sc[kStages][2];
 #pragma unroll
   for (int st = 0; st < kStages - 1; ++st) issue(st, st, sc[st]);
 
-  for (int g0 = 0; g0 < p.G; g0 += kStages) {
-#pragma unroll
-    for (int st = 0; st < kStages; ++st) {
-      const int g = g0 + st;
-      if (g < p.G) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kOpsPerStage * (kStages - 2)));  // group g has landed
-        __syncthreads();                                                    // ... for every wave
-        issue(g + kStages - 1, (st + kStages - 1) % kStages, sc[(st + kStages - 1) % kStages]);
+  // The main loop is specialised on the number of active row blocks so that a
+  // group's body has no branches: every wait the compiler adds then sits at a
+  // use of the data, not at a join right after the look-ahead loads.
+  auto main_loop = [&](auto nmb_c) __attribute__((always_inline)) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    // One K group from stage ST (a compile-time stage, so each LDS access names one array).
+    auto step = [&](int g, auto st_c) __attribute__((always_inline)) {
+      constexpr int st = decltype(st_c)::value;
+      constexpr int sn = (st + kStages - 1) % kStages;
+      // keep each group's instructions (notably the scale conversions) inside its own step
+      __builtin_amdgcn_sched_barrier(0);
+      // Group g has landed for this wave and this wave's reads of the stage about
+      // to be refilled are done; the barrier extends both to every wave.  (A
+      // workgroup fence here would also wait for the look-ahead DMA.)
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kOpsPerStage * (kStages - 2)));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
 
-        const uint8_t* sa = s_a + st * A_STAGE_BYTES;
-        const uint8_t* sb = s_b + st * B_STAGE_BYTES + wave * 2 * 1024 + lane * 16;
-        const uint4 rb0 = *reinterpret_cast<const uint4*>(sb);
-        const uint4 rb1 = *reinterpret_cast<const uint4*>(sb + 1024);
-        bf16x8_t bop[2][4];  // this group's B operands, converted once, used by every row block
+      const uint8_t* sa = stage_a(st);
+      const uint8_t* sb = stage_b(st) + wave * 2 * 1024 + lane * 16;
+      // This wave's B codes first, then A fragments double-buffered over row
+      // blocks: block 0's reads are in flight during the B conversion, block
+      // mb+1's during block mb's MFMAs.
+      uint4 af[2][4];
+      auto read_a = [&](int mb, uint4 (&dst)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          dst[s4] = *reinterpret_cast<const uint4*>(sa + a_slot(mb * 32 + ln, 4 * lh + s4) * 16);
+      };
+      const uint4 rb0 = *reinterpret_cast<const uint4*>(sb);
+      const uint4 rb1 = *reinterpret_cast<const uint4*>(sb + 1024);
+      read_a(0, af[0]);
+      issue(g + kStages - 1, sn, sc[sn]);  // the look-ahead group, after this step's LDS reads
+      bf16x8_t bop[2][4];  // this group's B operands, converted once, used by every row block
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        bop[0][s4] = as_bf16x8(codes_to_operand(s4 == 0 ? rb0.x : s4 == 1 ? rb0.y : s4 == 2 ? rb0.z : rb0.w));
+        bop[1][s4] = as_bf16x8(codes_to_operand(s4 == 0 ? rb1.x : s4 == 1 ? rb1.y : s4 == 2 ? rb1.z : rb1.w));
+      }
+      const float scale0 = bf16_bits_to_f32(sc[st][0]), scale1 = bf16_bits_to_f32(sc[st][1]);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        if (mb + 1 < NMB) read_a(mb + 1, af[(mb + 1) & 1]);
+        // two independent chains (one per column block) over the group's 4 K-steps, then the fold
+        f32x16_t p0 = zero16, p1 = zero16;
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          bop[0][s4] = as_bf16x8(codes_to_operand(s4 == 0 ? rb0.x : s4 == 1 ? rb0.y : s4 == 2 ? rb0.z : rb0.w));
-          bop[1][s4] = as_bf16x8(codes_to_operand(s4 == 0 ? rb1.x : s4 == 1 ? rb1.y : s4 == 2 ? rb1.z : rb1.w));
+          p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mb & 1][s4]), bop[0][s4], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mb & 1][s4]), bop[1][s4], p1, 0, 0, 0);
         }
-        const float scale0 = bf16_bits_to_f32(sc[st][0]), scale1 = bf16_bits_to_f32(sc[st][1]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          if (mb < mblocks) {
-            // two independent chains (one per column block) over the group's 4 K-steps, then the fold
-            f32x16_t p0 = zero16, p1 = zero16;
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-              const uint4 av = *reinterpret_cast<const uint4*>(sa + a_slot(mb * 32 + ln, 4 * lh + s4) * 16);
-              p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), bop[0][s4], p0, 0, 0, 0);
-              p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), bop[1][s4], p1, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              acc[mb][0][i] = fmaf(scale0, p0[i], acc[mb][0][i]);
-              acc[mb][1][i] = fmaf(scale1, p1[i], acc[mb][1][i]);
-            }
-          }
+        for (int i = 0; i < 16; ++i) {
+          acc[mb][0][i] = fmaf(scale0, p0[i], acc[mb][0][i]);
+          acc[mb][1][i] = fmaf(scale1, p1[i], acc[mb][1][i]);
         }
       }
+    };
+    static_assert(kStages == 3, "the steps below are written out for three stages");
+    int g0 = 0;
+    for (; g0 + kStages <= p.G; g0 += kStages) {
+      step(g0, std::integral_constant<int, 0>{});
+      step(g0 + 1, std::integral_constant<int, 1>{});
+      step(g0 + 2, std::integral_constant<int, 2>{});
     }
-  }
+    // the last G mod 3 groups
+    if (g0 < p.G) step(g0, std::integral_constant<int, 0>{});
+    if (g0 + 1 < p.G) step(g0 + 1, std::integral_constant<int, 1>{});
+  };
+  if (mblocks == 1)
+    main_loop(std::integral_constant<int, 1>{});
+  else if (mblocks == 2)
+    main_loop(std::integral_constant<int, 2>{});
+  else
+    main_loop(std::integral_constant<int, 3>{});
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing (unused) loads before LDS is released
 
   // ---- offset/bias term: sum_g (bias - 128 scale)[n][g] * rowsum_g[m], on MFMA with exact bf16 parts
@@ -250,9 +281,9 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       uint32_t hi[8], lo[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int g = gbase + j;
-        float c = 0.f;
-        if (g < p.G) c = bf16_bits_to_f32(bbias[nb][g]) - 128.0f * bf16_bits_to_f32(bscale[nb][g]);
+        const int g = min(gbase + j, p.G - 1);  // unconditional loads; padding groups get c = 0
+        float c = bf16_bits_to_f32(ld_global_u16(bbias[nb] + g)) - 128.0f * bf16_bits_to_f32(ld_global_u16(bscale[nb] + g));
+        c = gbase + j < p.G ? c : 0.f;
         hi[j] = f32_to_bf16_bits(c);
         lo[j] = f32_to_bf16_bits(c - bf16_bits_to_f32(hi[j]));
       }
@@ -293,8 +324,7 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
           reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + pc] = (uint16_t)f32_to_bf16_bits(a);
         }
       } else {
-        float wgt = 1.0f;
-        if (p.epi == EPI_SCALE && pos < p.P) wgt = p.route_w[p.sorted_rows[pos]];
+        const float wgt = s_wgt[r];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           if (col[nb] >= p.N) continue;
@@ -378,19 +408,11 @@ int grid_for(int64_t n, int block) {
 
 int pad16(int g) { return (g + 15) & ~15; }
 
-constexpr size_t kGemmLds = (size_t)kStages * (A_STAGE_BYTES + B_STAGE_BYTES);
-
 hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_q4_gemm_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  p.n_tiles = (int)max_tiles;
   const int64_t tiles_rounded = (max_tiles + kXcd - 1) / kXcd * kXcd;
   const int64_t blocks = tiles_rounded * p.n_slices;
-  hipLaunchKernelGGL(grouped_q4_gemm_kernel, dim3((unsigned)blocks), dim3(256), kGemmLds, stream, p);
+  hipLaunchKernelGGL(grouped_q4_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -426,15 +448,13 @@ hipError_t run_q4_gemm(const Q4Mat& W, int64_t n, int k, const uint16_t* X, int6
   p.N = (int)n;
   p.X = W;
   p.X2 = W;
-  p.n_routed = 0;
   p.extra_rows = m;
-  p.extra_tiles = (int)((m + BM - 1) / BM);
   p.n_slices = (int)((n + BN - 1) / BN);
   p.epi = EPI_STORE;
   p.out = Y;
   p.out_bf16 = out_bf16;
   p.ldo = n;
-  return launch_grouped(p, p.extra_tiles, stream);
+  return launch_grouped(p, (m + BM - 1) / BM, stream);
 }
 
 namespace {
@@ -443,9 +463,11 @@ struct PrefillWs {
   int32_t* ids;
   float* weights;
   int32_t* offsets;
-  int32_t* tile_offsets;
   int32_t* sorted_rows;
   int32_t* inv;
+  int4* tiles;
+  int32_t* row_src;
+  float* row_w;
   void* perm_ws;
   uint16_t* xs_x;
   uint16_t* xp;
@@ -461,13 +483,16 @@ PrefillWs carve(void* base, int64_t T, int H, int I, int E, int k, int has_share
   size_t off = 0;
   auto take = [&](size_t bytes) { char* r = c ? c + off : nullptr; off += align256(bytes); return r; };
   const int64_t P = T * k, R = P + (has_shared ? T : 0);
+  const int max_tiles = group_max_tiles(P, E, has_shared ? T : 0, BM);
   w.logits = reinterpret_cast<float*>(take(route_workspace_bytes(T, E)));
   w.ids = reinterpret_cast<int32_t*>(take(P * 4));
   w.weights = reinterpret_cast<float*>(take(P * 4));
   w.offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
-  w.tile_offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
   w.sorted_rows = reinterpret_cast<int32_t*>(take(P * 4));
   w.inv = reinterpret_cast<int32_t*>(take(P * 4));
+  w.tiles = reinterpret_cast<int4*>(take((size_t)max_tiles * 16));
+  w.row_src = reinterpret_cast<int32_t*>(take(P * 4));
+  w.row_w = reinterpret_cast<float*>(take(P * 4));
   w.perm_ws = take(permute_workspace_bytes(P, E));
   w.xs_x = reinterpret_cast<uint16_t*>(take((size_t)T * 3 * pad16(H / 64) * 2));
   w.xp = reinterpret_cast<uint16_t*>(take((size_t)T * H * 2));
@@ -488,23 +513,32 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   const int H = L.hidden, I = L.inter, E = L.n_experts, k = L.top_k;
   PrefillWs w = carve(ws, T, H, I, E, k, L.has_shared);
   const int64_t P = T * k;
+  const int64_t extra = L.has_shared ? T : 0;
+  const int max_tiles = group_max_tiles(P, E, extra, BM);
   hipError_t e = run_route_topk(L.router, E, H, X, T, k, w.ids, w.weights, w.logits, stream);
   if (e != hipSuccess) return e;
-  e = run_permute(w.ids, P, E, w.offsets, w.sorted_rows, w.inv, w.perm_ws, BM, w.tile_offsets, stream);
+  GroupTiles gt{};
+  gt.tile_rows = BM;
+  gt.max_tiles = max_tiles;
+  gt.extra_rows = extra;
+  gt.topk = k;
+  gt.weights = w.weights;
+  gt.table = w.tiles;
+  gt.row_src = w.row_src;
+  gt.row_w = w.row_w;
+  e = run_permute(w.ids, P, E, w.offsets, w.sorted_rows, w.inv, w.perm_ws, &gt, stream);
   if (e != hipSuccess) return e;
   e = launch_prep_rows(X, T, H, w.xs_x, w.xp, stream);
   if (e != hipSuccess) return e;
-
-  const int64_t max_routed_tiles = (P + BM - 1) / BM + E;
-  const int shared_tiles = L.has_shared ? (int)((T + BM - 1) / BM) : 0;
 
   // gate/up with SwiGLU -> act (bf16, sorted positions; shared rows appended)
   GemmParams p{};
   p.A = w.xp;
   p.xs = w.xs_x;
-  p.sorted_rows = w.sorted_rows;
+  p.tiles = w.tiles;
+  p.row_src = w.row_src;
+  p.route_w = w.row_w;
   p.gather = 1;
-  p.topk = k;
   p.P = P;
   p.K = H;
   p.G = H / 64;
@@ -516,20 +550,16 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   p.w_groups_stride = (int64_t)I * (H / 64);
   p.X = L.sh_gate;
   p.X2 = L.sh_up;
-  p.n_routed = E;
-  p.offsets = w.offsets;
-  p.tile_offsets = w.tile_offsets;
-  p.extra_rows = L.has_shared ? T : 0;
-  p.extra_tiles = shared_tiles;
+  p.extra_rows = extra;
   p.n_slices = (I + 127) / 128;
   p.epi = EPI_SWIGLU;
   p.out = w.act;
   p.out_bf16 = 1;
   p.ldo = I;
-  e = launch_grouped(p, max_routed_tiles + shared_tiles, stream);
+  e = launch_grouped(p, max_tiles, stream);
   if (e != hipSuccess) return e;
 
-  const int64_t R = P + (L.has_shared ? T : 0);
+  const int64_t R = P + extra;
   e = launch_prep_rows(w.act, R, I, w.xs_act, nullptr, stream);
   if (e != hipSuccess) return e;
 
@@ -553,8 +583,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   d.out = w.ys;
   d.out_bf16 = 0;
   d.ldo = H;
-  d.route_w = w.weights;
-  e = launch_grouped(d, max_routed_tiles + shared_tiles, stream);
+  e = launch_grouped(d, max_tiles, stream);
   if (e != hipSuccess) return e;
 
   hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * (H / 4), 256)), dim3(256), 0, stream, w.ys, w.inv, T, k, H,

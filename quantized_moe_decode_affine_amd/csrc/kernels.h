@@ -45,10 +45,25 @@ size_t route_workspace_bytes(int64_t T, int n_experts);
 hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* X, int64_t T, int k,
                           int32_t* ids, float* weights, void* ws, hipStream_t stream);
 size_t permute_workspace_bytes(int64_t rows, int n_experts);
-// Stable counting sort of `rows` ids by expert.  When tile_offsets is non-null,
-// it receives E+1 prefix sums of ceil(count_e / tile_rows).
+
+// Optional output of run_permute for the grouped GEMM: the sorted positions cut
+// into tiles of tile_rows rows (never crossing a segment), then extra_rows more
+// positions (the shared expert's rows, after the routed ones) cut the same way.
+struct GroupTiles {
+  int tile_rows;
+  int max_tiles;          // table length: at least rows / tile_rows + n_experts + extra tiles
+  int64_t extra_rows;
+  int topk;               // row r = t * topk + slot belongs to token t
+  const float* weights;   // routing weight of each row r (may be null: weight 1)
+  int4* table;            // [max_tiles] {segment (expert; -1 extra; -2 unused), first position, rows, 0}
+  int32_t* row_src;       // [rows] token of each sorted position
+  float* row_w;           // [rows] routing weight of each sorted position
+};
+int group_max_tiles(int64_t rows, int n_experts, int64_t extra_rows, int tile_rows);
+
+// Stable counting sort of `rows` ids by expert (tiles may be null).
 hipError_t run_permute(const int32_t* ids, int64_t rows, int n_experts, int32_t* offsets, int32_t* sorted_rows,
-                       int32_t* inv_rows, void* ws, int tile_rows, int32_t* tile_offsets, hipStream_t stream);
+                       int32_t* inv_rows, void* ws, const GroupTiles* tiles, hipStream_t stream);
 
 // ---- grouped MFMA GEMM and the prefill layer (gemm.hip)
 size_t gemm_workspace_bytes(int64_t m, int k);

@@ -12,30 +12,60 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // logits[t][e] = X[t] . router[e]: bf16 MFMA 32x32x16, fp32 accumulation.
-// Workgroup = 2x2 waves = 64 tokens x 64 experts; every lane loads its own
-// 64-byte strips of X and router per 64-column step, so both operands use the
-// same (arbitrary but consistent) order of the 64 columns inside a step.
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ router,
+// Workgroup = 32 tokens x 64 experts, 8 waves: wave w computes the 32x32 block
+// of expert half (w & 1) over K quarter (w >> 1), loading four 64-column steps
+// at a time so that each wave has eight 128-bit loads per lane in flight; the
+// quarters are summed through LDS in a fixed order.  Every lane loads its own
+// 64-byte strips of X and router per step, so both operands use the same
+// (arbitrary but consistent) order of the 64 columns inside a step.
+constexpr int kRouterBatch = 4;
+
+__global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __restrict__ router,
                                                             const uint16_t* __restrict__ X, int64_t T, int E,
                                                             int H, float* __restrict__ logits) {
+  __shared__ f32x16_t s_part[3][2][kWave];
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  const int64_t t0 = (int64_t)blockIdx.x * 64 + (wave & 1) * 32;
-  const int e0 = blockIdx.y * 64 + (wave >> 1) * 32;
+  const int eh = wave & 1, kq = wave >> 1;
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const int e0 = blockIdx.y * 64 + eh * 32;
   const int m = lane & 31, h = lane >> 5;
   const int64_t trow = min<int64_t>(t0 + m, T - 1);
   const int erow = min(e0 + m, E - 1);
   const uint4* xa = reinterpret_cast<const uint4*>(X + trow * H) + 4 * h;
   const uint4* rb = reinterpret_cast<const uint4*>(router + (int64_t)erow * H) + 4 * h;
+  const int steps = H >> 6;
+  const int s_begin = kq * steps / 4, s_end = (kq + 1) * steps / 4;
   f32x16_t acc = {};
-  for (int k0 = 0; k0 < H; k0 += 64) {
-    uint4 av[4], bv[4];
+  for (int s0 = s_begin; s0 < s_end; s0 += kRouterBatch) {
+    uint4 av[kRouterBatch][4], bv[kRouterBatch][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) { av[s] = xa[(k0 >> 3) + s]; bv[s] = rb[(k0 >> 3) + s]; }
+    for (int b = 0; b < kRouterBatch; ++b) {
+      const int st = min(s0 + b, s_end - 1);  // steps past the quarter's end are loaded but not used
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[s]),
-                                                    __builtin_bit_cast(bf16x8_t, bv[s]), acc, 0, 0, 0);
+      for (int q = 0; q < 4; ++q) {
+        av[b][q] = xa[st * 8 + q];
+        bv[b][q] = rb[st * 8 + q];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kRouterBatch; ++b) {
+      if (s0 + b < s_end) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[b][q]),
+                                                        __builtin_bit_cast(bf16x8_t, bv[b][q]), acc, 0, 0, 0);
+      }
+    }
+  }
+  if (kq > 0) s_part[kq - 1][eh][lane] = acc;
+  __syncthreads();
+  if (kq > 0) return;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const f32x16_t o = s_part[j][eh][lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += o[i];
   }
   // D layout: column (expert) = lane % 32, row (token) = 8*(i/4) + 4*(lane/32) + i%4
   const int e = e0 + m;
@@ -61,93 +91,120 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
   }
 }
 
-// ---- stable counting sort by expert via per-expert row bitmaps
-// bitmap[e][w] bit b <=> row 32*w + b has expert e.  The position of row r in
-// its segment is the number of set bits before it, so the order inside a
-// segment is increasing r (stable) and independent of scheduling.
+// ---- stable counting sort by expert, in two launches
+// expert_rank_kernel: one workgroup per expert e scans all rows in order and
+// gives each row r with ids[r] == e its rank (the number of earlier rows of
+// expert e), so the order inside a segment is increasing r (stable) and does
+// not depend on scheduling; it also writes counts[e].
+// expert_scatter_kernel: every workgroup scans the counts into segment offsets
+// (workgroup 0 also writes them out) and places its rows at offset + rank.
 
-__global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
-}
+constexpr int kRankThreads = 256;
+constexpr int kRankPer = 32;  // rows per thread per chunk (kept in registers)
 
-__global__ void bitmap_set_kernel(const int32_t* __restrict__ ids, int64_t rows, int E, int64_t W,
-                                  uint32_t* __restrict__ bitmap) {
-  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += (int64_t)gridDim.x * blockDim.x) {
-    const int e = ids[r];
-    if (e >= 0 && e < E) atomicOr(&bitmap[(int64_t)e * W + (r >> 5)], 1u << (r & 31));
+// Exclusive prefix sum of v over the workgroup (kRankThreads threads); *total gets the sum.
+__device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* s_wave, int32_t* total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  int32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  int32_t before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kRankThreads / kWave; ++w) {
+    before += w < wave ? s_wave[w] : 0;
+    sum += s_wave[w];
+  }
+  __syncthreads();  // s_wave may be reused by the next call
+  *total = sum;
+  return before + incl - v;
 }
 
-// One workgroup per expert: exclusive prefix of popcounts over its W words.
-__global__ __launch_bounds__(256) void bitmap_scan_kernel(const uint32_t* __restrict__ bitmap, int64_t W,
-                                                          uint32_t* __restrict__ prefix, int32_t* __restrict__ counts) {
-  __shared__ int32_t s_part[256];
+__global__ __launch_bounds__(kRankThreads) void expert_rank_kernel(const int32_t* __restrict__ ids, int64_t rows,
+                                                                   int32_t* __restrict__ rank,
+                                                                   int32_t* __restrict__ counts) {
+  __shared__ int32_t s_wave[kRankThreads / kWave];
   const int e = blockIdx.x;
-  const uint32_t* bm = bitmap + (int64_t)e * W;
-  uint32_t* pre = prefix + (int64_t)e * W;
-  const int64_t per = (W + blockDim.x - 1) / blockDim.x;
-  const int64_t w0 = threadIdx.x * per, w1 = min<int64_t>(W, w0 + per);
-  int32_t local = 0;
-  for (int64_t w = w0; w < w1; ++w) local += __popc(bm[w]);
-  s_part[threadIdx.x] = local;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over the 256 partial sums
-  for (int off = 1; off < 256; off <<= 1) {
-    int32_t v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
-    __syncthreads();
-    s_part[threadIdx.x] += v;
-    __syncthreads();
+  int32_t base = 0;
+  for (int64_t c0 = 0; c0 < rows; c0 += (int64_t)kRankThreads * kRankPer) {
+    const int64_t r0 = c0 + (int64_t)threadIdx.x * kRankPer;
+    uint32_t bits = 0;  // bit j: row r0 + j belongs to expert e
+#pragma unroll
+    for (int j = 0; j < kRankPer; ++j) {
+      const int64_t r = r0 + j;
+      bits |= (r < rows && ids[min(r, rows - 1)] == e ? 1u : 0u) << j;
+    }
+    int32_t total;
+    const int32_t before = block_exclusive_scan(__popc(bits), s_wave, &total);
+    uint32_t left = bits;
+    while (left) {
+      const int j = __builtin_ctz(left);
+      rank[r0 + j] = base + before + __popc(bits & ((1u << j) - 1u));
+      left &= left - 1u;
+    }
+    base += total;
   }
-  int32_t run = s_part[threadIdx.x] - local;
-  for (int64_t w = w0; w < w1; ++w) {
-    pre[w] = run;
-    run += __popc(bm[w]);
-  }
-  if (threadIdx.x == blockDim.x - 1) counts[e] = s_part[threadIdx.x];
+  if (threadIdx.x == 0) counts[e] = base;
 }
 
-// One workgroup: offsets = exclusive scan of counts; tile_offsets likewise of ceil(count/tile_rows).
-__global__ __launch_bounds__(1024) void offsets_scan_kernel(const int32_t* __restrict__ counts, int E,
-                                                            int32_t* __restrict__ offsets, int tile_rows,
-                                                            int32_t* __restrict__ tile_offsets) {
-  __shared__ int32_t s_c[1024];
-  __shared__ int32_t s_t[1024];
-  const int i = threadIdx.x;
+__global__ __launch_bounds__(1024) void expert_scatter_kernel(const int32_t* __restrict__ ids, int64_t rows, int E,
+                                                              const int32_t* __restrict__ rank,
+                                                              const int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_rows,
+                                                              int32_t* __restrict__ inv_rows, GroupTiles tiles) {
+  __shared__ int32_t s_c[kMaxExperts];
+  __shared__ int32_t s_t[kMaxExperts];
+  const int i = threadIdx.x;  // blockDim.x == kMaxExperts
+  const bool tiled = tiles.table != nullptr;
+  const int tr = tiled ? tiles.tile_rows : 1;
   const int32_t c = i < E ? counts[i] : 0;
-  const int32_t tc = (tile_rows > 0 && i < E) ? (c + tile_rows - 1) / tile_rows : 0;
   s_c[i] = c;
-  s_t[i] = tc;
+  s_t[i] = (c + tr - 1) / tr;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int32_t a = i >= off ? s_c[i - off] : 0;
-    int32_t b = i >= off ? s_t[i - off] : 0;
+  for (int off = 1; off < kMaxExperts; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int32_t a = i >= off ? s_c[i - off] : 0;
+    const int32_t b = i >= off ? s_t[i - off] : 0;
     __syncthreads();
     s_c[i] += a;
     s_t[i] += b;
     __syncthreads();
   }
-  if (i < E) {
-    offsets[i + 1] = s_c[i];
-    if (tile_offsets) tile_offsets[i + 1] = s_t[i];
+  if (blockIdx.x == 0) {
+    if (i < E) offsets[i + 1] = s_c[i];
+    if (i == 0) offsets[0] = 0;
+    if (tiled) {
+      // routed tiles of expert i, then the extra tiles, then unused slots
+      if (i < E) {
+        const int32_t t0 = i > 0 ? s_t[i - 1] : 0, p0 = i > 0 ? s_c[i - 1] : 0;
+        for (int32_t t = t0; t < s_t[i]; ++t) {
+          const int32_t first = p0 + (t - t0) * tr;
+          tiles.table[t] = make_int4(i, first, min(tr, s_c[i] - first), 0);
+        }
+      }
+      const int32_t routed = s_t[E - 1];
+      for (int32_t t = routed + i; t < tiles.max_tiles; t += blockDim.x) {
+        const int64_t first = (int64_t)(t - routed) * tr;
+        tiles.table[t] = first < tiles.extra_rows
+                             ? make_int4(-1, (int32_t)(rows + first), (int32_t)min<int64_t>(tr, tiles.extra_rows - first), 0)
+                             : make_int4(-2, 0, 0, 0);
+      }
+    }
   }
-  if (i == 0) {
-    offsets[0] = 0;
-    if (tile_offsets) tile_offsets[0] = 0;
-  }
-}
-
-__global__ void permute_scatter_kernel(const int32_t* __restrict__ ids, int64_t rows, int E, int64_t W,
-                                       const uint32_t* __restrict__ bitmap, const uint32_t* __restrict__ prefix,
-                                       const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
-                                       int32_t* __restrict__ inv_rows) {
   for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += (int64_t)gridDim.x * blockDim.x) {
     const int e = ids[r];
     if (e < 0 || e >= E) continue;
-    const int64_t w = (int64_t)e * W + (r >> 5);
-    const uint32_t below = bitmap[w] & ((1u << (r & 31)) - 1u);
-    const int32_t pos = offsets[e] + (int32_t)prefix[w] + __popc(below);
+    const int32_t pos = (e > 0 ? s_c[e - 1] : 0) + rank[r];
     sorted_rows[pos] = (int32_t)r;
     inv_rows[r] = pos;
+    if (tiled) {
+      tiles.row_src[pos] = (int32_t)(r / tiles.topk);
+      tiles.row_w[pos] = tiles.weights ? tiles.weights[r] : 1.0f;
+    }
   }
 }
 
@@ -164,8 +221,8 @@ size_t route_workspace_bytes(int64_t T, int n_experts) { return align256((size_t
 hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* X, int64_t T, int k, int32_t* ids,
                           float* weights, void* ws, hipStream_t stream) {
   float* logits = static_cast<float*>(ws);
-  dim3 grid((unsigned)((T + 63) / 64), (unsigned)((E + 63) / 64));
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, router, X, T, E, H, logits);
+  dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 63) / 64));
+  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(512), 0, stream, router, X, T, E, H, logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, logits, T, E, k, ids,
@@ -174,26 +231,24 @@ hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* 
 }
 
 size_t permute_workspace_bytes(int64_t rows, int n_experts) {
-  const int64_t W = (rows + 31) / 32;
-  return 2 * align256((size_t)n_experts * W * 4) + align256((size_t)n_experts * 4);
+  return align256((size_t)rows * 4) + align256((size_t)n_experts * 4);
+}
+
+int group_max_tiles(int64_t rows, int n_experts, int64_t extra_rows, int tile_rows) {
+  return (int)((rows + tile_rows - 1) / tile_rows + n_experts + (extra_rows + tile_rows - 1) / tile_rows);
 }
 
 hipError_t run_permute(const int32_t* ids, int64_t rows, int E, int32_t* offsets, int32_t* sorted_rows,
-                       int32_t* inv_rows, void* ws, int tile_rows, int32_t* tile_offsets, hipStream_t stream) {
-  const int64_t W = (rows + 31) / 32;
+                       int32_t* inv_rows, void* ws, const GroupTiles* tiles, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(w);
-  w += align256((size_t)E * W * 4);
-  uint32_t* prefix = reinterpret_cast<uint32_t*>(w);
-  w += align256((size_t)E * W * 4);
-  int32_t* counts = reinterpret_cast<int32_t*>(w);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(E * W, 256)), dim3(256), 0, stream, bitmap, (int64_t)E * W);
-  hipLaunchKernelGGL(bitmap_set_kernel, dim3(grid_for(rows, 256)), dim3(256), 0, stream, ids, rows, E, W, bitmap);
-  hipLaunchKernelGGL(bitmap_scan_kernel, dim3(E), dim3(256), 0, stream, bitmap, W, prefix, counts);
-  hipLaunchKernelGGL(offsets_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, E, offsets, tile_rows,
-                     tile_offsets);
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3(grid_for(rows, 256)), dim3(256), 0, stream, ids, rows, E, W,
-                     bitmap, prefix, offsets, sorted_rows, inv_rows);
+  int32_t* rank = reinterpret_cast<int32_t*>(w);
+  int32_t* counts = reinterpret_cast<int32_t*>(w + align256((size_t)rows * 4));
+  hipLaunchKernelGGL(expert_rank_kernel, dim3(E), dim3(kRankThreads), 0, stream, ids, rows, rank, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GroupTiles none{};
+  hipLaunchKernelGGL(expert_scatter_kernel, dim3(grid_for(rows, kMaxExperts)), dim3(kMaxExperts), 0, stream, ids,
+                     rows, E, rank, counts, offsets, sorted_rows, inv_rows, tiles ? *tiles : none);
   return hipGetLastError();
 }
 

@@ -4,22 +4,24 @@
 // README, "How the speed was achieved": decode is bandwidth-bound and its
 // kernels are tuned against the chain of reads).  One grid of one workgroup
 // per CU runs three phases:
-//   A: router logits (bf16 GEMV, one wave per expert row) and the shared
-//      expert's gate/up rows with SwiGLU, neither of which needs the routing;
-//   B: top-k of the logits (recomputed by every workgroup from the logit
-//      vector), then the routed experts' gate/up rows with SwiGLU; meanwhile
-//      each workgroup prefetches into registers the down-projection weights
-//      of the output rows it owns in phase C (known once the experts are);
+//   A: router logits (bf16 GEMV, one row per wave 0 of a workgroup), each
+//      published with this launch's epoch in one 64-bit word, while waves 1-3
+//      compute the shared expert's gate/up rows with SwiGLU (off the critical
+//      path: their results are needed only in phase C);
+//   B: top-k of the logits (recomputed by every workgroup straight from the
+//      tagged words, so seeing a logit and reading it are one load), then the
+//      routed experts' gate/up rows with SwiGLU; meanwhile each workgroup
+//      prefetches into registers the down-projection weights of the output
+//      rows it owns in phase C (known once the experts are);
 //   C: for each owned output row, the down rows of all selected experts and
 //      the shared expert, split over the workgroup's waves, combined in LDS in
 //      a fixed order (no atomics); y is written once.
 //
-// No grid-wide barrier: each workgroup, when its share of a phase is done and
-// its device-coherent stores have landed, publishes one flag word (this
-// launch's epoch) for that phase.  A consumer polls the 256-ish flags of the
-// phase it depends on, then reads the handed-over values (logits, SwiGLU
-// activations) once with device-coherent loads; so a handoff costs about two
-// memory round trips and light polling traffic.  The epoch is agreed through
+// No grid-wide barrier.  The logits carry the epoch themselves.  For the SwiGLU
+// activations each workgroup, when its phase A/B work is done and its
+// device-coherent stores have landed, publishes one flag word (the epoch); a
+// consumer polls the 256-ish flags, then reads the activations once with
+// device-coherent loads.  The epoch is agreed through
 // per-group arrival counters in the workspace.  Every poll is bounded: a lost
 // flag yields a wrong result and a recorded timeout, never a hang.
 #include "kernels.h"
@@ -44,11 +46,12 @@ struct DecodeWs {
   unsigned long long group_ctr[kEpochGroups][32];  // {epoch:hi32, arrivals:lo32}, one 256-byte slot each
   unsigned timeouts;
   unsigned pad[63];
-  // Phase flags, one per 64-byte line: flags that share a line are written by
-  // different CUs, and such partial-line stores slow their observers down
-  // severalfold.  flag_x[b][0] is the epoch once workgroup b's outputs of that
-  // phase are visible.
-  unsigned flag_a[kMaxBlocks][kFlagStride];
+  // Router logit of expert e: tag_logit[e][0] = {epoch:hi32, fp32 bits:lo32}.
+  // One 64-byte line per word (and per flag below): words that share a line
+  // are written by different CUs, and such partial-line stores slow their
+  // observers down severalfold.
+  unsigned long long tag_logit[kMaxExperts][8];
+  // flag_b[b][0] is the epoch once workgroup b's activations are visible.
   unsigned flag_b[kMaxBlocks][kFlagStride];
 };
 
@@ -60,7 +63,6 @@ struct DecodeParams {
   int32_t* ids_out;           // nullable [k]
   float* w_out;               // nullable [k]
   DecodeWs* ws;
-  float* logits;              // [E]
   float* act;                 // [k+1][I]: routed slots 0..k-1, shared slot k
   int lsH;                    // log2 lanes per row for rows of length hidden
   int lsI;                    // log2 lanes per row for rows of length inter
@@ -99,13 +101,17 @@ __device__ __forceinline__ void wave_wait_flags(const unsigned (*flag_rows)[kFla
   }
 }
 
-// Stage a bf16 vector of n values (n % 32 == 0) into LDS: one thread per
-// 8-value block, chunk sums by a quad reduction.
-__device__ __forceinline__ void stage_bf16_parallel(const uint16_t* __restrict__ x, int n, uint32_t* vp, float* vs) {
+// Stage a bf16 vector of n values (n % 32 == 0) into LDS: threads [t0, t0 + nthr)
+// take one 8-value block each per pass, chunk sums by a quad reduction (nthr and
+// t0 multiples of 4, so the 4 blocks of a chunk sit in one lane quad).
+__device__ __forceinline__ void stage_bf16_parallel(const uint16_t* __restrict__ x, int n, uint32_t* vp, float* vs,
+                                                    int t0, int nthr) {
   constexpr int ST = chunk_stride<1>();
+  const int t = threadIdx.x - t0;
+  if (t < 0 || t >= nthr) return;
   const int nblk = n >> 3;
-  for (int base = 0; base < nblk; base += blockDim.x) {
-    const int b = base + threadIdx.x;
+  for (int base = 0; base < nblk; base += nthr) {
+    const int b = base + t;
     float sum = 0.f;
     if (b < nblk) {
       const uint4 v = reinterpret_cast<const uint4*>(x)[b];
@@ -228,23 +234,41 @@ __device__ __forceinline__ void gate_up_dot(const GateUpRef (&ref)[NI], const bo
   for (int n = 0; n < NI; ++n) out[n] = make_float2(group_sum_rt(ag[n], lsh), group_sum_rt(au[n], lsh));
 }
 
-// Top-k of E logits (written by other workgroups, read device-coherently) by one
-// wave.  Lane l holds ids [l*V, l*V + V) with its keys sorted in descending
+// Top-k of E logits by one wave, polling the epoch-tagged words that other
+// workgroups publish until every one carries `epoch` (bounded; a timeout is
+// counted).  Lane l holds ids [l*V, l*V + V) with its keys sorted in descending
 // order, so each of the k rounds is a wave-wide maximum of the lane heads and a
 // pop in the winning lane.  Equal logits resolve to the lower expert id: inside
 // a lane by the sort order, across lanes because the lowest matching lane wins.
 // Writes ids/weights (renormalised softmax of the kept logits) to LDS and, when
 // given, to ids_out/w_out.
 template <int V>
-__device__ __forceinline__ void wave_topk_sorted(const float* logits, int E, int k, int32_t* s_ids, float* s_w,
-                                                 int32_t* ids_out, float* w_out) {
+__device__ __forceinline__ void wave_topk_tagged(const unsigned long long (*tags)[8], int E, int k, uint32_t epoch,
+                                                 unsigned* timeouts, int32_t* s_ids, float* s_w, int32_t* ids_out,
+                                                 float* w_out) {
   const int lane = lane_id();
   uint32_t key[V];
   int id[V];
 #pragma unroll
-  for (int j = 0; j < V; ++j) {
-    id[j] = lane * V + j;
-    key[j] = __float_as_uint(ld_agent(logits + min(id[j], E - 1)));  // all loads in flight together
+  for (int j = 0; j < V; ++j) id[j] = lane * V + j;
+  for (unsigned spins = 0;; ++spins) {
+    bool ready = true;
+    unsigned long long t[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j)  // all loads in flight together
+      t[j] = __hip_atomic_load(const_cast<unsigned long long*>(&tags[min(id[j], E - 1)][0]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      key[j] = (uint32_t)t[j];
+      ready &= id[j] >= E || (uint32_t)(t[j] >> 32) == epoch;
+    }
+    if (__all(ready)) break;
+    if (spins == kPollLimit) {
+      if (lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
   }
 #pragma unroll
   for (int j = 0; j < V; ++j) key[j] = id[j] < E ? float_key(__uint_as_float(key[j])) : 0u;
@@ -318,82 +342,89 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
   const int gwave = blockIdx.x * kWaves + wv;
   const int nwaves = gridDim.x * kWaves;
 
-  // ---- epoch of this launch: the arrivals of one group agree on its counter's epoch field
-  if (threadIdx.x == 0) {
+  // ---- epoch of this launch: the arrivals of one group agree on its counter's
+  // epoch field.  Taken by thread 0 once wave 0's first router loads are in
+  // flight, so the two latencies overlap.
+  uint32_t my_epoch = 0;
+  auto acquire_epoch = [&]() {
     const int g = blockIdx.x % kEpochGroups;
     const unsigned gsize = (gridDim.x - g + kEpochGroups - 1) / kEpochGroups;
     unsigned long long* ctr = &p.ws->group_ctr[g][0];
     const unsigned long long old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)old == gsize - 1)
       __hip_atomic_fetch_add(ctr, (1ull << 32) - gsize, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_epoch = (uint32_t)(old >> 32) + 1u;
+    my_epoch = (uint32_t)(old >> 32) + 1u;
+    s_epoch = my_epoch;
+  };
+
+  // ------------------------------------------------------------ phase A
+  if (wv == 0) {
+    // router rows e = blockIdx.x, blockIdx.x + gridDim.x, ...; x is read from global memory
+    bool have_epoch = false;
+    for (int it = blockIdx.x; it < E; it += gridDim.x) {
+      const uint4* r = reinterpret_cast<const uint4*>(p.L.router + (size_t)it * H);
+      const uint4* xv = reinterpret_cast<const uint4*>(p.x);
+      constexpr int kBatch = 4;  // row chunks in flight per lane
+      float acc0 = 0.f, acc1 = 0.f;
+      for (int c0 = 0; c0 < (H >> 3); c0 += kBatch * kWave) {
+        uint4 w[kBatch], v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          const int c = c0 + q * kWave + lane;
+          const bool ok = c < (H >> 3);
+          w[q] = ok ? r[c] : make_uint4(0, 0, 0, 0);
+          v[q] = ok ? xv[c] : make_uint4(0, 0, 0, 0);
+        }
+        if (!have_epoch) {
+          have_epoch = true;
+          if (lane == 0) acquire_epoch();
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          acc0 = dot2_bf16(w[q].x, v[q].x, acc0);
+          acc1 = dot2_bf16(w[q].y, v[q].y, acc1);
+          acc0 = dot2_bf16(w[q].z, v[q].z, acc0);
+          acc1 = dot2_bf16(w[q].w, v[q].w, acc1);
+        }
+      }
+      const float acc = group_sum_rt(acc0 + acc1, 6);
+      const uint32_t ep = __builtin_amdgcn_readfirstlane(my_epoch);  // lane 0 holds it
+      if (lane == 0)
+        __hip_atomic_store(&p.ws->tag_logit[it][0], ((unsigned long long)ep << 32) | __float_as_uint(acc),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!have_epoch && lane == 0) acquire_epoch();
+  } else {
+    stage_bf16_parallel(p.x, H, xp, xs, kWave, kThreads - kWave);
   }
-  stage_bf16_parallel(p.x, H, xp, xs);
   __syncthreads();
   const uint32_t epoch = s_epoch;
 
-  // ------------------------------------------------------------ phase A
-  // Items go round-robin over workgroups first (router row e on workgroup e),
-  // so every CU streams a similar share.
-  {
-    const int aw = wv * gridDim.x + blockIdx.x;
-    const int L = 1 << p.lsH, sub = lane & (L - 1), rsub = lane >> p.lsH, rpi = kWave >> p.lsH;
-    const int pair_items = p.L.has_shared ? (I + rpi - 1) / rpi : 0;
-    for (int it = aw; it < E + pair_items; it += nwaves) {
-      if (it < E) {
-        const uint4* r = reinterpret_cast<const uint4*>(p.L.router + (size_t)it * H);
-        const uint4* xv = reinterpret_cast<const uint4*>(p.x);
-        constexpr int kBatch = 4;  // row chunks in flight per lane
-        float acc0 = 0.f, acc1 = 0.f;
-        for (int c0 = 0; c0 < (H >> 3); c0 += kBatch * kWave) {
-          uint4 w[kBatch], v[kBatch];
-#pragma unroll
-          for (int q = 0; q < kBatch; ++q) {
-            const int c = c0 + q * kWave + lane;
-            const bool ok = c < (H >> 3);
-            w[q] = ok ? r[c] : make_uint4(0, 0, 0, 0);
-            v[q] = ok ? xv[c] : make_uint4(0, 0, 0, 0);
-          }
-#pragma unroll
-          for (int q = 0; q < kBatch; ++q) {
-            acc0 = dot2_bf16(w[q].x, v[q].x, acc0);
-            acc1 = dot2_bf16(w[q].y, v[q].y, acc1);
-            acc0 = dot2_bf16(w[q].z, v[q].z, acc0);
-            acc1 = dot2_bf16(w[q].w, v[q].w, acc1);
-          }
-        }
-        const float acc = group_sum_rt(acc0 + acc1, 6);
-        if (lane == 0) st_agent(p.logits + it, acc);
-      } else {
-        const int i = (it - E) * rpi + rsub;
-        const bool live[1] = {i < I};
-        const GateUpRef ref[1] = {gate_up_ref(p.L.sh_gate, p.L.sh_up, 0, live[0] ? i : 0, H, I)};
-        float2 gu[1];
-        gate_up_dot<1>(ref, live, H, sub, L, p.lsH, xp, xs, gu);
-        if (live[0] && sub == 0) st_agent(p.act + (size_t)k * I + i, silu(gu[0].x) * gu[0].y);
-      }
-    }
-  }
-  publish_flag(&p.ws->flag_a[blockIdx.x][0], epoch);
-
-  // ------------------------------------------------------------ phase B
-  if (wv == 0) wave_wait_flags(p.ws->flag_a, gridDim.x, epoch, timeouts);
-  __syncthreads();
   if (wv == 0) {
+    // B: top-k from the tagged logits (every workgroup, redundantly)
     if (E <= 4 * kWave)
-      wave_topk_sorted<4>(p.logits, E, k, s_ids, s_w, blockIdx.x == 0 ? p.ids_out : nullptr,
+      wave_topk_tagged<4>(p.ws->tag_logit, E, k, epoch, timeouts, s_ids, s_w, blockIdx.x == 0 ? p.ids_out : nullptr,
                           blockIdx.x == 0 ? p.w_out : nullptr);
     else
-      wave_topk_sorted<kMaxExperts / kWave>(p.logits, E, k, s_ids, s_w, blockIdx.x == 0 ? p.ids_out : nullptr,
-                                            blockIdx.x == 0 ? p.w_out : nullptr);
+      wave_topk_tagged<kMaxExperts / kWave>(p.ws->tag_logit, E, k, epoch, timeouts, s_ids, s_w,
+                                            blockIdx.x == 0 ? p.ids_out : nullptr, blockIdx.x == 0 ? p.w_out : nullptr);
     if (lane == 0 && p.L.has_shared) {
       s_ids[k] = -1;
       s_w[k] = 1.0f;
     }
   } else if (p.L.has_shared) {
-    // the shared expert's SwiGLU activations (from phase A) into LDS slot k
-    stage_coherent_split(p.act + (size_t)k * I, 1, I, ap + (size_t)k * CI * chunk_stride<2>(), as + k * CI, kWave,
-                         kThreads - kWave);
+    // A, off the critical path: the shared expert's gate/up rows over waves 1-3 of every workgroup
+    const int aw = (wv - 1) * gridDim.x + blockIdx.x, nw = (kWaves - 1) * gridDim.x;
+    const int L = 1 << p.lsH, sub = lane & (L - 1), rsub = lane >> p.lsH, rpi = kWave >> p.lsH;
+    const int pair_items = (I + rpi - 1) / rpi;
+    for (int it = aw; it < pair_items; it += nw) {
+      const int i = it * rpi + rsub;
+      const bool live[1] = {i < I};
+      const GateUpRef ref[1] = {gate_up_ref(p.L.sh_gate, p.L.sh_up, 0, live[0] ? i : 0, H, I)};
+      float2 gu[1];
+      gate_up_dot<1>(ref, live, H, sub, L, p.lsH, xp, xs, gu);
+      if (live[0] && sub == 0) st_agent(p.act + (size_t)k * I + i, silu(gu[0].x) * gu[0].y);
+    }
   }
   __syncthreads();
 
@@ -452,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
   // ------------------------------------------------------------ phase C
   if (wv == 0) wave_wait_flags(p.ws->flag_b, gridDim.x, epoch, timeouts);
   __syncthreads();
-  stage_coherent_split(p.act, k, I, ap, as, 0, kThreads);
+  stage_coherent_split(p.act, nslot, I, ap, as, 0, kThreads);  // routed slots and the shared slot
   __syncthreads();
   {
     constexpr int ST = chunk_stride<2>();
@@ -528,7 +559,7 @@ size_t decode_lds(const DecodeLayer& L) {
 size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k) {
   (void)hidden;
   (void)n_experts;
-  return align256(sizeof(DecodeWs)) + align256((size_t)kMaxExperts * 4) + align256((size_t)(top_k + 1) * inter * 4);
+  return align256(sizeof(DecodeWs)) + align256((size_t)(top_k + 1) * inter * 4);
 }
 
 size_t decode_lds_bytes(const DecodeLayer& L) { return decode_lds(L); }
@@ -545,8 +576,6 @@ hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, 
   char* w = static_cast<char*>(ws);
   p.ws = reinterpret_cast<DecodeWs*>(w);
   w += align256(sizeof(DecodeWs));
-  p.logits = reinterpret_cast<float*>(w);
-  w += align256((size_t)kMaxExperts * 4);
   p.act = reinterpret_cast<float*>(w);
   p.lsH = lanes_log2(L.hidden / kGroup);
   p.lsI = lanes_log2(L.inter / kGroup);

@@ -36,7 +36,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kEpochGroups = 8;
 constexpr int kPrefetchSlots = 3;   // down-row prefetch: slots per wave held in registers
-constexpr int kStageRounds = 2;     // phase C staging: 8-value blocks per thread with loads in flight
+constexpr int kStageRounds = 3;     // phase C staging: 8-value blocks per thread with loads in flight (9 x 512 values in one pass)
 constexpr unsigned kPollLimit = 1u << 18;  // ~0.25 s of polling
 
 constexpr int kMaxBlocks = 1024;

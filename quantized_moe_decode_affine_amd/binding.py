@@ -164,8 +164,10 @@ def workspace_bytes(op: int, layer: Optional[DeviceLayer] = None, W: Optional[De
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A zero-filled device byte buffer (torch's allocator returns 256-byte aligned blocks).
 
-    Zero-filled because the decode workspace holds a grid-barrier state that must
-    be zero before its first use; the other operations do not care."""
+    Zero-filled because the decode workspace holds arrival counters and phase
+    flags, and the LM-head workspace an arrival counter, that must be zero before
+    their first use (each call leaves them ready for the next); the other
+    operations do not care."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 

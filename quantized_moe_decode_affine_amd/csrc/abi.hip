@@ -86,7 +86,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? Q4MOE_OK : Q4MOE_EHIP; }
 size_t lmhead_ws(int64_t rows, int64_t k, int64_t B) {
   (void)rows;
   (void)k;
-  return (size_t)2048 * (size_t)B * 8;
+  return 256 + (size_t)q4moe::kMaxGemvBlocks * (size_t)B * 8;  // arrival counter, then the partials
 }
 
 }  // namespace
@@ -239,10 +239,12 @@ int lmhead_argmax(const q4moe_matrix* W, const q4moe_bf16* X, int64_t B, int32_t
     if (B > 8 || rows > kMaxRows32 || B * W->k > kMaxGemvK) return Q4MOE_EUNSUPPORTED;
     const size_t need = lmhead_ws(rows, W->k, B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
-    float* part_val = static_cast<float*>(workspace);
-    int32_t* part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + (size_t)2048 * B * 4);
+    char* w = static_cast<char*>(workspace);
+    unsigned* done = reinterpret_cast<unsigned*>(w);
+    float* part_val = reinterpret_cast<float*>(w + 256);
+    int32_t* part_idx = reinterpret_cast<int32_t*>(w + 256 + (size_t)q4moe::kMaxGemvBlocks * B * 4);
     return hip_status(q4moe::run_lmhead_argmax(W->codes, W->scales, W->biases, rows, (int)W->k, X, (int)B, ids,
-                                               max_logit, part_val, part_idx, (hipStream_t)stream));
+                                               max_logit, part_val, part_idx, done, (hipStream_t)stream));
   } catch (...) {
     return Q4MOE_EHIP;
   }

@@ -43,9 +43,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// Two nibbles of `word` (positions j and j+4, j = shift/4) as bfloat16 (128+q) pair.
+// kMagicPair in a VGPR, from an asm the compiler cannot turn back into a literal
+// (identical calls are merged).
+__device__ __forceinline__ uint32_t magic_pair_reg() {
+  uint32_t m;
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  return m;
+}
+
+// Two nibbles of `word` (positions j and j+4, j = shift/4) as bfloat16 (128+q) pair:
+// ((word >> shift) & kNibblePairMask) | kMagicPair in one v_and_or_b32 after the
+// shift.  (A VOP3 instruction on this target takes at most one literal, so
+// written in C the compiler splits it into v_and + v_or.)
 __device__ __forceinline__ uint32_t nib_pair(uint32_t word, int shift) {
-  return ((word >> shift) & kNibblePairMask) | kMagicPair;
+  static_assert(kNibblePairMask == 0x000F000Fu && kMagicPair == 0x43004300u, "constants in the asm below");
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(word >> shift), "s"(kNibblePairMask), "v"(magic_pair_reg()));
+  return r;
 }
 
 // acc + a.lo*b.lo + a.hi*b.hi on packed bfloat16 pairs, fp32 accumulate.

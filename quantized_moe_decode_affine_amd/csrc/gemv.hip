@@ -6,10 +6,11 @@
 // Mapping: L lanes cover one row (L = min(64, groups per row), a power of
 // two), each lane takes one 64-column group per step (two uint4 code loads,
 // one scale, one bias), so a wave instruction reads 64/L rows of contiguous
-// code bytes.  Each lane keeps S rows in flight.  Activations are staged once
-// per workgroup in LDS as permuted bfloat16 pairs; the group products run on
-// v_dot2 with exact 128+q dequantization (common.h), the row sum is a lane
-// butterfly.
+// code bytes.  Each lane keeps S rows in flight, and where a lane owns exactly
+// one group per row the next step's rows are loaded while the current one
+// computes.  Activations are staged once per workgroup in LDS as permuted
+// bfloat16 pairs; the group products run on v_dot2 with exact 128+q
+// dequantization (common.h), the row sums are DPP/permlane reductions.
 #include "kernels.h"
 #include "vecstage.h"
 
@@ -24,18 +25,22 @@ struct GemvParams {
   int64_t rows;
   int k;
   int lshift;              // log2 of lanes per row
+  int chunk_lanes;         // 1: exactly one group per lane (lanes per row == k/64)
   const uint16_t* x;       // [B][k]
   void* y;                 // store mode: [B][rows]
   int out_bf16;
-  float* part_val;         // argmax mode: [gridDim.x][B]
+  float* part_val;         // argmax mode: [gridDim.x][B] per-workgroup (max, lowest index)
   int32_t* part_idx;
+  unsigned* done;          // argmax mode: arrival counter (0 between calls)
+  int32_t* ids;            // argmax mode: [B]
+  float* max_logit;        // argmax mode: [B] or null
 };
 
 __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-template <int S, int B, bool ARGMAX>
+template <int S, int B, bool ARGMAX, bool CHUNK>
 __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
   extern __shared__ __align__(16) uint32_t smem[];
   constexpr int ST = chunk_stride<1>();
@@ -62,48 +67,9 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
 #pragma unroll
   for (int b = 0; b < B; ++b) { best[b] = -INFINITY; besti[b] = 0x7FFFFFFF; }
 
-  for (int64_t base = wave * step; base < p.rows; base += nwaves * step) {
-    float acc[S][B];
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int b = 0; b < B; ++b) acc[s][b] = 0.f;
-
-    for (int g = sub; g < G; g += L) {
-      uint4 c0[S], c1[S];
-      uint32_t sb[S], bb[S];
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const int64_t row = base + (int64_t)s * rpi + rsub;
-        if (row < p.rows) {
-          const uint4* cr = p.codes + row * C + 2 * g;
-          c0[s] = cr[0];
-          c1[s] = cr[1];
-          sb[s] = p.scales[row * G + g];
-          bb[s] = p.biases[row * G + g];
-        } else {
-          c0[s] = c1[s] = make_uint4(0, 0, 0, 0);
-          sb[s] = bb[s] = 0;
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const uint32_t* v = vp + b * C * ST + 2 * g * ST;
-        const float vsum = vs[b * C + 2 * g] + vs[b * C + 2 * g + 1];
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          float pd = chunk_pdot<1>(c0[s], v) + chunk_pdot<1>(c1[s], v + ST);
-          acc[s][b] += affine_term(pd, vsum, sb[s], bb[s]);
-        }
-      }
-    }
-
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-      for (int b = 0; b < B; ++b)
-        for (int m = 1; m < L; m <<= 1) acc[s][b] += __shfl_xor(acc[s][b], m, kWave);
-
+  // Row totals of one step (every lane of a row's group holds them): store, or
+  // fold into this lane's running argmax.
+  auto emit = [&](int64_t base, float (&acc)[S][B]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int64_t row = base + (int64_t)s * rpi + rsub;
@@ -122,11 +88,161 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
         }
       }
     }
+  };
+
+  if constexpr (CHUNK) {
+    // One lane per 64-column group of a row (L == G): the group's activation
+    // pairs and sum are loop invariants (in registers for B <= 2); each row's
+    // codes are converted once and shared by the batch rows; row sums are
+    // DPP/permlane reductions over the row's L lanes.
+    constexpr bool kXReg = B <= 2;
+    const int g = sub;
+    float vsum[B];
+    uint32_t xr[kXReg ? B : 1][32];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      vsum[b] = vs[b * C + 2 * g] + vs[b * C + 2 * g + 1];
+      if constexpr (kXReg) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint4 t = *reinterpret_cast<const uint4*>(vp + b * C * ST + (2 * g + (q >> 2)) * ST + 4 * (q & 3));
+          xr[b][4 * q] = t.x;
+          xr[b][4 * q + 1] = t.y;
+          xr[b][4 * q + 2] = t.z;
+          xr[b][4 * q + 3] = t.w;
+        }
+      }
+    }
+    struct RowFrag {
+      uint4 c0, c1;
+      uint32_t s, b;
+    };
+    auto convert = [&](const RowFrag& f, uint32_t (&q)[32]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint4& u = w < 4 ? f.c0 : f.c1;
+        const uint32_t word = (w & 3) == 0 ? u.x : (w & 3) == 1 ? u.y : (w & 3) == 2 ? u.z : u.w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[4 * w + j] = nib_pair(word, 4 * j);
+      }
+    };
+    auto dot = [&](const uint32_t (&q)[32], const uint32_t* xv) __attribute__((always_inline)) {
+      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; j += 4) {
+        p0 = dot2_bf16(q[j], xv[j], p0);
+        p1 = dot2_bf16(q[j + 1], xv[j + 1], p1);
+        p2 = dot2_bf16(q[j + 2], xv[j + 2], p2);
+        p3 = dot2_bf16(q[j + 3], xv[j + 3], p3);
+      }
+      return (p0 + p1) + (p2 + p3);
+    };
+    for (int64_t base = wave * step; base < p.rows; base += nwaves * step) {
+      // keeps the (loop-invariant) LDS activation reads of B > 2 inside the loop:
+      // hoisted, they would hold 32 registers per batch row
+      if constexpr (!kXReg) asm volatile("" ::: "memory");
+      RowFrag f[S];
+      {
+        // uniform 64-bit step bases, small 32-bit row offsets inside the step
+        const uint4* cb = p.codes + base * C;
+        const uint16_t* sp = p.scales + base * G;
+        const uint16_t* bp = p.biases + base * G;
+        const int left = (int)min<int64_t>(p.rows - 1 - base, (int64_t)S * rpi);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int r = min(s * rpi + rsub, left);  // rows past the end: loaded, unused
+          f[s].c0 = cb[r * C + 2 * g];
+          f[s].c1 = cb[r * C + 2 * g + 1];
+          f[s].s = sp[r * G + g];
+          f[s].b = bp[r * G + g];
+        }
+      }
+      float acc[S][B];
+      if constexpr (kXReg) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          __builtin_amdgcn_sched_barrier(0);  // one row at a time: a row's converted codes take 32 registers
+          uint32_t q[32];
+          convert(f[s], q);
+#pragma unroll
+          for (int b = 0; b < B; ++b) acc[s][b] = affine_term(dot(q, xr[b]), vsum[b], f[s].s, f[s].b);
+        }
+      } else {
+        uint32_t q[S][32];
+#pragma unroll
+        for (int s = 0; s < S; ++s) convert(f[s], q[s]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          uint32_t xl[32];
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) {
+            const uint4 t = *reinterpret_cast<const uint4*>(vp + b * C * ST + (2 * g + (qq >> 2)) * ST + 4 * (qq & 3));
+            xl[4 * qq] = t.x;
+            xl[4 * qq + 1] = t.y;
+            xl[4 * qq + 2] = t.z;
+            xl[4 * qq + 3] = t.w;
+          }
+#pragma unroll
+          for (int s = 0; s < S; ++s) acc[s][b] = affine_term(dot(q[s], xl), vsum[b], f[s].s, f[s].b);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[s][b] = group_sum_rt(acc[s][b], p.lshift);
+      emit(base, acc);
+    }
+  } else {
+    for (int64_t base = wave * step; base < p.rows; base += nwaves * step) {
+      float acc[S][B];
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[s][b] = 0.f;
+
+      for (int g = sub; g < G; g += L) {
+        uint4 c0[S], c1[S];
+        uint32_t sb[S], bb[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int64_t row = base + (int64_t)s * rpi + rsub;
+          if (row < p.rows) {
+            const uint4* cr = p.codes + row * C + 2 * g;
+            c0[s] = cr[0];
+            c1[s] = cr[1];
+            sb[s] = p.scales[row * G + g];
+            bb[s] = p.biases[row * G + g];
+          } else {
+            c0[s] = c1[s] = make_uint4(0, 0, 0, 0);
+            sb[s] = bb[s] = 0;
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const uint32_t* v = vp + b * C * ST + 2 * g * ST;
+          const float vsum = vs[b * C + 2 * g] + vs[b * C + 2 * g + 1];
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            float pd = chunk_pdot<1>(c0[s], v) + chunk_pdot<1>(c1[s], v + ST);
+            acc[s][b] += affine_term(pd, vsum, sb[s], bb[s]);
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[s][b] = group_sum_rt(acc[s][b], p.lshift);
+      emit(base, acc);
+    }
   }
 
   if constexpr (ARGMAX) {
+    // Workgroup (max, lowest index) per batch row, published device-coherently;
+    // the last workgroup to arrive reduces all partials in index order and
+    // resets the arrival counter for the next call.
     __shared__ float red_v[B][4];
     __shared__ int32_t red_i[B][4];
+    __shared__ int s_last;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       float v = best[b];
@@ -146,42 +262,45 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
       int32_t i = red_i[b][0];
       for (int w = 1; w < wpb; ++w)
         if (better(red_v[b][w], red_i[b][w], v, i)) { v = red_v[b][w]; i = red_i[b][w]; }
-      p.part_val[(size_t)blockIdx.x * B + b] = v;
-      p.part_idx[(size_t)blockIdx.x * B + b] = i;
+      st_agent(p.part_val + (size_t)blockIdx.x * B + b, v);
+      __hip_atomic_store(p.part_idx + (size_t)blockIdx.x * B + b, i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-  }
-}
-
-// One workgroup reduces the per-block (value, index) partials of each batch row.
-__global__ __launch_bounds__(256) void argmax_finalize_kernel(const float* part_val, const int32_t* part_idx,
-                                                              int nparts, int B, int32_t* ids, float* max_logit) {
-  __shared__ float sv[4];
-  __shared__ int32_t si[4];
-  for (int b = 0; b < B; ++b) {
-    float v = -INFINITY;
-    int32_t i = 0x7FFFFFFF;
-    for (int j = threadIdx.x; j < nparts; j += blockDim.x) {
-      float ov = part_val[(size_t)j * B + b];
-      int32_t oi = part_idx[(size_t)j * B + b];
-      if (better(ov, oi, v, i)) { v = ov; i = oi; }
-    }
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      float ov = __shfl_xor(v, m, kWave);
-      int32_t oi = __shfl_xor(i, m, kWave);
-      if (better(ov, oi, v, i)) { v = ov; i = oi; }
-    }
-    if (lane_id() == 0) { sv[threadIdx.x / kWave] = v; si[threadIdx.x / kWave] = i; }
+    wait_vmem();  // this thread's partial stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
-      float bv = sv[0];
-      int32_t bi = si[0];
-      for (int w = 1; w < (int)(blockDim.x / kWave); ++w)
-        if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
-      ids[b] = bi;
-      if (max_logit) max_logit[b] = bv;
+      const unsigned prev = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == gridDim.x - 1;
     }
     __syncthreads();
+    if (s_last) {
+      for (int b = 0; b < B; ++b) {
+        float v = -INFINITY;
+        int32_t i = 0x7FFFFFFF;
+        for (int j = threadIdx.x; j < (int)gridDim.x; j += blockDim.x) {
+          const float ov = ld_agent(p.part_val + (size_t)j * B + b);
+          const int32_t oi = __hip_atomic_load(p.part_idx + (size_t)j * B + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (better(ov, oi, v, i)) { v = ov; i = oi; }
+        }
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) {
+          float ov = __shfl_xor(v, m, kWave);
+          int32_t oi = __shfl_xor(i, m, kWave);
+          if (better(ov, oi, v, i)) { v = ov; i = oi; }
+        }
+        if (lane == 0) { red_v[0][threadIdx.x / kWave] = v; red_i[0][threadIdx.x / kWave] = i; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          float bv = red_v[0][0];
+          int32_t bi = red_i[0][0];
+          for (int w = 1; w < wpb; ++w)
+            if (better(red_v[0][w], red_i[0][w], bv, bi)) { bv = red_v[0][w]; bi = red_i[0][w]; }
+          p.ids[b] = bi;
+          if (p.max_logit) p.max_logit[b] = bv;
+        }
+        __syncthreads();
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -194,37 +313,83 @@ int log2_floor(int64_t v) {
 struct GemvGrid {
   int blocks;
   int lshift;
+  int chunk_lanes;
 };
 
-GemvGrid gemv_grid(int64_t rows, int k, int S) {
-  const int G = k / kGroup;
+// Lanes per row: one per 64-column group; the loop-invariant fast path applies
+// when the groups of a row are a power of two, at most 64.
+// The grid holds at most one resident round of workgroups (`resident` per CU,
+// from the occupancy of the instantiation that will run), so no workgroup
+// waits for another to finish; waves stride over the rows.
+GemvGrid gemv_grid(int64_t rows, int k, int S, int resident) {
+  const int C = k / 32, G = k / kGroup;
   GemvGrid g;
+  g.chunk_lanes = G <= kWave && (G & (G - 1)) == 0;
   g.lshift = log2_floor(G < kWave ? G : kWave);
   const int64_t rows_per_wave_iter = (int64_t)(kWave >> g.lshift) * S;
   const int64_t iters = (rows + rows_per_wave_iter - 1) / rows_per_wave_iter;
-  int64_t max_waves = (int64_t)device_cu_count() * 16;
-  if (max_waves > 8192) max_waves = 8192;  // at most 2048 blocks: bounds the argmax partials
-  const int64_t per_wave = (iters + max_waves - 1) / max_waves;
-  const int64_t waves = (iters + per_wave - 1) / per_wave;
-  g.blocks = (int)((waves + 3) / 4);
+  int64_t max_blocks = (int64_t)device_cu_count() * (resident > 0 ? resident : 1);
+  if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // bounds the argmax partials
+  const int64_t blocks = (iters + 3) / 4;
+  g.blocks = (int)(blocks < max_blocks ? blocks : max_blocks);
   return g;
+}
+
+template <int S, int B, bool ARGMAX, bool CHUNK>
+int resident_blocks(size_t lds) {
+  static int cached = -1;  // per instantiation; the LDS size only matters for large batches
+  if (cached < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, q4_gemv_kernel<S, B, ARGMAX, CHUNK>, 256, lds) != hipSuccess ||
+        n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
+
+size_t gemv_lds(int k, int B) { return (size_t)B * (k / 32) * (chunk_stride<1>() * 4 + 4); }
+
+template <int S, int B, bool ARGMAX>
+GemvGrid plan_gemv(int64_t rows, int k) {
+  const GemvGrid probe = gemv_grid(rows, k, S, 1);
+  const int res = probe.chunk_lanes ? resident_blocks<S, B, ARGMAX, true>(gemv_lds(k, B))
+                                    : resident_blocks<S, B, ARGMAX, false>(gemv_lds(k, B));
+  return gemv_grid(rows, k, S, res);
 }
 
 template <int S, int B, bool ARGMAX>
 hipError_t launch_gemv(GemvParams p, const GemvGrid& g, hipStream_t stream) {
-  const size_t lds = (size_t)B * (p.k / 32) * (chunk_stride<1>() * 4 + 4);
-  hipLaunchKernelGGL((q4_gemv_kernel<S, B, ARGMAX>), dim3(g.blocks), dim3(256), lds, stream, p);
+  const size_t lds = gemv_lds(p.k, B);
+  if (g.chunk_lanes)
+    hipLaunchKernelGGL((q4_gemv_kernel<S, B, ARGMAX, true>), dim3(g.blocks), dim3(256), lds, stream, p);
+  else
+    hipLaunchKernelGGL((q4_gemv_kernel<S, B, ARGMAX, false>), dim3(g.blocks), dim3(256), lds, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t gemv_lds_bytes(int k, int B) { return (size_t)B * (k / 32) * (chunk_stride<1>() * 4 + 4); }
+size_t gemv_lds_bytes(int k, int B) { return gemv_lds(k, B); }
 
-int lmhead_partial_blocks(int64_t rows, int k, int B) {
-  const int S = B <= 2 ? 4 : (B <= 4 ? 2 : 1);
-  return gemv_grid(rows, k, S).blocks;
+namespace {
+
+// Rows per lane and step by batch size: B = 1 keeps the most bytes in flight.
+template <int B>
+constexpr int lmhead_rows_per_lane() { return B <= 2 ? 4 : B <= 4 ? 2 : 1; }
+
+template <int B>
+hipError_t run_lmhead_b(GemvParams p, int32_t* ids, float* max_logit, hipStream_t stream) {
+  constexpr int S = lmhead_rows_per_lane<B>();
+  const GemvGrid g = plan_gemv<S, B, true>(p.rows, p.k);
+  p.lshift = g.lshift;
+  p.chunk_lanes = g.chunk_lanes;
+  p.ids = ids;
+  p.max_logit = max_logit;
+  return launch_gemv<S, B, true>(p, g, stream);
 }
+
+}  // namespace
 
 hipError_t run_q4_gemv(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t rows,
                        int k, const uint16_t* x, void* y, int out_bf16, hipStream_t stream) {
@@ -237,14 +402,15 @@ hipError_t run_q4_gemv(const uint32_t* codes, const uint16_t* scales, const uint
   p.x = x;
   p.y = y;
   p.out_bf16 = out_bf16;
-  GemvGrid g = gemv_grid(rows, k, 4);
+  const GemvGrid g = plan_gemv<4, 1, false>(rows, k);
   p.lshift = g.lshift;
+  p.chunk_lanes = g.chunk_lanes;
   return launch_gemv<4, 1, false>(p, g, stream);
 }
 
 hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                              int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
-                             float* part_val, int32_t* part_idx, hipStream_t stream) {
+                             float* part_val, int32_t* part_idx, unsigned* done, hipStream_t stream) {
   GemvParams p{};
   p.codes = reinterpret_cast<const uint4*>(codes);
   p.scales = scales;
@@ -254,25 +420,18 @@ hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, cons
   p.x = X;
   p.part_val = part_val;
   p.part_idx = part_idx;
-  const int S = B <= 2 ? 4 : (B <= 4 ? 2 : 1);
-  GemvGrid g = gemv_grid(rows, k, S);
-  p.lshift = g.lshift;
-  hipError_t e;
+  p.done = done;
   switch (B) {
-    case 1: e = launch_gemv<4, 1, true>(p, g, stream); break;
-    case 2: e = launch_gemv<4, 2, true>(p, g, stream); break;
-    case 3: e = launch_gemv<2, 3, true>(p, g, stream); break;
-    case 4: e = launch_gemv<2, 4, true>(p, g, stream); break;
-    case 5: e = launch_gemv<1, 5, true>(p, g, stream); break;
-    case 6: e = launch_gemv<1, 6, true>(p, g, stream); break;
-    case 7: e = launch_gemv<1, 7, true>(p, g, stream); break;
-    case 8: e = launch_gemv<1, 8, true>(p, g, stream); break;
+    case 1: return run_lmhead_b<1>(p, ids, max_logit, stream);
+    case 2: return run_lmhead_b<2>(p, ids, max_logit, stream);
+    case 3: return run_lmhead_b<3>(p, ids, max_logit, stream);
+    case 4: return run_lmhead_b<4>(p, ids, max_logit, stream);
+    case 5: return run_lmhead_b<5>(p, ids, max_logit, stream);
+    case 6: return run_lmhead_b<6>(p, ids, max_logit, stream);
+    case 7: return run_lmhead_b<7>(p, ids, max_logit, stream);
+    case 8: return run_lmhead_b<8>(p, ids, max_logit, stream);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(1), dim3(256), 0, stream, part_val, part_idx, g.blocks, B,
-                     ids, max_logit);
-  return hipGetLastError();
 }
 
 }  // namespace q4moe

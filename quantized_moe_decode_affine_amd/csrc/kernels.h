@@ -14,12 +14,13 @@ int device_cu_count();
 
 // ---- GEMV family (gemv.hip)
 size_t gemv_lds_bytes(int k, int B);
-int lmhead_partial_blocks(int64_t rows, int k, int B);
+// The LM-head GEMV launches at most this many workgroups (one argmax partial each).
+constexpr int kMaxGemvBlocks = 2048;
 hipError_t run_q4_gemv(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t rows,
                        int k, const uint16_t* x, void* y, int out_bf16, hipStream_t stream);
 hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                              int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
-                             float* part_val, int32_t* part_idx, hipStream_t stream);
+                             float* part_val, int32_t* part_idx, unsigned* done, hipStream_t stream);
 
 // ---- Q4 matrices as seen by the kernels
 struct Q4Mat {

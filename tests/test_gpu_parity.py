@@ -122,6 +122,23 @@ def test_lmhead_planted_and_ties(B):
         assert int(ids[0]) == min(planted) and float(mx[0]) == 15.0 * k
 
 
+def test_lmhead_workspace_reuse(B):
+    """Consecutive calls on one workspace: each result is right and the arrival
+    counter (first word of the workspace) is back at zero after every call."""
+    rows, k = 20000, 2048
+    mat = synth.q4_matrix(60, 0, 0, 0, rows, k)
+    W = _q4(B, mat)
+    for batch in (1, 4):
+        ws = B.workspace(B.workspace_bytes(B.OP_LMHEAD, W=W, rows=batch), "cuda")
+        for call in range(3):
+            say(f"lmhead reuse B={batch} call={call}")
+            X = synth.token_rows(61 + call, batch, k)
+            ids, mx = B.lmhead_argmax(W, B.bf16_tensor(X), ws=ws)
+            _sync()
+            assert int(ws[:4].view(torch.int32).item()) == 0
+            _check_argmax(ids.cpu().numpy(), mx.cpu().numpy(), orc.lmhead_logits(*mat, X))
+
+
 def test_lmhead_full_vocab(B):
     """LM-head shape 151,936 x 2048, batch 1 and 4."""
     mat = synth.lm_head()

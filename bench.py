@@ -33,6 +33,24 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def decode_traffic():
+    """HBM bytes per decode-layer launch from the committed rocprofv3 counter
+    summary, or None when the decode kernel's sources changed since it was taken."""
+    import re
+
+    from quantized_moe_decode_affine_amd import profsum
+
+    path = os.path.join(ROOT, "profiles", "decode_layer_kernel_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"decode sources sha256: ([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic bytes per launch: ([0-9]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != profsum.decode_sources_sha256():
+        return None
+    return int(m_val.group(1))
+
+
 def cpu_baseline(stack_host, seed, budget_s=12.0):
     """The oracle (as it stands) on (step, layer) pairs of the decode workload until ~budget_s."""
     import numpy as np
@@ -64,6 +82,9 @@ def main():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and LM-head legs")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (the known-size reference that scales the "
+                         "byte counters of a rocprofv3 --pmc run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU)",
@@ -130,10 +151,12 @@ def main():
                    "us_per_layer": round(layer_us, 3),
                    "host_enqueue_us_per_step": round(host_s / args.steps * 1e6, 1),
                    "ids_repeat": digest_ok},
+        # the timed loop is one decode_layer_kernel launch per layer, back to back on one
+        # stream, so its event time / launches is the kernel's average launch duration
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "moe_ffn_decode (one layer call)",
-                     "unit_bytes": layer_bytes, "avg_us": round(layer_us, 3)},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
+                     "kernel": "decode_layer_kernel (moe_ffn_decode, one launch per layer)",
+                     "unit_bytes": layer_bytes, "avg_launch_us": round(layer_us, 3)},
     }
     host_layers = dict(stack.host)
     del stack
@@ -196,6 +219,16 @@ def main():
         log(f"lmhead: {lm}")
         del Ws
         torch.cuda.empty_cache()
+
+    if args.calib_copy > 0:
+        n = args.calib_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read and written per copy, 3 copies")
+        del src, dst
 
     if not args.no_cpu:
         log("timing the CPU oracle")

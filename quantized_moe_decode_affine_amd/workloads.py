@@ -67,8 +67,11 @@ class DecodeStack:
     def weight_bytes(self) -> int:
         return sum(d.nbytes for d in self.layers)
 
-    def step(self, s: int, record_ids: bool = False) -> None:
-        """Enqueue one decode step (all layers, in order) on the current stream."""
+    def step(self, s: int, record_ids: bool = False, events=None) -> None:
+        """Enqueue one decode step (all layers, in order) on the current stream.
+
+        `events`, when given, is a list of (start, end) torch.cuda.Event pairs,
+        one per layer, recorded around each layer's launch on the same stream."""
         stream = torch.cuda.current_stream().cuda_stream
         xs = self.x[s % self.n_steps]
         H = self.y.shape[1]
@@ -76,7 +79,11 @@ class DecodeStack:
         ids0, kk = self.ids.data_ptr(), self.ids.shape[1]
         ws, wsn = self.ws.data_ptr(), self.ws.numel()
         for l in range(self.n_layers):
+            if events is not None:
+                events[l][0].record()
             st = self._fn(self._refs[l], x0 + 2 * H * l, y0 + 4 * H * l, B.OUT_F32,
                           (ids0 + 4 * kk * l) if record_ids else None, None, ws, wsn, stream)
+            if events is not None:
+                events[l][1].record()
             if st != B.OK:
                 B._check("moe_ffn_decode", st)

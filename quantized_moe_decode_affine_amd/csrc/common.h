@@ -178,6 +178,11 @@ __device__ __forceinline__ void st_agent(float* p, float v) {
 __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Word 3 of a raw buffer resource (no format conversion, bounds-checked by
+// byte count) and the cache-policy bits of a device-scope (sc1) load.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kLoadDeviceScope = 16;
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Grid-wide barrier over `nblocks` co-resident workgroups.  State {count, gen}

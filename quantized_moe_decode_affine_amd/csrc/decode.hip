@@ -17,11 +17,12 @@
 //      the shared expert, split over the workgroup's waves, combined in LDS in
 //      a fixed order (no atomics); y is written once.
 //
-// No grid-wide barrier.  The logits carry the epoch themselves.  For the SwiGLU
-// activations each workgroup, when its phase A/B work is done and its
-// device-coherent stores have landed, publishes one flag word (the epoch); a
-// consumer polls the 256-ish flags, then reads the activations once with
-// device-coherent loads.  The epoch is agreed through
+// No grid-wide barrier: every value handed from one workgroup to another (the
+// router logits, the SwiGLU activations) is published as one 64-bit word
+// {epoch, fp32 bits} of this launch, so a consumer's load both reads the value
+// and tells whether it is there yet; only late words are polled again.  The
+// activations are produced 8 rows at a time, and the 8 words of a 64-byte line
+// are written by one store instruction of one wave.  The epoch is agreed through
 // per-group arrival counters in the workspace.  Every poll is bounded: a lost
 // flag yields a wrong result and a recorded timeout, never a hang.
 #include "kernels.h"
@@ -36,23 +37,19 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kEpochGroups = 8;
 constexpr int kPrefetchSlots = 3;   // down-row prefetch: slots per wave held in registers
-constexpr int kStageRounds = 3;     // phase C staging: 8-value blocks per thread with loads in flight (9 x 512 values in one pass)
 constexpr unsigned kPollLimit = 1u << 18;  // ~0.25 s of polling
 
 constexpr int kMaxBlocks = 1024;
-constexpr int kFlagStride = 16;  // 64 bytes
 
 struct DecodeWs {
   unsigned long long group_ctr[kEpochGroups][32];  // {epoch:hi32, arrivals:lo32}, one 256-byte slot each
   unsigned timeouts;
   unsigned pad[63];
   // Router logit of expert e: tag_logit[e][0] = {epoch:hi32, fp32 bits:lo32}.
-  // One 64-byte line per word (and per flag below): words that share a line
-  // are written by different CUs, and such partial-line stores slow their
-  // observers down severalfold.
+  // One 64-byte line per word: words that share a line would be written by
+  // different CUs, and such partial-line stores slow their observers down
+  // severalfold.
   unsigned long long tag_logit[kMaxExperts][8];
-  // flag_b[b][0] is the epoch once workgroup b's activations are visible.
-  unsigned flag_b[kMaxBlocks][kFlagStride];
 };
 
 struct DecodeParams {
@@ -63,43 +60,10 @@ struct DecodeParams {
   int32_t* ids_out;           // nullable [k]
   float* w_out;               // nullable [k]
   DecodeWs* ws;
-  float* act;                 // [k+1][I]: routed slots 0..k-1, shared slot k
+  unsigned long long* act;    // [k+1][I] tagged SwiGLU outputs: routed slots 0..k-1, shared slot k
   int lsH;                    // log2 lanes per row for rows of length hidden
   int lsI;                    // log2 lanes per row for rows of length inter
 };
-
-// Publish this workgroup's phase flag once every thread's device-coherent stores
-// have completed.
-__device__ __forceinline__ void publish_flag(unsigned* flag, uint32_t epoch) {
-  wait_vmem();
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One wave waits until flags[i][0] for i < n all equal `epoch` (bounded).
-__device__ __forceinline__ void wave_wait_flags(const unsigned (*flag_rows)[kFlagStride], int n, uint32_t epoch,
-                                                unsigned* timeouts) {
-  const unsigned* flags = &flag_rows[0][0];
-  const int lane = lane_id();
-  for (unsigned spins = 0;; ++spins) {
-    bool ready = true;
-    for (int base = 0; base < n; base += 4 * kWave) {
-      unsigned f[4];  // four loads in flight per lane (clamped index, results past n ignored)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        f[q] = __hip_atomic_load(const_cast<unsigned*>(flags + kFlagStride * min(base + q * kWave + lane, n - 1)), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ready &= base + q * kWave + lane >= n || f[q] == epoch;
-    }
-    if (__all(ready)) break;
-    if (spins == kPollLimit) {
-      if (lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
 
 // Stage a bf16 vector of n values (n % 32 == 0) into LDS: threads [t0, t0 + nthr)
 // take one 8-value block each per pass, chunk sums by a quad reduction (nthr and
@@ -144,31 +108,62 @@ __device__ __forceinline__ float store_split_block(const float (&v)[8], uint32_t
   return sum;
 }
 
-// Stage `nvec` fp32 vectors of n values each (contiguous, written by other
-// workgroups) as hi/lo bf16 parts: threads [t0, t0 + nthr) take 8-value blocks,
-// kStageRounds blocks per thread with all loads issued first.  nthr must be a
-// multiple of 4 (the 4 blocks of a chunk sit in one lane quad).
-__device__ __forceinline__ void stage_coherent_split(const float* src, int nvec, int n, uint32_t* vp, float* vs,
-                                                     int t0, int nthr) {
+// Stage `nvec` tagged fp32 vectors of n values each (contiguous, published by
+// other workgroups as {epoch, bits} words; nvec * n a multiple of 32) as hi/lo
+// bf16 parts.  Lane-contiguous 16-byte device-coherent loads (two words per
+// lane, all rounds in flight together); only pairs not yet complete are loaded
+// again (bounded; a timeout is counted).  A lane quad holds one 8-value block:
+// lanes 0-1 of the quad assemble its permuted pair words from their own values
+// and the matching ones of lanes 2-3; 16 lanes hold one 32-value chunk.
+constexpr int kTagRounds = 9;  // 16-byte loads per thread: 9 x 256 x 2 words = 4608 = 9 slots x 512
+
+__device__ __forceinline__ void stage_tagged_split(const unsigned long long* src, int nvec, int n, uint32_t* vp,
+                                                   float* vs, uint32_t epoch, unsigned* timeouts) {
   constexpr int ST = chunk_stride<2>();
-  const int t = threadIdx.x - t0;
-  if (t < 0 || t >= nthr) return;
-  const int nblk = (nvec * n) >> 3;
-  for (int base = 0; base < nblk; base += nthr * kStageRounds) {
-    float v[kStageRounds][8];
+  const int t = threadIdx.x, nthr = blockDim.x;
+  const int npairs = (nvec * n) >> 1;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned long long*>(src), 0, npairs * 16, kBufferRsrcWord3);
+  for (int base = 0; base < npairs; base += nthr * kTagRounds) {
+    uint4 w[kTagRounds];
+    auto fetch = [&](int r) __attribute__((always_inline)) {
+      const int q = base + r * nthr + t;  // past the end: the bounds check returns zeros, not used
+      w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, q * 16, 0, kLoadDeviceScope));
+    };
+    auto complete = [&](int r) __attribute__((always_inline)) { return w[r].y == epoch && w[r].w == epoch; };
 #pragma unroll
-    for (int r = 0; r < kStageRounds; ++r) {
-      const int b = base + r * nthr + t;
+    for (int r = 0; r < kTagRounds; ++r) fetch(r);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[r][j] = ld_agent(src + 8 * min(b, nblk - 1) + j);
+    for (int r = 0; r < kTagRounds; ++r) {
+      if (base + r * nthr + t >= npairs) continue;
+      for (unsigned spins = 0; !complete(r); ++spins) {
+        if (spins == kPollLimit) {
+          __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        fetch(r);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < kStageRounds; ++r) {
-      const int b = base + r * nthr + t;
-      float sum = 0.f;
-      if (b < nblk) sum = store_split_block(v[r], vp + (b >> 2) * ST + (b & 3) * 4);
-      sum = group_sum_rt(sum, 2);
-      if (b < nblk && (b & 3) == 0) vs[b >> 2] = sum;
+    for (int r = 0; r < kTagRounds; ++r) {
+      const int q = base + r * nthr + t;
+      const bool ok = q < npairs;
+      // this lane's values j0, j0 + 1 of block q / 4, j0 = 2 * (q % 4)
+      const float v0 = ok ? __uint_as_float(w[r].x) : 0.f, v1 = ok ? __uint_as_float(w[r].z) : 0.f;
+      const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+      const uint32_t l0 = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0)), l1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
+      const float part = (bf16_bits_to_f32(h0) + bf16_bits_to_f32(l0)) + (bf16_bits_to_f32(h1) + bf16_bits_to_f32(l1));
+      // values j0 + 4, j0 + 5 from the lane two places over in the quad
+      const uint32_t hh = dpp_u32<kDppQuadXor2>(h0 | h1 << 16), ll = dpp_u32<kDppQuadXor2>(l0 | l1 << 16);
+      if (ok && (q & 2) == 0) {
+        const int b = q >> 2, j0 = 2 * (q & 3);
+        uint32_t* dst = vp + (b >> 2) * ST + (b & 3) * 4 + j0;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (hh & 0xFFFFu) << 16, h1 | (hh >> 16) << 16);
+        *reinterpret_cast<uint2*>(dst + 16) = make_uint2(l0 | (ll & 0xFFFFu) << 16, l1 | (ll >> 16) << 16);
+      }
+      const float sum = group_sum_rt(part, 4);
+      if (ok && (q & 15) == 0) vs[q >> 4] = sum;
     }
   }
 }
@@ -193,45 +188,63 @@ __device__ __forceinline__ GateUpRef gate_up_ref(const Q4Mat& gm, const Q4Mat& u
   return r;
 }
 
-// NI independent (gate row, up row) items against the staged x, loads of all
-// items issued before any arithmetic; every lane of a row's lane group returns (g, u).
-template <int NI>
-__device__ __forceinline__ void gate_up_dot(const GateUpRef (&ref)[NI], const bool (&live)[NI], int H, int sub,
-                                            int L, int lsh, const uint32_t* vp, const float* vs, float2 (&out)[NI]) {
+// Gate/up of rows i0..i0+7 of one expert (e >= 0: routed expert e; e < 0: the
+// shared expert) over groups [g_lo, g_hi) against the staged x: lane l takes
+// row i0 + l/8 and groups g_lo + l%8 + 8t, with IT groups' loads in flight per
+// lane; every lane of a row's 8-lane group returns that row's partial (g, u).
+// Rows past I are read clamped and their results are not used.
+constexpr int kUnitRows = 8;
+
+template <int IT>
+__device__ __forceinline__ float2 unit_gate_up(const DecodeLayer& L, int e, int i0, int g_lo, int g_hi,
+                                               const uint32_t* vp, const float* vs) {
   constexpr int ST = chunk_stride<1>();
-  const int G = H >> 6;
-  float ag[NI], au[NI];
+  const int H = L.hidden, I = L.inter;
+  const int lane = lane_id();
+  const int row = min(i0 + (lane >> 3), I - 1), gl = lane & 7;
+  const GateUpRef ref =
+      e >= 0 ? gate_up_ref(L.gate, L.up, e, row, H, I) : gate_up_ref(L.sh_gate, L.sh_up, 0, row, H, I);
+  float ag = 0.f, au = 0.f;
+  for (int base = g_lo; base < g_hi; base += 8 * IT) {  // wave-uniform trip count
+    uint4 gc[IT][2], uc[IT][2];
+    uint32_t gs[IT], gb[IT], us[IT], ub[IT];
 #pragma unroll
-  for (int n = 0; n < NI; ++n) ag[n] = au[n] = 0.f;
-  for (int g = sub; g < G; g += L) {
-    uint4 g0[NI], g1[NI], u0[NI], u1[NI];
-    uint32_t gsb[NI], gbb[NI], usb[NI], ubb[NI];
+    for (int t = 0; t < IT; ++t) {
+      const int g = min(base + gl + 8 * t, g_hi - 1);  // groups past the range: loaded, not used
+      gc[t][0] = ref.gc[2 * g];
+      gc[t][1] = ref.gc[2 * g + 1];
+      uc[t][0] = ref.uc[2 * g];
+      uc[t][1] = ref.uc[2 * g + 1];
+      gs[t] = ref.gs[g];
+      gb[t] = ref.gb[g];
+      us[t] = ref.us[g];
+      ub[t] = ref.ub[g];
+    }
 #pragma unroll
-    for (int n = 0; n < NI; ++n) {
-      if (live[n]) {
-        g0[n] = ref[n].gc[2 * g];
-        g1[n] = ref[n].gc[2 * g + 1];
-        u0[n] = ref[n].uc[2 * g];
-        u1[n] = ref[n].uc[2 * g + 1];
-        gsb[n] = ref[n].gs[g];
-        gbb[n] = ref[n].gb[g];
-        usb[n] = ref[n].us[g];
-        ubb[n] = ref[n].ub[g];
-      } else {
-        g0[n] = g1[n] = u0[n] = u1[n] = make_uint4(0, 0, 0, 0);
-        gsb[n] = gbb[n] = usb[n] = ubb[n] = 0;
+    for (int t = 0; t < IT; ++t) {
+      const int g = base + gl + 8 * t;
+      const int gc_ = min(g, g_hi - 1);
+      const uint32_t* v = vp + 2 * gc_ * ST;
+      const float vsum = vs[2 * gc_] + vs[2 * gc_ + 1];
+      const float tg = affine_term(chunk_pdot<1>(gc[t][0], v) + chunk_pdot<1>(gc[t][1], v + ST), vsum, gs[t], gb[t]);
+      const float tu = affine_term(chunk_pdot<1>(uc[t][0], v) + chunk_pdot<1>(uc[t][1], v + ST), vsum, us[t], ub[t]);
+      if (g < g_hi) {
+        ag += tg;
+        au += tu;
       }
     }
-    const uint32_t* v = vp + 2 * g * ST;
-    const float vsum = vs[2 * g] + vs[2 * g + 1];
-#pragma unroll
-    for (int n = 0; n < NI; ++n) {
-      ag[n] += affine_term(chunk_pdot<1>(g0[n], v) + chunk_pdot<1>(g1[n], v + ST), vsum, gsb[n], gbb[n]);
-      au[n] += affine_term(chunk_pdot<1>(u0[n], v) + chunk_pdot<1>(u1[n], v + ST), vsum, usb[n], ubb[n]);
-    }
   }
-#pragma unroll
-  for (int n = 0; n < NI; ++n) out[n] = make_float2(group_sum_rt(ag[n], lsh), group_sum_rt(au[n], lsh));
+  return make_float2(group_sum_rt(ag, 3), group_sum_rt(au, 3));
+}
+
+// Publish the SwiGLU outputs of a unit's rows as tagged words: the 8 lanes that
+// hold rows i0..i0+7 (lane % 8 == 0) write one 64-byte line together.
+__device__ __forceinline__ void publish_unit(unsigned long long* act_slot, int i0, int I, float a, uint32_t epoch) {
+  const int lane = lane_id();
+  const int i = i0 + (lane >> 3);
+  if ((lane & 7) == 0 && i < I)
+    __hip_atomic_store(act_slot + i, ((unsigned long long)epoch << 32) | __float_as_uint(a), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Top-k of E logits by one wave, polling the epoch-tagged words that other
@@ -326,6 +339,8 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
   __shared__ int32_t s_ids[kMaxTopK + 1];
   __shared__ float s_w[kMaxTopK + 1];
   __shared__ float s_red[kWaves][kWave];
+  __shared__ float2 s_pair[kWaves / 2][kUnitRows];
+  __shared__ float2 s_third[kWaves - 1][kUnitRows];
   __shared__ uint32_t s_epoch;
 
   const int H = p.L.hidden, I = p.L.inter, E = p.L.n_experts, k = p.L.top_k;
@@ -339,8 +354,6 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
 
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
-  const int gwave = blockIdx.x * kWaves + wv;
-  const int nwaves = gridDim.x * kWaves;
 
   // ---- epoch of this launch: the arrivals of one group agree on its counter's
   // epoch field.  Taken by thread 0 once wave 0's first router loads are in
@@ -413,20 +426,31 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
       s_w[k] = 1.0f;
     }
   } else if (p.L.has_shared) {
-    // A, off the critical path: the shared expert's gate/up rows over waves 1-3 of every workgroup
-    const int aw = (wv - 1) * gridDim.x + blockIdx.x, nw = (kWaves - 1) * gridDim.x;
-    const int L = 1 << p.lsH, sub = lane & (L - 1), rsub = lane >> p.lsH, rpi = kWave >> p.lsH;
-    const int pair_items = (I + rpi - 1) / rpi;
-    for (int it = aw; it < pair_items; it += nw) {
-      const int i = it * rpi + rsub;
-      const bool live[1] = {i < I};
-      const GateUpRef ref[1] = {gate_up_ref(p.L.sh_gate, p.L.sh_up, 0, live[0] ? i : 0, H, I)};
-      float2 gu[1];
-      gate_up_dot<1>(ref, live, H, sub, L, p.lsH, xp, xs, gu);
-      if (live[0] && sub == 0) st_agent(p.act + (size_t)k * I + i, silu(gu[0].x) * gu[0].y);
+    // A, off the critical path: the shared expert's gate/up in 8-row units.  With
+    // at most one unit per workgroup, waves 1-3 split its groups in thirds and
+    // wave 1 adds the thirds after the barrier below; otherwise each wave takes
+    // whole units.
+    const int units = (I + kUnitRows - 1) / kUnitRows, G = H >> 6;
+    if (units <= (int)gridDim.x) {
+      if ((int)blockIdx.x < units) {
+        const int w = wv - 1;
+        const float2 gu = unit_gate_up<2>(p.L, -1, blockIdx.x * kUnitRows, w * G / 3, (w + 1) * G / 3, xp, xs);
+        if ((lane & 7) == 0) s_third[w][lane >> 3] = gu;
+      }
+    } else {
+      for (int u = (wv - 1) * gridDim.x + blockIdx.x; u < units; u += (kWaves - 1) * gridDim.x) {
+        const float2 gu = unit_gate_up<4>(p.L, -1, u * kUnitRows, 0, G, xp, xs);
+        publish_unit(p.act + (size_t)k * I, u * kUnitRows, I, silu(gu.x) * gu.y, epoch);
+      }
     }
   }
   __syncthreads();
+  if (p.L.has_shared && wv == 1 && (int)blockIdx.x < (I + kUnitRows - 1) / kUnitRows &&
+      (I + kUnitRows - 1) / kUnitRows <= (int)gridDim.x) {
+    const float2 a = s_third[0][lane >> 3], b = s_third[1][lane >> 3], c = s_third[2][lane >> 3];
+    const float g = (a.x + b.x) + c.x, up = (a.y + b.y) + c.y;
+    publish_unit(p.act + (size_t)k * I, blockIdx.x * kUnitRows, I, silu(g) * up, epoch);
+  }
 
   // prefetch the down rows this workgroup owns in phase C (its first row block)
   const int LI = 1 << p.lsI, subI = lane & (LI - 1), rsubI = lane >> p.lsI, rpiI = kWave >> p.lsI;
@@ -456,34 +480,30 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
   }
 
   {
-    const int L = 1 << p.lsH, sub = lane & (L - 1), rsub = lane >> p.lsH, rpi = kWave >> p.lsH;
-    const int per_slot = (I + rpi - 1) / rpi;
-    const int items = k * per_slot;
-    for (int it = gwave; it < items; it += 2 * nwaves) {
-      int i[2], j[2];
-      bool live[2];
-      GateUpRef ref[2];
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int t = it + n * nwaves;
-        j[n] = t / per_slot;
-        i[n] = (t - j[n] * per_slot) * rpi + rsub;
-        live[n] = t < items && i[n] < I;
-        ref[n] = gate_up_ref(p.L.gate, p.L.up, live[n] ? s_ids[j[n]] : 0, live[n] ? i[n] : 0, H, I);
+    // B: the routed experts' gate/up in 8-row units; the two waves of a pair
+    // split the groups, one wave adds the halves and publishes the line.
+    const int per_slot = (I + kUnitRows - 1) / kUnitRows;
+    const int units = k * per_slot;
+    const int pair = wv >> 1, half = wv & 1;
+    const int G = H >> 6, gmid = (G + 1) >> 1;
+    for (int ub = 2 * blockIdx.x; ub < units; ub += 2 * gridDim.x) {  // same trip count for every wave
+      const int u = ub + pair;
+      const bool live = u < units;
+      const int j = live ? u / per_slot : 0, i0 = live ? (u - j * per_slot) * kUnitRows : 0;
+      const float2 gu = unit_gate_up<2>(p.L, s_ids[j], i0, half ? gmid : 0, half ? G : gmid, xp, xs);
+      if (half && (lane & 7) == 0) s_pair[pair][lane >> 3] = gu;
+      __syncthreads();
+      if (!half && live) {
+        const float2 o = s_pair[pair][lane >> 3];
+        const float g = gu.x + o.x, up = gu.y + o.y;
+        publish_unit(p.act + (size_t)j * I, i0, I, silu(g) * up, epoch);
       }
-      float2 gu[2];
-      gate_up_dot<2>(ref, live, H, sub, L, p.lsH, xp, xs, gu);
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        if (live[n] && sub == 0) st_agent(p.act + (size_t)j[n] * I + i[n], silu(gu[n].x) * gu[n].y);
+      __syncthreads();
     }
   }
-  publish_flag(&p.ws->flag_b[blockIdx.x][0], epoch);
 
   // ------------------------------------------------------------ phase C
-  if (wv == 0) wave_wait_flags(p.ws->flag_b, gridDim.x, epoch, timeouts);
-  __syncthreads();
-  stage_coherent_split(p.act, nslot, I, ap, as, 0, kThreads);  // routed slots and the shared slot
+  stage_tagged_split(p.act, nslot, I, ap, as, epoch, timeouts);  // routed slots and the shared slot
   __syncthreads();
   {
     constexpr int ST = chunk_stride<2>();
@@ -559,7 +579,7 @@ size_t decode_lds(const DecodeLayer& L) {
 size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k) {
   (void)hidden;
   (void)n_experts;
-  return align256(sizeof(DecodeWs)) + align256((size_t)(top_k + 1) * inter * 4);
+  return align256(sizeof(DecodeWs)) + align256((size_t)(top_k + 1) * inter * 8);
 }
 
 size_t decode_lds_bytes(const DecodeLayer& L) { return decode_lds(L); }
@@ -576,7 +596,7 @@ hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, 
   char* w = static_cast<char*>(ws);
   p.ws = reinterpret_cast<DecodeWs*>(w);
   w += align256(sizeof(DecodeWs));
-  p.act = reinterpret_cast<float*>(w);
+  p.act = reinterpret_cast<unsigned long long*>(w);
   p.lsH = lanes_log2(L.hidden / kGroup);
   p.lsI = lanes_log2(L.inter / kGroup);
   const size_t lds = decode_lds(L);

@@ -322,7 +322,7 @@ struct GemvGrid {
 // from the occupancy of the instantiation that will run), so no workgroup
 // waits for another to finish; waves stride over the rows.
 GemvGrid gemv_grid(int64_t rows, int k, int S, int resident) {
-  const int C = k / 32, G = k / kGroup;
+  const int G = k / kGroup;
   GemvGrid g;
   g.chunk_lanes = G <= kWave && (G & (G - 1)) == 0;
   g.lshift = log2_floor(G < kWave ? G : kWave);

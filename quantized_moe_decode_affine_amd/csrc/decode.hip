@@ -45,11 +45,10 @@ struct DecodeWs {
   unsigned long long group_ctr[kEpochGroups][32];  // {epoch:hi32, arrivals:lo32}, one 256-byte slot each
   unsigned timeouts;
   unsigned pad[63];
-  // Router logit of expert e: tag_logit[e][0] = {epoch:hi32, fp32 bits:lo32}.
-  // One 64-byte line per word: words that share a line would be written by
-  // different CUs, and such partial-line stores slow their observers down
-  // severalfold.
-  unsigned long long tag_logit[kMaxExperts][8];
+  // Router logit of expert e: tag_logit[e] = {epoch:hi32, fp32 bits:lo32}.  The
+  // 8 words of a 64-byte line are written by one store instruction of one wave
+  // (lines shared by several writers slow their observers down severalfold).
+  unsigned long long tag_logit[kMaxExperts];
 };
 
 struct DecodeParams {
@@ -256,32 +255,38 @@ __device__ __forceinline__ void publish_unit(unsigned long long* act_slot, int i
 // Writes ids/weights (renormalised softmax of the kept logits) to LDS and, when
 // given, to ids_out/w_out.
 template <int V>
-__device__ __forceinline__ void wave_topk_tagged(const unsigned long long (*tags)[8], int E, int k, uint32_t epoch,
+__device__ __forceinline__ void wave_topk_tagged(const unsigned long long* tags, int E, int k, uint32_t epoch,
                                                  unsigned* timeouts, int32_t* s_ids, float* s_w, int32_t* ids_out,
                                                  float* w_out) {
+  static_assert(V % 2 == 0, "two tagged words per 16-byte load");
   const int lane = lane_id();
   uint32_t key[V];
   int id[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) id[j] = lane * V + j;
+  // lane-contiguous 16-byte device-coherent loads; words past E read as zeros (bounds check)
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned long long*>(tags), 0, E * 8, kBufferRsrcWord3);
   for (unsigned spins = 0;; ++spins) {
     bool ready = true;
-    unsigned long long t[V];
+    uint4 t[V / 2];
 #pragma unroll
-    for (int j = 0; j < V; ++j)  // all loads in flight together
-      t[j] = __hip_atomic_load(const_cast<unsigned long long*>(&tags[min(id[j], E - 1)][0]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    for (int h = 0; h < V / 2; ++h)  // all loads in flight together
+      t[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (lane * V + 2 * h) * 8, 0,
+                                                                          kLoadDeviceScope));
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      key[j] = (uint32_t)t[j];
-      ready &= id[j] >= E || (uint32_t)(t[j] >> 32) == epoch;
+    for (int h = 0; h < V / 2; ++h) {
+      key[2 * h] = t[h].x;
+      key[2 * h + 1] = t[h].z;
+      ready &= id[2 * h] >= E || t[h].y == epoch;
+      ready &= id[2 * h + 1] >= E || t[h].w == epoch;
     }
     if (__all(ready)) break;
     if (spins == kPollLimit) {
       if (lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(1);
   }
 #pragma unroll
   for (int j = 0; j < V; ++j) key[j] = id[j] < E ? float_key(__uint_as_float(key[j])) : 0u;
@@ -329,6 +334,14 @@ __device__ __forceinline__ void wave_topk_tagged(const unsigned long long (*tags
   }
 }
 
+// The shared-expert unit of workgroup b when each workgroup takes at most one
+// (units + router workgroups <= grid): the workgroups after the router ones, so
+// no workgroup computes both; -1 for none.
+__device__ __forceinline__ int shared_unit_of(int b, int grid, int rgroups, int units) {
+  const int su = b - rgroups;
+  return units + rgroups <= grid && su >= 0 && su < units ? su : -1;
+}
+
 struct DownPrefetch {
   uint4 c0, c1;
   uint32_t s, b;
@@ -341,6 +354,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
   __shared__ float s_red[kWaves][kWave];
   __shared__ float2 s_pair[kWaves / 2][kUnitRows];
   __shared__ float2 s_third[kWaves - 1][kUnitRows];
+  __shared__ float s_rlog[2 * kWaves];
   __shared__ uint32_t s_epoch;
 
   const int H = p.L.hidden, I = p.L.inter, E = p.L.n_experts, k = p.L.top_k;
@@ -356,9 +370,8 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
   const int wv = threadIdx.x / kWave;
 
   // ---- epoch of this launch: the arrivals of one group agree on its counter's
-  // epoch field.  Taken by thread 0 once wave 0's first router loads are in
-  // flight, so the two latencies overlap.
-  uint32_t my_epoch = 0;
+  // epoch field.  Taken by thread 0 once its first router loads are in flight,
+  // so the two latencies overlap.
   auto acquire_epoch = [&]() {
     const int g = blockIdx.x % kEpochGroups;
     const unsigned gsize = (gridDim.x - g + kEpochGroups - 1) / kEpochGroups;
@@ -366,50 +379,59 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
     const unsigned long long old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)old == gsize - 1)
       __hip_atomic_fetch_add(ctr, (1ull << 32) - gsize, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    my_epoch = (uint32_t)(old >> 32) + 1u;
-    s_epoch = my_epoch;
+    s_epoch = (uint32_t)(old >> 32) + 1u;
   };
 
   // ------------------------------------------------------------ phase A
-  if (wv == 0) {
-    // router rows e = blockIdx.x, blockIdx.x + gridDim.x, ...; x is read from global memory
-    bool have_epoch = false;
-    for (int it = blockIdx.x; it < E; it += gridDim.x) {
-      const uint4* r = reinterpret_cast<const uint4*>(p.L.router + (size_t)it * H);
-      const uint4* xv = reinterpret_cast<const uint4*>(p.x);
-      constexpr int kBatch = 4;  // row chunks in flight per lane
-      float acc0 = 0.f, acc1 = 0.f;
-      for (int c0 = 0; c0 < (H >> 3); c0 += kBatch * kWave) {
-        uint4 w[kBatch], v[kBatch];
+  // Router: workgroup b computes experts 8b..8b+7 (two per wave, x read from
+  // global memory) and wave 0 publishes them as one line of tagged words.
+  const int rgroups = (E + 7) / 8;
+  bool have_epoch = false;
+  for (int rb = blockIdx.x; rb < rgroups; rb += gridDim.x) {  // same trip count for the whole workgroup
+    const uint4* xv = reinterpret_cast<const uint4*>(p.x);
+    const uint4* r0 = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(rb * 8 + 2 * wv, E - 1) * H);
+    const uint4* r1 = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(rb * 8 + 2 * wv + 1, E - 1) * H);
+    constexpr int kBatch = 4;  // row chunks in flight per lane and row
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    for (int c0 = 0; c0 < (H >> 3); c0 += kBatch * kWave) {
+      uint4 w0[kBatch], w1[kBatch], v[kBatch];
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-          const int c = c0 + q * kWave + lane;
-          const bool ok = c < (H >> 3);
-          w[q] = ok ? r[c] : make_uint4(0, 0, 0, 0);
-          v[q] = ok ? xv[c] : make_uint4(0, 0, 0, 0);
-        }
-        if (!have_epoch) {
-          have_epoch = true;
-          if (lane == 0) acquire_epoch();
-        }
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-          acc0 = dot2_bf16(w[q].x, v[q].x, acc0);
-          acc1 = dot2_bf16(w[q].y, v[q].y, acc1);
-          acc0 = dot2_bf16(w[q].z, v[q].z, acc0);
-          acc1 = dot2_bf16(w[q].w, v[q].w, acc1);
-        }
+      for (int q = 0; q < kBatch; ++q) {
+        const int c = c0 + q * kWave + lane;
+        const bool ok = c < (H >> 3);
+        w0[q] = ok ? r0[c] : make_uint4(0, 0, 0, 0);
+        w1[q] = ok ? r1[c] : make_uint4(0, 0, 0, 0);
+        v[q] = ok ? xv[c] : make_uint4(0, 0, 0, 0);
       }
-      const float acc = group_sum_rt(acc0 + acc1, 6);
-      const uint32_t ep = __builtin_amdgcn_readfirstlane(my_epoch);  // lane 0 holds it
-      if (lane == 0)
-        __hip_atomic_store(&p.ws->tag_logit[it][0], ((unsigned long long)ep << 32) | __float_as_uint(acc),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!have_epoch) {
+        have_epoch = true;
+        if (threadIdx.x == 0) acquire_epoch();
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        a0 = dot2_bf16(w0[q].x, v[q].x, a0);
+        a1 = dot2_bf16(w0[q].y, v[q].y, a1);
+        a0 = dot2_bf16(w0[q].z, v[q].z, a0);
+        a1 = dot2_bf16(w0[q].w, v[q].w, a1);
+        b0 = dot2_bf16(w1[q].x, v[q].x, b0);
+        b1 = dot2_bf16(w1[q].y, v[q].y, b1);
+        b0 = dot2_bf16(w1[q].z, v[q].z, b0);
+        b1 = dot2_bf16(w1[q].w, v[q].w, b1);
+      }
     }
-    if (!have_epoch && lane == 0) acquire_epoch();
-  } else {
-    stage_bf16_parallel(p.x, H, xp, xs, kWave, kThreads - kWave);
+    const float la = group_sum_rt(a0 + a1, 6), lb = group_sum_rt(b0 + b1, 6);
+    if (lane == 0) {
+      s_rlog[2 * wv] = la;
+      s_rlog[2 * wv + 1] = lb;
+    }
+    __syncthreads();
+    if (wv == 0 && lane < 8 && rb * 8 + lane < E)
+      __hip_atomic_store(&p.ws->tag_logit[rb * 8 + lane], ((unsigned long long)s_epoch << 32) | __float_as_uint(s_rlog[lane]),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // s_rlog is reused
   }
+  if (!have_epoch && threadIdx.x == 0) acquire_epoch();
+  stage_bf16_parallel(p.x, H, xp, xs, 0, kThreads);
   __syncthreads();
   const uint32_t epoch = s_epoch;
 
@@ -431,10 +453,11 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
     // wave 1 adds the thirds after the barrier below; otherwise each wave takes
     // whole units.
     const int units = (I + kUnitRows - 1) / kUnitRows, G = H >> 6;
-    if (units <= (int)gridDim.x) {
-      if ((int)blockIdx.x < units) {
+    const int su = shared_unit_of(blockIdx.x, gridDim.x, rgroups, units);
+    if (units + rgroups <= (int)gridDim.x) {
+      if (su >= 0) {
         const int w = wv - 1;
-        const float2 gu = unit_gate_up<2>(p.L, -1, blockIdx.x * kUnitRows, w * G / 3, (w + 1) * G / 3, xp, xs);
+        const float2 gu = unit_gate_up<2>(p.L, -1, su * kUnitRows, w * G / 3, (w + 1) * G / 3, xp, xs);
         if ((lane & 7) == 0) s_third[w][lane >> 3] = gu;
       }
     } else {
@@ -445,37 +468,13 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
     }
   }
   __syncthreads();
-  if (p.L.has_shared && wv == 1 && (int)blockIdx.x < (I + kUnitRows - 1) / kUnitRows &&
-      (I + kUnitRows - 1) / kUnitRows <= (int)gridDim.x) {
-    const float2 a = s_third[0][lane >> 3], b = s_third[1][lane >> 3], c = s_third[2][lane >> 3];
-    const float g = (a.x + b.x) + c.x, up = (a.y + b.y) + c.y;
-    publish_unit(p.act + (size_t)k * I, blockIdx.x * kUnitRows, I, silu(g) * up, epoch);
-  }
-
-  // prefetch the down rows this workgroup owns in phase C (its first row block)
-  const int LI = 1 << p.lsI, subI = lane & (LI - 1), rsubI = lane >> p.lsI, rpiI = kWave >> p.lsI;
-  const int GI = I >> 6;
-  const bool pf_ok = GI == LI && (int)blockIdx.x * rpiI < H;
-  DownPrefetch pf[kPrefetchSlots];
-  {
-    const int n = blockIdx.x * rpiI + rsubI;
-    const int64_t mat_codes = (int64_t)H * (I >> 3), mat_groups = (int64_t)H * GI;
-#pragma unroll
-    for (int s = 0; s < kPrefetchSlots; ++s) {
-      const int j = wv + kWaves * s;
-      if (pf_ok && j < nslot && n < H) {
-        const int e = s_ids[j];
-        const Q4Mat& m = e >= 0 ? p.L.down : p.L.sh_down;
-        const int64_t oc = e >= 0 ? e * mat_codes : 0, og = e >= 0 ? e * mat_groups : 0;
-        const uint4* cr = reinterpret_cast<const uint4*>(m.codes + oc) + (int64_t)n * CI;
-        pf[s].c0 = cr[2 * subI];
-        pf[s].c1 = cr[2 * subI + 1];
-        pf[s].s = m.scales[og + (int64_t)n * GI + subI];
-        pf[s].b = m.biases[og + (int64_t)n * GI + subI];
-      } else {
-        pf[s].c0 = pf[s].c1 = make_uint4(0, 0, 0, 0);
-        pf[s].s = pf[s].b = 0;
-      }
+  if (p.L.has_shared && wv == 1) {
+    const int units = (I + kUnitRows - 1) / kUnitRows;
+    const int su = shared_unit_of(blockIdx.x, gridDim.x, rgroups, units);
+    if (units + rgroups <= (int)gridDim.x && su >= 0) {
+      const float2 a = s_third[0][lane >> 3], b = s_third[1][lane >> 3], c = s_third[2][lane >> 3];
+      const float g = (a.x + b.x) + c.x, up = (a.y + b.y) + c.y;
+      publish_unit(p.act + (size_t)k * I, su * kUnitRows, I, silu(g) * up, epoch);
     }
   }
 
@@ -499,6 +498,35 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
         publish_unit(p.act + (size_t)j * I, i0, I, silu(g) * up, epoch);
       }
       __syncthreads();
+    }
+  }
+
+  // prefetch the down rows this workgroup owns in phase C (its first row block);
+  // issued after phase B's loads so they do not compete with them, and hidden
+  // behind the activation handoff
+  const int LI = 1 << p.lsI, subI = lane & (LI - 1), rsubI = lane >> p.lsI, rpiI = kWave >> p.lsI;
+  const int GI = I >> 6;
+  const bool pf_ok = GI == LI && (int)blockIdx.x * rpiI < H;
+  DownPrefetch pf[kPrefetchSlots];
+  {
+    const int n = blockIdx.x * rpiI + rsubI;
+    const int64_t mat_codes = (int64_t)H * (I >> 3), mat_groups = (int64_t)H * GI;
+#pragma unroll
+    for (int s = 0; s < kPrefetchSlots; ++s) {
+      const int j = wv + kWaves * s;
+      if (pf_ok && j < nslot && n < H) {
+        const int e = s_ids[j];
+        const Q4Mat& m = e >= 0 ? p.L.down : p.L.sh_down;
+        const int64_t oc = e >= 0 ? e * mat_codes : 0, og = e >= 0 ? e * mat_groups : 0;
+        const uint4* cr = reinterpret_cast<const uint4*>(m.codes + oc) + (int64_t)n * CI;
+        pf[s].c0 = cr[2 * subI];
+        pf[s].c1 = cr[2 * subI + 1];
+        pf[s].s = m.scales[og + (int64_t)n * GI + subI];
+        pf[s].b = m.biases[og + (int64_t)n * GI + subI];
+      } else {
+        pf[s].c0 = pf[s].c1 = make_uint4(0, 0, 0, 0);
+        pf[s].s = pf[s].b = 0;
+      }
     }
   }
 

@@ -51,6 +51,25 @@ def decode_traffic():
     return int(m_val.group(1))
 
 
+def profiled_gemm_us():
+    """Per-layer time of the two grouped-GEMM launches of the prefill layer (gate/up
+    with SwiGLU, down with the routing weight), from the committed rocprofv3 kernel
+    trace; None when the kernel sources changed since the trace was taken."""
+    import re
+
+    from quantized_moe_decode_affine_amd import profsum
+
+    path = os.path.join(ROOT, "profiles", "kernels_decode40_prefill2048_lmhead_trace.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel sources sha256: ([0-9a-f]{64})", text)
+    m_row = re.search(r"\| `grouped_q4_gemm_kernel` \| (\d+) \| ([0-9.]+) \|", text)
+    if not m_hash or not m_row or m_hash.group(1) != profsum.all_sources_sha256():
+        return None
+    return 2.0 * float(m_row.group(2))  # two launches per layer
+
+
 def cpu_baseline(stack_host, seed, budget_s=12.0):
     """The oracle (as it stands) on (step, layer) pairs of the decode workload until ~budget_s."""
     import numpy as np
@@ -183,12 +202,18 @@ def main():
         p_us = ev0.elapsed_time(ev1) * 1e3 / reps
         flops = workloads.prefill_expert_flops()
         tfl = flops / (p_us * 1e-6) / 1e12
+        g_us = profiled_gemm_us()
         result["prefill"] = {"workload": "2,048-token chunk through one MoE layer (route, permute, grouped Q4 "
                                          "GEMMs with SwiGLU, combine)",
                              "us_per_layer": round(p_us, 2), "tokens_per_s": round(2048 / (p_us * 1e-6), 1),
                              "expert_gflop": round(flops / 1e9, 3),
                              "tflops_whole_layer": round(tfl, 2),
-                             "pct_of_bf16_peak_whole_layer": round(100 * tfl / BF16_PEAK_TFLOPS, 2)}
+                             "pct_of_bf16_peak_whole_layer": round(100 * tfl / BF16_PEAK_TFLOPS, 2),
+                             # expert GFLOP over the grouped-GEMM kernels' rocprofv3 time (both launches)
+                             "grouped_gemm_us_rocprof": None if g_us is None else round(g_us, 2),
+                             "tflops_grouped_gemm": None if g_us is None else round(flops / (g_us * 1e-6) / 1e12, 2),
+                             "pct_of_bf16_peak_grouped_gemm":
+                                 None if g_us is None else round(100 * flops / (g_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 2)}
         log(f"prefill: {p_us:.1f} us/layer, {tfl:.1f} TFLOP/s over the whole layer")
         del dl, X, ws, Y
         torch.cuda.empty_cache()

@@ -23,14 +23,25 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 DECODE_SOURCES = ("decode.hip", "common.h", "vecstage.h", "topk.h", "kernels.h")
+ALL_SOURCES = ("abi.hip", "decode.hip", "gemm.hip", "gemv.hip", "route.hip", "common.h", "kernels.h", "topk.h",
+               "vecstage.h")
 
 
-def decode_sources_sha256() -> str:
+def _sha256(names) -> str:
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in names:
         with open(os.path.join(PKG, "csrc", name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
+
+
+def decode_sources_sha256() -> str:
+    return _sha256(DECODE_SOURCES)
+
+
+def all_sources_sha256() -> str:
+    """Hash of every kernel source: a kernel trace taken from other sources is stale."""
+    return _sha256(ALL_SOURCES)
 
 
 def _short(name: str) -> str:
@@ -55,6 +66,7 @@ def stats_markdown(db: str, cmd: str) -> str:
     for k, v in sorted(times.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{k[:70]}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
                      f"{sum(v) / 1000:.3f} | {100 * sum(v) / total:.1f} |")
+    lines += ["", f"kernel sources sha256: {all_sources_sha256()}"]
     return "\n".join(lines) + "\n"
 
 

@@ -51,15 +51,22 @@ __device__ __forceinline__ uint32_t magic_pair_reg() {
   return m;
 }
 
+// kNibblePairMask in an SGPR, likewise.
+__device__ __forceinline__ uint32_t nibble_mask_reg() {
+  uint32_t m;
+  asm("s_mov_b32 %0, 0x000f000f" : "=s"(m));
+  return m;
+}
+
 // Two nibbles of `word` (positions j and j+4, j = shift/4) as bfloat16 (128+q) pair:
-// ((word >> shift) & kNibblePairMask) | kMagicPair in one v_and_or_b32 after the
-// shift.  (A VOP3 instruction on this target takes at most one literal, so
-// written in C the compiler splits it into v_and + v_or.)
+// ((word >> shift) & kNibblePairMask) | kMagicPair, one v_and_or_b32 after the
+// shift.  A VOP3 instruction on this target takes at most one literal, so both
+// constants come from registers; the and-or itself is ordinary code, so the
+// compiler sees the register it writes and keeps the wait states a matrix
+// instruction reading it needs (an asm-emitted write would hide that).
 __device__ __forceinline__ uint32_t nib_pair(uint32_t word, int shift) {
-  static_assert(kNibblePairMask == 0x000F000Fu && kMagicPair == 0x43004300u, "constants in the asm below");
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(word >> shift), "s"(kNibblePairMask), "v"(magic_pair_reg()));
-  return r;
+  static_assert(kNibblePairMask == 0x000F000Fu && kMagicPair == 0x43004300u, "constants in the asm above");
+  return ((word >> shift) & nibble_mask_reg()) | magic_pair_reg();
 }
 
 // acc + a.lo*b.lo + a.hi*b.hi on packed bfloat16 pairs, fp32 accumulate.

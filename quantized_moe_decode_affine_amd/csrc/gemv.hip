@@ -40,6 +40,78 @@ __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi)
   return v > bv || (v == bv && i < bi);
 }
 
+// Greedy argmax over a grid: every lane passes its running (max, lowest index)
+// per batch row (-inf for rows it does not hold).  The workgroup's best per
+// batch row is published device-coherently; the last workgroup to arrive
+// reduces all partials in index order and resets the arrival counter for the
+// next call.
+template <int B>
+__device__ __forceinline__ void argmax_epilogue(float (&best)[B], int32_t (&besti)[B], const GemvParams& p) {
+  const int lane = lane_id();
+  const int wpb = blockDim.x / kWave;
+  __shared__ float red_v[B][4];
+  __shared__ int32_t red_i[B][4];
+  __shared__ int s_last;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    float v = best[b];
+    int32_t i = besti[b];
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      float ov = __shfl_xor(v, m, kWave);
+      int32_t oi = __shfl_xor(i, m, kWave);
+      if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+    if (lane == 0) { red_v[b][threadIdx.x / kWave] = v; red_i[b][threadIdx.x / kWave] = i; }
+  }
+  __syncthreads();
+  if (threadIdx.x < B) {
+    const int b = threadIdx.x;
+    float v = red_v[b][0];
+    int32_t i = red_i[b][0];
+    for (int w = 1; w < wpb; ++w)
+      if (better(red_v[b][w], red_i[b][w], v, i)) { v = red_v[b][w]; i = red_i[b][w]; }
+    st_agent(p.part_val + (size_t)blockIdx.x * B + b, v);
+    __hip_atomic_store(p.part_idx + (size_t)blockIdx.x * B + b, i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  wait_vmem();  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (s_last) {
+    for (int b = 0; b < B; ++b) {
+      float v = -INFINITY;
+      int32_t i = 0x7FFFFFFF;
+      for (int j = threadIdx.x; j < (int)gridDim.x; j += blockDim.x) {
+        const float ov = ld_agent(p.part_val + (size_t)j * B + b);
+        const int32_t oi = __hip_atomic_load(p.part_idx + (size_t)j * B + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+      }
+#pragma unroll
+      for (int m = 1; m < kWave; m <<= 1) {
+        float ov = __shfl_xor(v, m, kWave);
+        int32_t oi = __shfl_xor(i, m, kWave);
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+      }
+      if (lane == 0) { red_v[0][threadIdx.x / kWave] = v; red_i[0][threadIdx.x / kWave] = i; }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float bv = red_v[0][0];
+        int32_t bi = red_i[0][0];
+        for (int w = 1; w < wpb; ++w)
+          if (better(red_v[0][w], red_i[0][w], bv, bi)) { bv = red_v[0][w]; bi = red_i[0][w]; }
+        p.ids[b] = bi;
+        if (p.max_logit) p.max_logit[b] = bv;
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <int S, int B, bool ARGMAX, bool CHUNK>
 __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
   extern __shared__ __align__(16) uint32_t smem[];
@@ -236,72 +308,141 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
     }
   }
 
-  if constexpr (ARGMAX) {
-    // Workgroup (max, lowest index) per batch row, published device-coherently;
-    // the last workgroup to arrive reduces all partials in index order and
-    // resets the arrival counter for the next call.
-    __shared__ float red_v[B][4];
-    __shared__ int32_t red_i[B][4];
-    __shared__ int s_last;
+  if constexpr (ARGMAX) argmax_epilogue<B>(best, besti, p);
+}
+
+typedef short mfma4_bf16_t __attribute__((ext_vector_type(4)));
+
+// Broadcast of quad lane I's value to its whole quad (DPP quad_perm [I,I,I,I]).
+template <int I>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, I * 0x55, 0xF, 0xF, false);
+}
+
+// LM head for 2..8 batch rows on the 4x4x4 bf16 MFMA (16 independent 4x4
+// blocks per wave instruction).  Block b = 4*rq + ks of a wave covers rows
+// base + 4*rq .. +3 and K groups gg + ks (gg = 0, 4, 8, ...): lane 4b+i
+// supplies row i's codes of that group (the 4 blocks of a row quad together read
+// 128 contiguous bytes of each row), lane 4b+j the activations of batch row j
+// (+4 for the second instruction set when B > 4), and lane 4b+j receives the 4
+// rows' sums for batch row j.  Per group a lane converts 8 code words once
+// (exact 128+q pairs, common.h) into 16 A operands, runs 16 MFMAs per set into a
+// fresh partial sum P (exact products, fp32 sums) and adds
+// s*P + (b - 128 s)*sum_x with its quad's scales and offsets broadcast by DPP;
+// the four groups' sums of a row meet in one lane at the end.  The codes of the
+// next two steps are in flight while the current one computes.
+template <int B>
+__global__ __launch_bounds__(256) void lmhead_mfma_kernel(GemvParams p) {
+  constexpr int NB = (B + 3) / 4;
+  extern __shared__ __align__(16) uint32_t smem[];
+  constexpr int ST = chunk_stride<1>();
+  const int C = p.k >> 5;
+  const int G = p.k >> 6;
+  uint32_t* vp = smem;
+  float* vs = reinterpret_cast<float*>(smem + B * C * ST);
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      float v = best[b];
-      int32_t i = besti[b];
+  for (int b = 0; b < B; ++b) stage_bf16_vector(p.x + (size_t)b * p.k, C, vp + b * C * ST, vs + b * C);
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int q = lane & 3;          // row of the block (A side) and batch column (B and D sides)
+  const int ks = (lane >> 2) & 3;  // group offset of the block
+  const int rq = lane >> 4;        // row quad of the block
+  int jb[NB];                      // this lane's batch row per set (clamped: columns past B are computed, unused)
 #pragma unroll
-      for (int m = 1; m < kWave; m <<= 1) {
-        float ov = __shfl_xor(v, m, kWave);
-        int32_t oi = __shfl_xor(i, m, kWave);
-        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  for (int h = 0; h < NB; ++h) jb[h] = min(4 * h + q, B - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  constexpr int kRowsPerWave = 16;
+
+  float best[NB];
+  int32_t besti[NB];
+#pragma unroll
+  for (int h = 0; h < NB; ++h) { best[h] = -INFINITY; besti[h] = 0x7FFFFFFF; }
+
+  struct Frag {
+    uint4 c0, c1;
+    uint32_t s, b;
+  };
+  for (int64_t base = wave * kRowsPerWave; base < p.rows; base += nwaves * kRowsPerWave) {
+    const int64_t row = min(base + 4 * rq + q, p.rows - 1);  // rows past the end: loaded, unused
+    const uint4* cr = p.codes + row * C;
+    const uint16_t* sr = p.scales + row * G;
+    const uint16_t* br = p.biases + row * G;
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int h = 0; h < NB; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int g = min(ks, G - 1);
+    const int g1 = min(4 + ks, G - 1);
+    Frag f{cr[2 * g], cr[2 * g + 1], sr[g], br[g]};
+    Frag f1{cr[2 * g1], cr[2 * g1 + 1], sr[g1], br[g1]};
+    for (int gg = 0; gg < G; gg += 4) {
+      const bool live = gg + ks < G;  // groups past the end: loaded (clamped), not added
+      const int gn = min(gg + 4 + ks, G - 1);
+      const int g2 = min(gg + 8 + ks, G - 1);
+      const Frag f2{cr[2 * g2], cr[2 * g2 + 1], sr[g2], br[g2]};  // two steps ahead
+      uint32_t pr[32];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint4& u = w < 4 ? f.c0 : f.c1;
+        const uint32_t word = (w & 3) == 0 ? u.x : (w & 3) == 1 ? u.y : (w & 3) == 2 ? u.z : u.w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[4 * w + j] = nib_pair(word, 4 * j);
       }
-      if (lane == 0) { red_v[b][threadIdx.x / kWave] = v; red_i[b][threadIdx.x / kWave] = i; }
-    }
-    __syncthreads();
-    if (threadIdx.x < B) {
-      const int b = threadIdx.x;
-      float v = red_v[b][0];
-      int32_t i = red_i[b][0];
-      for (int w = 1; w < wpb; ++w)
-        if (better(red_v[b][w], red_i[b][w], v, i)) { v = red_v[b][w]; i = red_i[b][w]; }
-      st_agent(p.part_val + (size_t)blockIdx.x * B + b, v);
-      __hip_atomic_store(p.part_idx + (size_t)blockIdx.x * B + b, i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    wait_vmem();  // this thread's partial stores have completed
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (s_last) {
-      for (int b = 0; b < B; ++b) {
-        float v = -INFINITY;
-        int32_t i = 0x7FFFFFFF;
-        for (int j = threadIdx.x; j < (int)gridDim.x; j += blockDim.x) {
-          const float ov = ld_agent(p.part_val + (size_t)j * B + b);
-          const int32_t oi = __hip_atomic_load(p.part_idx + (size_t)j * B + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (better(ov, oi, v, i)) { v = ov; i = oi; }
-        }
+      const uint32_t s4[4] = {quad_bcast<0>(f.s), quad_bcast<1>(f.s), quad_bcast<2>(f.s), quad_bcast<3>(f.s)};
+      const uint32_t b4[4] = {quad_bcast<0>(f.b), quad_bcast<1>(f.b), quad_bcast<2>(f.b), quad_bcast<3>(f.b)};
 #pragma unroll
-        for (int m = 1; m < kWave; m <<= 1) {
-          float ov = __shfl_xor(v, m, kWave);
-          int32_t oi = __shfl_xor(i, m, kWave);
-          if (better(ov, oi, v, i)) { v = ov; i = oi; }
+      for (int h = 0; h < NB; ++h) {
+        // pair word m of group g sits in chunk 2g + m/16 at offset m%16
+        const uint32_t* xv = vp + jb[h] * C * ST + 2 * g * ST;
+        f32x4_t P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int m = 2 * t;
+          const uint2 xa = *reinterpret_cast<const uint2*>(xv + (m >> 4) * ST + (m & 15));
+          P = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(mfma4_bf16_t, make_uint2(pr[m], pr[m + 1])),
+                                                   __builtin_bit_cast(mfma4_bf16_t, xa), P, 0, 0, 0);
         }
-        if (lane == 0) { red_v[0][threadIdx.x / kWave] = v; red_i[0][threadIdx.x / kWave] = i; }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-          float bv = red_v[0][0];
-          int32_t bi = red_i[0][0];
-          for (int w = 1; w < wpb; ++w)
-            if (better(red_v[0][w], red_i[0][w], bv, bi)) { bv = red_v[0][w]; bi = red_i[0][w]; }
-          p.ids[b] = bi;
-          if (p.max_logit) p.max_logit[b] = bv;
-        }
-        __syncthreads();
+        const float vsum = vs[jb[h] * C + 2 * g] + vs[jb[h] * C + 2 * g + 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[h][i] += live ? affine_term(P[i], vsum, s4[i], b4[i]) : 0.f;
       }
-      if (threadIdx.x == 0) __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      f = f1;
+      f1 = f2;
+      g = gn;
+    }
+    // the four group offsets of a row quad meet in the ks = 0 lanes; lane 16rq + j
+    // then holds rows base + 4rq + i (i = 0..3) for batch row 4h + j
+#pragma unroll
+    for (int h = 0; h < NB; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[h][i] += __shfl_xor(acc[h][i], 4, kWave);
+        acc[h][i] += __shfl_xor(acc[h][i], 8, kWave);
+      }
+    if (ks == 0) {
+#pragma unroll
+      for (int h = 0; h < NB; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t r = base + 4 * rq + i;
+          if (r < p.rows && better(acc[h][i], (int32_t)r, best[h], besti[h])) {
+            best[h] = acc[h][i];
+            besti[h] = (int32_t)r;
+          }
+        }
     }
   }
+  // every lane offers its candidate for the batch rows it holds, -inf for the others
+  float bv[B];
+  int32_t bi[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const bool mine = (b & 3) == q;
+    bv[b] = mine ? best[b >> 2] : -INFINITY;
+    bi[b] = mine ? besti[b >> 2] : 0x7FFFFFFF;
+  }
+  argmax_epilogue<B>(bv, bi, p);
 }
 
 int log2_floor(int64_t v) {
@@ -379,7 +520,32 @@ template <int B>
 constexpr int lmhead_rows_per_lane() { return B <= 2 ? 4 : B <= 4 ? 2 : 1; }
 
 template <int B>
+int lmhead_mfma_resident(size_t lds) {
+  static int cached = -1;
+  if (cached < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_mfma_kernel<B>, 256, lds) != hipSuccess || n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
+
+template <int B>
 hipError_t run_lmhead_b(GemvParams p, int32_t* ids, float* max_logit, hipStream_t stream) {
+  if constexpr (B >= 2) {
+    // 16 rows per wave step; one resident round of workgroups
+    const size_t lds = gemv_lds(p.k, B);
+    const int64_t wave_steps = (p.rows + 15) / 16;
+    int64_t blocks = (wave_steps + 3) / 4;
+    int64_t max_blocks = (int64_t)device_cu_count() * lmhead_mfma_resident<B>(lds);
+    if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // bounds the argmax partials
+    if (blocks > max_blocks) blocks = max_blocks;
+    p.ids = ids;
+    p.max_logit = max_logit;
+    hipLaunchKernelGGL((lmhead_mfma_kernel<B>), dim3((int)blocks), dim3(256), lds, stream, p);
+    return hipGetLastError();
+  }
   constexpr int S = lmhead_rows_per_lane<B>();
   const GemvGrid g = plan_gemv<S, B, true>(p.rows, p.k);
   p.lshift = g.lshift;

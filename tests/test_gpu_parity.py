@@ -96,7 +96,8 @@ def _check_argmax(ids, mx, logits):
 
 
 @pytest.mark.parametrize("rows,k,batch", [(5000, 2048, 1), (5000, 2048, 4), (4097, 512, 8), (300, 128, 2),
-                                          (1, 64, 1), (9000, 1024, 3)])
+                                          (1, 64, 1), (9000, 1024, 3), (77, 64, 5), (130, 192, 7),
+                                          (1, 128, 6), (2111, 2048, 2)])
 def test_lmhead_parity(B, rows, k, batch):
     say(f"lmhead rows={rows} k={k} B={batch}")
     mat = synth.q4_matrix(40 + batch, 0, 0, 0, rows, k)
@@ -120,6 +121,26 @@ def test_lmhead_planted_and_ties(B):
         ids, mx = B.lmhead_argmax(_q4(B, (c, s, b)), B.bf16_tensor(x))
         _sync()
         assert int(ids[0]) == min(planted) and float(mx[0]) == 15.0 * k
+
+
+@pytest.mark.parametrize("batch", [2, 4, 7])
+def test_lmhead_planted_batches(B, batch):
+    """Batched LM head: identical maximal rows in every batch row resolve to the
+    lowest index, with the exact maximum."""
+    rows, k = 3000, 256
+    codes, scales, biases = synth.q4_matrix(51, 0, 0, 0, rows, k)
+    x = np.full((batch, k), 0x3F80, dtype=np.uint16)
+    for planted in ((2999,), (64, 65, 2000), (7, 2500)):
+        say(f"lmhead planted B={batch} {planted}")
+        c, s, b = codes.copy(), scales.copy(), biases.copy()
+        for r in planted:
+            c[r] = 0xFFFFFFFF
+            s[r] = 0x3F80
+            b[r] = 0
+        ids, mx = B.lmhead_argmax(_q4(B, (c, s, b)), B.bf16_tensor(x))
+        _sync()
+        assert [int(v) for v in ids.cpu()] == [min(planted)] * batch
+        assert [float(v) for v in mx.cpu()] == [15.0 * k] * batch
 
 
 def test_lmhead_workspace_reuse(B):

@@ -51,6 +51,7 @@ struct GemmParams {
   int gather;
   int64_t P;                  // positions of the routed segments
   int K, G, Gp;
+  int bs_vec;                 // 1: every scale/bias row may be read 8 groups (16 bytes) at a time
   int N;                      // output columns (store/scale) or intermediate width (swiglu)
   Q4Mat W, W2;                // routed experts (W2 = up for swiglu), stacked
   int64_t w_codes_stride, w_groups_stride;
@@ -272,18 +273,52 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
     main_loop(std::integral_constant<int, 3>{});
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing (unused) loads before LDS is released
 
-  // ---- offset/bias term: sum_g (bias - 128 scale)[n][g] * rowsum_g[m], on MFMA with exact bf16 parts
-  for (int t = 0; t * 16 < p.Gp; ++t) {
+  // ---- offset/bias term: sum_g (bias - 128 scale)[n][g] * rowsum_g[m], on MFMA with exact bf16 parts.
+  // Each 16-group slice takes one round of loads (the 8 groups' biases and scales of this lane's
+  // column, 16 bytes each where aligned, and the rows' group-sum parts), issued one slice ahead.
+  struct CorrLoads {
+    uint4 bias[2], scale[2];  // [nb]: 8 groups' bf16 values
+    uint4 xa[MB][3];          // [mb][part]: 8 groups' bf16 row-sum parts
+  };
+  auto corr_load = [&](int t, CorrLoads& L) __attribute__((always_inline)) {
     const int gbase = t * 16 + 8 * lh;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      if (p.bs_vec) {
+        const bool any = gbase < p.G;  // with G % 8 == 0 a slice half is all real groups or all padding
+        L.bias[nb] = any ? *reinterpret_cast<const uint4*>(bbias[nb] + gbase) : make_uint4(0, 0, 0, 0);
+        L.scale[nb] = any ? *reinterpret_cast<const uint4*>(bscale[nb] + gbase) : make_uint4(0, 0, 0, 0);
+      } else {
+        uint32_t bv[8], sv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int g = min(gbase + j, p.G - 1);  // padding groups: loaded clamped, zeroed
+          bv[j] = gbase + j < p.G ? ld_global_u16(bbias[nb] + g) : 0u;
+          sv[j] = gbase + j < p.G ? ld_global_u16(bscale[nb] + g) : 0u;
+        }
+        L.bias[nb] = make_uint4(bv[0] | bv[1] << 16, bv[2] | bv[3] << 16, bv[4] | bv[5] << 16, bv[6] | bv[7] << 16);
+        L.scale[nb] = make_uint4(sv[0] | sv[1] << 16, sv[2] | sv[3] << 16, sv[4] | sv[5] << 16, sv[6] | sv[7] << 16);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb >= mblocks) continue;
+      const uint16_t* xr = p.xs + (int64_t)s_src[mb * 32 + ln] * 3 * p.Gp + gbase;
+#pragma unroll
+      for (int part_i = 0; part_i < 3; ++part_i) L.xa[mb][part_i] = *reinterpret_cast<const uint4*>(xr + part_i * p.Gp);
+    }
+  };
+  auto corr_apply = [&](const CorrLoads& L) __attribute__((always_inline)) {
     uint4 bc[2][2];  // [nb][hi/lo]
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t bw[4] = {L.bias[nb].x, L.bias[nb].y, L.bias[nb].z, L.bias[nb].w};
+      const uint32_t sw[4] = {L.scale[nb].x, L.scale[nb].y, L.scale[nb].z, L.scale[nb].w};
       uint32_t hi[8], lo[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int g = min(gbase + j, p.G - 1);  // unconditional loads; padding groups get c = 0
-        float c = bf16_bits_to_f32(ld_global_u16(bbias[nb] + g)) - 128.0f * bf16_bits_to_f32(ld_global_u16(bscale[nb] + g));
-        c = gbase + j < p.G ? c : 0.f;
+        const uint32_t bj = (bw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu, sj = (sw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        const float c = bf16_bits_to_f32(bj) - 128.0f * bf16_bits_to_f32(sj);  // padding groups: 0 - 0
         hi[j] = f32_to_bf16_bits(c);
         lo[j] = f32_to_bf16_bits(c - bf16_bits_to_f32(hi[j]));
       }
@@ -293,16 +328,24 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb >= mblocks) continue;
-      const uint16_t* xr = p.xs + (int64_t)s_src[mb * 32 + ln] * 3 * p.Gp + gbase;
 #pragma unroll
-      for (int part_i = 0; part_i < 3; ++part_i) {
-        const uint4 xa = *reinterpret_cast<const uint4*>(xr + part_i * p.Gp);
+      for (int part_i = 0; part_i < 3; ++part_i)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int hl = 0; hl < 2; ++hl)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xa), as_bf16x8(bc[nb][hl]), acc[mb][nb], 0, 0, 0);
-      }
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(L.xa[mb][part_i]), as_bf16x8(bc[nb][hl]),
+                                                                 acc[mb][nb], 0, 0, 0);
+    }
+  };
+  {
+    const int nt = (p.Gp + 15) / 16;
+    CorrLoads cur, nxt;
+    corr_load(0, cur);
+    for (int t = 0; t < nt; ++t) {
+      if (t + 1 < nt) corr_load(t + 1, nxt);
+      corr_apply(cur);
+      cur = nxt;
     }
   }
 
@@ -408,7 +451,12 @@ int grid_for(int64_t n, int block) {
 
 int pad16(int g) { return (g + 15) & ~15; }
 
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
 hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream) {
+  p.bs_vec = p.G % 8 == 0;
+  for (const Q4Mat* m : {&p.W, &p.W2, &p.X, &p.X2})
+    if (m->scales && (!aligned16(m->scales) || !aligned16(m->biases))) p.bs_vec = 0;
   p.n_tiles = (int)max_tiles;
   const int64_t tiles_rounded = (max_tiles + kXcd - 1) / kXcd * kXcd;
   const int64_t blocks = tiles_rounded * p.n_slices;

@@ -92,77 +92,74 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
 }
 
 // ---- stable counting sort by expert, in two launches
-// expert_rank_kernel: one workgroup per expert e scans all rows in order and
-// gives each row r with ids[r] == e its rank (the number of earlier rows of
-// expert e), so the order inside a segment is increasing r (stable) and does
-// not depend on scheduling; it also writes counts[e].
-// expert_scatter_kernel: every workgroup scans the counts into segment offsets
-// (workgroup 0 also writes them out) and places its rows at offset + rank.
+// chunk_rank_kernel: workgroup c takes rows [c*kRankChunk, (c+1)*kRankChunk) in
+// order and gives each row its rank among the chunk's earlier rows of the same
+// expert; it writes the chunk's histogram hist[c][e].
+// expert_scatter_kernel: workgroup c adds the counts of expert e in chunks
+// before c (so a row's rank counts every earlier row of its expert: the order
+// inside a segment is increasing r, stable and independent of scheduling), scans
+// the per-expert totals into segment offsets (workgroup 0 also writes them out)
+// and places its chunk's rows.
 
 constexpr int kRankThreads = 256;
-constexpr int kRankPer = 32;  // rows per thread per chunk (kept in registers)
+constexpr int kRankChunk = kMaxExperts;  // rows per chunk: one per thread of the scatter kernel
 
-// Exclusive prefix sum of v over the workgroup (kRankThreads threads); *total gets the sum.
-__device__ inline int32_t block_exclusive_scan(int32_t v, int32_t* s_wave, int32_t* total) {
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  int32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  if (lane == kWave - 1) s_wave[wave] = incl;
+__global__ __launch_bounds__(kRankThreads) void chunk_rank_kernel(const int32_t* __restrict__ ids, int64_t rows, int E,
+                                                                  int32_t* __restrict__ local_rank,
+                                                                  int32_t* __restrict__ hist) {
+  __shared__ int32_t s_cnt[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += kRankThreads) s_cnt[e] = 0;
   __syncthreads();
-  int32_t before = 0, sum = 0;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
+  const int64_t c0 = (int64_t)blockIdx.x * kRankChunk;
+  for (int sub = 0; sub < kRankChunk / kRankThreads; ++sub) {  // 256 rows at a time, in row order
+    const int64_t r = c0 + sub * kRankThreads + threadIdx.x;
+    const int e = r < rows ? ids[r] : -1;
+    const bool valid = e >= 0 && e < E;
+    const uint32_t key = valid ? (uint32_t)e : 1024u;  // E <= 1024: 11 key bits
+    uint64_t same = ~0ull;  // lanes of this wave holding the same key
 #pragma unroll
-  for (int w = 0; w < kRankThreads / kWave; ++w) {
-    before += w < wave ? s_wave[w] : 0;
-    sum += s_wave[w];
-  }
-  __syncthreads();  // s_wave may be reused by the next call
-  *total = sum;
-  return before + incl - v;
-}
-
-__global__ __launch_bounds__(kRankThreads) void expert_rank_kernel(const int32_t* __restrict__ ids, int64_t rows,
-                                                                   int32_t* __restrict__ rank,
-                                                                   int32_t* __restrict__ counts) {
-  __shared__ int32_t s_wave[kRankThreads / kWave];
-  const int e = blockIdx.x;
-  int32_t base = 0;
-  for (int64_t c0 = 0; c0 < rows; c0 += (int64_t)kRankThreads * kRankPer) {
-    const int64_t r0 = c0 + (int64_t)threadIdx.x * kRankPer;
-    uint32_t bits = 0;  // bit j: row r0 + j belongs to expert e
-#pragma unroll
-    for (int j = 0; j < kRankPer; ++j) {
-      const int64_t r = r0 + j;
-      bits |= (r < rows && ids[min(r, rows - 1)] == e ? 1u : 0u) << j;
+    for (int bit = 0; bit < 11; ++bit) {
+      const uint64_t ones = __ballot((key >> bit) & 1u);
+      same &= ((key >> bit) & 1u) ? ones : ~ones;
     }
-    int32_t total;
-    const int32_t before = block_exclusive_scan(__popc(bits), s_wave, &total);
-    uint32_t left = bits;
-    while (left) {
-      const int j = __builtin_ctz(left);
-      rank[r0 + j] = base + before + __popc(bits & ((1u << j) - 1u));
-      left &= left - 1u;
+    const int before_in_wave = __popcll(same & below);
+    const bool leader = (same & below) == 0;  // first lane of its key in this wave
+    for (int w = 0; w < kRankThreads / kWave; ++w) {  // the waves' rows are in order: wave 0 first
+      if (wave == w && valid) {
+        const int32_t base = s_cnt[e];
+        if (r < rows) local_rank[r] = base + before_in_wave;
+        // every lane of the group has read base before the group leader moves it on
+        __builtin_amdgcn_wave_barrier();
+        if (leader) s_cnt[e] = base + __popcll(same);
+      }
+      __syncthreads();
     }
-    base += total;
   }
-  if (threadIdx.x == 0) counts[e] = base;
+  for (int e = threadIdx.x; e < E; e += kRankThreads) hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
 __global__ __launch_bounds__(1024) void expert_scatter_kernel(const int32_t* __restrict__ ids, int64_t rows, int E,
-                                                              const int32_t* __restrict__ rank,
-                                                              const int32_t* __restrict__ counts,
+                                                              const int32_t* __restrict__ local_rank,
+                                                              const int32_t* __restrict__ hist, int nchunks,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ sorted_rows,
                                                               int32_t* __restrict__ inv_rows, GroupTiles tiles) {
   __shared__ int32_t s_c[kMaxExperts];
   __shared__ int32_t s_t[kMaxExperts];
-  const int i = threadIdx.x;  // blockDim.x == kMaxExperts
+  __shared__ int32_t s_before[kMaxExperts];  // rows of expert i in chunks before this workgroup's
+  const int i = threadIdx.x;  // blockDim.x == kMaxExperts == kRankChunk
   const bool tiled = tiles.table != nullptr;
   const int tr = tiled ? tiles.tile_rows : 1;
-  const int32_t c = i < E ? counts[i] : 0;
+  int32_t c = 0, before = 0;
+  if (i < E)
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int32_t h = hist[(int64_t)ch * E + i];
+      before += ch < (int)blockIdx.x ? h : 0;
+      c += h;
+    }
+  s_before[i] = before;
   s_c[i] = c;
   s_t[i] = (c + tr - 1) / tr;
   __syncthreads();
@@ -195,10 +192,11 @@ __global__ __launch_bounds__(1024) void expert_scatter_kernel(const int32_t* __r
       }
     }
   }
-  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += (int64_t)gridDim.x * blockDim.x) {
-    const int e = ids[r];
-    if (e < 0 || e >= E) continue;
-    const int32_t pos = (e > 0 ? s_c[e - 1] : 0) + rank[r];
+  {
+    const int64_t r = (int64_t)blockIdx.x * kRankChunk + threadIdx.x;  // this workgroup's chunk, one row per thread
+    const int e = r < rows ? ids[r] : -1;
+    if (e < 0 || e >= E) return;
+    const int32_t pos = (e > 0 ? s_c[e - 1] : 0) + s_before[e] + local_rank[r];
     sorted_rows[pos] = (int32_t)r;
     inv_rows[r] = pos;
     if (tiled) {
@@ -231,7 +229,8 @@ hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* 
 }
 
 size_t permute_workspace_bytes(int64_t rows, int n_experts) {
-  return align256((size_t)rows * 4) + align256((size_t)n_experts * 4);
+  const int64_t nchunks = (rows + kRankChunk - 1) / kRankChunk;
+  return align256((size_t)rows * 4) + align256((size_t)(nchunks > 0 ? nchunks : 1) * n_experts * 4);
 }
 
 int group_max_tiles(int64_t rows, int n_experts, int64_t extra_rows, int tile_rows) {
@@ -241,14 +240,20 @@ int group_max_tiles(int64_t rows, int n_experts, int64_t extra_rows, int tile_ro
 hipError_t run_permute(const int32_t* ids, int64_t rows, int E, int32_t* offsets, int32_t* sorted_rows,
                        int32_t* inv_rows, void* ws, const GroupTiles* tiles, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  int32_t* rank = reinterpret_cast<int32_t*>(w);
-  int32_t* counts = reinterpret_cast<int32_t*>(w + align256((size_t)rows * 4));
-  hipLaunchKernelGGL(expert_rank_kernel, dim3(E), dim3(kRankThreads), 0, stream, ids, rows, rank, counts);
+  const int nchunks = (int)((rows + kRankChunk - 1) / kRankChunk);
+  int32_t* local_rank = reinterpret_cast<int32_t*>(w);
+  int32_t* hist = reinterpret_cast<int32_t*>(w + align256((size_t)rows * 4));
+  GroupTiles none{};
+  if (nchunks == 0) {  // no rows: offsets and the tile table still get written
+    hipLaunchKernelGGL(expert_scatter_kernel, dim3(1), dim3(kMaxExperts), 0, stream, ids, rows, E, local_rank, hist,
+                       0, offsets, sorted_rows, inv_rows, tiles ? *tiles : none);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(chunk_rank_kernel, dim3(nchunks), dim3(kRankThreads), 0, stream, ids, rows, E, local_rank, hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  GroupTiles none{};
-  hipLaunchKernelGGL(expert_scatter_kernel, dim3(grid_for(rows, kMaxExperts)), dim3(kMaxExperts), 0, stream, ids,
-                     rows, E, rank, counts, offsets, sorted_rows, inv_rows, tiles ? *tiles : none);
+  hipLaunchKernelGGL(expert_scatter_kernel, dim3(nchunks), dim3(kMaxExperts), 0, stream, ids, rows, E, local_rank,
+                     hist, nchunks, offsets, sorted_rows, inv_rows, tiles ? *tiles : none);
   return hipGetLastError();
 }
 

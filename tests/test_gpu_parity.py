@@ -222,6 +222,27 @@ def test_permute_exact(B, T, k, E, seed):
     np.testing.assert_array_equal(inv.cpu().numpy(), r_inv)
 
 
+def test_permute_chunk_edges(B):
+    """Rows crossing several 1,024-row ranking chunks, a ragged last chunk, one
+    expert taking every row of a chunk and experts absent from whole chunks."""
+    rng = np.random.default_rng(7)
+    T, k, E = 1500, 3, 40
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[200:560, 0] = 17          # expert 17 dense across the first chunk boundary (row 1024 = token 341)
+    ids[700:, 1] = np.where(ids[700:, 0] != 39, 39, 38)
+    ids[ids == 5] = 6             # expert 5 never used
+    for t in range(T):            # keep the k ids of a token distinct
+        if len(set(ids[t])) < k:
+            ids[t] = rng.choice([e for e in range(E) if e != 5], size=k, replace=False)
+    say("permute chunk edges")
+    off, rows, inv = B.moe_permute(torch.from_numpy(ids).to(DEV), E)
+    _sync()
+    r_off, r_rows, r_inv = orc.permute(ids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), r_off)
+    np.testing.assert_array_equal(rows.cpu().numpy(), r_rows)
+    np.testing.assert_array_equal(inv.cpu().numpy(), r_inv)
+
+
 def test_permute_skewed(B):
     """Most tokens pick expert 3: one segment spans many rows, several are empty."""
     T, k, E = 700, 2, 12

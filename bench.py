@@ -218,6 +218,49 @@ def main():
         del dl, X, ws, Y
         torch.cuda.empty_cache()
 
+        # ------------------------- wider layers: 512 routed experts, top-10, 4,096-token chunks
+        log("building 8 wide layers (512 routed + 1 shared experts, top-10)")
+        wide = dict(n_experts=512, top_k=10)
+        wstack = workloads.DecodeStack(seed=5, n_layers=8, n_steps=8, device=dev, **wide)
+        for s in range(2):
+            wstack.step(s)
+        torch.cuda.synchronize()
+        wsteps = 16
+        ev0.record()
+        for s in range(wsteps):
+            wstack.step(s)
+        ev1.record()
+        torch.cuda.synchronize()
+        w_layer_us = ev0.elapsed_time(ev1) * 1e3 / (wsteps * wstack.n_layers)
+        w_bytes = workloads.decode_layer_bytes(**wide)
+        dl = wstack.layers[0]
+        T4 = 4096
+        X = B.bf16_tensor(synth.token_rows(5, T4, synth.HIDDEN), dev)
+        ws = B.workspace(B.workspace_bytes(B.OP_FFN_PREFILL, dl, rows=T4), dev)
+        Y = torch.empty((T4, synth.HIDDEN), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
+        torch.cuda.synchronize()
+        reps = 5
+        ev0.record()
+        for _ in range(reps):
+            B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        w_p_us = ev0.elapsed_time(ev1) * 1e3 / reps
+        w_flops = workloads.prefill_expert_flops(T=T4, top_k=10)
+        result["wide"] = {
+            "workload": "512 routed + 1 shared experts, top-10 (hidden 2048, inter 512, affine Q4 g64): "
+                        "8-layer batch-1 decode loop and one 4,096-token prefill chunk",
+            "decode_us_per_layer": round(w_layer_us, 3), "decode_bytes_per_layer": w_bytes,
+            "decode_GB_s": round(w_bytes / (w_layer_us * 1e-6) / 1e9, 1),
+            "decode_pct_of_hbm_peak": round(100 * w_bytes / (w_layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "prefill_us_per_layer": round(w_p_us, 2), "prefill_expert_gflop": round(w_flops / 1e9, 3),
+            "prefill_tflops_whole_layer": round(w_flops / (w_p_us * 1e-6) / 1e12, 2)}
+        log(f"wide: {result['wide']}")
+        del wstack, dl, X, ws, Y
+        torch.cuda.empty_cache()
+
         # ------------------------------------------------------------ LM head
         log("building the LM head (two copies)")
         mat = synth.lm_head()

@@ -332,6 +332,22 @@ def test_decode_config1(B):
     assert int(ws[2048:2052].cpu().view(torch.int32)[0]) == 0
 
 
+def test_decode_512_experts_top10(B):
+    """Wider router at decode: hidden 2048, 512 routed experts + 1 shared, top-10."""
+    say("decode 512 experts top-10: generating")
+    layer = synth.moe_layer(92, 0, synth.HIDDEN, synth.INTER, 512, 10)
+    dl = B.DeviceLayer(layer)
+    ws = B.workspace(B.workspace_bytes(B.OP_FFN_DECODE, dl))
+    n_exact = 0
+    for step in range(6):
+        say(f"decode 512 experts top-10 step {step}")
+        err, exact = _decode_check(B, layer, dl, synth.hidden_vector(92, step, 0), ws=ws)
+        assert err <= 1e-5
+        n_exact += exact
+    assert n_exact >= 4
+    assert int(ws[2048:2052].cpu().view(torch.int32)[0]) == 0
+
+
 # ----------------------------------------------------------- MoE prefill --
 
 def _prefill_check(B, layer, dl, X, with_bf16=True):
@@ -398,4 +414,16 @@ def test_prefill_config3(B):
     say("prefill full chunk: running")
     err, worst = _prefill_check(B, layer, dl, X)
     say(f"prefill full chunk rel_l2={err:.3e} worst={worst:.3e}")
+    assert err <= REL_L2_TOL and worst <= 2 * REL_L2_TOL
+
+
+def test_prefill_4096_tokens_512_experts_top10(B):
+    """A 4,096-token chunk through a layer with 512 routed experts + 1 shared, top-10."""
+    say("prefill 4096 tokens, 512 experts top-10: generating")
+    layer = synth.moe_layer(93, 0, synth.HIDDEN, synth.INTER, 512, 10)
+    dl = B.DeviceLayer(layer)
+    X = synth.token_rows(93, 4096, synth.HIDDEN)
+    say("prefill 4096 tokens, 512 experts top-10: running")
+    err, worst = _prefill_check(B, layer, dl, X, with_bf16=False)
+    say(f"prefill 4096 tokens rel_l2={err:.3e} worst={worst:.3e}")
     assert err <= REL_L2_TOL and worst <= 2 * REL_L2_TOL

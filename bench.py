@@ -177,6 +177,39 @@ def main():
                      "kernel": "decode_layer_kernel (moe_ffn_decode, one launch per layer)",
                      "unit_bytes": layer_bytes, "avg_launch_us": round(layer_us, 3)},
     }
+    if not args.no_extra:
+        # ------------------------------------------- batched decode (several requests per step)
+        stack.enable_batch(8, dev)
+        expert_bytes = workloads.decode_layer_bytes(top_k=1, shared=False, n_experts=0, out_bytes=0) - 2 * synth.HIDDEN
+        batch = {}
+        for nb in (1, 4, 8):
+            for s in range(2):
+                stack.step_batch(s, nb)
+            torch.cuda.synchronize()
+            bsteps = 16
+            ev0.record()
+            for s in range(bsteps):
+                stack.step_batch(s, nb)
+            ev1.record()
+            torch.cuda.synchronize()
+            b_us = ev0.elapsed_time(ev1) * 1e3 / (bsteps * args.layers)
+            stack.step_batch(0, nb, record_ids=True)
+            torch.cuda.synchronize()
+            ids_nb = stack.idsb[:, :nb].cpu().numpy()
+            distinct = float(np.mean([len(np.unique(ids_nb[l])) for l in range(args.layers)]))
+            # algorithmic bytes: each distinct expert and the shared one once, the router, inputs and outputs
+            b_bytes = (distinct + 1) * expert_bytes + synth.N_EXPERTS * synth.HIDDEN * 2 + nb * synth.HIDDEN * 6
+            batch[f"B{nb}"] = {"us_per_layer": round(b_us, 3), "tokens_per_s": round(nb / (b_us * 1e-6 * args.layers), 1),
+                               "distinct_experts_per_layer": round(distinct, 2),
+                               "GB_s": round(b_bytes / (b_us * 1e-6) / 1e9, 1),
+                               "pct_of_hbm_peak": round(100 * b_bytes / (b_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        result["decode_batch"] = dict(
+            workload=f"{args.layers}-layer decode loop with B requests per step (moe_ffn_decode_batch, three "
+                     f"launches per layer); tokens_per_s counts all B rows; bytes = distinct + shared experts, "
+                     f"router, inputs and outputs",
+            batch1_kernel_tokens_per_s=round(1 / (layer_us * 1e-6 * args.layers), 1), **batch)
+        log(f"decode batch: {batch}")
+
     host_layers = dict(stack.host)
     del stack
     torch.cuda.empty_cache()

@@ -59,7 +59,8 @@ enum {
   Q4MOE_OP_PERMUTE = 3,
   Q4MOE_OP_FFN_DECODE = 4,
   Q4MOE_OP_FFN_PREFILL = 5,
-  Q4MOE_OP_LMHEAD = 6
+  Q4MOE_OP_LMHEAD = 6,
+  Q4MOE_OP_FFN_DECODE_BATCH = 7
 };
 
 /* A Q4 matrix, or `count` stacked matrices of the same shape. */
@@ -150,6 +151,25 @@ int moe_permute(const int32_t* ids, int64_t T, int32_t top_k, int32_t n_experts,
 int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int out_dtype,
                    int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
                    q4moe_stream stream);
+
+/*
+ * B tokens, one per request, through the MoE layer in one decode step
+ * (lily-qwen3.8-flash-next, "Running it": up to four requests by default
+ * decode together), 1 <= B <= 8: row b of Y equals moe_ffn_decode on X[b] up
+ * to rounding (intermediates stay fp32).  X bf16 [B][hidden]; Y fp32 or bf16
+ * [B][hidden]; ids_out int32 [B][top_k] and w_out fp32 [B][top_k] may be null.
+ * Each expert chosen by any of the tokens is read once for all of them.  Runs
+ * as four launches (router; top-k and the step's expert plan; gate/up with
+ * SwiGLU; down with the weighted sum) that hand values over only through the
+ * Q4MOE_OP_FFN_DECODE_BATCH workspace (B), which needs no initialisation;
+ * calls that share a workspace must not overlap.  Shapes
+ * whose staged vectors exceed 64 KB of LDS (B * hidden * 21 / 8 bytes of
+ * inputs, or (top_k + 1) * inter * 37 / 8 bytes of SwiGLU outputs for one
+ * token) return Q4MOE_EUNSUPPORTED.
+ */
+int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t B, void* Y,
+                         int out_dtype, int32_t* ids_out, float* w_out, void* workspace,
+                         size_t workspace_bytes, q4moe_stream stream);
 
 /*
  * T tokens through the MoE layer (a prefill chunk, 2,048 tokens in the

@@ -18,10 +18,10 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4moe.s
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 OUT_F32, OUT_BF16 = 0, 1
-OP_GEMV, OP_GEMM, OP_ROUTE, OP_PERMUTE, OP_FFN_DECODE, OP_FFN_PREFILL, OP_LMHEAD = range(7)
+OP_GEMV, OP_GEMM, OP_ROUTE, OP_PERMUTE, OP_FFN_DECODE, OP_FFN_PREFILL, OP_LMHEAD, OP_FFN_DECODE_BATCH = range(8)
 
-EXPORTS = ("q4_gemv", "q4_gemm", "moe_route_topk", "moe_permute", "moe_ffn_decode", "moe_ffn_prefill",
-           "lmhead_argmax", "q4moe_workspace_bytes", "q4moe_strerror")
+EXPORTS = ("q4_gemv", "q4_gemm", "moe_route_topk", "moe_permute", "moe_ffn_decode", "moe_ffn_decode_batch",
+           "moe_ffn_prefill", "lmhead_argmax", "q4moe_workspace_bytes", "q4moe_strerror")
 
 
 class Q4Error(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "moe_route_topk": [vp, i32, i32, vp, i64, i32, vp, vp, vp, sz, vp],
         "moe_permute": [vp, i64, i32, i32, vp, vp, vp, vp, sz, vp],
         "moe_ffn_decode": [pl, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp],
+        "moe_ffn_decode_batch": [pl, vp, i64, vp, ctypes.c_int, vp, vp, vp, sz, vp],
         "moe_ffn_prefill": [pl, vp, i64, vp, ctypes.c_int, vp, sz, vp],
         "lmhead_argmax": [pm, vp, i64, vp, vp, vp, sz, vp],
     }
@@ -231,6 +232,19 @@ def moe_ffn_decode(layer: DeviceLayer, x: torch.Tensor, out_dtype: int = OUT_F32
                                                            _ptr(ids_out), _ptr(w_out), _ptr(ws), ws.numel(),
                                                            _stream()))
     return y
+
+
+def moe_ffn_decode_batch(layer: DeviceLayer, X: torch.Tensor, out_dtype: int = OUT_F32, out=None,
+                         ids_out: Optional[torch.Tensor] = None, w_out: Optional[torch.Tensor] = None,
+                         ws: Optional[torch.Tensor] = None):
+    B = X.shape[0]
+    Y = _out((B, layer.hidden), out_dtype, X.device, out)
+    if ws is None:
+        ws = workspace(workspace_bytes(OP_FFN_DECODE_BATCH, layer, rows=B), X.device)
+    _check("moe_ffn_decode_batch", load_library().moe_ffn_decode_batch(
+        ctypes.byref(layer.struct), _ptr(X), B, _ptr(Y), out_dtype, _ptr(ids_out), _ptr(w_out), _ptr(ws),
+        ws.numel(), _stream()))
+    return Y
 
 
 def moe_ffn_prefill(layer: DeviceLayer, X: torch.Tensor, out_dtype: int = OUT_F32, out=None,

@@ -127,6 +127,11 @@ size_t q4moe_workspace_bytes(int op, const q4moe_layer* layer, const q4moe_matri
       if (layer_check(layer, &d) != Q4MOE_OK) return 0;
       return q4moe::prefill_workspace_bytes(rows, d.hidden, d.inter, d.n_experts, d.top_k, d.has_shared);
     }
+    case Q4MOE_OP_FFN_DECODE_BATCH: {
+      q4moe::DecodeLayer d;
+      if (layer_check(layer, &d) != Q4MOE_OK || rows < 1 || rows > q4moe::kMaxBatch) return 0;
+      return q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)rows);
+    }
     case Q4MOE_OP_LMHEAD:
       if (!W) return 0;
       return lmhead_ws(W->count * W->n, W->k, rows);
@@ -207,6 +212,24 @@ int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int o
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
     return hip_status(q4moe::run_moe_ffn_decode(d, x, y, out_dtype == Q4MOE_OUT_BF16, ids_out, w_out, workspace,
                                                 (hipStream_t)stream));
+  } catch (...) {
+    return Q4MOE_EHIP;
+  }
+}
+
+int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t B, void* Y, int out_dtype,
+                         int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
+                         q4moe_stream stream) {
+  try {
+    q4moe::DecodeLayer d;
+    const int st = layer_check(layer, &d);
+    if (st != Q4MOE_OK) return st;
+    if (!X || !aligned(X, 16) || B < 1 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
+    if (B > q4moe::kMaxBatch || !q4moe::decode_batch_supported(d, (int)B, kMaxDynLds)) return Q4MOE_EUNSUPPORTED;
+    const size_t need = q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)B);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
+    return hip_status(q4moe::run_moe_ffn_decode_batch(d, X, (int)B, Y, out_dtype == Q4MOE_OUT_BF16, ids_out, w_out,
+                                                      workspace, kMaxDynLds, (hipStream_t)stream));
   } catch (...) {
     return Q4MOE_EHIP;
   }

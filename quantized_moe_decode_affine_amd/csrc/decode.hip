@@ -290,47 +290,10 @@ __device__ __forceinline__ void wave_topk_tagged(const unsigned long long* tags,
   }
 #pragma unroll
   for (int j = 0; j < V; ++j) key[j] = id[j] < E ? float_key(__uint_as_float(key[j])) : 0u;
-  // insertion sort, descending key; ties keep the lower id first (ids ascend with j)
-#pragma unroll
-  for (int a = 1; a < V; ++a)
-#pragma unroll
-    for (int b = a; b > 0; --b) {
-      const bool sw = key[b] > key[b - 1];
-      const uint32_t tk = key[b];
-      const int ti = id[b];
-      key[b] = sw ? key[b - 1] : key[b];
-      id[b] = sw ? id[b - 1] : id[b];
-      key[b - 1] = sw ? tk : key[b - 1];
-      id[b - 1] = sw ? ti : id[b - 1];
-    }
-  float top = 0.f, my_val = 0.f;
-  int my_id = 0;
-  for (int r = 0; r < k; ++r) {
-    const uint32_t m = wave_max_u32(key[0]);
-    const int src = __builtin_ctzll(__ballot(key[0] == m));
-    const int sel = __builtin_amdgcn_readlane(id[0], src);
-    if (lane == src) {
-#pragma unroll
-      for (int j = 0; j + 1 < V; ++j) {
-        key[j] = key[j + 1];
-        id[j] = id[j + 1];
-      }
-      key[V - 1] = 0u;
-    }
-    const float v = key_float(m);
-    if (r == 0) top = v;
-    if (lane == r) {
-      my_id = sel;
-      my_val = v;
-    }
-  }
-  const float ex = lane < k ? expf(my_val - top) : 0.f;
-  const float sum = group_sum_rt(ex, 6);
+  wave_topk_keys<V>(key, id, k, s_ids, s_w);
   if (lane < k) {
-    s_ids[lane] = my_id;
-    s_w[lane] = ex / sum;
-    if (ids_out) ids_out[lane] = my_id;
-    if (w_out) w_out[lane] = ex / sum;
+    if (ids_out) ids_out[lane] = s_ids[lane];
+    if (w_out) w_out[lane] = s_w[lane];
   }
 }
 

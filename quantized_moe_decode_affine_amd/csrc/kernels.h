@@ -41,6 +41,13 @@ size_t decode_lds_bytes(const DecodeLayer& L);
 hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_bf16, int32_t* ids_out,
                               float* w_out, void* ws, hipStream_t stream);
 
+// ---- batched decode, 1..kMaxBatch tokens (decode_batch.hip)
+constexpr int kMaxBatch = 8;
+size_t decode_batch_workspace_bytes(int n_experts, int top_k, int inter, int B);
+bool decode_batch_supported(const DecodeLayer& L, int B, size_t max_lds);
+hipError_t run_moe_ffn_decode_batch(const DecodeLayer& L, const uint16_t* X, int B, void* y, int out_bf16,
+                                    int32_t* ids_out, float* w_out, void* ws, size_t max_lds, hipStream_t stream);
+
 // ---- routing and permutation (route.hip)
 size_t route_workspace_bytes(int64_t T, int n_experts);
 hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* X, int64_t T, int k,

@@ -76,6 +76,7 @@ __global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+template <int V>
 __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
                                                         int32_t* __restrict__ ids, float* __restrict__ weights) {
   __shared__ int32_t s_ids[4][kMaxTopK];
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
   const int wave = threadIdx.x / kWave;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
-  wave_topk(logits + t * E, E, k, s_ids[wave], s_w[wave]);
+  wave_topk_sorted<V>(logits + t * E, E, k, s_ids[wave], s_w[wave]);
   const int lane = lane_id();
   if (lane < k) {
     ids[t * k + lane] = s_ids[wave][lane];
@@ -223,8 +224,14 @@ hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* 
   hipLaunchKernelGGL(router_logits_kernel, grid, dim3(512), 0, stream, router, X, T, E, H, logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, logits, T, E, k, ids,
-                     weights);
+  const dim3 tgrid((unsigned)((T + 3) / 4)), tthreads(256);
+  if (E <= 4 * kWave)
+    hipLaunchKernelGGL(topk_rows_kernel<4>, tgrid, tthreads, 0, stream, logits, T, E, k, ids, weights);
+  else if (E <= 8 * kWave)
+    hipLaunchKernelGGL(topk_rows_kernel<8>, tgrid, tthreads, 0, stream, logits, T, E, k, ids, weights);
+  else
+    hipLaunchKernelGGL(topk_rows_kernel<kMaxExperts / kWave>, tgrid, tthreads, 0, stream, logits, T, E, k, ids,
+                       weights);
   return hipGetLastError();
 }
 

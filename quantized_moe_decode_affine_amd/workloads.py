@@ -87,3 +87,31 @@ class DecodeStack:
                 events[l][1].record()
             if st != B.OK:
                 B._check("moe_ffn_decode", st)
+
+    def enable_batch(self, max_batch: int = 8, device="cuda") -> None:
+        """Inputs for batched steps: x[s][l][b] drawn like the batch-1 inputs (seeded per
+        step, layer and row), outputs, ids and one workspace sized for max_batch rows."""
+        import numpy as np
+        H, k = self.layers[0].hidden, self.layers[0].top_k
+        xb = [[[synth.hidden_vector(self.seed, 1000 + s * max_batch + b, l, H) for b in range(max_batch)]
+               for l in range(self.n_layers)] for s in range(self.n_steps)]
+        self.xb = B.bf16_tensor(np.asarray(xb, dtype=np.uint16), device)       # [steps][layers][max_batch][H]
+        self.yb = torch.empty((self.n_layers, max_batch, H), dtype=torch.float32, device=device)
+        self.idsb = torch.empty((self.n_layers, max_batch, k), dtype=torch.int32, device=device)
+        self.wsb = B.workspace(B.workspace_bytes(B.OP_FFN_DECODE_BATCH, self.layers[0], rows=max_batch), device)
+        self.max_batch = max_batch
+        self._fnb = B.load_library().moe_ffn_decode_batch
+
+    def step_batch(self, s: int, nb: int, record_ids: bool = False) -> None:
+        """Enqueue one batched decode step of nb rows (all layers, in order) on the current stream."""
+        stream = torch.cuda.current_stream().cuda_stream
+        xs = self.xb[s % self.n_steps]
+        mb, H = self.max_batch, self.yb.shape[2]
+        k = self.idsb.shape[2]
+        x0, y0, ids0 = xs.data_ptr(), self.yb.data_ptr(), self.idsb.data_ptr()
+        ws, wsn = self.wsb.data_ptr(), self.wsb.numel()
+        for l in range(self.n_layers):
+            st = self._fnb(self._refs[l], x0 + 2 * H * mb * l, nb, y0 + 4 * H * mb * l, B.OUT_F32,
+                           (ids0 + 4 * k * mb * l) if record_ids else None, None, ws, wsn, stream)
+            if st != B.OK:
+                B._check("moe_ffn_decode_batch", st)

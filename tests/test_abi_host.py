@@ -130,6 +130,30 @@ def test_ffn_rejects(lib):
     assert lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(noshared), None, 50) < need_p
 
 
+def test_decode_batch_rejects(lib):
+    good = _layer()
+    need = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(good), None, 4)
+    assert need > 0
+    assert lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(good), None, 1) < need
+    assert lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(good), None, 0) == 0
+    assert lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(good), None, 9) == 0
+    f = lib.moe_ffn_decode_batch
+    assert f(ctypes.byref(_layer(hidden=100)), A, 4, A, 0, None, None, A, need, None) == B.EINVAL
+    assert f(ctypes.byref(good), A, 0, A, 0, None, None, A, need, None) == B.EINVAL
+    assert f(ctypes.byref(good), A, 9, A, 0, None, None, A, need, None) == B.EUNSUPPORTED
+    assert f(ctypes.byref(good), None, 4, A, 0, None, None, A, need, None) == B.EINVAL
+    assert f(ctypes.byref(good), A + 8, 4, A, 0, None, None, A, need, None) == B.EINVAL
+    assert f(ctypes.byref(good), A, 4, A, 2, None, None, A, need, None) == B.EINVAL
+    assert f(ctypes.byref(good), A, 4, A, 0, None, None, A, need - 256, None) == B.EWORKSPACE
+    assert f(ctypes.byref(good), A, 4, A, 0, None, None, A + 16, need, None) == B.EWORKSPACE
+    # staged SwiGLU outputs of one token beyond 64 KB of LDS: 33 slots x 4096 inter
+    wide = _layer(H=128, I=4096, E=64, k=32, gate=_mat(64, 4096, 128), up=_mat(64, 4096, 128),
+                  down=_mat(64, 128, 4096), sh_gate=_mat(1, 4096, 128), sh_up=_mat(1, 4096, 128),
+                  sh_down=_mat(1, 128, 4096))
+    wneed = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(wide), None, 2)
+    assert f(ctypes.byref(wide), A, 2, A, 0, None, None, A, wneed, None) == B.EUNSUPPORTED
+
+
 def test_lmhead_rejects(lib):
     W = ctypes.byref(_mat(1, 1000, 2048))
     need = lib.q4moe_workspace_bytes(B.OP_LMHEAD, None, W, 4)

@@ -23,7 +23,7 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 DECODE_SOURCES = ("decode.hip", "common.h", "vecstage.h", "topk.h", "kernels.h")
-ALL_SOURCES = ("abi.hip", "decode.hip", "gemm.hip", "gemv.hip", "route.hip", "common.h", "kernels.h", "topk.h",
+ALL_SOURCES = ("abi.hip", "decode.hip", "decode_batch.hip", "gemm.hip", "gemv.hip", "route.hip", "common.h", "kernels.h", "topk.h",
                "vecstage.h")
 
 

@@ -101,9 +101,13 @@ int q4_gemv(const q4moe_matrix* W, const q4moe_bf16* x, void* y, int out_dtype,
 
 /*
  * Y[m][r] = sum_j X[m][j] W[r][j] for bf16 rows X[m][k], Y [m][count*n] fp32 or
- * bf16.  The prefill form, run on bf16 matrix cores with exact dequantization
- * (lily-qwen3.8-flash-next README, "How the speed was achieved": prefill GEMMs
- * on the tensor units).  Needs Q4MOE_OP_GEMM workspace (m).
+ * bf16.  The prefill form, run on fp16 matrix cores (lily-qwen3.8-flash-next
+ * README, "How the speed was achieved": prefill GEMMs on the tensor units):
+ * each row of X is scaled by an exact power of two into fp16 (exact for bf16
+ * values within 2^-23 of the row's largest), each scale*q is rounded once to
+ * fp16 (at most 2^-12 relative), the bias term is exact up to fp32 summation,
+ * and accumulation is fp32.  Scales must be below 64 in magnitude.  Needs
+ * Q4MOE_OP_GEMM workspace (m).
  */
 int q4_gemm(const q4moe_matrix* W, const q4moe_bf16* X, int64_t m, void* Y, int out_dtype,
             void* workspace, size_t workspace_bytes, q4moe_stream stream);
@@ -174,10 +178,11 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
 /*
  * T tokens through the MoE layer (a prefill chunk, 2,048 tokens in the
  * "Measurement contract" of "2026-09-02: Lily vs MLX 0.32.2"): route, permute
- * by expert, grouped bf16-MFMA GEMMs for gate/up with SwiGLU and for down with
- * the routing weight, then combine back in token order.  Row t of Y equals
- * moe_ffn_decode on X[t] up to rounding; the SwiGLU output is rounded to bf16
- * once before the down GEMM.  Y fp32 or bf16 [T][hidden].  Needs
+ * by expert, grouped fp16-MFMA GEMMs (as q4_gemm) for gate/up with SwiGLU and
+ * for down with the routing weight, then combine back in token order.  Row t
+ * of Y equals moe_ffn_decode on X[t] up to rounding; the SwiGLU output is
+ * computed in fp32 and rounded once to fp16 (after an exact power-of-two row
+ * scaling) before the down GEMM.  Y fp32 or bf16 [T][hidden].  Needs
  * Q4MOE_OP_FFN_PREFILL workspace (T).
  */
 int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, void* Y,

@@ -1,27 +1,35 @@
-// Grouped affine-Q4 GEMM on bf16 matrix cores, and the prefill MoE layer
+// Grouped affine-Q4 GEMM on fp16 matrix cores, and the prefill MoE layer
 // built on it (lily-qwen3.8-flash-next README, "How the speed was achieved":
 // prefill is compute-bound and runs the expert GEMM over token-to-expert
 // groups; "2026-09-02: Lily vs MLX 0.32.2", "Measurement contract": prompts go
 // through in 2,048-token chunks).
 //
-// Exact dequantization on MFMA: the B operand holds the codes as bfloat16
-// (128 + q) (common.h), so one 64-column group yields
-//   P'[m][n] = sum_j x[m][j] (128 + q[n][j])        (exact products, fp32 sum)
-// and the output accumulates scale[n][g] * P'[m][n] per group (one VALU FMA
-// per element per group).  The remaining term
-//   sum_g (bias - 128*scale)[n][g] * rowsum_g(x)[m]
-// is itself a small product over the group index; both factors are split
-// exactly into bfloat16 parts (3 for the fp32 row sums, 2 for the offset
-// bias, which needs at most 16 significant bits) and fed to the same MFMA
-// after the main loop.  No weight is rounded.
+// Dequantization on MFMA without a per-group fold.  With w = s*q + b,
+//   y[m][n] = sum_j x[m][j] (s[n][g] q[n][j]) + sum_g b[n][g] rowsum_g(x)[m].
+// The B operand of the main product is s*q in fp16, made by one packed FMA per
+// code pair: (1024 + q) is an fp16 whose mantissa holds q (bits 0x6400 | q), and
+// fma(1024 + q, s, -1024 s) = s*q rounded once (s*q has at most 12 significant
+// bits, so the rounding is at most 2^-12 relative and often absent).  The
+// accumulators then run over the whole K range with no VALU work between the
+// matrix instructions.  The bias term is a small product over the group index
+// (biases in fp16 are exact; the row sums are split into two fp16 parts) fed to
+// the same MFMA after the main loop.
 //
-// Tiling: a workgroup (4 waves) owns 128 rows of one group (expert) and 256
+// Rows enter as fp16 after an exact power-of-two scaling per row (prep_rows_kernel):
+// the row's largest magnitude lands in [256, 512), so every value stays in fp16's
+// range, bf16 inputs convert exactly (8 significant bits fit in 11) unless they are
+// below 2^-23 of the row's largest, and a row's 64-wide group sums stay below 2^15.
+// The epilogue multiplies the power back in.  The SwiGLU activations are written
+// in fp32 and get the same treatment before the down GEMM, so they are rounded
+// once, to 11 significant bits.
+//
+// Tiling: a workgroup (4 waves) owns up to 96 rows of one group (expert) and 256
 // output columns (or 128 gate + 128 up columns for the SwiGLU epilogue); each
-// wave computes 4 x 2 MFMA 32x32 blocks.  The row tile is staged through LDS
-// (permuted into the nibble-pair order) with one group of look-ahead; each
-// lane loads its own 16 code bytes per group for its column.  Workgroups of
-// the same row tile are placed on the same XCD so the row tile stays in that
-// XCD's L2.
+// wave computes up to 3 x 2 MFMA 32x32 blocks.  The row tile is staged through
+// LDS (already in the nibble-pair order) with two groups of look-ahead; each lane
+// loads its own 16 code bytes per group for its column.  Workgroups of the same
+// row tile are placed on the same XCD so the row tile stays in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -38,11 +46,15 @@ constexpr int kXcd = 8;
 
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SCALE = 2 };
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct GemmParams {
-  const uint16_t* A;          // bf16 rows [*][K]
-  const uint16_t* xs;         // bf16 [*][3][Gp] row group-sum parts, same row indexing as A
+  const uint16_t* A;          // fp16 rows [*][K] (pair order), scaled by 2^-row_exp
+  const uint16_t* xs;         // fp16 [*][2][Gp] row group-sum parts, same row indexing as A
+  const int32_t* row_exp;     // [*] power of two taken out of each A row
   const int4* tiles;          // per tile {segment (expert; -1 extra; -2 none), first position, rows, 0};
                               // null: tile t covers positions t*BM.. of the extra segment
   int n_tiles;                // table length (the grid may hold a few more tiles)
@@ -51,7 +63,7 @@ struct GemmParams {
   int gather;
   int64_t P;                  // positions of the routed segments
   int K, G, Gp;
-  int bs_vec;                 // 1: every scale/bias row may be read 8 groups (16 bytes) at a time
+  int bs_vec;                 // 1: every bias row may be read 8 groups (16 bytes) at a time
   int N;                      // output columns (store/scale) or intermediate width (swiglu)
   Q4Mat W, W2;                // routed experts (W2 = up for swiglu), stacked
   int64_t w_codes_stride, w_groups_stride;
@@ -59,21 +71,41 @@ struct GemmParams {
   int64_t extra_rows;         // positions of the extra segment (uniform tiling when tiles is null)
   int n_slices;
   int epi;
-  void* out;
+  void* out;                  // swiglu: fp32 activations; store/scale: fp32 or bf16
   int out_bf16;
   int64_t ldo;
 };
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8_t, v); }
 
 // Global-address-space view of a pointer: a generic (flat) load could touch
 // LDS, so it would have to wait for every LDS DMA still in flight.
 typedef const uint16_t __attribute__((address_space(1)))* gu16_ptr;
 __device__ __forceinline__ uint32_t ld_global_u16(const uint16_t* ptr) { return *(gu16_ptr)ptr; }
 
-__device__ __forceinline__ uint4 codes_to_operand(uint32_t w) {
-  return make_uint4(nib_pair(w, 0), nib_pair(w, 4), nib_pair(w, 8), nib_pair(w, 12));
+// Two fp16 1024.0 in a VGPR (an and-or takes at most one literal).
+__device__ __forceinline__ uint32_t magic_pair_f16_reg() {
+  uint32_t m;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
 }
+
+// s*q for the nibbles at positions j and j+4 of `word` (j = shift/4), as an fp16 pair:
+// ((word >> shift) & 0x000F000F) | 0x64006400 is (1024 + q_j, 1024 + q_{j+4}) exactly,
+// and one packed FMA with (s, s) and (-1024 s, -1024 s) leaves s*q, rounded once.
+__device__ __forceinline__ uint32_t scaled_pair(uint32_t word, int shift, f16x2_t s2, f16x2_t m2) {
+  const uint32_t p = ((word >> shift) & nibble_mask_reg()) | magic_pair_f16_reg();
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, p), s2, m2));
+}
+
+// The 8 codes of one word as the B operand of one MFMA K-step (pair order).
+__device__ __forceinline__ uint4 codes_to_operand(uint32_t w, f16x2_t s2, f16x2_t m2) {
+  return make_uint4(scaled_pair(w, 0, s2, m2), scaled_pair(w, 4, s2, m2), scaled_pair(w, 8, s2, m2),
+                    scaled_pair(w, 12, s2, m2));
+}
+
+// bf16 bits -> fp16 (exact for magnitudes in fp16's normal range).
+__device__ __forceinline__ _Float16 bf16_bits_to_f16(uint32_t bits) { return (_Float16)bf16_bits_to_f32(bits); }
 
 // s_waitcnt immediate for "at most n vector-memory ops outstanding" (gfx9 encoding,
 // expcnt and lgkmcnt left at their maxima).
@@ -85,7 +117,7 @@ constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xF << 8); }
 // MB A-tile LDS loads, 2 B-code LDS loads, 2 scale loads.
 constexpr int kStages = 3;  // the stage arrays below are written out for exactly 3
 constexpr int kOpsPerStage = MB + 4;
-constexpr int A_STAGE_BYTES = BM * 128;           // BM rows x one 64-column group of bf16
+constexpr int A_STAGE_BYTES = BM * 128;           // BM rows x one 64-column group of fp16
 constexpr int B_STAGE_BYTES = 4 * 2 * 64 * 16;    // 4 waves x 2 column blocks x 64 lanes x 16 bytes
 
 // Swizzled slot of (row r, 16-byte word w) in an A stage: the words of a row
@@ -103,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
   auto stage_a = [&](int st) -> uint8_t* { return st == 0 ? s_st0 : st == 1 ? s_st1 : s_st2; };
   auto stage_b = [&](int st) -> uint8_t* { return stage_a(st) + A_STAGE_BYTES; };
   __shared__ int32_t s_src[BM];
-  __shared__ float s_wgt[BM];  // routing weight of each tile row (scale epilogue)
+  __shared__ float s_wgt[BM];  // per tile row: routing weight (scale epilogue) times 2^row_exp
 
   // ---- tile of this workgroup (XCD-aware: all slices of a tile share an XCD)
   const int bid = blockIdx.x;
@@ -126,13 +158,20 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
   }
   if (seg == -2) return;
 
-  // ---- source row and routing weight of each tile row (padding rows repeat the
-  // last real row; their outputs are dropped)
-  for (int r = threadIdx.x; r < BM; r += blockDim.x) {
+  // ---- source row of each tile row (padding rows repeat the last real row; their
+  // outputs are dropped).  Thread r < BM also loads its row's routing weight and
+  // exponent, which only the epilogue needs: those loads stay in flight meanwhile.
+  static_assert(BM <= 256, "one tile row per thread");
+  float row_wgt = 1.0f;
+  int row_e = 0;
+  if (threadIdx.x < BM) {
+    const int r = threadIdx.x;
     const int64_t pos = row0 + min(r, rows - 1);
     const bool routed = pos < p.P;
-    s_src[r] = p.gather ? (routed ? p.row_src[pos] : (int32_t)(pos - p.P)) : (int32_t)pos;
-    s_wgt[r] = p.epi == EPI_SCALE && routed ? p.route_w[pos] : 1.0f;
+    const int32_t src = p.gather ? (routed ? p.row_src[pos] : (int32_t)(pos - p.P)) : (int32_t)pos;
+    s_src[r] = src;
+    if (p.epi == EPI_SCALE && routed) row_wgt = p.route_w[pos];
+    row_e = p.row_exp[src];
   }
 
   const int lane = lane_id();
@@ -170,9 +209,9 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
     a_ptr[i] = p.A + (int64_t)s_src[r] * p.K + a_word[i] * 8;
   }
 
-  // Issue all loads of K group g into stage `st` (groups past the end repeat the last one).
+  // Issue all loads of K group g into stage `st`.
   auto issue = [&](int g, int st, uint32_t (&sc)[2]) {
-    g = min(g, p.G - 1);
+    if (g >= p.G) return;  // nothing past the last group (the step waits account for it)
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       __builtin_amdgcn_global_load_lds(a_ptr[i] + g * 64, stage_a(st) + (wave * MB + i) * 1024, 16, 0, 0);
@@ -197,6 +236,7 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int st = 0; st < kStages - 1; ++st) issue(st, st, sc[st]);
 
+
   // The main loop is specialised on the number of active row blocks so that a
   // group's body has no branches: every wait the compiler adds then sits at a
   // use of the data, not at a join right after the look-ahead loads.
@@ -211,8 +251,16 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       // Group g has landed for this wave and this wave's reads of the stage about
       // to be refilled are done; the barrier extends both to every wave.  (A
       // workgroup fence here would also wait for the look-ahead DMA.)
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kOpsPerStage * (kStages - 2)));
+      if (g + 1 < p.G)  // group g+1's loads (issued after group g's) may still be in flight
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kOpsPerStage * (kStages - 2)));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
       __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // The look-ahead group goes out first: every wave has finished reading the
+      // stage it refills (the barrier above), and loads issued here have two whole
+      // steps to land (left to the scheduler they sink below the MFMAs).
+      issue(g + kStages - 1, sn, sc[sn]);
       __builtin_amdgcn_sched_barrier(0);
 
       const uint8_t* sa = stage_a(st);
@@ -229,28 +277,29 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       const uint4 rb0 = *reinterpret_cast<const uint4*>(sb);
       const uint4 rb1 = *reinterpret_cast<const uint4*>(sb + 1024);
       read_a(0, af[0]);
-      issue(g + kStages - 1, sn, sc[sn]);  // the look-ahead group, after this step's LDS reads
-      bf16x8_t bop[2][4];  // this group's B operands, converted once, used by every row block
+      f16x2_t s2[2], m2[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float s = bf16_bits_to_f32(sc[st][nb]);
+        const _Float16 sh = (_Float16)s, mh = (_Float16)(-1024.0f * s);
+        s2[nb] = f16x2_t{sh, sh};
+        m2[nb] = f16x2_t{mh, mh};
+      }
+      uint4 bop[2][4];  // this group's B operands, converted once, used by every row block
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        bop[0][s4] = as_bf16x8(codes_to_operand(s4 == 0 ? rb0.x : s4 == 1 ? rb0.y : s4 == 2 ? rb0.z : rb0.w));
-        bop[1][s4] = as_bf16x8(codes_to_operand(s4 == 0 ? rb1.x : s4 == 1 ? rb1.y : s4 == 2 ? rb1.z : rb1.w));
+        bop[0][s4] = codes_to_operand(s4 == 0 ? rb0.x : s4 == 1 ? rb0.y : s4 == 2 ? rb0.z : rb0.w, s2[0], m2[0]);
+        bop[1][s4] = codes_to_operand(s4 == 0 ? rb1.x : s4 == 1 ? rb1.y : s4 == 2 ? rb1.z : rb1.w, s2[1], m2[1]);
       }
-      const float scale0 = bf16_bits_to_f32(sc[st][0]), scale1 = bf16_bits_to_f32(sc[st][1]);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
         if (mb + 1 < NMB) read_a(mb + 1, af[(mb + 1) & 1]);
-        // two independent chains (one per column block) over the group's 4 K-steps, then the fold
-        f32x16_t p0 = zero16, p1 = zero16;
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mb & 1][s4]), bop[0][s4], p0, 0, 0, 0);
-          p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mb & 1][s4]), bop[1][s4], p1, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          acc[mb][0][i] = fmaf(scale0, p0[i], acc[mb][0][i]);
-          acc[mb][1][i] = fmaf(scale1, p1[i], acc[mb][1][i]);
+          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(af[mb & 1][s4]), as_f16x8(bop[0][s4]),
+                                                              acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(af[mb & 1][s4]), as_f16x8(bop[1][s4]),
+                                                              acc[mb][1], 0, 0, 0);
         }
       }
     };
@@ -271,14 +320,12 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
     main_loop(std::integral_constant<int, 2>{});
   else
     main_loop(std::integral_constant<int, 3>{});
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing (unused) loads before LDS is released
-
-  // ---- offset/bias term: sum_g (bias - 128 scale)[n][g] * rowsum_g[m], on MFMA with exact bf16 parts.
-  // Each 16-group slice takes one round of loads (the 8 groups' biases and scales of this lane's
-  // column, 16 bytes each where aligned, and the rows' group-sum parts), issued one slice ahead.
+  // ---- bias term: sum_g bias[n][g] * rowsum_g[m], on MFMA (fp16 biases exact, row sums in two parts).
+  // Each 16-group slice takes one round of loads (the 8 groups' biases of this lane's column,
+  // 16 bytes where aligned, and the rows' group-sum parts), issued one slice ahead.
   struct CorrLoads {
-    uint4 bias[2], scale[2];  // [nb]: 8 groups' bf16 values
-    uint4 xa[MB][3];          // [mb][part]: 8 groups' bf16 row-sum parts
+    uint4 bias[2];   // [nb]: 8 groups' bf16 biases
+    uint4 xa[MB][2]; // [mb][part]: 8 groups' fp16 row-sum parts
   };
   auto corr_load = [&](int t, CorrLoads& L) __attribute__((always_inline)) {
     const int gbase = t * 16 + 8 * lh;
@@ -287,57 +334,49 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       if (p.bs_vec) {
         const bool any = gbase < p.G;  // with G % 8 == 0 a slice half is all real groups or all padding
         L.bias[nb] = any ? *reinterpret_cast<const uint4*>(bbias[nb] + gbase) : make_uint4(0, 0, 0, 0);
-        L.scale[nb] = any ? *reinterpret_cast<const uint4*>(bscale[nb] + gbase) : make_uint4(0, 0, 0, 0);
       } else {
-        uint32_t bv[8], sv[8];
+        uint32_t bv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int g = min(gbase + j, p.G - 1);  // padding groups: loaded clamped, zeroed
           bv[j] = gbase + j < p.G ? ld_global_u16(bbias[nb] + g) : 0u;
-          sv[j] = gbase + j < p.G ? ld_global_u16(bscale[nb] + g) : 0u;
         }
         L.bias[nb] = make_uint4(bv[0] | bv[1] << 16, bv[2] | bv[3] << 16, bv[4] | bv[5] << 16, bv[6] | bv[7] << 16);
-        L.scale[nb] = make_uint4(sv[0] | sv[1] << 16, sv[2] | sv[3] << 16, sv[4] | sv[5] << 16, sv[6] | sv[7] << 16);
       }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb >= mblocks) continue;
-      const uint16_t* xr = p.xs + (int64_t)s_src[mb * 32 + ln] * 3 * p.Gp + gbase;
+      const uint16_t* xr = p.xs + (int64_t)s_src[mb * 32 + ln] * 2 * p.Gp + gbase;
 #pragma unroll
-      for (int part_i = 0; part_i < 3; ++part_i) L.xa[mb][part_i] = *reinterpret_cast<const uint4*>(xr + part_i * p.Gp);
+      for (int part_i = 0; part_i < 2; ++part_i) L.xa[mb][part_i] = *reinterpret_cast<const uint4*>(xr + part_i * p.Gp);
     }
   };
   auto corr_apply = [&](const CorrLoads& L) __attribute__((always_inline)) {
-    uint4 bc[2][2];  // [nb][hi/lo]
+    uint4 bc[2];  // [nb]: the 8 groups' biases as fp16
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const uint32_t bw[4] = {L.bias[nb].x, L.bias[nb].y, L.bias[nb].z, L.bias[nb].w};
-      const uint32_t sw[4] = {L.scale[nb].x, L.scale[nb].y, L.scale[nb].z, L.scale[nb].w};
-      uint32_t hi[8], lo[8];
+      uint32_t hv[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t bj = (bw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu, sj = (sw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        const float c = bf16_bits_to_f32(bj) - 128.0f * bf16_bits_to_f32(sj);  // padding groups: 0 - 0
-        hi[j] = f32_to_bf16_bits(c);
-        lo[j] = f32_to_bf16_bits(c - bf16_bits_to_f32(hi[j]));
+      for (int j = 0; j < 4; ++j) {
+        const f16x2_t h2 = {bf16_bits_to_f16(bw[j] & 0xFFFFu), bf16_bits_to_f16(bw[j] >> 16)};
+        hv[j] = __builtin_bit_cast(uint32_t, h2);
       }
-      bc[nb][0] = make_uint4(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16);
-      bc[nb][1] = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16);
+      bc[nb] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb >= mblocks) continue;
 #pragma unroll
-      for (int part_i = 0; part_i < 3; ++part_i)
+      for (int part_i = 0; part_i < 2; ++part_i)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(L.xa[mb][part_i]), as_bf16x8(bc[nb][hl]),
-                                                                 acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(L.xa[mb][part_i]), as_f16x8(bc[nb]),
+                                                               acc[mb][nb], 0, 0, 0);
     }
   };
+
   {
     const int nt = (p.Gp + 15) / 16;
     CorrLoads cur, nxt;
@@ -349,6 +388,9 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
     }
   }
 
+  if (threadIdx.x < BM) s_wgt[threadIdx.x] = ldexpf(row_wgt, row_e);  // exact: a power of two
+  __syncthreads();
+
   // ---- epilogue.  D layout: column = lane % 32, row = 8*(i/4) + 4*(lane/32) + i%4.
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -358,20 +400,17 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       const int r = mb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
       if (r >= rows) continue;
       const int64_t pos = row0 + r;
+      const float f = s_wgt[r];
       if (swiglu) {
         if (col[0] < p.N) {
-          // activations are written in the permuted 8-column order the next GEMM's A operand uses
-          const int c = col[0], j = c & 7;
-          const int pc = (c & ~7) | (j < 4 ? 2 * j : 2 * (j - 4) + 1);
-          const float a = silu(acc[mb][0][i]) * acc[mb][1][i];
-          reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + pc] = (uint16_t)f32_to_bf16_bits(a);
+          const float a = silu(f * acc[mb][0][i]) * (f * acc[mb][1][i]);
+          reinterpret_cast<float*>(p.out)[pos * p.ldo + col[0]] = a;
         }
       } else {
-        const float wgt = s_wgt[r];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           if (col[nb] >= p.N) continue;
-          const float v = wgt * acc[mb][nb][i];
+          const float v = f * acc[mb][nb][i];
           if (p.out_bf16)
             reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + col[nb]] = (uint16_t)f32_to_bf16_bits(v);
           else
@@ -382,39 +421,85 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
   }
 }
 
-// Per-row, per-64-column-group sums of a bf16 matrix, split exactly into three
-// bfloat16 parts: sums[r][part][g] (groups padded with zeros to Gp).  When `ap`
-// is given, also writes the rows with each 8-column block permuted into the
-// (x0,x4),(x1,x5),(x2,x6),(x3,x7) pair order the MFMA A operand uses.
-__global__ void prep_rows_kernel(const uint16_t* __restrict__ A, int64_t rows, int K, int Gp,
-                                 uint16_t* __restrict__ sums, uint16_t* __restrict__ ap) {
-  const int G = K >> 6;
-  const int64_t total = rows * Gp;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / Gp;
-    const int g = (int)(i - r * Gp);
-    float s = 0.f;
-    if (g < G) {
-      const uint4* src = reinterpret_cast<const uint4*>(A + r * K + g * 64);
-      uint4* dst = ap ? reinterpret_cast<uint4*>(ap + r * K + g * 64) : nullptr;
+// Load 8 consecutive elements of a row as fp32 (bf16 bits or fp32 input).
+__device__ __forceinline__ void load8(const uint16_t* src, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint4 v = src[j];
-        s += (bf16_bits_to_f32(v.x & 0xFFFFu) + bf16_bits_to_f32(v.x >> 16)) +
-             (bf16_bits_to_f32(v.y & 0xFFFFu) + bf16_bits_to_f32(v.y >> 16)) +
-             (bf16_bits_to_f32(v.z & 0xFFFFu) + bf16_bits_to_f32(v.z >> 16)) +
-             (bf16_bits_to_f32(v.w & 0xFFFFu) + bf16_bits_to_f32(v.w >> 16));
-        if (dst) dst[j] = permute_block(v);
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+    v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+  }
+}
+__device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// fp16 copy of rows for the MFMA A operand, one wave per row.  The row's largest
+// magnitude M picks e with M * 2^-e in [256, 512) (e = 0 for an all-zero row); the
+// row is written as fp16(x * 2^-e) with each 8-element block in the pair order
+// (x0,x4),(x1,x5),(x2,x6),(x3,x7), e goes to exps[row], and the sums of each 64-wide
+// group of the fp16 values are split into two fp16 parts: sums[row][part][g], with
+// the groups padded with zeros to Gp.
+template <typename In>
+__global__ void prep_rows_kernel(const In* __restrict__ A, int64_t rows, int K, int Gp, uint16_t* __restrict__ out,
+                                 uint16_t* __restrict__ sums, int32_t* __restrict__ exps) {
+  const int lane = lane_id();
+  const int nblk = K >> 3, G = K >> 6;
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; r < rows; r += wstride) {
+    const In* row = A + r * K;
+    uint32_t mx = 0;  // largest |x| as float bits (non-negative floats order as integers)
+    for (int b = lane; b < nblk; b += kWave) {
+      float v[8];
+      load8(row + b * 8, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, __float_as_uint(fabsf(v[j])));
+    }
+    mx = wave_max_u32(mx);
+    const float m = __uint_as_float(mx);
+    int e = 0;
+    if (m > 0.0f && m <= 3.0e38f) {
+      int ex;
+      frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+      e = ex - 9;
+    }
+    uint16_t* orow = out + r * K;
+    uint16_t* srow = sums + r * 2 * Gp;
+    for (int b0 = 0; b0 < nblk; b0 += kWave) {
+      const int b = b0 + lane;
+      float gs = 0.0f;
+      if (b < nblk) {
+        float v[8];
+        load8(row + b * 8, v);
+        _Float16 h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          h[j] = (_Float16)ldexpf(v[j], -e);
+          gs += (float)h[j];
+        }
+        uint4 o;
+        o.x = __builtin_bit_cast(uint32_t, f16x2_t{h[0], h[4]});
+        o.y = __builtin_bit_cast(uint32_t, f16x2_t{h[1], h[5]});
+        o.z = __builtin_bit_cast(uint32_t, f16x2_t{h[2], h[6]});
+        o.w = __builtin_bit_cast(uint32_t, f16x2_t{h[3], h[7]});
+        *reinterpret_cast<uint4*>(orow + b * 8) = o;
+      }
+      gs = group_sum<8>(gs);  // the 8 blocks of a group sit in 8 consecutive lanes
+      if (b < nblk && (b & 7) == 0) {
+        const _Float16 hi = (_Float16)gs;
+        const _Float16 lo = (_Float16)(gs - (float)hi);
+        srow[b >> 3] = __builtin_bit_cast(uint16_t, hi);
+        srow[Gp + (b >> 3)] = __builtin_bit_cast(uint16_t, lo);
       }
     }
-    const uint32_t h = f32_to_bf16_bits(s);
-    const float r1 = s - bf16_bits_to_f32(h);
-    const uint32_t m = f32_to_bf16_bits(r1);
-    const uint32_t l = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));
-    uint16_t* o = sums + r * 3 * Gp + g;
-    o[0] = (uint16_t)h;
-    o[Gp] = (uint16_t)m;
-    o[2 * Gp] = (uint16_t)l;
+    if (lane < Gp - G) {
+      srow[G + lane] = 0;
+      srow[Gp + G + lane] = 0;
+    }
+    if (lane == 0) exps[r] = e;
   }
 }
 
@@ -464,30 +549,39 @@ hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream) 
   return hipGetLastError();
 }
 
-// Row sums (and, with ap, the permuted copy) of `rows` bf16 rows of length K.
-hipError_t launch_prep_rows(const uint16_t* A, int64_t rows, int K, uint16_t* sums, uint16_t* ap,
+// fp16 pair-order copy, row exponents and group-sum parts of `rows` rows of length K.
+template <typename In>
+hipError_t launch_prep_rows(const In* A, int64_t rows, int K, uint16_t* out, uint16_t* sums, int32_t* exps,
                             hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
   const int Gp = pad16(K >> 6);
-  hipLaunchKernelGGL(prep_rows_kernel, dim3(grid_for(rows * Gp, 256)), dim3(256), 0, stream, A, rows, K, Gp, sums,
-                     ap);
+  const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 8192);
+  hipLaunchKernelGGL(prep_rows_kernel<In>, dim3((unsigned)blocks), dim3(256), 0, stream, A, rows, K, Gp, out, sums,
+                     exps);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// q4_gemm workspace: row-sum parts [m][2][Gp] fp16, row exponents [m], fp16 rows [m][k].
 size_t gemm_workspace_bytes(int64_t m, int k) {
-  return align256((size_t)m * 3 * pad16(k / 64) * 2) + align256((size_t)m * k * 2);
+  return align256((size_t)m * 2 * pad16(k / 64) * 2) + align256((size_t)m * 4) + align256((size_t)m * k * 2);
 }
 
 hipError_t run_q4_gemm(const Q4Mat& W, int64_t n, int k, const uint16_t* X, int64_t m, void* Y, int out_bf16,
                        void* ws, hipStream_t stream) {
-  uint16_t* xs = static_cast<uint16_t*>(ws);
-  uint16_t* xp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align256((size_t)m * 3 * pad16(k / 64) * 2));
-  hipError_t e = launch_prep_rows(X, m, k, xs, xp, stream);
+  char* c = static_cast<char*>(ws);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(c);
+  c += align256((size_t)m * 2 * pad16(k / 64) * 2);
+  int32_t* xe = reinterpret_cast<int32_t*>(c);
+  c += align256((size_t)m * 4);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(c);
+  hipError_t e = launch_prep_rows(X, m, k, xp, xs, xe, stream);
   if (e != hipSuccess) return e;
   GemmParams p{};
   p.A = xp;
   p.xs = xs;
+  p.row_exp = xe;
   p.gather = 0;
   p.P = 0;
   p.K = k;
@@ -517,11 +611,14 @@ struct PrefillWs {
   int32_t* row_src;
   float* row_w;
   void* perm_ws;
-  uint16_t* xs_x;
-  uint16_t* xp;
-  uint16_t* act;
-  uint16_t* xs_act;
-  float* ys;
+  uint16_t* xs_x;   // [T][2][Gp(H)] fp16 group-sum parts of the rows
+  int32_t* xe_x;    // [T] row exponents
+  uint16_t* xp;     // [T][H] fp16 rows (pair order)
+  float* act32;     // [R][I] SwiGLU outputs, fp32
+  uint16_t* act;    // [R][I] fp16 activations (pair order)
+  uint16_t* xs_act; // [R][2][Gp(I)]
+  int32_t* xe_act;  // [R]
+  float* ys;        // [R][H] per-position outputs, weighted
   size_t total;
 };
 
@@ -542,10 +639,13 @@ PrefillWs carve(void* base, int64_t T, int H, int I, int E, int k, int has_share
   w.row_src = reinterpret_cast<int32_t*>(take(P * 4));
   w.row_w = reinterpret_cast<float*>(take(P * 4));
   w.perm_ws = take(permute_workspace_bytes(P, E));
-  w.xs_x = reinterpret_cast<uint16_t*>(take((size_t)T * 3 * pad16(H / 64) * 2));
+  w.xs_x = reinterpret_cast<uint16_t*>(take((size_t)T * 2 * pad16(H / 64) * 2));
+  w.xe_x = reinterpret_cast<int32_t*>(take((size_t)T * 4));
   w.xp = reinterpret_cast<uint16_t*>(take((size_t)T * H * 2));
+  w.act32 = reinterpret_cast<float*>(take((size_t)R * I * 4));
   w.act = reinterpret_cast<uint16_t*>(take((size_t)R * I * 2));
-  w.xs_act = reinterpret_cast<uint16_t*>(take((size_t)R * 3 * pad16(I / 64) * 2));
+  w.xs_act = reinterpret_cast<uint16_t*>(take((size_t)R * 2 * pad16(I / 64) * 2));
+  w.xe_act = reinterpret_cast<int32_t*>(take((size_t)R * 4));
   w.ys = reinterpret_cast<float*>(take((size_t)R * H * 4));
   w.total = off;
   return w;
@@ -576,13 +676,14 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   gt.row_w = w.row_w;
   e = run_permute(w.ids, P, E, w.offsets, w.sorted_rows, w.inv, w.perm_ws, &gt, stream);
   if (e != hipSuccess) return e;
-  e = launch_prep_rows(X, T, H, w.xs_x, w.xp, stream);
+  e = launch_prep_rows(X, T, H, w.xp, w.xs_x, w.xe_x, stream);
   if (e != hipSuccess) return e;
 
-  // gate/up with SwiGLU -> act (bf16, sorted positions; shared rows appended)
+  // gate/up with SwiGLU -> act32 (fp32, sorted positions; shared rows appended)
   GemmParams p{};
   p.A = w.xp;
   p.xs = w.xs_x;
+  p.row_exp = w.xe_x;
   p.tiles = w.tiles;
   p.row_src = w.row_src;
   p.route_w = w.row_w;
@@ -601,20 +702,21 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   p.extra_rows = extra;
   p.n_slices = (I + 127) / 128;
   p.epi = EPI_SWIGLU;
-  p.out = w.act;
-  p.out_bf16 = 1;
+  p.out = w.act32;
+  p.out_bf16 = 0;
   p.ldo = I;
   e = launch_grouped(p, max_tiles, stream);
   if (e != hipSuccess) return e;
 
   const int64_t R = P + extra;
-  e = launch_prep_rows(w.act, R, I, w.xs_act, nullptr, stream);
+  e = launch_prep_rows(w.act32, R, I, w.act, w.xs_act, w.xe_act, stream);
   if (e != hipSuccess) return e;
 
   // down with the routing weight -> ys (fp32, sorted positions)
   GemmParams d = p;
   d.A = w.act;
   d.xs = w.xs_act;
+  d.row_exp = w.xe_act;
   d.gather = 0;
   d.K = I;
   d.G = I / 64;

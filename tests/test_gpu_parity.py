@@ -272,10 +272,13 @@ def test_gemm_parity(B, m, n, k, seed):
     ref = orc.q4_gemm(*mat, X)
     got = to_f64(Y)
     err = rel_l2(got, ref)
-    assert err <= REL_L2_TOL and err <= 1e-5
+    # fp16 operands: each s*q is rounded once (at most 2^-12 of itself, and |s*q| is
+    # typically about twice |w|), the rows convert exactly; the whole product stays
+    # far inside the 2e-3 bar
+    assert err <= REL_L2_TOL and err <= 5e-4
     # row by row as well: no row may be off (a wrong tile would hide in the global norm)
     for r in range(0, m, max(1, m // 17)):
-        assert rel_l2(got[r], ref[r]) <= 1e-4
+        assert rel_l2(got[r], ref[r]) <= 1e-3
     check_bf16_output(Yb, Y, ref)
 
 

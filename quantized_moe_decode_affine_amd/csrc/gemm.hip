@@ -120,10 +120,13 @@ constexpr int kOpsPerStage = MB + 4;
 constexpr int A_STAGE_BYTES = BM * 128;           // BM rows x one 64-column group of fp16
 constexpr int B_STAGE_BYTES = 4 * 2 * 64 * 16;    // 4 waves x 2 column blocks x 64 lanes x 16 bytes
 
-// Swizzled slot of (row r, 16-byte word w) in an A stage: the words of a row
-// are XOR-rotated by the row's low bits so that 8 consecutive rows reading the
-// same word hit 8 different LDS bank groups.
-__device__ __forceinline__ int a_slot(int r, int w) { return r * 8 + (w ^ (r & 7)); }
+// Swizzled slot of (row r, 16-byte word w) in an A stage.  A 128-bit LDS read
+// serves 16 lanes (16 rows here) per cycle from 64 four-byte banks, i.e. two
+// 128-byte rows per bank sweep: rows of equal parity share a bank half, so the
+// words are XOR-rotated by row bits 1-3, which differ among the 8 rows of each
+// parity in any 16 consecutive rows.
+__device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int a_slot(int r, int w) { return r * 8 + (w ^ a_swz(r)); }
 
 __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
   // One LDS array per pipeline stage: distinct variables let the compiler see
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int r = (wave * MB + i) * 8 + (lane >> 3);
-    a_word[i] = (lane & 7) ^ (r & 7);
+    a_word[i] = (lane & 7) ^ a_swz(r);
     a_ptr[i] = p.A + (int64_t)s_src[r] * p.K + a_word[i] * 8;
   }
 

@@ -100,11 +100,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and LM-head legs")
+    ap.add_argument("--no-extra", action="store_true", help="skip every leg but the 40-layer decode loop")
+    ap.add_argument("--legs", default="batch,prefill,wide,lmhead",
+                    help="comma list of the legs run after the decode loop: batch (several requests per step), "
+                         "prefill (2,048-token chunk), wide (512 experts, top-10), lmhead")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (the known-size reference that scales the "
                          "byte counters of a rocprofv3 --pmc run)")
     args = ap.parse_args()
+    legs = set() if args.no_extra else {x for x in args.legs.split(",") if x}
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU)",
               file=sys.stderr, flush=True)
@@ -177,7 +181,7 @@ def main():
                      "kernel": "decode_layer_kernel (moe_ffn_decode, one launch per layer)",
                      "unit_bytes": layer_bytes, "avg_launch_us": round(layer_us, 3)},
     }
-    if not args.no_extra:
+    if "batch" in legs:
         # ------------------------------------------- batched decode (several requests per step)
         stack.enable_batch(8, dev)
         expert_bytes = workloads.decode_layer_bytes(top_k=1, shared=False, n_experts=0, out_bytes=0) - 2 * synth.HIDDEN
@@ -214,7 +218,7 @@ def main():
     del stack
     torch.cuda.empty_cache()
 
-    if not args.no_extra:
+    if "prefill" in legs:
         # ------------------------------------------------------- prefill chunk
         log("building the prefill layer")
         layer = synth.moe_layer(1)
@@ -251,6 +255,7 @@ def main():
         del dl, X, ws, Y
         torch.cuda.empty_cache()
 
+    if "wide" in legs:
         # ------------------------- wider layers: 512 routed experts, top-10, 4,096-token chunks
         log("building 8 wide layers (512 routed + 1 shared experts, top-10)")
         wide = dict(n_experts=512, top_k=10)
@@ -294,6 +299,7 @@ def main():
         del wstack, dl, X, ws, Y
         torch.cuda.empty_cache()
 
+    if "lmhead" in legs:
         # ------------------------------------------------------------ LM head
         log("building the LM head (two copies)")
         mat = synth.lm_head()

@@ -5,6 +5,8 @@ write), as short Markdown for the profiles/ directory.
     python -m quantized_moe_decode_affine_amd.profsum stats DB --cmd "..."
     python -m quantized_moe_decode_affine_amd.profsum traffic --fetch DB1 --write DB2 \\
         --kernel decode_layer_kernel --copy-bytes N --unit-bytes B --cmd-fetch "..." --cmd-write "..."
+    python -m quantized_moe_decode_affine_amd.profsum gemm-traffic --fetch DB1 --write DB2 \\
+        --copy-bytes N --cmd-fetch "..." --cmd-write "..."
 
 `traffic` scales the kernel's FETCH_SIZE / WRITE_SIZE readings (KiB per
 dispatch) by what the same counters read for a plain device copy of known size
@@ -66,6 +68,13 @@ def stats_markdown(db: str, cmd: str) -> str:
     for k, v in sorted(times.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{k[:70]}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
                      f"{sum(v) / 1000:.3f} | {100 * sum(v) / total:.1f} |")
+    g = times.get("grouped_q4_gemm_kernel")
+    if g:
+        # the prefill layer launches it twice per layer: gate/up (SwiGLU), then down
+        lines += ["", "| grouped_q4_gemm_kernel launch | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for name, v in (("gate/up (even dispatches)", g[0::2]), ("down (odd dispatches)", g[1::2])):
+            if v:
+                lines.append(f"| {name} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     lines += ["", f"kernel sources sha256: {all_sources_sha256()}"]
     return "\n".join(lines) + "\n"
 
@@ -121,6 +130,27 @@ def traffic_markdown(fetch_db: str, write_db: str, kernel: str, copy_bytes: int,
     return "\n".join(lines) + "\n"
 
 
+def gemm_traffic_markdown(fetch_db: str, write_db: str, copy_bytes: int, cmd_fetch: str, cmd_write: str) -> str:
+    """FETCH_SIZE / WRITE_SIZE of the grouped GEMM's gate/up (even) and down (odd)
+    launches, scaled like traffic_markdown."""
+    out = {}
+    for db, counter in ((fetch_db, "FETCH_SIZE"), (write_db, "WRITE_SIZE")):
+        per = counter_per_dispatch(db, counter)
+        kv = [v for n, v in per if n == "grouped_q4_gemm_kernel"]
+        cv = [v for n, v in per if "copyBuffer" in n]
+        if not kv or not cv:
+            raise SystemExit(f"{db}: no {counter} readings for the grouped GEMM or for a copyBuffer dispatch")
+        factor = copy_bytes / (max(cv) * 1024.0)
+        for name, v in (("gate/up", kv[0::2]), ("down", kv[1::2])):
+            out[(name, counter)] = (sum(v) / len(v), len(v), factor)
+    lines = [f"fetch command: `{cmd_fetch}`", f"write command: `{cmd_write}`", "",
+             "| launch | counter | avg KiB/dispatch | dispatches | scale | bytes per launch |", "|---|---|---|---|---|---|"]
+    for (name, counter), (avg, n, f) in out.items():
+        lines.append(f"| {name} | {counter} | {avg:.1f} | {n} | {f:.4f} | {int(round(avg * 1024 * f))} |")
+    lines += ["", f"kernel sources sha256: {all_sources_sha256()}"]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -135,8 +165,16 @@ def main():
     t.add_argument("--unit-bytes", type=int, required=True)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    m = sub.add_parser("gemm-traffic")
+    m.add_argument("--fetch", required=True)
+    m.add_argument("--write", required=True)
+    m.add_argument("--copy-bytes", type=int, required=True)
+    m.add_argument("--cmd-fetch", required=True)
+    m.add_argument("--cmd-write", required=True)
     args = ap.parse_args()
-    if args.what == "stats":
+    if args.what == "gemm-traffic":
+        print(gemm_traffic_markdown(args.fetch, args.write, args.copy_bytes, args.cmd_fetch, args.cmd_write), end="")
+    elif args.what == "stats":
         print(stats_markdown(args.db, args.cmd), end="")
     else:
         print(traffic_markdown(args.fetch, args.write, args.kernel, args.copy_bytes, args.unit_bytes,

@@ -9,7 +9,9 @@ steps are timed after `--warmup` untimed ones.  Bytes per layer are the
 algorithmic ones: the 9 touched experts at 4.5 bits per weight, the bf16
 router, the bf16 input and the fp32 output.
 
-Also reported: the 2,048-token prefill chunk through one layer (grouped-GEMM
+Also reported: the same 40 layers chained through a residual stream and ended
+by the LM-head argmax, as one decode step per token, enqueued launch by launch
+and replayed from a captured HIP graph; the 2,048-token prefill chunk through one layer (grouped-GEMM
 TFLOP/s against the bf16 MFMA peak), the LM-head GEMV + argmax
 (151,936 x 2048, two weight copies alternated so the 175 MB matrix is not
 cache-resident), and the CPU oracle timed on a bounded sample of the decode
@@ -101,9 +103,10 @@ def main():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip every leg but the 40-layer decode loop")
-    ap.add_argument("--legs", default="batch,prefill,wide,lmhead",
-                    help="comma list of the legs run after the decode loop: batch (several requests per step), "
-                         "prefill (2,048-token chunk), wide (512 experts, top-10), lmhead")
+    ap.add_argument("--legs", default="chain,batch,prefill,wide,lmhead",
+                    help="comma list of the legs run after the decode loop: chain (residual-chained step with the "
+                         "LM head, eager and as a replayed graph), batch (several requests per step), prefill "
+                         "(2,048-token chunk), wide (512 experts, top-10), lmhead")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (the known-size reference that scales the "
                          "byte counters of a rocprofv3 --pmc run)")
@@ -181,6 +184,46 @@ def main():
                      "kernel": "decode_layer_kernel (moe_ffn_decode, one launch per layer)",
                      "unit_bytes": layer_bytes, "avg_launch_us": round(layer_us, 3)},
     }
+    if "chain" in legs:
+        # ------------------- residual-chained decode step + LM head: eager launches vs a replayed graph
+        log("building the LM head for the chained step")
+        mat = synth.lm_head()
+        W = B.DeviceQ4(*mat, device=dev)
+        del mat
+        chain = workloads.DecodeChain(stack.layers, W, dev)
+        csteps = 16
+
+        def run_chain(fn):
+            for s in range(2):
+                chain.xs[0].copy_(stack.x[s % stack.n_steps][0])
+                fn()
+            torch.cuda.synchronize()
+            ev0.record()
+            h = time.perf_counter()
+            for s in range(csteps):
+                chain.xs[0].copy_(stack.x[s % stack.n_steps][0])
+                fn()
+            host = time.perf_counter() - h
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) * 1e3 / csteps, host * 1e6 / csteps
+
+        e_us, e_host = run_chain(chain.enqueue)
+        chain.capture()
+        g_us, g_host = run_chain(chain.replay)
+        step_bytes = args.layers * workloads.decode_layer_bytes(out_bytes=2) + \
+            workloads.q4_matrix_bytes(synth.VOCAB, synth.HIDDEN) + 2 * synth.HIDDEN
+        result["chain"] = {
+            "workload": f"decode step: {args.layers} layers chained through a residual stream (moe_ffn_decode "
+                        f"writes bf16(x + y)), then the LM-head argmax (151,936 x 2048); one token per step",
+            "eager_us_per_step": round(e_us, 1), "eager_host_enqueue_us_per_step": round(e_host, 1),
+            "graph_us_per_step": round(g_us, 1), "graph_host_enqueue_us_per_step": round(g_host, 1),
+            "graph_tokens_per_s": round(1e6 / g_us, 1), "bytes_per_step": step_bytes,
+            "graph_GB_s": round(step_bytes / (g_us * 1e-6) / 1e9, 1)}
+        log(f"chain: {result['chain']}")
+        del chain, W
+        torch.cuda.empty_cache()
+
     if "batch" in legs:
         # ------------------------------------------- batched decode (several requests per step)
         stack.enable_batch(8, dev)

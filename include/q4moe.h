@@ -49,7 +49,9 @@ enum {
   Q4MOE_EHIP = 4           /* a HIP runtime or launch error */
 };
 
-enum { Q4MOE_OUT_F32 = 0, Q4MOE_OUT_BF16 = 1 };
+/* Output forms.  Q4MOE_OUT_BF16_RESIDUAL is accepted by moe_ffn_decode only: it
+ * writes bf16(x + y), the next layer's input on a residual stream. */
+enum { Q4MOE_OUT_F32 = 0, Q4MOE_OUT_BF16 = 1, Q4MOE_OUT_BF16_RESIDUAL = 2 };
 
 /* Operation ids for q4moe_workspace_bytes. */
 enum {
@@ -142,8 +144,12 @@ int moe_permute(const int32_t* ids, int64_t T, int32_t top_k, int32_t n_experts,
  * One token through the MoE layer (batch-1 greedy decode step):
  *   y = sum_i w_i down_{e_i}(silu(gate_{e_i} x) * up_{e_i} x) + shared(x)
  * with (e_i, w_i) from the router as in moe_route_topk.  x bf16 [hidden]; y fp32
- * or bf16 [hidden].  ids_out int32 [top_k] and w_out fp32 [top_k] may be null.
- * Intermediates stay fp32.  Runs as one launch of one workgroup per compute
+ * or bf16 [hidden], or with Q4MOE_OUT_BF16_RESIDUAL the bf16 rounding (nearest,
+ * ties to even) of x + y computed in fp32, which is the next layer's input when
+ * layers are chained through a residual stream (lily-qwen3.8-flash-next, "How
+ * the speed was achieved": a decode step runs every layer on the GPU, so the
+ * host is off the critical path); y must not overlap x (Q4MOE_EINVAL).  ids_out
+ * int32 [top_k] and w_out fp32 [top_k] may be null.  Intermediates stay fp32.  Runs as one launch of one workgroup per compute
  * unit; values passed between workgroups carry a per-launch tag kept in the
  * workspace, so the Q4MOE_OP_FFN_DECODE workspace must be zero-filled before
  * its first use and must stay with one device; each call leaves it ready for

@@ -32,6 +32,8 @@ The pages never spell out the arithmetic, so it follows these plain readings
   the shared expert is added with weight 1.
 * Permutation: stable counting sort of the (token, slot) rows by expert id.
 * LM head: logits = W . x, greedy id = argmax with the lowest index on ties.
+* Residual stream (layers chained in a decode step): the next input is
+  bfloat16(x + y), round to nearest, ties to even.
 
 Every function is pinned by CPU tests against hand-computed examples, closed
 forms, library routines or brute force; none is "parity unpinned".
@@ -161,8 +163,11 @@ def permute(ids, n_experts: int):
 # ------------------------------------------------------------- expert FFN --
 
 def silu(z):
+    """silu(z) = z / (1 + e^-z), the SwiGLU gate activation; for z < 0 evaluated as the
+    equal z e^z / (1 + e^z), which never forms e^-z (that overflows below -709)."""
     z = np.asarray(z, dtype=np.float64)
-    return z / (1.0 + np.exp(-z))
+    ez = np.exp(-np.abs(z))                    # e^-|z| in (0, 1]
+    return np.where(z >= 0, z / (1.0 + ez), z * ez / (1.0 + ez))
 
 
 def swiglu(g, u):
@@ -231,6 +236,26 @@ def moe_ffn_prefill(layer, X_bits, ids=None):
     if layer.has_shared:
         Y += expert_ffn(layer.expert(layer.n_experts), X)
     return Y, sel, w, logits
+
+
+# ------------------------------------------------------- residual stream --
+
+def f64_to_bf16_rne(v) -> np.ndarray:
+    """Nearest bfloat16 to each float64 value, ties to an even significand, as bit patterns.
+
+    From the definition: bfloat16 keeps 8 significant bits, so v = m * 2**e with
+    m in [0.5, 1) rounds to rint(m * 256) * 2**(e - 8), where rint rounds halves
+    to even.  Finite values in the normal range of bfloat16 only."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    r = np.ldexp(np.rint(m * 256.0), e - 8)     # exact in float64 and in float32
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def residual_next(x_bits, y) -> np.ndarray:
+    """The next layer's input on a residual stream: bfloat16(x + y), rounded once from
+    the exact sum (x bfloat16 bits, y the layer's float64 output)."""
+    return f64_to_bf16_rne(bf16_to_f64(x_bits) + np.asarray(y, dtype=np.float64))
 
 
 # ---------------------------------------------------------------- LM head --

@@ -17,7 +17,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4moe.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
-OUT_F32, OUT_BF16 = 0, 1
+OUT_F32, OUT_BF16, OUT_BF16_RESIDUAL = 0, 1, 2  # residual: bf16(x + y), moe_ffn_decode only
 OP_GEMV, OP_GEMM, OP_ROUTE, OP_PERMUTE, OP_FFN_DECODE, OP_FFN_PREFILL, OP_LMHEAD, OP_FFN_DECODE_BATCH = range(8)
 
 EXPORTS = ("q4_gemv", "q4_gemm", "moe_route_topk", "moe_permute", "moe_ffn_decode", "moe_ffn_decode_batch",

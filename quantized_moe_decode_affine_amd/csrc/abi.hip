@@ -206,12 +206,18 @@ int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int o
     q4moe::DecodeLayer d;
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
-    if (!x || !aligned(x, 16) || !out_ok(y, out_dtype)) return Q4MOE_EINVAL;
+    const bool residual = out_dtype == Q4MOE_OUT_BF16_RESIDUAL;
+    if (!x || !aligned(x, 16) || !(residual ? y && aligned(y, 16) : out_ok(y, out_dtype))) return Q4MOE_EINVAL;
+    {  // y must not overlap x: the kernel still reads x while other workgroups write y
+      const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+      const uintptr_t xe = xb + (uintptr_t)d.hidden * 2, ye = yb + (uintptr_t)d.hidden * (out_dtype == Q4MOE_OUT_F32 ? 4 : 2);
+      if (xb < ye && yb < xe) return Q4MOE_EINVAL;
+    }
     if (q4moe::decode_lds_bytes(d) > kMaxDynLds) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_workspace_bytes(d.hidden, d.inter, d.n_experts, d.top_k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
-    return hip_status(q4moe::run_moe_ffn_decode(d, x, y, out_dtype == Q4MOE_OUT_BF16, ids_out, w_out, workspace,
-                                                (hipStream_t)stream));
+    const int mode = residual ? q4moe::kOutBf16Residual : out_dtype == Q4MOE_OUT_BF16 ? q4moe::kOutBf16 : q4moe::kOutF32;
+    return hip_status(q4moe::run_moe_ffn_decode(d, x, y, mode, ids_out, w_out, workspace, (hipStream_t)stream));
   } catch (...) {
     return Q4MOE_EHIP;
   }

@@ -55,7 +55,7 @@ struct DecodeParams {
   DecodeLayer L;
   const uint16_t* x;          // [H]
   void* y;                    // [H]
-  int out_bf16;
+  int out_mode;               // kOutF32, kOutBf16, kOutBf16Residual
   int32_t* ids_out;           // nullable [k]
   float* w_out;               // nullable [k]
   DecodeWs* ws;
@@ -540,7 +540,8 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
           float t = s_red[0][lane];
 #pragma unroll
           for (int w = 1; w < kWaves; ++w) t += s_red[w][lane];
-          if (p.out_bf16)
+          if (p.out_mode == kOutBf16Residual) t += bf16_bits_to_f32(p.x[nn]);
+          if (p.out_mode != kOutF32)
             reinterpret_cast<uint16_t*>(p.y)[nn] = (uint16_t)f32_to_bf16_bits(t);
           else
             reinterpret_cast<float*>(p.y)[nn] = t;
@@ -575,13 +576,13 @@ size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k) {
 
 size_t decode_lds_bytes(const DecodeLayer& L) { return decode_lds(L); }
 
-hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_bf16, int32_t* ids_out,
+hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_mode, int32_t* ids_out,
                               float* w_out, void* ws, hipStream_t stream) {
   DecodeParams p{};
   p.L = L;
   p.x = x;
   p.y = y;
-  p.out_bf16 = out_bf16;
+  p.out_mode = out_mode;
   p.ids_out = ids_out;
   p.w_out = w_out;
   char* w = static_cast<char*>(ws);

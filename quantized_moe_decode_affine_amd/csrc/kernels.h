@@ -38,7 +38,9 @@ struct DecodeLayer {
 };
 size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k);
 size_t decode_lds_bytes(const DecodeLayer& L);
-hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_bf16, int32_t* ids_out,
+// Output forms of the decode layer: fp32, bf16, or bf16(x + y) (the next layer's input).
+enum { kOutF32 = 0, kOutBf16 = 1, kOutBf16Residual = 2 };
+hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_mode, int32_t* ids_out,
                               float* w_out, void* ws, hipStream_t stream);
 
 // ---- batched decode, 1..kMaxBatch tokens (decode_batch.hip)

@@ -115,3 +115,62 @@ class DecodeStack:
                            (ids0 + 4 * k * mb * l) if record_ids else None, None, ws, wsn, stream)
             if st != B.OK:
                 B._check("moe_ffn_decode_batch", st)
+
+
+class DecodeChain:
+    """A decode step with every layer on the GPU: x_{l+1} = bf16(x_l + layer_l(x_l)) through
+    the layers (``moe_ffn_decode`` in its residual form, each writing the next layer's
+    input), then the LM-head argmax of the last x.  The step can be enqueued launch by
+    launch or captured once into a HIP graph and replayed, which takes the host off the
+    step's critical path: one replay call instead of one call per layer.
+
+    ``xs[0]`` is the step's input; the caller writes it (outside any graph) before a step."""
+
+    def __init__(self, layers, lm_head, device="cuda"):
+        self.layers, self.lm = list(layers), lm_head
+        H, k, L = self.layers[0].hidden, self.layers[0].top_k, len(self.layers)
+        self.xs = torch.zeros((L + 1, H), dtype=torch.bfloat16, device=device)   # x_0 .. x_L
+        self.ids = torch.zeros((L, k), dtype=torch.int32, device=device)
+        self.token = torch.zeros(1, dtype=torch.int32, device=device)
+        self.max_logit = torch.zeros(1, dtype=torch.float32, device=device)
+        self.ws = B.workspace(B.workspace_bytes(B.OP_FFN_DECODE, self.layers[0]), device)
+        self.ws_lm = B.workspace(B.workspace_bytes(B.OP_LMHEAD, W=lm_head, rows=1), device)
+        lib = B.load_library()
+        self._fn, self._lm = lib.moe_ffn_decode, lib.lmhead_argmax
+        self._refs = [ctypes.byref(d.struct) for d in self.layers]
+        self._lm_ref = ctypes.byref(lm_head.struct)
+        self.graph = None
+
+    @property
+    def n_layers(self) -> int:
+        return len(self.layers)
+
+    def enqueue(self) -> None:
+        """Enqueue one step (every layer, then the LM head) on the current stream."""
+        stream = torch.cuda.current_stream().cuda_stream
+        H, k = self.xs.shape[1], self.ids.shape[1]
+        x0, ids0 = self.xs.data_ptr(), self.ids.data_ptr()
+        ws, wsn = self.ws.data_ptr(), self.ws.numel()
+        for l in range(self.n_layers):
+            st = self._fn(self._refs[l], x0 + 2 * H * l, x0 + 2 * H * (l + 1), B.OUT_BF16_RESIDUAL,
+                          ids0 + 4 * k * l, None, ws, wsn, stream)
+            if st != B.OK:
+                B._check("moe_ffn_decode", st)
+        st = self._lm(self._lm_ref, x0 + 2 * H * self.n_layers, 1, self.token.data_ptr(), self.max_logit.data_ptr(),
+                      self.ws_lm.data_ptr(), self.ws_lm.numel(), stream)
+        if st != B.OK:
+            B._check("lmhead_argmax", st)
+
+    def capture(self) -> None:
+        """Run one step eagerly (so every host-side query the calls make is answered and
+        cached), then capture a step into a graph."""
+        self.enqueue()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.enqueue()
+        torch.cuda.synchronize()
+        self.graph = g
+
+    def replay(self) -> None:
+        self.graph.replay()

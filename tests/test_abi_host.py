@@ -110,18 +110,29 @@ def test_ffn_rejects(lib):
         _layer(router=None), _layer(router=A + 8),
     ]
     for L in bad_shapes:
-        assert d(ctypes.byref(L), A, A, 0, None, None, A, need_d, None) == B.EINVAL
+        assert d(ctypes.byref(L), A, A2, 0, None, None, A, need_d, None) == B.EINVAL
         assert p(ctypes.byref(L), A, 50, A, 0, A, need_p, None) == B.EINVAL
     L = _layer()
     L.down = _mat(4, 64, 128)            # down must be hidden x inter
-    assert d(ctypes.byref(L), A, A, 0, None, None, A, need_d, None) == B.EINVAL
+    assert d(ctypes.byref(L), A, A2, 0, None, None, A, need_d, None) == B.EINVAL
     L = _layer()
     L.sh_up = _mat(2, 64, 128)           # shared expert must have count 1
-    assert d(ctypes.byref(L), A, A, 0, None, None, A, need_d, None) == B.EINVAL
+    assert d(ctypes.byref(L), A, A2, 0, None, None, A, need_d, None) == B.EINVAL
     assert d(ctypes.byref(_layer(n_experts=2048, gate=_mat(2048, 64, 128), up=_mat(2048, 64, 128),
-                                 down=_mat(2048, 128, 64))), A, A, 0, None, None, A, need_d, None) == B.EUNSUPPORTED
-    assert d(ctypes.byref(good), A, A, 0, None, None, A, need_d - 1, None) == B.EWORKSPACE
-    assert d(ctypes.byref(good), A + 8, A, 0, None, None, A, need_d, None) == B.EINVAL
+                                 down=_mat(2048, 128, 64))), A, A2, 0, None, None, A, need_d, None) == B.EUNSUPPORTED
+    assert d(ctypes.byref(good), A, A2, 0, None, None, A, need_d - 1, None) == B.EWORKSPACE
+    assert d(ctypes.byref(good), A + 8, A2, 0, None, None, A, need_d, None) == B.EINVAL
+    # the residual form writes bf16(x + y): y may not overlap x (hidden 128: x spans 256 bytes)
+    for mode in (B.OUT_F32, B.OUT_BF16, B.OUT_BF16_RESIDUAL):
+        assert d(ctypes.byref(good), A, A, mode, None, None, A, need_d, None) == B.EINVAL
+        assert d(ctypes.byref(good), A, A + 128, mode, None, None, A, need_d, None) == B.EINVAL
+        # y just below x: an fp32 y (512 bytes) reaches into x, a bf16 one (256 bytes) does not
+        want = B.EINVAL if mode == B.OUT_F32 else B.EWORKSPACE
+        assert d(ctypes.byref(good), A + 256, A, mode, None, None, A, need_d - 1, None) == want
+        assert d(ctypes.byref(good), A, A + 256, mode, None, None, A, need_d - 1, None) == B.EWORKSPACE
+    assert d(ctypes.byref(good), A, A2, 3, None, None, A, need_d, None) == B.EINVAL
+    # the residual form is decode-only
+    assert p(ctypes.byref(good), A, 50, A2, B.OUT_BF16_RESIDUAL, A, need_p, None) == B.EINVAL
     assert p(ctypes.byref(good), A, -3, A, 0, A, need_p, None) == B.EINVAL
     assert p(ctypes.byref(good), A, 50, A, 0, A, need_p - 256, None) == B.EWORKSPACE
     assert p(ctypes.byref(good), A, 0, A, 0, None, 0, None) == B.OK

@@ -316,3 +316,51 @@ def test_lmhead_brute_force_batch():
     # chunked evaluation equals one-shot
     np.testing.assert_allclose(orc.lmhead_logits(codes, scales, biases, X, rows_per_chunk=50),
                                orc.bf16_to_f64(X) @ W.T, rtol=1e-13)
+
+
+# ------------------------------------------------------------ residual stream --
+
+def test_bf16_rne_hand_ties():
+    """Worked by hand: bfloat16 spacing at 1 is 2^-7, so 1 + 2^-8 is a tie (rounds down to
+    the even 1.0), 1 + 3*2^-8 is a tie between 1 + 2^-7 (odd) and 1 + 2^-6 (even), and
+    anything past a tie rounds away from it."""
+    cases = {
+        1.0 + 2.0 ** -8: 0x3F80,
+        1.0 + 3 * 2.0 ** -8: 0x3F82,
+        1.0 + 2.0 ** -8 + 2.0 ** -20: 0x3F81,
+        -(1.0 + 2.0 ** -8): 0xBF80,
+        -(1.0 + 3 * 2.0 ** -8): 0xBF82,
+        3.0: 0x4040,
+        0.0: 0x0000,
+        2.0 - 2.0 ** -9: 0x4000,  # rounds up across the binade boundary
+    }
+    for v, bits in cases.items():
+        assert int(orc.f64_to_bf16_rne(v)) == bits, (v, hex(int(orc.f64_to_bf16_rne(v))), hex(bits))
+
+
+def test_bf16_rne_brute_force():
+    """Against a search over neighbouring bfloat16 patterns: the nearest one, and on an exact
+    tie the one with an even last significand bit."""
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.normal(0, 1, 2000), rng.normal(0, 1e3, 500), rng.normal(0, 1e-3, 500),
+                        (1 + rng.integers(0, 256, 200) / 128 + 2.0 ** -8) * rng.choice([-1, 1], 200)])
+    got = orc.f64_to_bf16_rne(v)
+    for val, g in zip(v, got):
+        base = int(np.float32(val).view(np.uint32)) >> 16
+        best = None
+        for cand in range(base - 2, base + 3):
+            cv = float(np.uint32((cand & 0xFFFF) << 16).view(np.float32))
+            d = abs(cv - val)
+            key = (d, cand & 1)  # nearest, then even
+            if best is None or key < best[0]:
+                best = (key, cand & 0xFFFF)
+        assert int(g) == best[1], (val, hex(int(g)), hex(best[1]))
+
+
+def test_residual_next_exact_cases():
+    """x + 0 returns x; sums that are bfloat16 values come back exactly."""
+    x = synth.token_rows(8, 1, 256)[0]
+    assert np.array_equal(orc.residual_next(x, np.zeros(256)), x)
+    xf = orc.bf16_to_f64(x)
+    z = orc.residual_next(x, xf)  # x + x = 2x: exact, one binade up
+    assert np.array_equal(orc.bf16_to_f64(z), 2 * xf)

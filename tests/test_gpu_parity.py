@@ -430,3 +430,46 @@ def test_prefill_4096_tokens_512_experts_top10(B):
     err, worst = _prefill_check(B, layer, dl, X, with_bf16=False)
     say(f"prefill 4096 tokens rel_l2={err:.3e} worst={worst:.3e}")
     assert err <= REL_L2_TOL and worst <= 2 * REL_L2_TOL
+
+
+# ------------------------------------------- rows far outside the fp16 range --
+
+def _scaled_rows(seed, T, H):
+    """Rows of N(0,1) values, some scaled far past fp16's range (2^20: up to ~4e6), some far
+    below it (2^-20), one all zero, one mixing magnitudes 2^-24..2^12 inside the row."""
+    X = orc.bf16_to_f64(synth.token_rows(seed, T, H))
+    X[0] *= 2.0 ** 20
+    X[1] *= 2.0 ** -20
+    X[2] = 0.0
+    X[3] *= np.ldexp(1.0, (np.arange(H) % 37) - 24)
+    if T > 5:
+        X[5] *= 2.0 ** 14
+    return synth.to_bf16_bits(X)
+
+
+def test_gemm_row_magnitudes(B):
+    """q4_gemm scales each row by a power of two into fp16: rows of any magnitude keep the
+    accuracy of ordinary rows, and a zero row gives exactly zero."""
+    m, n, k = 40, 300, 512
+    say(f"gemm row magnitudes m={m} n={n} k={k}")
+    mat = synth.q4_matrix(77, 0, 0, 0, n, k)
+    X = _scaled_rows(77, m, k)
+    Y = B.q4_gemm(_q4(B, mat), B.bf16_tensor(X), 0)
+    _sync()
+    got, ref = to_f64(Y), orc.q4_gemm(*mat, X)
+    assert np.all(got[2] == 0.0)
+    for r in range(m):
+        if r != 2:
+            assert rel_l2(got[r], ref[r]) <= 1e-3, (r, rel_l2(got[r], ref[r]))
+
+
+def test_prefill_row_magnitudes(B):
+    """The prefill layer on rows far outside fp16's range (and their SwiGLU activations,
+    which scale with the square of the row) against the oracle, row by row."""
+    T, H, I, E, k = 64, 256, 128, 16, 4
+    say("prefill row magnitudes")
+    layer = synth.moe_layer(94, 0, H, I, E, k)
+    dl = B.DeviceLayer(layer)
+    X = _scaled_rows(94, T, H)
+    err, worst = _prefill_check(B, layer, dl, X, with_bf16=False)
+    assert err <= REL_L2_TOL and worst <= 2 * REL_L2_TOL, (err, worst)

@@ -16,7 +16,10 @@ Sources (web pages; no code is taken from them):
   bandwidth-bound stream of 4-bit weights; prefill runs the expert GEMM on
   token-to-expert groups.
 * "2026-09-02: Lily vs MLX 0.32.2", "Measurement contract": batch 1, greedy
-  argmax, prompts processed in 2,048-token chunks.
+  argmax, prompts processed in 2,048-token chunks; "Hardware and software": the
+  checkpoint is affine Q4 with group 64, with affine Q8 exceptions.
+* "lily-qwen3.8-flash-next" README, "The model": the q4-xl checkpoint keeps the
+  shared expert, the LM head and the embedding at 8 bits.
 
 The pages never spell out the arithmetic, so it follows these plain readings
 (each is listed with its reason in the design notes):
@@ -24,7 +27,9 @@ The pages never spell out the arithmetic, so it follows these plain readings
 * A 4-bit code for column j of a row sits in 32-bit word j//8 at bits
   [4*(j%8), 4*(j%8)+4) (least significant nibble first, as MLX packs).
 * One (scale, bias) pair per 64 consecutive columns of a row; the weight is
-  ``w = scale * q + bias``.
+  ``w = scale * q + bias``.  8-bit matrices (the checkpoint's 8-bit exceptions)
+  hold byte j%4 of word j//4, least significant byte first, with the same
+  groups and formula.
 * Routing: logits = router . x, softmax over all experts, keep the top_k
   largest (descending, equal logits ordered by lower expert id), renormalise
   the kept probabilities to sum to one.
@@ -62,9 +67,29 @@ def unpack_codes(codes, k: int) -> np.ndarray:
     return ((words >> shifts) & np.uint32(0xF)).astype(np.int64)
 
 
+def unpack_codes8(codes, k: int) -> np.ndarray:
+    """8-bit codes q[n][j] in 0..255 for j < k: byte j%4 of word j//4, least significant first."""
+    codes = np.asarray(codes, dtype=np.uint32)
+    j = np.arange(k)
+    words = codes[..., j // 4]
+    shifts = (8 * (j % 4)).astype(np.uint32)
+    return ((words >> shifts) & np.uint32(0xFF)).astype(np.int64)
+
+
+def code_bits(codes, k: int) -> int:
+    """4 or 8: the code width of a matrix whose rows hold k columns in codes.shape[-1] words."""
+    words = np.asarray(codes).shape[-1]
+    if words * 8 == k:
+        return 4
+    if words * 4 == k:
+        return 8
+    raise ValueError(f"{words} code words per row do not hold {k} columns at 4 or 8 bits")
+
+
 def dequantize(codes, scales, biases, k: int) -> np.ndarray:
-    """Affine dequantization w = scale*q + bias, one (scale, bias) per 64 columns (exact in fp64)."""
-    q = unpack_codes(codes, k).astype(np.float64)
+    """Affine dequantization w = scale*q + bias, one (scale, bias) per 64 columns (exact in fp64);
+    q is the 4-bit or 8-bit code, by the width of ``codes``."""
+    q = (unpack_codes(codes, k) if code_bits(codes, k) == 4 else unpack_codes8(codes, k)).astype(np.float64)
     s = np.repeat(bf16_to_f64(scales), GROUP, axis=-1)
     b = np.repeat(bf16_to_f64(biases), GROUP, axis=-1)
     return s * q + b

@@ -75,6 +75,23 @@ def q4_matrix(seed: int, layer: int, expert: int, matrix: int, n: int, k: int):
     return codes, scales, biases
 
 
+def q8_matrix(seed: int, layer: int, expert: int, matrix: int, n: int, k: int):
+    """One affine-Q8 matrix of n rows and k columns: 8-bit codes, 4 per uint32 word.
+
+    Codes are uniform bytes; scales ``|N(0, 0.02/16)|`` and biases ``-128*scale +
+    N(0, 0.002)``, so the weights span the same range as the 4-bit ones.
+    Returns ``(codes uint32[n][k/4], scales uint16[n][k/64], biases uint16[n][k/64])``.
+    """
+    if k % GROUP:
+        raise ValueError("k must be a multiple of 64")
+    rng = _rng(seed, layer, expert, matrix, 8)
+    codes = rng.integers(0, 1 << 32, size=(n, k // 4), dtype=np.uint32)
+    scales = to_bf16_bits(np.abs(rng.normal(0.0, 0.02 / 16, size=(n, k // GROUP))))
+    noise = rng.normal(0.0, 0.002, size=(n, k // GROUP))
+    biases = to_bf16_bits(-128.0 * _bf16_bits_to_f32(scales).astype(np.float64) + noise)
+    return codes, scales, biases
+
+
 def router(seed: int, layer: int, n_experts: int = N_EXPERTS, hidden: int = HIDDEN):
     """bfloat16 router matrix [n_experts][hidden], N(0, 0.02)."""
     return to_bf16_bits(_rng(seed, layer, ROUTER_STREAM).normal(0.0, 0.02, size=(n_experts, hidden)))
@@ -173,9 +190,9 @@ def moe_layer(seed: int, layer: int = 0, hidden: int = HIDDEN, inter: int = INTE
                     gate, up, down, *sh)
 
 
-def lm_head(seed: int = 4, rows: int = VOCAB, hidden: int = HIDDEN):
-    """LM-head-shaped Q4 matrix (rows x hidden)."""
-    return q4_matrix(seed, 0, 0, 0, rows, hidden)
+def lm_head(seed: int = 4, rows: int = VOCAB, hidden: int = HIDDEN, bits: int = 4):
+    """LM-head-shaped affine matrix (rows x hidden), 4-bit or 8-bit codes."""
+    return (q8_matrix if bits == 8 else q4_matrix)(seed, 0, 0, 0, rows, hidden)
 
 
 def fnv1a64(values) -> int:

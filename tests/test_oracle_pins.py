@@ -364,3 +364,59 @@ def test_residual_next_exact_cases():
     xf = orc.bf16_to_f64(x)
     z = orc.residual_next(x, xf)  # x + x = 2x: exact, one binade up
     assert np.array_equal(orc.bf16_to_f64(z), 2 * xf)
+
+
+# ------------------------------------------------------- 8-bit affine codes --
+
+def _pack_bytes(q_rows):
+    """Independent packer: element j of a row goes to byte j%4 of word j//4 (LSB first)."""
+    return np.array([[struct.unpack("<I", bytes(int(v) for v in row[4 * w:4 * w + 4]))[0]
+                      for w in range(len(row) // 4)] for row in q_rows], dtype=np.uint32)
+
+
+def test_q8_dequant_hand_example():
+    """Worked by hand: one row, K = 128, x = ones.  Group 0 holds q = 0..63 with scale 0.5 and
+    bias -4, so w_j = j/2 - 4 (w_13 = 2.5) and the group sums to 1008 - 256 = 752; group 1
+    holds q = 255 with scale 0.25 and bias 1, so w = 64.75 and the group sums to 4144."""
+    words = [0x03020100 + 0x04040404 * i for i in range(16)] + [0xFFFFFFFF] * 16
+    codes = np.array([words], dtype=np.uint32)
+    scales = np.array([[0x3F00, 0x3E80]], dtype=np.uint16)
+    biases = np.array([[0xC080, 0x3F80]], dtype=np.uint16)
+    W = orc.dequantize(codes, scales, biases, 128)
+    assert W[0, 13] == 2.5 and W[0, 63] == 27.5 and W[0, 64] == 64.75
+    ones = np.full(128, 0x3F80, dtype=np.uint16)
+    assert orc.q4_gemv(codes, scales, biases, ones)[0] == 752.0 + 4144.0
+
+
+def test_q8_unpack_roundtrips_independent_packer_and_width():
+    rng = np.random.default_rng(6)
+    q = rng.integers(0, 256, size=(3, 192))
+    codes = _pack_bytes(q)
+    np.testing.assert_array_equal(orc.unpack_codes8(codes, 192), q)
+    assert orc.code_bits(codes, 192) == 8 and orc.code_bits(_pack_nibbles(q % 16), 192) == 4
+    with pytest.raises(ValueError):
+        orc.code_bits(codes, 100)
+
+
+@pytest.mark.parametrize("n,k,seed", [(3, 64, 0), (2, 128, 1)])
+def test_q8_gemv_exact_rational_brute_force(n, k, seed):
+    """y from Fractions on an independently packed 8-bit matrix equals the fp64 oracle exactly."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 256, size=(n, k))
+    dy = [0.5, 0.25, 0.125, 0.75, 1.5, 0.0625, 2.0, -0.375]
+    s = rng.choice(dy[:7], size=(n, k // 64)) / 64
+    b = rng.choice(dy, size=(n, k // 64)) * -1.0
+    x = rng.choice([-2.0, -1.0, -0.5, 0.0, 0.25, 1.0, 3.0], size=k)
+    codes = _pack_bytes(q)
+    scales = np.array([[_bf16_bits_of(v) for v in r] for r in s], dtype=np.uint16)
+    biases = np.array([[_bf16_bits_of(v) for v in r] for r in b], dtype=np.uint16)
+    xb = np.array([_bf16_bits_of(v) for v in x], dtype=np.uint16)
+    expect = []
+    for r in range(n):
+        acc = Fraction(0)
+        for j in range(k):
+            acc += (Fraction(s[r, j // 64]) * int(q[r, j]) + Fraction(b[r, j // 64])) * Fraction(x[j])
+        expect.append(float(acc))
+    assert list(orc.q4_gemv(codes, scales, biases, xb)) == expect
+    ids, top, _ = orc.lmhead_argmax(codes, scales, biases, xb)
+    assert int(ids[0]) == int(np.argmax(expect)) and top[0] == max(expect)

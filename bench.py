@@ -369,6 +369,31 @@ def main():
         log(f"lmhead: {lm}")
         del Ws
         torch.cuda.empty_cache()
+        # the same head with 8-bit codes (the q4-xl checkpoint keeps its LM head at 8 bits)
+        mat = synth.lm_head(bits=8)
+        Ws = [B.DeviceQ4(*mat, device=dev), B.DeviceQ4(*mat, device=dev)]
+        del mat
+        lm8 = {}
+        for batch in (1, 4):
+            Xh = B.bf16_tensor(synth.token_rows(4, batch, synth.HIDDEN, index=batch), dev)
+            wsl = B.workspace(B.workspace_bytes(B.OP_LMHEAD, W=Ws[0], rows=batch), dev)
+            for i in range(4):
+                B.lmhead_argmax(Ws[i % 2], Xh, ws=wsl)
+            torch.cuda.synchronize()
+            reps = 20
+            ev0.record()
+            for i in range(reps):
+                B.lmhead_argmax(Ws[i % 2], Xh, ws=wsl)
+            ev1.record()
+            torch.cuda.synchronize()
+            us = ev0.elapsed_time(ev1) * 1e3 / reps
+            nbytes = Ws[0].nbytes + batch * synth.HIDDEN * 2
+            lm8[f"B{batch}"] = {"us": round(us, 2), "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        result["lmhead_q8"] = dict(workload="LM-head affine-Q8 GEMV + greedy argmax, 151,936 x 2048", **lm8)
+        log(f"lmhead q8: {lm8}")
+        del Ws
+        torch.cuda.empty_cache()
 
     if args.calib_copy > 0:
         n = args.calib_copy << 20

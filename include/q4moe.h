@@ -65,7 +65,13 @@ enum {
   Q4MOE_OP_FFN_DECODE_BATCH = 7
 };
 
-/* A Q4 matrix, or `count` stacked matrices of the same shape. */
+/* An affine matrix of 4-bit codes (the default), or of 8-bit codes (the
+ * checkpoint's 8-bit exceptions: "lily-qwen3.8-flash-next" README, "The model";
+ * "2026-09-02: Lily vs MLX 0.32.2", "Hardware and software"), or `count` stacked
+ * matrices of the same shape.  8-bit codes: uint32 [count][n][k/4], code j of a
+ * row in byte j%4 of word j/4 (least significant first), same groups and
+ * w = scale*q + bias.  Only q4_gemv and lmhead_argmax take 8-bit matrices; the
+ * other calls return Q4MOE_EUNSUPPORTED for them. */
 typedef struct {
   const uint32_t* codes;
   const q4moe_bf16* scales;
@@ -73,6 +79,8 @@ typedef struct {
   int64_t count;  /* >= 1 */
   int64_t n;      /* rows per matrix */
   int64_t k;      /* columns, a multiple of 64 */
+  int32_t bits;   /* code width: 4 (0 also means 4) or 8 */
+  int32_t reserved;  /* 0 */
 } q4moe_matrix;
 
 /*

@@ -32,7 +32,8 @@ class Q4Error(RuntimeError):
 
 class q4moe_matrix(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
-                ("count", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+                ("count", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class q4moe_layer(ctypes.Structure):
@@ -109,18 +110,25 @@ def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 class DeviceQ4:
-    """A Q4 matrix (or a stack of them) resident on the device."""
+    """An affine matrix (or a stack of them) resident on the device: 4-bit codes, or 8-bit
+    codes when the code words per row hold 4 columns each (k is taken from the groups)."""
 
     def __init__(self, codes: np.ndarray, scales: np.ndarray, biases: np.ndarray, device="cuda"):
         if codes.ndim == 2:
             codes, scales, biases = codes[None], scales[None], biases[None]
         self.count, self.n, words = codes.shape
-        self.k = words * 8
+        self.k = scales.shape[-1] * 64
+        if words * 8 == self.k:
+            self.bits = 4
+        elif words * 4 == self.k:
+            self.bits = 8
+        else:
+            raise ValueError(f"{words} code words per row do not hold {self.k} columns at 4 or 8 bits")
         self.codes = _dev(codes, device)
         self.scales = _dev(scales, device)
         self.biases = _dev(biases, device)
         self.struct = q4moe_matrix(self.codes.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
-                                   self.count, self.n, self.k)
+                                   self.count, self.n, self.k, self.bits, 0)
 
     @property
     def nbytes(self) -> int:

@@ -34,6 +34,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool matrix_ok(const q4moe_matrix* W) {
   if (!W || !W->codes || !W->scales || !W->biases) return false;
+  if (W->bits != 0 && W->bits != 4 && W->bits != 8) return false;
   if (W->count < 1 || W->n < 1 || W->k < 64 || W->k % 64) return false;
   if (!aligned(W->codes, 16) || !aligned(W->scales, 2) || !aligned(W->biases, 2)) return false;
   return true;
@@ -44,6 +45,8 @@ bool matrix_shape(const q4moe_matrix& W, int64_t count, int64_t n, int64_t k) {
 }
 
 Q4Mat to_mat(const q4moe_matrix& W) { return Q4Mat{W.codes, W.scales, W.biases}; }
+
+bool is_q8(const q4moe_matrix& W) { return W.bits == 8; }
 
 bool out_ok(const void* y, int out_dtype) {
   return y && aligned(y, 16) && (out_dtype == Q4MOE_OUT_F32 || out_dtype == Q4MOE_OUT_BF16);
@@ -62,6 +65,8 @@ int layer_check(const q4moe_layer* L, q4moe::DecodeLayer* d) {
   if (shared && (!matrix_shape(L->sh_gate, 1, I, H) || !matrix_shape(L->sh_up, 1, I, H) ||
                  !matrix_shape(L->sh_down, 1, H, I)))
     return Q4MOE_EINVAL;
+  for (const q4moe_matrix* m : {&L->gate, &L->up, &L->down, &L->sh_gate, &L->sh_up, &L->sh_down})
+    if (is_q8(*m)) return Q4MOE_EUNSUPPORTED;  // the layer kernels read 4-bit codes only
   d->hidden = L->hidden;
   d->inter = L->inter;
   d->n_experts = L->n_experts;
@@ -144,6 +149,11 @@ int q4_gemv(const q4moe_matrix* W, const q4moe_bf16* x, void* y, int out_dtype, 
     if (!matrix_ok(W) || !x || !aligned(x, 16) || !out_ok(y, out_dtype)) return Q4MOE_EINVAL;
     if (W->k > kMaxGemvK) return Q4MOE_EUNSUPPORTED;
     const int64_t rows = W->count * W->n;
+    if (is_q8(*W)) {
+      if (q4moe::q8_gemv_lds_bytes((int)W->k, 1) > kMaxDynLds) return Q4MOE_EUNSUPPORTED;
+      return hip_status(q4moe::run_q8_gemv(W->codes, W->scales, W->biases, rows, (int)W->k, x, y,
+                                           out_dtype == Q4MOE_OUT_BF16, (hipStream_t)stream));
+    }
     return hip_status(q4moe::run_q4_gemv(W->codes, W->scales, W->biases, rows, (int)W->k, x, y,
                                          out_dtype == Q4MOE_OUT_BF16, (hipStream_t)stream));
   } catch (...) {
@@ -156,7 +166,7 @@ int q4_gemm(const q4moe_matrix* W, const q4moe_bf16* X, int64_t m, void* Y, int 
   try {
     if (!matrix_ok(W) || !X || !aligned(X, 16) || m < 0 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
     const int64_t n = W->count * W->n;
-    if (n > kMaxRows32 || m > kMaxRows32) return Q4MOE_EUNSUPPORTED;
+    if (n > kMaxRows32 || m > kMaxRows32 || is_q8(*W)) return Q4MOE_EUNSUPPORTED;
     if (m == 0) return Q4MOE_OK;
     const size_t need = q4moe::gemm_workspace_bytes(m, (int)W->k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
@@ -266,12 +276,17 @@ int lmhead_argmax(const q4moe_matrix* W, const q4moe_bf16* X, int64_t B, int32_t
     if (!matrix_ok(W) || !X || !aligned(X, 16) || !ids || B < 1) return Q4MOE_EINVAL;
     const int64_t rows = W->count * W->n;
     if (B > 8 || rows > kMaxRows32 || B * W->k > kMaxGemvK) return Q4MOE_EUNSUPPORTED;
+    if (is_q8(*W) && (B > 7 || q4moe::q8_gemv_lds_bytes((int)W->k, (int)B) > kMaxDynLds))
+      return Q4MOE_EUNSUPPORTED;
     const size_t need = lmhead_ws(rows, W->k, B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
     char* w = static_cast<char*>(workspace);
     unsigned* done = reinterpret_cast<unsigned*>(w);
     float* part_val = reinterpret_cast<float*>(w + 256);
     int32_t* part_idx = reinterpret_cast<int32_t*>(w + 256 + (size_t)q4moe::kMaxGemvBlocks * B * 4);
+    if (is_q8(*W))
+      return hip_status(q4moe::run_lmhead_argmax_q8(W->codes, W->scales, W->biases, rows, (int)W->k, X, (int)B,
+                                                    ids, max_logit, part_val, part_idx, done, (hipStream_t)stream));
     return hip_status(q4moe::run_lmhead_argmax(W->codes, W->scales, W->biases, rows, (int)W->k, X, (int)B, ids,
                                                max_logit, part_val, part_idx, done, (hipStream_t)stream));
   } catch (...) {

@@ -311,6 +311,122 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
   if constexpr (ARGMAX) argmax_epilogue<B>(best, besti, p);
 }
 
+
+// Batch-1..7 GEMV over 8-bit affine codes (the 8-bit exceptions of the checkpoint:
+// lily-qwen3.8-flash-next README, "The model": the q4-xl conversion keeps the LM head
+// and the shared expert at 8 bits; "2026-09-02: Lily vs MLX 0.32.2", "Hardware and
+// software": affine Q8 router-gate exceptions).  Code j of a row is byte j%4 of word
+// j/4; w = scale*q + bias per 64-column group.  The activations are staged once per
+// workgroup in LDS as fp32 with their per-group sums, the groups interleaved by 4-value
+// chunks (chunk c of group g at (c*G + g)*4) so that the lanes of a row, each on its own
+// group, read consecutive 16-byte words; a lane takes one group of a row
+// at a time (64 code bytes: four 16-byte loads), converts each byte to fp32 (exact),
+// and accumulates the exact 8-bit x 8-bit products in fp32: per group
+// scale * sum(x q) + bias * sum(x).  Rows are strided over the waves as in the
+// 4-bit kernel, S rows per lane in flight; the L lanes of a row reduce with DPP.
+template <int S, int B, bool ARGMAX>
+__global__ __launch_bounds__(256) void q8_gemv_kernel(GemvParams p) {
+  extern __shared__ __align__(16) float q8_smem[];
+  const int K = p.k, G = K >> 6, C16 = K >> 4;  // C16: 16-byte code chunks per row
+  float* xs = q8_smem;             // [B][16 chunks][G][4]
+  float* gs = q8_smem + B * K;     // [B][G]
+  auto xslot = [&](int b, int g, int j) { return b * K + ((j >> 2) * G + g) * 4 + (j & 3); };
+  for (int i = threadIdx.x; i < B * K; i += blockDim.x) {
+    const int b = i / K, c = i - b * K;
+    xs[xslot(b, c >> 6, c & 63)] = bf16_bits_to_f32(p.x[i]);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < B * G; i += blockDim.x) {
+    const int b = i / G, g = i - b * G;
+    float t = 0.f;
+    for (int j = 0; j < kGroup; ++j) t += xs[xslot(b, g, j)];  // fixed order
+    gs[i] = t;
+  }
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int L = 1 << p.lshift;
+  const int sub = lane & (L - 1);
+  const int rsub = lane >> p.lshift;
+  const int rpi = kWave >> p.lshift;
+  const int wpb = blockDim.x / kWave;
+  const int64_t wave = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * wpb;
+  const int64_t step = (int64_t)rpi * S;
+
+  float best[B];
+  int32_t besti[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) { best[b] = -INFINITY; besti[b] = 0x7FFFFFFF; }
+
+  for (int64_t base = wave * step; base < p.rows; base += nwaves * step) {
+    float acc[S][B];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[s][b] = 0.f;
+    for (int g = sub; g < G; g += L) {
+      uint4 c[S][4];
+      float sc[S], bi[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int64_t row = min(base + (int64_t)s * rpi + rsub, p.rows - 1);  // past the end: loaded, unused
+        const uint4* cr = p.codes + row * C16 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[s][i] = cr[i];
+        sc[s] = bf16_bits_to_f32(p.scales[row * G + g]);
+        bi[s] = bf16_bits_to_f32(p.biases[row * G + g]);
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float4* xv = reinterpret_cast<const float4*>(xs + b * K) + g;  // chunk c at xv[c * G]
+        float P[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) P[s] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float4 x4 = xv[(4 * i + w) * G];
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+              const uint32_t word = w == 0 ? c[s][i].x : w == 1 ? c[s][i].y : w == 2 ? c[s][i].z : c[s][i].w;
+              P[s] = fmaf(x4.x, (float)(word & 0xFFu), P[s]);
+              P[s] = fmaf(x4.y, (float)((word >> 8) & 0xFFu), P[s]);
+              P[s] = fmaf(x4.z, (float)((word >> 16) & 0xFFu), P[s]);
+              P[s] = fmaf(x4.w, (float)(word >> 24), P[s]);
+            }
+          }
+        }
+        const float xsum = gs[b * G + g];
+#pragma unroll
+        for (int s = 0; s < S; ++s) acc[s][b] += fmaf(sc[s], P[s], bi[s] * xsum);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int64_t row = base + (int64_t)s * rpi + rsub;
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[s][b] = group_sum_rt(acc[s][b], p.lshift);
+      if (row >= p.rows) continue;
+      if constexpr (ARGMAX) {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          if (better(acc[s][b], (int32_t)row, best[b], besti[b])) { best[b] = acc[s][b]; besti[b] = (int32_t)row; }
+      } else if (sub == 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          if (p.out_bf16)
+            reinterpret_cast<uint16_t*>(p.y)[(size_t)b * p.rows + row] = (uint16_t)f32_to_bf16_bits(acc[s][b]);
+          else
+            reinterpret_cast<float*>(p.y)[(size_t)b * p.rows + row] = acc[s][b];
+        }
+      }
+    }
+  }
+  if constexpr (ARGMAX) argmax_epilogue<B>(best, besti, p);
+}
+
 typedef short mfma4_bf16_t __attribute__((ext_vector_type(4)));
 
 // Broadcast of quad lane I's value to its whole quad (DPP quad_perm [I,I,I,I]).
@@ -596,6 +712,84 @@ hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, cons
     case 6: return run_lmhead_b<6>(p, ids, max_logit, stream);
     case 7: return run_lmhead_b<7>(p, ids, max_logit, stream);
     case 8: return run_lmhead_b<8>(p, ids, max_logit, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+namespace {
+
+size_t q8_lds(int k, int B) { return (size_t)B * (k + k / kGroup) * 4; }
+
+template <int S, int B, bool ARGMAX>
+hipError_t launch_q8(GemvParams p, hipStream_t stream) {
+  const int G = p.k / kGroup;
+  p.lshift = log2_floor(G < kWave ? G : kWave);
+  const size_t lds = q8_lds(p.k, B);
+  static int resident = -1;  // per instantiation
+  if (resident < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, q8_gemv_kernel<S, B, ARGMAX>, 256, lds) != hipSuccess ||
+        n < 1)
+      n = 1;
+    resident = n;
+  }
+  const int64_t rows_per_wave_iter = (int64_t)(kWave >> p.lshift) * S;
+  const int64_t iters = (p.rows + rows_per_wave_iter - 1) / rows_per_wave_iter;
+  int64_t blocks = (iters + 3) / 4;
+  int64_t max_blocks = (int64_t)device_cu_count() * resident;
+  if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // bounds the argmax partials
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((q8_gemv_kernel<S, B, ARGMAX>), dim3((unsigned)blocks), dim3(256), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t run_lmhead_q8_b(GemvParams& p, int32_t* ids, float* max_logit, hipStream_t stream) {
+  p.ids = ids;
+  p.max_logit = max_logit;
+  return launch_q8<B <= 2 ? 2 : 1, B, true>(p, stream);
+}
+
+}  // namespace
+
+size_t q8_gemv_lds_bytes(int k, int B) { return q8_lds(k, B); }
+
+hipError_t run_q8_gemv(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t rows,
+                       int k, const uint16_t* x, void* y, int out_bf16, hipStream_t stream) {
+  GemvParams p{};
+  p.codes = reinterpret_cast<const uint4*>(codes);
+  p.scales = scales;
+  p.biases = biases;
+  p.rows = rows;
+  p.k = k;
+  p.x = x;
+  p.y = y;
+  p.out_bf16 = out_bf16;
+  return launch_q8<2, 1, false>(p, stream);
+}
+
+hipError_t run_lmhead_argmax_q8(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                                int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
+                                float* part_val, int32_t* part_idx, unsigned* done, hipStream_t stream) {
+  GemvParams p{};
+  p.codes = reinterpret_cast<const uint4*>(codes);
+  p.scales = scales;
+  p.biases = biases;
+  p.rows = rows;
+  p.k = k;
+  p.x = X;
+  p.part_val = part_val;
+  p.part_idx = part_idx;
+  p.done = done;
+  switch (B) {
+    case 1: return run_lmhead_q8_b<1>(p, ids, max_logit, stream);
+    case 2: return run_lmhead_q8_b<2>(p, ids, max_logit, stream);
+    case 3: return run_lmhead_q8_b<3>(p, ids, max_logit, stream);
+    case 4: return run_lmhead_q8_b<4>(p, ids, max_logit, stream);
+    case 5: return run_lmhead_q8_b<5>(p, ids, max_logit, stream);
+    case 6: return run_lmhead_q8_b<6>(p, ids, max_logit, stream);
+    case 7: return run_lmhead_q8_b<7>(p, ids, max_logit, stream);
     default: return hipErrorInvalidValue;
   }
 }

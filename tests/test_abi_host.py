@@ -185,3 +185,32 @@ def test_workspace_queries(lib):
     small = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(_layer()), None, 10)
     big = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(_layer()), None, 1000)
     assert 0 < small < big
+
+
+def test_q8_matrices_rejected_where_unsupported(lib):
+    """8-bit matrices: accepted by the GEMV and the LM head only; an unknown width is invalid."""
+    def m8(count=1, n=64, k=128, **kw):
+        w = _mat(count, n, k, **kw)
+        w.bits = 8
+        return w
+    bad = _mat(1, 64, 128)
+    bad.bits = 7
+    assert lib.q4_gemv(ctypes.byref(bad), A, A2, 0, None) == B.EINVAL
+    need_g = lib.q4moe_workspace_bytes(B.OP_GEMM, None, ctypes.byref(m8()), 10)
+    assert lib.q4_gemm(ctypes.byref(m8()), A, 10, A2, 0, A, need_g, None) == B.EUNSUPPORTED
+    # a layer whose matrices are 8-bit
+    L = _layer()
+    L.up = m8(4, 64, 128)
+    need_d = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE, ctypes.byref(_layer()), None, 1)
+    assert lib.moe_ffn_decode(ctypes.byref(L), A, A2, 0, None, None, A, need_d, None) == B.EUNSUPPORTED
+    L = _layer()
+    L.sh_down = m8(1, 128, 64)
+    assert lib.moe_ffn_decode(ctypes.byref(L), A, A2, 0, None, None, A, need_d, None) == B.EUNSUPPORTED
+    # LM head: up to 7 batch rows at 8 bits (LDS holds them as fp32); short workspace before any launch
+    W = ctypes.byref(m8(1, 1000, 2048))
+    need8 = lib.q4moe_workspace_bytes(B.OP_LMHEAD, None, W, 8)
+    need7 = lib.q4moe_workspace_bytes(B.OP_LMHEAD, None, W, 7)
+    f = lib.lmhead_argmax
+    assert f(W, A, 8, A2, None, A, need8, None) == B.EUNSUPPORTED
+    assert f(W, A, 7, A2, None, A, need7 - 1, None) == B.EWORKSPACE
+    assert f(ctypes.byref(m8(1, 10, 16384)), A, 1, A2, None, A, need8, None) == B.EUNSUPPORTED

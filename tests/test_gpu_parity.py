@@ -473,3 +473,70 @@ def test_prefill_row_magnitudes(B):
     X = _scaled_rows(94, T, H)
     err, worst = _prefill_check(B, layer, dl, X, with_bf16=False)
     assert err <= REL_L2_TOL and worst <= 2 * REL_L2_TOL, (err, worst)
+
+
+# ---------------------------------------------------- 8-bit affine matrices --
+
+def test_q8_gemv_hand_example_exact(B):
+    """The oracle's worked 8-bit example: x = ones gives exactly 752 + 4144."""
+    words = [0x03020100 + 0x04040404 * i for i in range(16)] + [0xFFFFFFFF] * 16
+    mat = (np.array([words], dtype=np.uint32), np.array([[0x3F00, 0x3E80]], dtype=np.uint16),
+           np.array([[0xC080, 0x3F80]], dtype=np.uint16))
+    y = B.q4_gemv(_q4(B, mat), B.bf16_tensor(np.full(128, 0x3F80, dtype=np.uint16)))
+    _sync()
+    assert float(y[0]) == 4896.0
+
+
+@pytest.mark.parametrize("n,k,seed", [(512, 2048, 0), (777, 640, 1), (33, 64, 2), (1000, 192, 3)])
+def test_q8_gemv_parity(B, n, k, seed):
+    say(f"q8 gemv n={n} k={k}")
+    mat = synth.q8_matrix(60 + seed, 0, 0, 0, n, k)
+    x = synth.token_rows(60 + seed, 1, k)[0]
+    W = _q4(B, mat)
+    assert W.bits == 8
+    y = B.q4_gemv(W, B.bf16_tensor(x))
+    yb = B.q4_gemv(W, B.bf16_tensor(x), 1)
+    _sync()
+    ref = orc.q4_gemv(*mat, x)
+    err = rel_l2(to_f64(y), ref)
+    assert err <= 1e-5, err  # exact 8-bit x 8-bit products, fp32 sums
+    check_bf16_output(yb, y, ref)
+
+
+@pytest.mark.parametrize("batch", [1, 4, 7])
+def test_q8_lmhead_parity(B, batch):
+    rows, k = 20000, 1024
+    say(f"q8 lmhead rows={rows} k={k} B={batch}")
+    mat = synth.q8_matrix(61, 0, 0, 0, rows, k)
+    X = synth.token_rows(61, batch, k, index=batch)
+    ids, mx = B.lmhead_argmax(_q4(B, mat), B.bf16_tensor(X))
+    _sync()
+    _check_argmax(ids.cpu().numpy(), mx.cpu().numpy(), orc.lmhead_logits(*mat, X))
+
+
+def test_q8_lmhead_planted_ties(B):
+    """Identical maximal 8-bit rows: the lowest index wins, with the exact maximum."""
+    rows, k = 3000, 256
+    codes, scales, biases = synth.q8_matrix(62, 0, 0, 0, rows, k)
+    x = np.full((1, k), 0x3F80, dtype=np.uint16)
+    for planted in ((2999,), (1234, 2000)):
+        c, s, b = codes.copy(), scales.copy(), biases.copy()
+        for r in planted:
+            c[r] = 0xFFFFFFFF
+            s[r] = 0x3F80
+            b[r] = 0
+        ids, mx = B.lmhead_argmax(_q4(B, (c, s, b)), B.bf16_tensor(x))
+        _sync()
+        assert int(ids[0]) == min(planted) and float(mx[0]) == 255.0 * k
+
+
+def test_q8_lmhead_full_vocab(B):
+    """8-bit LM head of the q4-xl kind, 151,936 x 2048, batch 1 and 4."""
+    mat = synth.lm_head(bits=8)
+    W = _q4(B, mat)
+    for batch in (1, 4):
+        say(f"q8 lmhead full vocab B={batch}")
+        X = synth.token_rows(4, batch, synth.HIDDEN, index=batch)
+        ids, mx = B.lmhead_argmax(W, B.bf16_tensor(X))
+        _sync()
+        _check_argmax(ids.cpu().numpy(), mx.cpu().numpy(), orc.lmhead_logits(*mat, X))

@@ -212,6 +212,16 @@ def expert_ffn(expert, X) -> np.ndarray:
     return a @ Wd.T
 
 
+def layer_router_logits(layer, X_bits) -> np.ndarray:
+    """The layer's router logits [T][E]: the 8-bit router ``layer.router_q8`` when the layer
+    has one (the checkpoint's affine Q8 router-gate exception), else the bf16 router."""
+    rq8 = getattr(layer, "router_q8", None)
+    if rq8 is None:
+        return router_logits(layer.router, X_bits)
+    X = np.atleast_2d(bf16_to_f64(X_bits))
+    return X @ dequantize(*rq8, X.shape[-1]).T
+
+
 def moe_ffn_token(layer, x_bits, ids=None):
     """One token through the MoE layer (the decode form).
 
@@ -222,7 +232,7 @@ def moe_ffn_token(layer, x_bits, ids=None):
     them from the logits).  Returns (y f64[hidden], ids, weights, logits).
     """
     x = bf16_to_f64(x_bits)
-    logits = router_logits(layer.router, x_bits)[0]
+    logits = layer_router_logits(layer, x_bits)[0]
     if ids is None:
         sel, w = topk_from_logits(logits, layer.top_k)
         sel, w = sel[0], w[0]
@@ -247,7 +257,7 @@ def moe_ffn_prefill(layer, X_bits, ids=None):
     """
     X = np.atleast_2d(bf16_to_f64(X_bits))
     T = X.shape[0]
-    logits = router_logits(layer.router, X_bits)
+    logits = layer_router_logits(layer, X_bits)
     if ids is None:
         sel, w = topk_from_logits(logits, layer.top_k)
     else:

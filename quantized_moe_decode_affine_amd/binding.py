@@ -40,7 +40,8 @@ class q4moe_layer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("router", ctypes.c_void_p),
                 ("gate", q4moe_matrix), ("up", q4moe_matrix), ("down", q4moe_matrix),
-                ("sh_gate", q4moe_matrix), ("sh_up", q4moe_matrix), ("sh_down", q4moe_matrix)]
+                ("sh_gate", q4moe_matrix), ("sh_up", q4moe_matrix), ("sh_down", q4moe_matrix),
+                ("router_q8", q4moe_matrix)]
 
 
 _lib = None
@@ -152,13 +153,16 @@ class DeviceLayer:
         else:
             self.sh = []
             sh = [q4moe_matrix() for _ in range(3)]
+        rq8 = getattr(layer, "router_q8", None)
+        self.router_q8 = DeviceQ4(*rq8, device=device) if rq8 is not None else None
         self.struct = q4moe_layer(self.hidden, self.inter, self.n_experts, self.top_k, self.router.data_ptr(),
-                                  self.gate.struct, self.up.struct, self.down.struct, *sh)
+                                  self.gate.struct, self.up.struct, self.down.struct, *sh,
+                                  self.router_q8.struct if self.router_q8 is not None else q4moe_matrix())
 
     @property
     def nbytes(self) -> int:
-        total = self.router.numel() * 2 + self.gate.nbytes + self.up.nbytes + self.down.nbytes
-        return total + sum(m.nbytes for m in self.sh)
+        total = self.gate.nbytes + self.up.nbytes + self.down.nbytes + sum(m.nbytes for m in self.sh)
+        return total + (self.router_q8.nbytes if self.router_q8 is not None else self.router.numel() * 2)
 
 
 # ---------------------------------------------------------------- workspaces --

@@ -54,7 +54,9 @@ bool out_ok(const void* y, int out_dtype) {
 
 // Validates a layer; on success fills `d`.
 int layer_check(const q4moe_layer* L, q4moe::DecodeLayer* d) {
-  if (!L || !L->router || !aligned(L->router, 16)) return Q4MOE_EINVAL;
+  if (!L) return Q4MOE_EINVAL;
+  const bool rq8 = L->router_q8.codes != nullptr;
+  if (!rq8 && (!L->router || !aligned(L->router, 16))) return Q4MOE_EINVAL;
   if (L->hidden < 64 || L->hidden % 64 || L->inter < 64 || L->inter % 64) return Q4MOE_EINVAL;
   if (L->n_experts < 1 || L->top_k < 1 || L->top_k > L->n_experts) return Q4MOE_EINVAL;
   if (L->n_experts > 1024 || L->top_k > 32 || L->hidden > kMaxGemvK) return Q4MOE_EUNSUPPORTED;
@@ -66,7 +68,8 @@ int layer_check(const q4moe_layer* L, q4moe::DecodeLayer* d) {
                  !matrix_shape(L->sh_down, 1, H, I)))
     return Q4MOE_EINVAL;
   for (const q4moe_matrix* m : {&L->gate, &L->up, &L->down, &L->sh_gate, &L->sh_up, &L->sh_down})
-    if (is_q8(*m)) return Q4MOE_EUNSUPPORTED;  // the layer kernels read 4-bit codes only
+    if (is_q8(*m)) return Q4MOE_EUNSUPPORTED;  // the layer kernels read 4-bit experts only
+  if (rq8 && (!matrix_shape(L->router_q8, 1, E, H) || !is_q8(L->router_q8))) return Q4MOE_EINVAL;
   d->hidden = L->hidden;
   d->inter = L->inter;
   d->n_experts = L->n_experts;
@@ -83,6 +86,7 @@ int layer_check(const q4moe_layer* L, q4moe::DecodeLayer* d) {
   } else {
     d->sh_gate = d->sh_up = d->sh_down = Q4Mat{nullptr, nullptr, nullptr};
   }
+  d->router_q8 = rq8 ? to_mat(L->router_q8) : Q4Mat{nullptr, nullptr, nullptr};
   return Q4MOE_OK;
 }
 
@@ -241,6 +245,7 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || B < 1 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
+    if (d.router_q8.codes) return Q4MOE_EUNSUPPORTED;  // 8-bit router: batch-1 decode only
     if (B > q4moe::kMaxBatch || !q4moe::decode_batch_supported(d, (int)B, kMaxDynLds)) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
@@ -258,6 +263,7 @@ int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, vo
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || T < 0 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
+    if (d.router_q8.codes) return Q4MOE_EUNSUPPORTED;  // 8-bit router: batch-1 decode only
     if (T * (d.top_k + 1) > kMaxRows32) return Q4MOE_EUNSUPPORTED;
     if (T == 0) return Q4MOE_OK;
     const size_t need =

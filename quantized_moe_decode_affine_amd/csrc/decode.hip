@@ -310,7 +310,9 @@ struct DownPrefetch {
   uint32_t s, b;
 };
 
-__global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) {
+// The layer's body, specialised on the router's format (bf16, or 8-bit affine codes).
+template <bool kQ8Router>
+__device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ int32_t s_ids[kMaxTopK + 1];
   __shared__ float s_w[kMaxTopK + 1];
@@ -350,8 +352,50 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
   // global memory) and wave 0 publishes them as one line of tagged words.
   const int rgroups = (E + 7) / 8;
   bool have_epoch = false;
+  constexpr bool router_q8 = kQ8Router;
   for (int rb = blockIdx.x; rb < rgroups; rb += gridDim.x) {  // same trip count for the whole workgroup
     const uint4* xv = reinterpret_cast<const uint4*>(p.x);
+    float la, lb;
+    if constexpr (router_q8) {
+      // 8-bit router (count 1, [E][H/4] words): a lane takes 16-code chunks (one
+      // 16-byte load per row), which lie inside one 64-column group, and adds
+      // scale * sum(x q) + bias * sum(x) for each; x as 8 bf16 per 16-byte load.
+      const int G = H >> 6;
+      const int e0 = min(rb * 8 + 2 * wv, E - 1), e1 = min(rb * 8 + 2 * wv + 1, E - 1);
+      const uint4* q0 = reinterpret_cast<const uint4*>(p.L.router_q8.codes) + (size_t)e0 * (H >> 4);
+      const uint4* q1 = reinterpret_cast<const uint4*>(p.L.router_q8.codes) + (size_t)e1 * (H >> 4);
+      float a = 0.f, b = 0.f;
+      for (int c = lane; c < (H >> 4); c += kWave) {
+        const uint4 w0 = q0[c], w1 = q1[c], xa = xv[2 * c], xb = xv[2 * c + 1];
+        const int g = c >> 2;
+        const float s0 = bf16_bits_to_f32(p.L.router_q8.scales[(size_t)e0 * G + g]);
+        const float o0 = bf16_bits_to_f32(p.L.router_q8.biases[(size_t)e0 * G + g]);
+        const float s1 = bf16_bits_to_f32(p.L.router_q8.scales[(size_t)e1 * G + g]);
+        const float o1 = bf16_bits_to_f32(p.L.router_q8.biases[(size_t)e1 * G + g]);
+        if (!have_epoch) {
+          have_epoch = true;
+          if (threadIdx.x == 0) acquire_epoch();
+        }
+        const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+        const uint32_t c0w[4] = {w0.x, w0.y, w0.z, w0.w}, c1w[4] = {w1.x, w1.y, w1.z, w1.w};
+        float p0 = 0.f, p1 = 0.f, xs_ = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float xi = bf16_bits_to_f32((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+          xs_ += xi;
+          p0 = fmaf(xi, (float)((c0w[i >> 2] >> (8 * (i & 3))) & 0xFFu), p0);
+          p1 = fmaf(xi, (float)((c1w[i >> 2] >> (8 * (i & 3))) & 0xFFu), p1);
+        }
+        a += fmaf(s0, p0, o0 * xs_);
+        b += fmaf(s1, p1, o1 * xs_);
+      }
+      if (!have_epoch) {
+        have_epoch = true;
+        if (threadIdx.x == 0) acquire_epoch();
+      }
+      la = group_sum_rt(a, 6);
+      lb = group_sum_rt(b, 6);
+    } else {
     const uint4* r0 = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(rb * 8 + 2 * wv, E - 1) * H);
     const uint4* r1 = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(rb * 8 + 2 * wv + 1, E - 1) * H);
     constexpr int kBatch = 4;  // row chunks in flight per lane and row
@@ -382,7 +426,9 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
         b1 = dot2_bf16(w1[q].w, v[q].w, b1);
       }
     }
-    const float la = group_sum_rt(a0 + a1, 6), lb = group_sum_rt(b0 + b1, 6);
+    la = group_sum_rt(a0 + a1, 6);
+    lb = group_sum_rt(b0 + b1, 6);
+    }
     if (lane == 0) {
       s_rlog[2 * wv] = la;
       s_rlog[2 * wv + 1] = lb;
@@ -552,6 +598,9 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) 
   }
 }
 
+__global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) { decode_layer<false>(p); }
+__global__ __launch_bounds__(kThreads) void decode_layer_q8router_kernel(DecodeParams p) { decode_layer<true>(p); }
+
 int lanes_log2(int groups) {
   int r = 0;
   while (r < 6 && (2 << r) <= groups) ++r;
@@ -594,7 +643,10 @@ hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, 
   const size_t lds = decode_lds(L);
   int blocks = device_cu_count();
   if (blocks > kMaxBlocks) blocks = kMaxBlocks;
-  hipLaunchKernelGGL(decode_layer_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
+  if (L.router_q8.codes)
+    hipLaunchKernelGGL(decode_layer_q8router_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
+  else
+    hipLaunchKernelGGL(decode_layer_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 

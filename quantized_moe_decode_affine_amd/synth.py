@@ -75,18 +75,18 @@ def q4_matrix(seed: int, layer: int, expert: int, matrix: int, n: int, k: int):
     return codes, scales, biases
 
 
-def q8_matrix(seed: int, layer: int, expert: int, matrix: int, n: int, k: int):
+def q8_matrix(seed: int, layer: int, expert: int, matrix: int, n: int, k: int, scale_std: float = 0.02 / 16):
     """One affine-Q8 matrix of n rows and k columns: 8-bit codes, 4 per uint32 word.
 
-    Codes are uniform bytes; scales ``|N(0, 0.02/16)|`` and biases ``-128*scale +
-    N(0, 0.002)``, so the weights span the same range as the 4-bit ones.
+    Codes are uniform bytes; scales ``|N(0, scale_std)|`` and biases ``-128*scale +
+    N(0, 0.002)`` (the default scale makes the weights span the range of the 4-bit ones).
     Returns ``(codes uint32[n][k/4], scales uint16[n][k/64], biases uint16[n][k/64])``.
     """
     if k % GROUP:
         raise ValueError("k must be a multiple of 64")
     rng = _rng(seed, layer, expert, matrix, 8)
     codes = rng.integers(0, 1 << 32, size=(n, k // 4), dtype=np.uint32)
-    scales = to_bf16_bits(np.abs(rng.normal(0.0, 0.02 / 16, size=(n, k // GROUP))))
+    scales = to_bf16_bits(np.abs(rng.normal(0.0, scale_std, size=(n, k // GROUP))))
     noise = rng.normal(0.0, 0.002, size=(n, k // GROUP))
     biases = to_bf16_bits(-128.0 * _bf16_bits_to_f32(scales).astype(np.float64) + noise)
     return codes, scales, biases
@@ -136,9 +136,10 @@ class MoELayer:
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, router_bits, gate, up, down,
-                 sh_gate=None, sh_up=None, sh_down=None):
+                 sh_gate=None, sh_up=None, sh_down=None, router_q8=None):
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.router = router_bits
+        self.router_q8 = router_q8  # (codes, scales, biases) of an 8-bit router, replacing `router`
         self.gate, self.up, self.down = gate, up, down
         self.sh_gate, self.sh_up, self.sh_down = sh_gate, sh_up, sh_down
 
@@ -162,8 +163,10 @@ class MoELayer:
 
 def moe_layer(seed: int, layer: int = 0, hidden: int = HIDDEN, inter: int = INTER,
               n_experts: int = N_EXPERTS, top_k: int = TOP_K, shared: bool = True,
-              threads: int | None = None) -> MoELayer:
-    """Generate one MoE layer; experts are drawn in parallel threads (numpy releases the GIL)."""
+              threads: int | None = None, router_bits: int = 16) -> MoELayer:
+    """Generate one MoE layer; experts are drawn in parallel threads (numpy releases the GIL).
+    router_bits = 8 adds an affine-Q8 router (weights of about the bf16 router's spread,
+    0.02) that replaces the bf16 one."""
     gate = Q4Stack(n_experts, inter, hidden)
     up = Q4Stack(n_experts, inter, hidden)
     down = Q4Stack(n_experts, hidden, inter)
@@ -186,8 +189,9 @@ def moe_layer(seed: int, layer: int = 0, hidden: int = HIDDEN, inter: int = INTE
     else:
         for e in ids:
             one(e)
+    rq8 = q8_matrix(seed, layer, ROUTER_STREAM, 0, n_experts, hidden, scale_std=0.02 / 74) if router_bits == 8 else None
     return MoELayer(hidden, inter, n_experts, top_k, router(seed, layer, n_experts, hidden),
-                    gate, up, down, *sh)
+                    gate, up, down, *sh, router_q8=rq8)
 
 
 def lm_head(seed: int = 4, rows: int = VOCAB, hidden: int = HIDDEN, bits: int = 4):

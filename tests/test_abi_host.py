@@ -214,3 +214,26 @@ def test_q8_matrices_rejected_where_unsupported(lib):
     assert f(W, A, 8, A2, None, A, need8, None) == B.EUNSUPPORTED
     assert f(W, A, 7, A2, None, A, need7 - 1, None) == B.EWORKSPACE
     assert f(ctypes.byref(m8(1, 10, 16384)), A, 1, A2, None, A, need8, None) == B.EUNSUPPORTED
+
+
+def test_q8_router_layers(lib):
+    """An 8-bit router replaces the bf16 one for moe_ffn_decode only; it must be one 8-bit
+    n_experts x hidden matrix."""
+    def rq8(E=4, H=128, bits=8):
+        m = _mat(1, E, H)
+        m.bits = bits
+        return m
+    L = _layer(router=None)
+    L.router_q8 = rq8()
+    need_d = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE, ctypes.byref(L), None, 1)
+    assert need_d > 0
+    d = lib.moe_ffn_decode
+    assert d(ctypes.byref(L), A, A2, 0, None, None, A, need_d - 1, None) == B.EWORKSPACE  # valid up to the workspace
+    for bad in (rq8(bits=4), rq8(E=5), rq8(H=64)):
+        L.router_q8 = bad
+        assert d(ctypes.byref(L), A, A2, 0, None, None, A, need_d, None) == B.EINVAL
+    L.router_q8 = rq8()
+    need_p = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(L), None, 50)
+    assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A2, 0, A, need_p, None) == B.EUNSUPPORTED
+    need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(L), None, 2)
+    assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b, None) == B.EUNSUPPORTED

@@ -540,3 +540,17 @@ def test_q8_lmhead_full_vocab(B):
         ids, mx = B.lmhead_argmax(W, B.bf16_tensor(X))
         _sync()
         _check_argmax(ids.cpu().numpy(), mx.cpu().numpy(), orc.lmhead_logits(*mat, X))
+
+
+@pytest.mark.parametrize("H,I,E,k", [(256, 128, 16, 4), (2048, 512, 256, 8)])
+def test_decode_q8_router(B, H, I, E, k):
+    """Batch-1 decode with the checkpoint's affine Q8 router gate in place of the bf16 router."""
+    say(f"decode q8 router H={H} I={I} E={E} k={k}")
+    layer = synth.moe_layer(97, 0, H, I, E, k, router_bits=8)
+    dl = B.DeviceLayer(layer)
+    assert dl.router_q8 is not None and dl.router_q8.bits == 8
+    n_exact = 0
+    for step in range(4):
+        err, exact = _decode_check(B, layer, dl, synth.hidden_vector(97, step, 0, H))
+        n_exact += exact
+    assert n_exact >= 3

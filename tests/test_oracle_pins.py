@@ -420,3 +420,24 @@ def test_q8_gemv_exact_rational_brute_force(n, k, seed):
     assert list(orc.q4_gemv(codes, scales, biases, xb)) == expect
     ids, top, _ = orc.lmhead_argmax(codes, scales, biases, xb)
     assert int(ids[0]) == int(np.argmax(expect)) and top[0] == max(expect)
+
+
+def test_q8_router_equals_bf16_router_on_shared_values():
+    """An 8-bit router whose weights (q - 128) / 128 are also bfloat16 values gives the same
+    logits, ids and layer output as the bfloat16 router holding those values."""
+    H, I, E, k = 128, 64, 8, 2
+    layer = synth.moe_layer(9, 0, H, I, E, k)
+    rng = np.random.default_rng(9)
+    q = rng.integers(0, 256, size=(E, H))
+    layer.router = np.array([[_bf16_bits_of((v - 128) / 128) for v in r] for r in q], dtype=np.uint16)
+    x = synth.hidden_vector(9, 0, 0, H)
+    y16, ids16, w16, l16 = orc.moe_ffn_token(layer, x)
+    scales = np.full((E, H // 64), _bf16_bits_of(1 / 128), dtype=np.uint16)
+    biases = np.full((E, H // 64), _bf16_bits_of(-1.0), dtype=np.uint16)
+    layer.router_q8 = (_pack_bytes(q), scales, biases)
+    y8, ids8, w8, l8 = orc.moe_ffn_token(layer, x)
+    np.testing.assert_array_equal(l8, l16)
+    np.testing.assert_array_equal(ids8, ids16)
+    np.testing.assert_array_equal(y8, y16)
+    Y8, _, _, _ = orc.moe_ffn_prefill(layer, np.stack([x, x]))
+    np.testing.assert_allclose(Y8[1], y16, rtol=1e-12, atol=1e-12)  # another fp64 summation order

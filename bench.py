@@ -103,10 +103,11 @@ def main():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip every leg but the 40-layer decode loop")
-    ap.add_argument("--legs", default="chain,batch,prefill,wide,lmhead",
-                    help="comma list of the legs run after the decode loop: chain (residual-chained step with the "
-                         "LM head, eager and as a replayed graph), batch (several requests per step), prefill "
-                         "(2,048-token chunk), wide (512 experts, top-10), lmhead")
+    ap.add_argument("--legs", default="q8router,chain,batch,prefill,wide,lmhead",
+                    help="comma list of the legs run after the decode loop: q8router (the same loop with affine-Q8 "
+                         "routers), chain (residual-chained step with the LM head, eager and as a replayed graph), "
+                         "batch (several requests per step), prefill (2,048-token chunk), wide (512 experts, "
+                         "top-10), lmhead")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (the known-size reference that scales the "
                          "byte counters of a rocprofv3 --pmc run)")
@@ -184,6 +185,29 @@ def main():
                      "kernel": "decode_layer_kernel (moe_ffn_decode, one launch per layer)",
                      "unit_bytes": layer_bytes, "avg_launch_us": round(layer_us, 3)},
     }
+    if "q8router" in legs:
+        # ------------------------- the decode loop with the checkpoint's affine-Q8 router gates
+        stack.enable_q8_router(dev)
+        stack.use_q8_router(True)
+        for s in range(args.warmup):
+            stack.step(s)
+        torch.cuda.synchronize()
+        ev0.record()
+        for s in range(args.steps):
+            stack.step(s)
+        ev1.record()
+        torch.cuda.synchronize()
+        q_us = ev0.elapsed_time(ev1) * 1e3 / (args.steps * args.layers)
+        stack.use_q8_router(False)
+        q_bytes = layer_bytes - synth.N_EXPERTS * synth.HIDDEN * 2 + workloads.q8_matrix_bytes(synth.N_EXPERTS,
+                                                                                               synth.HIDDEN)
+        result["decode_q8_router"] = {
+            "workload": f"{args.layers}-layer batch-1 decode loop with affine-Q8 router gates (decode_layer_q8router_kernel)",
+            "us_per_layer": round(q_us, 3), "bytes_per_layer": q_bytes,
+            "GB_s": round(q_bytes / (q_us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * q_bytes / (q_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        log(f"decode q8 router: {result['decode_q8_router']}")
+
     if "chain" in legs:
         # ------------------- residual-chained decode step + LM head: eager launches vs a replayed graph
         log("building the LM head for the chained step")

@@ -24,6 +24,11 @@ def q4_matrix_bytes(n: int, k: int) -> int:
     return n * k // 2 + 2 * 2 * n * (k // GROUP)
 
 
+def q8_matrix_bytes(n: int, k: int) -> int:
+    """Bytes of one affine-Q8 matrix: 8 bits per weight plus a bf16 scale and bias per 64 weights."""
+    return n * k + 2 * 2 * n * (k // GROUP)
+
+
 def decode_layer_bytes(hidden=synth.HIDDEN, inter=synth.INTER, n_experts=synth.N_EXPERTS, top_k=synth.TOP_K,
                        shared=True, out_bytes=4) -> int:
     """Algorithmic bytes of one decode MoE layer: the selected experts' weights (and the shared
@@ -87,6 +92,25 @@ class DecodeStack:
                 events[l][1].record()
             if st != B.OK:
                 B._check("moe_ffn_decode", st)
+
+    def enable_q8_router(self, device="cuda") -> None:
+        """Give every layer an affine-Q8 router (drawn as synth.moe_layer draws one) in place
+        of its bf16 router; :meth:`step` then runs the layers with it.  Only the router
+        changes: the experts are the same device tensors."""
+        H, E = self.layers[0].hidden, self.layers[0].n_experts
+        self.q8_routers, self._refs_q8 = [], []
+        for l, d in enumerate(self.layers):
+            m = B.DeviceQ4(*synth.q8_matrix(self.seed, l, synth.ROUTER_STREAM, 0, E, H, scale_std=0.02 / 74),
+                           device=device)
+            st = B.q4moe_layer()
+            ctypes.pointer(st)[0] = d.struct  # a copy of the layer's descriptor
+            st.router_q8 = m.struct
+            self.q8_routers.append((m, st))
+            self._refs_q8.append(ctypes.byref(st))
+        self._refs_bf16 = self._refs
+
+    def use_q8_router(self, on: bool) -> None:
+        self._refs = self._refs_q8 if on else self._refs_bf16
 
     def enable_batch(self, max_batch: int = 8, device="cuda") -> None:
         """Inputs for batched steps: x[s][l][b] drawn like the batch-1 inputs (seeded per

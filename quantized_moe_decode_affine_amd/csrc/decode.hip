@@ -52,7 +52,6 @@ struct DecodeWs {
 };
 
 struct DecodeParams {
-  DecodeLayer L;
   const uint16_t* x;          // [H]
   void* y;                    // [H]
   int out_mode;               // kOutF32, kOutBf16, kOutBf16Residual
@@ -62,6 +61,7 @@ struct DecodeParams {
   unsigned long long* act;    // [k+1][I] tagged SwiGLU outputs: routed slots 0..k-1, shared slot k
   int lsH;                    // log2 lanes per row for rows of length hidden
   int lsI;                    // log2 lanes per row for rows of length inter
+  DecodeLayer L;              // last: the per-call fields above keep fixed small offsets
 };
 
 // Stage a bf16 vector of n values (n % 32 == 0) into LDS: threads [t0, t0 + nthr)
@@ -312,7 +312,7 @@ struct DownPrefetch {
 
 // The layer's body, specialised on the router's format (bf16, or 8-bit affine codes).
 template <bool kQ8Router>
-__device__ __forceinline__ void decode_layer(const DecodeParams& p) {
+__device__ __forceinline__ void decode_layer(DecodeParams p) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ int32_t s_ids[kMaxTopK + 1];
   __shared__ float s_w[kMaxTopK + 1];

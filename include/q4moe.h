@@ -92,8 +92,8 @@ typedef struct {
  * router_q8.codes is non-null, the 8-bit affine matrix router_q8 (count 1,
  * n_experts x hidden, bits 8: the benchmark checkpoint's affine Q8 router-gate
  * exceptions, "2026-09-02: Lily vs MLX 0.32.2", "Hardware and software"), and
- * `router` may be null.  Only moe_ffn_decode takes an 8-bit router; the other
- * layer calls return Q4MOE_EUNSUPPORTED for it.
+ * `router` may be null.  moe_ffn_decode, moe_ffn_decode_batch and moe_ffn_prefill
+ * all take an 8-bit router (moe_route_topk takes a bf16 router only).
  */
 typedef struct {
   int32_t hidden;

@@ -245,7 +245,6 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || B < 1 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
-    if (d.router_q8.codes) return Q4MOE_EUNSUPPORTED;  // 8-bit router: batch-1 decode only
     if (B > q4moe::kMaxBatch || !q4moe::decode_batch_supported(d, (int)B, kMaxDynLds)) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
@@ -263,7 +262,6 @@ int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, vo
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || T < 0 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
-    if (d.router_q8.codes) return Q4MOE_EUNSUPPORTED;  // 8-bit router: batch-1 decode only
     if (T * (d.top_k + 1) > kMaxRows32) return Q4MOE_EUNSUPPORTED;
     if (T == 0) return Q4MOE_OK;
     const size_t need =

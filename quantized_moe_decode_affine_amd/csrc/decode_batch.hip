@@ -63,18 +63,45 @@ struct BatchParams {
 };
 
 // ---------------------------------------------------------------- launch 1
-// Wave w of workgroup r: logits[b][8r + w] = router[8r + w] . X[b] for every b < NB.
-template <int NB>
+// Wave w of workgroup r: logits[b][8r + w] = router[8r + w] . X[b] for every b < NB; with
+// kQ8 the router is the layer's 8-bit affine matrix (16-code chunks per lane, each inside
+// one 64-column group: scale * sum(x q) + bias * sum(x)).
+template <int NB, bool kQ8>
 __global__ __launch_bounds__(kRouteWaves * kWave) void batch_route_kernel(BatchParams p) {
   const int H = p.L.hidden, E = p.L.n_experts;
   const int lane = lane_id(), wv = threadIdx.x / kWave;
   const int e = blockIdx.x * kRouteWaves + wv;
-  const uint4* r = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(e, E - 1) * H);
-  const int nc = H >> 3;  // 16-byte chunks per row
-  constexpr int Q = 4;    // chunks per lane in flight
   float acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+  if constexpr (kQ8) {
+    const int G = H >> 6, er = min(e, E - 1);
+    const uint4* r = reinterpret_cast<const uint4*>(p.L.router_q8.codes) + (size_t)er * (H >> 4);
+    const uint16_t* sr = p.L.router_q8.scales + (size_t)er * G;
+    const uint16_t* br = p.L.router_q8.biases + (size_t)er * G;
+    for (int c = lane; c < (H >> 4); c += kWave) {
+      const uint4 w = r[c];
+      const float sc = bf16_bits_to_f32(sr[c >> 2]), bi = bf16_bits_to_f32(br[c >> 2]);
+      const uint32_t cw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint4 xa = reinterpret_cast<const uint4*>(p.X + (size_t)b * H)[2 * c];
+        const uint4 xb = reinterpret_cast<const uint4*>(p.X + (size_t)b * H)[2 * c + 1];
+        const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+        float pq = 0.f, xs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float xi = bf16_bits_to_f32((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+          xs += xi;
+          pq = fmaf(xi, (float)((cw[i >> 2] >> (8 * (i & 3))) & 0xFFu), pq);
+        }
+        acc[b] += fmaf(sc, pq, bi * xs);
+      }
+    }
+  } else {
+  const uint4* r = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(e, E - 1) * H);
+  const int nc = H >> 3;  // 16-byte chunks per row
+  constexpr int Q = 4;    // chunks per lane in flight
   for (int c0 = 0; c0 < nc; c0 += Q * kWave) {
     uint4 w[Q], v[NB][Q];
 #pragma unroll
@@ -92,6 +119,7 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void batch_route_kernel(BatchP
       for (int q = 0; q < Q; ++q)
         acc[b] = dot2_bf16(w[q].w, v[b][q].w,
                            dot2_bf16(w[q].z, v[b][q].z, dot2_bf16(w[q].y, v[b][q].y, dot2_bf16(w[q].x, v[b][q].x, acc[b]))));
+  }
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -412,7 +440,10 @@ size_t down_lds_per_token(const DecodeLayer& L) {
 
 template <int NB>
 void launch_route_plan(const BatchParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(batch_route_kernel<NB>, dim3(grid), dim3(kRouteWaves * kWave), 0, stream, p);
+  if (p.L.router_q8.codes)
+    hipLaunchKernelGGL((batch_route_kernel<NB, true>), dim3(grid), dim3(kRouteWaves * kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL((batch_route_kernel<NB, false>), dim3(grid), dim3(kRouteWaves * kWave), 0, stream, p);
   const dim3 one(1), threads(kRouteWaves * kWave);
   if (p.L.n_experts <= 4 * kWave)
     hipLaunchKernelGGL((batch_plan_kernel<NB, 4>), one, threads, 0, stream, p);

@@ -666,7 +666,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   const int64_t P = T * k;
   const int64_t extra = L.has_shared ? T : 0;
   const int max_tiles = group_max_tiles(P, E, extra, BM);
-  hipError_t e = run_route_topk(L.router, E, H, X, T, k, w.ids, w.weights, w.logits, stream);
+  hipError_t e = run_route_topk(L.router, E, H, X, T, k, w.ids, w.weights, w.logits, stream, &L.router_q8);
   if (e != hipSuccess) return e;
   GroupTiles gt{};
   gt.tile_rows = BM;

@@ -61,8 +61,10 @@ hipError_t run_moe_ffn_decode_batch(const DecodeLayer& L, const uint16_t* X, int
 
 // ---- routing and permutation (route.hip)
 size_t route_workspace_bytes(int64_t T, int n_experts);
+// router_q8 (optional): an 8-bit affine router used in place of the bf16 one.
 hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* X, int64_t T, int k,
-                          int32_t* ids, float* weights, void* ws, hipStream_t stream);
+                          int32_t* ids, float* weights, void* ws, hipStream_t stream,
+                          const Q4Mat* router_q8 = nullptr);
 size_t permute_workspace_bytes(int64_t rows, int n_experts);
 
 // Optional output of run_permute for the grouped GEMM: the sorted positions cut

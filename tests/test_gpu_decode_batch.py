@@ -128,3 +128,14 @@ def test_decode_batch_512_experts_top10(B):
         X = synth.token_rows(99, nb, synth.HIDDEN, index=nb)
         worst, _ = _check_batch(B, layer, dl, X, with_bf16=False)
         assert worst <= TOL, (nb, worst)
+
+
+@pytest.mark.parametrize("H,I,E,k,nb", [(256, 128, 16, 4, 4), (2048, 512, 256, 8, 8)])
+def test_decode_batch_q8_router(B, H, I, E, k, nb):
+    """Batched decode with the checkpoint's affine-Q8 router gate."""
+    say(f"decode batch q8 router H={H} E={E} k={k} B={nb}")
+    layer = synth.moe_layer(98, 0, H, I, E, k, router_bits=8)
+    dl = B.DeviceLayer(layer)
+    X = np.stack([synth.hidden_vector(98, s, 0, H) for s in range(nb)])
+    worst, n_exact = _check_batch(B, layer, dl, X)
+    assert worst <= 2e-3 and n_exact >= nb - 1, (worst, n_exact)

@@ -554,3 +554,22 @@ def test_decode_q8_router(B, H, I, E, k):
         err, exact = _decode_check(B, layer, dl, synth.hidden_vector(97, step, 0, H))
         n_exact += exact
     assert n_exact >= 3
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(300, 256, 128, 16, 4), (2048, 2048, 512, 256, 8)])
+def test_prefill_q8_router(B, T, H, I, E, k):
+    """Prefill with the checkpoint's affine-Q8 router gate.  The GPU's routing is not exposed
+    by the layer call, so tokens whose oracle routing lies within the 1e-3 logit tie band are
+    left out; every other token must match the oracle on the oracle's routing."""
+    say(f"prefill q8 router T={T} H={H} E={E} k={k}")
+    layer = synth.moe_layer(99, 0, H, I, E, k, router_bits=8)
+    dl = B.DeviceLayer(layer)
+    X = synth.token_rows(99, T, H)
+    Y = B.moe_ffn_prefill(dl, B.bf16_tensor(X), 0)
+    _sync()
+    got = to_f64(Y)
+    ref, _, _, logits = orc.moe_ffn_prefill(layer, X)
+    keep = np.array([orc.boundary_gap(logits[t], k) > TIE_BAND for t in range(T)])
+    assert keep.mean() > 0.9
+    assert rel_l2(got[keep], ref[keep]) <= REL_L2_TOL
+    assert max(rel_l2(got[t], ref[t]) for t in np.nonzero(keep)[0]) <= 2 * REL_L2_TOL

@@ -319,7 +319,23 @@ def main():
                              "pct_of_bf16_peak_grouped_gemm":
                                  None if g_us is None else round(100 * flops / (g_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 2)}
         log(f"prefill: {p_us:.1f} us/layer, {tfl:.1f} TFLOP/s over the whole layer")
-        del dl, X, ws, Y
+        # the same chunk with the checkpoint's affine-Q8 router gate (same experts)
+        layer = synth.moe_layer(1)
+        layer.router_q8 = synth.q8_matrix(1, 0, synth.ROUTER_STREAM, 0, synth.N_EXPERTS, synth.HIDDEN,
+                                          scale_std=0.02 / 74)
+        dl8 = B.DeviceLayer(layer, dev)
+        del layer
+        for _ in range(2):
+            B.moe_ffn_prefill(dl8, X, out=Y, ws=ws)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            B.moe_ffn_prefill(dl8, X, out=Y, ws=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        result["prefill"]["q8_router_us_per_layer"] = round(ev0.elapsed_time(ev1) * 1e3 / reps, 2)
+        log(f"prefill with q8 router: {result['prefill']['q8_router_us_per_layer']} us/layer")
+        del dl, dl8, X, ws, Y
         torch.cuda.empty_cache()
 
     if "wide" in legs:

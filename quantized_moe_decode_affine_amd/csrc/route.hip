@@ -213,85 +213,95 @@ int grid_for(int64_t n, int block) {
   return (int)(b < 1 ? 1 : b);
 }
 
-}  // namespace
-
 // Router logits from the 8-bit affine router (the checkpoint's Q8 router-gate exception,
 // "2026-09-02: Lily vs MLX 0.32.2", "Hardware and software"): logits[t][e] for a tile of
-// 32 tokens x 64 experts per workgroup, one 64-column group per step.  The group's rows of
-// X go to LDS as fp32 and the experts' codes transposed (byte e of word j: code j of expert
-// e), so a thread's 4 experts' codes at column j are one word and the 16 expert quads of a
-// wave read 16 consecutive words.  Thread (tt, te) accumulates tokens 2tt, 2tt+1 x experts
+// kQ8Tok tokens x 64 experts per workgroup (two workgroups per CU at 2,048 tokens), one
+// 64-column group per step.  The group's rows of X go to LDS as fp32 and the experts'
+// codes as fp32 transposed ([column][expert], each wave converting one 16-column slice for
+// all 64 experts), so a thread's 4 experts at column j are one 16-byte read and a wave's 16
+// expert quads read consecutive words; each thread's 16-byte pieces of the next group load
+// while the current one computes.  Thread (tt, te) accumulates token tt x experts
 // 4te..4te+3: per group scale * sum(x q) + bias * sum(x), products exact, fp32 sums.
+constexpr int kQ8Tok = 16;
 __global__ __launch_bounds__(256) void q8_router_logits_kernel(Q4Mat R, const uint16_t* __restrict__ X, int64_t T,
                                                                int E, int H, float* __restrict__ logits) {
-  __shared__ float s_x[32][65];          // one group of 32 token rows (padded row)
-  __shared__ uint32_t s_q[64][16];       // [column][expert quad]: 4 experts' codes
-  __shared__ float s_sc[64], s_bi[64], s_xs[32];
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
+  __shared__ float s_x[kQ8Tok][65];            // one group of the tile's token rows (padded row)
+  __shared__ __align__(16) float s_q[64][64];  // [column][expert]
+  __shared__ float s_sc[64], s_bi[64], s_xs[kQ8Tok];
+  const int64_t t0 = (int64_t)blockIdx.x * kQ8Tok;
+  const int e0 = blockIdx.y * 64;
   const int te = threadIdx.x & 15, tt = threadIdx.x >> 4;
   const int G = H >> 6;
-  float acc[2][4] = {};
+  float acc[4] = {};
+  // this thread's 16-byte pieces of a group: X row r, block blk (threads < 8 kQ8Tok);
+  // codes of expert e, slice ch
+  const bool xload = threadIdx.x < 8 * kQ8Tok;
+  const int r = (threadIdx.x >> 3) % kQ8Tok, blk = threadIdx.x & 7;
+  const int el = threadIdx.x & 63, ch = threadIdx.x >> 6;
+  const uint16_t* xrow = X + min<int64_t>(t0 + r, T - 1) * H + blk * 8;
+  const int e = min(e0 + el, E - 1);
+  const uint4* crow = reinterpret_cast<const uint4*>(R.codes) + (size_t)e * (H >> 4) + ch;
+  uint4 xv = xload ? *reinterpret_cast<const uint4*>(xrow) : make_uint4(0, 0, 0, 0), cv = crow[0];
+  uint32_t scb = 0, bib = 0;
+  if (ch == 0) {
+    scb = R.scales[(size_t)e * G];
+    bib = R.biases[(size_t)e * G];
+  }
   for (int g = 0; g < G; ++g) {
     __syncthreads();  // the previous group's LDS reads are done
-    // X: 32 rows x 64 columns as 8-value blocks (256 blocks, one per thread)
     {
-      const int r = threadIdx.x >> 3, blk = threadIdx.x & 7;
-      const int64_t t = min<int64_t>(t0 + r, T - 1);
-      const uint4 v = *reinterpret_cast<const uint4*>(X + t * H + g * 64 + blk * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      if (xload) {
+        const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s_x[r][blk * 8 + i] = bf16_bits_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-    }
-    // codes: 64 experts x 64 bytes as 16-byte chunks (256 chunks, one per thread), transposed
-    {
-      const int el = threadIdx.x >> 2, ch = threadIdx.x & 3;
-      const int e = min(e0 + el, E - 1);
-      const uint4 v = reinterpret_cast<const uint4*>(R.codes)[(size_t)e * (H >> 4) + g * 4 + ch];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint8_t* q8 = reinterpret_cast<uint8_t*>(&s_q[0][0]);
+        for (int i = 0; i < 8; ++i) s_x[r][blk * 8 + i] = bf16_bits_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      }
+      const uint32_t c[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) q8[(ch * 16 + i) * 64 + el] = (uint8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+      for (int i = 0; i < 16; ++i) s_q[ch * 16 + i][el] = (float)((c[i >> 2] >> (8 * (i & 3))) & 0xFFu);
       if (ch == 0) {
-        s_sc[el] = bf16_bits_to_f32(R.scales[(size_t)e * G + g]);
-        s_bi[el] = bf16_bits_to_f32(R.biases[(size_t)e * G + g]);
+        s_sc[el] = bf16_bits_to_f32(scb);
+        s_bi[el] = bf16_bits_to_f32(bib);
+      }
+    }
+    if (g + 1 < G) {  // the next group's pieces load while this group computes
+      if (xload) xv = *reinterpret_cast<const uint4*>(xrow + (g + 1) * 64);
+      cv = crow[(g + 1) * 4];
+      if (ch == 0) {
+        scb = R.scales[(size_t)e * G + g + 1];
+        bib = R.biases[(size_t)e * G + g + 1];
       }
     }
     __syncthreads();
-    if (threadIdx.x < 32) {
+    if (threadIdx.x < kQ8Tok) {
       float t = 0.f;
       for (int j = 0; j < 64; ++j) t += s_x[threadIdx.x][j];  // fixed order
       s_xs[threadIdx.x] = t;
     }
-    float pq[2][4] = {};
-#pragma unroll 8
+    float pq[4] = {};
+#pragma unroll 16
     for (int j = 0; j < 64; ++j) {
-      const uint32_t qw = s_q[j][te];
-      const float x0 = s_x[2 * tt][j], x1 = s_x[2 * tt + 1][j];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float qf = (float)((qw >> (8 * u)) & 0xFFu);
-        pq[0][u] = fmaf(x0, qf, pq[0][u]);
-        pq[1][u] = fmaf(x1, qf, pq[1][u]);
-      }
+      const float4 q = *reinterpret_cast<const float4*>(&s_q[j][4 * te]);
+      const float x0 = s_x[tt][j];
+      pq[0] = fmaf(x0, q.x, pq[0]);
+      pq[1] = fmaf(x0, q.y, pq[1]);
+      pq[2] = fmaf(x0, q.z, pq[2]);
+      pq[3] = fmaf(x0, q.w, pq[3]);
     }
     __syncthreads();  // s_xs written
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc[a][u] += fmaf(s_sc[4 * te + u], pq[a][u], s_bi[4 * te + u] * s_xs[2 * tt + a]);
+    for (int u = 0; u < 4; ++u) acc[u] += fmaf(s_sc[4 * te + u], pq[u], s_bi[4 * te + u] * s_xs[tt]);
   }
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int64_t t = t0 + 2 * tt + a;
-    if (t >= T) continue;
+  const int64_t t = t0 + tt;
+  if (t < T) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int e = e0 + 4 * te + u;
-      if (e < E) logits[t * E + e] = acc[a][u];
+      const int ee = e0 + 4 * te + u;
+      if (ee < E) logits[t * E + ee] = acc[u];
     }
   }
 }
+
+}  // namespace
 
 size_t route_workspace_bytes(int64_t T, int n_experts) { return align256((size_t)T * n_experts * 4); }
 
@@ -300,7 +310,8 @@ hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* 
   float* logits = static_cast<float*>(ws);
   dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 63) / 64));
   if (router_q8 && router_q8->codes)
-    hipLaunchKernelGGL(q8_router_logits_kernel, grid, dim3(256), 0, stream, *router_q8, X, T, E, H, logits);
+    hipLaunchKernelGGL(q8_router_logits_kernel, dim3((unsigned)((T + kQ8Tok - 1) / kQ8Tok), (unsigned)((E + 63) / 64)),
+                       dim3(256), 0, stream, *router_q8, X, T, E, H, logits);
   else
     hipLaunchKernelGGL(router_logits_kernel, grid, dim3(512), 0, stream, router, X, T, E, H, logits);
   hipError_t e = hipGetLastError();

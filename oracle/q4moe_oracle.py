@@ -34,7 +34,8 @@ The pages never spell out the arithmetic, so it follows these plain readings
   largest (descending, equal logits ordered by lower expert id), renormalise
   the kept probabilities to sum to one.
 * Expert: ``down . (silu(gate . x) * (up . x))`` with silu(z) = z / (1 + e^-z);
-  the shared expert is added with weight 1.
+  the shared expert is added with weight 1, or with weight sigmoid(g . x) when the
+  layer carries a shared-expert gate vector g.
 * Permutation: stable counting sort of the (token, slot) rows by expert id.
 * LM head: logits = W . x, greedy id = argmax with the lowest index on ties.
 * Residual stream (layers chained in a decode step): the next input is
@@ -222,6 +223,23 @@ def layer_router_logits(layer, X_bits) -> np.ndarray:
     return X @ dequantize(*rq8, X.shape[-1]).T
 
 
+def sigmoid(z):
+    """1 / (1 + e^-z), evaluated without forming e^-z for z < 0 (e^z / (1 + e^z) there)."""
+    z = np.asarray(z, dtype=np.float64)
+    ez = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + ez), ez / (1.0 + ez))
+
+
+def shared_gate(layer, X_bits) -> np.ndarray:
+    """Weight of the shared expert per token: sigmoid(sh_gate_w . x) when the layer carries a
+    shared-expert gate vector, else 1."""
+    X = np.atleast_2d(bf16_to_f64(X_bits))
+    w = getattr(layer, "sh_gate_w", None)
+    if w is None:
+        return np.ones(X.shape[0])
+    return sigmoid(X @ bf16_to_f64(w))
+
+
 def moe_ffn_token(layer, x_bits, ids=None):
     """One token through the MoE layer (the decode form).
 
@@ -243,7 +261,7 @@ def moe_ffn_token(layer, x_bits, ids=None):
     for e, we in zip(sel, w):
         y += we * expert_ffn(layer.expert(int(e)), x)
     if layer.has_shared:
-        y += expert_ffn(layer.expert(layer.n_experts), x)
+        y += shared_gate(layer, x_bits)[0] * expert_ffn(layer.expert(layer.n_experts), x)
     return y, sel, w, logits
 
 
@@ -269,7 +287,7 @@ def moe_ffn_prefill(layer, X_bits, ids=None):
         if tok.size:
             Y[tok] += w[tok, slot][:, None] * expert_ffn(layer.expert(e), X[tok])
     if layer.has_shared:
-        Y += expert_ffn(layer.expert(layer.n_experts), X)
+        Y += shared_gate(layer, X_bits)[:, None] * expert_ffn(layer.expert(layer.n_experts), X)
     return Y, sel, w, logits
 
 

@@ -136,10 +136,11 @@ class MoELayer:
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, router_bits, gate, up, down,
-                 sh_gate=None, sh_up=None, sh_down=None, router_q8=None):
+                 sh_gate=None, sh_up=None, sh_down=None, router_q8=None, sh_gate_w=None):
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.router = router_bits
         self.router_q8 = router_q8  # (codes, scales, biases) of an 8-bit router, replacing `router`
+        self.sh_gate_w = sh_gate_w  # bf16 [hidden]: the shared expert's weight is sigmoid(sh_gate_w . x)
         self.gate, self.up, self.down = gate, up, down
         self.sh_gate, self.sh_up, self.sh_down = sh_gate, sh_up, sh_down
 
@@ -163,10 +164,11 @@ class MoELayer:
 
 def moe_layer(seed: int, layer: int = 0, hidden: int = HIDDEN, inter: int = INTER,
               n_experts: int = N_EXPERTS, top_k: int = TOP_K, shared: bool = True,
-              threads: int | None = None, router_bits: int = 16) -> MoELayer:
+              threads: int | None = None, router_bits: int = 16, shared_gate: bool = False) -> MoELayer:
     """Generate one MoE layer; experts are drawn in parallel threads (numpy releases the GIL).
     router_bits = 8 adds an affine-Q8 router (weights of about the bf16 router's spread,
-    0.02) that replaces the bf16 one."""
+    0.02) that replaces the bf16 one.  shared_gate adds a bf16 shared-expert gate vector,
+    N(0, 0.02), stream [seed, layer, 20001]."""
     gate = Q4Stack(n_experts, inter, hidden)
     up = Q4Stack(n_experts, inter, hidden)
     down = Q4Stack(n_experts, hidden, inter)
@@ -190,8 +192,9 @@ def moe_layer(seed: int, layer: int = 0, hidden: int = HIDDEN, inter: int = INTE
         for e in ids:
             one(e)
     rq8 = q8_matrix(seed, layer, ROUTER_STREAM, 0, n_experts, hidden, scale_std=0.02 / 74) if router_bits == 8 else None
+    gw = to_bf16_bits(_rng(seed, layer, ROUTER_STREAM + 1).normal(0.0, 0.02, size=hidden)) if shared_gate else None
     return MoELayer(hidden, inter, n_experts, top_k, router(seed, layer, n_experts, hidden),
-                    gate, up, down, *sh, router_q8=rq8)
+                    gate, up, down, *sh, router_q8=rq8, sh_gate_w=gw)
 
 
 def lm_head(seed: int = 4, rows: int = VOCAB, hidden: int = HIDDEN, bits: int = 4):

@@ -441,3 +441,24 @@ def test_q8_router_equals_bf16_router_on_shared_values():
     np.testing.assert_array_equal(y8, y16)
     Y8, _, _, _ = orc.moe_ffn_prefill(layer, np.stack([x, x]))
     np.testing.assert_allclose(Y8[1], y16, rtol=1e-12, atol=1e-12)  # another fp64 summation order
+
+
+def test_shared_gate_closed_forms():
+    """A zero gate vector weighs the shared expert by sigmoid(0) = 1/2 exactly; a gate vector
+    along x with a large product weighs it by ~1; the routed part never changes."""
+    H, I, E, k = 128, 64, 8, 2
+    layer = synth.moe_layer(12, 0, H, I, E, k)
+    x = synth.hidden_vector(12, 0, 0, H)
+    y1, ids, _, _ = orc.moe_ffn_token(layer, x)
+    sh = orc.expert_ffn(layer.expert(E), orc.bf16_to_f64(x))
+    layer.sh_gate_w = np.zeros(H, dtype=np.uint16)
+    yh, ids_h, _, _ = orc.moe_ffn_token(layer, x)
+    np.testing.assert_array_equal(ids_h, ids)
+    np.testing.assert_allclose(yh, y1 - 0.5 * sh, rtol=1e-12, atol=1e-12)
+    layer.sh_gate_w = x.copy()  # w . x = |x|^2 > 100: sigmoid within 1e-40 of 1
+    yf, _, _, _ = orc.moe_ffn_token(layer, x)
+    np.testing.assert_allclose(yf, y1, rtol=1e-12, atol=1e-12)
+    assert orc.sigmoid(0.0) == 0.5 and orc.sigmoid(-800.0) == 0.0 and orc.sigmoid(800.0) == 1.0
+    np.testing.assert_allclose(orc.sigmoid(np.array([-3.0, 1.0])), scipy.special.expit([-3.0, 1.0]), rtol=1e-15)
+    Y, _, _, _ = orc.moe_ffn_prefill(layer, np.stack([x, x]))
+    np.testing.assert_allclose(Y[1], yf, rtol=1e-12, atol=1e-12)

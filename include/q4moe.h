@@ -88,7 +88,8 @@ typedef struct {
  * `inter` rows by `hidden` columns and a down matrix of `hidden` rows by
  * `inter` columns (gate/up/down stacked with count = n_experts).  The shared
  * expert, when sh_gate.codes is non-null, has the same shapes with count 1
- * and is added with weight 1.  The router is bf16 [n_experts][hidden], or, when
+ * and is added with weight 1, or with weight sigmoid(sh_gate_w . x) when the
+ * layer carries a shared-expert gate vector (Qwen-family MoE layers do).  The router is bf16 [n_experts][hidden], or, when
  * router_q8.codes is non-null, the 8-bit affine matrix router_q8 (count 1,
  * n_experts x hidden, bits 8: the benchmark checkpoint's affine Q8 router-gate
  * exceptions, "2026-09-02: Lily vs MLX 0.32.2", "Hardware and software"), and
@@ -104,6 +105,9 @@ typedef struct {
   q4moe_matrix gate, up, down;
   q4moe_matrix sh_gate, sh_up, sh_down;
   q4moe_matrix router_q8;  /* codes null: the bf16 router is used */
+  const q4moe_bf16* sh_gate_w;  /* null, or bf16 [hidden]: the shared expert is weighted by
+                                   sigmoid(sh_gate_w . x) (moe_ffn_decode and moe_ffn_prefill;
+                                   moe_ffn_decode_batch returns Q4MOE_EUNSUPPORTED) */
 } q4moe_layer;
 
 /*

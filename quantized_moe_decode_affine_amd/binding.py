@@ -41,7 +41,7 @@ class q4moe_layer(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("router", ctypes.c_void_p),
                 ("gate", q4moe_matrix), ("up", q4moe_matrix), ("down", q4moe_matrix),
                 ("sh_gate", q4moe_matrix), ("sh_up", q4moe_matrix), ("sh_down", q4moe_matrix),
-                ("router_q8", q4moe_matrix)]
+                ("router_q8", q4moe_matrix), ("sh_gate_w", ctypes.c_void_p)]
 
 
 _lib = None
@@ -155,9 +155,12 @@ class DeviceLayer:
             sh = [q4moe_matrix() for _ in range(3)]
         rq8 = getattr(layer, "router_q8", None)
         self.router_q8 = DeviceQ4(*rq8, device=device) if rq8 is not None else None
+        gw = getattr(layer, "sh_gate_w", None)
+        self.sh_gate_w = _dev(gw, device) if gw is not None else None
         self.struct = q4moe_layer(self.hidden, self.inter, self.n_experts, self.top_k, self.router.data_ptr(),
                                   self.gate.struct, self.up.struct, self.down.struct, *sh,
-                                  self.router_q8.struct if self.router_q8 is not None else q4moe_matrix())
+                                  self.router_q8.struct if self.router_q8 is not None else q4moe_matrix(),
+                                  self.sh_gate_w.data_ptr() if self.sh_gate_w is not None else None)
 
     @property
     def nbytes(self) -> int:

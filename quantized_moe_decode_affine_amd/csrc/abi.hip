@@ -87,6 +87,8 @@ int layer_check(const q4moe_layer* L, q4moe::DecodeLayer* d) {
     d->sh_gate = d->sh_up = d->sh_down = Q4Mat{nullptr, nullptr, nullptr};
   }
   d->router_q8 = rq8 ? to_mat(L->router_q8) : Q4Mat{nullptr, nullptr, nullptr};
+  if (L->sh_gate_w && (!shared || !aligned(L->sh_gate_w, 16))) return Q4MOE_EINVAL;
+  d->sh_gate_w = L->sh_gate_w;
   return Q4MOE_OK;
 }
 
@@ -245,6 +247,7 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || B < 1 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
+    if (d.sh_gate_w) return Q4MOE_EUNSUPPORTED;  // the shared-expert gate: decode and prefill only
     if (B > q4moe::kMaxBatch || !q4moe::decode_batch_supported(d, (int)B, kMaxDynLds)) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;

@@ -310,8 +310,9 @@ struct DownPrefetch {
   uint32_t s, b;
 };
 
-// The layer's body, specialised on the router's format (bf16, or 8-bit affine codes).
-template <bool kQ8Router>
+// The layer's body, specialised on the router's format (bf16, or 8-bit affine codes) and on
+// a shared-expert gate (the shared expert weighted by sigmoid(sh_gate_w . x)).
+template <bool kQ8Router, bool kShGate>
 __device__ __forceinline__ void decode_layer(DecodeParams p) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ int32_t s_ids[kMaxTopK + 1];
@@ -445,6 +446,23 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   const uint32_t epoch = s_epoch;
 
   if (wv == 0) {
+    // The shared expert's gate, sigmoid(sh_gate_w . x), taken while the router logits of the
+    // other workgroups are still arriving (the top-k below waits for them).
+    float sh_weight = 1.0f;
+    if constexpr (kShGate) {
+      const uint4* gw = reinterpret_cast<const uint4*>(p.L.sh_gate_w);
+      const uint4* gx = reinterpret_cast<const uint4*>(p.x);
+      float d0 = 0.f, d1 = 0.f;
+      for (int c = lane; c < (H >> 3); c += kWave) {
+        const uint4 a = gw[c], b = gx[c];
+        d0 = dot2_bf16(a.x, b.x, d0);
+        d1 = dot2_bf16(a.y, b.y, d1);
+        d0 = dot2_bf16(a.z, b.z, d0);
+        d1 = dot2_bf16(a.w, b.w, d1);
+      }
+      const float d = group_sum_rt(d0 + d1, 6);
+      sh_weight = 1.0f / (1.0f + __expf(-d));
+    }
     // B: top-k from the tagged logits (every workgroup, redundantly)
     if (E <= 4 * kWave)
       wave_topk_tagged<4>(p.ws->tag_logit, E, k, epoch, timeouts, s_ids, s_w, blockIdx.x == 0 ? p.ids_out : nullptr,
@@ -454,7 +472,7 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
                                             blockIdx.x == 0 ? p.ids_out : nullptr, blockIdx.x == 0 ? p.w_out : nullptr);
     if (lane == 0 && p.L.has_shared) {
       s_ids[k] = -1;
-      s_w[k] = 1.0f;
+      s_w[k] = sh_weight;
     }
   } else if (p.L.has_shared) {
     // A, off the critical path: the shared expert's gate/up in 8-row units.  With
@@ -598,8 +616,12 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) { decode_layer<false>(p); }
-__global__ __launch_bounds__(kThreads) void decode_layer_q8router_kernel(DecodeParams p) { decode_layer<true>(p); }
+__global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) { decode_layer<false, false>(p); }
+__global__ __launch_bounds__(kThreads) void decode_layer_q8router_kernel(DecodeParams p) { decode_layer<true, false>(p); }
+__global__ __launch_bounds__(kThreads) void decode_layer_gated_kernel(DecodeParams p) { decode_layer<false, true>(p); }
+__global__ __launch_bounds__(kThreads) void decode_layer_q8router_gated_kernel(DecodeParams p) {
+  decode_layer<true, true>(p);
+}
 
 int lanes_log2(int groups) {
   int r = 0;
@@ -643,8 +665,13 @@ hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, 
   const size_t lds = decode_lds(L);
   int blocks = device_cu_count();
   if (blocks > kMaxBlocks) blocks = kMaxBlocks;
-  if (L.router_q8.codes)
+  const bool q8 = L.router_q8.codes != nullptr, gated = L.sh_gate_w != nullptr && L.has_shared;
+  if (q8 && gated)
+    hipLaunchKernelGGL(decode_layer_q8router_gated_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
+  else if (q8)
     hipLaunchKernelGGL(decode_layer_q8router_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
+  else if (gated)
+    hipLaunchKernelGGL(decode_layer_gated_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
   else
     hipLaunchKernelGGL(decode_layer_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
   return hipGetLastError();

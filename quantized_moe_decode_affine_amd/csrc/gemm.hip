@@ -60,6 +60,7 @@ struct GemmParams {
   int n_tiles;                // table length (the grid may hold a few more tiles)
   const int32_t* row_src;     // gather mode: A row (token) of each routed position; positions >= P read row pos - P
   const float* route_w;       // scale epilogue: routing weight of each routed position
+  const float* extra_w;       // scale epilogue: weight of each extra-segment row (shared-expert gate), or null (1)
   int gather;
   int64_t P;                  // positions of the routed segments
   int K, G, Gp;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
     const bool routed = pos < p.P;
     const int32_t src = p.gather ? (routed ? p.row_src[pos] : (int32_t)(pos - p.P)) : (int32_t)pos;
     s_src[r] = src;
-    if (p.epi == EPI_SCALE && routed) row_wgt = p.route_w[pos];
+    if (p.epi == EPI_SCALE) row_wgt = routed ? p.route_w[pos] : (p.extra_w ? p.extra_w[pos - p.P] : 1.0f);
     row_e = p.row_exp[src];
   }
 
@@ -506,7 +507,29 @@ __global__ void prep_rows_kernel(const In* __restrict__ A, int64_t rows, int K, 
   }
 }
 
-// Y[t] = Ys[P + t] (shared expert, weight already 1) + sum_slot Ys[inv[t*k + slot]], fixed slot order.
+// The shared expert's weight per token, sigmoid(w . X[t]) (the shared-expert gate), one wave
+// per token.
+__global__ void shared_gate_kernel(const uint16_t* __restrict__ w, const uint16_t* __restrict__ X, int64_t T, int H,
+                                   float* __restrict__ gate) {
+  const int lane = lane_id();
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; t < T; t += wstride) {
+    const uint4* a = reinterpret_cast<const uint4*>(w);
+    const uint4* b = reinterpret_cast<const uint4*>(X + t * H);
+    float d0 = 0.f, d1 = 0.f;
+    for (int c = lane; c < (H >> 3); c += kWave) {
+      const uint4 u = a[c], v = b[c];
+      d0 = dot2_bf16(u.x, v.x, d0);
+      d1 = dot2_bf16(u.y, v.y, d1);
+      d0 = dot2_bf16(u.z, v.z, d0);
+      d1 = dot2_bf16(u.w, v.w, d1);
+    }
+    const float d = group_sum_rt(d0 + d1, 6);
+    if (lane == 0) gate[t] = 1.0f / (1.0f + __expf(-d));
+  }
+}
+
+// Y[t] = Ys[P + t] (shared expert, weight already applied) + sum_slot Ys[inv[t*k + slot]], fixed slot order.
 __global__ void combine_kernel(const float* __restrict__ Ys, const int32_t* __restrict__ inv, int64_t T, int k,
                                int H, int has_shared, int64_t P, void* __restrict__ Y, int out_bf16) {
   const int H4 = H >> 2;
@@ -622,6 +645,7 @@ struct PrefillWs {
   uint16_t* xs_act; // [R][2][Gp(I)]
   int32_t* xe_act;  // [R]
   float* ys;        // [R][H] per-position outputs, weighted
+  float* sh_gate;   // [T] shared-expert weight per token (with a shared-expert gate)
   size_t total;
 };
 
@@ -650,6 +674,7 @@ PrefillWs carve(void* base, int64_t T, int H, int I, int E, int k, int has_share
   w.xs_act = reinterpret_cast<uint16_t*>(take((size_t)R * 2 * pad16(I / 64) * 2));
   w.xe_act = reinterpret_cast<int32_t*>(take((size_t)R * 4));
   w.ys = reinterpret_cast<float*>(take((size_t)R * H * 4));
+  w.sh_gate = reinterpret_cast<float*>(take((size_t)T * 4));
   w.total = off;
   return w;
 }
@@ -736,6 +761,14 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   d.out = w.ys;
   d.out_bf16 = 0;
   d.ldo = H;
+  if (L.has_shared && L.sh_gate_w) {
+    const int64_t blocks = std::min<int64_t>((T + 3) / 4, 4096);
+    hipLaunchKernelGGL(shared_gate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, L.sh_gate_w, X, T, H,
+                       w.sh_gate);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    d.extra_w = w.sh_gate;
+  }
   e = launch_grouped(d, max_tiles, stream);
   if (e != hipSuccess) return e;
 

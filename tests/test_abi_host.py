@@ -237,3 +237,18 @@ def test_q8_router_layers(lib):
     assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A2, 0, A, need_p - 256, None) == B.EWORKSPACE
     need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(L), None, 2)
     assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b - 256, None) == B.EWORKSPACE
+
+
+def test_shared_gate_layers(lib):
+    """A shared-expert gate needs a shared expert and 16-byte alignment; the batched decode
+    call does not take one."""
+    need_d = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE, ctypes.byref(_layer()), None, 1)
+    d = lib.moe_ffn_decode
+    L = _layer(sh_gate_w=A)
+    assert d(ctypes.byref(L), A, A2, 0, None, None, A, need_d - 1, None) == B.EWORKSPACE  # valid up to the workspace
+    assert d(ctypes.byref(_layer(sh_gate_w=A + 2)), A, A2, 0, None, None, A, need_d, None) == B.EINVAL
+    assert d(ctypes.byref(_layer(shared=False, sh_gate_w=A)), A, A2, 0, None, None, A, need_d, None) == B.EINVAL
+    need_p = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(L), None, 50)
+    assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A2, 0, A, need_p - 1, None) == B.EWORKSPACE
+    need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(_layer()), None, 2)
+    assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b, None) == B.EUNSUPPORTED

@@ -573,3 +573,30 @@ def test_prefill_q8_router(B, T, H, I, E, k):
     assert keep.mean() > 0.9
     assert rel_l2(got[keep], ref[keep]) <= REL_L2_TOL
     assert max(rel_l2(got[t], ref[t]) for t in np.nonzero(keep)[0]) <= 2 * REL_L2_TOL
+
+
+@pytest.mark.parametrize("H,I,E,k,rbits", [(256, 128, 16, 4, 16), (256, 128, 16, 4, 8),
+                                           (2048, 512, 256, 8, 16), (2048, 512, 256, 8, 8)])
+def test_decode_shared_gate(B, H, I, E, k, rbits):
+    """Batch-1 decode with the shared expert weighted by sigmoid(g . x), with either router."""
+    say(f"decode shared gate H={H} I={I} E={E} k={k} router bits={rbits}")
+    layer = synth.moe_layer(98, 0, H, I, E, k, router_bits=rbits, shared_gate=True)
+    dl = B.DeviceLayer(layer)
+    n_exact = 0
+    for step in range(4):
+        err, exact = _decode_check(B, layer, dl, synth.hidden_vector(98, step, 0, H), with_bf16=True)
+        assert err <= 1e-5
+        n_exact += exact
+    assert n_exact >= 3
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(300, 256, 128, 16, 4), (2048, 2048, 512, 256, 8)])
+def test_prefill_shared_gate(B, T, H, I, E, k):
+    """Prefill with the shared expert weighted per token by sigmoid(g . x)."""
+    say(f"prefill shared gate T={T} H={H} E={E} k={k}")
+    layer = synth.moe_layer(100, 0, H, I, E, k, shared_gate=True)
+    dl = B.DeviceLayer(layer)
+    X = synth.token_rows(100, T, H)
+    err, worst = _prefill_check(B, layer, dl, X)
+    assert err <= REL_L2_TOL, err
+    assert worst <= 2 * REL_L2_TOL

@@ -70,8 +70,9 @@ enum {
  * "2026-09-02: Lily vs MLX 0.32.2", "Hardware and software"), or `count` stacked
  * matrices of the same shape.  8-bit codes: uint32 [count][n][k/4], code j of a
  * row in byte j%4 of word j/4 (least significant first), same groups and
- * w = scale*q + bias.  Only q4_gemv and lmhead_argmax take 8-bit matrices; the
- * other calls return Q4MOE_EUNSUPPORTED for them. */
+ * w = scale*q + bias.  q4_gemv and lmhead_argmax take 8-bit matrices, the layer
+ * calls an 8-bit router (router_q8) and moe_ffn_decode an 8-bit shared expert;
+ * the other calls return Q4MOE_EUNSUPPORTED for them. */
 typedef struct {
   const uint32_t* codes;
   const q4moe_bf16* scales;
@@ -94,7 +95,12 @@ typedef struct {
  * n_experts x hidden, bits 8: the benchmark checkpoint's affine Q8 router-gate
  * exceptions, "2026-09-02: Lily vs MLX 0.32.2", "Hardware and software"), and
  * `router` may be null.  moe_ffn_decode, moe_ffn_decode_batch and moe_ffn_prefill
- * all take an 8-bit router (moe_route_topk takes a bf16 router only).
+ * all take an 8-bit router (moe_route_topk takes a bf16 router only).  The
+ * shared expert's three matrices may be 8-bit together (the q4-xl conversion
+ * keeps it at 8 bits: "lily-qwen3.8-flash-next" README, "The model"); only
+ * moe_ffn_decode takes that form (moe_ffn_prefill and moe_ffn_decode_batch
+ * return Q4MOE_EUNSUPPORTED; a mix of 4- and 8-bit shared matrices is
+ * Q4MOE_EUNSUPPORTED everywhere).  Routed experts are 4-bit.
  */
 typedef struct {
   int32_t hidden;

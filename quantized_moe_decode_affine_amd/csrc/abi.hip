@@ -67,8 +67,11 @@ int layer_check(const q4moe_layer* L, q4moe::DecodeLayer* d) {
   if (shared && (!matrix_shape(L->sh_gate, 1, I, H) || !matrix_shape(L->sh_up, 1, I, H) ||
                  !matrix_shape(L->sh_down, 1, H, I)))
     return Q4MOE_EINVAL;
-  for (const q4moe_matrix* m : {&L->gate, &L->up, &L->down, &L->sh_gate, &L->sh_up, &L->sh_down})
-    if (is_q8(*m)) return Q4MOE_EUNSUPPORTED;  // the layer kernels read 4-bit experts only
+  for (const q4moe_matrix* m : {&L->gate, &L->up, &L->down})
+    if (is_q8(*m)) return Q4MOE_EUNSUPPORTED;  // routed experts: 4-bit codes only
+  // the shared expert: all three matrices 4-bit, or all three 8-bit (batch-1 decode only)
+  const bool sh_q8 = shared && is_q8(L->sh_gate);
+  if (shared && (is_q8(L->sh_up) != sh_q8 || is_q8(L->sh_down) != sh_q8)) return Q4MOE_EUNSUPPORTED;
   if (rq8 && (!matrix_shape(L->router_q8, 1, E, H) || !is_q8(L->router_q8))) return Q4MOE_EINVAL;
   d->hidden = L->hidden;
   d->inter = L->inter;
@@ -89,6 +92,7 @@ int layer_check(const q4moe_layer* L, q4moe::DecodeLayer* d) {
   d->router_q8 = rq8 ? to_mat(L->router_q8) : Q4Mat{nullptr, nullptr, nullptr};
   if (L->sh_gate_w && (!shared || !aligned(L->sh_gate_w, 16))) return Q4MOE_EINVAL;
   d->sh_gate_w = L->sh_gate_w;
+  d->sh_q8 = sh_q8 ? 1 : 0;
   return Q4MOE_OK;
 }
 
@@ -247,7 +251,7 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || B < 1 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
-    if (d.sh_gate_w) return Q4MOE_EUNSUPPORTED;  // the shared-expert gate: decode and prefill only
+    if (d.sh_gate_w || d.sh_q8) return Q4MOE_EUNSUPPORTED;  // gate: decode and prefill; 8-bit shared: decode
     if (B > q4moe::kMaxBatch || !q4moe::decode_batch_supported(d, (int)B, kMaxDynLds)) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
@@ -265,6 +269,7 @@ int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, vo
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || T < 0 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
+    if (d.sh_q8) return Q4MOE_EUNSUPPORTED;  // the grouped GEMM reads 4-bit experts only
     if (T * (d.top_k + 1) > kMaxRows32) return Q4MOE_EUNSUPPORTED;
     if (T == 0) return Q4MOE_OK;
     const size_t need =

@@ -236,6 +236,95 @@ __device__ __forceinline__ float2 unit_gate_up(const DecodeLayer& L, int e, int 
   return make_float2(group_sum_rt(ag, 3), group_sum_rt(au, 3));
 }
 
+// An 8-bit shared expert (affine Q8, code j of a row in byte j % 4 of word j / 4)
+// is read against fp32 copies of its input in LDS, one 64-column group per row of
+// kQ8Pad floats (the padding puts the groups of neighbouring lanes on different banks).
+constexpr int kQ8Pad = 68;
+
+// scale * sum(q v) + bias * sum(v) over one 64-column group of an 8-bit row, for
+// two rows (a: codes ca, b: codes cb) against the same 64 values v.
+__device__ __forceinline__ float2 q8_group_terms2(const uint4* ca, const uint4* cb, const float* v, uint32_t sa,
+                                                  uint32_t ba, uint32_t sb, uint32_t bb) {
+  uint4 wa[4], wb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    wa[q] = ca[q];
+    wb[q] = cb[q];
+  }
+  float pa = 0.f, pb = 0.f, sv = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a[4] = {wa[q].x, wa[q].y, wa[q].z, wa[q].w}, b[4] = {wb[q].x, wb[q].y, wb[q].z, wb[q].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(v + 16 * q + 4 * w);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv += xv[i];
+        pa = fmaf(xv[i], (float)((a[w] >> (8 * i)) & 0xFFu), pa);
+        pb = fmaf(xv[i], (float)((b[w] >> (8 * i)) & 0xFFu), pb);
+      }
+    }
+  }
+  return make_float2(fmaf(bf16_bits_to_f32(sa), pa, bf16_bits_to_f32(ba) * sv),
+                     fmaf(bf16_bits_to_f32(sb), pb, bf16_bits_to_f32(bb) * sv));
+}
+
+// The same for one row.
+__device__ __forceinline__ float q8_group_term(const uint4* c, const float* v, uint32_t s, uint32_t b) {
+  uint4 w4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w4[q] = c[q];
+  float p = 0.f, sv = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a[4] = {w4[q].x, w4[q].y, w4[q].z, w4[q].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(v + 16 * q + 4 * w);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv += xv[i];
+        p = fmaf(xv[i], (float)((a[w] >> (8 * i)) & 0xFFu), p);
+      }
+    }
+  }
+  return fmaf(bf16_bits_to_f32(s), p, bf16_bits_to_f32(b) * sv);
+}
+
+// Gate/up of rows i0..i0+7 of an 8-bit shared expert over groups [g_lo, g_hi),
+// in the lane layout of unit_gate_up; xf is the input in padded groups.
+__device__ __forceinline__ float2 unit_gate_up_q8(const DecodeLayer& L, int i0, int g_lo, int g_hi, const float* xf) {
+  const int H = L.hidden, I = L.inter, G = H >> 6;
+  const int lane = lane_id();
+  const int row = min(i0 + (lane >> 3), I - 1), gl = lane & 7;
+  const uint4* gc = reinterpret_cast<const uint4*>(L.sh_gate.codes) + (int64_t)row * (H >> 4);
+  const uint4* uc = reinterpret_cast<const uint4*>(L.sh_up.codes) + (int64_t)row * (H >> 4);
+  const uint16_t* gs = L.sh_gate.scales + (int64_t)row * G;
+  const uint16_t* gb = L.sh_gate.biases + (int64_t)row * G;
+  const uint16_t* us = L.sh_up.scales + (int64_t)row * G;
+  const uint16_t* ub = L.sh_up.biases + (int64_t)row * G;
+  float ag = 0.f, au = 0.f;
+  for (int g = g_lo + gl; g < g_hi; g += 8) {
+    const float2 t = q8_group_terms2(gc + 4 * g, uc + 4 * g, xf + g * kQ8Pad, gs[g], gb[g], us[g], ub[g]);
+    ag += t.x;
+    au += t.y;
+  }
+  return make_float2(group_sum_rt(ag, 3), group_sum_rt(au, 3));
+}
+
+// Gate/up of a shared-expert unit in the shared expert's format.
+template <bool kQ8Shared, int IT>
+__device__ __forceinline__ float2 shared_unit_gate_up(const DecodeLayer& L, int i0, int g_lo, int g_hi,
+                                                      const uint32_t* vp, const float* vs, const float* xf) {
+  if constexpr (kQ8Shared)
+    return unit_gate_up_q8(L, i0, g_lo, g_hi, xf);
+  else
+    return unit_gate_up<IT>(L, -1, i0, g_lo, g_hi, vp, vs);
+}
+
 // Publish the SwiGLU outputs of a unit's rows as tagged words: the 8 lanes that
 // hold rows i0..i0+7 (lane % 8 == 0) write one 64-byte line together.
 __device__ __forceinline__ void publish_unit(unsigned long long* act_slot, int i0, int I, float a, uint32_t epoch) {
@@ -311,8 +400,9 @@ struct DownPrefetch {
 };
 
 // The layer's body, specialised on the router's format (bf16, or 8-bit affine codes) and on
-// a shared-expert gate (the shared expert weighted by sigmoid(sh_gate_w . x)).
-template <bool kQ8Router, bool kShGate>
+// a shared-expert gate (the shared expert weighted by sigmoid(sh_gate_w . x)) and on
+// the shared expert's code width (4 or 8 bits).
+template <bool kQ8Router, bool kShGate, bool kQ8Shared>
 __device__ __forceinline__ void decode_layer(DecodeParams p) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ int32_t s_ids[kMaxTopK + 1];
@@ -330,6 +420,10 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   float* xs = reinterpret_cast<float*>(xp + CH * chunk_stride<1>());                   // [CH]
   uint32_t* ap = reinterpret_cast<uint32_t*>(xs + CH);                                // [nslot][CI][ST2]
   float* as = reinterpret_cast<float*>(ap + (size_t)nslot * CI * chunk_stride<2>());  // [nslot][CI]
+  const size_t xf_off = (reinterpret_cast<const uint32_t*>(as + (size_t)nslot * CI) - smem + 3) & ~size_t(3);
+  float* xf = reinterpret_cast<float*>(smem + xf_off);
+  // (xf: 8-bit shared expert only, x as fp32 [H/64][kQ8Pad], 16-byte aligned)
+  float* af = xf + (size_t)(H >> 6) * kQ8Pad;         // 8-bit shared expert: its activations [I/64][kQ8Pad]
   unsigned* timeouts = &p.ws->timeouts;
 
   const int lane = lane_id();
@@ -442,6 +536,8 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   }
   if (!have_epoch && threadIdx.x == 0) acquire_epoch();
   stage_bf16_parallel(p.x, H, xp, xs, 0, kThreads);
+  if constexpr (kQ8Shared)
+    for (int i = threadIdx.x; i < H; i += kThreads) xf[(i >> 6) * kQ8Pad + (i & 63)] = bf16_bits_to_f32(p.x[i]);
   __syncthreads();
   const uint32_t epoch = s_epoch;
 
@@ -484,12 +580,13 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
     if (units + rgroups <= (int)gridDim.x) {
       if (su >= 0) {
         const int w = wv - 1;
-        const float2 gu = unit_gate_up<2>(p.L, -1, su * kUnitRows, w * G / 3, (w + 1) * G / 3, xp, xs);
+        const float2 gu =
+            shared_unit_gate_up<kQ8Shared, 2>(p.L, su * kUnitRows, w * G / 3, (w + 1) * G / 3, xp, xs, xf);
         if ((lane & 7) == 0) s_third[w][lane >> 3] = gu;
       }
     } else {
       for (int u = (wv - 1) * gridDim.x + blockIdx.x; u < units; u += (kWaves - 1) * gridDim.x) {
-        const float2 gu = unit_gate_up<4>(p.L, -1, u * kUnitRows, 0, G, xp, xs);
+        const float2 gu = shared_unit_gate_up<kQ8Shared, 4>(p.L, u * kUnitRows, 0, G, xp, xs, xf);
         publish_unit(p.act + (size_t)k * I, u * kUnitRows, I, silu(gu.x) * gu.y, epoch);
       }
     }
@@ -541,7 +638,7 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < kPrefetchSlots; ++s) {
       const int j = wv + kWaves * s;
-      if (pf_ok && j < nslot && n < H) {
+      if (pf_ok && j < nslot && n < H && !(kQ8Shared && s_ids[j] < 0)) {
         const int e = s_ids[j];
         const Q4Mat& m = e >= 0 ? p.L.down : p.L.sh_down;
         const int64_t oc = e >= 0 ? e * mat_codes : 0, og = e >= 0 ? e * mat_groups : 0;
@@ -560,6 +657,14 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   // ------------------------------------------------------------ phase C
   stage_tagged_split(p.act, nslot, I, ap, as, epoch, timeouts);  // routed slots and the shared slot
   __syncthreads();
+  if constexpr (kQ8Shared) {
+    // the shared slot's activations again as fp32 (every tag was observed above)
+    const unsigned long long* sa = p.act + (size_t)k * I;
+    for (int i = threadIdx.x; i < I; i += kThreads)
+      af[(i >> 6) * kQ8Pad + (i & 63)] =
+          __uint_as_float((uint32_t)__hip_atomic_load(sa + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+  }
   {
     constexpr int ST = chunk_stride<2>();
     const int64_t mat_codes = (int64_t)H * (I >> 3), mat_groups = (int64_t)H * GI;
@@ -571,7 +676,12 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
         for (int j = wv, s = 0; j < nslot; j += kWaves, ++s) {
           const int e = s_ids[j];
           float part = 0.f;
-          if (first && s < kPrefetchSlots) {
+          if (kQ8Shared && e < 0) {
+            const uint4* cr = reinterpret_cast<const uint4*>(p.L.sh_down.codes) + (int64_t)n * (I >> 4);
+            const uint16_t* sr = p.L.sh_down.scales + (int64_t)n * GI;
+            const uint16_t* br = p.L.sh_down.biases + (int64_t)n * GI;
+            for (int g = subI; g < GI; g += LI) part += q8_group_term(cr + 4 * g, af + g * kQ8Pad, sr[g], br[g]);
+          } else if (first && s < kPrefetchSlots) {
             DownPrefetch d = pf[0];
 #pragma unroll
             for (int q = 1; q < kPrefetchSlots; ++q)
@@ -616,12 +726,17 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams p) { decode_layer<false, false>(p); }
-__global__ __launch_bounds__(kThreads) void decode_layer_q8router_kernel(DecodeParams p) { decode_layer<true, false>(p); }
-__global__ __launch_bounds__(kThreads) void decode_layer_gated_kernel(DecodeParams p) { decode_layer<false, true>(p); }
-__global__ __launch_bounds__(kThreads) void decode_layer_q8router_gated_kernel(DecodeParams p) {
-  decode_layer<true, true>(p);
-}
+#define Q4MOE_DECODE_KERNEL(name, q8r, gated, q8sh) \
+  __global__ __launch_bounds__(kThreads) void name(DecodeParams p) { decode_layer<q8r, gated, q8sh>(p); }
+Q4MOE_DECODE_KERNEL(decode_layer_kernel, false, false, false)
+Q4MOE_DECODE_KERNEL(decode_layer_q8router_kernel, true, false, false)
+Q4MOE_DECODE_KERNEL(decode_layer_gated_kernel, false, true, false)
+Q4MOE_DECODE_KERNEL(decode_layer_q8router_gated_kernel, true, true, false)
+Q4MOE_DECODE_KERNEL(decode_layer_q8shared_kernel, false, false, true)
+Q4MOE_DECODE_KERNEL(decode_layer_q8router_q8shared_kernel, true, false, true)
+Q4MOE_DECODE_KERNEL(decode_layer_gated_q8shared_kernel, false, true, true)
+Q4MOE_DECODE_KERNEL(decode_layer_q8router_gated_q8shared_kernel, true, true, true)
+#undef Q4MOE_DECODE_KERNEL
 
 int lanes_log2(int groups) {
   int r = 0;
@@ -633,8 +748,10 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 size_t decode_lds(const DecodeLayer& L) {
   const int nslot = L.top_k + (L.has_shared ? 1 : 0);
-  return (size_t)(L.hidden >> 5) * (chunk_stride<1>() * 4 + 4) +
-         (size_t)nslot * (L.inter >> 5) * (chunk_stride<2>() * 4 + 4);
+  size_t b = (size_t)(L.hidden >> 5) * (chunk_stride<1>() * 4 + 4) +
+             (size_t)nslot * (L.inter >> 5) * (chunk_stride<2>() * 4 + 4);
+  if (L.has_shared && L.sh_q8) b += 16 + (size_t)((L.hidden >> 6) + (L.inter >> 6)) * kQ8Pad * 4;
+  return b;
 }
 
 }  // namespace
@@ -665,15 +782,17 @@ hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, 
   const size_t lds = decode_lds(L);
   int blocks = device_cu_count();
   if (blocks > kMaxBlocks) blocks = kMaxBlocks;
-  const bool q8 = L.router_q8.codes != nullptr, gated = L.sh_gate_w != nullptr && L.has_shared;
-  if (q8 && gated)
-    hipLaunchKernelGGL(decode_layer_q8router_gated_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
-  else if (q8)
-    hipLaunchKernelGGL(decode_layer_q8router_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
-  else if (gated)
-    hipLaunchKernelGGL(decode_layer_gated_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
-  else
-    hipLaunchKernelGGL(decode_layer_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
+  typedef void (*Kernel)(DecodeParams);
+  static const Kernel kernels[2][2][2] = {
+      {{decode_layer_kernel, decode_layer_q8shared_kernel}, {decode_layer_gated_kernel, decode_layer_gated_q8shared_kernel}},
+      {{decode_layer_q8router_kernel, decode_layer_q8router_q8shared_kernel},
+       {decode_layer_q8router_gated_kernel, decode_layer_q8router_gated_q8shared_kernel}}};
+  const int q8 = L.router_q8.codes != nullptr, gated = L.sh_gate_w != nullptr && L.has_shared,
+            q8sh = L.has_shared && L.sh_q8;
+  void* args[] = {&p};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernels[q8][gated][q8sh]), dim3(blocks),
+                                       dim3(kThreads), args, lds, stream);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ struct DecodeLayer {
   Q4Mat sh_gate, sh_up, sh_down;         // shared (count 1) when has_shared
   Q4Mat router_q8;                       // 8-bit router [E][H/4] words, or codes null (bf16 router)
   const uint16_t* sh_gate_w;             // null, or bf16 [H]: shared expert weighted by sigmoid(w . x)
+  int sh_q8;                             // shared expert in 8-bit codes ([.][H/4] or [.][I/4] words)
 };
 size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k);
 size_t decode_lds_bytes(const DecodeLayer& L);

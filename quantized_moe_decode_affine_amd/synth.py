@@ -108,11 +108,12 @@ def token_rows(seed: int, rows: int, hidden: int = HIDDEN, index: int = 0):
 
 
 class Q4Stack:
-    """``count`` stacked Q4 matrices of shape n x k, as three contiguous arrays."""
+    """``count`` stacked affine matrices of shape n x k (4-bit codes, or 8-bit with
+    bits = 8), as three contiguous arrays."""
 
-    def __init__(self, count: int, n: int, k: int):
+    def __init__(self, count: int, n: int, k: int, bits: int = 4):
         self.count, self.n, self.k = count, n, k
-        self.codes = np.empty((count, n, k // 8), dtype=np.uint32)
+        self.codes = np.empty((count, n, k * bits // 32), dtype=np.uint32)
         self.scales = np.empty((count, n, k // GROUP), dtype=np.uint16)
         self.biases = np.empty((count, n, k // GROUP), dtype=np.uint16)
 
@@ -164,17 +165,24 @@ class MoELayer:
 
 def moe_layer(seed: int, layer: int = 0, hidden: int = HIDDEN, inter: int = INTER,
               n_experts: int = N_EXPERTS, top_k: int = TOP_K, shared: bool = True,
-              threads: int | None = None, router_bits: int = 16, shared_gate: bool = False) -> MoELayer:
+              threads: int | None = None, router_bits: int = 16, shared_gate: bool = False,
+              shared_bits: int = 4) -> MoELayer:
     """Generate one MoE layer; experts are drawn in parallel threads (numpy releases the GIL).
     router_bits = 8 adds an affine-Q8 router (weights of about the bf16 router's spread,
     0.02) that replaces the bf16 one.  shared_gate adds a bf16 shared-expert gate vector,
-    N(0, 0.02), stream [seed, layer, 20001]."""
+    N(0, 0.02), stream [seed, layer, 20001].  shared_bits = 8 draws the shared expert as
+    affine-Q8 matrices (q8_matrix streams, weights of about the 4-bit experts' spread)."""
     gate = Q4Stack(n_experts, inter, hidden)
     up = Q4Stack(n_experts, inter, hidden)
     down = Q4Stack(n_experts, hidden, inter)
-    sh = [Q4Stack(1, inter, hidden), Q4Stack(1, inter, hidden), Q4Stack(1, hidden, inter)] if shared else [None] * 3
+    sh_shapes = [(inter, hidden), (inter, hidden), (hidden, inter)]
+    sh = [Q4Stack(1, n, k, bits=shared_bits) for n, k in sh_shapes] if shared else [None] * 3
 
     def one(e: int) -> None:
+        if e == n_experts and shared_bits == 8:
+            for m, (n, k), which in zip(sh, sh_shapes, (GATE, UP, DOWN)):
+                m.fill(0, q8_matrix(seed, layer, e, which, n, k))
+            return
         g = q4_matrix(seed, layer, e, GATE, inter, hidden)
         u = q4_matrix(seed, layer, e, UP, inter, hidden)
         d = q4_matrix(seed, layer, e, DOWN, hidden, inter)

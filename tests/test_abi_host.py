@@ -252,3 +252,24 @@ def test_shared_gate_layers(lib):
     assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A2, 0, A, need_p - 1, None) == B.EWORKSPACE
     need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(_layer()), None, 2)
     assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b, None) == B.EUNSUPPORTED
+
+
+def test_q8_shared_expert_layers(lib):
+    """An 8-bit shared expert (all three matrices) is taken by moe_ffn_decode only; a mix of
+    4- and 8-bit shared matrices is rejected everywhere."""
+    def q8(n, k):
+        m = _mat(1, n, k)
+        m.bits = 8
+        return m
+    H, I = 128, 64
+    L = _layer(sh_gate=q8(I, H), sh_up=q8(I, H), sh_down=q8(H, I))
+    need_d = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE, ctypes.byref(L), None, 1)
+    assert need_d > 0
+    d = lib.moe_ffn_decode
+    assert d(ctypes.byref(L), A, A2, 0, None, None, A, need_d - 1, None) == B.EWORKSPACE  # valid up to the workspace
+    need_p = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(L), None, 50)
+    assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A2, 0, A, need_p, None) == B.EUNSUPPORTED
+    need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(_layer()), None, 2)
+    assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b, None) == B.EUNSUPPORTED
+    mixed = _layer(sh_gate=q8(I, H), sh_up=q8(I, H))
+    assert d(ctypes.byref(mixed), A, A2, 0, None, None, A, need_d, None) == B.EUNSUPPORTED

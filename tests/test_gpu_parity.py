@@ -600,3 +600,33 @@ def test_prefill_shared_gate(B, T, H, I, E, k):
     err, worst = _prefill_check(B, layer, dl, X)
     assert err <= REL_L2_TOL, err
     assert worst <= 2 * REL_L2_TOL
+
+
+@pytest.mark.parametrize("H,I,E,k,rbits,gated", [(256, 128, 16, 4, 16, False), (384, 192, 16, 4, 8, True),
+                                                 (64, 64, 4, 2, 16, False), (2048, 512, 256, 8, 8, False),
+                                                 (2048, 512, 256, 8, 8, True), (4096, 1024, 16, 4, 16, False)])
+def test_decode_q8_shared_expert(B, H, I, E, k, rbits, gated):
+    """Batch-1 decode with the shared expert in affine-Q8 codes (the q4-xl checkpoint's form),
+    alone or with the 8-bit router and the shared-expert gate."""
+    say(f"decode q8 shared H={H} I={I} E={E} k={k} router bits={rbits} gated={gated}")
+    layer = synth.moe_layer(101, 0, H, I, E, k, router_bits=rbits, shared_gate=gated, shared_bits=8)
+    dl = B.DeviceLayer(layer)
+    assert all(m.bits == 8 for m in dl.sh)
+    n_exact = 0
+    for step in range(4):
+        err, exact = _decode_check(B, layer, dl, synth.hidden_vector(101, step, 0, H), with_bf16=True)
+        assert err <= 1e-5
+        n_exact += exact
+    assert n_exact >= 3
+
+
+def test_decode_q8_shared_residual(B):
+    """The residual form with an 8-bit shared expert: bf16(x + y) of the layer's own fp32 output."""
+    H, I, E, k = 2048, 512, 256, 8
+    layer = synth.moe_layer(102, 0, H, I, E, k, router_bits=8, shared_bits=8)
+    dl = B.DeviceLayer(layer)
+    x = B.bf16_tensor(synth.hidden_vector(102, 0, 0, H))
+    xn = B.moe_ffn_decode(dl, x, B.OUT_BF16_RESIDUAL)
+    y = B.moe_ffn_decode(dl, x, B.OUT_F32)
+    _sync()
+    assert torch.equal(xn.cpu(), (x.cpu().float() + y.cpu()).to(torch.bfloat16))

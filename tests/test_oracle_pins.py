@@ -462,3 +462,34 @@ def test_shared_gate_closed_forms():
     np.testing.assert_allclose(orc.sigmoid(np.array([-3.0, 1.0])), scipy.special.expit([-3.0, 1.0]), rtol=1e-15)
     Y, _, _, _ = orc.moe_ffn_prefill(layer, np.stack([x, x]))
     np.testing.assert_allclose(Y[1], yf, rtol=1e-12, atol=1e-12)
+
+
+def _nibbles(words):
+    """Independent unpacker of 4-bit rows: nibble j of a row from bits [4(j%8), 4(j%8)+4) of word j//8."""
+    return np.array([[(int(wd) >> (4 * j)) & 15 for wd in row for j in range(8)] for row in words])
+
+
+def test_q8_shared_expert_equals_q4_on_same_codes():
+    """A shared expert stored as 8-bit codes that hold the 4-bit expert's codes (same scales and
+    biases) gives the layer output of the 4-bit one exactly; an 8-bit shared expert drawn by
+    the generator uses codes above 15 and changes only the shared part."""
+    H, I, E, k = 128, 64, 8, 2
+    layer = synth.moe_layer(13, 0, H, I, E, k)
+    x = synth.hidden_vector(13, 0, 0, H)
+    y4, ids4, _, _ = orc.moe_ffn_token(layer, x)
+    routed = y4 - orc.expert_ffn(layer.expert(E), orc.bf16_to_f64(x))
+    for name in ("sh_gate", "sh_up", "sh_down"):
+        st = getattr(layer, name)
+        c, s, b = st.matrix(0)
+        q8 = synth.Q4Stack(1, st.n, st.k, bits=8)
+        q8.fill(0, (_pack_bytes(_nibbles(c)), s, b))
+        setattr(layer, name, q8)
+    y8, ids8, _, _ = orc.moe_ffn_token(layer, x)
+    np.testing.assert_array_equal(ids8, ids4)
+    np.testing.assert_array_equal(y8, y4)
+    wide = synth.moe_layer(13, 0, H, I, E, k, shared_bits=8)
+    assert wide.sh_down.codes.shape == (1, H, I // 4) and (wide.sh_gate.codes >> 4 & 15).any()
+    yw, idsw, _, _ = orc.moe_ffn_token(wide, x)
+    np.testing.assert_array_equal(idsw, ids4)  # same router and routed experts
+    np.testing.assert_allclose(yw - orc.expert_ffn(wide.expert(E), orc.bf16_to_f64(x)), routed,
+                               rtol=1e-12, atol=1e-12)

@@ -207,6 +207,29 @@ def main():
             "GB_s": round(q_bytes / (q_us * 1e-6) / 1e9, 1),
             "pct_of_hbm_peak": round(100 * q_bytes / (q_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
         log(f"decode q8 router: {result['decode_q8_router']}")
+        # the checkpoint's form: 8-bit router and 8-bit shared expert (decode_layer_q8router_q8shared_kernel)
+        stack.enable_q8_shared(dev)
+        stack.use_q8_router(True)
+        for s in range(args.warmup):
+            stack.step(s)
+        torch.cuda.synchronize()
+        ev0.record()
+        for s in range(args.steps):
+            stack.step(s)
+        ev1.record()
+        torch.cuda.synchronize()
+        c_us = ev0.elapsed_time(ev1) * 1e3 / (args.steps * args.layers)
+        stack.use_q8_router(False)
+        c_bytes = q_bytes - 2 * workloads.q4_matrix_bytes(synth.INTER, synth.HIDDEN) - \
+            workloads.q4_matrix_bytes(synth.HIDDEN, synth.INTER) + \
+            2 * workloads.q8_matrix_bytes(synth.INTER, synth.HIDDEN) + workloads.q8_matrix_bytes(synth.HIDDEN, synth.INTER)
+        result["decode_q8_router"]["with_q8_shared_expert"] = {
+            "workload": "the same loop with the shared expert in affine-Q8 codes as well "
+                        "(decode_layer_q8router_q8shared_kernel)",
+            "us_per_layer": round(c_us, 3), "bytes_per_layer": c_bytes,
+            "GB_s": round(c_bytes / (c_us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * c_bytes / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        log(f"decode q8 router + q8 shared expert: {result['decode_q8_router']['with_q8_shared_expert']}")
 
     if "chain" in legs:
         # ------------------- residual-chained decode step + LM head: eager launches vs a replayed graph

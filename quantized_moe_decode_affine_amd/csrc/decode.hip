@@ -107,17 +107,24 @@ __device__ __forceinline__ float store_split_block(const float (&v)[8], uint32_t
   return sum;
 }
 
+// Padded row length (floats) of a 64-column group in the fp32 LDS copies that an
+// 8-bit shared expert is read against (the padding puts the groups of neighbouring
+// lanes on different banks).
+constexpr int kQ8Pad = 68;
+
 // Stage `nvec` tagged fp32 vectors of n values each (contiguous, published by
 // other workgroups as {epoch, bits} words; nvec * n a multiple of 32) as hi/lo
 // bf16 parts.  Lane-contiguous 16-byte device-coherent loads (two words per
 // lane, all rounds in flight together); only pairs not yet complete are loaded
 // again (bounded; a timeout is counted).  A lane quad holds one 8-value block:
 // lanes 0-1 of the quad assemble its permuted pair words from their own values
-// and the matching ones of lanes 2-3; 16 lanes hold one 32-value chunk.
+// and the matching ones of lanes 2-3; 16 lanes hold one 32-value chunk.  With f32_dst, the
+// values from flat index f32_first on are also written as fp32 in kQ8Pad-padded groups.
 constexpr int kTagRounds = 9;  // 16-byte loads per thread: 9 x 256 x 2 words = 4608 = 9 slots x 512
 
 __device__ __forceinline__ void stage_tagged_split(const unsigned long long* src, int nvec, int n, uint32_t* vp,
-                                                   float* vs, uint32_t epoch, unsigned* timeouts) {
+                                                   float* vs, uint32_t epoch, unsigned* timeouts,
+                                                   float* f32_dst = nullptr, int f32_first = 0) {
   constexpr int ST = chunk_stride<2>();
   const int t = threadIdx.x, nthr = blockDim.x;
   const int npairs = (nvec * n) >> 1;
@@ -153,6 +160,10 @@ __device__ __forceinline__ void stage_tagged_split(const unsigned long long* src
       const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
       const uint32_t l0 = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0)), l1 = f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1));
       const float part = (bf16_bits_to_f32(h0) + bf16_bits_to_f32(l0)) + (bf16_bits_to_f32(h1) + bf16_bits_to_f32(l1));
+      if (f32_dst && ok && 2 * q >= f32_first) {  // values from f32_first on, also as fp32 in padded groups
+        const int i = 2 * q - f32_first;
+        *reinterpret_cast<float2*>(f32_dst + (i >> 6) * kQ8Pad + (i & 63)) = make_float2(v0, v1);
+      }
       // values j0 + 4, j0 + 5 from the lane two places over in the quad
       const uint32_t hh = dpp_u32<kDppQuadXor2>(h0 | h1 << 16), ll = dpp_u32<kDppQuadXor2>(l0 | l1 << 16);
       if (ok && (q & 2) == 0) {
@@ -238,8 +249,22 @@ __device__ __forceinline__ float2 unit_gate_up(const DecodeLayer& L, int e, int 
 
 // An 8-bit shared expert (affine Q8, code j of a row in byte j % 4 of word j / 4)
 // is read against fp32 copies of its input in LDS, one 64-column group per row of
-// kQ8Pad floats (the padding puts the groups of neighbouring lanes on different banks).
-constexpr int kQ8Pad = 68;
+// kQ8Pad floats: the 64 values, then (for x) their sum.  Its gate/up units are 8 rows
+// of 8 lanes, as for 4-bit codes.
+constexpr int kQ8UnitRows = 8, kQ8LaneLog = 3;
+
+// Stage a vector of n values (n a multiple of 64; value i from get(i)) into padded
+// groups with their sums, one group per wave at a time.
+template <class Get>
+__device__ __forceinline__ void stage_q8_groups(float* dst, int n, Get get) {
+  const int lane = lane_id();
+  for (int g = threadIdx.x / kWave; g < (n >> 6); g += kThreads / kWave) {
+    const float v = get(g * 64 + lane);
+    dst[g * kQ8Pad + lane] = v;
+    const float t = group_sum_rt(v, 6);
+    if (lane == 0) dst[g * kQ8Pad + 64] = t;
+  }
+}
 
 // scale * sum(q v) + bias * sum(v) over one 64-column group of an 8-bit row, for
 // two rows (a: codes ca, b: codes cb) against the same 64 values v.
@@ -251,7 +276,8 @@ __device__ __forceinline__ float2 q8_group_terms2(const uint4* ca, const uint4* 
     wa[q] = ca[q];
     wb[q] = cb[q];
   }
-  float pa = 0.f, pb = 0.f, sv = 0.f;
+  float pa = 0.f, pb = 0.f;
+  const float sv = v[64];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t a[4] = {wa[q].x, wa[q].y, wa[q].z, wa[q].w}, b[4] = {wb[q].x, wb[q].y, wb[q].z, wb[q].w};
@@ -261,7 +287,6 @@ __device__ __forceinline__ float2 q8_group_terms2(const uint4* ca, const uint4* 
       const float xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv += xv[i];
         pa = fmaf(xv[i], (float)((a[w] >> (8 * i)) & 0xFFu), pa);
         pb = fmaf(xv[i], (float)((b[w] >> (8 * i)) & 0xFFu), pb);
       }
@@ -271,11 +296,8 @@ __device__ __forceinline__ float2 q8_group_terms2(const uint4* ca, const uint4* 
                      fmaf(bf16_bits_to_f32(sb), pb, bf16_bits_to_f32(bb) * sv));
 }
 
-// The same for one row.
-__device__ __forceinline__ float q8_group_term(const uint4* c, const float* v, uint32_t s, uint32_t b) {
-  uint4 w4[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) w4[q] = c[q];
+// The same for one row whose 64 codes are already in registers.
+__device__ __forceinline__ float q8_group_term_regs(const uint4 (&w4)[4], const float* v, uint32_t s, uint32_t b) {
   float p = 0.f, sv = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -294,12 +316,22 @@ __device__ __forceinline__ float q8_group_term(const uint4* c, const float* v, u
   return fmaf(bf16_bits_to_f32(s), p, bf16_bits_to_f32(b) * sv);
 }
 
-// Gate/up of rows i0..i0+7 of an 8-bit shared expert over groups [g_lo, g_hi),
-// in the lane layout of unit_gate_up; xf is the input in padded groups.
+// The same for one row read from memory.
+__device__ __forceinline__ float q8_group_term(const uint4* c, const float* v, uint32_t s, uint32_t b) {
+  uint4 w4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w4[q] = c[q];
+  return q8_group_term_regs(w4, v, s, b);
+}
+
+// Gate/up of rows i0..i0+3 of an 8-bit shared expert over groups [g_lo, g_hi): lane l
+// takes row i0 + l/16 and groups g_lo + l%16 + 16t, two groups' loads in flight; every
+// lane of a row's 16-lane group returns that row's (g, u).  xf is the input in padded groups.
 __device__ __forceinline__ float2 unit_gate_up_q8(const DecodeLayer& L, int i0, int g_lo, int g_hi, const float* xf) {
+  constexpr int LPR = 1 << kQ8LaneLog;
   const int H = L.hidden, I = L.inter, G = H >> 6;
   const int lane = lane_id();
-  const int row = min(i0 + (lane >> 3), I - 1), gl = lane & 7;
+  const int row = min(i0 + (lane >> kQ8LaneLog), I - 1), gl = lane & (LPR - 1);
   const uint4* gc = reinterpret_cast<const uint4*>(L.sh_gate.codes) + (int64_t)row * (H >> 4);
   const uint4* uc = reinterpret_cast<const uint4*>(L.sh_up.codes) + (int64_t)row * (H >> 4);
   const uint16_t* gs = L.sh_gate.scales + (int64_t)row * G;
@@ -307,12 +339,22 @@ __device__ __forceinline__ float2 unit_gate_up_q8(const DecodeLayer& L, int i0, 
   const uint16_t* us = L.sh_up.scales + (int64_t)row * G;
   const uint16_t* ub = L.sh_up.biases + (int64_t)row * G;
   float ag = 0.f, au = 0.f;
-  for (int g = g_lo + gl; g < g_hi; g += 8) {
-    const float2 t = q8_group_terms2(gc + 4 * g, uc + 4 * g, xf + g * kQ8Pad, gs[g], gb[g], us[g], ub[g]);
-    ag += t.x;
-    au += t.y;
+  for (int base = g_lo; base < g_hi; base += 2 * LPR) {  // wave-uniform trip count
+    // groups past the range are read clamped (in bounds) and their terms dropped
+    const bool ok0 = base + gl < g_hi, ok1 = base + gl + LPR < g_hi;
+    const int g0 = min(base + gl, g_hi - 1), g1 = min(base + gl + LPR, g_hi - 1);
+    const float2 t0 = q8_group_terms2(gc + 4 * g0, uc + 4 * g0, xf + g0 * kQ8Pad, gs[g0], gb[g0], us[g0], ub[g0]);
+    const float2 t1 = q8_group_terms2(gc + 4 * g1, uc + 4 * g1, xf + g1 * kQ8Pad, gs[g1], gb[g1], us[g1], ub[g1]);
+    if (ok0) {
+      ag += t0.x;
+      au += t0.y;
+    }
+    if (ok1) {
+      ag += t1.x;
+      au += t1.y;
+    }
   }
-  return make_float2(group_sum_rt(ag, 3), group_sum_rt(au, 3));
+  return make_float2(group_sum_rt(ag, kQ8LaneLog), group_sum_rt(au, kQ8LaneLog));
 }
 
 // Gate/up of a shared-expert unit in the shared expert's format.
@@ -327,10 +369,11 @@ __device__ __forceinline__ float2 shared_unit_gate_up(const DecodeLayer& L, int 
 
 // Publish the SwiGLU outputs of a unit's rows as tagged words: the 8 lanes that
 // hold rows i0..i0+7 (lane % 8 == 0) write one 64-byte line together.
+template <int LOG = 3>
 __device__ __forceinline__ void publish_unit(unsigned long long* act_slot, int i0, int I, float a, uint32_t epoch) {
   const int lane = lane_id();
-  const int i = i0 + (lane >> 3);
-  if ((lane & 7) == 0 && i < I)
+  const int i = i0 + (lane >> LOG);
+  if ((lane & ((1 << LOG) - 1)) == 0 && i < I)
     __hip_atomic_store(act_slot + i, ((unsigned long long)epoch << 32) | __float_as_uint(a), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -536,8 +579,7 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   }
   if (!have_epoch && threadIdx.x == 0) acquire_epoch();
   stage_bf16_parallel(p.x, H, xp, xs, 0, kThreads);
-  if constexpr (kQ8Shared)
-    for (int i = threadIdx.x; i < H; i += kThreads) xf[(i >> 6) * kQ8Pad + (i & 63)] = bf16_bits_to_f32(p.x[i]);
+  if constexpr (kQ8Shared) stage_q8_groups(xf, H, [&](int i) { return bf16_bits_to_f32(p.x[i]); });
   __syncthreads();
   const uint32_t epoch = s_epoch;
 
@@ -575,30 +617,31 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
     // at most one unit per workgroup, waves 1-3 split its groups in thirds and
     // wave 1 adds the thirds after the barrier below; otherwise each wave takes
     // whole units.
-    const int units = (I + kUnitRows - 1) / kUnitRows, G = H >> 6;
+    constexpr int R = kQ8Shared ? kQ8UnitRows : kUnitRows, LOG = kQ8Shared ? kQ8LaneLog : 3;
+    const int units = (I + R - 1) / R, G = H >> 6;
     const int su = shared_unit_of(blockIdx.x, gridDim.x, rgroups, units);
     if (units + rgroups <= (int)gridDim.x) {
       if (su >= 0) {
         const int w = wv - 1;
-        const float2 gu =
-            shared_unit_gate_up<kQ8Shared, 2>(p.L, su * kUnitRows, w * G / 3, (w + 1) * G / 3, xp, xs, xf);
-        if ((lane & 7) == 0) s_third[w][lane >> 3] = gu;
+        const float2 gu = shared_unit_gate_up<kQ8Shared, 2>(p.L, su * R, w * G / 3, (w + 1) * G / 3, xp, xs, xf);
+        if ((lane & ((1 << LOG) - 1)) == 0) s_third[w][lane >> LOG] = gu;
       }
     } else {
       for (int u = (wv - 1) * gridDim.x + blockIdx.x; u < units; u += (kWaves - 1) * gridDim.x) {
-        const float2 gu = shared_unit_gate_up<kQ8Shared, 4>(p.L, u * kUnitRows, 0, G, xp, xs, xf);
-        publish_unit(p.act + (size_t)k * I, u * kUnitRows, I, silu(gu.x) * gu.y, epoch);
+        const float2 gu = shared_unit_gate_up<kQ8Shared, 4>(p.L, u * R, 0, G, xp, xs, xf);
+        publish_unit<LOG>(p.act + (size_t)k * I, u * R, I, silu(gu.x) * gu.y, epoch);
       }
     }
   }
   __syncthreads();
   if (p.L.has_shared && wv == 1) {
-    const int units = (I + kUnitRows - 1) / kUnitRows;
+    constexpr int R = kQ8Shared ? kQ8UnitRows : kUnitRows, LOG = kQ8Shared ? kQ8LaneLog : 3;
+    const int units = (I + R - 1) / R;
     const int su = shared_unit_of(blockIdx.x, gridDim.x, rgroups, units);
     if (units + rgroups <= (int)gridDim.x && su >= 0) {
-      const float2 a = s_third[0][lane >> 3], b = s_third[1][lane >> 3], c = s_third[2][lane >> 3];
+      const float2 a = s_third[0][lane >> LOG], b = s_third[1][lane >> LOG], c = s_third[2][lane >> LOG];
       const float g = (a.x + b.x) + c.x, up = (a.y + b.y) + c.y;
-      publish_unit(p.act + (size_t)k * I, su * kUnitRows, I, silu(g) * up, epoch);
+      publish_unit<LOG>(p.act + (size_t)k * I, su * R, I, silu(g) * up, epoch);
     }
   }
 
@@ -632,6 +675,20 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   const int GI = I >> 6;
   const bool pf_ok = GI == LI && (int)blockIdx.x * rpiI < H;
   DownPrefetch pf[kPrefetchSlots];
+  // an 8-bit shared expert: the down-row group of this lane for the first row block,
+  // held by the wave that takes the shared slot (slot k, wave k % kWaves)
+  uint4 qpf[4] = {};
+  uint32_t qps = 0, qpb = 0;
+  if constexpr (kQ8Shared) {
+    const int n = blockIdx.x * rpiI + rsubI;
+    if (pf_ok && k % kWaves == wv && n < H) {
+      const uint4* cr = reinterpret_cast<const uint4*>(p.L.sh_down.codes) + (int64_t)n * (I >> 4) + 4 * subI;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) qpf[q] = cr[q];
+      qps = p.L.sh_down.scales[(int64_t)n * GI + subI];
+      qpb = p.L.sh_down.biases[(int64_t)n * GI + subI];
+    }
+  }
   {
     const int n = blockIdx.x * rpiI + rsubI;
     const int64_t mat_codes = (int64_t)H * (I >> 3), mat_groups = (int64_t)H * GI;
@@ -655,16 +712,9 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
   }
 
   // ------------------------------------------------------------ phase C
-  stage_tagged_split(p.act, nslot, I, ap, as, epoch, timeouts);  // routed slots and the shared slot
+  // routed slots and the shared slot (an 8-bit shared expert's slot also as fp32 into af)
+  stage_tagged_split(p.act, nslot, I, ap, as, epoch, timeouts, kQ8Shared ? af : nullptr, k * I);
   __syncthreads();
-  if constexpr (kQ8Shared) {
-    // the shared slot's activations again as fp32 (every tag was observed above)
-    const unsigned long long* sa = p.act + (size_t)k * I;
-    for (int i = threadIdx.x; i < I; i += kThreads)
-      af[(i >> 6) * kQ8Pad + (i & 63)] =
-          __uint_as_float((uint32_t)__hip_atomic_load(sa + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    __syncthreads();
-  }
   {
     constexpr int ST = chunk_stride<2>();
     const int64_t mat_codes = (int64_t)H * (I >> 3), mat_groups = (int64_t)H * GI;
@@ -676,7 +726,9 @@ __device__ __forceinline__ void decode_layer(DecodeParams p) {
         for (int j = wv, s = 0; j < nslot; j += kWaves, ++s) {
           const int e = s_ids[j];
           float part = 0.f;
-          if (kQ8Shared && e < 0) {
+          if (kQ8Shared && e < 0 && first) {
+            part = q8_group_term_regs(qpf, af + subI * kQ8Pad, qps, qpb);  // one group per lane (GI == LI)
+          } else if (kQ8Shared && e < 0) {
             const uint4* cr = reinterpret_cast<const uint4*>(p.L.sh_down.codes) + (int64_t)n * (I >> 4);
             const uint16_t* sr = p.L.sh_down.scales + (int64_t)n * GI;
             const uint16_t* br = p.L.sh_down.biases + (int64_t)n * GI;

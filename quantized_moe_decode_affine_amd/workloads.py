@@ -109,6 +109,18 @@ class DecodeStack:
             self._refs_q8.append(ctypes.byref(st))
         self._refs_bf16 = self._refs
 
+    def enable_q8_shared(self, device="cuda") -> None:
+        """Also give every layer's 8-bit-router descriptor an affine-Q8 shared expert (drawn as
+        synth.moe_layer draws one with shared_bits=8): the checkpoint's form, an 8-bit router and
+        an 8-bit shared expert.  :meth:`use_q8_router` then runs the layers in that form."""
+        H, I, E = self.layers[0].hidden, self.layers[0].inter, self.layers[0].n_experts
+        self.q8_shared = []
+        for l, (_, st) in enumerate(self.q8_routers):
+            mats = [B.DeviceQ4(*synth.q8_matrix(self.seed, l, E, which, n, k), device=device)
+                    for which, n, k in ((synth.GATE, I, H), (synth.UP, I, H), (synth.DOWN, H, I))]
+            st.sh_gate, st.sh_up, st.sh_down = (m.struct for m in mats)
+            self.q8_shared.append(mats)
+
     def use_q8_router(self, on: bool) -> None:
         self._refs = self._refs_q8 if on else self._refs_bf16
 

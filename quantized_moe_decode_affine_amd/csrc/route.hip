@@ -213,91 +213,110 @@ int grid_for(int64_t n, int block) {
   return (int)(b < 1 ? 1 : b);
 }
 
-// Router logits from the 8-bit affine router (the checkpoint's Q8 router-gate exception,
-// "2026-09-02: Lily vs MLX 0.32.2", "Hardware and software"): logits[t][e] for a tile of
-// kQ8Tok tokens x 64 experts per workgroup (two workgroups per CU at 2,048 tokens), one
-// 64-column group per step.  The group's rows of X go to LDS as fp32 and the experts'
-// codes as fp32 transposed ([column][expert], each wave converting one 16-column slice for
-// all 64 experts), so a thread's 4 experts at column j are one 16-byte read and a wave's 16
-// expert quads read consecutive words; each thread's 16-byte pieces of the next group load
-// while the current one computes.  Thread (tt, te) accumulates token tt x experts
-// 4te..4te+3: per group scale * sum(x q) + bias * sum(x), products exact, fp32 sums.
-constexpr int kQ8Tok = 16;
-__global__ __launch_bounds__(256) void q8_router_logits_kernel(Q4Mat R, const uint16_t* __restrict__ X, int64_t T,
+// Router logits from an 8-bit affine router on bf16 matrix cores: the tiling of
+// router_logits_kernel (32 tokens x 64 experts, 8 waves = 2 expert halves x 4 K
+// quarters), whose 64-column K steps are exactly the quantization groups.  Codes
+// 0..255 are exact in bfloat16 (the high half of their fp32 value), so each group's
+// sum(x q) comes exact-product, fp32-summed from 4 MFMAs into a fresh accumulator,
+// and is folded as acc += scale * sum(x q) + bias * sum(x); the tile's per-group
+// token sums sum(x) are computed first into LDS ([group][token], dynamic).
+__device__ __forceinline__ bf16x8_t bytes_to_bf16x8(uint2 c) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = i < 2 ? c.x : c.y;
+    const int sh = 16 * (i & 1);
+    const uint32_t lo = __float_as_uint((float)((w >> sh) & 0xFFu)) >> 16;
+    const uint32_t hi = __float_as_uint((float)((w >> (sh + 8)) & 0xFFu)) & 0xFFFF0000u;
+    o[i] = lo | hi;
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+__global__ __launch_bounds__(512) void q8_router_logits_kernel(Q4Mat R, const uint16_t* __restrict__ X, int64_t T,
                                                                int E, int H, float* __restrict__ logits) {
-  __shared__ float s_x[kQ8Tok][65];            // one group of the tile's token rows (padded row)
-  __shared__ __align__(16) float s_q[64][64];  // [column][expert]
-  __shared__ float s_sc[64], s_bi[64], s_xs[kQ8Tok];
-  const int64_t t0 = (int64_t)blockIdx.x * kQ8Tok;
-  const int e0 = blockIdx.y * 64;
-  const int te = threadIdx.x & 15, tt = threadIdx.x >> 4;
+  extern __shared__ __align__(16) float s_xsum[];  // [G][32]
+  __shared__ f32x16_t s_part[3][2][kWave];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int eh = wave & 1, kq = wave >> 1;
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const int e0 = blockIdx.y * 64 + eh * 32;
   const int G = H >> 6;
-  float acc[4] = {};
-  // this thread's 16-byte pieces of a group: X row r, block blk (threads < 8 kQ8Tok);
-  // codes of expert e, slice ch
-  const bool xload = threadIdx.x < 8 * kQ8Tok;
-  const int r = (threadIdx.x >> 3) % kQ8Tok, blk = threadIdx.x & 7;
-  const int el = threadIdx.x & 63, ch = threadIdx.x >> 6;
-  const uint16_t* xrow = X + min<int64_t>(t0 + r, T - 1) * H + blk * 8;
-  const int e = min(e0 + el, E - 1);
-  const uint4* crow = reinterpret_cast<const uint4*>(R.codes) + (size_t)e * (H >> 4) + ch;
-  uint4 xv = xload ? *reinterpret_cast<const uint4*>(xrow) : make_uint4(0, 0, 0, 0), cv = crow[0];
-  uint32_t scb = 0, bib = 0;
-  if (ch == 0) {
-    scb = R.scales[(size_t)e * G];
-    bib = R.biases[(size_t)e * G];
+  // token sums of each group (fixed order)
+  for (int pidx = threadIdx.x; pidx < 32 * G; pidx += blockDim.x) {
+    const int tl = pidx & 31, g = pidx >> 5;
+    const uint4* xr = reinterpret_cast<const uint4*>(X + min<int64_t>(t0 + tl, T - 1) * H) + 8 * g;
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v = xr[c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum += bf16_bits_to_f32(w[j] & 0xFFFFu) + bf16_bits_to_f32(w[j] >> 16);
+    }
+    s_xsum[g * 32 + tl] = sum;
   }
-  for (int g = 0; g < G; ++g) {
-    __syncthreads();  // the previous group's LDS reads are done
-    {
-      if (xload) {
-        const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+  __syncthreads();
+  const int m = lane & 31, h = lane >> 5;
+  const int64_t trow = min<int64_t>(t0 + m, T - 1);
+  const int erow = min(e0 + m, E - 1);
+  const uint4* xa = reinterpret_cast<const uint4*>(X + trow * H) + 4 * h;
+  const uint2* cb = reinterpret_cast<const uint2*>(R.codes) + (int64_t)erow * (H >> 3) + 4 * h;
+  const uint16_t* sc = R.scales + (int64_t)erow * G;
+  const uint16_t* bi = R.biases + (int64_t)erow * G;
+  const int s_begin = kq * G / 4, s_end = (kq + 1) * G / 4;
+  f32x16_t acc = {};
+  for (int s0 = s_begin; s0 < s_end; s0 += kRouterBatch) {
+    uint4 av[kRouterBatch][4];
+    uint2 bv[kRouterBatch][4];
+    uint32_t sb[kRouterBatch], bb[kRouterBatch];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s_x[r][blk * 8 + i] = bf16_bits_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      }
-      const uint32_t c[4] = {cv.x, cv.y, cv.z, cv.w};
+    for (int b = 0; b < kRouterBatch; ++b) {
+      const int g = min(s0 + b, s_end - 1);  // groups past the quarter's end are loaded but not used
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s_q[ch * 16 + i][el] = (float)((c[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-      if (ch == 0) {
-        s_sc[el] = bf16_bits_to_f32(scb);
-        s_bi[el] = bf16_bits_to_f32(bib);
+      for (int q = 0; q < 4; ++q) {
+        av[b][q] = xa[g * 8 + q];
+        bv[b][q] = cb[g * 8 + q];
       }
+      sb[b] = sc[g];
+      bb[b] = bi[g];
     }
-    if (g + 1 < G) {  // the next group's pieces load while this group computes
-      if (xload) xv = *reinterpret_cast<const uint4*>(xrow + (g + 1) * 64);
-      cv = crow[(g + 1) * 4];
-      if (ch == 0) {
-        scb = R.scales[(size_t)e * G + g + 1];
-        bib = R.biases[(size_t)e * G + g + 1];
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x < kQ8Tok) {
-      float t = 0.f;
-      for (int j = 0; j < 64; ++j) t += s_x[threadIdx.x][j];  // fixed order
-      s_xs[threadIdx.x] = t;
-    }
-    float pq[4] = {};
-#pragma unroll 16
-    for (int j = 0; j < 64; ++j) {
-      const float4 q = *reinterpret_cast<const float4*>(&s_q[j][4 * te]);
-      const float x0 = s_x[tt][j];
-      pq[0] = fmaf(x0, q.x, pq[0]);
-      pq[1] = fmaf(x0, q.y, pq[1]);
-      pq[2] = fmaf(x0, q.z, pq[2]);
-      pq[3] = fmaf(x0, q.w, pq[3]);
-    }
-    __syncthreads();  // s_xs written
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += fmaf(s_sc[4 * te + u], pq[u], s_bi[4 * te + u] * s_xs[tt]);
+    for (int b = 0; b < kRouterBatch; ++b) {
+      const int g = s0 + b;
+      if (g < s_end) {
+        f32x16_t pq = {};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[b][q]),
+                                                       bytes_to_bf16x8(bv[b][q]), pq, 0, 0, 0);
+        const float s = bf16_bits_to_f32(sb[b]), o = bf16_bits_to_f32(bb[b]);
+        // D layout: column (expert) = lane % 32, row (token) = 8*(i/4) + 4*(lane/32) + i%4
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 xs = *reinterpret_cast<const float4*>(s_xsum + g * 32 + 8 * r4 + 4 * h);
+          const float xv[4] = {xs.x, xs.y, xs.z, xs.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[4 * r4 + i] += fmaf(s, pq[4 * r4 + i], o * xv[i]);
+        }
+      }
+    }
   }
-  const int64_t t = t0 + tt;
-  if (t < T) {
+  if (kq > 0) s_part[kq - 1][eh][lane] = acc;
+  __syncthreads();
+  if (kq > 0) return;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ee = e0 + 4 * te + u;
-      if (ee < E) logits[t * E + ee] = acc[u];
-    }
+  for (int j = 0; j < 3; ++j) {
+    const f32x16_t o = s_part[j][eh][lane];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += o[i];
+  }
+  const int e = e0 + m;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t t = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
+    if (t < T && e < E) logits[t * E + e] = acc[i];
   }
 }
 
@@ -310,8 +329,8 @@ hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* 
   float* logits = static_cast<float*>(ws);
   dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 63) / 64));
   if (router_q8 && router_q8->codes)
-    hipLaunchKernelGGL(q8_router_logits_kernel, dim3((unsigned)((T + kQ8Tok - 1) / kQ8Tok), (unsigned)((E + 63) / 64)),
-                       dim3(256), 0, stream, *router_q8, X, T, E, H, logits);
+    hipLaunchKernelGGL(q8_router_logits_kernel, grid, dim3(512), (size_t)(H >> 6) * 32 * 4, stream, *router_q8, X, T,
+                       E, H, logits);
   else
     hipLaunchKernelGGL(router_logits_kernel, grid, dim3(512), 0, stream, router, X, T, E, H, logits);
   hipError_t e = hipGetLastError();

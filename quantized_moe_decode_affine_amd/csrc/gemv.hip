@@ -561,6 +561,145 @@ __global__ __launch_bounds__(256) void lmhead_mfma_kernel(GemvParams p) {
   argmax_epilogue<B>(bv, bi, p);
 }
 
+// The same on 8-bit codes (64 bytes per group): pair word m = 4w + j takes bytes j
+// of code words 2w and 2w + 1 (columns 8w + j and 8w + j + 4, the staged pair
+// order), each exact in bfloat16 as the high half of its fp32 value, and a group
+// adds s*P + b*sum_x.
+template <int B>
+__global__ __launch_bounds__(256) void lmhead_mfma_q8_kernel(GemvParams p) {
+  constexpr int NB = (B + 3) / 4;
+  extern __shared__ __align__(16) uint32_t smem[];
+  constexpr int ST = chunk_stride<1>();
+  const int C = p.k >> 5;
+  const int G = p.k >> 6;
+  uint32_t* vp = smem;
+  float* vs = reinterpret_cast<float*>(smem + B * C * ST);
+#pragma unroll
+  for (int b = 0; b < B; ++b) stage_bf16_vector(p.x + (size_t)b * p.k, C, vp + b * C * ST, vs + b * C);
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int q = lane & 3;          // row of the block (A side) and batch column (B and D sides)
+  const int ks = (lane >> 2) & 3;  // group offset of the block
+  const int rq = lane >> 4;        // row quad of the block
+  int jb[NB];                      // this lane's batch row per set (clamped: columns past B are computed, unused)
+#pragma unroll
+  for (int h = 0; h < NB; ++h) jb[h] = min(4 * h + q, B - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  constexpr int kRowsPerWave = 16;
+
+  float best[NB];
+  int32_t besti[NB];
+#pragma unroll
+  for (int h = 0; h < NB; ++h) { best[h] = -INFINITY; besti[h] = 0x7FFFFFFF; }
+
+  constexpr int NC = 4;  // 16-byte code pieces per group
+  struct Frag {
+    uint4 c[NC];
+    uint32_t s, b;
+  };
+  for (int64_t base = wave * kRowsPerWave; base < p.rows; base += nwaves * kRowsPerWave) {
+    const int64_t row = min(base + 4 * rq + q, p.rows - 1);  // rows past the end: loaded, unused
+    const uint4* cr = p.codes + row * (NC * G);
+    const uint16_t* sr = p.scales + row * G;
+    const uint16_t* br = p.biases + row * G;
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int h = 0; h < NB; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int g = min(ks, G - 1);
+    const int g1 = min(4 + ks, G - 1);
+    auto load = [&](int gi) __attribute__((always_inline)) {
+      Frag r;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) r.c[i] = cr[NC * gi + i];
+      r.s = sr[gi];
+      r.b = br[gi];
+      return r;
+    };
+    Frag f = load(g);
+    Frag f1 = load(g1);
+    for (int gg = 0; gg < G; gg += 4) {
+      const bool live = gg + ks < G;  // groups past the end: loaded (clamped), not added
+      const int gn = min(gg + 4 + ks, G - 1);
+      const int g2 = min(gg + 8 + ks, G - 1);
+      const Frag f2 = load(g2);  // two steps ahead
+      uint32_t pr[32];
+      uint32_t W[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        W[4 * i] = f.c[i].x;
+        W[4 * i + 1] = f.c[i].y;
+        W[4 * i + 2] = f.c[i].z;
+        W[4 * i + 3] = f.c[i].w;
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = __float_as_uint((float)((W[2 * w] >> (8 * j)) & 0xFFu)) >> 16;
+          const uint32_t hi = __float_as_uint((float)((W[2 * w + 1] >> (8 * j)) & 0xFFu)) & 0xFFFF0000u;
+          pr[4 * w + j] = lo | hi;
+        }
+      const uint32_t s4[4] = {quad_bcast<0>(f.s), quad_bcast<1>(f.s), quad_bcast<2>(f.s), quad_bcast<3>(f.s)};
+      const uint32_t b4[4] = {quad_bcast<0>(f.b), quad_bcast<1>(f.b), quad_bcast<2>(f.b), quad_bcast<3>(f.b)};
+#pragma unroll
+      for (int h = 0; h < NB; ++h) {
+        // pair word m of group g sits in chunk 2g + m/16 at offset m%16
+        const uint32_t* xv = vp + jb[h] * C * ST + 2 * g * ST;
+        f32x4_t P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int m = 2 * t;
+          const uint2 xa = *reinterpret_cast<const uint2*>(xv + (m >> 4) * ST + (m & 15));
+          P = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(mfma4_bf16_t, make_uint2(pr[m], pr[m + 1])),
+                                                   __builtin_bit_cast(mfma4_bf16_t, xa), P, 0, 0, 0);
+        }
+        const float vsum = vs[jb[h] * C + 2 * g] + vs[jb[h] * C + 2 * g + 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float t = fmaf(bf16_bits_to_f32(s4[i]), P[i], bf16_bits_to_f32(b4[i]) * vsum);
+          acc[h][i] += live ? t : 0.f;
+        }
+      }
+      f = f1;
+      f1 = f2;
+      g = gn;
+    }
+    // the four group offsets of a row quad meet in the ks = 0 lanes; lane 16rq + j
+    // then holds rows base + 4rq + i (i = 0..3) for batch row 4h + j
+#pragma unroll
+    for (int h = 0; h < NB; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[h][i] += __shfl_xor(acc[h][i], 4, kWave);
+        acc[h][i] += __shfl_xor(acc[h][i], 8, kWave);
+      }
+    if (ks == 0) {
+#pragma unroll
+      for (int h = 0; h < NB; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t r = base + 4 * rq + i;
+          if (r < p.rows && better(acc[h][i], (int32_t)r, best[h], besti[h])) {
+            best[h] = acc[h][i];
+            besti[h] = (int32_t)r;
+          }
+        }
+    }
+  }
+  // every lane offers its candidate for the batch rows it holds, -inf for the others
+  float bv[B];
+  int32_t bi[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const bool mine = (b & 3) == q;
+    bv[b] = mine ? best[b >> 2] : -INFINITY;
+    bi[b] = mine ? besti[b >> 2] : 0x7FFFFFFF;
+  }
+  argmax_epilogue<B>(bv, bi, p);
+}
+
 int log2_floor(int64_t v) {
   int r = 0;
   while ((int64_t(1) << (r + 1)) <= v) ++r;
@@ -635,12 +774,17 @@ namespace {
 template <int B>
 constexpr int lmhead_rows_per_lane() { return B <= 2 ? 4 : B <= 4 ? 2 : 1; }
 
-template <int B>
+template <int B, bool kQ8 = false>
 int lmhead_mfma_resident(size_t lds) {
   static int cached = -1;
   if (cached < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_mfma_kernel<B>, 256, lds) != hipSuccess || n < 1)
+    hipError_t e;
+    if constexpr (kQ8)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_mfma_q8_kernel<B>, 256, lds);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_mfma_kernel<B>, 256, lds);
+    if (e != hipSuccess || n < 1)
       n = 1;
     cached = n;
   }
@@ -744,10 +888,21 @@ hipError_t launch_q8(GemvParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// B = 1: the 8-bit GEMV with fused argmax; B = 2..7: the LM-head MFMA kernel on 8-bit codes.
 template <int B>
 hipError_t run_lmhead_q8_b(GemvParams& p, int32_t* ids, float* max_logit, hipStream_t stream) {
   p.ids = ids;
   p.max_logit = max_logit;
+  if constexpr (B >= 2) {
+    const size_t lds = gemv_lds(p.k, B);
+    const int64_t wave_steps = (p.rows + 15) / 16;  // 16 rows per wave step; one resident round
+    int64_t blocks = (wave_steps + 3) / 4;
+    int64_t max_blocks = (int64_t)device_cu_count() * lmhead_mfma_resident<B, true>(lds);
+    if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // bounds the argmax partials
+    if (blocks > max_blocks) blocks = max_blocks;
+    hipLaunchKernelGGL((lmhead_mfma_q8_kernel<B>), dim3((int)blocks), dim3(256), lds, stream, p);
+    return hipGetLastError();
+  }
   return launch_q8<B <= 2 ? 2 : 1, B, true>(p, stream);
 }
 

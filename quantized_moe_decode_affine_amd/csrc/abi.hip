@@ -288,7 +288,7 @@ int lmhead_argmax(const q4moe_matrix* W, const q4moe_bf16* X, int64_t B, int32_t
     if (!matrix_ok(W) || !X || !aligned(X, 16) || !ids || B < 1) return Q4MOE_EINVAL;
     const int64_t rows = W->count * W->n;
     if (B > 8 || rows > kMaxRows32 || B * W->k > kMaxGemvK) return Q4MOE_EUNSUPPORTED;
-    if (is_q8(*W) && (B > 7 || q4moe::q8_gemv_lds_bytes((int)W->k, (int)B) > kMaxDynLds))
+    if (is_q8(*W) && B == 1 && q4moe::q8_gemv_lds_bytes((int)W->k, 1) > kMaxDynLds)  // B >= 2: the MFMA head
       return Q4MOE_EUNSUPPORTED;
     const size_t need = lmhead_ws(rows, W->k, B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;

@@ -888,7 +888,7 @@ hipError_t launch_q8(GemvParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// B = 1: the 8-bit GEMV with fused argmax; B = 2..7: the LM-head MFMA kernel on 8-bit codes.
+// B = 1: the 8-bit GEMV with fused argmax; B = 2..8: the LM-head MFMA kernel on 8-bit codes.
 template <int B>
 hipError_t run_lmhead_q8_b(GemvParams& p, int32_t* ids, float* max_logit, hipStream_t stream) {
   p.ids = ids;
@@ -945,6 +945,7 @@ hipError_t run_lmhead_argmax_q8(const uint32_t* codes, const uint16_t* scales, c
     case 5: return run_lmhead_q8_b<5>(p, ids, max_logit, stream);
     case 6: return run_lmhead_q8_b<6>(p, ids, max_logit, stream);
     case 7: return run_lmhead_q8_b<7>(p, ids, max_logit, stream);
+    case 8: return run_lmhead_q8_b<8>(p, ids, max_logit, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -206,13 +206,12 @@ def test_q8_matrices_rejected_where_unsupported(lib):
     L = _layer()
     L.sh_down = m8(1, 128, 64)
     assert lib.moe_ffn_decode(ctypes.byref(L), A, A2, 0, None, None, A, need_d, None) == B.EUNSUPPORTED
-    # LM head: up to 7 batch rows at 8 bits (LDS holds them as fp32); short workspace before any launch
+    # LM head: up to 8 batch rows at 8 bits; short workspace before any launch
     W = ctypes.byref(m8(1, 1000, 2048))
     need8 = lib.q4moe_workspace_bytes(B.OP_LMHEAD, None, W, 8)
-    need7 = lib.q4moe_workspace_bytes(B.OP_LMHEAD, None, W, 7)
     f = lib.lmhead_argmax
-    assert f(W, A, 8, A2, None, A, need8, None) == B.EUNSUPPORTED
-    assert f(W, A, 7, A2, None, A, need7 - 1, None) == B.EWORKSPACE
+    assert f(W, A, 9, A2, None, A, need8 * 2, None) == B.EUNSUPPORTED
+    assert f(W, A, 8, A2, None, A, need8 - 1, None) == B.EWORKSPACE
     assert f(ctypes.byref(m8(1, 10, 16384)), A, 1, A2, None, A, need8, None) == B.EUNSUPPORTED
 
 

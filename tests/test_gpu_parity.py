@@ -503,7 +503,7 @@ def test_q8_gemv_parity(B, n, k, seed):
     check_bf16_output(yb, y, ref)
 
 
-@pytest.mark.parametrize("batch", [1, 4, 7])
+@pytest.mark.parametrize("batch", [1, 2, 4, 7, 8])
 def test_q8_lmhead_parity(B, batch):
     rows, k = 20000, 1024
     say(f"q8 lmhead rows={rows} k={k} B={batch}")

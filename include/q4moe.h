@@ -139,7 +139,11 @@ int q4_gemm(const q4moe_matrix* W, const q4moe_bf16* X, int64_t m, void* Y, int 
             void* workspace, size_t workspace_bytes, q4moe_stream stream);
 
 /*
- * Router: logits[t][e] = router[e] . X[t] (fp32 accumulation), softmax over
+ * Router of the mixture-of-experts layer (lily README, introduction: the
+ * checkpoint is a 35B-A3B model, about 3B of its 35B parameters active per
+ * token, which is a router picking a few experts per token; the pages give no
+ * rule, and softmax -> top-k -> renormalise is the plain reading):
+ * logits[t][e] = router[e] . X[t] (fp32 accumulation), softmax over
  * all n_experts, the top_k largest kept in descending order (equal logits:
  * lower expert id first), their probabilities renormalised to sum to 1.
  * Writes ids int32 [T][top_k] and weights fp32 [T][top_k].  1 <= top_k <= 32,

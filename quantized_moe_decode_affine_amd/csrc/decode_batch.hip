@@ -39,7 +39,7 @@ constexpr int kDownPrefetch = 4;               // experts per wave whose down ro
 constexpr int kBitWords = kMaxExperts / 32;
 constexpr int kMaxPlan = kMaxBatch * kMaxTopK + 1;  // distinct experts of a step, shared one included
 
-// The step's plan, written by the route launch's last workgroup.
+// The step's plan, written by batch_plan_kernel (one workgroup) after the router launch.
 struct BatchPlan {
   int n;                                // planned experts (distinct routed ones, then the shared one)
   int n_routed;

@@ -22,7 +22,8 @@ hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, cons
                              int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
                              float* part_val, int32_t* part_idx, unsigned* done, hipStream_t stream);
 
-// The same for 8-bit codes (4 per word); B <= 7 for the LM head, LDS per call from q8_gemv_lds_bytes.
+// The same for 8-bit codes (4 per word): B = 1 runs the GEMV form (LDS per call from
+// q8_gemv_lds_bytes), B = 2..8 the matrix-core LM head (LDS per call from gemv_lds_bytes).
 size_t q8_gemv_lds_bytes(int k, int B);
 hipError_t run_q8_gemv(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t rows,
                        int k, const uint16_t* x, void* y, int out_bf16, hipStream_t stream);

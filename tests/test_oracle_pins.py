@@ -282,6 +282,59 @@ def test_given_ids_reproduce_topk_result():
     np.testing.assert_array_equal(w, w2)
 
 
+def test_boundary_gap_hand_values():
+    # ranked logits 2 > 1 > 0 > -1 in scrambled positions: the k-th minus the (k+1)-th
+    row = [0.0, 2.0, -1.0, 1.0]
+    assert orc.boundary_gap(row, 1) == 1.0          # 2 - 1
+    assert orc.boundary_gap(row, 2) == 1.0          # 1 - 0
+    assert orc.boundary_gap(row, 3) == 1.0          # 0 - (-1)
+    assert orc.boundary_gap([5.0, 0.25, 3.0, 3.0, -7.0], 2) == 0.0  # exact tie across the k / k+1 boundary
+    assert orc.boundary_gap([5.0, 0.25, 3.0, 3.5, -7.0], 2) == 0.5  # 3.5 - 3.0, not 5 - 3.5
+    assert orc.boundary_gap([5.0, 0.25, 3.0, 3.5, -7.0], 4) == 7.25  # 0.25 - (-7)
+    assert orc.boundary_gap(row, 4) == math.inf     # k equal to the expert count: no (k+1)-th expert
+    assert orc.boundary_gap([-3.0], 1) == math.inf
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_boundary_gap_brute_force_distinct(seed):
+    # brute force on distinct values: the gap is min(selected) - max(unselected) of the top-k set
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(2, 40))
+    row = rng.permutation(np.arange(E, dtype=np.float64) * 0.37 - 5.0) + rng.normal(0, 1e-3, E)
+    for k in range(1, E):
+        chosen = set()
+        for _ in range(k):  # repeated selection of the largest remaining value, no sorting
+            best = None
+            for e in range(E):
+                if e not in chosen and (best is None or row[e] > row[best]):
+                    best = e
+            chosen.add(best)
+        lo_in = min(row[e] for e in chosen)
+        hi_out = max(row[e] for e in range(E) if e not in chosen)
+        assert orc.boundary_gap(row, k) == lo_in - hi_out
+        assert orc.boundary_gap(row, k) > 0
+
+
+def test_weights_for_ids_off_the_topk_set():
+    # logits (2, 1, 0, -1): the set {3, 1} is not the top-2; its weights are
+    # e^1 / (e^1 + e^-1) and e^-1 / (e^1 + e^-1) in the given order, i.e. sigma(2), sigma(-2)
+    w = orc.weights_for_ids([2.0, 1.0, 0.0, -1.0], [1, 3])
+    np.testing.assert_allclose(w, [1 / (1 + math.exp(-2)), 1 / (1 + math.exp(2))], rtol=1e-15)
+    w = orc.weights_for_ids([2.0, 1.0, 0.0, -1.0], [3, 1])     # order follows the given ids
+    np.testing.assert_allclose(w, [1 / (1 + math.exp(2)), 1 / (1 + math.exp(-2))], rtol=1e-15)
+    w = orc.weights_for_ids([2.0, 1.0, 0.0, -1.0], [2, 3, 0])  # three experts: e^0, e^-1, e^2 over their sum
+    den = 1 + math.exp(-1) + math.exp(2)
+    np.testing.assert_allclose(w, [1 / den, math.exp(-1) / den, math.exp(2) / den], rtol=1e-14)
+    # invariance under a constant shift of all logits, and large logits do not overflow
+    w2 = orc.weights_for_ids([802.0, 801.0, 800.0, 799.0], [2, 3, 0])
+    np.testing.assert_allclose(w2, w, rtol=1e-12)
+    # scipy's softmax of the kept logits gives the same (softmax over all, then renormalise)
+    rng = np.random.default_rng(3)
+    L = rng.normal(0, 1, 64)
+    ids = rng.choice(64, 8, replace=False)
+    np.testing.assert_allclose(orc.weights_for_ids(L, ids), scipy.special.softmax(L[ids]), rtol=1e-13)
+
+
 # ------------------------------------------------------------------ a8 ------
 
 def test_lmhead_planted_maximum_and_ties():

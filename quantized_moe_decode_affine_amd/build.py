@@ -27,6 +27,9 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # keep MFMA accumulators in ordinary VGPRs (the per-group scale fold reads them with VALU ops)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # single-lane atomics stay single atomics (the optimizer's lane aggregation reads the
+    # result back at once, which makes a wave wait for a counter it needs only later)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -236,6 +236,8 @@ int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int o
     if (q4moe::decode_lds_bytes(d) > kMaxDynLds) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_workspace_bytes(d.hidden, d.inter, d.n_experts, d.top_k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
+    // all workgroups must be resident together (they wait on each other's words)
+    if (!q4moe::decode_fits(d)) return Q4MOE_EUNSUPPORTED;
     const int mode = residual ? q4moe::kOutBf16Residual : out_dtype == Q4MOE_OUT_BF16 ? q4moe::kOutBf16 : q4moe::kOutF32;
     return hip_status(q4moe::run_moe_ffn_decode(d, x, y, mode, ids_out, w_out, workspace, (hipStream_t)stream));
   } catch (...) {

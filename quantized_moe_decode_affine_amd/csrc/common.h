@@ -192,6 +192,15 @@ constexpr int kLoadDeviceScope = 16;
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses, not
+// for its outstanding global loads (a __syncthreads would also wait for those, so
+// loads issued ahead of a barrier would have to land before it).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Grid-wide barrier over `nblocks` co-resident workgroups.  State {count, gen}
 // lives in caller memory that is zero when first used; count returns to zero
 // after every barrier.  Every thread first waits for its own outstanding

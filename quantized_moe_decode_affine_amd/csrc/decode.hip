@@ -3,28 +3,31 @@
 // The step is a dependent chain of weight streams (lily-qwen3.8-flash-next
 // README, "How the speed was achieved": decode is bandwidth-bound and its
 // kernels are tuned against the chain of reads).  One grid of one workgroup
-// per CU runs three phases:
-//   A: router logits (bf16 GEMV, one row per wave 0 of a workgroup), each
-//      published with this launch's epoch in one 64-bit word, while waves 1-3
-//      compute the shared expert's gate/up rows with SwiGLU (off the critical
-//      path: their results are needed only in phase C);
-//   B: top-k of the logits (recomputed by every workgroup straight from the
-//      tagged words, so seeing a logit and reading it are one load), then the
-//      routed experts' gate/up rows with SwiGLU; meanwhile each workgroup
-//      prefetches into registers the down-projection weights of the output
-//      rows it owns in phase C (known once the experts are);
-//   C: for each owned output row, the down rows of all selected experts and
-//      the shared expert, split over the workgroup's waves, combined in LDS in
-//      a fixed order (no atomics); y is written once.
+// per CU keeps that chain as short as it can be: three weight streams and two
+// handoffs between workgroups.
+//   A: every workgroup reads its router row(s) (one 4 KB row for 256 experts on
+//      256 CUs) and publishes the logit; meanwhile it issues the loads of the
+//      shared expert's gate/up rows it owns (they depend on nothing) and
+//      computes them with SwiGLU after the logit is out.
+//   B: every workgroup takes the top-k itself from the published logits, then
+//      issues at once every routed weight it will need in this launch: its
+//      gate/up rows AND the down rows of the output rows it owns (the down
+//      rows depend only on the expert ids, not on the activations), so the
+//      down stream is in flight while gate/up is computed and handed over.
+//   C: the SwiGLU activations of every slot are staged into LDS and the
+//      already-loaded down rows are reduced; each output row is combined in a
+//      fixed slot order (no atomics), y written once.
 //
 // No grid-wide barrier: every value handed from one workgroup to another (the
-// router logits, the SwiGLU activations) is published as one 64-bit word
-// {epoch, fp32 bits} of this launch, so a consumer's load both reads the value
-// and tells whether it is there yet; only late words are polled again.  The
-// activations are produced 8 rows at a time, and the 8 words of a 64-byte line
-// are written by one store instruction of one wave.  The epoch is agreed through
-// per-group arrival counters in the workspace.  Every poll is bounded: a lost
-// flag yields a wrong result and a recorded timeout, never a hang.
+// router logits, the SwiGLU activations) is one 64-bit word {epoch, fp32 bits}
+// written by one store of this launch, so a consumer's load both reads the value
+// and tells whether it is there yet; only late words are polled again.  Because
+// the value travels inside the flag word, no ordering between two memory
+// locations is needed: the handoff relies only on the single-copy atomicity of
+// an aligned 64-bit store and on device-coherent (L2-bypassing) loads.  The 8
+// words of an activation line are written by one store instruction.  The epoch
+// is agreed through per-group arrival counters in the workspace.  Every poll is
+// bounded: a lost flag yields a wrong result and a recorded timeout, never a hang.
 #include "kernels.h"
 #include "topk.h"
 #include "vecstage.h"
@@ -33,22 +36,48 @@ namespace q4moe {
 
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef Q4MOE_DECODE_THREADS
+#define Q4MOE_DECODE_THREADS 512
+#endif
+constexpr int kThreads = Q4MOE_DECODE_THREADS;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kEpochGroups = 8;
-constexpr int kPrefetchSlots = 3;   // down-row prefetch: slots per wave held in registers
 constexpr unsigned kPollLimit = 1u << 18;  // ~0.25 s of polling
 
 constexpr int kMaxBlocks = 1024;
+constexpr int kOutRows = 8;       // output rows of one down block
+constexpr int kUnitRows = 8;      // gate/up row pairs of one unit: one 64-byte line of activations
+constexpr int kGuSlots = 1024 / kThreads;  // routed gate/up row pairs per lane loaded at top-k time (16 pairs per CU)
+constexpr int kShSlots = 512 / kThreads;   // shared gate/up row pairs per lane loaded at launch (8 pairs per CU)
+constexpr int kDnSlots = 1536 / kThreads;  // down rows per lane loaded at top-k time (96 rows of 16 lanes per CU)
+constexpr int kRtRows = 2;        // router rows per workgroup whose loads go out at launch
+constexpr int kActBatch = 256;    // activations gathered in LDS before they are published
+#ifndef Q4MOE_DOWN_LATE
+#define Q4MOE_DOWN_LATE 0
+#endif
+constexpr bool kDownLate = Q4MOE_DOWN_LATE;  // down rows loaded after gate/up (else with it)
+
+#ifndef Q4MOE_HANDOFF_COPIES
+#define Q4MOE_HANDOFF_COPIES 8
+#endif
+#ifndef Q4MOE_LOGIT_STRIDE
+#define Q4MOE_LOGIT_STRIDE 1
+#endif
+constexpr int kLogitStride = Q4MOE_LOGIT_STRIDE;  // 64-bit words per logit slot
+// Every value handed between workgroups is written to kCopies copies, and workgroup b
+// reads copy b % kCopies: the copies sit on different memory channels, so the reads of
+// all workgroups do not queue at the few channels that would hold a single copy.
+constexpr int kCopies = Q4MOE_HANDOFF_COPIES;
+constexpr int kLogitCopyWords = kMaxExperts * kLogitStride + 64;  // words between logit copies (skewed)
 
 struct DecodeWs {
   unsigned long long group_ctr[kEpochGroups][32];  // {epoch:hi32, arrivals:lo32}, one 256-byte slot each
   unsigned timeouts;
   unsigned pad[63];
-  // Router logit of expert e: tag_logit[e] = {epoch:hi32, fp32 bits:lo32}.  The
-  // 8 words of a 64-byte line are written by one store instruction of one wave
-  // (lines shared by several writers slow their observers down severalfold).
-  unsigned long long tag_logit[kMaxExperts];
+  // Router logit of expert e: tag_logit[e * kLogitStride] = {epoch:hi32, fp32 bits:lo32}.
+  // Each logit has a 64-byte line of its own: a line written by several workgroups
+  // is observed several times more slowly than one written by a single store.
+  unsigned long long tag_logit[kCopies * kLogitCopyWords];
 };
 
 struct DecodeParams {
@@ -58,22 +87,31 @@ struct DecodeParams {
   int32_t* ids_out;           // nullable [k]
   float* w_out;               // nullable [k]
   DecodeWs* ws;
-  unsigned long long* act;    // [k+1][I] tagged SwiGLU outputs: routed slots 0..k-1, shared slot k
-  int lsH;                    // log2 lanes per row for rows of length hidden
-  int lsI;                    // log2 lanes per row for rows of length inter
+  unsigned long long* act;    // kCopies x [k+1][I] tagged SwiGLU outputs: routed slots 0..k-1, shared slot k
+  int64_t act_copy_words;     // words between the copies of act
   DecodeLayer L;              // last: the per-call fields above keep fixed small offsets
 };
 
-// Stage a bf16 vector of n values (n % 32 == 0) into LDS: threads [t0, t0 + nthr)
-// take one 8-value block each per pass, chunk sums by a quad reduction (nthr and
-// t0 multiples of 4, so the 4 blocks of a chunk sit in one lane quad).
-__device__ __forceinline__ void stage_bf16_parallel(const uint16_t* __restrict__ x, int n, uint32_t* vp, float* vs,
-                                                    int t0, int nthr) {
+int lanes_log2(int n) {
+  int r = 0;
+  while (r < 6 && (2 << r) <= n) ++r;
+  return r;
+}
+
+__device__ __forceinline__ int dev_lanes_log2(int n) {
+  int r = 0;
+  while (r < 6 && (2 << r) <= n) ++r;
+  return r;
+}
+
+// Stage a bf16 vector of n values (n % 32 == 0) into LDS as permuted pairs with
+// chunk sums: each thread takes one 8-value block per pass, chunk sums by a quad
+// reduction (the 4 blocks of a chunk sit in one lane quad).
+__device__ __forceinline__ void stage_bf16_parallel(const uint16_t* __restrict__ x, int n, uint32_t* vp, float* vs) {
   constexpr int ST = chunk_stride<1>();
-  const int t = threadIdx.x - t0;
-  if (t < 0 || t >= nthr) return;
+  const int t = threadIdx.x;
   const int nblk = n >> 3;
-  for (int base = 0; base < nblk; base += nthr) {
+  for (int base = 0; base < nblk; base += kThreads) {
     const int b = base + t;
     float sum = 0.f;
     if (b < nblk) {
@@ -89,22 +127,18 @@ __device__ __forceinline__ void stage_bf16_parallel(const uint16_t* __restrict__
   }
 }
 
-// Convert 8 fp32 values into the hi/lo permuted pair layout of one 8-value block.
-__device__ __forceinline__ float store_split_block(const float (&v)[8], uint32_t* dst) {
-  uint32_t hi[8], lo[8];
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    hi[j] = f32_to_bf16_bits(v[j]);
-    const float h = bf16_bits_to_f32(hi[j]);
-    lo[j] = f32_to_bf16_bits(v[j] - h);
-    sum += h + bf16_bits_to_f32(lo[j]);
-  }
-  *reinterpret_cast<uint4*>(dst) =
-      make_uint4(hi[0] | hi[4] << 16, hi[1] | hi[5] << 16, hi[2] | hi[6] << 16, hi[3] | hi[7] << 16);
-  *reinterpret_cast<uint4*>(dst + 16) =
-      make_uint4(lo[0] | lo[4] << 16, lo[1] | lo[5] << 16, lo[2] | lo[6] << 16, lo[3] | lo[7] << 16);
-  return sum;
+// Stage block b (8 values held in v) of a bf16 vector of nblk blocks into LDS: every
+// thread of the workgroup calls this with its own block (b >= nblk: nothing stored);
+// chunk sums by a quad reduction (the 4 blocks of a chunk sit in one lane quad).
+__device__ __forceinline__ void stage_bf16_block(uint4 v, int b, int nblk, uint32_t* vp, float* vs) {
+  constexpr int ST = chunk_stride<1>();
+  float sum = (bf16_bits_to_f32(v.x & 0xFFFFu) + bf16_bits_to_f32(v.x >> 16)) +
+              (bf16_bits_to_f32(v.y & 0xFFFFu) + bf16_bits_to_f32(v.y >> 16)) +
+              (bf16_bits_to_f32(v.z & 0xFFFFu) + bf16_bits_to_f32(v.z >> 16)) +
+              (bf16_bits_to_f32(v.w & 0xFFFFu) + bf16_bits_to_f32(v.w >> 16));
+  if (b < nblk) *reinterpret_cast<uint4*>(vp + (b >> 2) * ST + (b & 3) * 4) = permute_block(v);
+  sum = group_sum_rt(sum, 2);
+  if (b < nblk && (b & 3) == 0) vs[b >> 2] = sum;
 }
 
 // Padded row length (floats) of a 64-column group in the fp32 LDS copies that an
@@ -120,7 +154,7 @@ constexpr int kQ8Pad = 68;
 // lanes 0-1 of the quad assemble its permuted pair words from their own values
 // and the matching ones of lanes 2-3; 16 lanes hold one 32-value chunk.  With f32_dst, the
 // values from flat index f32_first on are also written as fp32 in kQ8Pad-padded groups.
-constexpr int kTagRounds = 9;  // 16-byte loads per thread: 9 x 256 x 2 words = 4608 = 9 slots x 512
+constexpr int kTagRounds = (4608 + 2 * kThreads - 1) / (2 * kThreads);  // 16-byte loads per thread: 9 slots x 512 words in one pass
 
 __device__ __forceinline__ void stage_tagged_split(const unsigned long long* src, int nvec, int n, uint32_t* vp,
                                                    float* vs, uint32_t epoch, unsigned* timeouts,
@@ -139,17 +173,21 @@ __device__ __forceinline__ void stage_tagged_split(const unsigned long long* src
     auto complete = [&](int r) __attribute__((always_inline)) { return w[r].y == epoch && w[r].w == epoch; };
 #pragma unroll
     for (int r = 0; r < kTagRounds; ++r) fetch(r);
+    // every pair still incomplete is fetched again, all of them in flight together, so a
+    // poll costs one round trip however many words are late
+    for (unsigned spins = 0;; ++spins) {
+      bool done = true;
 #pragma unroll
-    for (int r = 0; r < kTagRounds; ++r) {
-      if (base + r * nthr + t >= npairs) continue;
-      for (unsigned spins = 0; !complete(r); ++spins) {
-        if (spins == kPollLimit) {
-          __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        fetch(r);
+      for (int r = 0; r < kTagRounds; ++r) done &= base + r * nthr + t >= npairs || complete(r);
+      if (__all(done)) break;
+      if (spins == kPollLimit) {
+        if (lane_id() == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
       }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int r = 0; r < kTagRounds; ++r)
+        if (!(base + r * nthr + t >= npairs || complete(r))) fetch(r);
     }
 #pragma unroll
     for (int r = 0; r < kTagRounds; ++r) {
@@ -178,87 +216,142 @@ __device__ __forceinline__ void stage_tagged_split(const unsigned long long* src
   }
 }
 
-// Gate/up row pointers of row i of expert e (e indexes the stacked matrices).
-struct GateUpRef {
+// ------------------------------------------------------------ row tasks
+//
+// A row of C chunks (32 codes, one 16-byte word each) is taken by LR = 2^lr
+// consecutive lanes (lr = lanes_log2(C), at most 64): lane `sub` of the group
+// takes chunks sub, sub + LR, ...  A wave covers RPW = 64 / LR rows per pass and
+// the workgroup kWaves * RPW rows.  When C is a power of two no larger than 64 a
+// lane holds exactly one chunk of every row it takes (the form whose loads can be
+// issued ahead into registers).
+struct RowGeom {
+  int lr, LR, RPW, sub, lg, C;
+  bool one;  // one chunk per lane per row
+};
+
+__device__ __forceinline__ RowGeom row_geom(int C) {
+  RowGeom g;
+  g.C = C;
+  g.lr = dev_lanes_log2(C);
+  g.LR = 1 << g.lr;
+  g.RPW = kWave >> g.lr;
+  const int lane = lane_id();
+  g.sub = lane & (g.LR - 1);
+  g.lg = lane >> g.lr;
+  g.one = g.LR == C;
+  return g;
+}
+
+// One gate/up row pair (intermediate row i) of routed expert e, or of the shared expert.
+struct PairRef {
   const uint4* gc;
   const uint4* uc;
   const uint16_t *gs, *gb, *us, *ub;
 };
 
-__device__ __forceinline__ GateUpRef gate_up_ref(const Q4Mat& gm, const Q4Mat& um, int64_t e, int i, int H, int I) {
+__device__ __forceinline__ PairRef make_pair_ref(const uint32_t* gcodes, const uint16_t* gscales,
+                                                 const uint16_t* gbiases, const uint32_t* ucodes,
+                                                 const uint16_t* uscales, const uint16_t* ubiases, int64_t row,
+                                                 int H) {
   const int C = H >> 5, G = H >> 6;
-  const int64_t oc = e * (int64_t)I * (H >> 3), og = e * (int64_t)I * G;
-  GateUpRef r;
-  r.gc = reinterpret_cast<const uint4*>(gm.codes + oc) + (int64_t)i * C;
-  r.uc = reinterpret_cast<const uint4*>(um.codes + oc) + (int64_t)i * C;
-  r.gs = gm.scales + og + (int64_t)i * G;
-  r.gb = gm.biases + og + (int64_t)i * G;
-  r.us = um.scales + og + (int64_t)i * G;
-  r.ub = um.biases + og + (int64_t)i * G;
+  PairRef r;
+  r.gc = reinterpret_cast<const uint4*>(gcodes) + row * C;
+  r.uc = reinterpret_cast<const uint4*>(ucodes) + row * C;
+  r.gs = gscales + row * G;
+  r.gb = gbiases + row * G;
+  r.us = uscales + row * G;
+  r.ub = ubiases + row * G;
   return r;
 }
 
-// Gate/up of rows i0..i0+7 of one expert (e >= 0: routed expert e; e < 0: the
-// shared expert) over groups [g_lo, g_hi) against the staged x: lane l takes
-// row i0 + l/8 and groups g_lo + l%8 + 8t, with IT groups' loads in flight per
-// lane; every lane of a row's 8-lane group returns that row's partial (g, u).
-// Rows past I are read clamped and their results are not used.
-constexpr int kUnitRows = 8;
-
-template <int IT>
-__device__ __forceinline__ float2 unit_gate_up(const DecodeLayer& L, int e, int i0, int g_lo, int g_hi,
-                                               const uint32_t* vp, const float* vs) {
-  constexpr int ST = chunk_stride<1>();
-  const int H = L.hidden, I = L.inter;
-  const int lane = lane_id();
-  const int row = min(i0 + (lane >> 3), I - 1), gl = lane & 7;
-  const GateUpRef ref =
-      e >= 0 ? gate_up_ref(L.gate, L.up, e, row, H, I) : gate_up_ref(L.sh_gate, L.sh_up, 0, row, H, I);
-  float ag = 0.f, au = 0.f;
-  for (int base = g_lo; base < g_hi; base += 8 * IT) {  // wave-uniform trip count
-    uint4 gc[IT][2], uc[IT][2];
-    uint32_t gs[IT], gb[IT], us[IT], ub[IT];
-#pragma unroll
-    for (int t = 0; t < IT; ++t) {
-      const int g = min(base + gl + 8 * t, g_hi - 1);  // groups past the range: loaded, not used
-      gc[t][0] = ref.gc[2 * g];
-      gc[t][1] = ref.gc[2 * g + 1];
-      uc[t][0] = ref.uc[2 * g];
-      uc[t][1] = ref.uc[2 * g + 1];
-      gs[t] = ref.gs[g];
-      gb[t] = ref.gb[g];
-      us[t] = ref.us[g];
-      ub[t] = ref.ub[g];
-    }
-#pragma unroll
-    for (int t = 0; t < IT; ++t) {
-      const int g = base + gl + 8 * t;
-      const int gc_ = min(g, g_hi - 1);
-      const uint32_t* v = vp + 2 * gc_ * ST;
-      const float vsum = vs[2 * gc_] + vs[2 * gc_ + 1];
-      const float tg = affine_term(chunk_pdot<1>(gc[t][0], v) + chunk_pdot<1>(gc[t][1], v + ST), vsum, gs[t], gb[t]);
-      const float tu = affine_term(chunk_pdot<1>(uc[t][0], v) + chunk_pdot<1>(uc[t][1], v + ST), vsum, us[t], ub[t]);
-      if (g < g_hi) {
-        ag += tg;
-        au += tu;
-      }
-    }
-  }
-  return make_float2(group_sum_rt(ag, 3), group_sum_rt(au, 3));
+__device__ __forceinline__ PairRef routed_pair_ref(const DecodeLayer& L, int e, int i) {
+  return make_pair_ref(L.gate.codes, L.gate.scales, L.gate.biases, L.up.codes, L.up.scales, L.up.biases,
+                       (int64_t)e * L.inter + i, L.hidden);
 }
 
+__device__ __forceinline__ PairRef shared_pair_ref(const DecodeLayer& L, int i) {
+  return make_pair_ref(L.sh_gate.codes, L.sh_gate.scales, L.sh_gate.biases, L.sh_up.codes, L.sh_up.scales,
+                       L.sh_up.biases, i, L.hidden);
+}
+
+// The codes, scales and biases of one chunk of a gate/up row pair, loaded ahead.
+struct PairRegs {
+  uint4 g, u;
+  uint32_t gs, gb, us, ub;
+};
+
+__device__ __forceinline__ void load_pair(const PairRef& r, int c, PairRegs& d) {
+  d.g = r.gc[c];
+  d.u = r.uc[c];
+  d.gs = r.gs[c >> 1];
+  d.gb = r.gb[c >> 1];
+  d.us = r.us[c >> 1];
+  d.ub = r.ub[c >> 1];
+}
+
+// The 16 pair words of a staged bf16 chunk, read once from LDS.
+struct XChunk {
+  uint32_t v[16];
+  float sum;
+};
+
+__device__ __forceinline__ void read_xchunk(const uint32_t* xp, const float* xs, int c, XChunk& x) {
+  const uint32_t* src = xp + c * chunk_stride<1>();
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint4 t = *reinterpret_cast<const uint4*>(src + 4 * b);
+    x.v[4 * b] = t.x;
+    x.v[4 * b + 1] = t.y;
+    x.v[4 * b + 2] = t.z;
+    x.v[4 * b + 3] = t.w;
+  }
+  x.sum = xs[c];
+}
+
+__device__ __forceinline__ float chunk_pdot_regs(uint4 codes, const uint32_t (&v)[16]) {
+  float p0 = word_dot(codes.x, v + 0, 0.f);
+  float p1 = word_dot(codes.y, v + 4, 0.f);
+  p0 = word_dot(codes.z, v + 8, p0);
+  p1 = word_dot(codes.w, v + 12, p1);
+  return p0 + p1;
+}
+
+// (gate, up) partial of one chunk.
+__device__ __forceinline__ float2 pair_terms(const PairRegs& d, const XChunk& x) {
+  return make_float2(affine_term(chunk_pdot_regs(d.g, x.v), x.sum, d.gs, d.gb),
+                     affine_term(chunk_pdot_regs(d.u, x.v), x.sum, d.us, d.ub));
+}
+
+// Full (gate, up) dots of a row pair by the lane group, loads issued on the spot
+// (chunks sub, sub + LR, ...); every lane of the group returns the totals.
+__device__ __forceinline__ float2 pair_dot_now(const PairRef& r, const RowGeom& g, const uint32_t* xp,
+                                               const float* xs, bool live) {
+  float ag = 0.f, au = 0.f;
+  for (int c = g.sub; c < g.C; c += g.LR) {  // lanes past C idle
+    if (live) {
+      PairRegs d;
+      load_pair(r, c, d);
+      XChunk x;
+      read_xchunk(xp, xs, c, x);
+      const float2 t = pair_terms(d, x);
+      ag += t.x;
+      au += t.y;
+    }
+  }
+  return make_float2(group_sum_rt(ag, g.lr), group_sum_rt(au, g.lr));
+}
+
+// ------------------------------------------------------------ 8-bit shared expert
 // An 8-bit shared expert (affine Q8, code j of a row in byte j % 4 of word j / 4)
 // is read against fp32 copies of its input in LDS, one 64-column group per row of
 // kQ8Pad floats: the 64 values, then (for x) their sum.  Its gate/up units are 8 rows
-// of 8 lanes, as for 4-bit codes.
-constexpr int kQ8UnitRows = 8, kQ8LaneLog = 3;
+// of 8 lanes (one group per lane at a time).
+constexpr int kQ8LaneLog = 3;
 
-// Stage a vector of n values (n a multiple of 64; value i from get(i)) into padded
-// groups with their sums, one group per wave at a time.
 template <class Get>
 __device__ __forceinline__ void stage_q8_groups(float* dst, int n, Get get) {
   const int lane = lane_id();
-  for (int g = threadIdx.x / kWave; g < (n >> 6); g += kThreads / kWave) {
+  for (int g = threadIdx.x / kWave; g < (n >> 6); g += kWaves) {
     const float v = get(g * 64 + lane);
     dst[g * kQ8Pad + lane] = v;
     const float t = group_sum_rt(v, 6);
@@ -266,8 +359,6 @@ __device__ __forceinline__ void stage_q8_groups(float* dst, int n, Get get) {
   }
 }
 
-// scale * sum(q v) + bias * sum(v) over one 64-column group of an 8-bit row, for
-// two rows (a: codes ca, b: codes cb) against the same 64 values v.
 __device__ __forceinline__ float2 q8_group_terms2(const uint4* ca, const uint4* cb, const float* v, uint32_t sa,
                                                   uint32_t ba, uint32_t sb, uint32_t bb) {
   uint4 wa[4], wb[4];
@@ -296,8 +387,11 @@ __device__ __forceinline__ float2 q8_group_terms2(const uint4* ca, const uint4* 
                      fmaf(bf16_bits_to_f32(sb), pb, bf16_bits_to_f32(bb) * sv));
 }
 
-// The same for one row whose 64 codes are already in registers.
-__device__ __forceinline__ float q8_group_term_regs(const uint4 (&w4)[4], const float* v, uint32_t s, uint32_t b) {
+// scale * sum(q v) + bias * sum(v) over one 64-column group of an 8-bit row read from memory.
+__device__ __forceinline__ float q8_group_term(const uint4* c, const float* v, uint32_t s, uint32_t b) {
+  uint4 w4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w4[q] = c[q];
   float p = 0.f, sv = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -316,18 +410,10 @@ __device__ __forceinline__ float q8_group_term_regs(const uint4 (&w4)[4], const 
   return fmaf(bf16_bits_to_f32(s), p, bf16_bits_to_f32(b) * sv);
 }
 
-// The same for one row read from memory.
-__device__ __forceinline__ float q8_group_term(const uint4* c, const float* v, uint32_t s, uint32_t b) {
-  uint4 w4[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) w4[q] = c[q];
-  return q8_group_term_regs(w4, v, s, b);
-}
-
-// Gate/up of rows i0..i0+3 of an 8-bit shared expert over groups [g_lo, g_hi): lane l
-// takes row i0 + l/16 and groups g_lo + l%16 + 16t, two groups' loads in flight; every
-// lane of a row's 16-lane group returns that row's (g, u).  xf is the input in padded groups.
-__device__ __forceinline__ float2 unit_gate_up_q8(const DecodeLayer& L, int i0, int g_lo, int g_hi, const float* xf) {
+// Gate/up of rows i0..i0+7 of an 8-bit shared expert over all groups: lane l takes
+// row i0 + l/8 and groups l%8, l%8 + 8, ...; every lane of a row's 8-lane group
+// returns that row's (g, u).  xf is the input in padded groups.
+__device__ __forceinline__ float2 unit_gate_up_q8(const DecodeLayer& L, int i0, const float* xf) {
   constexpr int LPR = 1 << kQ8LaneLog;
   const int H = L.hidden, I = L.inter, G = H >> 6;
   const int lane = lane_id();
@@ -339,10 +425,9 @@ __device__ __forceinline__ float2 unit_gate_up_q8(const DecodeLayer& L, int i0, 
   const uint16_t* us = L.sh_up.scales + (int64_t)row * G;
   const uint16_t* ub = L.sh_up.biases + (int64_t)row * G;
   float ag = 0.f, au = 0.f;
-  for (int base = g_lo; base < g_hi; base += 2 * LPR) {  // wave-uniform trip count
-    // groups past the range are read clamped (in bounds) and their terms dropped
-    const bool ok0 = base + gl < g_hi, ok1 = base + gl + LPR < g_hi;
-    const int g0 = min(base + gl, g_hi - 1), g1 = min(base + gl + LPR, g_hi - 1);
+  for (int base = 0; base < G; base += 2 * LPR) {  // wave-uniform trip count
+    const bool ok0 = base + gl < G, ok1 = base + gl + LPR < G;
+    const int g0 = min(base + gl, G - 1), g1 = min(base + gl + LPR, G - 1);
     const float2 t0 = q8_group_terms2(gc + 4 * g0, uc + 4 * g0, xf + g0 * kQ8Pad, gs[g0], gb[g0], us[g0], ub[g0]);
     const float2 t1 = q8_group_terms2(gc + 4 * g1, uc + 4 * g1, xf + g1 * kQ8Pad, gs[g1], gb[g1], us[g1], ub[g1]);
     if (ok0) {
@@ -357,26 +442,22 @@ __device__ __forceinline__ float2 unit_gate_up_q8(const DecodeLayer& L, int i0, 
   return make_float2(group_sum_rt(ag, kQ8LaneLog), group_sum_rt(au, kQ8LaneLog));
 }
 
-// Gate/up of a shared-expert unit in the shared expert's format.
-template <bool kQ8Shared, int IT>
-__device__ __forceinline__ float2 shared_unit_gate_up(const DecodeLayer& L, int i0, int g_lo, int g_hi,
-                                                      const uint32_t* vp, const float* vs, const float* xf) {
-  if constexpr (kQ8Shared)
-    return unit_gate_up_q8(L, i0, g_lo, g_hi, xf);
-  else
-    return unit_gate_up<IT>(L, -1, i0, g_lo, g_hi, vp, vs);
+// Down row n of an 8-bit shared expert against its fp32 activations af (padded groups):
+// lanes sub, sub + LR, ... of the row's group take groups; returns the row total.
+__device__ __forceinline__ float q8_down_row(const DecodeLayer& L, int n, const float* af, int sub, int LR, int lr,
+                                             bool live) {
+  const int I = L.inter, GI = I >> 6;
+  float part = 0.f;
+  if (live) {
+    const uint4* cr = reinterpret_cast<const uint4*>(L.sh_down.codes) + (int64_t)n * (I >> 4);
+    const uint16_t* sr = L.sh_down.scales + (int64_t)n * GI;
+    const uint16_t* br = L.sh_down.biases + (int64_t)n * GI;
+    for (int g = sub; g < GI; g += LR) part += q8_group_term(cr + 4 * g, af + g * kQ8Pad, sr[g], br[g]);
+  }
+  return group_sum_rt(part, lr);
 }
 
-// Publish the SwiGLU outputs of a unit's rows as tagged words: the 8 lanes that
-// hold rows i0..i0+7 (lane % 8 == 0) write one 64-byte line together.
-template <int LOG = 3>
-__device__ __forceinline__ void publish_unit(unsigned long long* act_slot, int i0, int I, float a, uint32_t epoch) {
-  const int lane = lane_id();
-  const int i = i0 + (lane >> LOG);
-  if ((lane & ((1 << LOG) - 1)) == 0 && i < I)
-    __hip_atomic_store(act_slot + i, ((unsigned long long)epoch << 32) | __float_as_uint(a), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
+// ------------------------------------------------------------ handoffs
 
 // Top-k of E logits by one wave, polling the epoch-tagged words that other
 // workgroups publish until every one carries `epoch` (bounded; a timeout is
@@ -390,28 +471,25 @@ template <int V>
 __device__ __forceinline__ void wave_topk_tagged(const unsigned long long* tags, int E, int k, uint32_t epoch,
                                                  unsigned* timeouts, int32_t* s_ids, float* s_w, int32_t* ids_out,
                                                  float* w_out) {
-  static_assert(V % 2 == 0, "two tagged words per 16-byte load");
   const int lane = lane_id();
   uint32_t key[V];
   int id[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) id[j] = lane * V + j;
-  // lane-contiguous 16-byte device-coherent loads; words past E read as zeros (bounds check)
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned long long*>(tags), 0, E * 8, kBufferRsrcWord3);
+  // device-coherent 8-byte loads, one per logit slot; slots past E read as zeros (bounds check)
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned long long*>(tags), 0, E * kLogitStride * 8, kBufferRsrcWord3);
   for (unsigned spins = 0;; ++spins) {
     bool ready = true;
-    uint4 t[V / 2];
+    uint2 t[V];
 #pragma unroll
-    for (int h = 0; h < V / 2; ++h)  // all loads in flight together
-      t[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (lane * V + 2 * h) * 8, 0,
-                                                                          kLoadDeviceScope));
+    for (int j = 0; j < V; ++j)  // all loads in flight together
+      t[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, id[j] * kLogitStride * 8, 0,
+                                                                         kLoadDeviceScope));
 #pragma unroll
-    for (int h = 0; h < V / 2; ++h) {
-      key[2 * h] = t[h].x;
-      key[2 * h + 1] = t[h].z;
-      ready &= id[2 * h] >= E || t[h].y == epoch;
-      ready &= id[2 * h + 1] >= E || t[h].w == epoch;
+    for (int j = 0; j < V; ++j) {
+      key[j] = t[j].x;
+      ready &= id[j] >= E || t[j].y == epoch;
     }
     if (__all(ready)) break;
     if (spins == kPollLimit) {
@@ -429,357 +507,467 @@ __device__ __forceinline__ void wave_topk_tagged(const unsigned long long* tags,
   }
 }
 
-// The shared-expert unit of workgroup b when each workgroup takes at most one
-// (units + router workgroups <= grid): the workgroups after the router ones, so
-// no workgroup computes both; -1 for none.
-__device__ __forceinline__ int shared_unit_of(int b, int grid, int rgroups, int units) {
-  const int su = b - rgroups;
-  return units + rgroups <= grid && su >= 0 && su < units ? su : -1;
+__device__ __forceinline__ unsigned long long tag_word(uint32_t epoch, float v) {
+  return ((unsigned long long)epoch << 32) | __float_as_uint(v);
 }
 
-struct DownPrefetch {
-  uint4 c0, c1;
-  uint32_t s, b;
-};
+// Publish the activations gathered in LDS (s_act[m * 8 + r] = row r of unit m) as
+// tagged words, one 64-byte line per unit written by 8 lanes of one wave (the
+// waves take units in turn).  unit_slot(m) returns {slot, first row} of unit m.
+template <class UnitOf>
+__device__ __forceinline__ void publish_units(unsigned long long* act, int64_t copy_words, int I, const float* s_act,
+                                              int nunits, uint32_t epoch, UnitOf unit_of) {
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  for (int m = wv * 8 + (lane >> 3); m < nunits; m += kWaves * 8) {  // 8 units per wave instruction
+    const int2 su = unit_of(m);
+    const unsigned long long w = tag_word(epoch, s_act[m * 8 + (lane & 7)]);
+    unsigned long long* dst = act + (size_t)su.x * I + su.y + (lane & 7);
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c)
+      __hip_atomic_store(dst + c * copy_words, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
-// The layer's body, specialised on the router's format (bf16, or 8-bit affine codes) and on
-// a shared-expert gate (the shared expert weighted by sigmoid(sh_gate_w . x)) and on
-// the shared expert's code width (4 or 8 bits).
-template <bool kQ8Router, bool kShGate, bool kQ8Shared>
-__device__ __forceinline__ void decode_layer(DecodeParams p) {
+// The layer's body, specialised on the router's format (bf16, or 8-bit affine codes), on
+// a shared-expert gate (the shared expert weighted by sigmoid(sh_gate_w . x)), on the
+// shared expert's code width (4 or 8 bits) and on kFast: hidden 2048 and intermediate
+// 512 (the 35B-A3B layer's shape), compiled as constants, with every weight load issued
+// ahead into registers (unconditionally, dead tasks reading a clamped valid address, so
+// no load sits behind a branch and nothing waits for a load before its use).  Other
+// shapes load each weight where it is used.
+constexpr int kFastHidden = 2048, kFastInter = 512;
+template <bool kQ8Router, bool kShGate, bool kQ8Shared, bool kFast>
+__device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ int32_t s_ids[kMaxTopK + 1];
   __shared__ float s_w[kMaxTopK + 1];
-  __shared__ float s_red[kWaves][kWave];
-  __shared__ float2 s_pair[kWaves / 2][kUnitRows];
-  __shared__ float2 s_third[kWaves - 1][kUnitRows];
-  __shared__ float s_rlog[2 * kWaves];
+  __shared__ float s_rpart[kRtRows][kWaves];
+  __shared__ float s_act[kActBatch];
+  __shared__ float s_sh[kActBatch];
+  __shared__ float s_red[(kMaxTopK + 1) * kOutRows];
   __shared__ uint32_t s_epoch;
 
-  const int H = p.L.hidden, I = p.L.inter, E = p.L.n_experts, k = p.L.top_k;
+  const DecodeLayer& L = p.L;
+  // the fast form is compiled for one shape, so every row geometry below is a constant
+  const int H = kFast ? kFastHidden : L.hidden, I = kFast ? kFastInter : L.inter;
+  const int E = L.n_experts, k = L.top_k;
   const int CH = H >> 5, CI = I >> 5;
-  const int nslot = k + (p.L.has_shared ? 1 : 0);
+  const bool has_shared = L.has_shared != 0;
+  const int nslot = k + (has_shared ? 1 : 0);
+  const int NB = gridDim.x, b = blockIdx.x;
   uint32_t* xp = smem;                                                                // [CH][ST1]
   float* xs = reinterpret_cast<float*>(xp + CH * chunk_stride<1>());                   // [CH]
   uint32_t* ap = reinterpret_cast<uint32_t*>(xs + CH);                                // [nslot][CI][ST2]
   float* as = reinterpret_cast<float*>(ap + (size_t)nslot * CI * chunk_stride<2>());  // [nslot][CI]
   const size_t xf_off = (reinterpret_cast<const uint32_t*>(as + (size_t)nslot * CI) - smem + 3) & ~size_t(3);
-  float* xf = reinterpret_cast<float*>(smem + xf_off);
-  // (xf: 8-bit shared expert only, x as fp32 [H/64][kQ8Pad], 16-byte aligned)
-  float* af = xf + (size_t)(H >> 6) * kQ8Pad;         // 8-bit shared expert: its activations [I/64][kQ8Pad]
+  float* xf = reinterpret_cast<float*>(smem + xf_off);  // 8-bit shared expert: x as fp32 [H/64][kQ8Pad]
+  float* af = xf + (size_t)(H >> 6) * kQ8Pad;           // 8-bit shared expert: its activations [I/64][kQ8Pad]
   unsigned* timeouts = &p.ws->timeouts;
 
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
+  const int t = threadIdx.x;
 
-  // ---- epoch of this launch: the arrivals of one group agree on its counter's
-  // epoch field.  Taken by thread 0 once its first router loads are in flight,
-  // so the two latencies overlap.
-  auto acquire_epoch = [&]() {
-    const int g = blockIdx.x % kEpochGroups;
-    const unsigned gsize = (gridDim.x - g + kEpochGroups - 1) / kEpochGroups;
-    unsigned long long* ctr = &p.ws->group_ctr[g][0];
-    const unsigned long long old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)old == gsize - 1)
-      __hip_atomic_fetch_add(ctr, (1ull << 32) - gsize, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---- epoch of this launch: the arrivals of one group agree on its counter's epoch
+  // field.  Thread 0's arrival goes out right after the router loads; its result is
+  // used after the dots.
+  const int eg = b % kEpochGroups;
+  const unsigned egsize = (NB - eg + kEpochGroups - 1) / kEpochGroups;
+  unsigned long long* ectr = &p.ws->group_ctr[eg][0];
+  auto finish_epoch = [&](unsigned long long old) {
+    if ((uint32_t)old == egsize - 1)
+      __hip_atomic_fetch_add(ectr, (1ull << 32) - egsize, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_epoch = (uint32_t)(old >> 32) + 1u;
   };
 
-  // ------------------------------------------------------------ phase A
-  // Router: workgroup b computes experts 8b..8b+7 (two per wave, x read from
-  // global memory) and wave 0 publishes them as one line of tagged words.
-  const int rgroups = (E + 7) / 8;
-  bool have_epoch = false;
-  constexpr bool router_q8 = kQ8Router;
-  for (int rb = blockIdx.x; rb < rgroups; rb += gridDim.x) {  // same trip count for the whole workgroup
-    const uint4* xv = reinterpret_cast<const uint4*>(p.x);
-    float la, lb;
-    if constexpr (router_q8) {
-      // 8-bit router (count 1, [E][H/4] words): a lane takes 16-code chunks (one
-      // 16-byte load per row), which lie inside one 64-column group, and adds
-      // scale * sum(x q) + bias * sum(x) for each; x as 8 bf16 per 16-byte load.
-      const int G = H >> 6;
-      const int e0 = min(rb * 8 + 2 * wv, E - 1), e1 = min(rb * 8 + 2 * wv + 1, E - 1);
-      const uint4* q0 = reinterpret_cast<const uint4*>(p.L.router_q8.codes) + (size_t)e0 * (H >> 4);
-      const uint4* q1 = reinterpret_cast<const uint4*>(p.L.router_q8.codes) + (size_t)e1 * (H >> 4);
-      float a = 0.f, b = 0.f;
-      for (int c = lane; c < (H >> 4); c += kWave) {
-        const uint4 w0 = q0[c], w1 = q1[c], xa = xv[2 * c], xb = xv[2 * c + 1];
-        const int g = c >> 2;
-        const float s0 = bf16_bits_to_f32(p.L.router_q8.scales[(size_t)e0 * G + g]);
-        const float o0 = bf16_bits_to_f32(p.L.router_q8.biases[(size_t)e0 * G + g]);
-        const float s1 = bf16_bits_to_f32(p.L.router_q8.scales[(size_t)e1 * G + g]);
-        const float o1 = bf16_bits_to_f32(p.L.router_q8.biases[(size_t)e1 * G + g]);
-        if (!have_epoch) {
-          have_epoch = true;
-          if (threadIdx.x == 0) acquire_epoch();
-        }
-        const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-        const uint32_t c0w[4] = {w0.x, w0.y, w0.z, w0.w}, c1w[4] = {w1.x, w1.y, w1.z, w1.w};
-        float p0 = 0.f, p1 = 0.f, xs_ = 0.f;
+  const RowGeom gh = row_geom(CH);
+  const RowGeom gd = row_geom(CI);
+  const int PS = kWaves * gh.RPW;  // gate/up row pairs per pass
+  const int nbatch_units = kActBatch / kUnitRows;
+  const int upe = I / kUnitRows;   // gate/up units per expert
+
+  // ================================================================ phase A
+  // Router rows e = b, b + NB, ... (one 16-byte word of a row per thread when fast).
+  const int nrows_rt = b < E ? (E - 1 - b) / NB + 1 : 0;
+  constexpr bool rt_pf = kFast && !kQ8Router;
+  uint4 rreg[kRtRows], xreg;
+  if constexpr (rt_pf) {
+    const int c = min(t, (H >> 3) - 1);
+    xreg = reinterpret_cast<const uint4*>(p.x)[c];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float xi = bf16_bits_to_f32((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-          xs_ += xi;
-          p0 = fmaf(xi, (float)((c0w[i >> 2] >> (8 * (i & 3))) & 0xFFu), p0);
-          p1 = fmaf(xi, (float)((c1w[i >> 2] >> (8 * (i & 3))) & 0xFFu), p1);
-        }
-        a += fmaf(s0, p0, o0 * xs_);
-        b += fmaf(s1, p1, o1 * xs_);
-      }
-      if (!have_epoch) {
-        have_epoch = true;
-        if (threadIdx.x == 0) acquire_epoch();
-      }
-      la = group_sum_rt(a, 6);
-      lb = group_sum_rt(b, 6);
-    } else {
-    const uint4* r0 = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(rb * 8 + 2 * wv, E - 1) * H);
-    const uint4* r1 = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(rb * 8 + 2 * wv + 1, E - 1) * H);
-    constexpr int kBatch = 4;  // row chunks in flight per lane and row
-    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-    for (int c0 = 0; c0 < (H >> 3); c0 += kBatch * kWave) {
-      uint4 w0[kBatch], w1[kBatch], v[kBatch];
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        const int c = c0 + q * kWave + lane;
-        const bool ok = c < (H >> 3);
-        w0[q] = ok ? r0[c] : make_uint4(0, 0, 0, 0);
-        w1[q] = ok ? r1[c] : make_uint4(0, 0, 0, 0);
-        v[q] = ok ? xv[c] : make_uint4(0, 0, 0, 0);
-      }
-      if (!have_epoch) {
-        have_epoch = true;
-        if (threadIdx.x == 0) acquire_epoch();
-      }
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        a0 = dot2_bf16(w0[q].x, v[q].x, a0);
-        a1 = dot2_bf16(w0[q].y, v[q].y, a1);
-        a0 = dot2_bf16(w0[q].z, v[q].z, a0);
-        a1 = dot2_bf16(w0[q].w, v[q].w, a1);
-        b0 = dot2_bf16(w1[q].x, v[q].x, b0);
-        b1 = dot2_bf16(w1[q].y, v[q].y, b1);
-        b0 = dot2_bf16(w1[q].z, v[q].z, b0);
-        b1 = dot2_bf16(w1[q].w, v[q].w, b1);
-      }
-    }
-    la = group_sum_rt(a0 + a1, 6);
-    lb = group_sum_rt(b0 + b1, 6);
-    }
-    if (lane == 0) {
-      s_rlog[2 * wv] = la;
-      s_rlog[2 * wv + 1] = lb;
-    }
-    __syncthreads();
-    if (wv == 0 && lane < 8 && rb * 8 + lane < E)
-      __hip_atomic_store(&p.ws->tag_logit[rb * 8 + lane], ((unsigned long long)s_epoch << 32) | __float_as_uint(s_rlog[lane]),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();  // s_rlog is reused
+    for (int m = 0; m < kRtRows; ++m)
+      rreg[m] = reinterpret_cast<const uint4*>(L.router + (size_t)min(b + m * NB, E - 1) * H)[c];
   }
-  if (!have_epoch && threadIdx.x == 0) acquire_epoch();
-  stage_bf16_parallel(p.x, H, xp, xs, 0, kThreads);
-  if constexpr (kQ8Shared) stage_q8_groups(xf, H, [&](int i) { return bf16_bits_to_f32(p.x[i]); });
-  __syncthreads();
+  unsigned long long arrival;
+  if (t == 0) arrival = __hip_atomic_fetch_add(ectr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // Shared gate/up units su = b, b + NB, ... (8 row pairs each): in the fast form the
+  // loads of the first kShSlots passes go out now (they depend on nothing).
+  const int sh_units = has_shared && b < upe ? (upe - 1 - b) / NB + 1 : 0;
+  const int sh_pairs = min(sh_units, nbatch_units) * kUnitRows;  // the first batch
+  const int sh_passes = (sh_pairs + PS - 1) / PS;
+  auto sh_row = [&](int P) { return (b + (P / kUnitRows) * NB) * kUnitRows + (P % kUnitRows); };
+  constexpr bool sh_pf = kFast && !kQ8Shared;
+  const int sh_pfp = sh_pf ? min(sh_passes, kShSlots) : 0;
+  PairRegs shr[kShSlots];
+  if constexpr (sh_pf) {
+    // clamped: a workgroup without shared work reads the last unit's rows (never used)
+    const int lastP = sh_pairs > 0 ? sh_pairs - 1 : 0;
+    const int bsh = sh_pairs > 0 ? b : upe - 1;
+#pragma unroll
+    for (int q = 0; q < kShSlots; ++q) {
+      const int P = min(q * PS + wv * gh.RPW + gh.lg, lastP);
+      const int i = has_shared ? (bsh + (P / kUnitRows) * NB) * kUnitRows + (P % kUnitRows) : 0;
+      load_pair(has_shared ? shared_pair_ref(L, i) : routed_pair_ref(L, 0, 0), gh.sub, shr[q]);
+    }
+  }
+
+  // Router dots, one partial per thread, then a fixed-order sum over the waves.
+  for (int m0 = 0; m0 < nrows_rt; m0 += kRtRows) {
+#pragma unroll
+    for (int mm = 0; mm < kRtRows; ++mm) {
+      const int m = m0 + mm;
+      if (m >= nrows_rt) break;
+      const int e = b + m * NB;
+      float part = 0.f;
+      if constexpr (kQ8Router) {
+        // 8-bit router (count 1, [E][H/4] words): 16-code chunks per thread (inside one group)
+        const int G = H >> 6;
+        const uint4* qr = reinterpret_cast<const uint4*>(L.router_q8.codes) + (size_t)e * (H >> 4);
+        const uint4* xv = reinterpret_cast<const uint4*>(p.x);
+        for (int c = t; c < (H >> 4); c += kThreads) {
+          const uint4 w = qr[c], xa = xv[2 * c], xb = xv[2 * c + 1];
+          const float sc = bf16_bits_to_f32(L.router_q8.scales[(size_t)e * G + (c >> 2)]);
+          const float o = bf16_bits_to_f32(L.router_q8.biases[(size_t)e * G + (c >> 2)]);
+          const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+          const uint32_t cw[4] = {w.x, w.y, w.z, w.w};
+          float pq = 0.f, xsum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float xi = bf16_bits_to_f32((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+            xsum += xi;
+            pq = fmaf(xi, (float)((cw[i >> 2] >> (8 * (i & 3))) & 0xFFu), pq);
+          }
+          part += fmaf(sc, pq, o * xsum);
+        }
+      } else if (rt_pf && m < kRtRows) {
+        const uint4 w = rreg[mm];
+        float a0 = dot2_bf16(w.x, xreg.x, 0.f), a1 = dot2_bf16(w.y, xreg.y, 0.f);
+        a0 = dot2_bf16(w.z, xreg.z, a0);
+        a1 = dot2_bf16(w.w, xreg.w, a1);
+        part = t < (H >> 3) ? a0 + a1 : 0.f;
+      } else {
+        const uint4* rr = reinterpret_cast<const uint4*>(L.router + (size_t)e * H);
+        const uint4* xv = reinterpret_cast<const uint4*>(p.x);
+        float a0 = 0.f, a1 = 0.f;
+        for (int c = t; c < (H >> 3); c += kThreads) {
+          const uint4 w = rr[c], v = xv[c];
+          a0 = dot2_bf16(w.x, v.x, a0);
+          a1 = dot2_bf16(w.y, v.y, a1);
+          a0 = dot2_bf16(w.z, v.z, a0);
+          a1 = dot2_bf16(w.w, v.w, a1);
+        }
+        part = a0 + a1;
+      }
+      part = group_sum_rt(part, 6);
+      if (lane == 0) s_rpart[mm][wv] = part;
+    }
+    if constexpr (rt_pf) {
+      if (m0 == 0) stage_bf16_block(xreg, t, H >> 3, xp, xs);  // x from the router pass's registers
+    }
+    if (t == 0 && m0 == 0) finish_epoch(arrival);
+    lds_sync();  // partials (and, on the first pass, the epoch) visible
+    if (t < kRtRows * kCopies && m0 + t / kCopies < nrows_rt) {  // one thread per (row, copy)
+      const int mm = t / kCopies, c = t % kCopies;
+      float v = s_rpart[mm][0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v += s_rpart[mm][w];
+      __hip_atomic_store(&p.ws->tag_logit[(size_t)c * kLogitCopyWords + (size_t)(b + (m0 + mm) * NB) * kLogitStride],
+                         tag_word(s_epoch, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lds_sync();  // s_rpart is reused
+  }
+  if (t == 0 && nrows_rt == 0) finish_epoch(arrival);
+  if (!rt_pf || nrows_rt == 0) {
+    stage_bf16_parallel(p.x, H, xp, xs);
+    lds_sync();  // x staged; the epoch is visible
+  }
+  if constexpr (kQ8Shared) {
+    stage_q8_groups(xf, H, [&](int i) { return bf16_bits_to_f32(p.x[i]); });
+    lds_sync();
+  }
   const uint32_t epoch = s_epoch;
+
+  // Shared expert gate/up with SwiGLU (off the critical path: needed only in phase C),
+  // into s_sh.  Waves 1.. take their share while wave 0 takes the top-k; wave 0 takes
+  // its share once the routed loads are out.
+  auto shared_compute = [&]() {
+    if (!has_shared) return;
+    if constexpr (kQ8Shared) {
+      // 8-row units, one per wave at a time, on waves 1..
+      for (int m = wv - 1; m >= 0 && m < min(sh_units, nbatch_units); m += kWaves - 1) {
+        const float2 gu = unit_gate_up_q8(L, (b + m * NB) * kUnitRows, xf);
+        if ((lane & 7) == 0) s_sh[m * kUnitRows + (lane >> 3)] = silu(gu.x) * gu.y;
+      }
+    } else {
+      if constexpr (sh_pf) {
+        XChunk x1;
+        read_xchunk(xp, xs, gh.sub, x1);
+#pragma unroll
+        for (int q = 0; q < kShSlots; ++q) {
+          if (q < sh_pfp) {
+            const int P = q * PS + wv * gh.RPW + gh.lg;
+            const float2 tt = pair_terms(shr[q], x1);
+            const float g = group_sum_rt(tt.x, gh.lr), u = group_sum_rt(tt.y, gh.lr);
+            if (gh.sub == 0 && P < sh_pairs) s_sh[P] = silu(g) * u;
+          }
+        }
+      }
+      for (int q = sh_pfp; q < sh_passes; ++q) {
+        const int P = q * PS + wv * gh.RPW + gh.lg;
+        const bool live = P < sh_pairs;
+        const float2 gu = pair_dot_now(shared_pair_ref(L, live ? sh_row(P) : 0), gh, xp, xs, live);
+        if (gh.sub == 0 && live) s_sh[P] = silu(gu.x) * gu.y;
+      }
+    }
+  };
+  if (wv != 0) shared_compute();
 
   if (wv == 0) {
     // The shared expert's gate, sigmoid(sh_gate_w . x), taken while the router logits of the
     // other workgroups are still arriving (the top-k below waits for them).
     float sh_weight = 1.0f;
     if constexpr (kShGate) {
-      const uint4* gw = reinterpret_cast<const uint4*>(p.L.sh_gate_w);
+      const uint4* gw = reinterpret_cast<const uint4*>(L.sh_gate_w);
       const uint4* gx = reinterpret_cast<const uint4*>(p.x);
       float d0 = 0.f, d1 = 0.f;
       for (int c = lane; c < (H >> 3); c += kWave) {
-        const uint4 a = gw[c], b = gx[c];
-        d0 = dot2_bf16(a.x, b.x, d0);
-        d1 = dot2_bf16(a.y, b.y, d1);
-        d0 = dot2_bf16(a.z, b.z, d0);
-        d1 = dot2_bf16(a.w, b.w, d1);
+        const uint4 a = gw[c], bb = gx[c];
+        d0 = dot2_bf16(a.x, bb.x, d0);
+        d1 = dot2_bf16(a.y, bb.y, d1);
+        d0 = dot2_bf16(a.z, bb.z, d0);
+        d1 = dot2_bf16(a.w, bb.w, d1);
       }
       const float d = group_sum_rt(d0 + d1, 6);
       sh_weight = 1.0f / (1.0f + __expf(-d));
     }
     // B: top-k from the tagged logits (every workgroup, redundantly)
     if (E <= 4 * kWave)
-      wave_topk_tagged<4>(p.ws->tag_logit, E, k, epoch, timeouts, s_ids, s_w, blockIdx.x == 0 ? p.ids_out : nullptr,
-                          blockIdx.x == 0 ? p.w_out : nullptr);
+      wave_topk_tagged<4>(p.ws->tag_logit + (size_t)(b % kCopies) * kLogitCopyWords, E, k, epoch, timeouts, s_ids, s_w, b == 0 ? p.ids_out : nullptr,
+                          b == 0 ? p.w_out : nullptr);
     else
-      wave_topk_tagged<kMaxExperts / kWave>(p.ws->tag_logit, E, k, epoch, timeouts, s_ids, s_w,
-                                            blockIdx.x == 0 ? p.ids_out : nullptr, blockIdx.x == 0 ? p.w_out : nullptr);
-    if (lane == 0 && p.L.has_shared) {
+      wave_topk_tagged<kMaxExperts / kWave>(p.ws->tag_logit + (size_t)(b % kCopies) * kLogitCopyWords, E, k, epoch, timeouts, s_ids, s_w,
+                                            b == 0 ? p.ids_out : nullptr, b == 0 ? p.w_out : nullptr);
+    if (lane == 0 && has_shared) {
       s_ids[k] = -1;
       s_w[k] = sh_weight;
     }
-  } else if (p.L.has_shared) {
-    // A, off the critical path: the shared expert's gate/up in 8-row units.  With
-    // at most one unit per workgroup, waves 1-3 split its groups in thirds and
-    // wave 1 adds the thirds after the barrier below; otherwise each wave takes
-    // whole units.
-    constexpr int R = kQ8Shared ? kQ8UnitRows : kUnitRows, LOG = kQ8Shared ? kQ8LaneLog : 3;
-    const int units = (I + R - 1) / R, G = H >> 6;
-    const int su = shared_unit_of(blockIdx.x, gridDim.x, rgroups, units);
-    if (units + rgroups <= (int)gridDim.x) {
-      if (su >= 0) {
-        const int w = wv - 1;
-        const float2 gu = shared_unit_gate_up<kQ8Shared, 2>(p.L, su * R, w * G / 3, (w + 1) * G / 3, xp, xs, xf);
-        if ((lane & ((1 << LOG) - 1)) == 0) s_third[w][lane >> LOG] = gu;
+  }
+  lds_sync();  // ids known; shared activations gathered
+
+  // ================================================================ phase B
+  // Routed gate/up units u = b, b + NB, ... of the k * I / 8 units (slot u / upe, rows
+  // (u % upe) * 8 ..) and this workgroup's 8-row output blocks of the down
+  // projection, for every slot.  Fast form: the loads of the first kGuSlots gate/up
+  // passes and kDnSlots down passes go out now, all at once.
+  const int U = k * upe;
+  const int my_units = b < U ? (U - 1 - b) / NB + 1 : 0;
+  auto unit_of = [&](int m) -> int2 {
+    const int u = min(b + m * NB, U - 1);
+    return make_int2(u / upe, (u % upe) * kUnitRows);
+  };
+  const int pairs0 = min(my_units, nbatch_units) * kUnitRows;
+  const int passes0 = (pairs0 + PS - 1) / PS;
+  const int gu_pfp = kFast ? min(passes0, kGuSlots) : 0;
+  const int GI = I >> 6;
+  const int PSd = kWaves * gd.RPW;
+  const int dtasks = nslot * kOutRows;
+  const int dpasses = (dtasks + PSd - 1) / PSd;
+  const int nblocks = H / kOutRows;
+  const int dn_pfp = kFast && b < nblocks ? min(dpasses, kDnSlots) : 0;
+  const int64_t dmat_rows = (int64_t)H;
+  // down row n of slot j: its code row, scales and biases (routed expert s_ids[j], or shared)
+  // The shared expert's down rows are addressed from the routed stack's base by their
+  // element distance, so a row pointer is one base plus a selected offset (a select
+  // between two pointers would become a per-lane load of the selected argument field).
+  const int64_t sh_dc = has_shared ? (int64_t)((uintptr_t)L.sh_down.codes - (uintptr_t)L.down.codes) / 4 : 0;
+  const int64_t sh_ds = has_shared ? (int64_t)((uintptr_t)L.sh_down.scales - (uintptr_t)L.down.scales) / 2 : 0;
+  const int64_t sh_db = has_shared ? (int64_t)((uintptr_t)L.sh_down.biases - (uintptr_t)L.down.biases) / 2 : 0;
+  auto down_row = [&](int j, int n, const uint4*& cr, const uint16_t*& sr, const uint16_t*& br) {
+    const int e = s_ids[j];
+    const bool routed = e >= 0;
+    const int64_t row = routed ? (int64_t)e * dmat_rows + n : (int64_t)n;
+    cr = reinterpret_cast<const uint4*>(L.down.codes + (routed ? 0 : sh_dc) + row * (I >> 3));
+    sr = L.down.scales + (routed ? 0 : sh_ds) + row * GI;
+    br = L.down.biases + (routed ? 0 : sh_db) + row * GI;
+  };
+  PairRegs gur[kGuSlots];
+  struct DnRegs {
+    uint4 c;
+    uint32_t s, bb;
+  };
+  DnRegs dnr[kDnSlots];
+  if constexpr (kFast) {
+    const int lastP = pairs0 > 0 ? pairs0 - 1 : 0;
+#pragma unroll
+    for (int q = 0; q < kGuSlots; ++q) {
+      const int P = min(q * PS + wv * gh.RPW + gh.lg, lastP);
+      const int2 su = unit_of(P / kUnitRows);
+      load_pair(routed_pair_ref(L, s_ids[su.x], su.y + P % kUnitRows), gh.sub, gur[q]);
+    }
+  }
+  auto issue_down = [&]() {
+    if constexpr (!kFast) return;
+    const int rb0 = min(b, nblocks - 1);
+#pragma unroll
+    for (int q = 0; q < kDnSlots; ++q) {
+      const int task = min(q * PSd + wv * gd.RPW + gd.lg, dtasks - 1);
+      int j = task / kOutRows;
+      if (kQ8Shared && j == k) j = 0;  // the 8-bit shared slot is read in phase C
+      const uint4* cr;
+      const uint16_t *sr, *br;
+      down_row(j, rb0 * kOutRows + task % kOutRows, cr, sr, br);
+      dnr[q].c = cr[gd.sub];
+      dnr[q].s = sr[gd.sub >> 1];
+      dnr[q].bb = br[gd.sub >> 1];
+    }
+  };
+  if (!kDownLate) issue_down();
+
+  // gate/up with SwiGLU, gathered per batch of units in LDS, then published; the
+  // shared units of phase A go out with the first batch
+  for (int m0 = 0; m0 < max(my_units, 1); m0 += nbatch_units) {
+    const int nm = min(nbatch_units, my_units - m0);
+    const int np = max(nm, 0) * kUnitRows;
+    const int npass = (np + PS - 1) / PS;
+    if (m0 == 0 && wv == 0) shared_compute();  // wave 0's share of the shared expert, loads already out
+    int q0 = 0;
+    if constexpr (kFast) {
+      if (m0 == 0) {
+        XChunk x1;
+        read_xchunk(xp, xs, gh.sub, x1);
+#pragma unroll
+        for (int q = 0; q < kGuSlots; ++q) {
+          if (q < gu_pfp) {
+            const int P = q * PS + wv * gh.RPW + gh.lg;
+            const float2 tt = pair_terms(gur[q], x1);
+            const float g = group_sum_rt(tt.x, gh.lr), u = group_sum_rt(tt.y, gh.lr);
+            if (gh.sub == 0 && P < np) s_act[P] = silu(g) * u;
+          }
+        }
+        q0 = gu_pfp;
+      }
+    }
+    for (int q = q0; q < npass; ++q) {
+      const int P = q * PS + wv * gh.RPW + gh.lg;
+      const bool live = P < np;
+      const int2 su = unit_of(m0 + (live ? P / kUnitRows : 0));
+      const float2 gu =
+          pair_dot_now(routed_pair_ref(L, s_ids[su.x], su.y + (live ? P % kUnitRows : 0)), gh, xp, xs, live);
+      if (gh.sub == 0 && live) s_act[P] = silu(gu.x) * gu.y;
+    }
+    if (kDownLate && m0 == 0) issue_down();
+    lds_sync();
+    if (nm > 0) publish_units(p.act, p.act_copy_words, I, s_act, nm, epoch, [&](int m) { return unit_of(m0 + m); });
+    if (m0 == 0 && has_shared && sh_units > 0)
+      publish_units(p.act, p.act_copy_words, I, s_sh, min(sh_units, nbatch_units), epoch,
+                    [&](int m) { return make_int2(k, (b + m * NB) * kUnitRows); });
+    lds_sync();  // s_act is reused
+  }
+  // (rarely: more shared units than one batch holds, i.e. fewer than I / 256 workgroups)
+  for (int m0 = nbatch_units; m0 < sh_units; m0 += nbatch_units) {
+    const int nm = min(nbatch_units, sh_units - m0);
+    if constexpr (kQ8Shared) {
+      for (int m = wv; m < nm; m += kWaves) {
+        const float2 gu = unit_gate_up_q8(L, (b + (m0 + m) * NB) * kUnitRows, xf);
+        if ((lane & 7) == 0) s_sh[m * kUnitRows + (lane >> 3)] = silu(gu.x) * gu.y;
       }
     } else {
-      for (int u = (wv - 1) * gridDim.x + blockIdx.x; u < units; u += (kWaves - 1) * gridDim.x) {
-        const float2 gu = shared_unit_gate_up<kQ8Shared, 4>(p.L, u * R, 0, G, xp, xs, xf);
-        publish_unit<LOG>(p.act + (size_t)k * I, u * R, I, silu(gu.x) * gu.y, epoch);
+      const int np = nm * kUnitRows;
+      for (int q = 0; q * PS < np; ++q) {
+        const int P = q * PS + wv * gh.RPW + gh.lg;
+        const bool live = P < np;
+        const int i = live ? (b + (m0 + P / kUnitRows) * NB) * kUnitRows + P % kUnitRows : 0;
+        const float2 gu = pair_dot_now(shared_pair_ref(L, i), gh, xp, xs, live);
+        if (gh.sub == 0 && live) s_sh[P] = silu(gu.x) * gu.y;
       }
     }
-  }
-  __syncthreads();
-  if (p.L.has_shared && wv == 1) {
-    constexpr int R = kQ8Shared ? kQ8UnitRows : kUnitRows, LOG = kQ8Shared ? kQ8LaneLog : 3;
-    const int units = (I + R - 1) / R;
-    const int su = shared_unit_of(blockIdx.x, gridDim.x, rgroups, units);
-    if (units + rgroups <= (int)gridDim.x && su >= 0) {
-      const float2 a = s_third[0][lane >> LOG], b = s_third[1][lane >> LOG], c = s_third[2][lane >> LOG];
-      const float g = (a.x + b.x) + c.x, up = (a.y + b.y) + c.y;
-      publish_unit<LOG>(p.act + (size_t)k * I, su * R, I, silu(g) * up, epoch);
-    }
+    lds_sync();
+    publish_units(p.act, p.act_copy_words, I, s_sh, nm, epoch, [&](int m) { return make_int2(k, (b + (m0 + m) * NB) * kUnitRows); });
+    lds_sync();
   }
 
-  {
-    // B: the routed experts' gate/up in 8-row units; the two waves of a pair
-    // split the groups, one wave adds the halves and publishes the line.
-    const int per_slot = (I + kUnitRows - 1) / kUnitRows;
-    const int units = k * per_slot;
-    const int pair = wv >> 1, half = wv & 1;
-    const int G = H >> 6, gmid = (G + 1) >> 1;
-    for (int ub = 2 * blockIdx.x; ub < units; ub += 2 * gridDim.x) {  // same trip count for every wave
-      const int u = ub + pair;
-      const bool live = u < units;
-      const int j = live ? u / per_slot : 0, i0 = live ? (u - j * per_slot) * kUnitRows : 0;
-      const float2 gu = unit_gate_up<2>(p.L, s_ids[j], i0, half ? gmid : 0, half ? G : gmid, xp, xs);
-      if (half && (lane & 7) == 0) s_pair[pair][lane >> 3] = gu;
-      __syncthreads();
-      if (!half && live) {
-        const float2 o = s_pair[pair][lane >> 3];
-        const float g = gu.x + o.x, up = gu.y + o.y;
-        publish_unit(p.act + (size_t)j * I, i0, I, silu(g) * up, epoch);
-      }
-      __syncthreads();
-    }
-  }
-
-  // prefetch the down rows this workgroup owns in phase C (its first row block);
-  // issued after phase B's loads so they do not compete with them, and hidden
-  // behind the activation handoff
-  const int LI = 1 << p.lsI, subI = lane & (LI - 1), rsubI = lane >> p.lsI, rpiI = kWave >> p.lsI;
-  const int GI = I >> 6;
-  const bool pf_ok = GI == LI && (int)blockIdx.x * rpiI < H;
-  DownPrefetch pf[kPrefetchSlots];
-  // an 8-bit shared expert: the down-row group of this lane for the first row block,
-  // held by the wave that takes the shared slot (slot k, wave k % kWaves)
-  uint4 qpf[4] = {};
-  uint32_t qps = 0, qpb = 0;
-  if constexpr (kQ8Shared) {
-    const int n = blockIdx.x * rpiI + rsubI;
-    if (pf_ok && k % kWaves == wv && n < H) {
-      const uint4* cr = reinterpret_cast<const uint4*>(p.L.sh_down.codes) + (int64_t)n * (I >> 4) + 4 * subI;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) qpf[q] = cr[q];
-      qps = p.L.sh_down.scales[(int64_t)n * GI + subI];
-      qpb = p.L.sh_down.biases[(int64_t)n * GI + subI];
-    }
-  }
-  {
-    const int n = blockIdx.x * rpiI + rsubI;
-    const int64_t mat_codes = (int64_t)H * (I >> 3), mat_groups = (int64_t)H * GI;
-#pragma unroll
-    for (int s = 0; s < kPrefetchSlots; ++s) {
-      const int j = wv + kWaves * s;
-      if (pf_ok && j < nslot && n < H && !(kQ8Shared && s_ids[j] < 0)) {
-        const int e = s_ids[j];
-        const Q4Mat& m = e >= 0 ? p.L.down : p.L.sh_down;
-        const int64_t oc = e >= 0 ? e * mat_codes : 0, og = e >= 0 ? e * mat_groups : 0;
-        const uint4* cr = reinterpret_cast<const uint4*>(m.codes + oc) + (int64_t)n * CI;
-        pf[s].c0 = cr[2 * subI];
-        pf[s].c1 = cr[2 * subI + 1];
-        pf[s].s = m.scales[og + (int64_t)n * GI + subI];
-        pf[s].b = m.biases[og + (int64_t)n * GI + subI];
-      } else {
-        pf[s].c0 = pf[s].c1 = make_uint4(0, 0, 0, 0);
-        pf[s].s = pf[s].b = 0;
-      }
-    }
-  }
-
-  // ------------------------------------------------------------ phase C
+  // ================================================================ phase C
   // routed slots and the shared slot (an 8-bit shared expert's slot also as fp32 into af)
-  stage_tagged_split(p.act, nslot, I, ap, as, epoch, timeouts, kQ8Shared ? af : nullptr, k * I);
-  __syncthreads();
+  stage_tagged_split(p.act + (size_t)(b % kCopies) * p.act_copy_words, nslot, I, ap, as, epoch, timeouts,
+                     kQ8Shared ? af : nullptr, k * I);
+  lds_sync();  // activations staged
   {
     constexpr int ST = chunk_stride<2>();
-    const int64_t mat_codes = (int64_t)H * (I >> 3), mat_groups = (int64_t)H * GI;
-    for (int rb = blockIdx.x; rb * rpiI < H; rb += gridDim.x) {
-      const int n = rb * rpiI + rsubI;
-      const bool first = rb == (int)blockIdx.x && pf_ok;
-      float acc = 0.f;
-      if (n < H) {
-        for (int j = wv, s = 0; j < nslot; j += kWaves, ++s) {
-          const int e = s_ids[j];
-          float part = 0.f;
-          if (kQ8Shared && e < 0 && first) {
-            part = q8_group_term_regs(qpf, af + subI * kQ8Pad, qps, qpb);  // one group per lane (GI == LI)
-          } else if (kQ8Shared && e < 0) {
-            const uint4* cr = reinterpret_cast<const uint4*>(p.L.sh_down.codes) + (int64_t)n * (I >> 4);
-            const uint16_t* sr = p.L.sh_down.scales + (int64_t)n * GI;
-            const uint16_t* br = p.L.sh_down.biases + (int64_t)n * GI;
-            for (int g = subI; g < GI; g += LI) part += q8_group_term(cr + 4 * g, af + g * kQ8Pad, sr[g], br[g]);
-          } else if (first && s < kPrefetchSlots) {
-            DownPrefetch d = pf[0];
+    for (int rb = b; rb < nblocks; rb += NB) {
+      int q0 = 0;
+      if constexpr (kFast) {
+        if (rb == b) {
 #pragma unroll
-            for (int q = 1; q < kPrefetchSlots; ++q)
-              if (q == s) d = pf[q];
-            const uint32_t* v = ap + ((size_t)j * CI + 2 * subI) * ST;
-            const float vsum = as[j * CI + 2 * subI] + as[j * CI + 2 * subI + 1];
-            part = affine_term(chunk_pdot<2>(d.c0, v) + chunk_pdot<2>(d.c1, v + ST), vsum, d.s, d.b);
-          } else {
-            const Q4Mat& m = e >= 0 ? p.L.down : p.L.sh_down;
-            const int64_t oc = e >= 0 ? e * mat_codes : 0, og = e >= 0 ? e * mat_groups : 0;
-            const uint4* cr = reinterpret_cast<const uint4*>(m.codes + oc) + (int64_t)n * CI;
-            const uint16_t* sr = m.scales + og + (int64_t)n * GI;
-            const uint16_t* br = m.biases + og + (int64_t)n * GI;
-            for (int g = subI; g < GI; g += LI) {
-              const uint4 c0 = cr[2 * g], c1 = cr[2 * g + 1];
-              const uint32_t* v = ap + ((size_t)j * CI + 2 * g) * ST;
-              const float vsum = as[j * CI + 2 * g] + as[j * CI + 2 * g + 1];
-              part += affine_term(chunk_pdot<2>(c0, v) + chunk_pdot<2>(c1, v + ST), vsum, sr[g], br[g]);
+          for (int q = 0; q < kDnSlots; ++q) {
+            if (q < dn_pfp) {
+              const int task = q * PSd + wv * gd.RPW + gd.lg;
+              const bool live = task < dtasks;
+              const int j = live ? task / kOutRows : 0, r = task % kOutRows;
+              float part;
+              if (kQ8Shared && j == k) {
+                part = q8_down_row(L, rb * kOutRows + r, af, gd.sub, gd.LR, gd.lr, live);
+              } else {
+                const int c = gd.sub;
+                part = affine_term(chunk_pdot<2>(dnr[q].c, ap + ((size_t)j * CI + c) * ST), as[j * CI + c],
+                                   dnr[q].s, dnr[q].bb);
+                part = group_sum_rt(part, gd.lr);
+              }
+              if (gd.sub == 0 && live) s_red[task] = part;
             }
           }
-          acc = fmaf(s_w[j], part, acc);
+          q0 = dn_pfp;
         }
       }
-      acc = group_sum_rt(acc, p.lsI);
-      if (subI == 0) s_red[wv][rsubI] = acc;
-      __syncthreads();
-      if (wv == 0 && lane < rpiI) {
-        const int nn = rb * rpiI + lane;
-        if (nn < H) {
-          float t = s_red[0][lane];
-#pragma unroll
-          for (int w = 1; w < kWaves; ++w) t += s_red[w][lane];
-          if (p.out_mode == kOutBf16Residual) t += bf16_bits_to_f32(p.x[nn]);
-          if (p.out_mode != kOutF32)
-            reinterpret_cast<uint16_t*>(p.y)[nn] = (uint16_t)f32_to_bf16_bits(t);
-          else
-            reinterpret_cast<float*>(p.y)[nn] = t;
+      for (int q = q0; q < dpasses; ++q) {
+        const int task = q * PSd + wv * gd.RPW + gd.lg;
+        const bool live = task < dtasks;
+        const int j = live ? task / kOutRows : 0, n = rb * kOutRows + task % kOutRows;
+        float part = 0.f;
+        if (kQ8Shared && j == k) {
+          part = q8_down_row(L, n, af, gd.sub, gd.LR, gd.lr, live);
+        } else {
+          if (live) {
+            const uint4* cr;
+            const uint16_t *sr, *br;
+            down_row(j, n, cr, sr, br);
+            for (int c = gd.sub; c < CI; c += gd.LR)
+              part += affine_term(chunk_pdot<2>(cr[c], ap + ((size_t)j * CI + c) * ST), as[j * CI + c], sr[c >> 1],
+                                  br[c >> 1]);
+          }
+          part = group_sum_rt(part, gd.lr);
         }
+        if (gd.sub == 0 && live) s_red[task] = part;
       }
-      __syncthreads();
+      lds_sync();
+      if (t < kOutRows) {
+        const int n = rb * kOutRows + t;
+        float acc = 0.f;
+        for (int j = 0; j < nslot; ++j) acc = fmaf(s_w[j], s_red[j * kOutRows + t], acc);  // fixed slot order
+        if (p.out_mode == kOutBf16Residual) acc += bf16_bits_to_f32(p.x[n]);
+        if (p.out_mode != kOutF32)
+          reinterpret_cast<uint16_t*>(p.y)[n] = (uint16_t)f32_to_bf16_bits(acc);
+        else
+          reinterpret_cast<float*>(p.y)[n] = acc;
+      }
+      lds_sync();  // s_red is reused
     }
   }
 }
 
-#define Q4MOE_DECODE_KERNEL(name, q8r, gated, q8sh) \
-  __global__ __launch_bounds__(kThreads) void name(DecodeParams p) { decode_layer<q8r, gated, q8sh>(p); }
+#define Q4MOE_DECODE_KERNEL(name, q8r, gated, q8sh)                                                  \
+  __global__ __launch_bounds__(kThreads) void name(DecodeParams p) { decode_layer<q8r, gated, q8sh, true>(p); } \
+  __global__ __launch_bounds__(kThreads) void name##_any(DecodeParams p) { decode_layer<q8r, gated, q8sh, false>(p); }
 Q4MOE_DECODE_KERNEL(decode_layer_kernel, false, false, false)
 Q4MOE_DECODE_KERNEL(decode_layer_q8router_kernel, true, false, false)
 Q4MOE_DECODE_KERNEL(decode_layer_gated_kernel, false, true, false)
@@ -789,12 +977,6 @@ Q4MOE_DECODE_KERNEL(decode_layer_q8router_q8shared_kernel, true, false, true)
 Q4MOE_DECODE_KERNEL(decode_layer_gated_q8shared_kernel, false, true, true)
 Q4MOE_DECODE_KERNEL(decode_layer_q8router_gated_q8shared_kernel, true, true, true)
 #undef Q4MOE_DECODE_KERNEL
-
-int lanes_log2(int groups) {
-  int r = 0;
-  while (r < 6 && (2 << r) <= groups) ++r;
-  return r;
-}
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -806,15 +988,70 @@ size_t decode_lds(const DecodeLayer& L) {
   return b;
 }
 
+typedef void (*DecodeKernel)(DecodeParams);
+
+DecodeKernel decode_kernel_for(const DecodeLayer& L) {
+  static const DecodeKernel kernels[2][2][2][2] = {
+      {{{decode_layer_kernel_any, decode_layer_q8shared_kernel_any},
+        {decode_layer_gated_kernel_any, decode_layer_gated_q8shared_kernel_any}},
+       {{decode_layer_q8router_kernel_any, decode_layer_q8router_q8shared_kernel_any},
+        {decode_layer_q8router_gated_kernel_any, decode_layer_q8router_gated_q8shared_kernel_any}}},
+      {{{decode_layer_kernel, decode_layer_q8shared_kernel},
+        {decode_layer_gated_kernel, decode_layer_gated_q8shared_kernel}},
+       {{decode_layer_q8router_kernel, decode_layer_q8router_q8shared_kernel},
+        {decode_layer_q8router_gated_kernel, decode_layer_q8router_gated_q8shared_kernel}}}};
+  const int q8 = L.router_q8.codes != nullptr, gated = L.sh_gate_w != nullptr && L.has_shared,
+            q8sh = L.has_shared && L.sh_q8;
+  // the fast form: the compiled shape (one 16-byte word of every gate/up and down row per
+  // lane, one word of a router row per thread)
+  const int fast = L.hidden == kFastHidden && L.inter == kFastInter;
+  return kernels[fast][q8][gated][q8sh];
+}
+
+int decode_grid() {
+  int blocks = device_cu_count();
+  return blocks > kMaxBlocks ? kMaxBlocks : blocks;
+}
+
 }  // namespace
+
+// bytes between the copies of the tagged activations: the copy rounded up to 4 KB plus
+// 256 bytes, so that consecutive copies start on different channels
+size_t act_copy_bytes(int top_k, int inter) { return (((size_t)(top_k + 1) * inter * 8 + 4095) & ~size_t(4095)) + 256; }
 
 size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k) {
   (void)hidden;
   (void)n_experts;
-  return align256(sizeof(DecodeWs)) + align256((size_t)(top_k + 1) * inter * 8);
+  return align256(sizeof(DecodeWs)) + (size_t)kCopies * act_copy_bytes(top_k, inter);
 }
 
 size_t decode_lds_bytes(const DecodeLayer& L) { return decode_lds(L); }
+
+// Every workgroup of the grid waits on words that the others publish, so all of them
+// must be resident at once: one workgroup per CU must fit (registers and LDS).  The
+// answer is cached per device and LDS size.
+bool decode_fits(const DecodeLayer& L) {
+  struct Entry {
+    int dev;
+    DecodeKernel k;
+    size_t lds;
+    bool ok;
+  };
+  static Entry cache[32];
+  static int ncache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const DecodeKernel kern = decode_kernel_for(L);
+  const size_t lds = decode_lds(L);
+  for (int i = 0; i < ncache; ++i)
+    if (cache[i].dev == dev && cache[i].k == kern && cache[i].lds == lds) return cache[i].ok;
+  int per_cu = 0;
+  const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kThreads,
+                                                               lds) == hipSuccess &&
+                  per_cu >= 1;
+  if (ncache < 32) cache[ncache++] = Entry{dev, kern, lds, ok};
+  return ok;
+}
 
 hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_mode, int32_t* ids_out,
                               float* w_out, void* ws, hipStream_t stream) {
@@ -829,21 +1066,10 @@ hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, 
   p.ws = reinterpret_cast<DecodeWs*>(w);
   w += align256(sizeof(DecodeWs));
   p.act = reinterpret_cast<unsigned long long*>(w);
-  p.lsH = lanes_log2(L.hidden / kGroup);
-  p.lsI = lanes_log2(L.inter / kGroup);
-  const size_t lds = decode_lds(L);
-  int blocks = device_cu_count();
-  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
-  typedef void (*Kernel)(DecodeParams);
-  static const Kernel kernels[2][2][2] = {
-      {{decode_layer_kernel, decode_layer_q8shared_kernel}, {decode_layer_gated_kernel, decode_layer_gated_q8shared_kernel}},
-      {{decode_layer_q8router_kernel, decode_layer_q8router_q8shared_kernel},
-       {decode_layer_q8router_gated_kernel, decode_layer_q8router_gated_q8shared_kernel}}};
-  const int q8 = L.router_q8.codes != nullptr, gated = L.sh_gate_w != nullptr && L.has_shared,
-            q8sh = L.has_shared && L.sh_q8;
+  p.act_copy_words = (int64_t)act_copy_bytes(L.top_k, L.inter) / 8;
   void* args[] = {&p};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernels[q8][gated][q8sh]), dim3(blocks),
-                                       dim3(kThreads), args, lds, stream);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(decode_kernel_for(L)), dim3(decode_grid()),
+                                       dim3(kThreads), args, decode_lds(L), stream);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

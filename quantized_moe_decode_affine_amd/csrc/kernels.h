@@ -50,6 +50,8 @@ struct DecodeLayer {
 };
 size_t decode_workspace_bytes(int hidden, int inter, int n_experts, int top_k);
 size_t decode_lds_bytes(const DecodeLayer& L);
+// True when one decode workgroup fits on every CU at once (its waits need them all resident).
+bool decode_fits(const DecodeLayer& L);
 // Output forms of the decode layer: fp32, bf16, or bf16(x + y) (the next layer's input).
 enum { kOutF32 = 0, kOutBf16 = 1, kOutBf16Residual = 2 };
 hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_mode, int32_t* ids_out,

@@ -149,6 +149,7 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
+    stack.check()  # no decode launch abandoned a wait (else its outputs are wrong)
     ms_step = ms / args.steps
     layer_bytes = workloads.decode_layer_bytes()
     step_bytes = layer_bytes * args.layers
@@ -198,6 +199,7 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         q_us = ev0.elapsed_time(ev1) * 1e3 / (args.steps * args.layers)
+        stack.check()
         stack.use_q8_router(False)
         q_bytes = layer_bytes - synth.N_EXPERTS * synth.HIDDEN * 2 + workloads.q8_matrix_bytes(synth.N_EXPERTS,
                                                                                                synth.HIDDEN)
@@ -219,6 +221,7 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         c_us = ev0.elapsed_time(ev1) * 1e3 / (args.steps * args.layers)
+        stack.check()
         stack.use_q8_router(False)
         c_bytes = q_bytes - 2 * workloads.q4_matrix_bytes(synth.INTER, synth.HIDDEN) - \
             workloads.q4_matrix_bytes(synth.HIDDEN, synth.INTER) + \
@@ -258,6 +261,7 @@ def main():
         e_us, e_host = run_chain(chain.enqueue)
         chain.capture()
         g_us, g_host = run_chain(chain.replay)
+        chain.check()
         step_bytes = args.layers * workloads.decode_layer_bytes(out_bytes=2) + \
             workloads.q4_matrix_bytes(synth.VOCAB, synth.HIDDEN) + 2 * synth.HIDDEN
         result["chain"] = {

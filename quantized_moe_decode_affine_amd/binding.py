@@ -237,15 +237,42 @@ def moe_permute(ids: torch.Tensor, n_experts: int, ws: Optional[torch.Tensor] = 
     return offsets, rows, inv
 
 
+# Byte offset of the decode workspace's abandoned-wait counter (include/q4moe.h, moe_ffn_decode).
+DECODE_TIMEOUT_OFFSET = 2048
+
+
+class DecodeTimeout(RuntimeError):
+    """A decode launch gave up waiting for a value another workgroup publishes; its result is wrong."""
+
+
+def decode_timeouts(ws: torch.Tensor) -> int:
+    """The abandoned-wait counter of a decode workspace (synchronises with the device)."""
+    return int(ws[DECODE_TIMEOUT_OFFSET:DECODE_TIMEOUT_OFFSET + 4].view(torch.int32).item())
+
+
+def check_decode_workspace(ws: torch.Tensor) -> None:
+    """Raise DecodeTimeout when any decode call that used `ws` abandoned a wait."""
+    n = decode_timeouts(ws)
+    if n:
+        raise DecodeTimeout(f"{n} bounded wait(s) inside moe_ffn_decode gave up: the outputs written since the "
+                            f"workspace was zeroed are wrong (were all workgroups resident at once?)")
+
+
 def moe_ffn_decode(layer: DeviceLayer, x: torch.Tensor, out_dtype: int = OUT_F32, out=None,
                    ids_out: Optional[torch.Tensor] = None, w_out: Optional[torch.Tensor] = None,
                    ws: Optional[torch.Tensor] = None):
+    """One decode step through the layer.  With a workspace of its own (ws None) the call
+    synchronises and raises DecodeTimeout if the launch abandoned a wait; a caller that passes
+    `ws` checks it with check_decode_workspace when it synchronises."""
     y = _out((layer.hidden,), out_dtype, x.device, out)
-    if ws is None:
+    own = ws is None
+    if own:
         ws = workspace(workspace_bytes(OP_FFN_DECODE, layer), x.device)
     _check("moe_ffn_decode", load_library().moe_ffn_decode(ctypes.byref(layer.struct), _ptr(x), _ptr(y), out_dtype,
                                                            _ptr(ids_out), _ptr(w_out), _ptr(ws), ws.numel(),
                                                            _stream()))
+    if own:
+        check_decode_workspace(ws)
     return y
 
 

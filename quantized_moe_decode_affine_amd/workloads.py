@@ -93,6 +93,10 @@ class DecodeStack:
             if st != B.OK:
                 B._check("moe_ffn_decode", st)
 
+    def check(self) -> None:
+        """Synchronise and raise binding.DecodeTimeout if any layer launch abandoned a wait."""
+        B.check_decode_workspace(self.ws)
+
     def enable_q8_router(self, device="cuda") -> None:
         """Give every layer an affine-Q8 router (drawn as synth.moe_layer draws one) in place
         of its bf16 router; :meth:`step` then runs the layers with it.  Only the router
@@ -210,3 +214,7 @@ class DecodeChain:
 
     def replay(self) -> None:
         self.graph.replay()
+
+    def check(self) -> None:
+        """Synchronise and raise binding.DecodeTimeout if any layer launch abandoned a wait."""
+        B.check_decode_workspace(self.ws)

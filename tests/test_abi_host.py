@@ -141,6 +141,19 @@ def test_ffn_rejects(lib):
     assert lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(noshared), None, 50) < need_p
 
 
+def test_decode_needs_coresident_workgroups(lib):
+    """Every argument valid, but the call cannot confirm that one workgroup per CU fits on
+    the device (here: no device at all): it refuses with EUNSUPPORTED and launches nothing,
+    since its workgroups wait on each other's words."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the occupancy query can pass")
+    good = _layer()
+    need = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE, ctypes.byref(good), None, 1)
+    for mode in (B.OUT_F32, B.OUT_BF16, B.OUT_BF16_RESIDUAL):
+        assert lib.moe_ffn_decode(ctypes.byref(good), A, A2, mode, None, None, A, need, None) == B.EUNSUPPORTED
+
+
 def test_decode_batch_rejects(lib):
     good = _layer()
     need = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(good), None, 4)

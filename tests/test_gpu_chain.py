@@ -138,3 +138,16 @@ def test_chain_graph_replay_matches_eager(B):
             assert torch.equal(g, r), rep
         other = eager(xb if x is xa else xa)  # eager work between the replays
         assert other[2].numel() == 1
+    chain.check()  # no layer launch of the eager steps or the replays abandoned a wait
+    assert B.decode_timeouts(chain.ws) == 0
+
+
+def test_decode_stack_timeout_word_stays_zero(B):
+    """A 6-layer stack, 4 steps enqueued back to back on one workspace: the abandoned-wait
+    counter stays 0 (every workgroup of every launch was resident and saw every word)."""
+    say("decode stack: timeout word after back-to-back steps")
+    stack = workloads.DecodeStack(seed=97, n_layers=6, n_steps=4, device=DEV)
+    for s in range(4):
+        stack.step(s)
+    stack.check()
+    assert B.decode_timeouts(stack.ws) == 0

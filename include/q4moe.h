@@ -191,6 +191,21 @@ int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int o
                    q4moe_stream stream);
 
 /*
+ * moe_ffn_decode for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments, result
+ * and kernels, without a workspace: the call uses a fixed scratch array of 1 MiB
+ * inside the library (one per device, held until the process ends; zero at load,
+ * and every call leaves it ready for the next).  The call allocates nothing.
+ * Layers whose Q4MOE_OP_FFN_DECODE workspace would exceed 1 MiB return
+ * Q4MOE_EUNSUPPORTED (no layer that moe_ffn_decode takes needs that much).  All calls on one device share the array: calls that
+ * overlap on one device (on different streams without ordering) race and give
+ * wrong results.  Its abandoned-wait counter is internal (use moe_ffn_decode to
+ * read one).
+ */
+int moe_ffn_decode_noalloc(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int out_dtype,
+                           int32_t* ids_out, float* w_out, q4moe_stream stream);
+
+/*
  * B tokens, one per request, through the MoE layer in one decode step
  * (lily-qwen3.8-flash-next, "Running it": up to four requests by default
  * decode together), 1 <= B <= 8: row b of Y equals moe_ffn_decode on X[b] up

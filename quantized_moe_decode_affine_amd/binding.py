@@ -20,7 +20,8 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 OUT_F32, OUT_BF16, OUT_BF16_RESIDUAL = 0, 1, 2  # residual: bf16(x + y), moe_ffn_decode only
 OP_GEMV, OP_GEMM, OP_ROUTE, OP_PERMUTE, OP_FFN_DECODE, OP_FFN_PREFILL, OP_LMHEAD, OP_FFN_DECODE_BATCH = range(8)
 
-EXPORTS = ("q4_gemv", "q4_gemm", "moe_route_topk", "moe_permute", "moe_ffn_decode", "moe_ffn_decode_batch",
+EXPORTS = ("q4_gemv", "q4_gemm", "moe_route_topk", "moe_permute", "moe_ffn_decode", "moe_ffn_decode_noalloc",
+           "moe_ffn_decode_batch",
            "moe_ffn_prefill", "lmhead_argmax", "q4moe_workspace_bytes", "q4moe_strerror")
 
 
@@ -64,6 +65,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "moe_route_topk": [vp, i32, i32, vp, i64, i32, vp, vp, vp, sz, vp],
         "moe_permute": [vp, i64, i32, i32, vp, vp, vp, vp, sz, vp],
         "moe_ffn_decode": [pl, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp],
+        "moe_ffn_decode_noalloc": [pl, vp, vp, ctypes.c_int, vp, vp, vp],
         "moe_ffn_decode_batch": [pl, vp, i64, vp, ctypes.c_int, vp, vp, vp, sz, vp],
         "moe_ffn_prefill": [pl, vp, i64, vp, ctypes.c_int, vp, sz, vp],
         "lmhead_argmax": [pm, vp, i64, vp, vp, vp, sz, vp],
@@ -273,6 +275,16 @@ def moe_ffn_decode(layer: DeviceLayer, x: torch.Tensor, out_dtype: int = OUT_F32
                                                            _stream()))
     if own:
         check_decode_workspace(ws)
+    return y
+
+
+def moe_ffn_decode_noalloc(layer: DeviceLayer, x: torch.Tensor, out_dtype: int = OUT_F32, out=None,
+                           ids_out: Optional[torch.Tensor] = None, w_out: Optional[torch.Tensor] = None):
+    """moe_ffn_decode on the library's fixed scratch array (no workspace, nothing allocated
+    by the call; `out` must be given for that)."""
+    y = _out((layer.hidden,), out_dtype, x.device, out)
+    _check("moe_ffn_decode_noalloc", load_library().moe_ffn_decode_noalloc(
+        ctypes.byref(layer.struct), _ptr(x), _ptr(y), out_dtype, _ptr(ids_out), _ptr(w_out), _stream()))
     return y
 
 

@@ -245,6 +245,33 @@ int moe_ffn_decode(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int o
   }
 }
 
+int moe_ffn_decode_noalloc(const q4moe_layer* layer, const q4moe_bf16* x, void* y, int out_dtype, int32_t* ids_out,
+                           float* w_out, q4moe_stream stream) {
+  try {
+    q4moe::DecodeLayer d;
+    const int st = layer_check(layer, &d);
+    if (st != Q4MOE_OK) return st;
+    const bool residual = out_dtype == Q4MOE_OUT_BF16_RESIDUAL;
+    if (!x || !aligned(x, 16) || !(residual ? y && aligned(y, 16) : out_ok(y, out_dtype))) return Q4MOE_EINVAL;
+    {  // y must not overlap x
+      const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+      const uintptr_t xe = xb + (uintptr_t)d.hidden * 2, ye = yb + (uintptr_t)d.hidden * (out_dtype == Q4MOE_OUT_F32 ? 4 : 2);
+      if (xb < ye && yb < xe) return Q4MOE_EINVAL;
+    }
+    if (q4moe::decode_lds_bytes(d) > kMaxDynLds) return Q4MOE_EUNSUPPORTED;
+    // the layer's workspace must fit the fixed scratch array
+    if (q4moe::decode_workspace_bytes(d.hidden, d.inter, d.n_experts, d.top_k) > q4moe::kNoAllocScratchBytes)
+      return Q4MOE_EUNSUPPORTED;
+    if (!q4moe::decode_fits(d)) return Q4MOE_EUNSUPPORTED;
+    void* scratch = nullptr;
+    if (q4moe::noalloc_scratch(&scratch) != hipSuccess) return Q4MOE_EHIP;
+    const int mode = residual ? q4moe::kOutBf16Residual : out_dtype == Q4MOE_OUT_BF16 ? q4moe::kOutBf16 : q4moe::kOutF32;
+    return hip_status(q4moe::run_moe_ffn_decode(d, x, y, mode, ids_out, w_out, scratch, (hipStream_t)stream));
+  } catch (...) {
+    return Q4MOE_EHIP;
+  }
+}
+
 int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t B, void* Y, int out_dtype,
                          int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
                          q4moe_stream stream) {

@@ -32,6 +32,8 @@
 #include "topk.h"
 #include "vecstage.h"
 
+#include <mutex>
+
 namespace q4moe {
 
 namespace {
@@ -1051,6 +1053,32 @@ bool decode_fits(const DecodeLayer& L) {
                   per_cu >= 1;
   if (ncache < 32) cache[ncache++] = Entry{dev, kern, lds, ok};
   return ok;
+}
+
+// ---- the no-allocation form: the workspace is a file-scope device array.
+// Each device that runs the library holds its own copy of `scratch` until the process
+// ends; host code uses the per-device address from hipGetSymbolAddress (the array's
+// name in host code is only a stand-in).  The array starts as zeros, which is the state
+// the decode workspace needs before its first use; every call leaves it ready for the
+// next one.  Calls on one device share it, so calls that overlap on one device race.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_mode, int32_t* ids_out,

@@ -56,6 +56,11 @@ bool decode_fits(const DecodeLayer& L);
 enum { kOutF32 = 0, kOutBf16 = 1, kOutBf16Residual = 2 };
 hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, int out_mode, int32_t* ids_out,
                               float* w_out, void* ws, hipStream_t stream);
+// The no-allocation decode form's scratch: a file-scope device array of this many
+// bytes; *out receives its address on the current device (taken once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;  // more than any layer the decode kernel takes needs (its LDS bounds the slots x intermediate)
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void** out);
 
 // ---- batched decode, 1..kMaxBatch tokens (decode_batch.hip)
 constexpr int kMaxBatch = 8;

@@ -71,8 +71,9 @@ enum {
  * matrices of the same shape.  8-bit codes: uint32 [count][n][k/4], code j of a
  * row in byte j%4 of word j/4 (least significant first), same groups and
  * w = scale*q + bias.  q4_gemv and lmhead_argmax take 8-bit matrices, the layer
- * calls an 8-bit router (router_q8) and moe_ffn_decode an 8-bit shared expert;
- * the other calls return Q4MOE_EUNSUPPORTED for them. */
+ * calls an 8-bit router (router_q8) and an 8-bit shared expert, and
+ * moe_route_topk_q8 an 8-bit router; the other calls return Q4MOE_EUNSUPPORTED
+ * for them. */
 typedef struct {
   const uint32_t* codes;
   const q4moe_bf16* scales;
@@ -95,12 +96,11 @@ typedef struct {
  * n_experts x hidden, bits 8: the benchmark checkpoint's affine Q8 router-gate
  * exceptions, "2026-09-02: Lily vs MLX 0.32.2", "Hardware and software"), and
  * `router` may be null.  moe_ffn_decode, moe_ffn_decode_batch and moe_ffn_prefill
- * all take an 8-bit router (moe_route_topk takes a bf16 router only).  The
+ * all take an 8-bit router (the standalone router: moe_route_topk_q8).  The
  * shared expert's three matrices may be 8-bit together (the q4-xl conversion
- * keeps it at 8 bits: "lily-qwen3.8-flash-next" README, "The model"); only
- * moe_ffn_decode takes that form (moe_ffn_prefill and moe_ffn_decode_batch
- * return Q4MOE_EUNSUPPORTED; a mix of 4- and 8-bit shared matrices is
- * Q4MOE_EUNSUPPORTED everywhere).  Routed experts are 4-bit.
+ * keeps it at 8 bits: "lily-qwen3.8-flash-next" README, "The model"); the layer
+ * calls take that form (a mix of 4- and 8-bit shared matrices is
+ * Q4MOE_EUNSUPPORTED).  Routed experts are 4-bit.
  */
 typedef struct {
   int32_t hidden;
@@ -112,8 +112,7 @@ typedef struct {
   q4moe_matrix sh_gate, sh_up, sh_down;
   q4moe_matrix router_q8;  /* codes null: the bf16 router is used */
   const q4moe_bf16* sh_gate_w;  /* null, or bf16 [hidden]: the shared expert is weighted by
-                                   sigmoid(sh_gate_w . x) (moe_ffn_decode and moe_ffn_prefill;
-                                   moe_ffn_decode_batch returns Q4MOE_EUNSUPPORTED) */
+                                   sigmoid(sh_gate_w . x) in every layer call */
 } q4moe_layer;
 
 /*
@@ -153,6 +152,18 @@ int q4_gemm(const q4moe_matrix* W, const q4moe_bf16* X, int64_t m, void* Y, int 
 int moe_route_topk(const q4moe_bf16* router, int32_t n_experts, int32_t hidden,
                    const q4moe_bf16* X, int64_t T, int32_t top_k, int32_t* ids, float* weights,
                    void* workspace, size_t workspace_bytes, q4moe_stream stream);
+
+/*
+ * moe_route_topk with the benchmark checkpoint's affine-Q8 router gate
+ * ("2026-09-02: Lily vs MLX 0.32.2", "Hardware and software": the Q4 checkpoint
+ * keeps its router gates at 8 bits): router_q8 is an 8-bit matrix (bits 8,
+ * count 1) of n = n_experts rows by k = hidden columns, its logits
+ * logits[t][e] = sum_j (scale*q + bias)[e][j] X[t][j] in fp32, the rest as
+ * moe_route_topk.  The same workspace (Q4MOE_OP_ROUTE with n_experts).
+ */
+int moe_route_topk_q8(const q4moe_matrix* router_q8, const q4moe_bf16* X, int64_t T, int32_t top_k,
+                      int32_t* ids, float* weights, void* workspace, size_t workspace_bytes,
+                      q4moe_stream stream);
 
 /*
  * Stable counting sort of the T*top_k rows r = t*top_k + slot by expert id

@@ -20,7 +20,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 OUT_F32, OUT_BF16, OUT_BF16_RESIDUAL = 0, 1, 2  # residual: bf16(x + y), moe_ffn_decode only
 OP_GEMV, OP_GEMM, OP_ROUTE, OP_PERMUTE, OP_FFN_DECODE, OP_FFN_PREFILL, OP_LMHEAD, OP_FFN_DECODE_BATCH = range(8)
 
-EXPORTS = ("q4_gemv", "q4_gemm", "moe_route_topk", "moe_permute", "moe_ffn_decode", "moe_ffn_decode_noalloc",
+EXPORTS = ("q4_gemv", "q4_gemm", "moe_route_topk", "moe_route_topk_q8", "moe_permute", "moe_ffn_decode", "moe_ffn_decode_noalloc",
            "moe_ffn_decode_batch",
            "moe_ffn_prefill", "lmhead_argmax", "q4moe_workspace_bytes", "q4moe_strerror")
 
@@ -63,6 +63,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "q4_gemv": [pm, vp, vp, ctypes.c_int, vp],
         "q4_gemm": [pm, vp, i64, vp, ctypes.c_int, vp, sz, vp],
         "moe_route_topk": [vp, i32, i32, vp, i64, i32, vp, vp, vp, sz, vp],
+        "moe_route_topk_q8": [pm, vp, i64, i32, vp, vp, vp, sz, vp],
         "moe_permute": [vp, i64, i32, i32, vp, vp, vp, vp, sz, vp],
         "moe_ffn_decode": [pl, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp],
         "moe_ffn_decode_noalloc": [pl, vp, vp, ctypes.c_int, vp, vp, vp],
@@ -224,6 +225,27 @@ def moe_route_topk(router: torch.Tensor, X: torch.Tensor, top_k: int, ws: Option
     _check("moe_route_topk", load_library().moe_route_topk(_ptr(router), E, H, _ptr(X), T, top_k, _ptr(ids),
                                                            _ptr(w), _ptr(ws), ws.numel(), _stream()))
     return ids, w
+
+
+def moe_route_topk_q8(router_q8: DeviceQ4, X: torch.Tensor, top_k: int, ws: Optional[torch.Tensor] = None):
+    """Top-k routing through an affine-Q8 router matrix (n_experts x hidden, 8-bit codes)."""
+    E = router_q8.n
+    T = X.shape[0]
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=X.device)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = workspace(load_library().q4moe_workspace_bytes(
+            OP_ROUTE, ctypes.byref(q4moe_layer(router_q8.k, 0, E, top_k)), None, T), X.device)
+    _check("moe_route_topk_q8", load_library().moe_route_topk_q8(ctypes.byref(router_q8.struct), _ptr(X), T, top_k,
+                                                                 _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream()))
+    return ids, w
+
+
+def gpu_routing(layer: DeviceLayer, X: torch.Tensor):
+    """The layer's routing of the rows X through its own router (bf16 or 8-bit)."""
+    if layer.router_q8 is not None:
+        return moe_route_topk_q8(layer.router_q8, X, layer.top_k)
+    return moe_route_topk(layer.router, X, layer.top_k)
 
 
 def moe_permute(ids: torch.Tensor, n_experts: int, ws: Optional[torch.Tensor] = None):

@@ -204,6 +204,25 @@ int moe_route_topk(const q4moe_bf16* router, int32_t n_experts, int32_t hidden, 
   }
 }
 
+int moe_route_topk_q8(const q4moe_matrix* router_q8, const q4moe_bf16* X, int64_t T, int32_t top_k, int32_t* ids,
+                      float* weights, void* workspace, size_t workspace_bytes, q4moe_stream stream) {
+  try {
+    if (!matrix_ok(router_q8) || !is_q8(*router_q8) || router_q8->count != 1) return Q4MOE_EINVAL;
+    if (!X || !aligned(X, 16) || !ids || !weights || T < 0) return Q4MOE_EINVAL;
+    const int64_t E = router_q8->n, H = router_q8->k;
+    if (top_k < 1 || top_k > E) return Q4MOE_EINVAL;
+    if (E > 1024 || top_k > 32 || H > kMaxGemvK || T * top_k > kMaxRows32) return Q4MOE_EUNSUPPORTED;
+    if (T == 0) return Q4MOE_OK;
+    if (!workspace || workspace_bytes < q4moe::route_workspace_bytes(T, (int)E) || !aligned(workspace, 256))
+      return Q4MOE_EWORKSPACE;
+    const Q4Mat m = to_mat(*router_q8);
+    return hip_status(q4moe::run_route_topk(nullptr, (int)E, (int)H, X, T, top_k, ids, weights, workspace,
+                                            (hipStream_t)stream, &m));
+  } catch (...) {
+    return Q4MOE_EHIP;
+  }
+}
+
 int moe_permute(const int32_t* ids, int64_t T, int32_t top_k, int32_t n_experts, int32_t* offsets,
                 int32_t* sorted_rows, int32_t* inv_rows, void* workspace, size_t workspace_bytes,
                 q4moe_stream stream) {
@@ -280,7 +299,6 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || B < 1 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
-    if (d.sh_gate_w || d.sh_q8) return Q4MOE_EUNSUPPORTED;  // gate: decode and prefill; 8-bit shared: decode
     if (B > q4moe::kMaxBatch || !q4moe::decode_batch_supported(d, (int)B, kMaxDynLds)) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
@@ -298,7 +316,6 @@ int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, vo
     const int st = layer_check(layer, &d);
     if (st != Q4MOE_OK) return st;
     if (!X || !aligned(X, 16) || T < 0 || !out_ok(Y, out_dtype)) return Q4MOE_EINVAL;
-    if (d.sh_q8) return Q4MOE_EUNSUPPORTED;  // the grouped GEMM reads 4-bit experts only
     if (T * (d.top_k + 1) > kMaxRows32) return Q4MOE_EUNSUPPORTED;
     if (T == 0) return Q4MOE_OK;
     const size_t need =

@@ -53,7 +53,7 @@ struct BatchParams {
   int B;
   float* logits;      // [B][E]
   BatchPlan* plan;
-  float* wts;         // [B][k]
+  float* wts;         // [B][k+1]: routing weights, then the shared expert's weight
   float* act;         // [B][nslot][I]
   void* y;            // [B][H]
   int out_bf16;
@@ -147,10 +147,28 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void batch_plan_kernel(BatchPa
     const int b = wv;
     wave_topk_sorted<V>(p.logits + (size_t)b * E, E, k, s_id[b], s_w[b]);
     if (lane < k) {
-      p.wts[b * k + lane] = s_w[b][lane];
+      p.wts[b * (k + 1) + lane] = s_w[b][lane];
       if (p.ids_out) p.ids_out[b * k + lane] = s_id[b][lane];
       if (p.w_out) p.w_out[b * k + lane] = s_w[b][lane];
     }
+    // the shared expert's weight: 1, or sigmoid(sh_gate_w . x_b) when the layer has the gate
+    float sw = 1.0f;
+    if (p.L.sh_gate_w) {
+      const int H = p.L.hidden;
+      const uint4* gw = reinterpret_cast<const uint4*>(p.L.sh_gate_w);
+      const uint4* gx = reinterpret_cast<const uint4*>(p.X + (size_t)b * H);
+      float d0 = 0.f, d1 = 0.f;
+      for (int c = lane; c < (H >> 3); c += kWave) {
+        const uint4 a = gw[c], x = gx[c];
+        d0 = dot2_bf16(a.x, x.x, d0);
+        d1 = dot2_bf16(a.y, x.y, d1);
+        d0 = dot2_bf16(a.z, x.z, d0);
+        d1 = dot2_bf16(a.w, x.w, d1);
+      }
+      const float d = group_sum_rt(d0 + d1, 6);
+      sw = 1.0f / (1.0f + __expf(-d));
+    }
+    if (lane == 0) p.wts[b * (k + 1) + k] = sw;
   }
   for (int i = threadIdx.x; i < kBitWords; i += blockDim.x) s_bits[i] = 0u;
   __syncthreads();
@@ -197,6 +215,65 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void batch_plan_kernel(BatchPa
 }
 
 // ---------------------------------------------------------------- launch 3
+// The 8-bit shared expert's gate/up rows i0 + lane/8 of this workgroup's block (planned
+// expert d; every token chose it): lane takes groups lane%8, lane%8 + 8, ...; a group is 64
+// code bytes per matrix, dotted with the tokens' staged x as exact bf16 code pairs.
+__device__ __forceinline__ void batch_gate_up_q8_shared(const BatchParams& p, int rblk, int d) {
+  extern __shared__ __align__(16) uint32_t smem[];
+  const int H = p.L.hidden, I = p.L.inter, k = p.L.top_k, B = p.B;
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const int CH = H >> 5, G = H >> 6;
+  const int i0 = rblk * kGateUpRows + wv * 8;
+  const int row = min(i0 + (lane >> 3), I - 1), gl = lane & 7;
+  const uint4* gq = reinterpret_cast<const uint4*>(p.L.sh_gate.codes) + (int64_t)row * (H >> 4);
+  const uint4* uq = reinterpret_cast<const uint4*>(p.L.sh_up.codes) + (int64_t)row * (H >> 4);
+  const uint16_t* gs = p.L.sh_gate.scales + (int64_t)row * G;
+  const uint16_t* gb = p.L.sh_gate.biases + (int64_t)row * G;
+  const uint16_t* us = p.L.sh_up.scales + (int64_t)row * G;
+  const uint16_t* ub = p.L.sh_up.biases + (int64_t)row * G;
+  // stage x of every token (all chose the shared expert)
+  constexpr int ST = chunk_stride<1>();
+  uint32_t* vp = smem;
+  float* vs = reinterpret_cast<float*>(vp + (size_t)B * CH * ST);
+  for (int i = threadIdx.x; i < B * CH; i += blockDim.x) {
+    const int b = i / CH, c = i - b * CH;
+    stage_bf16_chunk(p.X + (size_t)b * H, c, vp + (size_t)i * ST, vs + i);
+  }
+  __syncthreads();
+  float ag[kMaxBatch], au[kMaxBatch];
+#pragma unroll
+  for (int t = 0; t < kMaxBatch; ++t) ag[t] = au[t] = 0.f;
+  for (int g = gl; g < G; g += 8) {
+    uint4 cg[4], cu[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      cg[q] = gq[4 * g + q];
+      cu[q] = uq[4 * g + q];
+    }
+    const float sg = bf16_bits_to_f32(gs[g]), bg = bf16_bits_to_f32(gb[g]);
+    const float su = bf16_bits_to_f32(us[g]), bu = bf16_bits_to_f32(ub[g]);
+#pragma unroll
+    for (int t = 0; t < kMaxBatch; ++t) {
+      if (t >= B) break;
+      const uint32_t* v = vp + ((size_t)t * CH + 2 * g) * ST;
+      const float vsum = vs[t * CH + 2 * g] + vs[t * CH + 2 * g + 1];
+      const float pg = q8_chunk_pdot<1>(cg[0], cg[1], v) + q8_chunk_pdot<1>(cg[2], cg[3], v + ST);
+      const float pu = q8_chunk_pdot<1>(cu[0], cu[1], v) + q8_chunk_pdot<1>(cu[2], cu[3], v + ST);
+      ag[t] += fmaf(sg, pg, bg * vsum);
+      au[t] += fmaf(su, pu, bu * vsum);
+    }
+  }
+  const int nslot = k + 1;
+  const int i = i0 + (lane >> 3);
+#pragma unroll
+  for (int t = 0; t < kMaxBatch; ++t) {
+    if (t >= B) break;
+    const float g = group_sum_rt(ag[t], 3), u = group_sum_rt(au[t], 3);
+    if ((lane & 7) == 0 && i < I) p.act[((size_t)t * nslot + k) * I + i] = silu(g) * u;
+  }
+  (void)d;
+}
+
 __global__ __launch_bounds__(kThreads) void batch_gate_up_kernel(BatchParams p) {
   extern __shared__ __align__(16) uint32_t smem[];
   const int H = p.L.hidden, I = p.L.inter, k = p.L.top_k, B = p.B;
@@ -207,6 +284,10 @@ __global__ __launch_bounds__(kThreads) void batch_gate_up_kernel(BatchParams p) 
   if (d >= plan->n) return;  // beyond this step's experts (uniform)
   const int e = plan->expert[d];
 
+  if (e < 0 && p.L.sh_q8) {  // the shared expert in 8-bit codes
+    batch_gate_up_q8_shared(p, rblk, d);
+    return;
+  }
   // this lane's weights: row i0 + lane/8, groups lane%8 + 8q
   const Q4Mat& gm = e >= 0 ? p.L.gate : p.L.sh_gate;
   const Q4Mat& um = e >= 0 ? p.L.up : p.L.sh_up;
@@ -327,7 +408,9 @@ __global__ __launch_bounds__(kThreads) void batch_down_kernel(BatchParams p) {
     if (lane == 0) s_nlist = cnt;
   }
   __syncthreads();
-  const int nplan = s_nlist;
+  // an 8-bit shared expert (the plan's last entry, chosen by every token) is taken apart below
+  const bool q8sh = p.L.has_shared && p.L.sh_q8;
+  const int nplan = s_nlist - (q8sh ? 1 : 0);
 
   // lane: row n0 + lane / 8, groups sub, sub + 8, ...; wave w takes planned experts w, w + 4, ...
   const int sub = lane & (kDownLanes - 1), rsub = lane / kDownLanes;
@@ -360,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void batch_down_kernel(BatchParams p) {
 
   for (int i = threadIdx.x; i < nb * (k + 1); i += blockDim.x) {
     const int b = i / (k + 1), j = i - b * (k + 1);
-    s_w[b][j] = j < k ? p.wts[(b0 + b) * k + j] : 1.0f;
+    s_w[b][j] = p.wts[(b0 + b) * (k + 1) + j];  // slot k: the shared expert's weight
   }
   // stage the SwiGLU outputs of these tokens: [nb][nslot] x ([CI][ST2] pairs, [CI] sums)
   constexpr int ST = chunk_stride<2>();
@@ -403,6 +486,25 @@ __global__ __launch_bounds__(kThreads) void batch_down_kernel(BatchParams p) {
         const int dd = wv + kWaves * (q0 + q);
         if (dd >= nplan) break;
         for (int g = sub + kDownLanes; g < GI; g += kDownLanes) apply(dd, g, load_row(dd, g));
+      }
+    }
+  }
+  if (q8sh && wv == nplan % kWaves) {
+    // 8-bit shared down row n: group g is 64 code bytes, chunks 2g and 2g + 1 of slot k
+    const uint4* cr = reinterpret_cast<const uint4*>(p.L.sh_down.codes) + (int64_t)n * (I >> 4);
+    const uint16_t* sr = p.L.sh_down.scales + (int64_t)n * GI;
+    const uint16_t* br = p.L.sh_down.biases + (int64_t)n * GI;
+    for (int g = sub; g < GI; g += kDownLanes) {
+      const uint4 c0 = cr[4 * g], c1 = cr[4 * g + 1], c2 = cr[4 * g + 2], c3 = cr[4 * g + 3];
+      const float sc = bf16_bits_to_f32(sr[g]), bi = bf16_bits_to_f32(br[g]);
+#pragma unroll
+      for (int b = 0; b < kMaxBatch; ++b) {
+        if (b >= nb) break;
+        const size_t vi = ((size_t)b * nslot + k) * CI + 2 * g;
+        const uint32_t* v = ap + vi * ST;
+        const float part = fmaf(sc, q8_chunk_pdot<2>(c0, c1, v) + q8_chunk_pdot<2>(c2, c3, v + ST),
+                                bi * (as[vi] + as[vi + 1]));
+        acc[b] = fmaf(s_w[b][k], part, acc[b]);
       }
     }
   }
@@ -456,7 +558,7 @@ void launch_route_plan(const BatchParams& p, int grid, hipStream_t stream) {
 }  // namespace
 
 size_t decode_batch_workspace_bytes(int n_experts, int top_k, int inter, int B) {
-  return align256((size_t)B * n_experts * 4) + align256(sizeof(BatchPlan)) + align256((size_t)B * top_k * 4) +
+  return align256((size_t)B * n_experts * 4) + align256(sizeof(BatchPlan)) + align256((size_t)B * (top_k + 1) * 4) +
          align256((size_t)B * (top_k + 1) * inter * 4);
 }
 
@@ -477,7 +579,7 @@ hipError_t run_moe_ffn_decode_batch(const DecodeLayer& L, const uint16_t* X, int
   p.plan = reinterpret_cast<BatchPlan*>(w);
   w += align256(sizeof(BatchPlan));
   p.wts = reinterpret_cast<float*>(w);
-  w += align256((size_t)B * L.top_k * 4);
+  w += align256((size_t)B * (L.top_k + 1) * 4);
   p.act = reinterpret_cast<float*>(w);
   p.y = y;
   p.out_bf16 = out_bf16;

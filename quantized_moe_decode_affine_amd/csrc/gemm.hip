@@ -105,6 +105,23 @@ __device__ __forceinline__ uint4 codes_to_operand(uint32_t w, f16x2_t s2, f16x2_
                     scaled_pair(w, 12, s2, m2));
 }
 
+// The same for 8-bit codes: the 8 codes of a block are bytes 0..3 of w0 and of w1, and
+// the pair (q_j, q_{j+4}) is byte j of each, placed by one v_perm into the low bytes of
+// an fp16 pair; 1024 + q is exact in fp16 for q <= 255, and s*q (at most 16
+// significant bits) is rounded once, as for 4-bit codes.
+__device__ __forceinline__ uint32_t scaled_pair8(uint32_t w0, uint32_t w1, uint32_t sel, f16x2_t s2, f16x2_t m2) {
+  const uint32_t p = __builtin_amdgcn_perm(w1, w0, sel) | magic_pair_f16_reg();
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, p), s2, m2));
+}
+
+// selector of byte j of the low source and byte j of the high source, zero bytes between
+constexpr uint32_t perm_pair_sel(int j) { return (uint32_t)j | (0x0Cu << 8) | ((4u + j) << 16) | (0x0Cu << 24); }
+
+__device__ __forceinline__ uint4 codes8_to_operand(uint32_t w0, uint32_t w1, f16x2_t s2, f16x2_t m2) {
+  return make_uint4(scaled_pair8(w0, w1, perm_pair_sel(0), s2, m2), scaled_pair8(w0, w1, perm_pair_sel(1), s2, m2),
+                    scaled_pair8(w0, w1, perm_pair_sel(2), s2, m2), scaled_pair8(w0, w1, perm_pair_sel(3), s2, m2));
+}
+
 // bf16 bits -> fp16 (exact for magnitudes in fp16's normal range).
 __device__ __forceinline__ _Float16 bf16_bits_to_f16(uint32_t bits) { return (_Float16)bf16_bits_to_f32(bits); }
 
@@ -115,11 +132,16 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xF << 8); }
 
 // Pipeline depth (K groups in flight) and per-stage vector-memory ops per thread:
-// MB A-tile LDS loads, 2 B-code LDS loads, 2 scale loads.
+// MB A-tile LDS loads, 2 (4-bit) or 4 (8-bit) B-code LDS loads, 2 scale loads.
 constexpr int kStages = 3;  // the stage arrays below are written out for exactly 3
-constexpr int kOpsPerStage = MB + 4;
+template <int kBits> constexpr int ops_per_stage() { return MB + 2 * (kBits / 4) + 2; }
 constexpr int A_STAGE_BYTES = BM * 128;           // BM rows x one 64-column group of fp16
-constexpr int B_STAGE_BYTES = 4 * 2 * 64 * 16;    // 4 waves x 2 column blocks x 64 lanes x 16 bytes
+// 4 waves x 2 column blocks x 64 lanes x 16 bytes (4-bit codes) or 32 bytes (8-bit codes)
+template <int kBits> constexpr int b_stage_bytes() { return 4 * 2 * 64 * 16 * (kBits / 4); }
+
+// Which tiles of the table a launch takes: all, the routed experts' only, or the extra
+// segment's (shared expert) only.
+enum TileSel { TILES_ALL = 0, TILES_ROUTED = 1, TILES_EXTRA = 2 };
 
 // Swizzled slot of (row r, 16-byte word w) in an A stage.  A 128-bit LDS read
 // serves 16 lanes (16 rows here) per cycle from 64 four-byte banks, i.e. two
@@ -129,7 +151,12 @@ constexpr int B_STAGE_BYTES = 4 * 2 * 64 * 16;    // 4 waves x 2 column blocks x
 __device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int a_slot(int r, int w) { return r * 8 + (w ^ a_swz(r)); }
 
-__global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
+// kBits: the code width of the weights this launch reads (8: the extra segment only).
+template <int kBits, int kSel>
+__device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
+  constexpr int B_STAGE_BYTES = b_stage_bytes<kBits>();
+  constexpr int kOpsPerStage = ops_per_stage<kBits>();
+  constexpr int kBW = kBits / 4;  // 16-byte code words per lane, column block and group
   // One LDS array per pipeline stage: distinct variables let the compiler see
   // that reading one stage does not depend on the DMA still filling another,
   // so it does not wait for every outstanding load before each LDS read.
@@ -161,6 +188,8 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
     rows = (int)min<int64_t>(BM, p.extra_rows - row0);
   }
   if (seg == -2) return;
+  if (kSel == TILES_ROUTED && seg < 0) return;
+  if (kSel == TILES_EXTRA && seg >= 0) return;
 
   // ---- source row of each tile row (padding rows repeat the last real row; their
   // outputs are dropped).  Thread r < BM also loads its row's routing weight and
@@ -197,7 +226,8 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
     col[nb] = swiglu ? slice * 128 + wave * 32 + ln : slice * BN + wave * 64 + nb * 32 + ln;
     const int64_t wrow = min(col[nb], p.N - 1);
     const Q4Mat& Mx = nb == 0 ? M0 : M1;
-    bcodes[nb] = reinterpret_cast<const uint4*>(Mx.codes + oc + wrow * (p.K >> 3)) + lh;
+    // this lane's half of a group: 32 codes = 16 bytes (4-bit) or 32 bytes (8-bit)
+    bcodes[nb] = reinterpret_cast<const uint4*>(Mx.codes + oc + wrow * (p.K * kBits / 32)) + kBW * lh;
     bscale[nb] = Mx.scales + og + wrow * p.G;
     bbias[nb] = Mx.biases + og + wrow * p.G;
   }
@@ -221,7 +251,10 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       __builtin_amdgcn_global_load_lds(a_ptr[i] + g * 64, stage_a(st) + (wave * MB + i) * 1024, 16, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
-      __builtin_amdgcn_global_load_lds(bcodes[nb] + 2 * g, stage_b(st) + (wave * 2 + nb) * 1024, 16, 0, 0);
+#pragma unroll
+      for (int h = 0; h < kBW; ++h)
+        __builtin_amdgcn_global_load_lds(bcodes[nb] + 2 * kBW * g + h, stage_b(st) + ((wave * 2 + nb) * kBW + h) * 1024,
+                                         16, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) sc[nb] = ld_global_u16(bscale[nb] + g);
   };
@@ -268,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
 
       const uint8_t* sa = stage_a(st);
-      const uint8_t* sb = stage_b(st) + wave * 2 * 1024 + lane * 16;
+      const uint8_t* sb = stage_b(st) + wave * 2 * kBW * 1024 + lane * 16;
       // This wave's B codes first, then A fragments double-buffered over row
       // blocks: block 0's reads are in flight during the B conversion, block
       // mb+1's during block mb's MFMAs.
@@ -278,8 +311,11 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
         for (int s4 = 0; s4 < 4; ++s4)
           dst[s4] = *reinterpret_cast<const uint4*>(sa + a_slot(mb * 32 + ln, 4 * lh + s4) * 16);
       };
-      const uint4 rb0 = *reinterpret_cast<const uint4*>(sb);
-      const uint4 rb1 = *reinterpret_cast<const uint4*>(sb + 1024);
+      uint4 rb[2][kBW];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int h = 0; h < kBW; ++h) rb[nb][h] = *reinterpret_cast<const uint4*>(sb + (nb * kBW + h) * 1024);
       read_a(0, af[0]);
       f16x2_t s2[2], m2[2];
 #pragma unroll
@@ -291,9 +327,19 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       }
       uint4 bop[2][4];  // this group's B operands, converted once, used by every row block
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        bop[0][s4] = codes_to_operand(s4 == 0 ? rb0.x : s4 == 1 ? rb0.y : s4 == 2 ? rb0.z : rb0.w, s2[0], m2[0]);
-        bop[1][s4] = codes_to_operand(s4 == 0 ? rb1.x : s4 == 1 ? rb1.y : s4 == 2 ? rb1.z : rb1.w, s2[1], m2[1]);
+      for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (kBits == 4) {
+          const uint4 r = rb[nb][0];
+          bop[nb][0] = codes_to_operand(r.x, s2[nb], m2[nb]);
+          bop[nb][1] = codes_to_operand(r.y, s2[nb], m2[nb]);
+          bop[nb][2] = codes_to_operand(r.z, s2[nb], m2[nb]);
+          bop[nb][3] = codes_to_operand(r.w, s2[nb], m2[nb]);
+        } else {  // 8 codes per word pair
+          bop[nb][0] = codes8_to_operand(rb[nb][0].x, rb[nb][0].y, s2[nb], m2[nb]);
+          bop[nb][1] = codes8_to_operand(rb[nb][0].z, rb[nb][0].w, s2[nb], m2[nb]);
+          bop[nb][2] = codes8_to_operand(rb[nb][1].x, rb[nb][1].y, s2[nb], m2[nb]);
+          bop[nb][3] = codes8_to_operand(rb[nb][1].z, rb[nb][1].w, s2[nb], m2[nb]);
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
@@ -423,6 +469,15 @@ __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) {
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) { grouped_gemm_body<4, TILES_ALL>(p); }
+__global__ __launch_bounds__(256, 2) void grouped_q4_gemm_routed_kernel(GemmParams p) {
+  grouped_gemm_body<4, TILES_ROUTED>(p);
+}
+// the extra segment with 8-bit codes: its doubled code stages take one workgroup per CU
+__global__ __launch_bounds__(256, 1) void grouped_q8_gemm_extra_kernel(GemmParams p) {
+  grouped_gemm_body<8, TILES_EXTRA>(p);
 }
 
 // Load 8 consecutive elements of a row as fp32 (bf16 bits or fp32 input).
@@ -564,14 +619,21 @@ int pad16(int g) { return (g + 15) & ~15; }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream) {
+// extra_q8: the extra segment (shared expert) holds 8-bit codes; it then takes a launch
+// of its own after the routed tiles'.
+hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream, bool extra_q8 = false) {
   p.bs_vec = p.G % 8 == 0;
   for (const Q4Mat* m : {&p.W, &p.W2, &p.X, &p.X2})
     if (m->scales && (!aligned16(m->scales) || !aligned16(m->biases))) p.bs_vec = 0;
   p.n_tiles = (int)max_tiles;
   const int64_t tiles_rounded = (max_tiles + kXcd - 1) / kXcd * kXcd;
   const int64_t blocks = tiles_rounded * p.n_slices;
-  hipLaunchKernelGGL(grouped_q4_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  if (!extra_q8) {
+    hipLaunchKernelGGL(grouped_q4_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(grouped_q4_gemm_routed_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(grouped_q8_gemm_extra_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -733,7 +795,8 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   p.out = w.act32;
   p.out_bf16 = 0;
   p.ldo = I;
-  e = launch_grouped(p, max_tiles, stream);
+  const bool sh_q8 = L.has_shared && L.sh_q8;
+  e = launch_grouped(p, max_tiles, stream, sh_q8);
   if (e != hipSuccess) return e;
 
   const int64_t R = P + extra;
@@ -769,7 +832,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
     if (e != hipSuccess) return e;
     d.extra_w = w.sh_gate;
   }
-  e = launch_grouped(d, max_tiles, stream);
+  e = launch_grouped(d, max_tiles, stream, sh_q8);
   if (e != hipSuccess) return e;
 
   hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * (H / 4), 256)), dim3(256), 0, stream, w.ys, w.inv, T, k, H,

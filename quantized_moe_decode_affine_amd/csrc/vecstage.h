@@ -100,6 +100,45 @@ __device__ __forceinline__ float chunk_pdot(uint4 codes, const uint32_t* vchunk)
   return p0 + p1;
 }
 
+// 8-bit codes against a staged chunk.  A code q in 0..255 is an integer of at most 8
+// significant bits, so it is exact in bfloat16 (the high half of its fp32 value); the
+// pairs (q_j, q_{j+4}) of an 8-code block (words w0 = codes 0..3, w1 = codes 4..7, byte
+// j of a word = code j) match the staged activation pairs (x_j, x_{j+4}).
+__device__ __forceinline__ void q8_block_pairs(uint32_t w0, uint32_t w1, uint32_t (&pr)[4]) {
+  // (one v_cvt_f32_ubyteN each)
+  const float a0 = (float)(w0 & 0xFFu), b0 = (float)(w1 & 0xFFu);
+  const float a1 = (float)((w0 >> 8) & 0xFFu), b1 = (float)((w1 >> 8) & 0xFFu);
+  const float a2 = (float)((w0 >> 16) & 0xFFu), b2 = (float)((w1 >> 16) & 0xFFu);
+  const float a3 = (float)(w0 >> 24), b3 = (float)(w1 >> 24);
+  // high halves of two fp32 values as one bf16 pair (lo from the first)
+  pr[0] = __builtin_amdgcn_perm(__float_as_uint(b0), __float_as_uint(a0), 0x07060302u);
+  pr[1] = __builtin_amdgcn_perm(__float_as_uint(b1), __float_as_uint(a1), 0x07060302u);
+  pr[2] = __builtin_amdgcn_perm(__float_as_uint(b2), __float_as_uint(a2), 0x07060302u);
+  pr[3] = __builtin_amdgcn_perm(__float_as_uint(b3), __float_as_uint(a3), 0x07060302u);
+}
+
+// sum over a chunk's 32 columns of q * v for 8-bit codes c (32 bytes: c0 = codes 0..15,
+// c1 = codes 16..31) against a chunk staged with NV parts.
+template <int NV>
+__device__ __forceinline__ float q8_chunk_pdot(uint4 c0, uint4 c1, const uint32_t* vchunk) {
+  const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {  // 8-code blocks
+    uint32_t pr[4];
+    q8_block_pairs(w[2 * b], w[2 * b + 1], pr);
+#pragma unroll
+    for (int part = 0; part < NV; ++part) {
+      const uint4 t = *reinterpret_cast<const uint4*>(vchunk + 16 * part + 4 * b);
+      p0 = dot2_bf16(pr[0], t.x, p0);
+      p1 = dot2_bf16(pr[1], t.y, p1);
+      p0 = dot2_bf16(pr[2], t.z, p0);
+      p1 = dot2_bf16(pr[3], t.w, p1);
+    }
+  }
+  return p0 + p1;
+}
+
 // Contribution of a group-aligned chunk pair or single chunk: scale*P' + (bias-128*scale)*sum.
 __device__ __forceinline__ float affine_term(float p, float vsum, uint32_t s_bits, uint32_t b_bits) {
   float s = bf16_bits_to_f32(s_bits);

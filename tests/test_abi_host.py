@@ -141,6 +141,27 @@ def test_ffn_rejects(lib):
     assert lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(noshared), None, 50) < need_p
 
 
+def test_route_topk_q8_rejects(lib):
+    r8 = _mat(1, 256, 2048)
+    r8.bits = 8
+    need = lib.q4moe_workspace_bytes(B.OP_ROUTE, ctypes.byref(_layer(E=256, k=8)), None, 10)
+    f = lib.moe_route_topk_q8
+    assert f(ctypes.byref(_mat(1, 256, 2048)), A, 10, 8, A, A, A, need, None) == B.EINVAL   # 4-bit codes
+    r2 = _mat(2, 256, 2048)
+    r2.bits = 8
+    assert f(ctypes.byref(r2), A, 10, 8, A, A, A, need, None) == B.EINVAL                  # count 2
+    assert f(ctypes.byref(r8), A, 10, 0, A, A, A, need, None) == B.EINVAL                  # top_k 0
+    assert f(ctypes.byref(r8), A, 10, 257, A, A, A, need, None) == B.EINVAL                # top_k > E
+    assert f(ctypes.byref(r8), A, 10, 33, A, A, A, need, None) == B.EUNSUPPORTED           # top_k > 32
+    big = _mat(1, 2048, 2048)
+    big.bits = 8
+    assert f(ctypes.byref(big), A, 10, 8, A, A, A, need, None) == B.EUNSUPPORTED           # E > 1024
+    assert f(ctypes.byref(r8), A + 8, 10, 8, A, A, A, need, None) == B.EINVAL              # X misaligned
+    assert f(ctypes.byref(r8), A, 10, 8, None, A, A, need, None) == B.EINVAL               # ids null
+    assert f(ctypes.byref(r8), A, 10, 8, A, A, A, 16, None) == B.EWORKSPACE
+    assert f(ctypes.byref(r8), A, 0, 8, A, A, None, 0, None) == B.OK                       # T = 0
+
+
 def test_decode_needs_coresident_workgroups(lib):
     """Every argument valid, but the call cannot confirm that one workgroup per CU fits on
     the device (here: no device at all): it refuses with EUNSUPPORTED and launches nothing,
@@ -252,8 +273,7 @@ def test_q8_router_layers(lib):
 
 
 def test_shared_gate_layers(lib):
-    """A shared-expert gate needs a shared expert and 16-byte alignment; the batched decode
-    call does not take one."""
+    """A shared-expert gate needs a shared expert and 16-byte alignment; every layer call takes one."""
     need_d = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE, ctypes.byref(_layer()), None, 1)
     d = lib.moe_ffn_decode
     L = _layer(sh_gate_w=A)
@@ -262,12 +282,12 @@ def test_shared_gate_layers(lib):
     assert d(ctypes.byref(_layer(shared=False, sh_gate_w=A)), A, A2, 0, None, None, A, need_d, None) == B.EINVAL
     need_p = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(L), None, 50)
     assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A2, 0, A, need_p - 1, None) == B.EWORKSPACE
-    need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(_layer()), None, 2)
-    assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b, None) == B.EUNSUPPORTED
+    need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(L), None, 2)
+    assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b - 1, None) == B.EWORKSPACE
 
 
 def test_q8_shared_expert_layers(lib):
-    """An 8-bit shared expert (all three matrices) is taken by moe_ffn_decode only; a mix of
+    """An 8-bit shared expert (all three matrices) is taken by the decode calls; a mix of
     4- and 8-bit shared matrices is rejected everywhere."""
     def q8(n, k):
         m = _mat(1, n, k)
@@ -280,8 +300,8 @@ def test_q8_shared_expert_layers(lib):
     d = lib.moe_ffn_decode
     assert d(ctypes.byref(L), A, A2, 0, None, None, A, need_d - 1, None) == B.EWORKSPACE  # valid up to the workspace
     need_p = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(L), None, 50)
-    assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A2, 0, A, need_p, None) == B.EUNSUPPORTED
-    need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(_layer()), None, 2)
-    assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b, None) == B.EUNSUPPORTED
+    assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A2, 0, A, need_p - 1, None) == B.EWORKSPACE
+    need_b = lib.q4moe_workspace_bytes(B.OP_FFN_DECODE_BATCH, ctypes.byref(L), None, 2)
+    assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b - 1, None) == B.EWORKSPACE
     mixed = _layer(sh_gate=q8(I, H), sh_up=q8(I, H))
     assert d(ctypes.byref(mixed), A, A2, 0, None, None, A, need_d, None) == B.EUNSUPPORTED

@@ -139,3 +139,18 @@ def test_decode_batch_q8_router(B, H, I, E, k, nb):
     X = np.stack([synth.hidden_vector(98, s, 0, H) for s in range(nb)])
     worst, n_exact = _check_batch(B, layer, dl, X)
     assert worst <= 2e-3 and n_exact >= nb - 1, (worst, n_exact)
+
+
+@pytest.mark.parametrize("H,I,E,k,nb,rbits,gated,sbits", [
+    (256, 128, 16, 4, 3, 16, True, 4), (256, 128, 16, 4, 8, 8, True, 8), (384, 192, 16, 4, 5, 16, False, 8),
+    (2048, 512, 256, 8, 4, 8, True, 8), (2048, 512, 256, 8, 8, 8, True, 8), (2048, 512, 256, 8, 8, 16, True, 4)])
+def test_decode_batch_checkpoint_form(B, H, I, E, k, nb, rbits, gated, sbits):
+    """Batched decode in the checkpoint's forms: the shared expert weighted by sigmoid(g . x)
+    and/or held in affine-Q8 codes, with either router; every row against the oracle."""
+    say(f"decode batch checkpoint form H={H} E={E} k={k} B={nb} router bits={rbits} gated={gated} shared bits={sbits}")
+    layer = synth.moe_layer(114, 0, H, I, E, k, router_bits=rbits, shared_gate=gated, shared_bits=sbits)
+    dl = B.DeviceLayer(layer)
+    X = synth.token_rows(114, nb, H, index=nb)
+    worst, n_exact = _check_batch(B, layer, dl, X)
+    assert worst <= TOL, worst
+    assert n_exact >= nb - 1

@@ -359,11 +359,11 @@ def _prefill_check(B, layer, dl, X, with_bf16=True):
     Xd = B.bf16_tensor(X)
     Y = B.moe_ffn_prefill(dl, Xd, 0)
     Yb = B.moe_ffn_prefill(dl, Xd, 1) if with_bf16 else None
-    ids, _ = B.moe_route_topk(dl.router, B.bf16_tensor(X), layer.top_k)
+    ids, _ = B.gpu_routing(dl, B.bf16_tensor(X))
     _sync()
     got = to_f64(Y)
     gids = ids.cpu().numpy()
-    logits = orc.router_logits(layer.router, X)
+    logits = orc.layer_router_logits(layer, X)
     r_ids, _ = orc.topk_from_logits(logits, layer.top_k)
     use = r_ids.copy()
     for t in range(X.shape[0]):
@@ -558,21 +558,36 @@ def test_decode_q8_router(B, H, I, E, k):
 
 @pytest.mark.parametrize("T,H,I,E,k", [(300, 256, 128, 16, 4), (2048, 2048, 512, 256, 8)])
 def test_prefill_q8_router(B, T, H, I, E, k):
-    """Prefill with the checkpoint's affine-Q8 router gate.  The GPU's routing is not exposed
-    by the layer call, so tokens whose oracle routing lies within the 1e-3 logit tie band are
-    left out; every other token must match the oracle on the oracle's routing."""
+    """Prefill with the checkpoint's affine-Q8 router gate: every token against the oracle,
+    on the GPU's own routing (moe_route_topk_q8) wherever it differs within the tie band."""
     say(f"prefill q8 router T={T} H={H} E={E} k={k}")
     layer = synth.moe_layer(99, 0, H, I, E, k, router_bits=8)
     dl = B.DeviceLayer(layer)
     X = synth.token_rows(99, T, H)
-    Y = B.moe_ffn_prefill(dl, B.bf16_tensor(X), 0)
+    err, worst = _prefill_check(B, layer, dl, X)
+    assert err <= REL_L2_TOL, err
+    assert worst <= 2 * REL_L2_TOL
+
+
+@pytest.mark.parametrize("T,H,E,k", [(300, 256, 16, 4), (2048, 2048, 256, 8), (777, 2048, 512, 10)])
+def test_route_topk_q8(B, T, H, E, k):
+    """The standalone 8-bit router: ids bit-exact against the oracle outside the tie band,
+    weights to 1e-4 (on the GPU's set where it differs within the band)."""
+    say(f"route q8 T={T} H={H} E={E} k={k}")
+    codes, scales, biases = synth.q8_matrix(113, 0, synth.ROUTER_STREAM, 0, E, H, scale_std=0.02 / 74)
+    Rq = B.DeviceQ4(codes, scales, biases)
+    X = synth.token_rows(113, T, H)
+    ids, w = B.moe_route_topk_q8(Rq, B.bf16_tensor(X), k)
     _sync()
-    got = to_f64(Y)
-    ref, _, _, logits = orc.moe_ffn_prefill(layer, X)
-    keep = np.array([orc.boundary_gap(logits[t], k) > TIE_BAND for t in range(T)])
-    assert keep.mean() > 0.9
-    assert rel_l2(got[keep], ref[keep]) <= REL_L2_TOL
-    assert max(rel_l2(got[t], ref[t]) for t in np.nonzero(keep)[0]) <= 2 * REL_L2_TOL
+    gids, gw = ids.cpu().numpy(), w.cpu().numpy()
+    logits = orc.q4_gemm(codes, scales, biases, X)        # the 8-bit router's logits, exact
+    n_exact = 0
+    for t in range(T):
+        ok, exact = routing_ok(gids[t], logits[t], k)
+        assert ok, (t, gids[t])
+        n_exact += exact
+        np.testing.assert_allclose(gw[t], orc.weights_for_ids(logits[t], gids[t]), rtol=1e-4, atol=1e-6)
+    assert n_exact >= 0.9 * T
 
 
 @pytest.mark.parametrize("H,I,E,k,rbits", [(256, 128, 16, 4, 16), (256, 128, 16, 4, 8),
@@ -625,8 +640,42 @@ def test_decode_q8_shared_residual(B):
     H, I, E, k = 2048, 512, 256, 8
     layer = synth.moe_layer(102, 0, H, I, E, k, router_bits=8, shared_bits=8)
     dl = B.DeviceLayer(layer)
-    x = B.bf16_tensor(synth.hidden_vector(102, 0, 0, H))
-    xn = B.moe_ffn_decode(dl, x, B.OUT_BF16_RESIDUAL)
-    y = B.moe_ffn_decode(dl, x, B.OUT_F32)
-    _sync()
-    assert torch.equal(xn.cpu(), (x.cpu().float() + y.cpu()).to(torch.bfloat16))
+    for step in range(3):
+        x_bits = synth.hidden_vector(102, step, 0, H)
+        x = B.bf16_tensor(x_bits)
+        ids = torch.empty(k, dtype=torch.int32, device=DEV)
+        xn = B.moe_ffn_decode(dl, x, B.OUT_BF16_RESIDUAL, ids_out=ids)
+        y = B.moe_ffn_decode(dl, x, B.OUT_F32)
+        _sync()
+        # the same call's own rounding of x + y ...
+        assert torch.equal(xn.cpu(), (x.cpu().float() + y.cpu()).to(torch.bfloat16))
+        # ... and the oracle's: y to the float bar, bf16(x + y) within y's error plus half a step
+        gids = ids.cpu().numpy()
+        ref, _, _, logits = orc.moe_ffn_token(layer, x_bits)
+        ok, exact = routing_ok(gids, logits, k)
+        assert ok
+        if not exact:
+            ref, _, _, _ = orc.moe_ffn_token(layer, x_bits, ids=gids)
+        yg = to_f64(y)
+        assert rel_l2(yg, ref) <= 1e-5
+        got = orc.bf16_to_f64(xn.cpu().view(torch.int16).numpy().view(np.uint16))
+        want = orc.bf16_to_f64(orc.residual_next(x_bits, ref))
+        _, e1 = np.frexp(got)
+        _, e2 = np.frexp(want)
+        half = np.where(got == 0, 0, np.ldexp(0.5, e1 - 8)) + np.where(want == 0, 0, np.ldexp(0.5, e2 - 8))
+        assert np.all(np.abs(got - want) <= (np.abs(yg - ref) + half) * (1 + 1e-12))
+        assert np.mean(got == want) >= 0.95
+
+
+@pytest.mark.parametrize("T,H,I,E,k,rbits,gated", [(300, 256, 128, 16, 4, 16, False), (257, 384, 192, 8, 3, 8, True),
+                                                   (2048, 2048, 512, 256, 8, 8, True)])
+def test_prefill_q8_shared_expert(B, T, H, I, E, k, rbits, gated):
+    """Prefill with the shared expert in affine-Q8 codes (its GEMM tiles on the 8-bit B
+    operand), alone or in the checkpoint's full form (8-bit router, shared-expert gate)."""
+    say(f"prefill q8 shared T={T} H={H} E={E} k={k} router bits={rbits} gated={gated}")
+    layer = synth.moe_layer(115, 0, H, I, E, k, router_bits=rbits, shared_gate=gated, shared_bits=8)
+    dl = B.DeviceLayer(layer)
+    X = synth.token_rows(115, T, H)
+    err, worst = _prefill_check(B, layer, dl, X)
+    assert err <= REL_L2_TOL, err
+    assert worst <= 2 * REL_L2_TOL

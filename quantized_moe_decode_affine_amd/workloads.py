@@ -72,16 +72,20 @@ class DecodeStack:
     def weight_bytes(self) -> int:
         return sum(d.nbytes for d in self.layers)
 
-    def step(self, s: int, record_ids: bool = False, events=None) -> None:
+    def step(self, s: int, record_ids: bool = False, events=None, ids_buf=None) -> None:
         """Enqueue one decode step (all layers, in order) on the current stream.
 
-        `events`, when given, is a list of (start, end) torch.cuda.Event pairs,
-        one per layer, recorded around each layer's launch on the same stream."""
+        The step's expert ids go to ``self.ids`` when `record_ids`, or to `ids_buf`
+        (int32 [n_layers][top_k]) when given.  `events`, when given, is a list of
+        (start, end) torch.cuda.Event pairs, one per layer, recorded around each
+        layer's launch on the same stream."""
         stream = torch.cuda.current_stream().cuda_stream
         xs = self.x[s % self.n_steps]
         H = self.y.shape[1]
         x0, y0 = xs.data_ptr(), self.y.data_ptr()
-        ids0, kk = self.ids.data_ptr(), self.ids.shape[1]
+        if ids_buf is not None:
+            record_ids = True
+        ids0, kk = (ids_buf if ids_buf is not None else self.ids).data_ptr(), self.ids.shape[1]
         ws, wsn = self.ws.data_ptr(), self.ws.numel()
         for l in range(self.n_layers):
             if events is not None:

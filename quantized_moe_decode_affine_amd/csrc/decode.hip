@@ -291,6 +291,27 @@ __device__ __forceinline__ void load_pair(const PairRef& r, int c, PairRegs& d) 
   d.ub = r.ub[c >> 1];
 }
 
+// One chunk (32 codes, 32 bytes per matrix) of a gate/up row pair of an 8-bit shared
+// expert ([I][H/4] words), loaded ahead.
+struct PairRegs8 {
+  uint4 g0, g1, u0, u1;
+  uint32_t gs, gb, us, ub;
+};
+
+__device__ __forceinline__ void load_pair8(const DecodeLayer& L, int64_t row, int c, PairRegs8& d) {
+  const int H = L.hidden, G = H >> 6;
+  const uint4* gc = reinterpret_cast<const uint4*>(L.sh_gate.codes) + row * (H >> 4) + 2 * c;
+  const uint4* uc = reinterpret_cast<const uint4*>(L.sh_up.codes) + row * (H >> 4) + 2 * c;
+  d.g0 = gc[0];
+  d.g1 = gc[1];
+  d.u0 = uc[0];
+  d.u1 = uc[1];
+  d.gs = L.sh_gate.scales[row * G + (c >> 1)];
+  d.gb = L.sh_gate.biases[row * G + (c >> 1)];
+  d.us = L.sh_up.scales[row * G + (c >> 1)];
+  d.ub = L.sh_up.biases[row * G + (c >> 1)];
+}
+
 // The 16 pair words of a staged bf16 chunk, read once from LDS.
 struct XChunk {
   uint32_t v[16];
@@ -322,6 +343,13 @@ __device__ __forceinline__ float chunk_pdot_regs(uint4 codes, const uint32_t (&v
 __device__ __forceinline__ float2 pair_terms(const PairRegs& d, const XChunk& x) {
   return make_float2(affine_term(chunk_pdot_regs(d.g, x.v), x.sum, d.gs, d.gb),
                      affine_term(chunk_pdot_regs(d.u, x.v), x.sum, d.us, d.ub));
+}
+
+// (gate, up) partial of one chunk of an 8-bit pair: 8-bit codes are exact bf16 values,
+// so a group contributes scale * sum(q x) + bias * sum(x).
+__device__ __forceinline__ float2 pair_terms8(const PairRegs8& d, const XChunk& x) {
+  return make_float2(fmaf(bf16_bits_to_f32(d.gs), q8_chunk_pdot_regs(d.g0, d.g1, x.v), bf16_bits_to_f32(d.gb) * x.sum),
+                     fmaf(bf16_bits_to_f32(d.us), q8_chunk_pdot_regs(d.u0, d.u1, x.v), bf16_bits_to_f32(d.ub) * x.sum));
 }
 
 // Full (gate, up) dots of a row pair by the lane group, loads issued on the spot
@@ -610,8 +638,19 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   const int sh_passes = (sh_pairs + PS - 1) / PS;
   auto sh_row = [&](int P) { return (b + (P / kUnitRows) * NB) * kUnitRows + (P % kUnitRows); };
   constexpr bool sh_pf = kFast && !kQ8Shared;
-  const int sh_pfp = sh_pf ? min(sh_passes, kShSlots) : 0;
+  constexpr bool sh_pf8 = kFast && kQ8Shared;  // the fast form's 8-bit shared expert: same tasks, byte codes
+  const int sh_pfp = sh_pf || sh_pf8 ? min(sh_passes, kShSlots) : 0;
   PairRegs shr[kShSlots];
+  PairRegs8 shr8[kShSlots];
+  if constexpr (sh_pf8) {
+    const int lastP = sh_pairs > 0 ? sh_pairs - 1 : 0;
+    const int bsh = sh_pairs > 0 ? b : upe - 1;
+#pragma unroll
+    for (int q = 0; q < kShSlots; ++q) {
+      const int P = min(q * PS + wv * gh.RPW + gh.lg, lastP);
+      load_pair8(L, (int64_t)(bsh + (P / kUnitRows) * NB) * kUnitRows + (P % kUnitRows), gh.sub, shr8[q]);
+    }
+  }
   if constexpr (sh_pf) {
     // clamped: a workgroup without shared work reads the last unit's rows (never used)
     const int lastP = sh_pairs > 0 ? sh_pairs - 1 : 0;
@@ -694,7 +733,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     stage_bf16_parallel(p.x, H, xp, xs);
     lds_sync();  // x staged; the epoch is visible
   }
-  if constexpr (kQ8Shared) {
+  if constexpr (kQ8Shared && !kFast) {
     stage_q8_groups(xf, H, [&](int i) { return bf16_bits_to_f32(p.x[i]); });
     lds_sync();
   }
@@ -705,7 +744,27 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   // its share once the routed loads are out.
   auto shared_compute = [&]() {
     if (!has_shared) return;
-    if constexpr (kQ8Shared) {
+    if constexpr (sh_pf8) {
+      XChunk x1;
+      read_xchunk(xp, xs, gh.sub, x1);
+#pragma unroll
+      for (int q = 0; q < kShSlots; ++q) {
+        if (q < sh_pfp) {
+          const int P = q * PS + wv * gh.RPW + gh.lg;
+          const float2 tt = pair_terms8(shr8[q], x1);
+          const float g = group_sum_rt(tt.x, gh.lr), u = group_sum_rt(tt.y, gh.lr);
+          if (gh.sub == 0 && P < sh_pairs) s_sh[P] = silu(g) * u;
+        }
+      }
+      for (int q = sh_pfp; q < sh_passes; ++q) {  // (more passes than prefetched: loaded now)
+        const int P = q * PS + wv * gh.RPW + gh.lg;
+        PairRegs8 d;
+        load_pair8(L, sh_row(min(P, sh_pairs - 1)), gh.sub, d);
+        const float2 tt = pair_terms8(d, x1);
+        const float g = group_sum_rt(tt.x, gh.lr), u = group_sum_rt(tt.y, gh.lr);
+        if (gh.sub == 0 && P < sh_pairs) s_sh[P] = silu(g) * u;
+      }
+    } else if constexpr (kQ8Shared) {
       // 8-row units, one per wave at a time, on waves 1..
       for (int m = wv - 1; m >= 0 && m < min(sh_units, nbatch_units); m += kWaves - 1) {
         const float2 gu = unit_gate_up_q8(L, (b + m * NB) * kUnitRows, xf);
@@ -788,6 +847,9 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   const int nblocks = H / kOutRows;
   const int dn_pfp = kFast && b < nblocks ? min(dpasses, kDnSlots) : 0;
   const int64_t dmat_rows = (int64_t)H;
+  // down tasks take the slots in the order k, 0, 1, .., k-1: the shared slot (the heavier
+  // rows when 8-bit) lands in the first pass, which every wave has
+  auto slot_of_task = [&](int task) { return (task / kOutRows + nslot - 1) % nslot; };
   // down row n of slot j: its code row, scales and biases (routed expert s_ids[j], or shared)
   // The shared expert's down rows are addressed from the routed stack's base by their
   // element distance, so a row pointer is one base plus a selected offset (a select
@@ -805,7 +867,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   };
   PairRegs gur[kGuSlots];
   struct DnRegs {
-    uint4 c;
+    uint4 c, c2;  // c2: the second 16 bytes of an 8-bit shared row's chunk
     uint32_t s, bb;
   };
   DnRegs dnr[kDnSlots];
@@ -824,14 +886,22 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
 #pragma unroll
     for (int q = 0; q < kDnSlots; ++q) {
       const int task = min(q * PSd + wv * gd.RPW + gd.lg, dtasks - 1);
-      int j = task / kOutRows;
-      if (kQ8Shared && j == k) j = 0;  // the 8-bit shared slot is read in phase C
-      const uint4* cr;
-      const uint16_t *sr, *br;
-      down_row(j, rb0 * kOutRows + task % kOutRows, cr, sr, br);
-      dnr[q].c = cr[gd.sub];
-      dnr[q].s = sr[gd.sub >> 1];
-      dnr[q].bb = br[gd.sub >> 1];
+      const int j = slot_of_task(task), n = rb0 * kOutRows + task % kOutRows;
+      // one base (the routed stack's) plus selected offsets, no branch: an 8-bit shared
+      // row's chunk is 32 bytes (two words c, c2), any other row's 16 bytes (c2 = c)
+      const bool q8row = kQ8Shared && j == k;
+      const int e = s_ids[j];
+      const bool routed = e >= 0;
+      const int64_t row = routed ? (int64_t)e * dmat_rows + n : (int64_t)n;
+      const int64_t coff = q8row ? sh_dc / 4 + (int64_t)n * (I >> 4) + 2 * gd.sub
+                                 : (routed ? 0 : sh_dc / 4) + row * CI + gd.sub;
+      const int64_t soff = q8row ? sh_ds + (int64_t)n * GI : (routed ? 0 : sh_ds) + row * GI;
+      const int64_t boff = q8row ? sh_db + (int64_t)n * GI : (routed ? 0 : sh_db) + row * GI;
+      const uint4* cr = reinterpret_cast<const uint4*>(L.down.codes) + coff;
+      dnr[q].c = cr[0];
+      dnr[q].c2 = cr[q8row ? 1 : 0];
+      dnr[q].s = L.down.scales[soff + (gd.sub >> 1)];
+      dnr[q].bb = L.down.biases[boff + (gd.sub >> 1)];
     }
   };
   if (!kDownLate) issue_down();
@@ -902,7 +972,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   // ================================================================ phase C
   // routed slots and the shared slot (an 8-bit shared expert's slot also as fp32 into af)
   stage_tagged_split(p.act + (size_t)(b % kCopies) * p.act_copy_words, nslot, I, ap, as, epoch, timeouts,
-                     kQ8Shared ? af : nullptr, k * I);
+                     kQ8Shared && !kFast ? af : nullptr, k * I);
   lds_sync();  // activations staged
   {
     constexpr int ST = chunk_stride<2>();
@@ -915,17 +985,19 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
             if (q < dn_pfp) {
               const int task = q * PSd + wv * gd.RPW + gd.lg;
               const bool live = task < dtasks;
-              const int j = live ? task / kOutRows : 0, r = task % kOutRows;
+              const int j = live ? slot_of_task(task) : 0, r = task % kOutRows;
               float part;
-              if (kQ8Shared && j == k) {
-                part = q8_down_row(L, rb * kOutRows + r, af, gd.sub, gd.LR, gd.lr, live);
+              const int c = gd.sub;
+              if (kQ8Shared && j == k) {  // exact bf16 byte codes: scale * sum(q a) + bias * sum(a)
+                part = fmaf(bf16_bits_to_f32(dnr[q].s), q8_chunk_pdot<2>(dnr[q].c, dnr[q].c2, ap + ((size_t)j * CI + c) * ST),
+                            bf16_bits_to_f32(dnr[q].bb) * as[j * CI + c]);
               } else {
-                const int c = gd.sub;
                 part = affine_term(chunk_pdot<2>(dnr[q].c, ap + ((size_t)j * CI + c) * ST), as[j * CI + c],
                                    dnr[q].s, dnr[q].bb);
-                part = group_sum_rt(part, gd.lr);
               }
-              if (gd.sub == 0 && live) s_red[task] = part;
+              part = group_sum_rt(part, gd.lr);
+              (void)r;
+              if (gd.sub == 0 && live) s_red[j * kOutRows + r] = part;
             }
           }
           q0 = dn_pfp;
@@ -934,7 +1006,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
       for (int q = q0; q < dpasses; ++q) {
         const int task = q * PSd + wv * gd.RPW + gd.lg;
         const bool live = task < dtasks;
-        const int j = live ? task / kOutRows : 0, n = rb * kOutRows + task % kOutRows;
+        const int j = live ? slot_of_task(task) : 0, n = rb * kOutRows + task % kOutRows;
         float part = 0.f;
         if (kQ8Shared && j == k) {
           part = q8_down_row(L, n, af, gd.sub, gd.LR, gd.lr, live);
@@ -949,7 +1021,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
           }
           part = group_sum_rt(part, gd.lr);
         }
-        if (gd.sub == 0 && live) s_red[task] = part;
+        if (gd.sub == 0 && live) s_red[j * kOutRows + task % kOutRows] = part;
       }
       lds_sync();
       if (t < kOutRows) {

@@ -139,6 +139,22 @@ __device__ __forceinline__ float q8_chunk_pdot(uint4 c0, uint4 c1, const uint32_
   return p0 + p1;
 }
 
+// The same against one bf16 chunk already in registers (16 pair words).
+__device__ __forceinline__ float q8_chunk_pdot_regs(uint4 c0, uint4 c1, const uint32_t (&v)[16]) {
+  const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint32_t pr[4];
+    q8_block_pairs(w[2 * b], w[2 * b + 1], pr);
+    p0 = dot2_bf16(pr[0], v[4 * b], p0);
+    p1 = dot2_bf16(pr[1], v[4 * b + 1], p1);
+    p0 = dot2_bf16(pr[2], v[4 * b + 2], p0);
+    p1 = dot2_bf16(pr[3], v[4 * b + 3], p1);
+  }
+  return p0 + p1;
+}
+
 // Contribution of a group-aligned chunk pair or single chunk: scale*P' + (bias-128*scale)*sum.
 __device__ __forceinline__ float affine_term(float p, float vsum, uint32_t s_bits, uint32_t b_bits) {
   float s = bf16_bits_to_f32(s_bits);

@@ -58,6 +58,10 @@ constexpr int kActBatch = 256;    // activations gathered in LDS before they are
 #define Q4MOE_DOWN_LATE 0
 #endif
 constexpr bool kDownLate = Q4MOE_DOWN_LATE;  // down rows loaded after gate/up (else with it)
+#ifndef Q4MOE_SHARED_LATE
+#define Q4MOE_SHARED_LATE 1
+#endif
+constexpr bool kSharedLate = Q4MOE_SHARED_LATE;  // shared gate/up rows issued after the router rows are in
 
 #ifndef Q4MOE_HANDOFF_COPIES
 #define Q4MOE_HANDOFF_COPIES 8
@@ -619,20 +623,38 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   // ================================================================ phase A
   // Router rows e = b, b + NB, ... (one 16-byte word of a row per thread when fast).
   const int nrows_rt = b < E ? (E - 1 - b) / NB + 1 : 0;
-  constexpr bool rt_pf = kFast && !kQ8Router;
-  uint4 rreg[kRtRows], xreg;
+  // Fast form: the first kRtRows rows go out now into registers (8-bit router: one
+  // 16-code word of a row, with its group's scale and bias and the matching 16 values
+  // of x, per thread of the first H / 16).
+  constexpr bool rt_pf = kFast && !kQ8Router, rt_pf8 = kFast && kQ8Router;
+  uint4 rreg[kRtRows], xreg, xq0, xq1;
+  uint16_t rsc[kRtRows], rbi[kRtRows];
+  if constexpr (rt_pf || rt_pf8) xreg = reinterpret_cast<const uint4*>(p.x)[min(t, (H >> 3) - 1)];
   if constexpr (rt_pf) {
     const int c = min(t, (H >> 3) - 1);
-    xreg = reinterpret_cast<const uint4*>(p.x)[c];
 #pragma unroll
     for (int m = 0; m < kRtRows; ++m)
       rreg[m] = reinterpret_cast<const uint4*>(L.router + (size_t)min(b + m * NB, E - 1) * H)[c];
+  }
+  if constexpr (rt_pf8) {
+    const int c = min(t, (H >> 4) - 1), G = H >> 6;
+    xq0 = reinterpret_cast<const uint4*>(p.x)[2 * c];
+    xq1 = reinterpret_cast<const uint4*>(p.x)[2 * c + 1];
+#pragma unroll
+    for (int m = 0; m < kRtRows; ++m) {
+      const size_t e = (size_t)min(b + m * NB, E - 1);
+      rreg[m] = reinterpret_cast<const uint4*>(L.router_q8.codes)[e * (H >> 4) + c];
+      rsc[m] = L.router_q8.scales[e * G + (c >> 2)];
+      rbi[m] = L.router_q8.biases[e * G + (c >> 2)];
+    }
   }
   unsigned long long arrival;
   if (t == 0) arrival = __hip_atomic_fetch_add(ectr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Shared gate/up units su = b, b + NB, ... (8 row pairs each): in the fast form the
-  // loads of the first kShSlots passes go out now (they depend on nothing).
+  // loads of the first kShSlots passes go out into registers once the router rows are
+  // in (they depend on nothing, and issued with the router rows they would only slow
+  // the logits that every workgroup waits for).
   const int sh_units = has_shared && b < upe ? (upe - 1 - b) / NB + 1 : 0;
   const int sh_pairs = min(sh_units, nbatch_units) * kUnitRows;  // the first batch
   const int sh_passes = (sh_pairs + PS - 1) / PS;
@@ -642,6 +664,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   const int sh_pfp = sh_pf || sh_pf8 ? min(sh_passes, kShSlots) : 0;
   PairRegs shr[kShSlots];
   PairRegs8 shr8[kShSlots];
+  auto issue_shared = [&]() {
   if constexpr (sh_pf8) {
     const int lastP = sh_pairs > 0 ? sh_pairs - 1 : 0;
     const int bsh = sh_pairs > 0 ? b : upe - 1;
@@ -662,6 +685,11 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
       load_pair(has_shared ? shared_pair_ref(L, i) : routed_pair_ref(L, 0, 0), gh.sub, shr[q]);
     }
   }
+  };
+  // (8-bit shared rows, four times the bytes of 4-bit ones on a quarter of the workgroups,
+  // go out at once: issued late they would hold up phase B)
+  constexpr bool sh_late = kSharedLate && !kQ8Shared;
+  if (!sh_late) issue_shared();
 
   // Router dots, one partial per thread, then a fixed-order sum over the waves.
   for (int m0 = 0; m0 < nrows_rt; m0 += kRtRows) {
@@ -671,7 +699,18 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
       if (m >= nrows_rt) break;
       const int e = b + m * NB;
       float part = 0.f;
-      if constexpr (kQ8Router) {
+      if (rt_pf8 && m < kRtRows) {
+        const uint32_t xw[8] = {xq0.x, xq0.y, xq0.z, xq0.w, xq1.x, xq1.y, xq1.z, xq1.w};
+        const uint32_t cw[4] = {rreg[mm].x, rreg[mm].y, rreg[mm].z, rreg[mm].w};
+        float pq = 0.f, xsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float xi = bf16_bits_to_f32((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+          xsum += xi;
+          pq = fmaf(xi, (float)((cw[i >> 2] >> (8 * (i & 3))) & 0xFFu), pq);
+        }
+        part = t < (H >> 4) ? fmaf(bf16_bits_to_f32(rsc[mm]), pq, bf16_bits_to_f32(rbi[mm]) * xsum) : 0.f;
+      } else if constexpr (kQ8Router) {
         // 8-bit router (count 1, [E][H/4] words): 16-code chunks per thread (inside one group)
         const int G = H >> 6;
         const uint4* qr = reinterpret_cast<const uint4*>(L.router_q8.codes) + (size_t)e * (H >> 4);
@@ -713,7 +752,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
       part = group_sum_rt(part, 6);
       if (lane == 0) s_rpart[mm][wv] = part;
     }
-    if constexpr (rt_pf) {
+    if constexpr (rt_pf || rt_pf8) {
       if (m0 == 0) stage_bf16_block(xreg, t, H >> 3, xp, xs);  // x from the router pass's registers
     }
     if (t == 0 && m0 == 0) finish_epoch(arrival);
@@ -729,7 +768,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     lds_sync();  // s_rpart is reused
   }
   if (t == 0 && nrows_rt == 0) finish_epoch(arrival);
-  if (!rt_pf || nrows_rt == 0) {
+  if (!(rt_pf || rt_pf8) || nrows_rt == 0) {
     stage_bf16_parallel(p.x, H, xp, xs);
     lds_sync();  // x staged; the epoch is visible
   }
@@ -737,6 +776,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     stage_q8_groups(xf, H, [&](int i) { return bf16_bits_to_f32(p.x[i]); });
     lds_sync();
   }
+  if (sh_late) issue_shared();
   const uint32_t epoch = s_epoch;
 
   // Shared expert gate/up with SwiGLU (off the critical path: needed only in phase C),
@@ -845,11 +885,26 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   const int dtasks = nslot * kOutRows;
   const int dpasses = (dtasks + PSd - 1) / PSd;
   const int nblocks = H / kOutRows;
-  const int dn_pfp = kFast && b < nblocks ? min(dpasses, kDnSlots) : 0;
+  // Fast form: the k routed slots' rows of the output block are k * 8 tasks of one
+  // 16-lane row chunk each, PSd a pass, the first kDnSlots passes prefetched; the shared
+  // expert's 8 rows take one pass more, row r on wave r over its 64 lanes (8 columns a
+  // lane), so no pass has dead tasks for k = 8 and no wave branches between row kinds.
+  const int dtasks_r = k * kOutRows;
+  const int dpasses_r = (dtasks_r + PSd - 1) / PSd;
+  const int dn_pfp = kFast && b < nblocks ? min(dpasses_r, kDnSlots) : 0;
   const int64_t dmat_rows = (int64_t)H;
-  // down tasks take the slots in the order k, 0, 1, .., k-1: the shared slot (the heavier
-  // rows when 8-bit) lands in the first pass, which every wave has
-  auto slot_of_task = [&](int task) { return (task / kOutRows + nslot - 1) % nslot; };
+  // Down task -> {slot, row}.  With a shared expert its 8 rows sit every shs tasks from
+  // task 0 (for hidden 2048 / inter 512: the first task of every wave in the first pass,
+  // row r on wave r, so its heavier 8-bit rows do not pile onto two waves); the routed
+  // (slot, row) pairs fill the other tasks in order.
+  static_assert(kOutRows == kWaves, "one shared down row per wave");
+  const int shs = max(1, min(gd.RPW, dtasks / kOutRows));  // shared rows every shs tasks (all live)
+  auto task_jr = [&](int task) -> int2 {
+    if (!has_shared) return make_int2(task / kOutRows, task % kOutRows);
+    if (task < kOutRows * shs && task % shs == 0) return make_int2(k, task / shs);
+    const int i = task - min(kOutRows, (task + shs - 1) / shs);
+    return make_int2(i / kOutRows, i % kOutRows);
+  };
   // down row n of slot j: its code row, scales and biases (routed expert s_ids[j], or shared)
   // The shared expert's down rows are addressed from the routed stack's base by their
   // element distance, so a row pointer is one base plus a selected offset (a select
@@ -866,11 +921,6 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     br = L.down.biases + (routed ? 0 : sh_db) + row * GI;
   };
   PairRegs gur[kGuSlots];
-  struct DnRegs {
-    uint4 c, c2;  // c2: the second 16 bytes of an 8-bit shared row's chunk
-    uint32_t s, bb;
-  };
-  DnRegs dnr[kDnSlots];
   if constexpr (kFast) {
     const int lastP = pairs0 > 0 ? pairs0 - 1 : 0;
 #pragma unroll
@@ -880,29 +930,38 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
       load_pair(routed_pair_ref(L, s_ids[su.x], su.y + P % kUnitRows), gh.sub, gur[q]);
     }
   }
+  struct DnRegs {  // one routed row chunk: 32 codes, its group's scale and bias
+    uint4 c;
+    uint32_t s, bb;
+  };
+  struct ShDnRegs {  // 8 columns of a shared row: 8 codes (4- or 8-bit), scale, bias
+    uint2 c;
+    uint32_t s, bb;
+  };
+  auto load_dn = [&](int q, int rb, DnRegs& d) {  // routed task of pass q (dead tasks read a valid row)
+    const int task = min(q * PSd + wv * gd.RPW + gd.lg, dtasks_r - 1);
+    const int64_t row = (int64_t)s_ids[task / kOutRows] * dmat_rows + rb * kOutRows + task % kOutRows;
+    d.c = reinterpret_cast<const uint4*>(L.down.codes + row * (I >> 3))[gd.sub];
+    d.s = L.down.scales[row * GI + (gd.sub >> 1)];
+    d.bb = L.down.biases[row * GI + (gd.sub >> 1)];
+  };
+  auto load_shdn = [&](int rb, ShDnRegs& d) {  // shared row rb * 8 + wv, lane's 8 columns
+    const int64_t n = (int64_t)rb * kOutRows + wv;
+    if constexpr (kQ8Shared)
+      d.c = reinterpret_cast<const uint2*>(L.sh_down.codes + n * (I >> 2))[lane];
+    else
+      d.c = make_uint2(L.sh_down.codes[n * (I >> 3) + lane], 0u);
+    d.s = L.sh_down.scales[n * GI + (lane >> 3)];
+    d.bb = L.sh_down.biases[n * GI + (lane >> 3)];
+  };
+  DnRegs dnr[kDnSlots];
+  ShDnRegs shdn;
   auto issue_down = [&]() {
     if constexpr (!kFast) return;
     const int rb0 = min(b, nblocks - 1);
 #pragma unroll
-    for (int q = 0; q < kDnSlots; ++q) {
-      const int task = min(q * PSd + wv * gd.RPW + gd.lg, dtasks - 1);
-      const int j = slot_of_task(task), n = rb0 * kOutRows + task % kOutRows;
-      // one base (the routed stack's) plus selected offsets, no branch: an 8-bit shared
-      // row's chunk is 32 bytes (two words c, c2), any other row's 16 bytes (c2 = c)
-      const bool q8row = kQ8Shared && j == k;
-      const int e = s_ids[j];
-      const bool routed = e >= 0;
-      const int64_t row = routed ? (int64_t)e * dmat_rows + n : (int64_t)n;
-      const int64_t coff = q8row ? sh_dc / 4 + (int64_t)n * (I >> 4) + 2 * gd.sub
-                                 : (routed ? 0 : sh_dc / 4) + row * CI + gd.sub;
-      const int64_t soff = q8row ? sh_ds + (int64_t)n * GI : (routed ? 0 : sh_ds) + row * GI;
-      const int64_t boff = q8row ? sh_db + (int64_t)n * GI : (routed ? 0 : sh_db) + row * GI;
-      const uint4* cr = reinterpret_cast<const uint4*>(L.down.codes) + coff;
-      dnr[q].c = cr[0];
-      dnr[q].c2 = cr[q8row ? 1 : 0];
-      dnr[q].s = L.down.scales[soff + (gd.sub >> 1)];
-      dnr[q].bb = L.down.biases[boff + (gd.sub >> 1)];
-    }
+    for (int q = 0; q < kDnSlots; ++q) load_dn(q, rb0, dnr[q]);
+    if (has_shared) load_shdn(rb0, shdn);
   };
   if (!kDownLate) issue_down();
 
@@ -976,52 +1035,93 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   lds_sync();  // activations staged
   {
     constexpr int ST = chunk_stride<2>();
-    for (int rb = b; rb < nblocks; rb += NB) {
-      int q0 = 0;
-      if constexpr (kFast) {
-        if (rb == b) {
+    // fast form: a routed task's part from its row chunk
+    auto routed_part = [&](const DnRegs& d, int q) {
+      const int task = q * PSd + wv * gd.RPW + gd.lg;
+      const bool live = task < dtasks_r;
+      const int j = live ? task / kOutRows : 0, c = gd.sub;
+      float part = affine_term(chunk_pdot<2>(d.c, ap + ((size_t)j * CI + c) * ST), as[j * CI + c], d.s, d.bb);
+      part = group_sum_rt(part, gd.lr);
+      if (gd.sub == 0 && live) s_red[j * kOutRows + task % kOutRows] = part;
+    };
+    // fast form: shared row rb * 8 + wv, lane l on columns 8l .. 8l + 7 (block l % 4 of
+    // chunk l / 4); the group's bias term is added once, by its first lane
+    auto shared_part = [&](const ShDnRegs& d) {
+      const int c = lane >> 2, g = lane >> 3;
+      const uint32_t* hv = ap + ((size_t)k * CI + c) * ST + 4 * (lane & 3);
+      const uint4 hi = *reinterpret_cast<const uint4*>(hv), lo = *reinterpret_cast<const uint4*>(hv + 16);
+      uint32_t pr[4];
+      if constexpr (kQ8Shared) {
+        q8_block_pairs(d.c.x, d.c.y, pr);
+      } else {
 #pragma unroll
-          for (int q = 0; q < kDnSlots; ++q) {
-            if (q < dn_pfp) {
-              const int task = q * PSd + wv * gd.RPW + gd.lg;
-              const bool live = task < dtasks;
-              const int j = live ? slot_of_task(task) : 0, r = task % kOutRows;
-              float part;
-              const int c = gd.sub;
-              if (kQ8Shared && j == k) {  // exact bf16 byte codes: scale * sum(q a) + bias * sum(a)
-                part = fmaf(bf16_bits_to_f32(dnr[q].s), q8_chunk_pdot<2>(dnr[q].c, dnr[q].c2, ap + ((size_t)j * CI + c) * ST),
-                            bf16_bits_to_f32(dnr[q].bb) * as[j * CI + c]);
-              } else {
-                part = affine_term(chunk_pdot<2>(dnr[q].c, ap + ((size_t)j * CI + c) * ST), as[j * CI + c],
-                                   dnr[q].s, dnr[q].bb);
-              }
-              part = group_sum_rt(part, gd.lr);
-              (void)r;
-              if (gd.sub == 0 && live) s_red[j * kOutRows + r] = part;
+        for (int i = 0; i < 4; ++i) pr[i] = nib_pair(d.c.x, 4 * i);
+      }
+      float p0 = dot2_bf16(pr[0], hi.x, 0.f), p1 = dot2_bf16(pr[1], hi.y, 0.f);
+      p0 = dot2_bf16(pr[2], hi.z, p0);
+      p1 = dot2_bf16(pr[3], hi.w, p1);
+      p0 = dot2_bf16(pr[0], lo.x, p0);
+      p1 = dot2_bf16(pr[1], lo.y, p1);
+      p0 = dot2_bf16(pr[2], lo.z, p0);
+      p1 = dot2_bf16(pr[3], lo.w, p1);
+      const float sc = bf16_bits_to_f32(d.s), bi = bf16_bits_to_f32(d.bb);
+      // 8-bit: codes are q; 4-bit: codes are 128 + q (bias - 128 * scale is exact)
+      const float cb = kQ8Shared ? bi : bi - 128.0f * sc;
+      const float gsum = (lane & 7) == 0 ? as[k * CI + 2 * g] + as[k * CI + 2 * g + 1] : 0.f;
+      const float part = group_sum_rt(fmaf(sc, p0 + p1, cb * gsum), 6);
+      if (lane == 0) s_red[k * kOutRows + wv] = part;
+    };
+    for (int rb = b; rb < nblocks; rb += NB) {
+      if constexpr (kFast) {
+        const bool first = rb == b;
+#pragma unroll
+        for (int q = 0; q < kDnSlots; ++q) {
+          if (q < dpasses_r) {
+            if (first && q < dn_pfp) {
+              routed_part(dnr[q], q);
+            } else {
+              DnRegs d;
+              load_dn(q, rb, d);
+              routed_part(d, q);
             }
           }
-          q0 = dn_pfp;
         }
-      }
-      for (int q = q0; q < dpasses; ++q) {
-        const int task = q * PSd + wv * gd.RPW + gd.lg;
-        const bool live = task < dtasks;
-        const int j = live ? slot_of_task(task) : 0, n = rb * kOutRows + task % kOutRows;
-        float part = 0.f;
-        if (kQ8Shared && j == k) {
-          part = q8_down_row(L, n, af, gd.sub, gd.LR, gd.lr, live);
-        } else {
-          if (live) {
-            const uint4* cr;
-            const uint16_t *sr, *br;
-            down_row(j, n, cr, sr, br);
-            for (int c = gd.sub; c < CI; c += gd.LR)
-              part += affine_term(chunk_pdot<2>(cr[c], ap + ((size_t)j * CI + c) * ST), as[j * CI + c], sr[c >> 1],
-                                  br[c >> 1]);
+        for (int q = kDnSlots; q < dpasses_r; ++q) {  // (more passes than prefetched: loaded now)
+          DnRegs d;
+          load_dn(q, rb, d);
+          routed_part(d, q);
+        }
+        if (has_shared) {
+          if (first) {
+            shared_part(shdn);
+          } else {
+            ShDnRegs d;
+            load_shdn(rb, d);
+            shared_part(d);
           }
-          part = group_sum_rt(part, gd.lr);
         }
-        if (gd.sub == 0 && live) s_red[j * kOutRows + task % kOutRows] = part;
+      } else {
+        for (int q = 0; q < dpasses; ++q) {
+          const int task = q * PSd + wv * gd.RPW + gd.lg;
+          const bool live = task < dtasks;
+          const int2 jr = task_jr(task);
+          const int j = live ? jr.x : 0, n = rb * kOutRows + jr.y;
+          float part = 0.f;
+          if (kQ8Shared && j == k) {
+            part = q8_down_row(L, n, af, gd.sub, gd.LR, gd.lr, live);
+          } else {
+            if (live) {
+              const uint4* cr;
+              const uint16_t *sr, *br;
+              down_row(j, n, cr, sr, br);
+              for (int c = gd.sub; c < CI; c += gd.LR)
+                part += affine_term(chunk_pdot<2>(cr[c], ap + ((size_t)j * CI + c) * ST), as[j * CI + c], sr[c >> 1],
+                                    br[c >> 1]);
+            }
+            part = group_sum_rt(part, gd.lr);
+          }
+          if (gd.sub == 0 && live) s_red[j * kOutRows + jr.y] = part;
+        }
       }
       lds_sync();
       if (t < kOutRows) {

@@ -223,13 +223,21 @@ int moe_ffn_decode_noalloc(const q4moe_layer* layer, const q4moe_bf16* x, void* 
  * to rounding (intermediates stay fp32).  X bf16 [B][hidden]; Y fp32 or bf16
  * [B][hidden]; ids_out int32 [B][top_k] and w_out fp32 [B][top_k] may be null.
  * Each expert chosen by any of the tokens is read once for all of them.  Runs
- * as four launches (router; top-k and the step's expert plan; gate/up with
- * SwiGLU; down with the weighted sum) that hand values over only through the
- * Q4MOE_OP_FFN_DECODE_BATCH workspace (B), which needs no initialisation;
- * calls that share a workspace must not overlap.  Shapes
- * whose staged vectors exceed 64 KB of LDS (B * hidden * 21 / 8 bytes of
- * inputs, or (top_k + 1) * inter * 37 / 8 bytes of SwiGLU outputs for one
- * token) return Q4MOE_EUNSUPPORTED.
+ * as two launches: one of one workgroup per compute unit (router, every
+ * token's top-k, the step's expert plan, gate/up with SwiGLU), whose
+ * workgroups pass the router logits to each other as tagged words as
+ * moe_ffn_decode does, then the down projection with the weighted sum.  B = 1
+ * runs moe_ffn_decode's single launch when it applies (y not overlapping x,
+ * and a workspace as large as Q4MOE_OP_FFN_DECODE needs: the
+ * Q4MOE_OP_FFN_DECODE_BATCH size for one row includes it).  The
+ * Q4MOE_OP_FFN_DECODE_BATCH workspace (B) must be zero-filled before its
+ * first use and stay with one device; each call leaves it ready for the next,
+ * and calls that share a workspace must not overlap.  Waits are bounded as in
+ * moe_ffn_decode (the same counter at byte offset 2048).  Q4MOE_EUNSUPPORTED:
+ * shapes whose staged vectors exceed 64 KB of LDS (B * hidden * 21 / 8 bytes
+ * of inputs, or (top_k + 1) * inter * 37 / 8 bytes of SwiGLU outputs for one
+ * token), or a device on which one front workgroup per compute unit cannot be
+ * resident at once.
  */
 int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t B, void* Y,
                          int out_dtype, int32_t* ids_out, float* w_out, void* workspace,

@@ -4,6 +4,7 @@
 #include "../../include/q4moe.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <new>
 
 namespace q4moe {
@@ -145,7 +146,9 @@ size_t q4moe_workspace_bytes(int op, const q4moe_layer* layer, const q4moe_matri
     case Q4MOE_OP_FFN_DECODE_BATCH: {
       q4moe::DecodeLayer d;
       if (layer_check(layer, &d) != Q4MOE_OK || rows < 1 || rows > q4moe::kMaxBatch) return 0;
-      return q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)rows);
+      const size_t nb = q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)rows);
+      // one row runs the batch-1 layer kernel when it applies: room for its workspace too
+      return rows == 1 ? std::max(nb, q4moe::decode_workspace_bytes(d.hidden, d.inter, d.n_experts, d.top_k)) : nb;
     }
     case Q4MOE_OP_LMHEAD:
       if (!W) return 0;
@@ -302,6 +305,17 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
     if (B > q4moe::kMaxBatch || !q4moe::decode_batch_supported(d, (int)B, kMaxDynLds)) return Q4MOE_EUNSUPPORTED;
     const size_t need = q4moe::decode_batch_workspace_bytes(d.n_experts, d.top_k, d.inter, (int)B);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
+    if (B == 1) {  // one token: the batch-1 layer kernel when it applies (one launch instead of two)
+      const uintptr_t xb = reinterpret_cast<uintptr_t>(X), yb = reinterpret_cast<uintptr_t>(Y);
+      const uintptr_t xe = xb + (uintptr_t)d.hidden * 2, ye = yb + (uintptr_t)d.hidden * (out_dtype == Q4MOE_OUT_F32 ? 4 : 2);
+      if (!(xb < ye && yb < xe) && q4moe::decode_lds_bytes(d) <= kMaxDynLds &&
+          workspace_bytes >= q4moe::decode_workspace_bytes(d.hidden, d.inter, d.n_experts, d.top_k) &&
+          q4moe::decode_fits(d))
+        return hip_status(q4moe::run_moe_ffn_decode(d, X, Y, out_dtype == Q4MOE_OUT_BF16 ? q4moe::kOutBf16 : q4moe::kOutF32,
+                                                    ids_out, w_out, workspace, (hipStream_t)stream));
+    }
+    // the front launch's workgroups wait on each other: all must be resident together
+    if (!q4moe::decode_batch_fits(d, (int)B)) return Q4MOE_EUNSUPPORTED;
     return hip_status(q4moe::run_moe_ffn_decode_batch(d, X, (int)B, Y, out_dtype == Q4MOE_OUT_BF16, ids_out, w_out,
                                                       workspace, kMaxDynLds, (hipStream_t)stream));
   } catch (...) {

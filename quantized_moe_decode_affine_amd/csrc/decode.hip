@@ -28,6 +28,7 @@
 // words of an activation line are written by one store instruction.  The epoch
 // is agreed through per-group arrival counters in the workspace.  Every poll is
 // bounded: a lost flag yields a wrong result and a recorded timeout, never a hang.
+#include "handoff.h"
 #include "kernels.h"
 #include "topk.h"
 #include "vecstage.h"
@@ -43,8 +44,6 @@ namespace {
 #endif
 constexpr int kThreads = Q4MOE_DECODE_THREADS;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kEpochGroups = 8;
-constexpr unsigned kPollLimit = 1u << 18;  // ~0.25 s of polling
 
 constexpr int kMaxBlocks = 1024;
 constexpr int kOutRows = 8;       // output rows of one down block
@@ -77,9 +76,7 @@ constexpr int kCopies = Q4MOE_HANDOFF_COPIES;
 constexpr int kLogitCopyWords = kMaxExperts * kLogitStride + 64;  // words between logit copies (skewed)
 
 struct DecodeWs {
-  unsigned long long group_ctr[kEpochGroups][32];  // {epoch:hi32, arrivals:lo32}, one 256-byte slot each
-  unsigned timeouts;
-  unsigned pad[63];
+  HandoffHead h;  // epoch counters; the timeout count at byte 2048
   // Router logit of expert e: tag_logit[e * kLogitStride] = {epoch:hi32, fp32 bits:lo32}.
   // Each logit has a 64-byte line of its own: a line written by several workgroups
   // is observed several times more slowly than one written by a single store.
@@ -493,58 +490,6 @@ __device__ __forceinline__ float q8_down_row(const DecodeLayer& L, int n, const 
 
 // ------------------------------------------------------------ handoffs
 
-// Top-k of E logits by one wave, polling the epoch-tagged words that other
-// workgroups publish until every one carries `epoch` (bounded; a timeout is
-// counted).  Lane l holds ids [l*V, l*V + V) with its keys sorted in descending
-// order, so each of the k rounds is a wave-wide maximum of the lane heads and a
-// pop in the winning lane.  Equal logits resolve to the lower expert id: inside
-// a lane by the sort order, across lanes because the lowest matching lane wins.
-// Writes ids/weights (renormalised softmax of the kept logits) to LDS and, when
-// given, to ids_out/w_out.
-template <int V>
-__device__ __forceinline__ void wave_topk_tagged(const unsigned long long* tags, int E, int k, uint32_t epoch,
-                                                 unsigned* timeouts, int32_t* s_ids, float* s_w, int32_t* ids_out,
-                                                 float* w_out) {
-  const int lane = lane_id();
-  uint32_t key[V];
-  int id[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) id[j] = lane * V + j;
-  // device-coherent 8-byte loads, one per logit slot; slots past E read as zeros (bounds check)
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned long long*>(tags), 0, E * kLogitStride * 8, kBufferRsrcWord3);
-  for (unsigned spins = 0;; ++spins) {
-    bool ready = true;
-    uint2 t[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j)  // all loads in flight together
-      t[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, id[j] * kLogitStride * 8, 0,
-                                                                         kLoadDeviceScope));
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      key[j] = t[j].x;
-      ready &= id[j] >= E || t[j].y == epoch;
-    }
-    if (__all(ready)) break;
-    if (spins == kPollLimit) {
-      if (lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-#pragma unroll
-  for (int j = 0; j < V; ++j) key[j] = id[j] < E ? float_key(__uint_as_float(key[j])) : 0u;
-  wave_topk_keys<V>(key, id, k, s_ids, s_w);
-  if (lane < k) {
-    if (ids_out) ids_out[lane] = s_ids[lane];
-    if (w_out) w_out[lane] = s_w[lane];
-  }
-}
-
-__device__ __forceinline__ unsigned long long tag_word(uint32_t epoch, float v) {
-  return ((unsigned long long)epoch << 32) | __float_as_uint(v);
-}
-
 // Publish the activations gathered in LDS (s_act[m * 8 + r] = row r of unit m) as
 // tagged words, one 64-byte line per unit written by 8 lanes of one wave (the
 // waves take units in turn).  unit_slot(m) returns {slot, first row} of unit m.
@@ -596,7 +541,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   const size_t xf_off = (reinterpret_cast<const uint32_t*>(as + (size_t)nslot * CI) - smem + 3) & ~size_t(3);
   float* xf = reinterpret_cast<float*>(smem + xf_off);  // 8-bit shared expert: x as fp32 [H/64][kQ8Pad]
   float* af = xf + (size_t)(H >> 6) * kQ8Pad;           // 8-bit shared expert: its activations [I/64][kQ8Pad]
-  unsigned* timeouts = &p.ws->timeouts;
+  unsigned* timeouts = &p.ws->h.timeouts;
 
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
@@ -605,14 +550,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   // ---- epoch of this launch: the arrivals of one group agree on its counter's epoch
   // field.  Thread 0's arrival goes out right after the router loads; its result is
   // used after the dots.
-  const int eg = b % kEpochGroups;
-  const unsigned egsize = (NB - eg + kEpochGroups - 1) / kEpochGroups;
-  unsigned long long* ectr = &p.ws->group_ctr[eg][0];
-  auto finish_epoch = [&](unsigned long long old) {
-    if ((uint32_t)old == egsize - 1)
-      __hip_atomic_fetch_add(ectr, (1ull << 32) - egsize, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_epoch = (uint32_t)(old >> 32) + 1u;
-  };
+  auto finish_epoch = [&](unsigned long long old) { s_epoch = epoch_finish(&p.ws->h, b, NB, old); };
 
   const RowGeom gh = row_geom(CH);
   const RowGeom gd = row_geom(CI);
@@ -649,7 +587,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     }
   }
   unsigned long long arrival;
-  if (t == 0) arrival = __hip_atomic_fetch_add(ectr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == 0) arrival = epoch_arrive(&p.ws->h, b);
 
   // Shared gate/up units su = b, b + NB, ... (8 row pairs each): in the fast form the
   // loads of the first kShSlots passes go out into registers once the router rows are
@@ -854,10 +792,10 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     }
     // B: top-k from the tagged logits (every workgroup, redundantly)
     if (E <= 4 * kWave)
-      wave_topk_tagged<4>(p.ws->tag_logit + (size_t)(b % kCopies) * kLogitCopyWords, E, k, epoch, timeouts, s_ids, s_w, b == 0 ? p.ids_out : nullptr,
+      wave_topk_tagged<4, kLogitStride>(p.ws->tag_logit + (size_t)(b % kCopies) * kLogitCopyWords, E, k, epoch, timeouts, s_ids, s_w, b == 0 ? p.ids_out : nullptr,
                           b == 0 ? p.w_out : nullptr);
     else
-      wave_topk_tagged<kMaxExperts / kWave>(p.ws->tag_logit + (size_t)(b % kCopies) * kLogitCopyWords, E, k, epoch, timeouts, s_ids, s_w,
+      wave_topk_tagged<kMaxExperts / kWave, kLogitStride>(p.ws->tag_logit + (size_t)(b % kCopies) * kLogitCopyWords, E, k, epoch, timeouts, s_ids, s_w,
                                             b == 0 ? p.ids_out : nullptr, b == 0 ? p.w_out : nullptr);
     if (lane == 0 && has_shared) {
       s_ids[k] = -1;

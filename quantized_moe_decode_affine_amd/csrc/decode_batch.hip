@@ -2,17 +2,19 @@
 // request, decoded together (lily-qwen3.8-flash-next, "Running it": several
 // requests, four by default, decode in one step).
 //
-// Four launches on one stream, each reading what the previous one wrote:
-//   1 route: logits[b][e] for every token, each router row read once for all
-//     tokens (one row per wave);
-//   2 plan (one workgroup): the B top-k lists, the distinct experts they name
-//     in ascending id, then the shared expert, and per planned expert the slot
-//     of each token that chose it;
-//   3 gate/up: a workgroup takes a 32-row block of one planned expert: its
-//     weight loads are issued, the x of the tokens that chose the expert are
-//     staged, and each row is dotted with each of them; SwiGLU outputs go to
-//     act[b][slot][i] (fp32);
-//   4 down: a workgroup owns 8 output rows for a subset of the tokens; its
+// Two launches on one stream:
+//   1 front (one workgroup per CU, all resident together): every workgroup
+//     dots its router row(s) with every token and publishes the logits as
+//     epoch-tagged words (handoff.h); wave b then takes token b's top-k from
+//     the published logits, and every workgroup builds the same plan: the
+//     distinct experts named, in ascending id, then the shared expert, and per
+//     planned expert the slot of each token that chose it.  The gate/up row
+//     pairs of the planned experts are then spread over every wave of the grid
+//     (a wave takes one row pair, its 64 lanes a 32-column chunk each, with
+//     the next row pairs' loads in flight); each pair is dotted with the x of
+//     each token that chose the expert, and the SwiGLU outputs go to
+//     act[b][slot][i] (fp32).  Workgroup 0 writes the plan and the weights.
+//   2 down: a workgroup owns 8 output rows for a subset of the tokens; its
 //     waves issue the down-row loads of the planned experts those tokens
 //     chose, the SwiGLU outputs are staged exactly as hi/lo bfloat16 pairs, and
 //     each expert's rows are dotted with every token that chose it; the waves'
@@ -20,7 +22,9 @@
 // The weights are read once per step whatever the number of tokens sharing an
 // expert, which is what batching buys on a bandwidth-bound step.
 #include <algorithm>
+#include <mutex>
 
+#include "handoff.h"
 #include "kernels.h"
 #include "topk.h"
 #include "vecstage.h"
@@ -29,17 +33,14 @@ namespace q4moe {
 
 namespace {
 
-constexpr int kRouteWaves = 8;                 // one router row per wave; one wave per token for the top-k
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kGateUpRows = kWaves * 8;        // rows of one expert per gate/up workgroup (8 per wave)
-constexpr int kDownLanes = 8;                  // lanes per down row (groups sub, sub + 8, ...)
-constexpr int kDownRows = kWave / kDownLanes;  // output rows per down workgroup: one per lane octet
-constexpr int kDownPrefetch = 4;               // experts per wave whose down rows are loaded ahead
 constexpr int kBitWords = kMaxExperts / 32;
 constexpr int kMaxPlan = kMaxBatch * kMaxTopK + 1;  // distinct experts of a step, shared one included
+constexpr int kFrontThreads = 512;             // front launch
+constexpr int kFrontWaves = kFrontThreads / kWave;
+constexpr int kFrontSlots = 4;                 // gate/up row pairs per wave whose loads are in flight together
+constexpr int kLogitCopies = 8;                // copies of the tagged logits (workgroup b reads copy b % 8)
 
-// The step's plan, written by batch_plan_kernel (one workgroup) after the router launch.
+// The step's plan, built by every front workgroup and written out by workgroup 0.
 struct BatchPlan {
   int n;                                // planned experts (distinct routed ones, then the shared one)
   int n_routed;
@@ -47,14 +48,21 @@ struct BatchPlan {
   alignas(8) int8_t slot[kMaxPlan][kMaxBatch];  // slot of token b that chose planned expert d, or -1
 };
 
+// Head of the workspace: the front launch's epoch counters (timeout count at byte
+// 2048) and its tagged logits, logit (token b, expert e) at word b * E + e of a copy.
+struct FrontWs {
+  HandoffHead h;
+  unsigned long long tag_logit[kLogitCopies][kMaxBatch * kMaxExperts];
+};
+
 struct BatchParams {
   DecodeLayer L;
   const uint16_t* X;  // [B][H]
   int B;
-  float* logits;      // [B][E]
+  FrontWs* fws;
   BatchPlan* plan;
   float* wts;         // [B][k+1]: routing weights, then the shared expert's weight
-  float* act;         // [B][nslot][I]
+  float* act;         // [B][nslot]: I / 32 chunk images of 32 words (16 hi, 16 lo bf16 pair words)
   void* y;            // [B][H]
   int out_bf16;
   int32_t* ids_out;   // nullable [B][k]
@@ -63,100 +71,113 @@ struct BatchParams {
 };
 
 // ---------------------------------------------------------------- launch 1
-// Wave w of workgroup r: logits[b][8r + w] = router[8r + w] . X[b] for every b < NB; with
-// kQ8 the router is the layer's 8-bit affine matrix (16-code chunks per lane, each inside
-// one 64-column group: scale * sum(x q) + bias * sum(x)).
-template <int NB, bool kQ8>
-__global__ __launch_bounds__(kRouteWaves * kWave) void batch_route_kernel(BatchParams p) {
-  const int H = p.L.hidden, E = p.L.n_experts;
-  const int lane = lane_id(), wv = threadIdx.x / kWave;
-  const int e = blockIdx.x * kRouteWaves + wv;
-  float acc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-  if constexpr (kQ8) {
-    const int G = H >> 6, er = min(e, E - 1);
-    const uint4* r = reinterpret_cast<const uint4*>(p.L.router_q8.codes) + (size_t)er * (H >> 4);
-    const uint16_t* sr = p.L.router_q8.scales + (size_t)er * G;
-    const uint16_t* br = p.L.router_q8.biases + (size_t)er * G;
-    for (int c = lane; c < (H >> 4); c += kWave) {
-      const uint4 w = r[c];
-      const float sc = bf16_bits_to_f32(sr[c >> 2]), bi = bf16_bits_to_f32(br[c >> 2]);
-      const uint32_t cw[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint4 xa = reinterpret_cast<const uint4*>(p.X + (size_t)b * H)[2 * c];
-        const uint4 xb = reinterpret_cast<const uint4*>(p.X + (size_t)b * H)[2 * c + 1];
-        const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-        float pq = 0.f, xs = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float xi = bf16_bits_to_f32((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-          xs += xi;
-          pq = fmaf(xi, (float)((cw[i >> 2] >> (8 * (i & 3))) & 0xFFu), pq);
-        }
-        acc[b] += fmaf(sc, pq, bi * xs);
-      }
-    }
-  } else {
-  const uint4* r = reinterpret_cast<const uint4*>(p.L.router + (size_t)min(e, E - 1) * H);
-  const int nc = H >> 3;  // 16-byte chunks per row
-  constexpr int Q = 4;    // chunks per lane in flight
-  for (int c0 = 0; c0 < nc; c0 += Q * kWave) {
-    uint4 w[Q], v[NB][Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int c = c0 + q * kWave + lane;
-      const bool ok = c < nc;
-      w[q] = ok ? r[c] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        v[b][q] = ok ? reinterpret_cast<const uint4*>(p.X + (size_t)b * H)[c] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int q = 0; q < Q; ++q)
-        acc[b] = dot2_bf16(w[q].w, v[b][q].w,
-                           dot2_bf16(w[q].z, v[b][q].z, dot2_bf16(w[q].y, v[b][q].y, dot2_bf16(w[q].x, v[b][q].x, acc[b]))));
-  }
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const float l = group_sum_rt(acc[b], 6);
-    if (lane == 0 && e < E) p.logits[(size_t)b * E + e] = l;
-  }
-}
+// One gate/up row pair: this lane's 32-column chunk of each row (4-bit: 16 bytes;
+// 8-bit shared rows: 32 bytes, g/g2 and u/u2) and the chunk's group scale and bias.
+struct GuRegs {
+  uint4 g, u, g2, u2;
+  uint32_t gs, gb, us, ub;
+};
 
-// ---------------------------------------------------------------- launch 2
-// One workgroup plans the step: wave b takes token b's top-k; the distinct
-// experts named are ranked by id through a bitmap with per-word prefix counts;
-// the plan (per planned expert its id and the slot of each token that chose
-// it, the shared expert last) is built in LDS and written out once.
-template <int NB, int V>
-__global__ __launch_bounds__(kRouteWaves * kWave) void batch_plan_kernel(BatchParams p) {
+template <int NB, bool kLong>
+__device__ __forceinline__ void batch_front(const BatchParams& p) {
+  extern __shared__ __align__(16) uint32_t smem[];
   __shared__ int32_t s_id[kMaxBatch][kMaxTopK];
   __shared__ float s_w[kMaxBatch][kMaxTopK];
+  __shared__ float s_rpart[kMaxBatch][kFrontWaves];
   __shared__ uint32_t s_bits[kBitWords];
   __shared__ int s_pre[kBitWords + 1];
-  __shared__ int8_t s_slot[kMaxPlan][kMaxBatch];
+  __shared__ alignas(8) int8_t s_slot[kMaxPlan][kMaxBatch];
   __shared__ int32_t s_expert[kMaxPlan];
-  const int E = p.L.n_experts, k = p.L.top_k;
-  const int lane = lane_id(), wv = threadIdx.x / kWave;
-  if (wv < NB) {
-    const int b = wv;
-    wave_topk_sorted<V>(p.logits + (size_t)b * E, E, k, s_id[b], s_w[b]);
-    if (lane < k) {
-      p.wts[b * (k + 1) + lane] = s_w[b][lane];
-      if (p.ids_out) p.ids_out[b * k + lane] = s_id[b][lane];
-      if (p.w_out) p.w_out[b * k + lane] = s_w[b][lane];
+  __shared__ uint32_t s_epoch;
+
+  const DecodeLayer& L = p.L;
+  const int H = L.hidden, I = L.inter, E = L.n_experts, k = L.top_k;
+  const int CH = H >> 5, G = H >> 6;
+  // (the wave index read through a scalar register: the compiler then knows every task
+  // index below is wave-uniform, so the branches on them stay scalar)
+  const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), t = threadIdx.x;
+  const int NBk = gridDim.x, b = blockIdx.x;
+  FrontWs* ws = p.fws;
+  constexpr int ST = chunk_stride<1>();
+  uint32_t* xp = smem;                                              // [NB][CH][ST] x as permuted bf16 pairs
+  float* xs = reinterpret_cast<float*>(xp + (size_t)NB * CH * ST);  // [NB][CH] chunk sums
+
+  unsigned long long arrival = 0;
+  if (t == 0) arrival = epoch_arrive(&ws->h, b);
+
+  // ---- A: router rows e = b, b + NBk, ... dotted with every token, published as tagged words
+  const int nrows = b < E ? (E - 1 - b) / NBk + 1 : 0;
+  for (int m = 0; m < nrows; ++m) {
+    const int e = b + m * NBk;
+    float acc[NB];
+#pragma unroll
+    for (int tok = 0; tok < NB; ++tok) acc[tok] = 0.f;
+    if (L.router_q8.codes) {  // 8-bit router: 16-code chunks, each inside one 64-column group
+      const uint4* r = reinterpret_cast<const uint4*>(L.router_q8.codes) + (size_t)e * (H >> 4);
+      for (int c = t; c < (H >> 4); c += kFrontThreads) {
+        const uint4 w = r[c];
+        const float sc = bf16_bits_to_f32(L.router_q8.scales[(size_t)e * G + (c >> 2)]);
+        const float bi = bf16_bits_to_f32(L.router_q8.biases[(size_t)e * G + (c >> 2)]);
+        const uint32_t cw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int tok = 0; tok < NB; ++tok) {
+          const uint4 xa = reinterpret_cast<const uint4*>(p.X + (size_t)tok * H)[2 * c];
+          const uint4 xb = reinterpret_cast<const uint4*>(p.X + (size_t)tok * H)[2 * c + 1];
+          const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+          float pq = 0.f, xsum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float xi = bf16_bits_to_f32((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+            xsum += xi;
+            pq = fmaf(xi, (float)((cw[i >> 2] >> (8 * (i & 3))) & 0xFFu), pq);
+          }
+          acc[tok] += fmaf(sc, pq, bi * xsum);
+        }
+      }
+    } else {
+      const uint4* r = reinterpret_cast<const uint4*>(L.router) + (size_t)e * (H >> 3);
+      for (int c = t; c < (H >> 3); c += kFrontThreads) {
+        const uint4 w = r[c];
+#pragma unroll
+        for (int tok = 0; tok < NB; ++tok) {
+          const uint4 v = reinterpret_cast<const uint4*>(p.X + (size_t)tok * H)[c];
+          acc[tok] = dot2_bf16(w.w, v.w, dot2_bf16(w.z, v.z, dot2_bf16(w.y, v.y, dot2_bf16(w.x, v.x, acc[tok]))));
+        }
+      }
     }
-    // the shared expert's weight: 1, or sigmoid(sh_gate_w . x_b) when the layer has the gate
+#pragma unroll
+    for (int tok = 0; tok < NB; ++tok) {
+      const float r = group_sum_rt(acc[tok], 6);
+      if (lane == 0) s_rpart[tok][wv] = r;
+    }
+    if (t == 0 && m == 0) s_epoch = epoch_finish(&ws->h, b, NBk, arrival);
+    lds_sync();
+    if (t < NB * kLogitCopies) {  // one thread per (token, copy); the waves' partials in a fixed order
+      const int tok = t / kLogitCopies, c = t % kLogitCopies;
+      float v = s_rpart[tok][0];
+#pragma unroll
+      for (int w = 1; w < kFrontWaves; ++w) v += s_rpart[tok][w];
+      __hip_atomic_store(&ws->tag_logit[c][(size_t)tok * E + e], tag_word(s_epoch, v), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lds_sync();  // s_rpart is reused
+  }
+  if (t == 0 && nrows == 0) s_epoch = epoch_finish(&ws->h, b, NBk, arrival);
+  // x of every token, for the gate/up dots (while the other workgroups' logits arrive)
+  for (int i = t; i < NB * CH; i += kFrontThreads) {
+    const int tok = i / CH, c = i - tok * CH;
+    stage_bf16_chunk(p.X + (size_t)tok * H, c, xp + (size_t)i * ST, xs + i);
+  }
+  lds_sync();
+  const uint32_t epoch = s_epoch;
+
+  // ---- B: wave tok takes token tok's top-k (and its shared-expert weight)
+  if (wv < NB) {
+    const int tok = wv;
     float sw = 1.0f;
-    if (p.L.sh_gate_w) {
-      const int H = p.L.hidden;
-      const uint4* gw = reinterpret_cast<const uint4*>(p.L.sh_gate_w);
-      const uint4* gx = reinterpret_cast<const uint4*>(p.X + (size_t)b * H);
+    if (L.sh_gate_w) {  // sigmoid(sh_gate_w . x)
+      const uint4* gw = reinterpret_cast<const uint4*>(L.sh_gate_w);
+      const uint4* gx = reinterpret_cast<const uint4*>(p.X + (size_t)tok * H);
       float d0 = 0.f, d1 = 0.f;
       for (int c = lane; c < (H >> 3); c += kWave) {
         const uint4 a = gw[c], x = gx[c];
@@ -165,18 +186,30 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void batch_plan_kernel(BatchPa
         d0 = dot2_bf16(a.z, x.z, d0);
         d1 = dot2_bf16(a.w, x.w, d1);
       }
-      const float d = group_sum_rt(d0 + d1, 6);
-      sw = 1.0f / (1.0f + __expf(-d));
+      sw = 1.0f / (1.0f + __expf(-group_sum_rt(d0 + d1, 6)));
     }
-    if (lane == 0) p.wts[b * (k + 1) + k] = sw;
+    const unsigned long long* tags = ws->tag_logit[b % kLogitCopies] + (size_t)tok * E;
+    int32_t* io = b == 0 && p.ids_out ? p.ids_out + tok * k : nullptr;
+    float* wo = b == 0 && p.w_out ? p.w_out + tok * k : nullptr;
+    if (E <= 4 * kWave)
+      wave_topk_tagged<4, 1>(tags, E, k, epoch, &ws->h.timeouts, s_id[tok], s_w[tok], io, wo);
+    else if (E <= 8 * kWave)
+      wave_topk_tagged<8, 1>(tags, E, k, epoch, &ws->h.timeouts, s_id[tok], s_w[tok], io, wo);
+    else
+      wave_topk_tagged<kMaxExperts / kWave, 1>(tags, E, k, epoch, &ws->h.timeouts, s_id[tok], s_w[tok], io, wo);
+    if (b == 0) {
+      if (lane < k) p.wts[tok * (k + 1) + lane] = s_w[tok][lane];
+      if (lane == 0) p.wts[tok * (k + 1) + k] = sw;
+    }
   }
-  for (int i = threadIdx.x; i < kBitWords; i += blockDim.x) s_bits[i] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < NB * k; i += blockDim.x) {
+  // ---- the plan (every workgroup alike): distinct experts ranked by id through a bitmap
+  for (int i = t; i < kBitWords; i += kFrontThreads) s_bits[i] = 0u;
+  lds_sync();
+  for (int i = t; i < NB * k; i += kFrontThreads) {
     const int id = s_id[i / k][i % k];
     atomicOr(&s_bits[id >> 5], 1u << (id & 31));
   }
-  __syncthreads();
+  lds_sync();
   if (wv == 0) {  // exclusive prefix of the per-word counts
     const int c = lane < kBitWords ? __popc(s_bits[lane]) : 0;
     int incl = c;
@@ -188,350 +221,345 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void batch_plan_kernel(BatchPa
     if (lane < kBitWords) s_pre[lane] = incl - c;
     if (lane == kWave - 1) s_pre[kBitWords] = incl;
   }
-  __syncthreads();
+  lds_sync();
   const int nd = s_pre[kBitWords];
-  const int n = nd + (p.L.has_shared ? 1 : 0);
-  for (int i = threadIdx.x; i < n * kMaxBatch; i += blockDim.x) {
-    const int d = i / kMaxBatch, b = i - d * kMaxBatch;
-    s_slot[d][b] = (int8_t)(d == nd && b < NB ? k : -1);  // the shared expert serves every token with weight 1
-    if (b == 0 && d == nd) s_expert[d] = -1;
+  const int n = nd + (L.has_shared ? 1 : 0);
+  for (int i = t; i < n * kMaxBatch; i += kFrontThreads) {
+    const int d = i / kMaxBatch, tok = i - d * kMaxBatch;
+    s_slot[d][tok] = (int8_t)(d == nd && tok < NB ? k : -1);  // the shared expert serves every token
+    if (tok == 0 && d == nd) s_expert[d] = -1;
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < NB * k; i += blockDim.x) {
-    const int b = i / k, j = i - b * k, id = s_id[b][j];
+  lds_sync();
+  for (int i = t; i < NB * k; i += kFrontThreads) {
+    const int tok = i / k, j = i - tok * k, id = s_id[tok][j];
     const int d = s_pre[id >> 5] + __popc(s_bits[id >> 5] & ((1u << (id & 31)) - 1u));
-    s_slot[d][b] = (int8_t)j;
+    s_slot[d][tok] = (int8_t)j;
     s_expert[d] = id;  // every token naming the expert writes the same value
   }
-  __syncthreads();
-  BatchPlan* plan = p.plan;
-  for (int i = threadIdx.x; i < n * kMaxBatch; i += blockDim.x)
-    plan->slot[i / kMaxBatch][i % kMaxBatch] = s_slot[i / kMaxBatch][i % kMaxBatch];
-  for (int i = threadIdx.x; i < n; i += blockDim.x) plan->expert[i] = s_expert[i];
-  if (threadIdx.x == 0) {
-    plan->n = n;
-    plan->n_routed = nd;
-  }
-}
-
-// ---------------------------------------------------------------- launch 3
-// The 8-bit shared expert's gate/up rows i0 + lane/8 of this workgroup's block (planned
-// expert d; every token chose it): lane takes groups lane%8, lane%8 + 8, ...; a group is 64
-// code bytes per matrix, dotted with the tokens' staged x as exact bf16 code pairs.
-__device__ __forceinline__ void batch_gate_up_q8_shared(const BatchParams& p, int rblk, int d) {
-  extern __shared__ __align__(16) uint32_t smem[];
-  const int H = p.L.hidden, I = p.L.inter, k = p.L.top_k, B = p.B;
-  const int lane = lane_id(), wv = threadIdx.x / kWave;
-  const int CH = H >> 5, G = H >> 6;
-  const int i0 = rblk * kGateUpRows + wv * 8;
-  const int row = min(i0 + (lane >> 3), I - 1), gl = lane & 7;
-  const uint4* gq = reinterpret_cast<const uint4*>(p.L.sh_gate.codes) + (int64_t)row * (H >> 4);
-  const uint4* uq = reinterpret_cast<const uint4*>(p.L.sh_up.codes) + (int64_t)row * (H >> 4);
-  const uint16_t* gs = p.L.sh_gate.scales + (int64_t)row * G;
-  const uint16_t* gb = p.L.sh_gate.biases + (int64_t)row * G;
-  const uint16_t* us = p.L.sh_up.scales + (int64_t)row * G;
-  const uint16_t* ub = p.L.sh_up.biases + (int64_t)row * G;
-  // stage x of every token (all chose the shared expert)
-  constexpr int ST = chunk_stride<1>();
-  uint32_t* vp = smem;
-  float* vs = reinterpret_cast<float*>(vp + (size_t)B * CH * ST);
-  for (int i = threadIdx.x; i < B * CH; i += blockDim.x) {
-    const int b = i / CH, c = i - b * CH;
-    stage_bf16_chunk(p.X + (size_t)b * H, c, vp + (size_t)i * ST, vs + i);
-  }
-  __syncthreads();
-  float ag[kMaxBatch], au[kMaxBatch];
-#pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t) ag[t] = au[t] = 0.f;
-  for (int g = gl; g < G; g += 8) {
-    uint4 cg[4], cu[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      cg[q] = gq[4 * g + q];
-      cu[q] = uq[4 * g + q];
-    }
-    const float sg = bf16_bits_to_f32(gs[g]), bg = bf16_bits_to_f32(gb[g]);
-    const float su = bf16_bits_to_f32(us[g]), bu = bf16_bits_to_f32(ub[g]);
-#pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) {
-      if (t >= B) break;
-      const uint32_t* v = vp + ((size_t)t * CH + 2 * g) * ST;
-      const float vsum = vs[t * CH + 2 * g] + vs[t * CH + 2 * g + 1];
-      const float pg = q8_chunk_pdot<1>(cg[0], cg[1], v) + q8_chunk_pdot<1>(cg[2], cg[3], v + ST);
-      const float pu = q8_chunk_pdot<1>(cu[0], cu[1], v) + q8_chunk_pdot<1>(cu[2], cu[3], v + ST);
-      ag[t] += fmaf(sg, pg, bg * vsum);
-      au[t] += fmaf(su, pu, bu * vsum);
+  lds_sync();
+  if (b == 0) {
+    BatchPlan* plan = p.plan;
+    for (int i = t; i < n * kMaxBatch; i += kFrontThreads)
+      plan->slot[i / kMaxBatch][i % kMaxBatch] = s_slot[i / kMaxBatch][i % kMaxBatch];
+    for (int i = t; i < n; i += kFrontThreads) plan->expert[i] = s_expert[i];
+    if (t == 0) {
+      plan->n = n;
+      plan->n_routed = nd;
     }
   }
-  const int nslot = k + 1;
-  const int i = i0 + (lane >> 3);
-#pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t) {
-    if (t >= B) break;
-    const float g = group_sum_rt(ag[t], 3), u = group_sum_rt(au[t], 3);
-    if ((lane & 7) == 0 && i < I) p.act[((size_t)t * nslot + k) * I + i] = silu(g) * u;
-  }
-  (void)d;
-}
 
-__global__ __launch_bounds__(kThreads) void batch_gate_up_kernel(BatchParams p) {
-  extern __shared__ __align__(16) uint32_t smem[];
-  const int H = p.L.hidden, I = p.L.inter, k = p.L.top_k, B = p.B;
-  const int lane = lane_id(), wv = threadIdx.x / kWave;
-  const int per_expert = (I + kGateUpRows - 1) / kGateUpRows;
-  const int d = blockIdx.x / per_expert, rblk = blockIdx.x - d * per_expert;
-  const BatchPlan* plan = p.plan;
-  if (d >= plan->n) return;  // beyond this step's experts (uniform)
-  const int e = plan->expert[d];
-
-  if (e < 0 && p.L.sh_q8) {  // the shared expert in 8-bit codes
-    batch_gate_up_q8_shared(p, rblk, d);
-    return;
-  }
-  // this lane's weights: row i0 + lane/8, groups lane%8 + 8q
-  const Q4Mat& gm = e >= 0 ? p.L.gate : p.L.sh_gate;
-  const Q4Mat& um = e >= 0 ? p.L.up : p.L.sh_up;
-  const int CH = H >> 5, G = H >> 6;
-  const int i0 = rblk * kGateUpRows + wv * 8;
-  const int row = min(i0 + (lane >> 3), I - 1), gl = lane & 7;
-  const int64_t oc = (e >= 0 ? e : 0) * (int64_t)I * (H >> 3), og = (e >= 0 ? e : 0) * (int64_t)I * G;
-  const uint4* gc = reinterpret_cast<const uint4*>(gm.codes + oc) + (int64_t)row * CH;
-  const uint4* uc = reinterpret_cast<const uint4*>(um.codes + oc) + (int64_t)row * CH;
-  const uint16_t* gs = gm.scales + og + (int64_t)row * G;
-  const uint16_t* gb = gm.biases + og + (int64_t)row * G;
-  const uint16_t* us = um.scales + og + (int64_t)row * G;
-  const uint16_t* ub = um.biases + og + (int64_t)row * G;
-  constexpr int IT = 4;  // groups per lane per round (hidden 2048: one round)
-  uint4 cg[IT][2], cu[IT][2];
-  uint32_t sg[IT], bg[IT], su[IT], bu[IT];
-  auto load = [&](int base) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < IT; ++q) {
-      const int g = min(base + gl + 8 * q, G - 1);  // groups past the end: loaded, not used
-      cg[q][0] = gc[2 * g];
-      cg[q][1] = gc[2 * g + 1];
-      cu[q][0] = uc[2 * g];
-      cu[q][1] = uc[2 * g + 1];
-      sg[q] = gs[g];
-      bg[q] = gb[g];
-      su[q] = us[g];
-      bu[q] = ub[g];
-    }
+  // ---- C: gate/up row pairs tau = d * I + i over every wave of the grid, pass q taking
+  // tau = (q * NBk + b) * waves + wave; each wave keeps kFrontSlots passes of loads in
+  // flight.  4-bit experts (routed, and a 4-bit shared one) take that pipelined loop; an
+  // 8-bit shared expert's rows (plan entry nd) are spread over the waves the same way,
+  // one pass at a time.
+  const int nslot = k + (L.has_shared ? 1 : 0);
+  const bool q8sh = L.has_shared && L.sh_q8;
+  const int ntask = (q8sh ? nd : n) * I;  // 4-bit row pairs
+  const int per_pass = NBk * kFrontWaves;
+  const int npass = (ntask + per_pass - 1) / per_pass;
+  const int64_t mat_codes = (int64_t)I * (H >> 3), mat_groups = (int64_t)I * G;
+  const int c0 = min(lane, CH - 1);  // this lane's first chunk (lanes past CH: a valid chunk, not used)
+  auto task_of = [&](int q) { return (q * NBk + b) * kFrontWaves + wv; };
+  // this lane's chunk c of row pair (d, i) of a 4-bit expert (routed, or the shared one)
+  auto load_chunk = [&](int d, int i, int c) __attribute__((always_inline)) {
+    GuRegs r;
+    const int e = __builtin_amdgcn_readfirstlane(s_expert[d]);
+    const int64_t oc = e >= 0 ? e * mat_codes : 0, og = e >= 0 ? e * mat_groups : 0;
+    const uint32_t* gc = e >= 0 ? L.gate.codes : L.sh_gate.codes;
+    const uint32_t* uc = e >= 0 ? L.up.codes : L.sh_up.codes;
+    const uint16_t* gsp = e >= 0 ? L.gate.scales : L.sh_gate.scales;
+    const uint16_t* gbp = e >= 0 ? L.gate.biases : L.sh_gate.biases;
+    const uint16_t* usp = e >= 0 ? L.up.scales : L.sh_up.scales;
+    const uint16_t* ubp = e >= 0 ? L.up.biases : L.sh_up.biases;
+    r.g = reinterpret_cast<const uint4*>(gc + oc + (int64_t)i * (H >> 3))[c];
+    r.u = reinterpret_cast<const uint4*>(uc + oc + (int64_t)i * (H >> 3))[c];
+    r.g2 = r.g;
+    r.u2 = r.u;
+    r.gs = gsp[og + (int64_t)i * G + (c >> 1)];
+    r.gb = gbp[og + (int64_t)i * G + (c >> 1)];
+    r.us = usp[og + (int64_t)i * G + (c >> 1)];
+    r.ub = ubp[og + (int64_t)i * G + (c >> 1)];
+    return r;
   };
-  load(0);
-
-  // the slots by which tokens 0..7 chose this expert (-1: not chosen), the same in every lane
-  const uint2 sw = *reinterpret_cast<const uint2*>(&plan->slot[d][0]);
-  auto slot_of = [&](int b) __attribute__((always_inline)) {
-    return (int)(int8_t)(((b < 4 ? sw.x : sw.y) >> (8 * (b & 3))) & 0xFFu);
+  // the same for the 8-bit shared expert's row pair i: 32 code bytes per chunk
+  auto load_chunk8 = [&](int i, int c) __attribute__((always_inline)) {
+    GuRegs r;
+    const uint4* gq = reinterpret_cast<const uint4*>(L.sh_gate.codes) + (int64_t)i * (H >> 4) + 2 * c;
+    const uint4* uq = reinterpret_cast<const uint4*>(L.sh_up.codes) + (int64_t)i * (H >> 4) + 2 * c;
+    r.g = gq[0];
+    r.g2 = gq[1];
+    r.u = uq[0];
+    r.u2 = uq[1];
+    r.gs = L.sh_gate.scales[(int64_t)i * G + (c >> 1)];
+    r.gb = L.sh_gate.biases[(int64_t)i * G + (c >> 1)];
+    r.us = L.sh_up.scales[(int64_t)i * G + (c >> 1)];
+    r.ub = L.sh_up.biases[(int64_t)i * G + (c >> 1)];
+    return r;
   };
-  uint32_t chosen = 0;  // bit b: token b chose this expert
+  // row pair (d, i) against the x of each token that chose expert d; SwiGLU into act
+  auto compute_pair = [&](int d, int i, const GuRegs r0, bool q8) __attribute__((always_inline)) {
+    uint2 sl = *reinterpret_cast<const uint2*>(&s_slot[d][0]);
+    sl.x = __builtin_amdgcn_readfirstlane(sl.x);
+    sl.y = __builtin_amdgcn_readfirstlane(sl.y);
+    auto slot_of = [&](int tok) { return (int)(int8_t)(((tok < 4 ? sl.x : sl.y) >> (8 * (tok & 3))) & 0xFFu); };
+    float ag[NB], au[NB];
 #pragma unroll
-  for (int b = 0; b < kMaxBatch; ++b) chosen |= (b < B && slot_of(b) >= 0 ? 1u : 0u) << b;
-
-  // stage x of those tokens at their token index: [B] x [CH][ST1] pairs, then [B] x [CH] sums
-  constexpr int ST = chunk_stride<1>();
-  uint32_t* vp = smem;
-  float* vs = reinterpret_cast<float*>(vp + (size_t)B * CH * ST);
-  for (int i = threadIdx.x; i < B * CH; i += blockDim.x) {
-    const int b = i / CH, c = i - b * CH;
-    if (chosen >> b & 1u) stage_bf16_chunk(p.X + (size_t)b * H, c, vp + (size_t)i * ST, vs + i);
-  }
-  __syncthreads();
-
-  float ag[kMaxBatch], au[kMaxBatch];
+    for (int tok = 0; tok < NB; ++tok) ag[tok] = au[tok] = 0.f;
+    auto accumulate = [&](const GuRegs& r, int c) __attribute__((always_inline)) {
 #pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t) ag[t] = au[t] = 0.f;
-  for (int base = 0; base < G; base += 8 * IT) {  // wave-uniform trip count
-    if (base > 0) load(base);
-#pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) {
-      if (!(chosen >> t & 1u)) continue;
-      const uint32_t* vt = vp + (size_t)t * CH * ST;
-      const float* st = vs + t * CH;
-#pragma unroll
-      for (int q = 0; q < IT; ++q) {
-        const int g = base + gl + 8 * q;
-        const int gq = min(g, G - 1);
-        const uint32_t* v = vt + 2 * gq * ST;
-        const float vsum = st[2 * gq] + st[2 * gq + 1];
-        const float tg = affine_term(chunk_pdot<1>(cg[q][0], v) + chunk_pdot<1>(cg[q][1], v + ST), vsum, sg[q], bg[q]);
-        const float tu = affine_term(chunk_pdot<1>(cu[q][0], v) + chunk_pdot<1>(cu[q][1], v + ST), vsum, su[q], bu[q]);
-        if (g < G) {
-          ag[t] += tg;
-          au[t] += tu;
+      for (int tok = 0; tok < NB; ++tok) {
+        if (slot_of(tok) < 0) continue;  // (uniform over the wave)
+        const uint32_t* v = xp + ((size_t)tok * CH + c) * ST;
+        const float vs = xs[tok * CH + c];
+        if (q8) {  // w = s q + b
+          ag[tok] += fmaf(bf16_bits_to_f32(r.gs), q8_chunk_pdot<1>(r.g, r.g2, v), bf16_bits_to_f32(r.gb) * vs);
+          au[tok] += fmaf(bf16_bits_to_f32(r.us), q8_chunk_pdot<1>(r.u, r.u2, v), bf16_bits_to_f32(r.ub) * vs);
+        } else {
+          ag[tok] += affine_term(chunk_pdot<1>(r.g, v), vs, r.gs, r.gb);
+          au[tok] += affine_term(chunk_pdot<1>(r.u, v), vs, r.us, r.ub);
         }
       }
+    };
+    if (lane < CH) accumulate(r0, lane);
+    // rows longer than 2048 columns (kLong): the further chunks, loaded here (a loop that
+    // loads makes the compiler wait for every load in flight at its head, so the form
+    // for rows of at most 2048 columns has none)
+    if constexpr (kLong)
+      for (int c = lane + kWave; c < CH; c += kWave) accumulate(q8 ? load_chunk8(i, c) : load_chunk(d, i, c), c);
+#pragma unroll
+    for (int tok = 0; tok < NB; ++tok) {
+      const int j = slot_of(tok);
+      if (j < 0) continue;
+      const float g = group_sum_rt(ag[tok], 6), u = group_sum_rt(au[tok], 6);
+      if (lane == 0) {  // into the staged image: hi/lo bf16 parts at the permuted pair positions
+        const float a = silu(g) * u;
+        const uint32_t hb = f32_to_bf16_bits(a), lb = f32_to_bf16_bits(a - bf16_bits_to_f32(hb));
+        uint16_t* img = reinterpret_cast<uint16_t*>(p.act) + ((size_t)(tok * nslot + j) * I + (i & ~31)) * 2;
+        const int w = i & 7, off = (4 * ((i & 31) >> 3) + (w & 3)) * 2 + (w >> 2);
+        img[off] = (uint16_t)hb;
+        img[off + 32] = (uint16_t)lb;
+      }
+    }
+  };
+  // loads are issued unconditionally (a task past the end reads the last valid row pair,
+  // unused): a load behind a branch makes the compiler wait for every load in flight
+  const int last = max(ntask - 1, 0);
+  GuRegs rr[kFrontSlots];
+#pragma unroll
+  for (int s = 0; s < kFrontSlots; ++s) {
+    const int tau = min(task_of(s), last);
+    rr[s] = load_chunk(tau / I, tau % I, c0);
+  }
+  if (q8sh) {  // the 8-bit shared expert's row pairs, loaded behind the first 4-bit passes
+    for (int q = 0;; ++q) {
+      const int i = task_of(q);
+      if (i >= I) break;
+      compute_pair(nd, i, load_chunk8(i, c0), true);
     }
   }
-  const int nslot = k + (p.L.has_shared ? 1 : 0);
-  const int i = i0 + (lane >> 3);
+  for (int q0 = 0; q0 < npass; q0 += kFrontSlots) {
 #pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t) {
-    if (!(chosen >> t & 1u)) continue;
-    const float g = group_sum_rt(ag[t], 3), u = group_sum_rt(au[t], 3);
-    if ((lane & 7) == 0 && i < I) p.act[((size_t)t * nslot + slot_of(t)) * I + i] = silu(g) * u;
+    for (int s = 0; s < kFrontSlots; ++s) {
+      const int tau = task_of(q0 + s), tau2 = min(task_of(q0 + s + kFrontSlots), last);
+      if (tau < ntask) compute_pair(tau / I, tau % I, rr[s], false);
+      rr[s] = load_chunk(tau2 / I, tau2 % I, c0);
+    }
   }
 }
 
-// ---------------------------------------------------------------- launch 4
-__global__ __launch_bounds__(kThreads) void batch_down_kernel(BatchParams p) {
+// NB tokens; kLong: hidden above 2048 (more than one 32-column chunk per lane)
+#define Q4MOE_FRONT_KERNEL(NB)                                                                       \
+  __global__ __launch_bounds__(kFrontThreads) void batch_front_kernel_##NB(BatchParams p) { batch_front<NB, false>(p); } \
+  __global__ __launch_bounds__(kFrontThreads) void batch_front_long_kernel_##NB(BatchParams p) { batch_front<NB, true>(p); }
+Q4MOE_FRONT_KERNEL(1)
+Q4MOE_FRONT_KERNEL(2)
+Q4MOE_FRONT_KERNEL(3)
+Q4MOE_FRONT_KERNEL(4)
+Q4MOE_FRONT_KERNEL(5)
+Q4MOE_FRONT_KERNEL(6)
+Q4MOE_FRONT_KERNEL(7)
+Q4MOE_FRONT_KERNEL(8)
+#undef Q4MOE_FRONT_KERNEL
+
+// ---------------------------------------------------------------- launch 2
+// Workgroup (x, y) owns output rows 8x .. 8x + 7 for tokens y*tpp .. of the pass.  The
+// planned experts that a token of the pass chose are listed; each listed expert's 8 rows
+// are two tasks of 4 rows (16 lanes a row, one 32-column chunk a lane; an 8-bit shared
+// row's chunk is 32 bytes), spread over the waves, and the loads of the first
+// kDownSlots tasks of every wave are issued before the SwiGLU outputs are staged.  Each
+// task writes the 4-row dot of every token of the pass that chose the expert to
+// s_red[token][slot][row]; the output is the fixed-order weighted sum over the slots.
+constexpr int kDownThreads = 1024;
+constexpr int kDownWaves = kDownThreads / kWave;
+constexpr int kDownSlots = 6;     // tasks per wave whose loads are issued ahead
+constexpr int kDownRowLanes = 16;  // lanes per down row
+constexpr int kDownTaskRows = kWave / kDownRowLanes;  // rows of one task
+constexpr int kDownRows = 8;      // output rows per workgroup
+
+struct DnRegs {
+  uint4 c, c2;  // c2: the second 16 bytes of an 8-bit row's chunk (else c again)
+  uint32_t s, b;
+};
+
+template <bool kLong>
+__device__ __forceinline__ void batch_down(const BatchParams& p) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ float s_w[kMaxBatch][kMaxTopK + 1];
-  __shared__ float s_red[kWaves][kMaxBatch][kDownRows];
-  __shared__ int16_t s_list[kMaxPlan];
+  __shared__ float s_red[kMaxBatch][kMaxTopK + 1][kDownRows];
+  __shared__ alignas(8) int8_t s_slot[kMaxPlan][kMaxBatch];
+  __shared__ int32_t s_expert[kMaxPlan];
+  __shared__ int16_t s_list[kMaxPlan * kMaxBatch];  // (planned expert << 3 | token of the pass)
   __shared__ int s_nlist;
 
-  const int H = p.L.hidden, I = p.L.inter, k = p.L.top_k;
-  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const DecodeLayer& L = p.L;
+  const int H = L.hidden, I = L.inter, k = L.top_k;
+  const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), t = threadIdx.x;
   const int b0 = blockIdx.y * p.tpp, nb = min(p.tpp, p.B - b0);
   const int n0 = blockIdx.x * kDownRows;
-  const int nslot = k + (p.L.has_shared ? 1 : 0);
+  const int nslot = k + (L.has_shared ? 1 : 0);
+  const int GI = I >> 6, CI = I >> 5;
   const BatchPlan* plan = p.plan;
   const int nall = plan->n;
-  // the planned experts chosen by a token of this pass, in plan order (wave 0, 64 entries per ballot)
-  if (wv == 0) {
+  // every plan entry, used or not, so that these loads go out with the one of n
+  for (int i = t; i < kMaxPlan * kMaxBatch / 8; i += kDownThreads)
+    reinterpret_cast<uint2*>(&s_slot[0][0])[i] = reinterpret_cast<const uint2*>(&plan->slot[0][0])[i];
+  for (int i = t; i < kMaxPlan; i += kDownThreads) s_expert[i] = plan->expert[i];
+  for (int i = t; i < nb * (k + 1); i += kDownThreads) {
+    const int bb = i / (k + 1), j = i - bb * (k + 1);
+    s_w[bb][j] = p.wts[(b0 + bb) * (k + 1) + j];  // slot k: the shared expert's weight
+  }
+  lds_sync();
+  if (wv == 0) {  // (planned expert, token) for each token of the pass that chose it, in plan order
     int cnt = 0;
     for (int d0 = 0; d0 < nall; d0 += kWave) {
       const int dd = d0 + lane;
-      const uint2 sw = dd < nall ? *reinterpret_cast<const uint2*>(&plan->slot[dd][0]) : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
-      bool mine = false;
+      uint32_t mine = 0;  // bit bb: token b0 + bb chose expert dd
+      if (dd < nall) {
 #pragma unroll
-      for (int b = 0; b < kMaxBatch; ++b) {
-        const int j = (int)(int8_t)(((b < 4 ? sw.x : sw.y) >> (8 * (b & 3))) & 0xFFu);
-        mine |= b >= b0 && b < b0 + nb && j >= 0;
+        for (int bb = 0; bb < kMaxBatch; ++bb) mine |= (bb < nb && s_slot[dd][b0 + bb] >= 0 ? 1u : 0u) << bb;
       }
-      const unsigned long long m = __ballot(mine);
-      if (mine) s_list[cnt + __popcll(m & ((1ull << lane) - 1ull))] = (int16_t)dd;
-      cnt += __popcll(m);
+      const int c = __popc(mine);
+      int incl = c;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      int at = cnt + incl - c;
+      for (uint32_t m = mine; m; m &= m - 1) s_list[at++] = (int16_t)(dd << 3 | __builtin_ctz(m));
+      cnt += __shfl(incl, kWave - 1);
     }
     if (lane == 0) s_nlist = cnt;
   }
-  __syncthreads();
-  // an 8-bit shared expert (the plan's last entry, chosen by every token) is taken apart below
-  const bool q8sh = p.L.has_shared && p.L.sh_q8;
-  const int nplan = s_nlist - (q8sh ? 1 : 0);
-
-  // lane: row n0 + lane / 8, groups sub, sub + 8, ...; wave w takes planned experts w, w + 4, ...
-  const int sub = lane & (kDownLanes - 1), rsub = lane / kDownLanes;
-  const int GI = I >> 6, CI = I >> 5;
-  const int n = min(n0 + rsub, H - 1);
+  lds_sync();
+  // task tau: entry tau / 2 of the list, rows (tau % 2) * 4 + rsub of the block
+  const int ntask = 2 * s_nlist;
+  const int last = max(ntask - 1, 0);
+  const int sub = lane & (kDownRowLanes - 1), rsub = lane / kDownRowLanes;
+  const int c0 = min(sub, CI - 1);  // this lane's first chunk (lanes past CI: a valid chunk, not used)
+  const bool q8sh = L.has_shared && L.sh_q8;
   const int64_t mat_codes = (int64_t)H * (I >> 3), mat_groups = (int64_t)H * GI;
-  struct DownRow {
-    uint4 c0, c1;
-    uint32_t s, b;
-  };
-  auto load_row = [&](int li, int g) __attribute__((always_inline)) {
-    DownRow r;
-    const int e = plan->expert[s_list[li]];
-    const Q4Mat& m = e >= 0 ? p.L.down : p.L.sh_down;
-    const int64_t oc = e >= 0 ? e * mat_codes : 0, og = e >= 0 ? e * mat_groups : 0;
-    const uint4* cr = reinterpret_cast<const uint4*>(m.codes + oc) + (int64_t)n * CI;
-    const int gq = min(g, GI - 1);
-    r.c0 = cr[2 * gq];
-    r.c1 = cr[2 * gq + 1];
-    r.s = m.scales[og + (int64_t)n * GI + gq];
-    r.b = m.biases[og + (int64_t)n * GI + gq];
+  // (loads branch-free)
+  auto load_dn = [&](int tau, int c) __attribute__((always_inline)) {
+    DnRegs r;
+    const int e = __builtin_amdgcn_readfirstlane(s_expert[s_list[tau >> 1] >> 3]);
+    const int n = min(n0 + (tau & 1) * kDownTaskRows + rsub, H - 1);
+    const bool q8 = e < 0 && q8sh;
+    const uint32_t* codes = e >= 0 ? L.down.codes + e * mat_codes : L.sh_down.codes;
+    const uint16_t* sc = e >= 0 ? L.down.scales + e * mat_groups : L.sh_down.scales;
+    const uint16_t* bi = e >= 0 ? L.down.biases + e * mat_groups : L.sh_down.biases;
+    const uint4* cr = reinterpret_cast<const uint4*>(codes + (int64_t)n * (q8 ? I >> 2 : I >> 3)) + (q8 ? 2 * c : c);
+    r.c = cr[0];
+    r.c2 = cr[q8 ? 1 : 0];
+    r.s = sc[(int64_t)n * GI + (c >> 1)];
+    r.b = bi[(int64_t)n * GI + (c >> 1)];
     return r;
   };
-  // the first experts' rows are loaded before the staging below
-  DownRow pf[kDownPrefetch];
-  if (nplan > 0) {
-#pragma unroll
-    for (int q = 0; q < kDownPrefetch; ++q) pf[q] = load_row(min(wv + kWaves * q, nplan - 1), sub);
-  }
-
-  for (int i = threadIdx.x; i < nb * (k + 1); i += blockDim.x) {
-    const int b = i / (k + 1), j = i - b * (k + 1);
-    s_w[b][j] = p.wts[(b0 + b) * (k + 1) + j];  // slot k: the shared expert's weight
-  }
-  // stage the SwiGLU outputs of these tokens: [nb][nslot] x ([CI][ST2] pairs, [CI] sums)
+  // stage the SwiGLU outputs of this pass's tokens, [nb][nslot] x ([CI][ST2] pairs, [CI]
+  // sums): the chunk images are copied; a chunk's sum is the dot of its 32 words with
+  // (1, 1).  The first chunk of each thread is loaded before the weight rows (its wait
+  // then does not include theirs), the rest after.
   constexpr int ST = chunk_stride<2>();
+  constexpr uint32_t kOnes = 0x3F803F80u;  // two bfloat16 1.0
   uint32_t* ap = smem;
   float* as = reinterpret_cast<float*>(ap + (size_t)p.tpp * nslot * CI * ST);
-  for (int i = threadIdx.x; i < nb * nslot * CI; i += blockDim.x) {
-    const int v = i / CI, c = i - v * CI;  // v = b * nslot + slot
-    stage_f32_split_chunk(p.act + ((size_t)b0 * nslot + v) * I, c, ap + (size_t)i * ST, as + i);
-  }
-  __syncthreads();
-
-  float acc[kMaxBatch];
+  const int nchunk = nb * nslot * CI;
+  const uint4* img = reinterpret_cast<const uint4*>(p.act) + (size_t)b0 * nslot * CI * 8;
+  uint4 w0[8];
 #pragma unroll
-  for (int b = 0; b < kMaxBatch; ++b) acc[b] = 0.f;
-  auto apply = [&](int li, int g, const DownRow& r) __attribute__((always_inline)) {
-    const int dd = s_list[li];
+  for (int q = 0; q < 8; ++q) w0[q] = img[(size_t)min(t, nchunk - 1) * 8 + q];
+  DnRegs dr[kDownSlots];
 #pragma unroll
-    for (int b = 0; b < kMaxBatch; ++b) {
-      if (b >= nb) break;
-      const int j = plan->slot[dd][b0 + b];
-      if (j < 0) continue;
-      const size_t vi = ((size_t)b * nslot + j) * CI + 2 * g;
-      const uint32_t* v = ap + vi * ST;
-      const float part = affine_term(chunk_pdot<2>(r.c0, v) + chunk_pdot<2>(r.c1, v + ST), as[vi] + as[vi + 1], r.s, r.b);
-      acc[b] = fmaf(s_w[b][j], part, acc[b]);
+  for (int q = 0; q < kDownSlots; ++q) dr[q] = load_dn(min(q * kDownWaves + wv, last), c0);
+  auto put = [&](int i, const uint4 (&w)[8]) __attribute__((always_inline)) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      *reinterpret_cast<uint4*>(ap + (size_t)i * ST + 4 * q) = w[q];
+      s0 = dot2_bf16(w[q].x, kOnes, dot2_bf16(w[q].y, kOnes, s0));
+      s1 = dot2_bf16(w[q].z, kOnes, dot2_bf16(w[q].w, kOnes, s1));
     }
+    as[i] = s0 + s1;
   };
-  for (int q0 = 0; wv + kWaves * q0 < nplan; q0 += kDownPrefetch) {
-    if (q0 > 0) {
+  if (t < nchunk) put(t, w0);
+  for (int i = t + kDownThreads; i < nchunk; i += kDownThreads) {
+    uint4 w[8];
 #pragma unroll
-      for (int q = 0; q < kDownPrefetch; ++q) pf[q] = load_row(min(wv + kWaves * (q0 + q), nplan - 1), sub);
-    }
-#pragma unroll
-    for (int q = 0; q < kDownPrefetch; ++q) {
-      const int dd = wv + kWaves * (q0 + q);
-      if (dd < nplan && sub < GI) apply(dd, sub, pf[q]);
-    }
-    if (GI > kDownLanes) {  // rows longer than 8 groups: the further groups, loaded as they are used
-      for (int q = 0; q < kDownPrefetch; ++q) {
-        const int dd = wv + kWaves * (q0 + q);
-        if (dd >= nplan) break;
-        for (int g = sub + kDownLanes; g < GI; g += kDownLanes) apply(dd, g, load_row(dd, g));
-      }
-    }
+    for (int q = 0; q < 8; ++q) w[q] = img[(size_t)i * 8 + q];
+    put(i, w);
   }
-  if (q8sh && wv == nplan % kWaves) {
-    // 8-bit shared down row n: group g is 64 code bytes, chunks 2g and 2g + 1 of slot k
-    const uint4* cr = reinterpret_cast<const uint4*>(p.L.sh_down.codes) + (int64_t)n * (I >> 4);
-    const uint16_t* sr = p.L.sh_down.scales + (int64_t)n * GI;
-    const uint16_t* br = p.L.sh_down.biases + (int64_t)n * GI;
-    for (int g = sub; g < GI; g += kDownLanes) {
-      const uint4 c0 = cr[4 * g], c1 = cr[4 * g + 1], c2 = cr[4 * g + 2], c3 = cr[4 * g + 3];
-      const float sc = bf16_bits_to_f32(sr[g]), bi = bf16_bits_to_f32(br[g]);
+  lds_sync();  // (an LDS-only barrier: the weight loads stay in flight)
+
+  auto compute = [&](int tau, const DnRegs r0) __attribute__((always_inline)) {
+    const int ent = __builtin_amdgcn_readfirstlane(s_list[tau >> 1]);
+    const int dd = ent >> 3, bb = ent & 7;
+    const bool q8 = __builtin_amdgcn_readfirstlane(s_expert[dd]) < 0 && q8sh;
+    const int j = __builtin_amdgcn_readfirstlane(s_slot[dd][b0 + bb]);
+    auto dot = [&](const DnRegs r, int c, int vi) __attribute__((always_inline)) {
+      const uint32_t* v = ap + (size_t)vi * ST;
+      return q8 ? fmaf(bf16_bits_to_f32(r.s), q8_chunk_pdot<2>(r.c, r.c2, v), bf16_bits_to_f32(r.b) * as[vi])
+                : affine_term(chunk_pdot<2>(r.c, v), as[vi], r.s, r.b);
+    };
+    const int r = (tau & 1) * kDownTaskRows + rsub;
+    const int vi = (bb * nslot + j) * CI;
+    float part = sub < CI ? dot(r0, sub, vi + sub) : 0.f;
+    if constexpr (kLong)  // rows of more than 16 chunks: the further chunks, loaded here
+      for (int c = sub + kDownRowLanes; c < CI; c += kDownRowLanes) part += dot(load_dn(tau, c), c, vi + c);
+    part = group_sum_rt(part, 4);
+    if (sub == 0) s_red[bb][j][r] = part;
+  };
+  const int npass = (ntask + kDownWaves - 1) / kDownWaves;
 #pragma unroll
-      for (int b = 0; b < kMaxBatch; ++b) {
-        if (b >= nb) break;
-        const size_t vi = ((size_t)b * nslot + k) * CI + 2 * g;
-        const uint32_t* v = ap + vi * ST;
-        const float part = fmaf(sc, q8_chunk_pdot<2>(c0, c1, v) + q8_chunk_pdot<2>(c2, c3, v + ST),
-                                bi * (as[vi] + as[vi + 1]));
-        acc[b] = fmaf(s_w[b][k], part, acc[b]);
-      }
-    }
+  for (int q = 0; q < kDownSlots; ++q) {
+    const int tau = q * kDownWaves + wv;
+    if (tau < ntask) compute(tau, dr[q]);
   }
-#pragma unroll
-  for (int b = 0; b < kMaxBatch; ++b) {
-    if (b >= nb) break;
-    const float r = group_sum_rt(acc[b], 3);
-    if (sub == 0) s_red[wv][b][rsub] = r;
+  for (int q = kDownSlots; q < npass; ++q) {  // (more tasks than the loads issued ahead)
+    const int tau = q * kDownWaves + wv;
+    const DnRegs r = load_dn(min(tau, last), c0);
+    if (tau < ntask) compute(tau, r);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < nb * kDownRows; i += blockDim.x) {
-    const int b = i / kDownRows, r = i - b * kDownRows, nn = n0 + r;
+  lds_sync();
+  for (int i = t; i < nb * kDownRows; i += kDownThreads) {
+    const int bb = i / kDownRows, r = i - bb * kDownRows, nn = n0 + r;
     if (nn >= H) continue;
-    float t = s_red[0][b][r];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) t += s_red[w][b][r];
-    const size_t o = (size_t)(b0 + b) * H + nn;
+    float acc = 0.f;
+    for (int j = 0; j < nslot; ++j) acc = fmaf(s_w[bb][j], s_red[bb][j][r], acc);  // fixed slot order
+    const size_t o = (size_t)(b0 + bb) * H + nn;
     if (p.out_bf16)
-      reinterpret_cast<uint16_t*>(p.y)[o] = (uint16_t)f32_to_bf16_bits(t);
+      reinterpret_cast<uint16_t*>(p.y)[o] = (uint16_t)f32_to_bf16_bits(acc);
     else
-      reinterpret_cast<float*>(p.y)[o] = t;
+      reinterpret_cast<float*>(p.y)[o] = acc;
   }
 }
 
+__global__ __launch_bounds__(kDownThreads) void batch_down_kernel(BatchParams p) { batch_down<false>(p); }
+__global__ __launch_bounds__(kDownThreads) void batch_down_long_kernel(BatchParams p) { batch_down<true>(p); }
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-size_t gate_up_lds(const DecodeLayer& L, int B) {
+size_t front_lds(const DecodeLayer& L, int B) {
   return (size_t)B * (L.hidden >> 5) * (chunk_stride<1>() * 4 + 4);
 }
 
@@ -540,31 +568,89 @@ size_t down_lds_per_token(const DecodeLayer& L) {
   return (size_t)nslot * (L.inter >> 5) * (chunk_stride<2>() * 4 + 4);
 }
 
-template <int NB>
-void launch_route_plan(const BatchParams& p, int grid, hipStream_t stream) {
-  if (p.L.router_q8.codes)
-    hipLaunchKernelGGL((batch_route_kernel<NB, true>), dim3(grid), dim3(kRouteWaves * kWave), 0, stream, p);
-  else
-    hipLaunchKernelGGL((batch_route_kernel<NB, false>), dim3(grid), dim3(kRouteWaves * kWave), 0, stream, p);
-  const dim3 one(1), threads(kRouteWaves * kWave);
-  if (p.L.n_experts <= 4 * kWave)
-    hipLaunchKernelGGL((batch_plan_kernel<NB, 4>), one, threads, 0, stream, p);
-  else if (p.L.n_experts <= 8 * kWave)
-    hipLaunchKernelGGL((batch_plan_kernel<NB, 8>), one, threads, 0, stream, p);
-  else
-    hipLaunchKernelGGL((batch_plan_kernel<NB, kMaxExperts / kWave>), one, threads, 0, stream, p);
+typedef void (*FrontKernel)(BatchParams);
+
+FrontKernel front_kernel_for(const DecodeLayer& L, int B) {
+  const bool lng = L.hidden > 32 * kWave;
+#define Q4MOE_FRONT_CASE(NB) \
+  case NB: return lng ? batch_front_long_kernel_##NB : batch_front_kernel_##NB;
+  switch (B) {
+    Q4MOE_FRONT_CASE(1)
+    Q4MOE_FRONT_CASE(2)
+    Q4MOE_FRONT_CASE(3)
+    Q4MOE_FRONT_CASE(4)
+    Q4MOE_FRONT_CASE(5)
+    Q4MOE_FRONT_CASE(6)
+    Q4MOE_FRONT_CASE(7)
+    default: return lng ? batch_front_long_kernel_8 : batch_front_kernel_8;
+  }
+#undef Q4MOE_FRONT_CASE
 }
 
 }  // namespace
 
 size_t decode_batch_workspace_bytes(int n_experts, int top_k, int inter, int B) {
-  return align256((size_t)B * n_experts * 4) + align256(sizeof(BatchPlan)) + align256((size_t)B * (top_k + 1) * 4) +
+  (void)n_experts;
+  return align256(sizeof(FrontWs)) + align256(sizeof(BatchPlan)) + align256((size_t)B * (top_k + 1) * 4) +
          align256((size_t)B * (top_k + 1) * inter * 4);
 }
 
 bool decode_batch_supported(const DecodeLayer& L, int B, size_t max_lds) {
   // the down launch needs room for at least one token's SwiGLU outputs
-  return gate_up_lds(L, B) <= max_lds && down_lds_per_token(L) <= max_lds;
+  return front_lds(L, B) <= max_lds && down_lds_per_token(L) <= max_lds;
+}
+
+// The front launch's workgroups wait on each other's logits, so one per CU must fit
+// at once (registers and LDS); cached per device, batch size and LDS size.
+bool decode_batch_fits(const DecodeLayer& L, int B) {
+  struct Entry {
+    int dev;
+    FrontKernel k;
+    size_t lds;
+    bool ok;
+  };
+  static Entry cache[64];
+  static int ncache = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const size_t lds = front_lds(L, B);
+  const FrontKernel kern = front_kernel_for(L, B);
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < ncache; ++i)
+    if (cache[i].dev == dev && cache[i].k == kern && cache[i].lds == lds) return cache[i].ok;
+  int per_cu = 0;
+  const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                               kFrontThreads, lds) == hipSuccess &&
+                  per_cu >= 1;
+  if (ncache < 64) cache[ncache++] = Entry{dev, kern, lds, ok};
+  return ok;
+}
+
+// Dynamic LDS the down launch may take on the current device: the device's per-workgroup
+// limit less the kernel's static arrays (at least max_lds, the limit every launch takes);
+// above 64 KB the kernels are told once per device.
+size_t down_lds_limit(size_t max_lds) {
+  static size_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return max_lds;
+  if (cached[dev]) return cached[dev];
+  int per_block = 0;
+  size_t lim = max_lds;
+  hipFuncAttributes fa{};
+  if (hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+      hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(batch_down_long_kernel)) == hipSuccess &&
+      (size_t)per_block > fa.sharedSizeBytes + max_lds) {
+    const size_t want = (size_t)per_block - fa.sharedSizeBytes;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(batch_down_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)want) == hipSuccess &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(batch_down_long_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)want) == hipSuccess)
+      lim = want;
+  }
+  (void)hipGetLastError();
+  cached[dev] = lim;
+  return lim;
 }
 
 hipError_t run_moe_ffn_decode_batch(const DecodeLayer& L, const uint16_t* X, int B, void* y, int out_bf16,
@@ -574,8 +660,8 @@ hipError_t run_moe_ffn_decode_batch(const DecodeLayer& L, const uint16_t* X, int
   p.X = X;
   p.B = B;
   char* w = static_cast<char*>(ws);
-  p.logits = reinterpret_cast<float*>(w);
-  w += align256((size_t)B * L.n_experts * 4);
+  p.fws = reinterpret_cast<FrontWs*>(w);
+  w += align256(sizeof(FrontWs));
   p.plan = reinterpret_cast<BatchPlan*>(w);
   w += align256(sizeof(BatchPlan));
   p.wts = reinterpret_cast<float*>(w);
@@ -586,25 +672,13 @@ hipError_t run_moe_ffn_decode_batch(const DecodeLayer& L, const uint16_t* X, int
   p.ids_out = ids_out;
   p.w_out = w_out;
   const size_t per_tok = down_lds_per_token(L);
-  p.tpp = (int)std::min<size_t>((size_t)B, max_lds / per_tok);
+  p.tpp = (int)std::min<size_t>((size_t)B, down_lds_limit(max_lds) / per_tok);
 
-  const int rgrid = (L.n_experts + kRouteWaves - 1) / kRouteWaves;
-  switch (B) {
-    case 1: launch_route_plan<1>(p, rgrid, stream); break;
-    case 2: launch_route_plan<2>(p, rgrid, stream); break;
-    case 3: launch_route_plan<3>(p, rgrid, stream); break;
-    case 4: launch_route_plan<4>(p, rgrid, stream); break;
-    case 5: launch_route_plan<5>(p, rgrid, stream); break;
-    case 6: launch_route_plan<6>(p, rgrid, stream); break;
-    case 7: launch_route_plan<7>(p, rgrid, stream); break;
-    default: launch_route_plan<8>(p, rgrid, stream); break;
-  }
-  const int nd_max = std::min(B * L.top_k, L.n_experts) + (L.has_shared ? 1 : 0);
-  const int per_expert = (L.inter + kGateUpRows - 1) / kGateUpRows;
-  hipLaunchKernelGGL(batch_gate_up_kernel, dim3(nd_max * per_expert), dim3(kThreads), gate_up_lds(L, B), stream, p);
+  hipLaunchKernelGGL(front_kernel_for(L, B), dim3(device_cu_count()), dim3(kFrontThreads), front_lds(L, B), stream, p);
   const int passes = (B + p.tpp - 1) / p.tpp;
-  hipLaunchKernelGGL(batch_down_kernel, dim3((L.hidden + kDownRows - 1) / kDownRows, passes), dim3(kThreads),
-                     (size_t)p.tpp * per_tok, stream, p);
+  hipLaunchKernelGGL((L.inter > 32 * kDownRowLanes ? batch_down_long_kernel : batch_down_kernel),
+                     dim3((L.hidden + kDownRows - 1) / kDownRows, passes), dim3(kDownThreads), (size_t)p.tpp * per_tok,
+                     stream, p);
   return hipGetLastError();
 }
 

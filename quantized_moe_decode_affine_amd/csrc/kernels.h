@@ -66,6 +66,8 @@ hipError_t noalloc_scratch(void** out);
 constexpr int kMaxBatch = 8;
 size_t decode_batch_workspace_bytes(int n_experts, int top_k, int inter, int B);
 bool decode_batch_supported(const DecodeLayer& L, int B, size_t max_lds);
+// True when one front workgroup of the batched step fits on every CU at once.
+bool decode_batch_fits(const DecodeLayer& L, int B);
 hipError_t run_moe_ffn_decode_batch(const DecodeLayer& L, const uint16_t* X, int B, void* y, int out_bf16,
                                     int32_t* ids_out, float* w_out, void* ws, size_t max_lds, hipStream_t stream);
 

@@ -359,9 +359,9 @@ def main():
                                "GB_s": round(b_bytes / (b_us * 1e-6) / 1e9, 1),
                                "pct_of_hbm_peak": round(100 * b_bytes / (b_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
         result["decode_batch"] = dict(
-            workload=f"{args.layers}-layer decode loop with B requests per step (moe_ffn_decode_batch, four "
-                     f"launches per layer); tokens_per_s counts all B rows; bytes = distinct + shared experts, "
-                     f"router, inputs and outputs",
+            workload=f"{args.layers}-layer decode loop with B requests per step (moe_ffn_decode_batch: two "
+                     f"launches per layer, one for B = 1); tokens_per_s counts all B rows; bytes = distinct + "
+                     f"shared experts, router, inputs and outputs",
             batch1_kernel_tokens_per_s=round(1 / (layer_us * 1e-6 * args.layers), 1), **batch)
         log(f"decode batch: {batch}")
 

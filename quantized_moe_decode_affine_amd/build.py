@@ -3,6 +3,10 @@
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
 parallel), then linked into ``quantized_moe_decode_affine_amd/libq4moe.so``.
 Always recompiles; run ``python -m quantized_moe_decode_affine_amd.build``.
+
+``--stamps`` also links ``libq4moe_stamps.so``: the same library with the decode
+layer kernel built with phase stamps (``-DQ4MOE_DECODE_STAMPS``), read by
+``phase_timeline.py``.  The product path never loads it.
 """
 from __future__ import annotations
 
@@ -18,6 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq4moe.so")
+STAMPS_LIB = os.path.join(PKG, "libq4moe_stamps.so")
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -67,5 +72,20 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_stamps() -> str:
+    """The diagnostic library: every object of build(), the decode kernel rebuilt with stamps."""
+    hipcc = _hipcc()
+    build()
+    d = os.path.join(BUILD, "stamps")
+    os.makedirs(d, exist_ok=True)
+    obj = os.path.join(d, "decode.o")
+    _run([hipcc, *CFLAGS, "-DQ4MOE_DECODE_STAMPS", "-c", os.path.join(CSRC, "decode.hip"), "-o", obj])
+    objs = [o for o in sorted(glob.glob(os.path.join(BUILD, "*.o"))) if os.path.basename(o) != "decode.o"]
+    tmp = STAMPS_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, obj, "-o", tmp])
+    os.replace(tmp, STAMPS_LIB)
+    return STAMPS_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build_stamps() if "--stamps" in sys.argv else build(verbose="-v" in sys.argv))

@@ -75,6 +75,24 @@ constexpr int kLogitStride = Q4MOE_LOGIT_STRIDE;  // 64-bit words per logit slot
 constexpr int kCopies = Q4MOE_HANDOFF_COPIES;
 constexpr int kLogitCopyWords = kMaxExperts * kLogitStride + 64;  // words between logit copies (skewed)
 
+// Phase stamps, in a diagnostic build only (-DQ4MOE_DECODE_STAMPS: build.py --stamps
+// writes it to a library file of its own): thread 0 of every workgroup records the
+// 100 MHz s_memrealtime counter at the layer's phase boundaries, slot (epoch % 4) of the
+// array, so the last four launches can be read back (q4moe_decode_stamps below).
+// Stamps: 0 launch start, 1 router logits published, 2 top-k known, 3 gate/up computed,
+// 4 activations staged, 5 end.
+#ifdef Q4MOE_DECODE_STAMPS
+__device__ unsigned long long g_decode_stamps[4][kMaxBlocks][8];
+#define Q4MOE_STAMP(i, v)                                                                   \
+  do {                                                                                     \
+    if (threadIdx.x == 0) g_decode_stamps[s_epoch & 3][blockIdx.x][i] = (v);               \
+  } while (0)
+#else
+#define Q4MOE_STAMP(i, v) \
+  do {                    \
+  } while (0)
+#endif
+
 struct DecodeWs {
   HandoffHead h;  // epoch counters; the timeout count at byte 2048
   // Router logit of expert e: tag_logit[e * kLogitStride] = {epoch:hi32, fp32 bits:lo32}.
@@ -546,6 +564,9 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
   const int t = threadIdx.x;
+#ifdef Q4MOE_DECODE_STAMPS
+  const unsigned long long stamp0 = __builtin_amdgcn_s_memrealtime();
+#endif
 
   // ---- epoch of this launch: the arrivals of one group agree on its counter's epoch
   // field.  Thread 0's arrival goes out right after the router loads; its result is
@@ -695,6 +716,12 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     }
     if (t == 0 && m0 == 0) finish_epoch(arrival);
     lds_sync();  // partials (and, on the first pass, the epoch) visible
+#ifdef Q4MOE_DECODE_STAMPS
+    if (m0 == 0) {
+      Q4MOE_STAMP(0, stamp0);
+      Q4MOE_STAMP(1, __builtin_amdgcn_s_memrealtime());
+    }
+#endif
     if (t < kRtRows * kCopies && m0 + t / kCopies < nrows_rt) {  // one thread per (row, copy)
       const int mm = t / kCopies, c = t % kCopies;
       float v = s_rpart[mm][0];
@@ -803,6 +830,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     }
   }
   lds_sync();  // ids known; shared activations gathered
+  Q4MOE_STAMP(2, __builtin_amdgcn_s_memrealtime());
 
   // ================================================================ phase B
   // Routed gate/up units u = b, b + NB, ... of the k * I / 8 units (slot u / upe, rows
@@ -937,6 +965,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     }
     if (kDownLate && m0 == 0) issue_down();
     lds_sync();
+    if (m0 == 0) Q4MOE_STAMP(3, __builtin_amdgcn_s_memrealtime());
     if (nm > 0) publish_units(p.act, p.act_copy_words, I, s_act, nm, epoch, [&](int m) { return unit_of(m0 + m); });
     if (m0 == 0 && has_shared && sh_units > 0)
       publish_units(p.act, p.act_copy_words, I, s_sh, min(sh_units, nbatch_units), epoch,
@@ -971,6 +1000,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
   stage_tagged_split(p.act + (size_t)(b % kCopies) * p.act_copy_words, nslot, I, ap, as, epoch, timeouts,
                      kQ8Shared && !kFast ? af : nullptr, k * I);
   lds_sync();  // activations staged
+  Q4MOE_STAMP(4, __builtin_amdgcn_s_memrealtime());
   {
     constexpr int ST = chunk_stride<2>();
     // fast form: a routed task's part from its row chunk
@@ -1075,6 +1105,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
       lds_sync();  // s_red is reused
     }
   }
+  Q4MOE_STAMP(5, __builtin_amdgcn_s_memrealtime());
 }
 
 #define Q4MOE_DECODE_KERNEL(name, q8r, gated, q8sh)                                                  \
@@ -1213,3 +1244,11 @@ hipError_t run_moe_ffn_decode(const DecodeLayer& L, const uint16_t* x, void* y, 
 }
 
 }  // namespace q4moe
+
+#ifdef Q4MOE_DECODE_STAMPS
+// Diagnostic build only (not part of the library's interface): copies the stamp array
+// ([4][1024][8] uint64, slot epoch % 4, stamps as listed above) to host memory.
+extern "C" int q4moe_decode_stamps(void* host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(q4moe::g_decode_stamps), bytes);
+}
+#endif

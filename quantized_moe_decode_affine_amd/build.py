@@ -5,8 +5,9 @@ parallel), then linked into ``quantized_moe_decode_affine_amd/libq4moe.so``.
 Always recompiles; run ``python -m quantized_moe_decode_affine_amd.build``.
 
 ``--stamps`` also links ``libq4moe_stamps.so``: the same library with the decode
-layer kernel built with phase stamps (``-DQ4MOE_DECODE_STAMPS``), read by
-``phase_timeline.py``.  The product path never loads it.
+layer kernel built with phase stamps (``-DQ4MOE_DECODE_STAMPS``) and the grouped
+GEMM with workgroup stamps (``-DQ4MOE_GEMM_STAMPS``), read by ``phase_timeline.py``.
+The product path never loads it.
 """
 from __future__ import annotations
 
@@ -72,17 +73,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# sources rebuilt with stamps in the diagnostic library, and their macros
+STAMPED = {"decode.hip": "-DQ4MOE_DECODE_STAMPS", "gemm.hip": "-DQ4MOE_GEMM_STAMPS"}
+
+
 def build_stamps() -> str:
-    """The diagnostic library: every object of build(), the decode kernel rebuilt with stamps."""
+    """The diagnostic library: every object of build(), the decode layer kernel and the
+    grouped GEMM rebuilt with stamps."""
     hipcc = _hipcc()
     build()
     d = os.path.join(BUILD, "stamps")
     os.makedirs(d, exist_ok=True)
-    obj = os.path.join(d, "decode.o")
-    _run([hipcc, *CFLAGS, "-DQ4MOE_DECODE_STAMPS", "-c", os.path.join(CSRC, "decode.hip"), "-o", obj])
-    objs = [o for o in sorted(glob.glob(os.path.join(BUILD, "*.o"))) if os.path.basename(o) != "decode.o"]
+    stamped = []
+    for src, flag in STAMPED.items():
+        obj = os.path.join(d, src[:-4] + ".o")
+        _run([hipcc, *CFLAGS, flag, "-c", os.path.join(CSRC, src), "-o", obj])
+        stamped.append(obj)
+    skip = {src[:-4] + ".o" for src in STAMPED}
+    objs = [o for o in sorted(glob.glob(os.path.join(BUILD, "*.o"))) if os.path.basename(o) not in skip]
     tmp = STAMPS_LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, obj, "-o", tmp])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *stamped, "-o", tmp])
     os.replace(tmp, STAMPS_LIB)
     return STAMPS_LIB
 

@@ -26,9 +26,10 @@
 // Tiling: a workgroup (4 waves) owns up to 96 rows of one group (expert) and 256
 // output columns (or 128 gate + 128 up columns for the SwiGLU epilogue); each
 // wave computes up to 3 x 2 MFMA 32x32 blocks.  The row tile is staged through
-// LDS (already in the nibble-pair order) with two groups of look-ahead; each lane
-// loads its own 16 code bytes per group for its column.  Workgroups of the same
-// row tile are placed on the same XCD so the row tile stays in that XCD's L2.
+// LDS (already in the nibble-pair order) with three groups of look-ahead (four
+// stages: two workgroups fill a CU's 160 KB of LDS); each lane loads its own 16
+// code bytes per group for its column.  Workgroups of the same row tile are placed
+// on the same XCD so the row tile stays in that XCD's L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -75,7 +76,37 @@ struct GemmParams {
   void* out;                  // swiglu: fp32 activations; store/scale: fp32 or bf16
   int out_bf16;
   int64_t ldo;
+#ifdef Q4MOE_GEMM_STAMPS
+  int stamp_slot;             // which of the four stamp records this launch fills
+#endif
 };
+
+// Workgroup stamps, in a diagnostic build only (-DQ4MOE_GEMM_STAMPS, built into the
+// diagnostic library by build.py --stamps): thread 0 of every workgroup records the
+// 100 MHz s_memrealtime counter at entry, once its tile's row indices are known, after
+// the main loop, after the bias term and at the end, then the hardware ids it ran on
+// (XCC id << 32 | HW_ID) and its work item (tile | slice << 20 | active row blocks << 28;
+// all ones for a workgroup without a tile), into record stamp_slot of the array.
+#ifdef Q4MOE_GEMM_STAMPS
+constexpr int kGemmStampBlocks = 4096;
+__device__ unsigned long long g_gemm_stamps[4][kGemmStampBlocks][8];
+__device__ __forceinline__ void gemm_stamps_write(const GemmParams& p, const unsigned long long (&t)[5],
+                                                  unsigned long long item) {
+  if (threadIdx.x != 0 || blockIdx.x >= kGemmStampBlocks) return;
+  unsigned long long* r = g_gemm_stamps[p.stamp_slot & 3][blockIdx.x];
+  const unsigned long long hw = (unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 4);     // HW_ID
+  const unsigned long long xcc = (unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+  for (int i = 0; i < 5; ++i) r[i] = t[i];
+  r[5] = xcc << 32 | hw;
+  r[6] = item;
+  r[7] = 0;
+}
+#define Q4MOE_GSTAMP(i) (gst[i] = __builtin_amdgcn_s_memrealtime())
+#else
+#define Q4MOE_GSTAMP(i) \
+  do {                  \
+  } while (0)
+#endif
 
 __device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8_t, v); }
 
@@ -133,7 +164,8 @@ constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xF << 8); }
 
 // Pipeline depth (K groups in flight) and per-stage vector-memory ops per thread:
 // MB A-tile LDS loads, 2 (4-bit) or 4 (8-bit) B-code LDS loads, 2 scale loads.
-constexpr int kStages = 3;  // the stage arrays below are written out for exactly 3
+// The main loop waits for a group with up to kStages - 2 later groups still in flight.
+constexpr int kStages = 4;  // the stage arrays below are written out for exactly 4
 template <int kBits> constexpr int ops_per_stage() { return MB + 2 * (kBits / 4) + 2; }
 constexpr int A_STAGE_BYTES = BM * 128;           // BM rows x one 64-column group of fp16
 // 4 waves x 2 column blocks x 64 lanes x 16 bytes (4-bit codes) or 32 bytes (8-bit codes)
@@ -162,12 +194,20 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   // so it does not wait for every outstanding load before each LDS read.
   // (The compiler tracks only a few distinct DMA targets, so A and B of a stage share one array.)
   __shared__ __align__(16) uint8_t s_st0[A_STAGE_BYTES + B_STAGE_BYTES], s_st1[A_STAGE_BYTES + B_STAGE_BYTES],
-      s_st2[A_STAGE_BYTES + B_STAGE_BYTES];
-  auto stage_a = [&](int st) -> uint8_t* { return st == 0 ? s_st0 : st == 1 ? s_st1 : s_st2; };
+      s_st2[A_STAGE_BYTES + B_STAGE_BYTES], s_st3[A_STAGE_BYTES + B_STAGE_BYTES];
+  auto stage_a = [&](int st) -> uint8_t* { return st == 0 ? s_st0 : st == 1 ? s_st1 : st == 2 ? s_st2 : s_st3; };
   auto stage_b = [&](int st) -> uint8_t* { return stage_a(st) + A_STAGE_BYTES; };
-  __shared__ int32_t s_src[BM];
-  __shared__ float s_wgt[BM];  // per tile row: routing weight (scale epilogue) times 2^row_exp
+  // Two small arrays live in stage memory that is idle while they are used: the tile
+  // rows' source rows in stage 3 (read before the main loop, which fills stage 3 only
+  // after its first barrier), the rows' epilogue factors in stage 0 (after the main loop).
+  static_assert(kStages == 4, "s_src sits in the stage the prologue leaves empty");
+  int32_t* const s_src = reinterpret_cast<int32_t*>(s_st3);
+  float* const s_wgt = reinterpret_cast<float*>(s_st0);  // routing weight (scale epilogue) times 2^row_exp
 
+#ifdef Q4MOE_GEMM_STAMPS
+  unsigned long long gst[5] = {0, 0, 0, 0, 0};
+  Q4MOE_GSTAMP(0);
+#endif
   // ---- tile of this workgroup (XCD-aware: all slices of a tile share an XCD)
   const int bid = blockIdx.x;
   const int xcd = bid % kXcd;
@@ -176,7 +216,15 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   const int tile = (q / p.n_slices) * kXcd + xcd;
   int seg, rows;
   int64_t row0;
+#ifdef Q4MOE_GEMM_STAMPS
+  if (tile >= p.n_tiles) {
+    gst[4] = __builtin_amdgcn_s_memrealtime();
+    gemm_stamps_write(p, gst, ~0ull);
+    return;
+  }
+#else
   if (tile >= p.n_tiles) return;
+#endif
   if (p.tiles) {
     const int4 ti = p.tiles[tile];
     seg = ti.x;
@@ -187,9 +235,13 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     seg = row0 < p.extra_rows ? -1 : -2;
     rows = (int)min<int64_t>(BM, p.extra_rows - row0);
   }
-  if (seg == -2) return;
-  if (kSel == TILES_ROUTED && seg < 0) return;
-  if (kSel == TILES_EXTRA && seg >= 0) return;
+  if (seg == -2 || (kSel == TILES_ROUTED && seg < 0) || (kSel == TILES_EXTRA && seg >= 0)) {
+#ifdef Q4MOE_GEMM_STAMPS
+    gst[4] = __builtin_amdgcn_s_memrealtime();
+    gemm_stamps_write(p, gst, ~0ull);
+#endif
+    return;
+  }
 
   // ---- source row of each tile row (padding rows repeat the last real row; their
   // outputs are dropped).  Thread r < BM also loads its row's routing weight and
@@ -232,6 +284,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     bbias[nb] = Mx.biases + og + wrow * p.G;
   }
   __syncthreads();  // s_src ready
+  Q4MOE_GSTAMP(1);
 
   // ---- A-tile loads of this thread: MB instructions, rows (wave*MB+i)*8 + lane/8, swizzled word
   const uint16_t* a_ptr[MB];
@@ -242,10 +295,20 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     a_word[i] = (lane & 7) ^ a_swz(r);
     a_ptr[i] = p.A + (int64_t)s_src[r] * p.K + a_word[i] * 8;
   }
+  // source rows of this lane's bias-term rows (s_src is overwritten by the main loop)
+  int src_mb[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    src_mb[mb] = s_src[mb * 32 + ln];
+    asm volatile("" : "+v"(src_mb[mb]));  // read here, before the loads that refill stage 3
+  }
 
-  // Issue all loads of K group g into stage `st`.
+  // Issue all loads of K group g into stage `st`.  Past the last group the last group
+  // is loaded again (an L2 hit into a stage no step reads): every step then issues the
+  // same loads and waits for the same count, with no branch for the compiler's own
+  // wait placement to merge (after such a branch it waits for every load in flight).
   auto issue = [&](int g, int st, uint32_t (&sc)[2]) {
-    if (g >= p.G) return;  // nothing past the last group (the step waits account for it)
+    g = min(g, p.G - 1);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       __builtin_amdgcn_global_load_lds(a_ptr[i] + g * 64, stage_a(st) + (wave * MB + i) * 1024, 16, 0, 0);
@@ -287,11 +350,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
       __builtin_amdgcn_sched_barrier(0);
       // Group g has landed for this wave and this wave's reads of the stage about
       // to be refilled are done; the barrier extends both to every wave.  (A
-      // workgroup fence here would also wait for the look-ahead DMA.)
-      if (g + 1 < p.G)  // group g+1's loads (issued after group g's) may still be in flight
-        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kOpsPerStage * (kStages - 2)));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+      // workgroup fence here would also wait for the look-ahead DMA.)  The loads of
+      // groups g+1 and g+2, issued after group g's, may still be in flight.
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kOpsPerStage * (kStages - 2)));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // The look-ahead group goes out first: every wave has finished reading the
@@ -353,16 +414,17 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
         }
       }
     };
-    static_assert(kStages == 3, "the steps below are written out for three stages");
     int g0 = 0;
     for (; g0 + kStages <= p.G; g0 += kStages) {
       step(g0, std::integral_constant<int, 0>{});
       step(g0 + 1, std::integral_constant<int, 1>{});
       step(g0 + 2, std::integral_constant<int, 2>{});
+      step(g0 + 3, std::integral_constant<int, 3>{});
     }
-    // the last G mod 3 groups
+    // the last G mod 4 groups
     if (g0 < p.G) step(g0, std::integral_constant<int, 0>{});
     if (g0 + 1 < p.G) step(g0 + 1, std::integral_constant<int, 1>{});
+    if (g0 + 2 < p.G) step(g0 + 2, std::integral_constant<int, 2>{});
   };
   if (mblocks == 1)
     main_loop(std::integral_constant<int, 1>{});
@@ -370,6 +432,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     main_loop(std::integral_constant<int, 2>{});
   else
     main_loop(std::integral_constant<int, 3>{});
+  // the repeated last-group loads of the final steps are still in flight (into stages)
+  __builtin_amdgcn_s_waitcnt(0);
+  Q4MOE_GSTAMP(2);
   // ---- bias term: sum_g bias[n][g] * rowsum_g[m], on MFMA (fp16 biases exact, row sums in two parts).
   // Each 16-group slice takes one round of loads (the 8 groups' biases of this lane's column,
   // 16 bytes where aligned, and the rows' group-sum parts), issued one slice ahead.
@@ -397,7 +462,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb >= mblocks) continue;
-      const uint16_t* xr = p.xs + (int64_t)s_src[mb * 32 + ln] * 2 * p.Gp + gbase;
+      const uint16_t* xr = p.xs + (int64_t)src_mb[mb] * 2 * p.Gp + gbase;
 #pragma unroll
       for (int part_i = 0; part_i < 2; ++part_i) L.xa[mb][part_i] = *reinterpret_cast<const uint4*>(xr + part_i * p.Gp);
     }
@@ -438,6 +503,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     }
   }
 
+  Q4MOE_GSTAMP(3);
+  __syncthreads();  // every wave is past its last read of stage 0 (s_wgt below)
   if (threadIdx.x < BM) s_wgt[threadIdx.x] = ldexpf(row_wgt, row_e);  // exact: a power of two
   __syncthreads();
 
@@ -469,6 +536,11 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
       }
     }
   }
+#ifdef Q4MOE_GEMM_STAMPS
+  gst[4] = __builtin_amdgcn_s_memrealtime();
+  gemm_stamps_write(p, gst, (unsigned long long)tile | (unsigned long long)slice << 20 |
+                                (unsigned long long)mblocks << 28);
+#endif
 }
 
 __global__ __launch_bounds__(256, 2) void grouped_q4_gemm_kernel(GemmParams p) { grouped_gemm_body<4, TILES_ALL>(p); }
@@ -622,6 +694,10 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // extra_q8: the extra segment (shared expert) holds 8-bit codes; it then takes a launch
 // of its own after the routed tiles'.
 hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream, bool extra_q8 = false) {
+#ifdef Q4MOE_GEMM_STAMPS
+  static int stamp_launches = 0;
+  p.stamp_slot = stamp_launches++ & 3;
+#endif
   p.bs_vec = p.G % 8 == 0;
   for (const Q4Mat* m : {&p.W, &p.W2, &p.X, &p.X2})
     if (m->scales && (!aligned16(m->scales) || !aligned16(m->biases))) p.bs_vec = 0;
@@ -841,3 +917,11 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
 }
 
 }  // namespace q4moe
+
+#ifdef Q4MOE_GEMM_STAMPS
+// Diagnostic build only: copy the grouped-GEMM workgroup stamps ([4][4096][8] uint64,
+// records filled in launch order modulo 4, layout as described above) to host memory.
+extern "C" int q4moe_gemm_stamps(void* host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(q4moe::g_gemm_stamps), bytes);
+}
+#endif

@@ -2,6 +2,7 @@
 
     python -m quantized_moe_decode_affine_amd.build --stamps
     python -m quantized_moe_decode_affine_amd.phase_timeline [--out FILE.md]
+    python -m quantized_moe_decode_affine_amd.phase_timeline --gemm [--out FILE.md]
 
 Runs the 40-layer decode loop (hidden 2048, 256 routed + 1 shared experts, top-8) on
 ``libq4moe_stamps.so``, where thread 0 of every workgroup records the 100 MHz
@@ -12,6 +13,13 @@ relative to each launch's first workgroup start: median and maximum over the
 workgroups, and the gap from one launch's last workgroup end to the next launch's
 first start.  The stamps cost a few stores per workgroup; the loop time printed
 with them is the diagnostic library's, not the product's.
+
+``--gemm`` instead runs the 2,048-token prefill layer and summarises the two
+grouped-GEMM launches (gate/up with SwiGLU, down with the routing weight) from the
+workgroup stamps of gemm.hip: how many workgroups carry a tile, the launch's span,
+per-workgroup times by active row blocks (row indices known, main loop, bias term,
+epilogue), how many workgroups run at once across the span, and where they ran
+(XCC and CU ids).
 """
 from __future__ import annotations
 
@@ -63,11 +71,111 @@ def run(form: str, n_layers: int = 40, steps: int = 8):
     return loop_us, rows, gaps
 
 
+def gemm_run(reps: int = 3):
+    """Stamps of the last prefill layer's two grouped-GEMM launches (bf16 router, 4-bit shared expert)."""
+    from . import synth
+    lib = B.load_library(STAMPS_LIB)
+    dev = "cuda"
+    dl = B.DeviceLayer(synth.moe_layer(1), dev)
+    X = B.bf16_tensor(synth.token_rows(3, 2048, synth.HIDDEN), dev)
+    ws = B.workspace(B.workspace_bytes(B.OP_FFN_PREFILL, dl, rows=2048), dev)
+    Y = torch.empty((2048, synth.HIDDEN), dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(reps - 1):
+        B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
+    torch.cuda.synchronize()
+    e0.record()
+    B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    layer_us = e0.elapsed_time(e1) * 1e3
+    buf = np.zeros((4, 4096, 8), dtype=np.uint64)
+    rc = lib.q4moe_gemm_stamps(buf.ctypes.data_as(ctypes.c_void_p), ctypes.c_size_t(buf.nbytes))
+    if rc != 0:
+        raise RuntimeError(f"q4moe_gemm_stamps failed ({rc})")
+    last = 2 * reps - 1  # launches are recorded in slots (launch index) % 4
+    return layer_us, {"gate/up": buf[(last - 1) % 4], "down": buf[last % 4]}
+
+
+def gemm_summary(name, rec):
+    used = np.nonzero(rec[:, 0])[0]
+    r = rec[used].astype(np.int64)
+    item = rec[used, 6]
+    live = item != np.uint64(0xFFFFFFFFFFFFFFFF)
+    t0 = r[:, 0].min()
+    ns = lambda v: (v - t0) * 10  # noqa: E731
+    start, known, main, bias, end = (ns(r[:, i]) for i in range(5))
+    span = int(end.max())
+    lines = [f"## {name}", "", f"workgroups launched: {len(used)}, with a tile: {int(live.sum())}; "
+             f"span from the first start to the last end: {span} ns", ""]
+    mb = (item[live] >> np.uint64(28)).astype(np.int64) & 0xF
+    lines += ["| active row blocks | workgroups | entry -> rows known | main loop | bias term | epilogue | "
+              "whole workgroup (p10 / median / p90) |", "|---|---|---|---|---|---|---|"]
+    L = {k: v[live] for k, v in dict(start=start, known=known, main=main, bias=bias, end=end).items()}
+    for m in sorted(set(mb.tolist())):
+        sel = mb == m
+        d = L["end"][sel] - L["start"][sel]
+        med = lambda a: int(np.median(a))  # noqa: E731
+        lines.append(f"| {m} | {int(sel.sum())} | {med(L['known'][sel] - L['start'][sel])} | "
+                     f"{med(L['main'][sel] - L['known'][sel])} | {med(L['bias'][sel] - L['main'][sel])} | "
+                     f"{med(L['end'][sel] - L['bias'][sel])} | {int(np.percentile(d, 10))} / {med(d)} / "
+                     f"{int(np.percentile(d, 90))} |")
+    # workgroups running at once, averaged over tenths of the span
+    edges = np.linspace(0, span, 11)
+    conc = []
+    for a, b in zip(edges[:-1], edges[1:]):
+        ov = np.clip(np.minimum(end, b) - np.maximum(start, a), 0, None)
+        conc.append(ov.sum() / max(b - a, 1))
+    lines += ["", "workgroups running at once, by tenth of the span: " + ", ".join(f"{c:.0f}" for c in conc)]
+    starts = np.sort(L["start"])
+    lines += [f"start times of workgroups with a tile (ns): first {int(starts[0])}, 25% {int(np.percentile(starts, 25))}, "
+              f"median {int(np.median(starts))}, 75% {int(np.percentile(starts, 75))}, last {int(starts[-1])}"]
+    hw = rec[used, 5]
+    xcc = (hw >> np.uint64(32)).astype(np.int64) & 0xF
+    lines += [f"workgroups on XCC blockIdx % 8: {int((xcc == used % 8).sum())} of {len(used)}"]
+    tile = (item[live] & np.uint64(0xFFFFF)).astype(np.int64)
+    xl = xcc[live]
+    same, spread = 0, []
+    for t in np.unique(tile):
+        sel = tile == t
+        same += int(len(set(xl[sel].tolist())) == 1)
+        spread.append(L["start"][sel].max() - L["start"][sel].min())
+    lines += [f"tiles whose column slices all ran on one XCC: {same} of {len(np.unique(tile))}; spread of the "
+              f"slices' start times per tile (ns): median {int(np.median(spread))}, 90% {int(np.percentile(spread, 90))}, "
+              f"max {int(np.max(spread))}", ""]
+    return lines
+
+
+def gemm_main(args):
+    layer_us, recs = gemm_run()
+    lines = ["# grouped_q4_gemm_kernel: workgroup timeline (2,048-token prefill layer)", "",
+             "The two grouped-GEMM launches of one prefill layer (hidden 2048, inter 512, 256 routed + 1 shared "
+             "experts, top-8, bf16 router, affine Q4 g64): thread 0 of every workgroup stamps the 100 MHz "
+             "s_memrealtime counter at entry, once its tile's row indices are known, after the main loop, after the "
+             "bias term and at the end, in the diagnostic build (gemm.hip with Q4MOE_GEMM_STAMPS, "
+             "libq4moe_stamps.so). Times are in ns from the launch's first workgroup start; per-phase columns are "
+             "medians.", ""]
+    if args.cmd:
+        lines += [f"command: `{args.cmd}`", ""]
+    lines += [f"prefill layer time with stamps: {layer_us:.1f} us", ""]
+    for name, rec in recs.items():
+        lines += gemm_summary(name, rec)
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=None, help="write the Markdown summary here as well")
     ap.add_argument("--cmd", default="", help="the command line to record in the summary")
+    ap.add_argument("--gemm", action="store_true", help="the prefill layer's grouped GEMMs instead of decode")
     args = ap.parse_args()
+    if args.gemm:
+        text = "\n".join(gemm_main(args))
+        print(text, flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        return
     lines = ["# decode_layer_kernel: phase timeline (40-layer batch-1 decode loop)", "",
              "Phase boundaries of the batch-1 MoE decode layer (hidden 2048, 256 routed + 1 shared experts, top-8, "
              "affine Q4 g64), stamped by thread 0 of every workgroup with the 100 MHz s_memrealtime counter in the "

@@ -261,8 +261,9 @@ int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, vo
  * ids[b] = the lowest index of the largest logit (Lily decodes greedily: lily
  * README, introduction).  max_logit fp32 [B] may be null.  Needs
  * Q4MOE_OP_LMHEAD workspace (B), zero-filled before its first use: the call
- * counts its workgroups' arrivals there (the last one reduces) and leaves the
- * count at zero again, so calls that share a workspace must not overlap.
+ * keeps an arrival count of its workgroups and one running 64-bit maximum per
+ * batch row there (the last workgroup to arrive reads them) and leaves both at
+ * zero again, so calls that share a workspace must not overlap.
  */
 int lmhead_argmax(const q4moe_matrix* W, const q4moe_bf16* X, int64_t B, int32_t* ids,
                   float* max_logit, void* workspace, size_t workspace_bytes, q4moe_stream stream);

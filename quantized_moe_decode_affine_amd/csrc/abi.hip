@@ -102,7 +102,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? Q4MOE_OK : Q4MOE_EHIP; }
 size_t lmhead_ws(int64_t rows, int64_t k, int64_t B) {
   (void)rows;
   (void)k;
-  return 256 + (size_t)q4moe::kMaxGemvBlocks * (size_t)B * 8;  // arrival counter, then the partials
+  return 256 + (size_t)B * 8;  // arrival counter, then one 64-bit running maximum per batch row
 }
 
 }  // namespace
@@ -354,13 +354,12 @@ int lmhead_argmax(const q4moe_matrix* W, const q4moe_bf16* X, int64_t B, int32_t
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
     char* w = static_cast<char*>(workspace);
     unsigned* done = reinterpret_cast<unsigned*>(w);
-    float* part_val = reinterpret_cast<float*>(w + 256);
-    int32_t* part_idx = reinterpret_cast<int32_t*>(w + 256 + (size_t)q4moe::kMaxGemvBlocks * B * 4);
+    unsigned long long* keys = reinterpret_cast<unsigned long long*>(w + 256);
     if (is_q8(*W))
       return hip_status(q4moe::run_lmhead_argmax_q8(W->codes, W->scales, W->biases, rows, (int)W->k, X, (int)B,
-                                                    ids, max_logit, part_val, part_idx, done, (hipStream_t)stream));
+                                                    ids, max_logit, keys, done, (hipStream_t)stream));
     return hip_status(q4moe::run_lmhead_argmax(W->codes, W->scales, W->biases, rows, (int)W->k, X, (int)B, ids,
-                                               max_logit, part_val, part_idx, done, (hipStream_t)stream));
+                                               max_logit, keys, done, (hipStream_t)stream));
   } catch (...) {
     return Q4MOE_EHIP;
   }

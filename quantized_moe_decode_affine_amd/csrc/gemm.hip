@@ -76,6 +76,7 @@ struct GemmParams {
   void* out;                  // swiglu: fp32 activations; store/scale: fp32 or bf16
   int out_bf16;
   int64_t ldo;
+  int vec_out;                // N and ldo multiples of 4, out aligned to 4 elements: 4-column stores
 #ifdef Q4MOE_GEMM_STAMPS
   int stamp_slot;             // which of the four stamp records this launch fills
 #endif
@@ -509,29 +510,79 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   __syncthreads();
 
   // ---- epilogue.  D layout: column = lane % 32, row = 8*(i/4) + 4*(lane/32) + i%4.
+  if (p.vec_out) {
+    // Through LDS, 16 tile rows at a time (registers i = 8h .. 8h+7 of row block mb), in
+    // stages 1 and 2 alternately, so that each thread stores whole 4-column chunks and a
+    // wave's stores cover contiguous row segments: 4 (SwiGLU: 2) 16-byte stores per thread
+    // and half block instead of one 4-byte store per lane and register.  The barriers are
+    // LDS-only, so the stores of one half stay in flight while the next is staged.
+    const int ncol = swiglu ? 128 : BN;  // columns of this workgroup's tile
+    const int ostr = ncol + 8;           // row stride (floats): rows r and r + 4 fall 32 banks apart
+    const int cpr = ncol >> 2;           // 4-column chunks per row
+    const int colw = swiglu ? slice * 128 : slice * BN;
+    static_assert(16 * (BN + 8) * 4 <= A_STAGE_BYTES + b_stage_bytes<4>(), "a half block fits one stage");
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    if (mb >= mblocks) continue;
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb >= mblocks) break;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = mb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-      if (r >= rows) continue;
-      const int64_t pos = row0 + r;
-      const float f = s_wgt[r];
-      if (swiglu) {
-        if (col[0] < p.N) {
-          const float a = silu(f * acc[mb][0][i]) * (f * acc[mb][1][i]);
-          reinterpret_cast<float*>(p.out)[pos * p.ldo + col[0]] = a;
+      for (int h = 0; h < 2; ++h) {
+        float* so = reinterpret_cast<float*>(h ? s_st2 : s_st1);
+        const int rbase = mb * 32 + 16 * h;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int i = 8 * h + ii;
+          const int rr = 8 * (ii >> 2) + 4 * lh + (ii & 3);
+          const float f = s_wgt[rbase + rr];
+          if (swiglu) {
+            so[rr * ostr + wave * 32 + ln] = silu(f * acc[mb][0][i]) * (f * acc[mb][1][i]);
+          } else {
+            so[rr * ostr + wave * 64 + ln] = f * acc[mb][0][i];
+            so[rr * ostr + wave * 64 + 32 + ln] = f * acc[mb][1][i];
+          }
         }
-      } else {
+        lds_sync();
+        for (int c = threadIdx.x; c < 16 * cpr; c += 256) {
+          const int rr = c / cpr, q = c - rr * cpr;
+          const int r = rbase + rr, cc = colw + 4 * q;
+          if (r < rows && cc < p.N) {
+            const float4 v = *reinterpret_cast<const float4*>(so + rr * ostr + 4 * q);
+            const int64_t o = (row0 + r) * p.ldo + cc;
+            if (p.out_bf16) {
+              const uint2 w = make_uint2(f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16),
+                                         f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16));
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = w;
+            } else {
+              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = v;
+            }
+          }
+        }
+      }
+    }
+  } else {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          if (col[nb] >= p.N) continue;
-          const float v = f * acc[mb][nb][i];
-          if (p.out_bf16)
-            reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + col[nb]] = (uint16_t)f32_to_bf16_bits(v);
-          else
-            reinterpret_cast<float*>(p.out)[pos * p.ldo + col[nb]] = v;
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb >= mblocks) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = mb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (r >= rows) continue;
+        const int64_t pos = row0 + r;
+        const float f = s_wgt[r];
+        if (swiglu) {
+          if (col[0] < p.N) {
+            const float a = silu(f * acc[mb][0][i]) * (f * acc[mb][1][i]);
+            reinterpret_cast<float*>(p.out)[pos * p.ldo + col[0]] = a;
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            if (col[nb] >= p.N) continue;
+            const float v = f * acc[mb][nb][i];
+            if (p.out_bf16)
+              reinterpret_cast<uint16_t*>(p.out)[pos * p.ldo + col[nb]] = (uint16_t)f32_to_bf16_bits(v);
+            else
+              reinterpret_cast<float*>(p.out)[pos * p.ldo + col[nb]] = v;
+          }
         }
       }
     }
@@ -694,6 +745,9 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // extra_q8: the extra segment (shared expert) holds 8-bit codes; it then takes a launch
 // of its own after the routed tiles'.
 hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream, bool extra_q8 = false) {
+  // (the SwiGLU epilogue writes a quarter of the bytes per tile and measured no faster staged)
+  p.vec_out = p.epi != EPI_SWIGLU && p.N % 4 == 0 && p.ldo % 4 == 0 &&
+              (reinterpret_cast<uintptr_t>(p.out) & (p.out_bf16 ? 7u : 15u)) == 0;
 #ifdef Q4MOE_GEMM_STAMPS
   static int stamp_launches = 0;
   p.stamp_slot = stamp_launches++ & 3;

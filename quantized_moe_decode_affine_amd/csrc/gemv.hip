@@ -29,8 +29,7 @@ struct GemvParams {
   const uint16_t* x;       // [B][k]
   void* y;                 // store mode: [B][rows]
   int out_bf16;
-  float* part_val;         // argmax mode: [gridDim.x][B] per-workgroup (max, lowest index)
-  int32_t* part_idx;
+  unsigned long long* keys;  // argmax mode: [B] running {value key : ~index} maxima (0 between calls)
   unsigned* done;          // argmax mode: arrival counter (0 between calls)
   int32_t* ids;            // argmax mode: [B]
   float* max_logit;        // argmax mode: [B] or null
@@ -41,75 +40,52 @@ __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi)
 }
 
 // Greedy argmax over a grid: every lane passes its running (max, lowest index)
-// per batch row (-inf for rows it does not hold).  The workgroup's best per
-// batch row is published device-coherently; the last workgroup to arrive
-// reduces all partials in index order and resets the arrival counter for the
-// next call.
+// per batch row (-inf and index 0x7FFFFFFF for rows it does not hold).  The pair
+// is one 64-bit key, {order-preserving key of the value : ~index}, so the largest
+// key is the largest value with the lowest index.  A wave reduces the keys with
+// two DPP maxima (value keys, then the inverted indices of the lanes holding the
+// largest), the workgroup folds its waves in LDS and applies one 64-bit atomic max
+// per batch row to keys[b]; the last workgroup to arrive reads the keys, writes
+// ids and max_logit, and leaves keys and the arrival counter at zero for the next
+// call.
 template <int B>
 __device__ __forceinline__ void argmax_epilogue(float (&best)[B], int32_t (&besti)[B], const GemvParams& p) {
   const int lane = lane_id();
   const int wpb = blockDim.x / kWave;
-  __shared__ float red_v[B][4];
-  __shared__ int32_t red_i[B][4];
+  __shared__ uint32_t red_hi[B][4], red_lo[B][4];
   __shared__ int s_last;
 #pragma unroll
   for (int b = 0; b < B; ++b) {
-    float v = best[b];
-    int32_t i = besti[b];
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      float ov = __shfl_xor(v, m, kWave);
-      int32_t oi = __shfl_xor(i, m, kWave);
-      if (better(ov, oi, v, i)) { v = ov; i = oi; }
-    }
-    if (lane == 0) { red_v[b][threadIdx.x / kWave] = v; red_i[b][threadIdx.x / kWave] = i; }
+    const uint32_t hi = float_key(best[b]);
+    const uint32_t m = wave_max_u32(hi);
+    const uint32_t lo = wave_max_u32(hi == m ? ~(uint32_t)besti[b] : 0u);
+    if (lane == 0) { red_hi[b][threadIdx.x / kWave] = m; red_lo[b][threadIdx.x / kWave] = lo; }
   }
   __syncthreads();
   if (threadIdx.x < B) {
     const int b = threadIdx.x;
-    float v = red_v[b][0];
-    int32_t i = red_i[b][0];
-    for (int w = 1; w < wpb; ++w)
-      if (better(red_v[b][w], red_i[b][w], v, i)) { v = red_v[b][w]; i = red_i[b][w]; }
-    st_agent(p.part_val + (size_t)blockIdx.x * B + b, v);
-    __hip_atomic_store(p.part_idx + (size_t)blockIdx.x * B + b, i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long key = 0;
+    for (int w = 0; w < wpb; ++w) {
+      const unsigned long long kw = (unsigned long long)red_hi[b][w] << 32 | red_lo[b][w];
+      key = kw > key ? kw : key;
+    }
+    __hip_atomic_fetch_max(p.keys + b, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  wait_vmem();  // this thread's partial stores have completed
+  wait_vmem();  // this thread's atomic max has been performed
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned prev = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == gridDim.x - 1;
   }
   __syncthreads();
-  if (s_last) {
-    for (int b = 0; b < B; ++b) {
-      float v = -INFINITY;
-      int32_t i = 0x7FFFFFFF;
-      for (int j = threadIdx.x; j < (int)gridDim.x; j += blockDim.x) {
-        const float ov = ld_agent(p.part_val + (size_t)j * B + b);
-        const int32_t oi = __hip_atomic_load(p.part_idx + (size_t)j * B + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (better(ov, oi, v, i)) { v = ov; i = oi; }
-      }
-#pragma unroll
-      for (int m = 1; m < kWave; m <<= 1) {
-        float ov = __shfl_xor(v, m, kWave);
-        int32_t oi = __shfl_xor(i, m, kWave);
-        if (better(ov, oi, v, i)) { v = ov; i = oi; }
-      }
-      if (lane == 0) { red_v[0][threadIdx.x / kWave] = v; red_i[0][threadIdx.x / kWave] = i; }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        float bv = red_v[0][0];
-        int32_t bi = red_i[0][0];
-        for (int w = 1; w < wpb; ++w)
-          if (better(red_v[0][w], red_i[0][w], bv, bi)) { bv = red_v[0][w]; bi = red_i[0][w]; }
-        p.ids[b] = bi;
-        if (p.max_logit) p.max_logit[b] = bv;
-      }
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (s_last && threadIdx.x < B) {
+    const int b = threadIdx.x;
+    const unsigned long long key = __hip_atomic_load(p.keys + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    p.ids[b] = (int32_t)~(uint32_t)key;
+    if (p.max_logit) p.max_logit[b] = key_float((uint32_t)(key >> 32));
+    __hip_atomic_store(p.keys + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (s_last && threadIdx.x == 0) __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int S, int B, bool ARGMAX, bool CHUNK>
@@ -120,9 +96,20 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
   const int G = p.k >> 6;
   uint32_t* vp = smem;
   float* vs = reinterpret_cast<float*>(smem + B * C * ST);
+  // One batch row in chunks of one thread each: the thread's 64 bytes of x are loaded
+  // now (past the last chunk, the last one again) and staged after the first rows'
+  // loads are out, so the two latencies overlap.
+  const bool xpre = CHUNK && B == 1 && C <= (int)blockDim.x;
+  uint4 xw[4];
+  if (xpre) {
+    const uint4* src = reinterpret_cast<const uint4*>(p.x) + 4 * min((int)threadIdx.x, C - 1);
 #pragma unroll
-  for (int b = 0; b < B; ++b) stage_bf16_vector(p.x + (size_t)b * p.k, C, vp + b * C * ST, vs + b * C);
-  __syncthreads();
+    for (int b = 0; b < 4; ++b) xw[b] = src[b];
+  } else {
+#pragma unroll
+    for (int b = 0; b < B; ++b) stage_bf16_vector(p.x + (size_t)b * p.k, C, vp + b * C * ST, vs + b * C);
+    __syncthreads();
+  }
 
   const int lane = lane_id();
   const int L = 1 << p.lshift;
@@ -171,20 +158,6 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
     const int g = sub;
     float vsum[B];
     uint32_t xr[kXReg ? B : 1][32];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      vsum[b] = vs[b * C + 2 * g] + vs[b * C + 2 * g + 1];
-      if constexpr (kXReg) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint4 t = *reinterpret_cast<const uint4*>(vp + b * C * ST + (2 * g + (q >> 2)) * ST + 4 * (q & 3));
-          xr[b][4 * q] = t.x;
-          xr[b][4 * q + 1] = t.y;
-          xr[b][4 * q + 2] = t.z;
-          xr[b][4 * q + 3] = t.w;
-        }
-      }
-    }
     struct RowFrag {
       uint4 c0, c1;
       uint32_t s, b;
@@ -209,40 +182,41 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
       }
       return (p0 + p1) + (p2 + p3);
     };
-    for (int64_t base = wave * step; base < p.rows; base += nwaves * step) {
-      // keeps the (loop-invariant) LDS activation reads of B > 2 inside the loop:
-      // hoisted, they would hold 32 registers per batch row
-      if constexpr (!kXReg) asm volatile("" ::: "memory");
-      RowFrag f[S];
-      {
-        // uniform 64-bit step bases, small 32-bit row offsets inside the step
-        const uint4* cb = p.codes + base * C;
-        const uint16_t* sp = p.scales + base * G;
-        const uint16_t* bp = p.biases + base * G;
-        const int left = (int)min<int64_t>(p.rows - 1 - base, (int64_t)S * rpi);
+    // The rows of step base (S per lane), loaded into registers.  Bases past the end
+    // read the last row (in bounds, unused), so every step issues the same loads.
+    auto load_step = [&](int64_t base, RowFrag (&f)[S]) __attribute__((always_inline)) {
+      base = min<int64_t>(base, p.rows - 1);
+      // uniform 64-bit step bases, small 32-bit row offsets inside the step
+      const uint4* cb = p.codes + base * C;
+      const uint16_t* sp = p.scales + base * G;
+      const uint16_t* bp = p.biases + base * G;
+      const int left = (int)min<int64_t>(p.rows - 1 - base, (int64_t)S * rpi);
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int r = min(s * rpi + rsub, left);  // rows past the end: loaded, unused
-          f[s].c0 = cb[r * C + 2 * g];
-          f[s].c1 = cb[r * C + 2 * g + 1];
-          f[s].s = sp[r * G + g];
-          f[s].b = bp[r * G + g];
-        }
+      for (int s = 0; s < S; ++s) {
+        const int r = min(s * rpi + rsub, left);  // rows past the end: loaded, unused
+        f[s].c0 = cb[r * C + 2 * g];
+        f[s].c1 = cb[r * C + 2 * g + 1];
+        f[s].s = sp[r * G + g];
+        f[s].b = bp[r * G + g];
       }
+    };
+    // Software-pipelined over two register sets: the next step's rows are in flight
+    // while this step computes (the sets swap roles, so no copy waits for the loads).
+    auto compute_step = [&](int64_t base, const RowFrag (&F)[S]) __attribute__((always_inline)) {
       float acc[S][B];
       if constexpr (kXReg) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           __builtin_amdgcn_sched_barrier(0);  // one row at a time: a row's converted codes take 32 registers
           uint32_t q[32];
-          convert(f[s], q);
+          convert(F[s], q);
 #pragma unroll
-          for (int b = 0; b < B; ++b) acc[s][b] = affine_term(dot(q, xr[b]), vsum[b], f[s].s, f[s].b);
+          for (int b = 0; b < B; ++b) acc[s][b] = affine_term(dot(q, xr[b]), vsum[b], F[s].s, F[s].b);
         }
       } else {
         uint32_t q[S][32];
 #pragma unroll
-        for (int s = 0; s < S; ++s) convert(f[s], q[s]);
+        for (int s = 0; s < S; ++s) convert(F[s], q[s]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           uint32_t xl[32];
@@ -255,7 +229,7 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
             xl[4 * qq + 3] = t.w;
           }
 #pragma unroll
-          for (int s = 0; s < S; ++s) acc[s][b] = affine_term(dot(q[s], xl), vsum[b], f[s].s, f[s].b);
+          for (int s = 0; s < S; ++s) acc[s][b] = affine_term(dot(q[s], xl), vsum[b], F[s].s, F[s].b);
         }
       }
 #pragma unroll
@@ -263,6 +237,49 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[s][b] = group_sum_rt(acc[s][b], p.lshift);
       emit(base, acc);
+    };
+    const int64_t stride = nwaves * step;
+    RowFrag fa[S], fb[S];
+    load_step(wave * step, fa);
+    if (xpre) {
+      if ((int)threadIdx.x < C) {
+        float sx = 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint4 v = xw[b];
+          sx += (bf16_bits_to_f32(v.x & 0xFFFFu) + bf16_bits_to_f32(v.x >> 16)) +
+                (bf16_bits_to_f32(v.y & 0xFFFFu) + bf16_bits_to_f32(v.y >> 16)) +
+                (bf16_bits_to_f32(v.z & 0xFFFFu) + bf16_bits_to_f32(v.z >> 16)) +
+                (bf16_bits_to_f32(v.w & 0xFFFFu) + bf16_bits_to_f32(v.w >> 16));
+          *reinterpret_cast<uint4*>(vp + threadIdx.x * ST + 4 * b) = permute_block(v);
+        }
+        vs[threadIdx.x] = sx;
+      }
+      lds_sync();  // (the first rows' loads stay in flight)
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      vsum[b] = vs[b * C + 2 * g] + vs[b * C + 2 * g + 1];
+      if constexpr (kXReg) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint4 t = *reinterpret_cast<const uint4*>(vp + b * C * ST + (2 * g + (q >> 2)) * ST + 4 * (q & 3));
+          xr[b][4 * q] = t.x;
+          xr[b][4 * q + 1] = t.y;
+          xr[b][4 * q + 2] = t.z;
+          xr[b][4 * q + 3] = t.w;
+        }
+      }
+    }
+    for (int64_t base = wave * step; base < p.rows; base += 2 * stride) {
+      // keeps the (loop-invariant) LDS activation reads of B > 2 inside the loop:
+      // hoisted, they would hold 32 registers per batch row
+      if constexpr (!kXReg) asm volatile("" ::: "memory");
+      load_step(base + stride, fb);
+      compute_step(base, fa);
+      if (base + stride >= p.rows) break;
+      load_step(base + 2 * stride, fa);
+      compute_step(base + stride, fb);
     }
   } else {
     for (int64_t base = wave * step; base < p.rows; base += nwaves * step) {
@@ -725,7 +742,7 @@ GemvGrid gemv_grid(int64_t rows, int k, int S, int resident) {
   const int64_t rows_per_wave_iter = (int64_t)(kWave >> g.lshift) * S;
   const int64_t iters = (rows + rows_per_wave_iter - 1) / rows_per_wave_iter;
   int64_t max_blocks = (int64_t)device_cu_count() * (resident > 0 ? resident : 1);
-  if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // bounds the argmax partials
+  if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // one resident round at most
   const int64_t blocks = (iters + 3) / 4;
   g.blocks = (int)(blocks < max_blocks ? blocks : max_blocks);
   return g;
@@ -799,7 +816,7 @@ hipError_t run_lmhead_b(GemvParams p, int32_t* ids, float* max_logit, hipStream_
     const int64_t wave_steps = (p.rows + 15) / 16;
     int64_t blocks = (wave_steps + 3) / 4;
     int64_t max_blocks = (int64_t)device_cu_count() * lmhead_mfma_resident<B>(lds);
-    if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // bounds the argmax partials
+    if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // one resident round at most
     if (blocks > max_blocks) blocks = max_blocks;
     p.ids = ids;
     p.max_logit = max_logit;
@@ -836,7 +853,7 @@ hipError_t run_q4_gemv(const uint32_t* codes, const uint16_t* scales, const uint
 
 hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                              int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
-                             float* part_val, int32_t* part_idx, unsigned* done, hipStream_t stream) {
+                             unsigned long long* keys, unsigned* done, hipStream_t stream) {
   GemvParams p{};
   p.codes = reinterpret_cast<const uint4*>(codes);
   p.scales = scales;
@@ -844,8 +861,7 @@ hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, cons
   p.rows = rows;
   p.k = k;
   p.x = X;
-  p.part_val = part_val;
-  p.part_idx = part_idx;
+  p.keys = keys;
   p.done = done;
   switch (B) {
     case 1: return run_lmhead_b<1>(p, ids, max_logit, stream);
@@ -881,7 +897,7 @@ hipError_t launch_q8(GemvParams p, hipStream_t stream) {
   const int64_t iters = (p.rows + rows_per_wave_iter - 1) / rows_per_wave_iter;
   int64_t blocks = (iters + 3) / 4;
   int64_t max_blocks = (int64_t)device_cu_count() * resident;
-  if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // bounds the argmax partials
+  if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // one resident round at most
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((q8_gemv_kernel<S, B, ARGMAX>), dim3((unsigned)blocks), dim3(256), lds, stream, p);
@@ -898,7 +914,7 @@ hipError_t run_lmhead_q8_b(GemvParams& p, int32_t* ids, float* max_logit, hipStr
     const int64_t wave_steps = (p.rows + 15) / 16;  // 16 rows per wave step; one resident round
     int64_t blocks = (wave_steps + 3) / 4;
     int64_t max_blocks = (int64_t)device_cu_count() * lmhead_mfma_resident<B, true>(lds);
-    if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // bounds the argmax partials
+    if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // one resident round at most
     if (blocks > max_blocks) blocks = max_blocks;
     hipLaunchKernelGGL((lmhead_mfma_q8_kernel<B>), dim3((int)blocks), dim3(256), lds, stream, p);
     return hipGetLastError();
@@ -926,7 +942,7 @@ hipError_t run_q8_gemv(const uint32_t* codes, const uint16_t* scales, const uint
 
 hipError_t run_lmhead_argmax_q8(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                                 int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
-                                float* part_val, int32_t* part_idx, unsigned* done, hipStream_t stream) {
+                                unsigned long long* keys, unsigned* done, hipStream_t stream) {
   GemvParams p{};
   p.codes = reinterpret_cast<const uint4*>(codes);
   p.scales = scales;
@@ -934,8 +950,7 @@ hipError_t run_lmhead_argmax_q8(const uint32_t* codes, const uint16_t* scales, c
   p.rows = rows;
   p.k = k;
   p.x = X;
-  p.part_val = part_val;
-  p.part_idx = part_idx;
+  p.keys = keys;
   p.done = done;
   switch (B) {
     case 1: return run_lmhead_q8_b<1>(p, ids, max_logit, stream);

@@ -14,13 +14,13 @@ int device_cu_count();
 
 // ---- GEMV family (gemv.hip)
 size_t gemv_lds_bytes(int k, int B);
-// The LM-head GEMV launches at most this many workgroups (one argmax partial each).
+// The GEMV family launches at most this many workgroups (one resident round).
 constexpr int kMaxGemvBlocks = 2048;
 hipError_t run_q4_gemv(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t rows,
                        int k, const uint16_t* x, void* y, int out_bf16, hipStream_t stream);
 hipError_t run_lmhead_argmax(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                              int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
-                             float* part_val, int32_t* part_idx, unsigned* done, hipStream_t stream);
+                             unsigned long long* keys, unsigned* done, hipStream_t stream);
 
 // The same for 8-bit codes (4 per word): B = 1 runs the GEMV form (LDS per call from
 // q8_gemv_lds_bytes), B = 2..8 the matrix-core LM head (LDS per call from gemv_lds_bytes).
@@ -29,7 +29,7 @@ hipError_t run_q8_gemv(const uint32_t* codes, const uint16_t* scales, const uint
                        int k, const uint16_t* x, void* y, int out_bf16, hipStream_t stream);
 hipError_t run_lmhead_argmax_q8(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                                 int64_t rows, int k, const uint16_t* X, int B, int32_t* ids, float* max_logit,
-                                float* part_val, int32_t* part_idx, unsigned* done, hipStream_t stream);
+                                unsigned long long* keys, unsigned* done, hipStream_t stream);
 
 // ---- Q4 matrices as seen by the kernels
 struct Q4Mat {

@@ -160,6 +160,11 @@ def gemm_main(args):
     lines += [f"prefill layer time with stamps: {layer_us:.1f} us", ""]
     for name, rec in recs.items():
         lines += gemm_summary(name, rec)
+    gu, dn = (r[np.nonzero(r[:, 0])[0]].astype(np.int64) for r in recs.values())
+    lines += [f"from the gate/up launch's last workgroup end to the down launch's first workgroup start "
+              f"(the activations' fp16 preparation runs between them): {int((dn[:, 0].min() - gu[:, 4].max()) * 10)} ns; "
+              f"from the gate/up launch's first start to the down launch's last end: "
+              f"{int((dn[:, 4].max() - gu[:, 0].min()) * 10)} ns", ""]
     return lines
 
 

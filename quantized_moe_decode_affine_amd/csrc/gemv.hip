@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(GemvParams p) {
   const int rsub = lane >> p.lshift;
   const int rpi = kWave >> p.lshift;
   const int wpb = blockDim.x / kWave;
-  const int64_t wave = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+  const int64_t wave = (int64_t)blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
   const int64_t nwaves = (int64_t)gridDim.x * wpb;
   const int64_t step = (int64_t)rpi * S;
 
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void q8_gemv_kernel(GemvParams p) {
   const int rsub = lane >> p.lshift;
   const int rpi = kWave >> p.lshift;
   const int wpb = blockDim.x / kWave;
-  const int64_t wave = (int64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+  const int64_t wave = (int64_t)blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
   const int64_t nwaves = (int64_t)gridDim.x * wpb;
   const int64_t step = (int64_t)rpi * S;
 
@@ -453,17 +453,20 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
 }
 
 // LM head for 2..8 batch rows on the 4x4x4 bf16 MFMA (16 independent 4x4
-// blocks per wave instruction).  Block b = 4*rq + ks of a wave covers rows
-// base + 4*rq .. +3 and K groups gg + ks (gg = 0, 4, 8, ...): lane 4b+i
-// supplies row i's codes of that group (the 4 blocks of a row quad together read
-// 128 contiguous bytes of each row), lane 4b+j the activations of batch row j
-// (+4 for the second instruction set when B > 4), and lane 4b+j receives the 4
-// rows' sums for batch row j.  Per group a lane converts 8 code words once
-// (exact 128+q pairs, common.h) into 16 A operands, runs 16 MFMAs per set into a
-// fresh partial sum P (exact products, fp32 sums) and adds
-// s*P + (b - 128 s)*sum_x with its quad's scales and offsets broadcast by DPP;
-// the four groups' sums of a row meet in one lane at the end.  The codes of the
-// next two steps are in flight while the current one computes.
+// blocks per wave instruction).  A wave works through 8-row blocks of the matrix
+// (blocks wave, wave + nwaves, ...), each in steps of 8 K groups: block b =
+// 8*rq + ks of an instruction covers rows base + 4*rq .. +3 (rq = 0, 1) and K group
+// 8*step + ks, with lane 4b+i supplying row i's codes of that group (the 8 blocks
+// of a row quad read 256 contiguous bytes of each row), lane 4b+j the activations
+// of batch row j (+4 for the second instruction set when B > 4), and lane 4b+j
+// receiving the 4 rows' sums for batch row j.  Per group a lane converts 8 code
+// words once (exact 128+q pairs, common.h) into 16 A operands, runs 16 MFMAs per
+// set into a fresh partial sum P (exact products, fp32 sums) and adds
+// s*P + (b - 128 s)*sum_x with its quad's scales and offsets broadcast by DPP; at
+// a block's last step the eight groups' sums of a row meet in one lane.  The wave's
+// (block, step) items form one stream: the codes of the next two items are in
+// flight while the current one computes, across block boundaries, in three
+// register sets that take turns (a copy between sets would wait for the loads).
 template <int B>
 __global__ __launch_bounds__(256) void lmhead_mfma_kernel(GemvParams p) {
   constexpr int NB = (B + 3) / 4;
@@ -479,14 +482,19 @@ __global__ __launch_bounds__(256) void lmhead_mfma_kernel(GemvParams p) {
 
   const int lane = lane_id();
   const int q = lane & 3;          // row of the block (A side) and batch column (B and D sides)
-  const int ks = (lane >> 2) & 3;  // group offset of the block
-  const int rq = lane >> 4;        // row quad of the block
+  const int ks = (lane >> 2) & 7;  // group offset of the block
+  const int rq = lane >> 5;        // row quad of the block
   int jb[NB];                      // this lane's batch row per set (clamped: columns past B are computed, unused)
 #pragma unroll
   for (int h = 0; h < NB; ++h) jb[h] = min(4 * h + q, B - 1);
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t wave =
+      (int64_t)blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  constexpr int kRowsPerWave = 16;
+  constexpr int kRowsPerBlock = 8;
+  const int64_t nblocks = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int spb = (G + 7) >> 3;  // steps per block
+  const int64_t my_blocks = wave < nblocks ? (nblocks - 1 - wave) / nwaves + 1 : 0;
+  const int64_t n_items = my_blocks * spb;
 
   float best[NB];
   int32_t besti[NB];
@@ -497,73 +505,108 @@ __global__ __launch_bounds__(256) void lmhead_mfma_kernel(GemvParams p) {
     uint4 c0, c1;
     uint32_t s, b;
   };
-  for (int64_t base = wave * kRowsPerWave; base < p.rows; base += nwaves * kRowsPerWave) {
-    const int64_t row = min(base + 4 * rq + q, p.rows - 1);  // rows past the end: loaded, unused
+  // Item cursor: block j of the wave and step gs inside it.
+  struct Cursor {
+    int64_t j;
+    int gs;
+  };
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+    if (++c.gs == spb) { c.gs = 0; ++c.j; }
+  };
+  // Loads of the item at c (past the wave's last item, its last block's rows and groups
+  // again: in bounds, unused).
+  auto load = [&](const Cursor& c) __attribute__((always_inline)) {
+    const int64_t jj = min(c.j, my_blocks > 0 ? my_blocks - 1 : 0);
+    const int64_t row = min((wave + jj * nwaves) * kRowsPerBlock + 4 * rq + q, p.rows - 1);
+    const int g = min(8 * c.gs + ks, G - 1);
     const uint4* cr = p.codes + row * C;
-    const uint16_t* sr = p.scales + row * G;
-    const uint16_t* br = p.biases + row * G;
-    f32x4_t acc[NB];
+    return Frag{cr[2 * g], cr[2 * g + 1], p.scales[row * G + g], p.biases[row * G + g]};
+  };
+  f32x4_t acc[NB];
 #pragma unroll
-    for (int h = 0; h < NB; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    int g = min(ks, G - 1);
-    const int g1 = min(4 + ks, G - 1);
-    Frag f{cr[2 * g], cr[2 * g + 1], sr[g], br[g]};
-    Frag f1{cr[2 * g1], cr[2 * g1 + 1], sr[g1], br[g1]};
-    for (int gg = 0; gg < G; gg += 4) {
-      const bool live = gg + ks < G;  // groups past the end: loaded (clamped), not added
-      const int gn = min(gg + 4 + ks, G - 1);
-      const int g2 = min(gg + 8 + ks, G - 1);
-      const Frag f2{cr[2 * g2], cr[2 * g2 + 1], sr[g2], br[g2]};  // two steps ahead
-      uint32_t pr[32];
+  for (int h = 0; h < NB; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // One item: its group's products into acc; at the block's last step the row sums.
+  auto compute = [&](const Cursor& c, const Frag& f) __attribute__((always_inline)) {
+    const int g0 = 8 * c.gs + ks;
+    const bool live = g0 < G;  // groups past the end: loaded (clamped), not added
+    const int g = min(g0, G - 1);
+    uint32_t pr[32];
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const uint4& u = w < 4 ? f.c0 : f.c1;
-        const uint32_t word = (w & 3) == 0 ? u.x : (w & 3) == 1 ? u.y : (w & 3) == 2 ? u.z : u.w;
+    for (int w = 0; w < 8; ++w) {
+      const uint4& u = w < 4 ? f.c0 : f.c1;
+      const uint32_t word = (w & 3) == 0 ? u.x : (w & 3) == 1 ? u.y : (w & 3) == 2 ? u.z : u.w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pr[4 * w + j] = nib_pair(word, 4 * j);
-      }
-      const uint32_t s4[4] = {quad_bcast<0>(f.s), quad_bcast<1>(f.s), quad_bcast<2>(f.s), quad_bcast<3>(f.s)};
-      const uint32_t b4[4] = {quad_bcast<0>(f.b), quad_bcast<1>(f.b), quad_bcast<2>(f.b), quad_bcast<3>(f.b)};
-#pragma unroll
-      for (int h = 0; h < NB; ++h) {
-        // pair word m of group g sits in chunk 2g + m/16 at offset m%16
-        const uint32_t* xv = vp + jb[h] * C * ST + 2 * g * ST;
-        f32x4_t P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int m = 2 * t;
-          const uint2 xa = *reinterpret_cast<const uint2*>(xv + (m >> 4) * ST + (m & 15));
-          P = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(mfma4_bf16_t, make_uint2(pr[m], pr[m + 1])),
-                                                   __builtin_bit_cast(mfma4_bf16_t, xa), P, 0, 0, 0);
-        }
-        const float vsum = vs[jb[h] * C + 2 * g] + vs[jb[h] * C + 2 * g + 1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[h][i] += live ? affine_term(P[i], vsum, s4[i], b4[i]) : 0.f;
-      }
-      f = f1;
-      f1 = f2;
-      g = gn;
+      for (int j = 0; j < 4; ++j) pr[4 * w + j] = nib_pair(word, 4 * j);
     }
-    // the four group offsets of a row quad meet in the ks = 0 lanes; lane 16rq + j
-    // then holds rows base + 4rq + i (i = 0..3) for batch row 4h + j
+    const uint32_t s4[4] = {quad_bcast<0>(f.s), quad_bcast<1>(f.s), quad_bcast<2>(f.s), quad_bcast<3>(f.s)};
+    const uint32_t b4[4] = {quad_bcast<0>(f.b), quad_bcast<1>(f.b), quad_bcast<2>(f.b), quad_bcast<3>(f.b)};
 #pragma unroll
-    for (int h = 0; h < NB; ++h)
+    for (int h = 0; h < NB; ++h) {
+      // pair word m of group g sits in chunk 2g + m/16 at offset m%16
+      const uint32_t* xv = vp + jb[h] * C * ST + 2 * g * ST;
+      f32x4_t P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[h][i] += __shfl_xor(acc[h][i], 4, kWave);
-        acc[h][i] += __shfl_xor(acc[h][i], 8, kWave);
+      for (int t = 0; t < 16; ++t) {
+        const int m = 2 * t;
+        const uint2 xa = *reinterpret_cast<const uint2*>(xv + (m >> 4) * ST + (m & 15));
+        P = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(mfma4_bf16_t, make_uint2(pr[m], pr[m + 1])),
+                                                 __builtin_bit_cast(mfma4_bf16_t, xa), P, 0, 0, 0);
       }
-    if (ks == 0) {
+      const float vsum = vs[jb[h] * C + 2 * g] + vs[jb[h] * C + 2 * g + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[h][i] += live ? affine_term(P[i], vsum, s4[i], b4[i]) : 0.f;
+    }
+    if (c.gs == spb - 1) {
+      // the eight group offsets of a row quad meet in the ks = 0 lanes; lane 32rq + j
+      // then holds rows base + 4rq + i (i = 0..3) for batch row 4h + j
 #pragma unroll
       for (int h = 0; h < NB; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t r = base + 4 * rq + i;
-          if (r < p.rows && better(acc[h][i], (int32_t)r, best[h], besti[h])) {
-            best[h] = acc[h][i];
-            besti[h] = (int32_t)r;
-          }
+          acc[h][i] += __shfl_xor(acc[h][i], 4, kWave);
+          acc[h][i] += __shfl_xor(acc[h][i], 8, kWave);
+          acc[h][i] += __shfl_xor(acc[h][i], 16, kWave);
         }
+      if (ks == 0) {
+        const int64_t base = (wave + c.j * nwaves) * kRowsPerBlock;
+#pragma unroll
+        for (int h = 0; h < NB; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t r = base + 4 * rq + i;
+            if (r < p.rows && better(acc[h][i], (int32_t)r, best[h], besti[h])) {
+              best[h] = acc[h][i];
+              besti[h] = (int32_t)r;
+            }
+          }
+      }
+#pragma unroll
+      for (int h = 0; h < NB; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // Item i lives in register set i mod 3; step t loads item t + 2 and computes item
+  // t.  The stream starts two steps early (no loads before the loop), so the loop is
+  // entered with nothing in flight and the sets rotate without copies.
+  Cursor cl{0, 0}, cc{0, 0};  // next item to load, next item to compute
+  Frag fa{}, fb{}, fc{};
+  for (int64_t t = -2; t < n_items; t += 3) {
+    fa = load(cl);
+    advance(cl);
+    if (t >= 0) {
+      compute(cc, fb);
+      advance(cc);
+    }
+    fb = load(cl);
+    advance(cl);
+    if (t + 1 >= 0 && t + 1 < n_items) {
+      compute(cc, fc);
+      advance(cc);
+    }
+    fc = load(cl);
+    advance(cl);
+    if (t + 2 < n_items) {
+      compute(cc, fa);
+      advance(cc);
     }
   }
   // every lane offers its candidate for the batch rows it holds, -inf for the others
@@ -602,7 +645,8 @@ __global__ __launch_bounds__(256) void lmhead_mfma_q8_kernel(GemvParams p) {
   int jb[NB];                      // this lane's batch row per set (clamped: columns past B are computed, unused)
 #pragma unroll
   for (int h = 0; h < NB; ++h) jb[h] = min(4 * h + q, B - 1);
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t wave =
+      (int64_t)blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
   constexpr int kRowsPerWave = 16;
 
@@ -811,10 +855,10 @@ int lmhead_mfma_resident(size_t lds) {
 template <int B>
 hipError_t run_lmhead_b(GemvParams p, int32_t* ids, float* max_logit, hipStream_t stream) {
   if constexpr (B >= 2) {
-    // 16 rows per wave step; one resident round of workgroups
+    // 8-row blocks over the waves; one resident round of workgroups
     const size_t lds = gemv_lds(p.k, B);
-    const int64_t wave_steps = (p.rows + 15) / 16;
-    int64_t blocks = (wave_steps + 3) / 4;
+    const int64_t row_blocks = (p.rows + 7) / 8;
+    int64_t blocks = (row_blocks + 3) / 4;
     int64_t max_blocks = (int64_t)device_cu_count() * lmhead_mfma_resident<B>(lds);
     if (max_blocks > kMaxGemvBlocks) max_blocks = kMaxGemvBlocks;  // one resident round at most
     if (blocks > max_blocks) blocks = max_blocks;

@@ -57,6 +57,12 @@ constexpr int kActBatch = 256;    // activations gathered in LDS before they are
 #define Q4MOE_DOWN_LATE 0
 #endif
 constexpr bool kDownLate = Q4MOE_DOWN_LATE;  // down rows loaded after gate/up (else with it)
+#ifndef Q4MOE_DOWN_AFTER_GU
+#define Q4MOE_DOWN_AFTER_GU 1
+#endif
+// down rows issued once this wave's routed gate/up rows are in (they are needed only
+// after the activation handoff; issued with the gate/up rows they share the stream)
+constexpr bool kDownAfterGu = Q4MOE_DOWN_AFTER_GU;
 #ifndef Q4MOE_SHARED_LATE
 #define Q4MOE_SHARED_LATE 1
 #endif
@@ -929,7 +935,7 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     for (int q = 0; q < kDnSlots; ++q) load_dn(q, rb0, dnr[q]);
     if (has_shared) load_shdn(rb0, shdn);
   };
-  if (!kDownLate) issue_down();
+  if (!kDownLate && !kDownAfterGu) issue_down();
 
   // gate/up with SwiGLU, gathered per batch of units in LDS, then published; the
   // shared units of phase A go out with the first batch
@@ -941,6 +947,10 @@ __device__ __forceinline__ void decode_layer(const DecodeParams& p) {
     int q0 = 0;
     if constexpr (kFast) {
       if (m0 == 0) {
+        if constexpr (kDownAfterGu && !kDownLate) {
+          wait_vmem();  // this wave's gate/up rows (and everything before them) are in
+          issue_down();
+        }
         XChunk x1;
         read_xchunk(xp, xs, gh.sub, x1);
 #pragma unroll

@@ -80,21 +80,15 @@ def gemm_run(reps: int = 3):
     X = B.bf16_tensor(synth.token_rows(3, 2048, synth.HIDDEN), dev)
     ws = B.workspace(B.workspace_bytes(B.OP_FFN_PREFILL, dl, rows=2048), dev)
     Y = torch.empty((2048, synth.HIDDEN), dtype=torch.float32, device=dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(reps - 1):
+    for _ in range(reps):
         B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
     torch.cuda.synchronize()
-    e0.record()
-    B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    layer_us = e0.elapsed_time(e1) * 1e3
     buf = np.zeros((4, 4096, 8), dtype=np.uint64)
     rc = lib.q4moe_gemm_stamps(buf.ctypes.data_as(ctypes.c_void_p), ctypes.c_size_t(buf.nbytes))
     if rc != 0:
         raise RuntimeError(f"q4moe_gemm_stamps failed ({rc})")
     last = 2 * reps - 1  # launches are recorded in slots (launch index) % 4
-    return layer_us, {"gate/up": buf[(last - 1) % 4], "down": buf[last % 4]}
+    return {"gate/up": buf[(last - 1) % 4], "down": buf[last % 4]}
 
 
 def gemm_summary(name, rec):
@@ -147,7 +141,7 @@ def gemm_summary(name, rec):
 
 
 def gemm_main(args):
-    layer_us, recs = gemm_run()
+    recs = gemm_run()
     lines = ["# grouped_q4_gemm_kernel: workgroup timeline (2,048-token prefill layer)", "",
              "The two grouped-GEMM launches of one prefill layer (hidden 2048, inter 512, 256 routed + 1 shared "
              "experts, top-8, bf16 router, affine Q4 g64): thread 0 of every workgroup stamps the 100 MHz "
@@ -157,7 +151,6 @@ def gemm_main(args):
              "medians.", ""]
     if args.cmd:
         lines += [f"command: `{args.cmd}`", ""]
-    lines += [f"prefill layer time with stamps: {layer_us:.1f} us", ""]
     for name, rec in recs.items():
         lines += gemm_summary(name, rec)
     gu, dn = (r[np.nonzero(r[:, 0])[0]].astype(np.int64) for r in recs.values())

@@ -74,12 +74,13 @@ def build(verbose: bool = False) -> str:
 
 
 # sources rebuilt with stamps in the diagnostic library, and their macros
-STAMPED = {"decode.hip": "-DQ4MOE_DECODE_STAMPS", "gemm.hip": "-DQ4MOE_GEMM_STAMPS"}
+STAMPED = {"decode.hip": "-DQ4MOE_DECODE_STAMPS", "decode_batch.hip": "-DQ4MOE_DECODE_STAMPS",
+           "gemm.hip": "-DQ4MOE_GEMM_STAMPS"}
 
 
 def build_stamps() -> str:
-    """The diagnostic library: every object of build(), the decode layer kernel and the
-    grouped GEMM rebuilt with stamps."""
+    """The diagnostic library: every object of build(), the decode layer kernels (batch-1
+    and the batched front launch) and the grouped GEMM rebuilt with stamps."""
     hipcc = _hipcc()
     build()
     d = os.path.join(BUILD, "stamps")

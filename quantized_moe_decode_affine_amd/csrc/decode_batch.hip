@@ -34,6 +34,7 @@ namespace q4moe {
 namespace {
 
 constexpr int kBitWords = kMaxExperts / 32;
+static_assert(kBitWords <= kWave, "one bitmap word per lane of a wave");
 constexpr int kMaxPlan = kMaxBatch * kMaxTopK + 1;  // distinct experts of a step, shared one included
 constexpr int kFrontThreads = 512;             // front launch
 constexpr int kFrontWaves = kFrontThreads / kWave;
@@ -70,6 +71,26 @@ struct BatchParams {
   int tpp;            // tokens per down workgroup
 };
 
+// Phase stamps of the front launch, in the diagnostic build only (-DQ4MOE_DECODE_STAMPS):
+// thread 0 of every workgroup records the 100 MHz s_memrealtime counter, slot (epoch % 4)
+// of the array (q4moe_front_stamps below): 0 launch start, 1 router logits published,
+// 2 x staged, 3 top-k known, 4 plan ready, 5 end.
+#ifdef Q4MOE_DECODE_STAMPS
+constexpr int kStampBlocks = 1024;
+__device__ unsigned long long g_front_stamps[4][kStampBlocks][8];
+// the down launch's: 0 launch start, 1 plan in LDS, 2 task list built, 3 activations staged,
+// 4 dots done, 5 end (slot: the front launch's epoch % 4; workgroup blockIdx.x of pass 0)
+__device__ unsigned long long g_down_stamps[4][kStampBlocks][8];
+#define Q4MOE_FSTAMP(i, v)                                                                        \
+  do {                                                                                            \
+    if (threadIdx.x == 0 && blockIdx.x < kStampBlocks) g_front_stamps[s_epoch & 3][blockIdx.x][i] = (v); \
+  } while (0)
+#else
+#define Q4MOE_FSTAMP(i, v) \
+  do {                     \
+  } while (0)
+#endif
+
 // ---------------------------------------------------------------- launch 1
 // One gate/up row pair: this lane's 32-column chunk of each row (4-bit: 16 bytes;
 // 8-bit shared rows: 32 bytes, g/g2 and u/u2) and the chunk's group scale and bias.
@@ -104,6 +125,9 @@ __device__ __forceinline__ void batch_front(const BatchParams& p) {
 
   unsigned long long arrival = 0;
   if (t == 0) arrival = epoch_arrive(&ws->h, b);
+#ifdef Q4MOE_DECODE_STAMPS
+  const unsigned long long stamp0 = __builtin_amdgcn_s_memrealtime();
+#endif
 
   // ---- A: router rows e = b, b + NBk, ... dotted with every token, published as tagged words
   const int nrows = b < E ? (E - 1 - b) / NBk + 1 : 0;
@@ -163,6 +187,10 @@ __device__ __forceinline__ void batch_front(const BatchParams& p) {
     lds_sync();  // s_rpart is reused
   }
   if (t == 0 && nrows == 0) s_epoch = epoch_finish(&ws->h, b, NBk, arrival);
+#ifdef Q4MOE_DECODE_STAMPS
+  Q4MOE_FSTAMP(0, stamp0);  // (thread 0 wrote s_epoch itself)
+  Q4MOE_FSTAMP(1, __builtin_amdgcn_s_memrealtime());
+#endif
   // x of every token, for the gate/up dots (while the other workgroups' logits arrive)
   for (int i = t; i < NB * CH; i += kFrontThreads) {
     const int tok = i / CH, c = i - tok * CH;
@@ -170,6 +198,7 @@ __device__ __forceinline__ void batch_front(const BatchParams& p) {
   }
   lds_sync();
   const uint32_t epoch = s_epoch;
+  Q4MOE_FSTAMP(2, __builtin_amdgcn_s_memrealtime());
 
   // ---- B: wave tok takes token tok's top-k (and its shared-expert weight)
   if (wv < NB) {
@@ -205,21 +234,23 @@ __device__ __forceinline__ void batch_front(const BatchParams& p) {
   // ---- the plan (every workgroup alike): distinct experts ranked by id through a bitmap
   for (int i = t; i < kBitWords; i += kFrontThreads) s_bits[i] = 0u;
   lds_sync();
+  Q4MOE_FSTAMP(3, __builtin_amdgcn_s_memrealtime());
   for (int i = t; i < NB * k; i += kFrontThreads) {
     const int id = s_id[i / k][i % k];
     atomicOr(&s_bits[id >> 5], 1u << (id & 31));
   }
   lds_sync();
-  if (wv == 0) {  // exclusive prefix of the per-word counts
+  if (wv == 0) {  // exclusive prefix of the per-word counts (at most 32), from six bit-plane ballots
     const int c = lane < kBitWords ? __popc(s_bits[lane]) : 0;
-    int incl = c;
+    int before = 0, total = 0;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
+    for (int bit = 0; bit < 6; ++bit) {
+      const uint64_t plane = __ballot((c >> bit) & 1);
+      before += __builtin_amdgcn_mbcnt_hi((uint32_t)(plane >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)plane, 0u)) << bit;
+      total += __popcll(plane) << bit;
     }
-    if (lane < kBitWords) s_pre[lane] = incl - c;
-    if (lane == kWave - 1) s_pre[kBitWords] = incl;
+    if (lane < kBitWords) s_pre[lane] = before;
+    if (lane == 0) s_pre[kBitWords] = total;
   }
   lds_sync();
   const int nd = s_pre[kBitWords];
@@ -248,6 +279,7 @@ __device__ __forceinline__ void batch_front(const BatchParams& p) {
     }
   }
 
+  Q4MOE_FSTAMP(4, __builtin_amdgcn_s_memrealtime());
   // ---- C: gate/up row pairs tau = d * I + i over every wave of the grid, pass q taking
   // tau = (q * NBk + b) * waves + wave; each wave keeps kFrontSlots passes of loads in
   // flight.  4-bit experts (routed, and a 4-bit shared one) take that pipelined loop; an
@@ -366,6 +398,11 @@ __device__ __forceinline__ void batch_front(const BatchParams& p) {
       rr[s] = load_chunk(tau2 / I, tau2 % I, c0);
     }
   }
+#ifdef Q4MOE_DECODE_STAMPS
+  wait_vmem();  // (the activation stores are out)
+  __syncthreads();  // every wave of the workgroup is done
+  Q4MOE_FSTAMP(5, __builtin_amdgcn_s_memrealtime());
+#endif
 }
 
 // NB tokens; kLong: hidden above 2048 (more than one 32-column chunk per lane)
@@ -385,7 +422,7 @@ Q4MOE_FRONT_KERNEL(8)
 // ---------------------------------------------------------------- launch 2
 // Workgroup (x, y) owns output rows 8x .. 8x + 7 for tokens y*tpp .. of the pass.  The
 // planned experts that a token of the pass chose are listed; each listed expert's 8 rows
-// are two tasks of 4 rows (16 lanes a row, one 32-column chunk a lane; an 8-bit shared
+// are kDownTPE tasks of 4 rows (16 lanes a row, one 32-column chunk a lane; an 8-bit shared
 // row's chunk is 32 bytes), spread over the waves, and the loads of the first
 // kDownSlots tasks of every wave are issued before the SwiGLU outputs are staged.  Each
 // task writes the 4-row dot of every token of the pass that chose the expert to
@@ -395,7 +432,12 @@ constexpr int kDownWaves = kDownThreads / kWave;
 constexpr int kDownSlots = 6;     // tasks per wave whose loads are issued ahead
 constexpr int kDownRowLanes = 16;  // lanes per down row
 constexpr int kDownTaskRows = kWave / kDownRowLanes;  // rows of one task
-constexpr int kDownRows = 8;      // output rows per workgroup
+#ifndef Q4MOE_DOWN_ROWS
+#define Q4MOE_DOWN_ROWS 8
+#endif
+constexpr int kDownRows = Q4MOE_DOWN_ROWS;  // output rows per workgroup
+constexpr int kDownTPE = kDownRows / kDownTaskRows;  // tasks per (planned expert, token) entry
+static_assert(kDownRows % kDownTaskRows == 0 && (kDownTPE & (kDownTPE - 1)) == 0, "whole tasks, a power of two");
 
 struct DnRegs {
   uint4 c, c2;  // c2: the second 16 bytes of an 8-bit row's chunk (else c again)
@@ -421,40 +463,85 @@ __device__ __forceinline__ void batch_down(const BatchParams& p) {
   const int GI = I >> 6, CI = I >> 5;
   const BatchPlan* plan = p.plan;
   const int nall = plan->n;
-  // every plan entry, used or not, so that these loads go out with the one of n
-  for (int i = t; i < kMaxPlan * kMaxBatch / 8; i += kDownThreads)
-    reinterpret_cast<uint2*>(&s_slot[0][0])[i] = reinterpret_cast<const uint2*>(&plan->slot[0][0])[i];
-  for (int i = t; i < kMaxPlan; i += kDownThreads) s_expert[i] = plan->expert[i];
-  for (int i = t; i < nb * (k + 1); i += kDownThreads) {
-    const int bb = i / (k + 1), j = i - bb * (k + 1);
-    s_w[bb][j] = p.wts[(b0 + bb) * (k + 1) + j];  // slot k: the shared expert's weight
-  }
+#ifdef Q4MOE_DECODE_STAMPS
+  const unsigned long long dstamp0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned dslot = (unsigned)(p.fws->h.group_ctr[0][0] >> 32) & 3u;
+  unsigned long long* dst = g_down_stamps[dslot][blockIdx.x < kStampBlocks ? blockIdx.x : 0];
+  const bool dstamp = threadIdx.x == 0 && blockIdx.y == 0 && blockIdx.x < kStampBlocks;
+#define Q4MOE_DSTAMP(i, v) \
+  do {                     \
+    if (dstamp) dst[i] = (v); \
+  } while (0)
+#else
+#define Q4MOE_DSTAMP(i, v) \
+  do {                     \
+  } while (0)
+#endif
+  Q4MOE_DSTAMP(0, dstamp0);
+  // The plan (every entry, used or not, so that these loads go out with the one of n) and
+  // the routing weights into registers, then the SwiGLU output images of this pass's
+  // tokens (they do not depend on the plan; the first chunk of each thread is loaded here,
+  // so its latency overlaps the plan's), then the plan into LDS.
+  static_assert(kMaxPlan <= kDownThreads && kMaxBatch == 8, "one plan row (8 bytes) per thread");
+  const int nwt = nb * (k + 1);
+  const int ip = min(t, kMaxPlan - 1), iw = min(t, nwt - 1);
+  const int bw = iw / (k + 1), jw = iw - bw * (k + 1);
+  const uint2* ps = reinterpret_cast<const uint2*>(&plan->slot[0][0]) + ip;
+  const int32_t* pe = plan->expert + ip;
+  const float* pwp = p.wts + (b0 + bw) * (k + 1) + jw;  // slot k: the shared expert's weight
+  __builtin_amdgcn_sched_barrier(0);  // addresses first, then the three loads back to back
+  const float pw = *pwp;
+  const uint2 pslot = *ps;
+  const int32_t pexp = *pe;
+  __builtin_amdgcn_sched_barrier(0);  // the plan's loads go out first: its wait then excludes the images
+  constexpr int ST = chunk_stride<2>();
+  const int nchunk = nb * nslot * CI;
+  const uint4* img = reinterpret_cast<const uint4*>(p.act) + (size_t)b0 * nslot * CI * 8;
+  // Wave wv copies chunks 64 wv .. 64 wv + 63 (8 KB, contiguous) in eight 1 KB loads:
+  // load q of lane l is 16-byte piece l % 8 of chunk 64 wv + 8q + l / 8.
+  const int nw = nchunk * 8;  // 16-byte pieces of the images
+  uint4 w0[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) w0[q] = img[min(wv * 512 + q * 64 + lane, nw - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  // (unconditional: threads past the plan rewrite its last entry with the same value, so
+  // no branch invites the compiler to sink the plan's loads behind the images')
+  reinterpret_cast<uint2*>(&s_slot[0][0])[ip] = pslot;
+  s_expert[ip] = pexp;
+  s_w[bw][jw] = pw;
   lds_sync();
+  Q4MOE_DSTAMP(1, __builtin_amdgcn_s_memrealtime());
   if (wv == 0) {  // (planned expert, token) for each token of the pass that chose it, in plan order
     int cnt = 0;
     for (int d0 = 0; d0 < nall; d0 += kWave) {
       const int dd = d0 + lane;
       uint32_t mine = 0;  // bit bb: token b0 + bb chose expert dd
       if (dd < nall) {
+        const uint2 row = *reinterpret_cast<const uint2*>(&s_slot[dd][0]);  // slot bytes of tokens 0..7
+        const uint64_t r64 = (uint64_t)row.y << 32 | row.x;
 #pragma unroll
-        for (int bb = 0; bb < kMaxBatch; ++bb) mine |= (bb < nb && s_slot[dd][b0 + bb] >= 0 ? 1u : 0u) << bb;
+        for (int bb = 0; bb < kMaxBatch; ++bb)
+          mine |= (bb < nb && (int8_t)((r64 >> (8 * ((b0 + bb) & 7))) & 0xFFu) >= 0 ? 1u : 0u) << bb;
       }
+      // exclusive prefix of the counts (at most 8) over the lanes, from four bit-plane ballots
       const int c = __popc(mine);
-      int incl = c;
+      int before = 0, total = 0;
 #pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const int o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
+      for (int bit = 0; bit < 4; ++bit) {
+        const uint64_t plane = __ballot((c >> bit) & 1);
+        before += __builtin_amdgcn_mbcnt_hi((uint32_t)(plane >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)plane, 0u)) << bit;
+        total += __popcll(plane) << bit;
       }
-      int at = cnt + incl - c;
+      int at = cnt + before;
       for (uint32_t m = mine; m; m &= m - 1) s_list[at++] = (int16_t)(dd << 3 | __builtin_ctz(m));
-      cnt += __shfl(incl, kWave - 1);
+      cnt += total;
     }
     if (lane == 0) s_nlist = cnt;
   }
   lds_sync();
-  // task tau: entry tau / 2 of the list, rows (tau % 2) * 4 + rsub of the block
-  const int ntask = 2 * s_nlist;
+  Q4MOE_DSTAMP(2, __builtin_amdgcn_s_memrealtime());
+  // task tau: entry tau / kDownTPE of the list, rows (tau % kDownTPE) * 4 + rsub of the block
+  const int ntask = kDownTPE * s_nlist;
   const int last = max(ntask - 1, 0);
   const int sub = lane & (kDownRowLanes - 1), rsub = lane / kDownRowLanes;
   const int c0 = min(sub, CI - 1);  // this lane's first chunk (lanes past CI: a valid chunk, not used)
@@ -463,8 +550,8 @@ __device__ __forceinline__ void batch_down(const BatchParams& p) {
   // (loads branch-free)
   auto load_dn = [&](int tau, int c) __attribute__((always_inline)) {
     DnRegs r;
-    const int e = __builtin_amdgcn_readfirstlane(s_expert[s_list[tau >> 1] >> 3]);
-    const int n = min(n0 + (tau & 1) * kDownTaskRows + rsub, H - 1);
+    const int e = __builtin_amdgcn_readfirstlane(s_expert[s_list[tau / kDownTPE] >> 3]);
+    const int n = min(n0 + (tau % kDownTPE) * kDownTaskRows + rsub, H - 1);
     const bool q8 = e < 0 && q8sh;
     const uint32_t* codes = e >= 0 ? L.down.codes + e * mat_codes : L.sh_down.codes;
     const uint16_t* sc = e >= 0 ? L.down.scales + e * mat_groups : L.sh_down.scales;
@@ -478,41 +565,41 @@ __device__ __forceinline__ void batch_down(const BatchParams& p) {
   };
   // stage the SwiGLU outputs of this pass's tokens, [nb][nslot] x ([CI][ST2] pairs, [CI]
   // sums): the chunk images are copied; a chunk's sum is the dot of its 32 words with
-  // (1, 1).  The first chunk of each thread is loaded before the weight rows (its wait
+  // (1, 1).  The first chunk of each thread was loaded before the weight rows (its wait
   // then does not include theirs), the rest after.
-  constexpr int ST = chunk_stride<2>();
   constexpr uint32_t kOnes = 0x3F803F80u;  // two bfloat16 1.0
   uint32_t* ap = smem;
   float* as = reinterpret_cast<float*>(ap + (size_t)p.tpp * nslot * CI * ST);
-  const int nchunk = nb * nslot * CI;
-  const uint4* img = reinterpret_cast<const uint4*>(p.act) + (size_t)b0 * nslot * CI * 8;
-  uint4 w0[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) w0[q] = img[(size_t)min(t, nchunk - 1) * 8 + q];
   DnRegs dr[kDownSlots];
 #pragma unroll
   for (int q = 0; q < kDownSlots; ++q) dr[q] = load_dn(min(q * kDownWaves + wv, last), c0);
-  auto put = [&](int i, const uint4 (&w)[8]) __attribute__((always_inline)) {
-    float s0 = 0.f, s1 = 0.f;
+  // pieces of chunks c0w + 8q + lane / 8 into LDS; a chunk's sum meets in its 8 lanes
+  auto put = [&](int c0w, const uint4 (&w)[8]) __attribute__((always_inline)) {
+    const int pc = lane & 7;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      *reinterpret_cast<uint4*>(ap + (size_t)i * ST + 4 * q) = w[q];
-      s0 = dot2_bf16(w[q].x, kOnes, dot2_bf16(w[q].y, kOnes, s0));
-      s1 = dot2_bf16(w[q].z, kOnes, dot2_bf16(w[q].w, kOnes, s1));
+      const int c = c0w + 8 * q + (lane >> 3);
+      const float part = dot2_bf16(w[q].x, kOnes, dot2_bf16(w[q].y, kOnes, 0.f)) +
+                         dot2_bf16(w[q].z, kOnes, dot2_bf16(w[q].w, kOnes, 0.f));
+      const float sum = group_sum<8>(part);
+      if (c < nchunk) {
+        *reinterpret_cast<uint4*>(ap + (size_t)c * ST + 4 * pc) = w[q];
+        if (pc == 0) as[c] = sum;
+      }
     }
-    as[i] = s0 + s1;
   };
-  if (t < nchunk) put(t, w0);
-  for (int i = t + kDownThreads; i < nchunk; i += kDownThreads) {
+  put(wv * 64, w0);
+  for (int c0w = kDownThreads + wv * 64; c0w < nchunk; c0w += kDownThreads) {  // (more than 1,024 chunks)
     uint4 w[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) w[q] = img[(size_t)i * 8 + q];
-    put(i, w);
+    for (int q = 0; q < 8; ++q) w[q] = img[min(c0w * 8 + q * 64 + lane, nw - 1)];
+    put(c0w, w);
   }
   lds_sync();  // (an LDS-only barrier: the weight loads stay in flight)
+  Q4MOE_DSTAMP(3, __builtin_amdgcn_s_memrealtime());
 
   auto compute = [&](int tau, const DnRegs r0) __attribute__((always_inline)) {
-    const int ent = __builtin_amdgcn_readfirstlane(s_list[tau >> 1]);
+    const int ent = __builtin_amdgcn_readfirstlane(s_list[tau / kDownTPE]);
     const int dd = ent >> 3, bb = ent & 7;
     const bool q8 = __builtin_amdgcn_readfirstlane(s_expert[dd]) < 0 && q8sh;
     const int j = __builtin_amdgcn_readfirstlane(s_slot[dd][b0 + bb]);
@@ -521,7 +608,7 @@ __device__ __forceinline__ void batch_down(const BatchParams& p) {
       return q8 ? fmaf(bf16_bits_to_f32(r.s), q8_chunk_pdot<2>(r.c, r.c2, v), bf16_bits_to_f32(r.b) * as[vi])
                 : affine_term(chunk_pdot<2>(r.c, v), as[vi], r.s, r.b);
     };
-    const int r = (tau & 1) * kDownTaskRows + rsub;
+    const int r = (tau % kDownTPE) * kDownTaskRows + rsub;
     const int vi = (bb * nslot + j) * CI;
     float part = sub < CI ? dot(r0, sub, vi + sub) : 0.f;
     if constexpr (kLong)  // rows of more than 16 chunks: the further chunks, loaded here
@@ -541,6 +628,7 @@ __device__ __forceinline__ void batch_down(const BatchParams& p) {
     if (tau < ntask) compute(tau, r);
   }
   lds_sync();
+  Q4MOE_DSTAMP(4, __builtin_amdgcn_s_memrealtime());
   for (int i = t; i < nb * kDownRows; i += kDownThreads) {
     const int bb = i / kDownRows, r = i - bb * kDownRows, nn = n0 + r;
     if (nn >= H) continue;
@@ -552,6 +640,12 @@ __device__ __forceinline__ void batch_down(const BatchParams& p) {
     else
       reinterpret_cast<float*>(p.y)[o] = acc;
   }
+#ifdef Q4MOE_DECODE_STAMPS
+  wait_vmem();
+  __syncthreads();  // every wave of the workgroup is done
+  Q4MOE_DSTAMP(5, __builtin_amdgcn_s_memrealtime());
+#endif
+#undef Q4MOE_DSTAMP
 }
 
 __global__ __launch_bounds__(kDownThreads) void batch_down_kernel(BatchParams p) { batch_down<false>(p); }
@@ -683,3 +777,15 @@ hipError_t run_moe_ffn_decode_batch(const DecodeLayer& L, const uint16_t* X, int
 }
 
 }  // namespace q4moe
+
+#ifdef Q4MOE_DECODE_STAMPS
+// Diagnostic build only: copy the front launch's phase stamps ([4][1024][8] uint64, slot
+// epoch % 4, stamps as listed above) to host memory.
+extern "C" int q4moe_front_stamps(void* host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(q4moe::g_front_stamps), bytes);
+}
+// The same for the down launch's stamps.
+extern "C" int q4moe_down_stamps(void* host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(q4moe::g_down_stamps), bytes);
+}
+#endif

@@ -3,6 +3,7 @@
     python -m quantized_moe_decode_affine_amd.build --stamps
     python -m quantized_moe_decode_affine_amd.phase_timeline [--out FILE.md]
     python -m quantized_moe_decode_affine_amd.phase_timeline --gemm [--out FILE.md]
+    python -m quantized_moe_decode_affine_amd.phase_timeline --batch [--out FILE.md]
 
 Runs the 40-layer decode loop (hidden 2048, 256 routed + 1 shared experts, top-8) on
 ``libq4moe_stamps.so``, where thread 0 of every workgroup records the 100 MHz
@@ -69,6 +70,76 @@ def run(form: str, n_layers: int = 40, steps: int = 8):
         rows.append((NAMES[k], int(np.median(rel)), int(rel.max())))
     gaps = [int((st[b][:, 0].min() - st[a][:, 5].max()) * 10) for a, b in zip(order[:-1], order[1:])]
     return loop_us, rows, gaps
+
+
+FRONT_NAMES = ["launch start", "router logits published", "x staged", "top-k known", "plan ready",
+               "end (every wave done, its stores out)"]
+DOWN_NAMES = ["launch start", "plan in LDS", "task list built", "activations staged", "dots done",
+              "end (every wave done, its stores out)"]
+
+
+def batch_run(nb: int, n_layers: int = 40, steps: int = 4):
+    """Phase stamps of the batched front launch (the last four launches of a 40-layer loop
+    of nb-row steps)."""
+    lib = B.load_library(STAMPS_LIB)
+    stack = workloads.DecodeStack(seed=2, n_layers=n_layers, n_steps=steps, device="cuda")
+    stack.enable_batch(8, "cuda")
+    for s in range(2):
+        stack.step_batch(s, nb)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        stack.step_batch(s, nb)
+    e1.record()
+    torch.cuda.synchronize()
+    loop_us = e0.elapsed_time(e1) * 1e3 / (steps * n_layers)
+    def read(fn):
+        buf = np.zeros((4, 1024, 8), dtype=np.uint64)
+        rc = fn(buf.ctypes.data_as(ctypes.c_void_p), ctypes.c_size_t(buf.nbytes))
+        if rc != 0:
+            raise RuntimeError(f"stamp read failed ({rc})")
+        n = int(np.count_nonzero(buf[0, :, 0]))
+        return buf[:, :n, :6].astype(np.int64), n
+
+    fr, nbk = read(lib.q4moe_front_stamps)
+    dn, ndn = read(lib.q4moe_down_stamps)
+    order = np.argsort(fr[:, :, 0].min(axis=1))  # the four front launches in time order (same slots)
+
+    def table(st, names):
+        rows = []
+        for k in range(6):
+            rel = np.concatenate([(st[i][:, k] - st[i][:, 0].min()) * 10 for i in order])
+            rows.append((names[k], int(np.median(rel)), int(rel.max())))
+        return rows
+    gaps = [(int((dn[i][:, 0].min() - fr[i][:, 5].max()) * 10), int((fr[j][:, 0].min() - dn[i][:, 5].max()) * 10))
+            for i, j in zip(order[:-1], order[1:])]
+    return loop_us, nbk, ndn, table(fr, FRONT_NAMES), table(dn, DOWN_NAMES), gaps
+
+
+def batch_main(args):
+    lines = ["# batch_front_kernel: phase timeline (40-layer batched decode loop)", "",
+             "Phase boundaries of the front launch of batched decode (router for every token, per-token top-k, the "
+             "step's expert plan, gate/up with SwiGLU for the planned experts; hidden 2048, 256 routed + 1 shared "
+             "experts, top-8, affine Q4 g64), stamped by thread 0 of every workgroup with the 100 MHz s_memrealtime "
+             "counter in the diagnostic build (decode_batch.hip with Q4MOE_DECODE_STAMPS, libq4moe_stamps.so), over "
+             "the last four launches of each kind; times are relative to the launch's first workgroup start. "
+             "The end stamps follow a wait for the stores and a workgroup barrier.", ""]
+    if args.cmd:
+        lines += [f"command: `{args.cmd}`", ""]
+    for nb in (4, 8):
+        loop_us, nbk, ndn, fr, dn, gaps = batch_run(nb)
+        lines += [f"## B = {nb}", "", f"loop time with stamps (both launches): {loop_us:.2f} us per layer", ""]
+        for title, n, rows in ((f"front launch, {nbk} workgroups", nbk, fr),
+                               (f"down launch, {ndn} workgroups of the first token pass", ndn, dn)):
+            lines += [title, "", "| phase boundary | median over workgroups (ns) | latest workgroup (ns) |",
+                      "|---|---|---|"]
+            lines += [f"| {a} | {m} | {x} |" for a, m, x in rows]
+            lines += [""]
+        lines += ["gaps from the front launch's last end to the down launch's first start, and from the down "
+                  "launch's last end to the next front launch's first start (ns): "
+                  + ", ".join(f"{a} / {b}" for a, b in gaps), ""]
+    return lines
 
 
 def gemm_run(reps: int = 3):
@@ -166,9 +237,10 @@ def main():
     ap.add_argument("--out", default=None, help="write the Markdown summary here as well")
     ap.add_argument("--cmd", default="", help="the command line to record in the summary")
     ap.add_argument("--gemm", action="store_true", help="the prefill layer's grouped GEMMs instead of decode")
+    ap.add_argument("--batch", action="store_true", help="the batched decode's front launch instead")
     args = ap.parse_args()
-    if args.gemm:
-        text = "\n".join(gemm_main(args))
+    if args.gemm or args.batch:
+        text = "\n".join(gemm_main(args) if args.gemm else batch_main(args))
         print(text, flush=True)
         if args.out:
             with open(args.out, "w") as f:

@@ -831,9 +831,13 @@ size_t gemv_lds_bytes(int k, int B) { return gemv_lds(k, B); }
 
 namespace {
 
-// Rows per lane and step by batch size: B = 1 keeps the most bytes in flight.
+// Rows per lane and step by batch size (B = 1: two rows, software-pipelined; measured against
+// one, four and eight, two leaves the most waves per SIMD with enough bytes in flight).
+#ifndef Q4MOE_LMHEAD_ROWS_B1
+#define Q4MOE_LMHEAD_ROWS_B1 2
+#endif
 template <int B>
-constexpr int lmhead_rows_per_lane() { return B <= 2 ? 4 : B <= 4 ? 2 : 1; }
+constexpr int lmhead_rows_per_lane() { return B <= 2 ? Q4MOE_LMHEAD_ROWS_B1 : B <= 4 ? 2 : 1; }
 
 template <int B, bool kQ8 = false>
 int lmhead_mfma_resident(size_t lds) {

@@ -114,9 +114,17 @@ __global__ __launch_bounds__(kRankThreads) void chunk_rank_kernel(const int32_t*
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
   const int64_t c0 = (int64_t)blockIdx.x * kRankChunk;
-  for (int sub = 0; sub < kRankChunk / kRankThreads; ++sub) {  // 256 rows at a time, in row order
+  constexpr int kSubs = kRankChunk / kRankThreads;
+  int ids_sub[kSubs];  // this thread's rows' experts, all loaded before the first barrier
+#pragma unroll
+  for (int sub = 0; sub < kSubs; ++sub) {
     const int64_t r = c0 + sub * kRankThreads + threadIdx.x;
-    const int e = r < rows ? ids[r] : -1;
+    ids_sub[sub] = ids[min(r, rows - 1)];
+  }
+#pragma unroll
+  for (int sub = 0; sub < kSubs; ++sub) {  // 256 rows at a time, in row order
+    const int64_t r = c0 + sub * kRankThreads + threadIdx.x;
+    const int e = r < rows ? ids_sub[sub] : -1;
     const bool valid = e >= 0 && e < E;
     const uint32_t key = valid ? (uint32_t)e : 1024u;  // E <= 1024: 11 key bits
     uint64_t same = ~0ull;  // lanes of this wave holding the same key
@@ -155,10 +163,18 @@ __global__ __launch_bounds__(1024) void expert_scatter_kernel(const int32_t* __r
   const int tr = tiled ? tiles.tile_rows : 1;
   int32_t c = 0, before = 0;
   if (i < E)
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int32_t h = hist[(int64_t)ch * E + i];
-      before += ch < (int)blockIdx.x ? h : 0;
-      c += h;
+    for (int ch0 = 0; ch0 < nchunks; ch0 += 16) {  // 16 chunks' counts in flight at once
+      int32_t h[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) h[j] = hist[(int64_t)min(ch0 + j, nchunks - 1) * E + i];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int ch = ch0 + j;
+        if (ch < nchunks) {
+          before += ch < (int)blockIdx.x ? h[j] : 0;
+          c += h[j];
+        }
+      }
     }
   s_before[i] = before;
   s_c[i] = c;

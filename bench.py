@@ -157,10 +157,11 @@ def main():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip every leg but the 40-layer decode loop")
-    ap.add_argument("--legs", default="q8router,chain,batch,prefill,wide,lmhead",
+    ap.add_argument("--legs", default="q8router,chain,batch,prefill,prefill_rm,wide,lmhead",
                     help="comma list of the legs run after the decode loop: q8router (the same loop with affine-Q8 "
                          "routers), chain (residual-chained step with the LM head, eager and as a replayed graph), "
-                         "batch (several requests per step), prefill (2,048-token chunk), wide (512 experts, "
+                         "batch (several requests per step), prefill (2,048-token chunk), prefill_rm (the same chunk "
+                         "reading the expert codes row-major), wide (512 experts, "
                          "top-10), lmhead")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (the known-size reference that scales the "
@@ -374,6 +375,7 @@ def main():
         log("building the prefill layer")
         layer = synth.moe_layer(1)
         dl = B.DeviceLayer(layer, dev)
+        dl.pack_group_major()  # the GEMMs read the expert codes group-major (a load-time layout step)
         del layer
         X = B.bf16_tensor(synth.token_rows(3, 2048, synth.HIDDEN), dev)
         ws = B.workspace(B.workspace_bytes(B.OP_FFN_PREFILL, dl, rows=2048), dev)
@@ -392,7 +394,7 @@ def main():
         tfl = flops / (p_us * 1e-6) / 1e12
         g_us = profiled_gemm_us()
         result["prefill"] = {"workload": "2,048-token chunk through one MoE layer (route, permute, grouped Q4 "
-                                         "GEMMs with SwiGLU, combine)",
+                                         "GEMMs with SwiGLU, combine; expert codes also held group-major)",
                              "us_per_layer": round(p_us, 2), "tokens_per_s": round(2048 / (p_us * 1e-6), 1),
                              "expert_gflop": round(flops / 1e9, 3),
                              "tflops_whole_layer": round(tfl, 2),
@@ -408,6 +410,7 @@ def main():
         layer.router_q8 = synth.q8_matrix(1, 0, synth.ROUTER_STREAM, 0, synth.N_EXPERTS, synth.HIDDEN,
                                           scale_std=0.02 / 74)
         dl8 = B.DeviceLayer(layer, dev)
+        dl8.pack_group_major()
         del layer
         for _ in range(2):
             B.moe_ffn_prefill(dl8, X, out=Y, ws=ws)
@@ -420,6 +423,29 @@ def main():
         result["prefill"]["q8_router_us_per_layer"] = round(ev0.elapsed_time(ev1) * 1e3 / reps, 2)
         log(f"prefill with q8 router: {result['prefill']['q8_router_us_per_layer']} us/layer")
         del dl, dl8, X, ws, Y
+        torch.cuda.empty_cache()
+
+    if "prefill_rm" in legs:
+        # ---------------- the same chunk with the expert codes read in their row-major (MLX) layout only
+        layer = synth.moe_layer(1)
+        dl = B.DeviceLayer(layer, dev)
+        del layer
+        X = B.bf16_tensor(synth.token_rows(3, 2048, synth.HIDDEN), dev)
+        ws = B.workspace(B.workspace_bytes(B.OP_FFN_PREFILL, dl, rows=2048), dev)
+        Y = torch.empty((2048, synth.HIDDEN), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
+        torch.cuda.synchronize()
+        reps = 10
+        ev0.record()
+        for _ in range(reps):
+            B.moe_ffn_prefill(dl, X, out=Y, ws=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        rm_us = round(ev0.elapsed_time(ev1) * 1e3 / reps, 2)
+        result.setdefault("prefill", {})["row_major_codes_us_per_layer"] = rm_us
+        log(f"prefill, row-major codes only: {rm_us} us/layer")
+        del dl, X, ws, Y
         torch.cuda.empty_cache()
 
     if "wide" in legs:

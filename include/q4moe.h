@@ -73,7 +73,16 @@ enum {
  * w = scale*q + bias.  q4_gemv and lmhead_argmax take 8-bit matrices, the layer
  * calls an 8-bit router (router_q8) and an 8-bit shared expert, and
  * moe_route_topk_q8 an 8-bit router; the other calls return Q4MOE_EUNSUPPORTED
- * for them. */
+ * for them.
+ *
+ * codes_gm (optional, 4-bit only): the same codes group-major, as written by
+ * q4moe_pack_group_major: uint32 [count][k/64][n][8], the 32 code bytes of group
+ * g of row r at word ((e*k/64 + g)*n + r)*8, so that a group's bytes of consecutive
+ * rows are contiguous.  q4_gemm and moe_ffn_prefill read it for their grouped GEMMs
+ * (the products, their order and the results are those of the `codes` form) when
+ * every 4-bit matrix they multiply carries it; every other call reads `codes`.  It is
+ * a layout of the prefill's own, next to the MLX layout that decode streams row by
+ * row. */
 typedef struct {
   const uint32_t* codes;
   const q4moe_bf16* scales;
@@ -83,6 +92,7 @@ typedef struct {
   int64_t k;      /* columns, a multiple of 64 */
   int32_t bits;   /* code width: 4 (0 also means 4) or 8 */
   int32_t reserved;  /* 0 */
+  const uint32_t* codes_gm;  /* null, or the group-major copy of codes (16-byte aligned) */
 } q4moe_matrix;
 
 /*
@@ -267,6 +277,15 @@ int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, vo
  */
 int lmhead_argmax(const q4moe_matrix* W, const q4moe_bf16* X, int64_t B, int32_t* ids,
                   float* max_logit, void* workspace, size_t workspace_bytes, q4moe_stream stream);
+
+/*
+ * Write the group-major copy of a 4-bit matrix's codes (see q4moe_matrix) to dst:
+ * uint32 [count][k/64][n][8] (count*n*k/8 words, 16-byte aligned, device memory the
+ * caller owns; it must not overlap W->codes).  A layout step for prefill, done once per
+ * matrix (when weights are loaded), not per call.  W must be 4-bit (8-bit:
+ * Q4MOE_EUNSUPPORTED); W->codes_gm is ignored.  Asynchronous on `stream`.
+ */
+int q4moe_pack_group_major(const q4moe_matrix* W, uint32_t* dst, q4moe_stream stream);
 
 /*
  * Workspace bytes for an operation.  `layer` is read for the FFN and ROUTE

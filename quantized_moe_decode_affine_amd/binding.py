@@ -22,7 +22,7 @@ OP_GEMV, OP_GEMM, OP_ROUTE, OP_PERMUTE, OP_FFN_DECODE, OP_FFN_PREFILL, OP_LMHEAD
 
 EXPORTS = ("q4_gemv", "q4_gemm", "moe_route_topk", "moe_route_topk_q8", "moe_permute", "moe_ffn_decode", "moe_ffn_decode_noalloc",
            "moe_ffn_decode_batch",
-           "moe_ffn_prefill", "lmhead_argmax", "q4moe_workspace_bytes", "q4moe_strerror")
+           "moe_ffn_prefill", "lmhead_argmax", "q4moe_pack_group_major", "q4moe_workspace_bytes", "q4moe_strerror")
 
 
 class Q4Error(RuntimeError):
@@ -34,7 +34,7 @@ class Q4Error(RuntimeError):
 class q4moe_matrix(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("count", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
-                ("bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("bits", ctypes.c_int32), ("reserved", ctypes.c_int32), ("codes_gm", ctypes.c_void_p)]
 
 
 class q4moe_layer(ctypes.Structure):
@@ -70,6 +70,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
         "moe_ffn_decode_batch": [pl, vp, i64, vp, ctypes.c_int, vp, vp, vp, sz, vp],
         "moe_ffn_prefill": [pl, vp, i64, vp, ctypes.c_int, vp, sz, vp],
         "lmhead_argmax": [pm, vp, i64, vp, vp, vp, sz, vp],
+        "q4moe_pack_group_major": [pm, vp, vp],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -131,8 +132,18 @@ class DeviceQ4:
         self.codes = _dev(codes, device)
         self.scales = _dev(scales, device)
         self.biases = _dev(biases, device)
+        self.codes_gm = None
         self.struct = q4moe_matrix(self.codes.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
                                    self.count, self.n, self.k, self.bits, 0)
+
+    def pack_group_major(self) -> None:
+        """Add the group-major copy of the codes that the prefill GEMMs read (4-bit only)."""
+        if self.bits != 4 or self.codes_gm is not None:
+            return
+        self.codes_gm = torch.empty_like(self.codes)
+        _check("q4moe_pack_group_major", load_library().q4moe_pack_group_major(
+            ctypes.byref(self.struct), _ptr(self.codes_gm), _stream()))
+        self.struct.codes_gm = self.codes_gm.data_ptr()
 
     @property
     def nbytes(self) -> int:
@@ -152,18 +163,27 @@ class DeviceLayer:
         self.has_shared = layer.has_shared
         if layer.has_shared:
             self.sh = [DeviceQ4(m.codes, m.scales, m.biases, device) for m in (layer.sh_gate, layer.sh_up, layer.sh_down)]
-            sh = [m.struct for m in self.sh]
         else:
             self.sh = []
-            sh = [q4moe_matrix() for _ in range(3)]
         rq8 = getattr(layer, "router_q8", None)
         self.router_q8 = DeviceQ4(*rq8, device=device) if rq8 is not None else None
         gw = getattr(layer, "sh_gate_w", None)
         self.sh_gate_w = _dev(gw, device) if gw is not None else None
+        self._describe()
+
+    def _describe(self) -> None:
+        sh = [m.struct for m in self.sh] if self.has_shared else [q4moe_matrix() for _ in range(3)]
         self.struct = q4moe_layer(self.hidden, self.inter, self.n_experts, self.top_k, self.router.data_ptr(),
                                   self.gate.struct, self.up.struct, self.down.struct, *sh,
                                   self.router_q8.struct if self.router_q8 is not None else q4moe_matrix(),
                                   self.sh_gate_w.data_ptr() if self.sh_gate_w is not None else None)
+
+    def pack_group_major(self) -> None:
+        """Give every 4-bit expert matrix its group-major copy (moe_ffn_prefill reads those;
+        the decode calls keep reading the row-major codes).  Doubles the 4-bit code memory."""
+        for m in (self.gate, self.up, self.down, *self.sh):
+            m.pack_group_major()
+        self._describe()
 
     @property
     def nbytes(self) -> int:

@@ -38,6 +38,7 @@ bool matrix_ok(const q4moe_matrix* W) {
   if (W->bits != 0 && W->bits != 4 && W->bits != 8) return false;
   if (W->count < 1 || W->n < 1 || W->k < 64 || W->k % 64) return false;
   if (!aligned(W->codes, 16) || !aligned(W->scales, 2) || !aligned(W->biases, 2)) return false;
+  if (W->codes_gm && (W->bits == 8 || !aligned(W->codes_gm, 16))) return false;
   return true;
 }
 
@@ -45,7 +46,7 @@ bool matrix_shape(const q4moe_matrix& W, int64_t count, int64_t n, int64_t k) {
   return matrix_ok(&W) && W.count == count && W.n == n && W.k == k;
 }
 
-Q4Mat to_mat(const q4moe_matrix& W) { return Q4Mat{W.codes, W.scales, W.biases}; }
+Q4Mat to_mat(const q4moe_matrix& W) { return Q4Mat{W.codes, W.scales, W.biases, W.codes_gm}; }
 
 bool is_q8(const q4moe_matrix& W) { return W.bits == 8; }
 
@@ -183,8 +184,10 @@ int q4_gemm(const q4moe_matrix* W, const q4moe_bf16* X, int64_t m, void* Y, int 
     if (m == 0) return Q4MOE_OK;
     const size_t need = q4moe::gemm_workspace_bytes(m, (int)W->k);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return Q4MOE_EWORKSPACE;
-    return hip_status(q4moe::run_q4_gemm(to_mat(*W), n, (int)W->k, X, m, Y, out_dtype == Q4MOE_OUT_BF16,
-                                         workspace, (hipStream_t)stream));
+    Q4Mat w = to_mat(*W);
+    if (W->count != 1) w.codes_gm = nullptr;  // the group-major form is per matrix; a stack is read row-major
+    return hip_status(q4moe::run_q4_gemm(w, n, (int)W->k, X, m, Y, out_dtype == Q4MOE_OUT_BF16, workspace,
+                                         (hipStream_t)stream));
   } catch (...) {
     return Q4MOE_EHIP;
   }
@@ -360,6 +363,22 @@ int lmhead_argmax(const q4moe_matrix* W, const q4moe_bf16* X, int64_t B, int32_t
                                                     ids, max_logit, keys, done, (hipStream_t)stream));
     return hip_status(q4moe::run_lmhead_argmax(W->codes, W->scales, W->biases, rows, (int)W->k, X, (int)B, ids,
                                                max_logit, keys, done, (hipStream_t)stream));
+  } catch (...) {
+    return Q4MOE_EHIP;
+  }
+}
+
+int q4moe_pack_group_major(const q4moe_matrix* W, uint32_t* dst, q4moe_stream stream) {
+  try {
+    if (!W || !dst || !aligned(dst, 16)) return Q4MOE_EINVAL;
+    q4moe_matrix m = *W;
+    m.codes_gm = nullptr;  // not read here
+    if (!matrix_ok(&m)) return Q4MOE_EINVAL;
+    if (is_q8(m)) return Q4MOE_EUNSUPPORTED;
+    const uintptr_t bytes = (uintptr_t)(m.count * m.n * (m.k / 8)) * 4;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(m.codes), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return Q4MOE_EINVAL;  // overlapping copies
+    return hip_status(q4moe::run_pack_group_major(m.codes, m.count, m.n, (int)m.k, dst, (hipStream_t)stream));
   } catch (...) {
     return Q4MOE_EHIP;
   }

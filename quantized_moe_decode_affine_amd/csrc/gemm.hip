@@ -77,6 +77,7 @@ struct GemmParams {
   int out_bf16;
   int64_t ldo;
   int vec_out;                // N and ldo multiples of 4, out aligned to 4 elements: 4-column stores
+  int b_gm;                   // the 4-bit matrices' codes are read from their group-major copies
 #ifdef Q4MOE_GEMM_STAMPS
   int stamp_slot;             // which of the four stamp records this launch fills
 #endif
@@ -270,6 +271,10 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   const Q4Mat& M1 = seg >= 0 ? (swiglu ? p.W2 : p.W) : (swiglu ? p.X2 : p.X);
   const int64_t oc = seg >= 0 ? seg * p.w_codes_stride : 0;
   const int64_t og = seg >= 0 ? seg * p.w_groups_stride : 0;
+  // Group-major codes: one K group of 32 consecutive rows is 1 KB of contiguous bytes,
+  // so each B load instruction reads whole cache lines instead of 32 rows' 32-byte pieces.
+  const bool gm = kBits == 4 && p.b_gm;
+  const int64_t bstep = gm ? (int64_t)p.N * 2 : 2 * kBW;  // per K group, in 16-byte words
   int col[2];
   const uint4* bcodes[2];
   const uint16_t* bscale[2];
@@ -280,7 +285,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     const int64_t wrow = min(col[nb], p.N - 1);
     const Q4Mat& Mx = nb == 0 ? M0 : M1;
     // this lane's half of a group: 32 codes = 16 bytes (4-bit) or 32 bytes (8-bit)
-    bcodes[nb] = reinterpret_cast<const uint4*>(Mx.codes + oc + wrow * (p.K * kBits / 32)) + kBW * lh;
+    bcodes[nb] = gm ? reinterpret_cast<const uint4*>(Mx.codes_gm + oc) + wrow * 2 + lh
+                    : reinterpret_cast<const uint4*>(Mx.codes + oc + wrow * (p.K * kBits / 32)) + kBW * lh;
     bscale[nb] = Mx.scales + og + wrow * p.G;
     bbias[nb] = Mx.biases + og + wrow * p.G;
   }
@@ -317,7 +323,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int h = 0; h < kBW; ++h)
-        __builtin_amdgcn_global_load_lds(bcodes[nb] + 2 * kBW * g + h, stage_b(st) + ((wave * 2 + nb) * kBW + h) * 1024,
+        __builtin_amdgcn_global_load_lds(bcodes[nb] + g * bstep + h, stage_b(st) + ((wave * 2 + nb) * kBW + h) * 1024,
                                          16, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) sc[nb] = ld_global_u16(bscale[nb] + g);
@@ -781,6 +787,32 @@ hipError_t launch_prep_rows(const In* A, int64_t rows, int K, uint16_t* out, uin
 
 }  // namespace
 
+namespace {
+// Group-major copy of 4-bit codes: 16-byte word i of dst is half (i & 1) of group g of
+// row r of matrix e, with i >> 1 = (e*G + g)*n + r; the source row holds G*2 such words.
+__global__ void pack_group_major_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t count,
+                                        int64_t n, int64_t G) {
+  const int64_t total = count * G * n * 2;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rn = i >> 1;
+    const int64_t r = rn % n, eg = rn / n;
+    const int64_t g = eg % G, e = eg / G;
+    dst[i] = src[(e * n + r) * (G * 2) + g * 2 + (i & 1)];
+  }
+}
+}  // namespace
+
+hipError_t run_pack_group_major(const uint32_t* codes, int64_t count, int64_t n, int k, uint32_t* dst,
+                                hipStream_t stream) {
+  const int64_t words = count * n * (k / 64) * 2;
+  if (words == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((words + 255) / 256, 8192);
+  hipLaunchKernelGGL(pack_group_major_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(codes), reinterpret_cast<uint4*>(dst), count, n,
+                     (int64_t)(k / 64));
+  return hipGetLastError();
+}
+
 // q4_gemm workspace: row-sum parts [m][2][Gp] fp16, row exponents [m], fp16 rows [m][k].
 size_t gemm_workspace_bytes(int64_t m, int k) {
   return align256((size_t)m * 2 * pad16(k / 64) * 2) + align256((size_t)m * 4) + align256((size_t)m * k * 2);
@@ -808,6 +840,7 @@ hipError_t run_q4_gemm(const Q4Mat& W, int64_t n, int k, const uint16_t* X, int6
   p.N = (int)n;
   p.X = W;
   p.X2 = W;
+  p.b_gm = W.codes_gm != nullptr;
   p.extra_rows = m;
   p.n_slices = (int)((n + BN - 1) / BN);
   p.epi = EPI_STORE;
@@ -926,6 +959,10 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   p.out_bf16 = 0;
   p.ldo = I;
   const bool sh_q8 = L.has_shared && L.sh_q8;
+  // group-major codes when every 4-bit matrix of the launch has them (an 8-bit shared
+  // expert runs in a launch of its own that reads its row-major codes)
+  auto gm = [](const Q4Mat& a, const Q4Mat& b) { return a.codes_gm && b.codes_gm; };
+  p.b_gm = gm(L.gate, L.up) && (!L.has_shared || sh_q8 || gm(L.sh_gate, L.sh_up));
   e = launch_grouped(p, max_tiles, stream, sh_q8);
   if (e != hipSuccess) return e;
 
@@ -949,6 +986,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   d.w_groups_stride = (int64_t)H * (I / 64);
   d.X = L.sh_down;
   d.X2 = L.sh_down;
+  d.b_gm = gm(L.down, L.down) && (!L.has_shared || sh_q8 || gm(L.sh_down, L.sh_down));
   d.n_slices = (H + BN - 1) / BN;
   d.epi = EPI_SCALE;
   d.out = w.ys;

@@ -36,6 +36,7 @@ struct Q4Mat {
   const uint32_t* codes;   // [count][n][k/8]
   const uint16_t* scales;  // [count][n][k/64]
   const uint16_t* biases;
+  const uint32_t* codes_gm = nullptr;  // null, or the codes group-major: [count][k/64][n][8]
 };
 
 // ---- decode MoE layer (decode.hip)
@@ -102,6 +103,9 @@ hipError_t run_permute(const int32_t* ids, int64_t rows, int n_experts, int32_t*
 size_t gemm_workspace_bytes(int64_t m, int k);
 hipError_t run_q4_gemm(const Q4Mat& W, int64_t n, int k, const uint16_t* X, int64_t m, void* Y, int out_bf16,
                        void* ws, hipStream_t stream);
+// Group-major copy of a stack of 4-bit matrices' codes (Q4Mat::codes_gm layout).
+hipError_t run_pack_group_major(const uint32_t* codes, int64_t count, int64_t n, int k, uint32_t* dst,
+                                hipStream_t stream);
 size_t prefill_workspace_bytes(int64_t T, int hidden, int inter, int n_experts, int top_k, int has_shared);
 hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t T, void* Y, int out_bf16,
                                void* ws, hipStream_t stream);

@@ -211,6 +211,28 @@ def test_lmhead_rejects(lib):
     assert f(ctypes.byref(_mat(1, 1000, 8192)), A, 4, A, None, A, need, None) == B.EUNSUPPORTED
 
 
+def test_group_major_rejects(lib):
+    f = lib.q4moe_pack_group_major
+    W = _mat(2, 64, 128)                                   # codes span 2*64*128/2 = 8 KiB from A
+    assert f(None, A2 + 0x10000, None) == B.EINVAL
+    assert f(ctypes.byref(W), None, None) == B.EINVAL
+    assert f(ctypes.byref(W), A2 + 0x10004, None) == B.EINVAL    # dst misaligned
+    assert f(ctypes.byref(W), A + 0x1000, None) == B.EINVAL      # dst overlaps the codes
+    assert f(ctypes.byref(_mat(k=100)), A2 + 0x10000, None) == B.EINVAL
+    q8 = B.q4moe_matrix(A, A2, A2 + 0x1000, 1, 64, 128, 8)
+    assert f(ctypes.byref(q8), A2 + 0x10000, None) == B.EUNSUPPORTED
+    # a group-major copy must be 16-byte aligned and belongs to 4-bit matrices only
+    bad = _mat()
+    bad.codes_gm = A2 + 0x10008
+    assert lib.q4_gemv(ctypes.byref(bad), A, A, 0, None) == B.EINVAL
+    q8.codes_gm = A2 + 0x10000
+    assert lib.q4_gemv(ctypes.byref(q8), A, A, 0, None) == B.EINVAL
+    L = _layer()
+    L.down.codes_gm = A2 + 0x10008
+    need_p = lib.q4moe_workspace_bytes(B.OP_FFN_PREFILL, ctypes.byref(L), None, 50)
+    assert lib.moe_ffn_prefill(ctypes.byref(L), A, 50, A, 0, A, need_p, None) == B.EINVAL
+
+
 def test_workspace_queries(lib):
     assert lib.q4moe_workspace_bytes(B.OP_GEMV, None, None, 1) == 0
     assert lib.q4moe_workspace_bytes(99, None, None, 1) == 0

@@ -465,6 +465,7 @@ def main():
         w_layer_us = ev0.elapsed_time(ev1) * 1e3 / (wsteps * wstack.n_layers)
         w_bytes = workloads.decode_layer_bytes(**wide)
         dl = wstack.layers[0]
+        dl.pack_group_major()
         T4 = 4096
         X = B.bf16_tensor(synth.token_rows(5, T4, synth.HIDDEN), dev)
         ws = B.workspace(B.workspace_bytes(B.OP_FFN_PREFILL, dl, rows=T4), dev)

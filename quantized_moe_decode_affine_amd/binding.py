@@ -173,10 +173,14 @@ class DeviceLayer:
 
     def _describe(self) -> None:
         sh = [m.struct for m in self.sh] if self.has_shared else [q4moe_matrix() for _ in range(3)]
-        self.struct = q4moe_layer(self.hidden, self.inter, self.n_experts, self.top_k, self.router.data_ptr(),
-                                  self.gate.struct, self.up.struct, self.down.struct, *sh,
-                                  self.router_q8.struct if self.router_q8 is not None else q4moe_matrix(),
-                                  self.sh_gate_w.data_ptr() if self.sh_gate_w is not None else None)
+        new = q4moe_layer(self.hidden, self.inter, self.n_experts, self.top_k, self.router.data_ptr(),
+                          self.gate.struct, self.up.struct, self.down.struct, *sh,
+                          self.router_q8.struct if self.router_q8 is not None else q4moe_matrix(),
+                          self.sh_gate_w.data_ptr() if self.sh_gate_w is not None else None)
+        if hasattr(self, "struct"):  # rewritten in place: references taken to it stay current
+            ctypes.memmove(ctypes.addressof(self.struct), ctypes.addressof(new), ctypes.sizeof(new))
+        else:
+            self.struct = new
 
     def pack_group_major(self) -> None:
         """Give every 4-bit expert matrix its group-major copy (moe_ffn_prefill reads those;

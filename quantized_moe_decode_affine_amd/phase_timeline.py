@@ -148,6 +148,7 @@ def gemm_run(reps: int = 3):
     lib = B.load_library(STAMPS_LIB)
     dev = "cuda"
     dl = B.DeviceLayer(synth.moe_layer(1), dev)
+    dl.pack_group_major()
     X = B.bf16_tensor(synth.token_rows(3, 2048, synth.HIDDEN), dev)
     ws = B.workspace(B.workspace_bytes(B.OP_FFN_PREFILL, dl, rows=2048), dev)
     Y = torch.empty((2048, synth.HIDDEN), dtype=torch.float32, device=dev)

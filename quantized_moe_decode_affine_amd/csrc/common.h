@@ -190,6 +190,12 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kLoadDeviceScope = 16;
 
+// s_waitcnt immediate for "at most n vector-memory ops outstanding" (gfx9 encoding,
+// expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// The same with lgkmcnt(0) (all of this wave's LDS reads done).
+constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xF << 8); }
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses, not

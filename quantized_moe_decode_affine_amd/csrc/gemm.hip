@@ -158,11 +158,6 @@ __device__ __forceinline__ uint4 codes8_to_operand(uint32_t w0, uint32_t w1, f16
 // bf16 bits -> fp16 (exact for magnitudes in fp16's normal range).
 __device__ __forceinline__ _Float16 bf16_bits_to_f16(uint32_t bits) { return (_Float16)bf16_bits_to_f32(bits); }
 
-// s_waitcnt immediate for "at most n vector-memory ops outstanding" (gfx9 encoding,
-// expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-// The same with lgkmcnt(0) (all of this wave's LDS reads done).
-constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~(0xF << 8); }
 
 // Pipeline depth (K groups in flight) and per-stage vector-memory ops per thread:
 // MB A-tile LDS loads, 2 (4-bit) or 4 (8-bit) B-code LDS loads, 2 scale loads.

@@ -2,6 +2,8 @@
 // and the stable counting sort that groups (token, slot) rows by expert for
 // the prefill expert GEMM (lily-qwen3.8-flash-next README, "How the speed was
 // achieved": prefill runs the expert GEMM over token-to-expert groups).
+#include <type_traits>
+
 #include "kernels.h"
 #include "topk.h"
 
@@ -12,67 +14,134 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // logits[t][e] = X[t] . router[e]: bf16 MFMA 32x32x16, fp32 accumulation.
-// Workgroup = 32 tokens x 64 experts, 8 waves: wave w computes the 32x32 block
-// of expert half (w & 1) over K quarter (w >> 1), loading four 64-column steps
-// at a time so that each wave has eight 128-bit loads per lane in flight; the
-// quarters are summed through LDS in a fixed order.  Every lane loads its own
-// 64-byte strips of X and router per step, so both operands use the same
-// (arbitrary but consistent) order of the 64 columns inside a step.
-constexpr int kRouterBatch = 4;
+// Workgroup = 32 tokens x 64 experts, 8 waves: wave w computes the 32x32 block of
+// expert half (w & 1) over K quarter (w >> 1); the quarters are summed through LDS in
+// a fixed order.  Each 64-column K step of both operands goes through LDS: one
+// 16-byte-per-lane load instruction reads 8 whole 128-byte row pieces (8 cache lines;
+// a row per lane would touch 32 lines per instruction), and three steps are in flight.
+// Inside a row the eight 16-byte pieces are XOR-rotated by row bits 1-3, so that the
+// MFMA operand reads (a row per lane) spread over all banks.
+constexpr int kRouterBatch = 4;  // the 8-bit router's groups loaded per batch
+constexpr int kRouterStages = 3;
+constexpr int kRouterQuarterBytes = (32 + 64) * 128;  // one quarter's token and expert rows of a step
+constexpr int kRouterOps = 6;                         // load instructions per wave and step
+
+__device__ __forceinline__ int router_swz(int r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __restrict__ router,
                                                             const uint16_t* __restrict__ X, int64_t T, int E,
                                                             int H, float* __restrict__ logits) {
-  __shared__ f32x16_t s_part[3][2][kWave];
+  // one array per stage, so that the compiler can tell a stage's reads from the loads
+  // still filling another
+  __shared__ __align__(16) uint8_t s_st0[4 * kRouterQuarterBytes], s_st1[4 * kRouterQuarterBytes],
+      s_st2[4 * kRouterQuarterBytes];
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int eh = wave & 1, kq = wave >> 1;
   const int64_t t0 = (int64_t)blockIdx.x * 32;
-  const int e0 = blockIdx.y * 64 + eh * 32;
-  const int m = lane & 31, h = lane >> 5;
-  const int64_t trow = min<int64_t>(t0 + m, T - 1);
-  const int erow = min(e0 + m, E - 1);
-  const uint4* xa = reinterpret_cast<const uint4*>(X + trow * H) + 4 * h;
-  const uint4* rb = reinterpret_cast<const uint4*>(router + (int64_t)erow * H) + 4 * h;
+  const int eb = blockIdx.y * 64;
   const int steps = H >> 6;
-  const int s_begin = kq * steps / 4, s_end = (kq + 1) * steps / 4;
-  f32x16_t acc = {};
-  for (int s0 = s_begin; s0 < s_end; s0 += kRouterBatch) {
-    uint4 av[kRouterBatch][4], bv[kRouterBatch][4];
+  const int per_q = (steps + 3) >> 2;  // steps per quarter: every wave runs the same count
+  const int q_first = kq * per_q;
+
+  // This wave's share of each step's loads: token rows (2 x 8) and expert rows (4 x 8)
+  // of its quarter; lane l takes row base + l/8, piece (l%8) ^ swz(row).
+  const uint16_t* src[kRouterOps];
+  int dst[kRouterOps];
 #pragma unroll
-    for (int b = 0; b < kRouterBatch; ++b) {
-      const int st = min(s0 + b, s_end - 1);  // steps past the quarter's end are loaded but not used
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        av[b][q] = xa[st * 8 + q];
-        bv[b][q] = rb[st * 8 + q];
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kRouterBatch; ++b) {
-      if (s0 + b < s_end) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[b][q]),
-                                                        __builtin_bit_cast(bf16x8_t, bv[b][q]), acc, 0, 0, 0);
-      }
-    }
+  for (int j = 0; j < kRouterOps; ++j) {
+    const bool tok = j < 2;
+    const int blk = tok ? eh * 2 + j : eh * 4 + (j - 2);
+    const int r = blk * 8 + (lane >> 3);
+    const int piece = (lane & 7) ^ router_swz(r);
+    src[j] = tok ? X + min<int64_t>(t0 + r, T - 1) * H + piece * 8
+                 : router + (int64_t)min(eb + r, E - 1) * H + piece * 8;
+    dst[j] = kq * kRouterQuarterBytes + (tok ? 0 : 32 * 128) + blk * 1024;
   }
-  if (kq > 0) s_part[kq - 1][eh][lane] = acc;
+  auto stage = [&](int st) -> uint8_t* { return st == 0 ? s_st0 : st == 1 ? s_st1 : s_st2; };
+  // Steps past the quarter's end load the quarter's (or the matrix's) last step again
+  // and are not computed: every wave issues the same loads per iteration.
+  auto issue = [&](int i, int st) {
+    const int s = min(q_first + min(i, per_q - 1), steps - 1);
+#pragma unroll
+    for (int j = 0; j < kRouterOps; ++j)
+      __builtin_amdgcn_global_load_lds(src[j] + s * 64, stage(st) + dst[j], 16, 0, 0);
+  };
+
+  const int m = lane & 31, h = lane >> 5;
+  const int a_row = m, b_row = 32 + eh * 32 + m;  // rows inside the quarter's region
+  f32x16_t acc = {};
+  // kGuard: some quarter has fewer steps than the others (H / 64 not a multiple of 4),
+  // so a wave checks each step before computing it
+  auto step = [&](int i, auto st_c, auto guard_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(st_c)::value;
+    constexpr bool kGuard = decltype(guard_c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kRouterOps * (kRouterStages - 2)));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(i + kRouterStages - 1, (st + kRouterStages - 1) % kRouterStages);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* base = stage(st) + kq * kRouterQuarterBytes;
+    uint4 av[4], bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = 2 * q + h;  // the 8 columns 8c..8c+7 of the step
+      av[q] = *reinterpret_cast<const uint4*>(base + a_row * 128 + ((c ^ router_swz(a_row)) << 4));
+      bv[q] = *reinterpret_cast<const uint4*>(base + b_row * 128 + ((c ^ router_swz(b_row)) << 4));
+    }
+    // all eight reads go out before the first MFMA waits (left alone, the scheduler
+    // pairs each MFMA with its two reads and waits four times)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      asm volatile("" : "+v"(av[q].x), "+v"(av[q].y), "+v"(av[q].z), "+v"(av[q].w), "+v"(bv[q].x), "+v"(bv[q].y),
+                   "+v"(bv[q].z), "+v"(bv[q].w));
+    if (!kGuard || q_first + i < steps) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[q]),
+                                                      __builtin_bit_cast(bf16x8_t, bv[q]), acc, 0, 0, 0);
+    }
+  };
+  auto run = [&](auto guard_c) __attribute__((always_inline)) {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    int i = 0;
+    for (; i + kRouterStages <= per_q; i += kRouterStages) {
+      step(i, S0{}, guard_c);
+      step(i + 1, S1{}, guard_c);
+      step(i + 2, S2{}, guard_c);
+    }
+    if (i < per_q) step(i, S0{}, guard_c);
+    if (i + 1 < per_q) step(i + 1, S1{}, guard_c);
+  };
+  issue(0, 0);
+  issue(1, 1);
+  if (4 * per_q == steps)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
+  // the repeated loads of the last steps are still landing in the stages
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16_t* s_part = reinterpret_cast<f32x16_t*>(s_st0);  // [3][2][64], the stages are idle now
+  if (kq > 0) s_part[((kq - 1) * 2 + eh) * kWave + lane] = acc;
   __syncthreads();
   if (kq > 0) return;
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const f32x16_t o = s_part[j][eh][lane];
+    const f32x16_t o = s_part[(j * 2 + eh) * kWave + lane];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += o[i];
+    for (int k = 0; k < 16; ++k) acc[k] += o[k];
   }
   // D layout: column (expert) = lane % 32, row (token) = 8*(i/4) + 4*(lane/32) + i%4
-  const int e = e0 + m;
+  const int e = eb + eh * 32 + m;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t t = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
-    if (t < T && e < E) logits[t * E + e] = acc[i];
+  for (int k = 0; k < 16; ++k) {
+    const int64_t t = t0 + 8 * (k >> 2) + 4 * h + (k & 3);
+    if (t < T && e < E) logits[t * E + e] = acc[k];
   }
 }
 

@@ -78,6 +78,14 @@ struct GemmParams {
   int64_t ldo;
   int vec_out;                // N and ldo multiples of 4, out aligned to 4 elements: 4-column stores
   int b_gm;                   // the 4-bit matrices' codes are read from their group-major copies
+  // K-split extra segment (SwiGLU launch): its tiles leave the table's grid region and
+  // take an appended region from main_blocks on, in which each (tile, slice) is ksplit
+  // workgroups over consecutive K group ranges, each writing its raw gate and up sums
+  // (times 2^row_exp) to part[ks][extra row][2N]; the activation preparation adds them.
+  int ksplit;                 // 1: off
+  int extra_tiles;            // ceil(extra_rows / BM)
+  int64_t main_blocks;        // workgroups of the table region
+  float* part;
 #ifdef Q4MOE_GEMM_STAMPS
   int stamp_slot;             // which of the four stamp records this launch fills
 #endif
@@ -124,18 +132,34 @@ __device__ __forceinline__ uint32_t magic_pair_f16_reg() {
   return m;
 }
 
-// s*q for the nibbles at positions j and j+4 of `word` (j = shift/4), as an fp16 pair:
-// ((word >> shift) & 0x000F000F) | 0x64006400 is (1024 + q_j, 1024 + q_{j+4}) exactly,
-// and one packed FMA with (s, s) and (-1024 s, -1024 s) leaves s*q, rounded once.
-__device__ __forceinline__ uint32_t scaled_pair(uint32_t word, int shift, f16x2_t s2, f16x2_t m2) {
-  const uint32_t p = ((word >> shift) & nibble_mask_reg()) | magic_pair_f16_reg();
+// Two fp16 64.0 in a VGPR, and the mask of bits 4-7 of each half in an SGPR.
+__device__ __forceinline__ uint32_t magic64_pair_f16_reg() {
+  uint32_t m;
+  asm("v_mov_b32 %0, 0x54005400" : "=v"(m));
+  return m;
+}
+__device__ __forceinline__ uint32_t nibble_hi_mask_reg() {
+  uint32_t m;
+  asm("s_mov_b32 %0, 0x00f000f0" : "=s"(m));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t pair_fma(uint32_t p, f16x2_t s2, f16x2_t m2) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, p), s2, m2));
 }
 
-// The 8 codes of one word as the B operand of one MFMA K-step (pair order).
-__device__ __forceinline__ uint4 codes_to_operand(uint32_t w, f16x2_t s2, f16x2_t m2) {
-  return make_uint4(scaled_pair(w, 0, s2, m2), scaled_pair(w, 4, s2, m2), scaled_pair(w, 8, s2, m2),
-                    scaled_pair(w, 12, s2, m2));
+// The 8 codes of one word as the B operand of one MFMA K-step (pair order), s*q each
+// rounded once.  A pair (q_j, q_{j+4}) is nibble j of each 16-bit half.  Nibbles 0 and
+// 2 (of w and of w >> 8) go into the low mantissa bits of 1024: (word & 0x000F000F) |
+// 0x64006400 is (1024 + q_j, 1024 + q_{j+4}) exactly, and one packed FMA with (s, s)
+// and (-1024 s, -1024 s) leaves s*q.  Nibbles 1 and 3 stay where they are, in mantissa
+// bits 4-7 of 64: 0x5400 | q << 4 is 64 + q exactly, taken with -64 s (no shift needed).
+__device__ __forceinline__ uint4 codes_to_operand(uint32_t w, f16x2_t s2, f16x2_t m2, f16x2_t m2_64) {
+  const uint32_t w8 = w >> 8;
+  return make_uint4(pair_fma((w & nibble_mask_reg()) | magic_pair_f16_reg(), s2, m2),
+                    pair_fma((w & nibble_hi_mask_reg()) | magic64_pair_f16_reg(), s2, m2_64),
+                    pair_fma((w8 & nibble_mask_reg()) | magic_pair_f16_reg(), s2, m2),
+                    pair_fma((w8 & nibble_hi_mask_reg()) | magic64_pair_f16_reg(), s2, m2_64));
 }
 
 // The same for 8-bit codes: the 8 codes of a block are bytes 0..3 of w0 and of w1, and
@@ -206,23 +230,30 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   Q4MOE_GSTAMP(0);
 #endif
   // ---- tile of this workgroup (XCD-aware: all slices of a tile share an XCD)
-  const int bid = blockIdx.x;
+  const bool split_region = (int64_t)blockIdx.x >= p.main_blocks;  // (only with ksplit > 1)
+  const int bid = split_region ? (int)(blockIdx.x - p.main_blocks) : (int)blockIdx.x;
   const int xcd = bid % kXcd;
   const int q = bid / kXcd;
   const int slice = q % p.n_slices;
-  const int tile = (q / p.n_slices) * kXcd + xcd;
+  const int q2 = q / p.n_slices;
+  const int ks = split_region ? q2 % p.ksplit : 0;
+  const int tile = (split_region ? q2 / p.ksplit : q2) * kXcd + xcd;
   int seg, rows;
   int64_t row0;
 #ifdef Q4MOE_GEMM_STAMPS
-  if (tile >= p.n_tiles) {
+  if (tile >= (split_region ? p.extra_tiles : p.n_tiles)) {
     gst[4] = __builtin_amdgcn_s_memrealtime();
     gemm_stamps_write(p, gst, ~0ull);
     return;
   }
 #else
-  if (tile >= p.n_tiles) return;
+  if (tile >= (split_region ? p.extra_tiles : p.n_tiles)) return;
 #endif
-  if (p.tiles) {
+  if (split_region) {  // extra tile `tile`: positions P + tile*BM ..
+    row0 = p.P + (int64_t)tile * BM;
+    seg = -1;
+    rows = (int)min<int64_t>(BM, p.extra_rows - (int64_t)tile * BM);
+  } else if (p.tiles) {
     const int4 ti = p.tiles[tile];
     seg = ti.x;
     row0 = ti.y;
@@ -232,7 +263,11 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     seg = row0 < p.extra_rows ? -1 : -2;
     rows = (int)min<int64_t>(BM, p.extra_rows - row0);
   }
-  if (seg == -2 || (kSel == TILES_ROUTED && seg < 0) || (kSel == TILES_EXTRA && seg >= 0)) {
+  // this workgroup's K groups
+  const int nks = split_region ? p.ksplit : 1;
+  const int g_lo = ks * p.G / nks, g_hi = (ks + 1) * p.G / nks;
+  if (seg == -2 || (kSel == TILES_ROUTED && seg < 0) || (kSel == TILES_EXTRA && seg >= 0) ||
+      (seg == -1 && p.ksplit > 1 && !split_region)) {
 #ifdef Q4MOE_GEMM_STAMPS
     gst[4] = __builtin_amdgcn_s_memrealtime();
     gemm_stamps_write(p, gst, ~0ull);
@@ -305,12 +340,12 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     asm volatile("" : "+v"(src_mb[mb]));  // read here, before the loads that refill stage 3
   }
 
-  // Issue all loads of K group g into stage `st`.  Past the last group the last group
+  // Issue all loads of K group g_lo + g into stage `st`.  Past the last group the last group
   // is loaded again (an L2 hit into a stage no step reads): every step then issues the
   // same loads and waits for the same count, with no branch for the compiler's own
   // wait placement to merge (after such a branch it waits for every load in flight).
   auto issue = [&](int g, int st, uint32_t (&sc)[2]) {
-    g = min(g, p.G - 1);
+    g = min(g_lo + g, g_hi - 1);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
       __builtin_amdgcn_global_load_lds(a_ptr[i] + g * 64, stage_a(st) + (wave * MB + i) * 1024, 16, 0, 0);
@@ -380,23 +415,25 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
 #pragma unroll
         for (int h = 0; h < kBW; ++h) rb[nb][h] = *reinterpret_cast<const uint4*>(sb + (nb * kBW + h) * 1024);
       read_a(0, af[0]);
-      f16x2_t s2[2], m2[2];
+      f16x2_t s2[2], m2[2], m64[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const float s = bf16_bits_to_f32(sc[st][nb]);
-        const _Float16 sh = (_Float16)s, mh = (_Float16)(-1024.0f * s);
+        // the fp16 scale and its exact multiples -1024 s and -64 s
+        const _Float16 sh = (_Float16)bf16_bits_to_f32(sc[st][nb]);
+        const _Float16 mh = sh * (_Float16)-1024.0f, m6 = sh * (_Float16)-64.0f;
         s2[nb] = f16x2_t{sh, sh};
         m2[nb] = f16x2_t{mh, mh};
+        m64[nb] = f16x2_t{m6, m6};
       }
       uint4 bop[2][4];  // this group's B operands, converted once, used by every row block
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if constexpr (kBits == 4) {
           const uint4 r = rb[nb][0];
-          bop[nb][0] = codes_to_operand(r.x, s2[nb], m2[nb]);
-          bop[nb][1] = codes_to_operand(r.y, s2[nb], m2[nb]);
-          bop[nb][2] = codes_to_operand(r.z, s2[nb], m2[nb]);
-          bop[nb][3] = codes_to_operand(r.w, s2[nb], m2[nb]);
+          bop[nb][0] = codes_to_operand(r.x, s2[nb], m2[nb], m64[nb]);
+          bop[nb][1] = codes_to_operand(r.y, s2[nb], m2[nb], m64[nb]);
+          bop[nb][2] = codes_to_operand(r.z, s2[nb], m2[nb], m64[nb]);
+          bop[nb][3] = codes_to_operand(r.w, s2[nb], m2[nb], m64[nb]);
         } else {  // 8 codes per word pair
           bop[nb][0] = codes8_to_operand(rb[nb][0].x, rb[nb][0].y, s2[nb], m2[nb]);
           bop[nb][1] = codes8_to_operand(rb[nb][0].z, rb[nb][0].w, s2[nb], m2[nb]);
@@ -417,16 +454,17 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
       }
     };
     int g0 = 0;
-    for (; g0 + kStages <= p.G; g0 += kStages) {
+    const int ng = g_hi - g_lo;
+    for (; g0 + kStages <= ng; g0 += kStages) {
       step(g0, std::integral_constant<int, 0>{});
       step(g0 + 1, std::integral_constant<int, 1>{});
       step(g0 + 2, std::integral_constant<int, 2>{});
       step(g0 + 3, std::integral_constant<int, 3>{});
     }
     // the last G mod 4 groups
-    if (g0 < p.G) step(g0, std::integral_constant<int, 0>{});
-    if (g0 + 1 < p.G) step(g0 + 1, std::integral_constant<int, 1>{});
-    if (g0 + 2 < p.G) step(g0 + 2, std::integral_constant<int, 2>{});
+    if (g0 < ng) step(g0, std::integral_constant<int, 0>{});
+    if (g0 + 1 < ng) step(g0 + 1, std::integral_constant<int, 1>{});
+    if (g0 + 2 < ng) step(g0 + 2, std::integral_constant<int, 2>{});
   };
   if (mblocks == 1)
     main_loop(std::integral_constant<int, 1>{});
@@ -494,7 +532,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     }
   };
 
-  {
+  if (ks == 0) {  // (a K-split tile's bias term, over all groups, goes with its first range)
     const int nt = (p.Gp + 15) / 16;
     CorrLoads cur, nxt;
     corr_load(0, cur);
@@ -511,7 +549,24 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   __syncthreads();
 
   // ---- epilogue.  D layout: column = lane % 32, row = 8*(i/4) + 4*(lane/32) + i%4.
-  if (p.vec_out) {
+  if (split_region) {
+    // raw gate and up sums of this K range (exact power-of-two factor), 32 consecutive
+    // columns per store instruction
+    float* part = p.part + (int64_t)ks * p.extra_rows * 2 * p.N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb >= mblocks) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = mb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (r >= rows || col[0] >= p.N) continue;
+        const float f = s_wgt[r];
+        float* o = part + (row0 - p.P + r) * 2 * p.N + col[0];
+        o[0] = f * acc[mb][0][i];
+        o[p.N] = f * acc[mb][1][i];
+      }
+    }
+  } else if (p.vec_out) {
     // Through LDS, 16 tile rows at a time (registers i = 8h .. 8h+7 of row block mb), in
     // stages 1 and 2 alternately, so that each thread stores whole 4-column chunks and a
     // wave's stores cover contiguous row segments: 4 (SwiGLU: 2) 16-byte stores per thread
@@ -620,6 +675,15 @@ __device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Rows whose values come from K-split partial sums: row r >= from is silu(g) * u with
+// g = sum_k part[k*stride + (r-from)*2K + j] and u the same at + K (k in order).
+struct SplitRows {
+  const float* part;
+  int64_t from;    // no such rows: INT64_MAX
+  int64_t stride;  // floats between ranges
+  int ks;
+};
+
 // fp16 copy of rows for the MFMA A operand, one wave per row.  The row's largest
 // magnitude M picks e with M * 2^-e in [256, 512) (e = 0 for an all-zero row); the
 // row is written as fp16(x * 2^-e) with each 8-element block in the pair order
@@ -628,18 +692,49 @@ __device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
 // the groups padded with zeros to Gp.
 template <typename In>
 __global__ void prep_rows_kernel(const In* __restrict__ A, int64_t rows, int K, int Gp, uint16_t* __restrict__ out,
-                                 uint16_t* __restrict__ sums, int32_t* __restrict__ exps) {
+                                 uint16_t* __restrict__ sums, int32_t* __restrict__ exps, SplitRows sp) {
   const int lane = lane_id();
   const int nblk = K >> 3, G = K >> 6;
   const int64_t wstride = (int64_t)gridDim.x * (blockDim.x / kWave);
   for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; r < rows; r += wstride) {
     const In* row = A + r * K;
-    uint32_t mx = 0;  // largest |x| as float bits (non-negative floats order as integers)
-    for (int b = lane; b < nblk; b += kWave) {
-      float v[8];
-      load8(row + b * 8, v);
+    // rows from sp.from on: the SwiGLU of K-split gate and up sums, added in range order
+    const float* prow = r >= sp.from ? sp.part + (r - sp.from) * 2 * K : nullptr;
+    auto load = [&](int b, float (&v)[8]) __attribute__((always_inline)) {
+      if (prow) {
+        float g[8], u[8], t[8];
+        load8(prow + b * 8, g);
+        load8(prow + K + b * 8, u);
+        for (int k = 1; k < sp.ks; ++k) {
+          load8(prow + k * sp.stride + b * 8, t);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mx = max(mx, __float_as_uint(fabsf(v[j])));
+          for (int j = 0; j < 8; ++j) g[j] += t[j];
+          load8(prow + k * sp.stride + K + b * 8, t);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) u[j] += t[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = silu(g[j]) * u[j];
+      } else {
+        load8(row + b * 8, v);
+      }
+    };
+    // A row of at most 64 blocks is read once and kept in registers; a longer one is
+    // read again for the conversion.
+    const bool one = nblk <= kWave;
+    float vk[8] = {};
+    uint32_t mx = 0;  // largest |x| as float bits (non-negative floats order as integers)
+    if (one) {
+      if (lane < nblk) load(lane, vk);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, __float_as_uint(fabsf(vk[j])));
+    } else {
+      for (int b = lane; b < nblk; b += kWave) {
+        float v[8];
+        load(b, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = max(mx, __float_as_uint(fabsf(v[j])));
+      }
     }
     mx = wave_max_u32(mx);
     const float m = __uint_as_float(mx);
@@ -656,7 +751,12 @@ __global__ void prep_rows_kernel(const In* __restrict__ A, int64_t rows, int K, 
       float gs = 0.0f;
       if (b < nblk) {
         float v[8];
-        load8(row + b * 8, v);
+        if (one) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = vk[j];
+        } else {
+          load(b, v);
+        }
         _Float16 h[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -758,7 +858,11 @@ hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream, 
     if (m->scales && (!aligned16(m->scales) || !aligned16(m->biases))) p.bs_vec = 0;
   p.n_tiles = (int)max_tiles;
   const int64_t tiles_rounded = (max_tiles + kXcd - 1) / kXcd * kXcd;
-  const int64_t blocks = tiles_rounded * p.n_slices;
+  if (p.ksplit < 1) p.ksplit = 1;
+  p.main_blocks = tiles_rounded * p.n_slices;
+  p.extra_tiles = (int)((p.extra_rows + BM - 1) / BM);
+  const int64_t blocks =
+      p.main_blocks + (p.ksplit > 1 ? (int64_t)(p.extra_tiles + kXcd - 1) / kXcd * kXcd * p.n_slices * p.ksplit : 0);
   if (!extra_q8) {
     hipLaunchKernelGGL(grouped_q4_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {
@@ -771,12 +875,12 @@ hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream, 
 // fp16 pair-order copy, row exponents and group-sum parts of `rows` rows of length K.
 template <typename In>
 hipError_t launch_prep_rows(const In* A, int64_t rows, int K, uint16_t* out, uint16_t* sums, int32_t* exps,
-                            hipStream_t stream) {
+                            hipStream_t stream, SplitRows sp = SplitRows{nullptr, INT64_MAX, 0, 1}) {
   if (rows == 0) return hipSuccess;
   const int Gp = pad16(K >> 6);
   const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 8192);
   hipLaunchKernelGGL(prep_rows_kernel<In>, dim3((unsigned)blocks), dim3(256), 0, stream, A, rows, K, Gp, out, sums,
-                     exps);
+                     exps, sp);
   return hipGetLastError();
 }
 
@@ -846,6 +950,13 @@ hipError_t run_q4_gemm(const Q4Mat& W, int64_t n, int k, const uint16_t* X, int6
 }
 
 namespace {
+// The shared expert's gate/up tiles (all T rows, the last of the launch) are split in K
+// this many ways, so that the launch's last partial round of workgroups is short.
+#ifndef Q4MOE_SHARED_KSPLIT
+#define Q4MOE_SHARED_KSPLIT 2
+#endif
+constexpr int kSharedKSplit = Q4MOE_SHARED_KSPLIT;
+
 struct PrefillWs {
   float* logits;
   int32_t* ids;
@@ -866,6 +977,7 @@ struct PrefillWs {
   int32_t* xe_act;  // [R]
   float* ys;        // [R][H] per-position outputs, weighted
   float* sh_gate;   // [T] shared-expert weight per token (with a shared-expert gate)
+  float* part;      // [kSharedKSplit][T][2I] K-split gate and up sums of the 4-bit shared expert
   size_t total;
 };
 
@@ -895,6 +1007,7 @@ PrefillWs carve(void* base, int64_t T, int H, int I, int E, int k, int has_share
   w.xe_act = reinterpret_cast<int32_t*>(take((size_t)R * 4));
   w.ys = reinterpret_cast<float*>(take((size_t)R * H * 4));
   w.sh_gate = reinterpret_cast<float*>(take((size_t)T * 4));
+  w.part = reinterpret_cast<float*>(take(has_shared ? (size_t)kSharedKSplit * T * 2 * I * 4 : 0));
   w.total = off;
   return w;
 }
@@ -954,6 +1067,10 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   p.out_bf16 = 0;
   p.ldo = I;
   const bool sh_q8 = L.has_shared && L.sh_q8;
+  // the 4-bit shared expert's tiles split in K (the 8-bit one runs in a launch of its own)
+  const int ksplit = L.has_shared && !sh_q8 ? std::min(kSharedKSplit, p.G) : 1;
+  p.ksplit = ksplit;
+  p.part = w.part;
   // group-major codes when every 4-bit matrix of the launch has them (an 8-bit shared
   // expert runs in a launch of its own that reads its row-major codes)
   auto gm = [](const Q4Mat& a, const Q4Mat& b) { return a.codes_gm && b.codes_gm; };
@@ -962,11 +1079,14 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   if (e != hipSuccess) return e;
 
   const int64_t R = P + extra;
-  e = launch_prep_rows(w.act32, R, I, w.act, w.xs_act, w.xe_act, stream);
+  const SplitRows sp = ksplit > 1 ? SplitRows{w.part, P, T * 2 * I, ksplit} : SplitRows{nullptr, INT64_MAX, 0, 1};
+  e = launch_prep_rows(w.act32, R, I, w.act, w.xs_act, w.xe_act, stream, sp);
   if (e != hipSuccess) return e;
 
   // down with the routing weight -> ys (fp32, sorted positions)
   GemmParams d = p;
+  d.ksplit = 1;
+  d.part = nullptr;
   d.A = w.act;
   d.xs = w.xs_act;
   d.row_exp = w.xe_act;

@@ -9,7 +9,8 @@
 // The B operand of the main product is s*q in fp16, made by one packed FMA per
 // code pair: (1024 + q) is an fp16 whose mantissa holds q (bits 0x6400 | q), and
 // fma(1024 + q, s, -1024 s) = s*q rounded once (s*q has at most 12 significant
-// bits, so the rounding is at most 2^-12 relative and often absent).  The
+// bits, so the rounding is at most 2^-12 relative and often absent); a nibble that
+// sits in bits 4-7 is used in place as 64 + q (bits 0x5400 | q << 4) with -64 s.  The
 // accumulators then run over the whole K range with no VALU work between the
 // matrix instructions.  The bias term is a small product over the group index
 // (biases in fp16 are exact; the row sums are split into two fp16 parts) fed to
@@ -96,7 +97,8 @@ struct GemmParams {
 // 100 MHz s_memrealtime counter at entry, once its tile's row indices are known, after
 // the main loop, after the bias term and at the end, then the hardware ids it ran on
 // (XCC id << 32 | HW_ID) and its work item (tile | slice << 20 | active row blocks << 28;
-// all ones for a workgroup without a tile), into record stamp_slot of the array.
+// all ones for a workgroup without a tile; bit 32 marks a K-split workgroup, bits 33..
+// its K range), into record stamp_slot of the array.
 #ifdef Q4MOE_GEMM_STAMPS
 constexpr int kGemmStampBlocks = 4096;
 __device__ unsigned long long g_gemm_stamps[4][kGemmStampBlocks][8];
@@ -646,7 +648,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
 #ifdef Q4MOE_GEMM_STAMPS
   gst[4] = __builtin_amdgcn_s_memrealtime();
   gemm_stamps_write(p, gst, (unsigned long long)tile | (unsigned long long)slice << 20 |
-                                (unsigned long long)mblocks << 28);
+                                (unsigned long long)mblocks << 28 | (unsigned long long)split_region << 32 |
+                                (unsigned long long)ks << 33);
 #endif
 }
 

@@ -175,14 +175,15 @@ def gemm_summary(name, rec):
     lines = [f"## {name}", "", f"workgroups launched: {len(used)}, with a tile: {int(live.sum())}; "
              f"span from the first start to the last end: {span} ns", ""]
     mb = (item[live] >> np.uint64(28)).astype(np.int64) & 0xF
+    split = (item[live] >> np.uint64(32)).astype(np.int64) & 1  # a K-split workgroup (shared-expert tile)
     lines += ["| active row blocks | workgroups | entry -> rows known | main loop | bias term | epilogue | "
               "whole workgroup (p10 / median / p90) |", "|---|---|---|---|---|---|---|"]
     L = {k: v[live] for k, v in dict(start=start, known=known, main=main, bias=bias, end=end).items()}
-    for m in sorted(set(mb.tolist())):
-        sel = mb == m
+    for sp, m in sorted(set(zip(split.tolist(), mb.tolist()))):
+        sel = (mb == m) & (split == sp)
         d = L["end"][sel] - L["start"][sel]
         med = lambda a: int(np.median(a))  # noqa: E731
-        lines.append(f"| {m} | {int(sel.sum())} | {med(L['known'][sel] - L['start'][sel])} | "
+        lines.append(f"| {m}{' (K-split)' if sp else ''} | {int(sel.sum())} | {med(L['known'][sel] - L['start'][sel])} | "
                      f"{med(L['main'][sel] - L['known'][sel])} | {med(L['bias'][sel] - L['main'][sel])} | "
                      f"{med(L['end'][sel] - L['bias'][sel])} | {int(np.percentile(d, 10))} / {med(d)} / "
                      f"{int(np.percentile(d, 90))} |")
@@ -199,7 +200,7 @@ def gemm_summary(name, rec):
     hw = rec[used, 5]
     xcc = (hw >> np.uint64(32)).astype(np.int64) & 0xF
     lines += [f"workgroups on XCC blockIdx % 8: {int((xcc == used % 8).sum())} of {len(used)}"]
-    tile = (item[live] & np.uint64(0xFFFFF)).astype(np.int64)
+    tile = (item[live] & np.uint64(0xFFFFF)).astype(np.int64) + (split << 24)  # split tiles number on their own
     xl = xcc[live]
     same, spread = 0, []
     for t in np.unique(tile):

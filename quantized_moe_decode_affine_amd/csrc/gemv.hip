@@ -11,6 +11,8 @@
 // computes.  Activations are staged once per workgroup in LDS as permuted
 // bfloat16 pairs; the group products run on v_dot2 with exact 128+q
 // dequantization (common.h), the row sums are DPP/permlane reductions.
+#include <mutex>
+
 #include "kernels.h"
 #include "vecstage.h"
 
@@ -839,10 +841,15 @@ namespace {
 template <int B>
 constexpr int lmhead_rows_per_lane() { return B <= 2 ? Q4MOE_LMHEAD_ROWS_B1 : B <= 4 ? 2 : 1; }
 
+// Workgroups of the head resident per CU at `lds` bytes of LDS each (the activations'
+// size grows with k): kept for the last LDS size asked about, asked again when it changes.
 template <int B, bool kQ8 = false>
 int lmhead_mfma_resident(size_t lds) {
+  static std::mutex mu;
+  static size_t cached_lds = 0;
   static int cached = -1;
-  if (cached < 0) {
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached < 0 || cached_lds != lds) {
     int n = 0;
     hipError_t e;
     if constexpr (kQ8)
@@ -852,6 +859,7 @@ int lmhead_mfma_resident(size_t lds) {
     if (e != hipSuccess || n < 1)
       n = 1;
     cached = n;
+    cached_lds = lds;
   }
   return cached;
 }

@@ -21,7 +21,6 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // a row per lane would touch 32 lines per instruction), and three steps are in flight.
 // Inside a row the eight 16-byte pieces are XOR-rotated by row bits 1-3, so that the
 // MFMA operand reads (a row per lane) spread over all banks.
-constexpr int kRouterBatch = 4;  // the 8-bit router's groups loaded per batch
 constexpr int kRouterStages = 3;
 constexpr int kRouterQuarterBytes = (32 + 64) * 128;  // one quarter's token and expert rows of a step
 constexpr int kRouterOps = 6;                         // load instructions per wave and step
@@ -300,11 +299,13 @@ int grid_for(int64_t n, int block) {
 
 // Router logits from an 8-bit affine router on bf16 matrix cores: the tiling of
 // router_logits_kernel (32 tokens x 64 experts, 8 waves = 2 expert halves x 4 K
-// quarters), whose 64-column K steps are exactly the quantization groups.  Codes
-// 0..255 are exact in bfloat16 (the high half of their fp32 value), so each group's
-// sum(x q) comes exact-product, fp32-summed from 4 MFMAs into a fresh accumulator,
-// and is folded as acc += scale * sum(x q) + bias * sum(x); the tile's per-group
-// token sums sum(x) are computed first into LDS ([group][token], dynamic).
+// quarters, operands of each step staged through LDS), whose 64-column K steps are
+// exactly the quantization groups.  Codes 0..255 are exact in bfloat16 (the high half
+// of their fp32 value), so each group's sum(x q) comes exact-product, fp32-summed from
+// 4 MFMAs into a fresh accumulator; 4 more against all-ones codes give the group's
+// token sums sum(x) in the same layout, and the group is folded as
+// acc += scale * sum(x q) + bias * sum(x).  A code row's 64 bytes of a group are four
+// 16-byte pieces, XOR-rotated by row bits 2-3.
 __device__ __forceinline__ bf16x8_t bytes_to_bf16x8(uint2 c) {
   uint32_t o[4];
 #pragma unroll
@@ -318,90 +319,155 @@ __device__ __forceinline__ bf16x8_t bytes_to_bf16x8(uint2 c) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
+constexpr int kQ8RouterQuarterBytes = 32 * 128;  // a quarter's token rows (128 B each) of a step; its code rows
+                                                 // (64 B each) sit in arrays of their own
+constexpr int kQ8RouterOps = 6;  // per wave and step: 2 token-row and 2 code-row loads, the scale and the bias
+
+__device__ __forceinline__ int code_swz(int r) { return (r >> 2) & 3; }
+
 __global__ __launch_bounds__(512) void q8_router_logits_kernel(Q4Mat R, const uint16_t* __restrict__ X, int64_t T,
                                                                int E, int H, float* __restrict__ logits) {
-  extern __shared__ __align__(16) float s_xsum[];  // [G][32]
-  __shared__ f32x16_t s_part[3][2][kWave];
+  __shared__ __align__(16) uint8_t s_st0[4 * kQ8RouterQuarterBytes], s_st1[4 * kQ8RouterQuarterBytes],
+      s_st2[4 * kQ8RouterQuarterBytes];
+  __shared__ __align__(16) uint8_t s_cd0[4 * 64 * 64], s_cd1[4 * 64 * 64], s_cd2[4 * 64 * 64];
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int eh = wave & 1, kq = wave >> 1;
   const int64_t t0 = (int64_t)blockIdx.x * 32;
-  const int e0 = blockIdx.y * 64 + eh * 32;
+  const int eb = blockIdx.y * 64;
   const int G = H >> 6;
-  // token sums of each group (fixed order)
-  for (int pidx = threadIdx.x; pidx < 32 * G; pidx += blockDim.x) {
-    const int tl = pidx & 31, g = pidx >> 5;
-    const uint4* xr = reinterpret_cast<const uint4*>(X + min<int64_t>(t0 + tl, T - 1) * H) + 8 * g;
-    float sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 v = xr[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sum += bf16_bits_to_f32(w[j] & 0xFFFFu) + bf16_bits_to_f32(w[j] >> 16);
-    }
-    s_xsum[g * 32 + tl] = sum;
-  }
-  __syncthreads();
+  const int per_q = (G + 3) >> 2;
+  const int q_first = kq * per_q;
   const int m = lane & 31, h = lane >> 5;
-  const int64_t trow = min<int64_t>(t0 + m, T - 1);
-  const int erow = min(e0 + m, E - 1);
-  const uint4* xa = reinterpret_cast<const uint4*>(X + trow * H) + 4 * h;
-  const uint2* cb = reinterpret_cast<const uint2*>(R.codes) + (int64_t)erow * (H >> 3) + 4 * h;
+  const int erow = min(eb + eh * 32 + m, E - 1);  // this lane's expert (its output column)
+
+  // loads of this wave: token rows (eh*2 + j)*8 + lane/8, piece (lane%8)^swz; code rows
+  // (eh*2 + j)*16 + lane/4, piece (lane%4)^swz
+  const uint16_t* xsrc[2];
+  const uint8_t* csrc[2];
+  int xdst[2], cdst[2];
+  const uint8_t* codes = reinterpret_cast<const uint8_t*>(R.codes);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int xb = eh * 2 + j, xr = xb * 8 + (lane >> 3);
+    xsrc[j] = X + min<int64_t>(t0 + xr, T - 1) * H + ((lane & 7) ^ router_swz(xr)) * 8;
+    xdst[j] = kq * kQ8RouterQuarterBytes + xb * 1024;
+    const int cb = eh * 2 + j, cr = cb * 16 + (lane >> 2);
+    csrc[j] = codes + (int64_t)min(eb + cr, E - 1) * H + ((lane & 3) ^ code_swz(cr)) * 16;
+    cdst[j] = kq * 64 * 64 + cb * 1024;
+  }
   const uint16_t* sc = R.scales + (int64_t)erow * G;
   const uint16_t* bi = R.biases + (int64_t)erow * G;
-  const int s_begin = kq * G / 4, s_end = (kq + 1) * G / 4;
-  f32x16_t acc = {};
-  for (int s0 = s_begin; s0 < s_end; s0 += kRouterBatch) {
-    uint4 av[kRouterBatch][4];
-    uint2 bv[kRouterBatch][4];
-    uint32_t sb[kRouterBatch], bb[kRouterBatch];
+  auto stage = [&](int st) -> uint8_t* { return st == 0 ? s_st0 : st == 1 ? s_st1 : s_st2; };
+  auto cstage = [&](int st) -> uint8_t* { return st == 0 ? s_cd0 : st == 1 ? s_cd1 : s_cd2; };
+  uint32_t scv[kRouterStages], biv[kRouterStages];  // raw bf16 scale and bias of the group in each stage
+  // ga: the step's load addresses, returned so that the caller can keep them live past
+  // its LDS reads (the compiler waits for every load in flight before it reuses a load's
+  // address registers, e.g. as an LDS read's destination)
+  auto issue = [&](int i, int st, uintptr_t (&ga)[6]) {
+    const int g = min(q_first + min(i, per_q - 1), G - 1);
+    ga[4] = reinterpret_cast<uintptr_t>(sc + g);
+    ga[5] = reinterpret_cast<uintptr_t>(bi + g);
+    scv[st] = *reinterpret_cast<const uint16_t*>(ga[4]);
+    biv[st] = *reinterpret_cast<const uint16_t*>(ga[5]);
 #pragma unroll
-    for (int b = 0; b < kRouterBatch; ++b) {
-      const int g = min(s0 + b, s_end - 1);  // groups past the quarter's end are loaded but not used
+    for (int j = 0; j < 2; ++j) {
+      ga[2 * j] = reinterpret_cast<uintptr_t>(xsrc[j] + g * 64);
+      ga[2 * j + 1] = reinterpret_cast<uintptr_t>(csrc[j] + g * 64);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ga[2 * j]), stage(st) + xdst[j], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ga[2 * j + 1]), cstage(st) + cdst[j], 16, 0, 0);
+    }
+  };
+
+  const int a_row = m, b_row = eh * 32 + m;
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0 pairs
+  f32x16_t acc = {};
+  auto step = [&](int i, auto st_c, auto guard_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(st_c)::value;
+    constexpr bool kGuard = decltype(guard_c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kQ8RouterOps * (kRouterStages - 2)));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    uintptr_t ga[6];
+    issue(i + kRouterStages - 1, (st + kRouterStages - 1) % kRouterStages, ga);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* xb = stage(st) + kq * kQ8RouterQuarterBytes;
+    const uint8_t* cbp = cstage(st) + kq * 64 * 64;
+    uint4 av[4];
+    uint2 bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = 2 * q + h;  // columns 8c..8c+7 of the group
+      av[q] = *reinterpret_cast<const uint4*>(xb + a_row * 128 + ((c ^ router_swz(a_row)) << 4));
+      const uint4 cw = *reinterpret_cast<const uint4*>(cbp + b_row * 64 + ((q ^ code_swz(b_row)) << 4));
+      bv[q] = h ? make_uint2(cw.z, cw.w) : make_uint2(cw.x, cw.y);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      asm volatile("" : "+v"(av[q].x), "+v"(av[q].y), "+v"(av[q].z), "+v"(av[q].w), "+v"(bv[q].x), "+v"(bv[q].y));
+#pragma unroll
+    for (int j = 0; j < 6; ++j) asm volatile("" ::"v"(ga[j]));
+    if (!kGuard || q_first + i < G) {
+      f32x16_t pq = {}, px = {};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        av[b][q] = xa[g * 8 + q];
-        bv[b][q] = cb[g * 8 + q];
+        pq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[q]), bytes_to_bf16x8(bv[q]), pq,
+                                                     0, 0, 0);
+        px = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[q]),
+                                                     __builtin_bit_cast(bf16x8_t, ones), px, 0, 0, 0);
       }
-      sb[b] = sc[g];
-      bb[b] = bi[g];
+      const float s = bf16_bits_to_f32(scv[st]), o = bf16_bits_to_f32(biv[st]);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc[k] += fmaf(s, pq[k], o * px[k]);
     }
-#pragma unroll
-    for (int b = 0; b < kRouterBatch; ++b) {
-      const int g = s0 + b;
-      if (g < s_end) {
-        f32x16_t pq = {};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          pq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[b][q]),
-                                                       bytes_to_bf16x8(bv[b][q]), pq, 0, 0, 0);
-        const float s = bf16_bits_to_f32(sb[b]), o = bf16_bits_to_f32(bb[b]);
-        // D layout: column (expert) = lane % 32, row (token) = 8*(i/4) + 4*(lane/32) + i%4
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 xs = *reinterpret_cast<const float4*>(s_xsum + g * 32 + 8 * r4 + 4 * h);
-          const float xv[4] = {xs.x, xs.y, xs.z, xs.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[4 * r4 + i] += fmaf(s, pq[4 * r4 + i], o * xv[i]);
-        }
-      }
+  };
+  auto run = [&](auto guard_c) __attribute__((always_inline)) {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    int i = 0;
+    for (; i + kRouterStages <= per_q; i += kRouterStages) {
+      step(i, S0{}, guard_c);
+      step(i + 1, S1{}, guard_c);
+      step(i + 2, S2{}, guard_c);
     }
+    if (i < per_q) step(i, S0{}, guard_c);
+    if (i + 1 < per_q) step(i + 1, S1{}, guard_c);
+  };
+  {
+    uintptr_t ga[6];
+    issue(0, 0, ga);
+    issue(1, 1, ga);
   }
-  if (kq > 0) s_part[kq - 1][eh][lane] = acc;
+  if (4 * per_q == G)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
+  __builtin_amdgcn_s_waitcnt(0);  // the repeated loads of the last steps are still landing
+  __syncthreads();
+
+  // quarters 1..3 hand their sums to quarter 0 through the idle stages ([2][64] each:
+  // quarters 1 and 2 in stage 0, quarter 3 in stage 1)
+  auto s_part = [&](int j) -> f32x16_t* {
+    return j < 2 ? reinterpret_cast<f32x16_t*>(s_st0) + j * 2 * kWave : reinterpret_cast<f32x16_t*>(s_st1);
+  };
+  static_assert(4 * kQ8RouterQuarterBytes >= 2 * 2 * kWave * 64, "two quarters' sums fit a stage");
+  if (kq > 0) s_part(kq - 1)[eh * kWave + lane] = acc;
   __syncthreads();
   if (kq > 0) return;
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const f32x16_t o = s_part[j][eh][lane];
+    const f32x16_t o = s_part(j)[eh * kWave + lane];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += o[i];
+    for (int k = 0; k < 16; ++k) acc[k] += o[k];
   }
-  const int e = e0 + m;
+  // D layout: column (expert) = lane % 32, row (token) = 8*(i/4) + 4*(lane/32) + i%4
+  const int e = eb + eh * 32 + m;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t t = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
-    if (t < T && e < E) logits[t * E + e] = acc[i];
+  for (int k = 0; k < 16; ++k) {
+    const int64_t t = t0 + 8 * (k >> 2) + 4 * h + (k & 3);
+    if (t < T && e < E) logits[t * E + e] = acc[k];
   }
 }
 
@@ -414,7 +480,7 @@ hipError_t run_route_topk(const uint16_t* router, int E, int H, const uint16_t* 
   float* logits = static_cast<float*>(ws);
   dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 63) / 64));
   if (router_q8 && router_q8->codes)
-    hipLaunchKernelGGL(q8_router_logits_kernel, grid, dim3(512), (size_t)(H >> 6) * 32 * 4, stream, *router_q8, X, T,
+    hipLaunchKernelGGL(q8_router_logits_kernel, grid, dim3(512), 0, stream, *router_q8, X, T,
                        E, H, logits);
   else
     hipLaunchKernelGGL(router_logits_kernel, grid, dim3(512), 0, stream, router, X, T, E, H, logits);

@@ -161,10 +161,10 @@ def test_lmhead_workspace_reuse(B):
 
 
 def test_lmhead_full_vocab(B):
-    """LM-head shape 151,936 x 2048, batch 1 and 4."""
+    """LM-head shape 151,936 x 2048, batch 1, 4 and 8 (8 x 2048: the largest activation block)."""
     mat = synth.lm_head()
     W = _q4(B, mat)
-    for batch in (1, 4):
+    for batch in (1, 4, 8):
         say(f"lmhead full vocab B={batch}")
         X = synth.token_rows(4, batch, synth.HIDDEN, index=batch)
         ids, mx = B.lmhead_argmax(W, B.bf16_tensor(X))
@@ -531,10 +531,10 @@ def test_q8_lmhead_planted_ties(B):
 
 
 def test_q8_lmhead_full_vocab(B):
-    """8-bit LM head of the q4-xl kind, 151,936 x 2048, batch 1 and 4."""
+    """8-bit LM head of the q4-xl kind, 151,936 x 2048, batch 1, 4 and 8."""
     mat = synth.lm_head(bits=8)
     W = _q4(B, mat)
-    for batch in (1, 4):
+    for batch in (1, 4, 8):
         say(f"q8 lmhead full vocab B={batch}")
         X = synth.token_rows(4, batch, synth.HIDDEN, index=batch)
         ids, mx = B.lmhead_argmax(W, B.bf16_tensor(X))

@@ -260,8 +260,10 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
  * for down with the routing weight, then combine back in token order.  Row t
  * of Y equals moe_ffn_decode on X[t] up to rounding; the SwiGLU output is
  * computed in fp32 and rounded once to fp16 (after an exact power-of-two row
- * scaling) before the down GEMM.  Y fp32 or bf16 [T][hidden].  Needs
- * Q4MOE_OP_FFN_PREFILL workspace (T).
+ * scaling) before the down GEMM.  The GEMMs read the experts' group-major
+ * codes when every 4-bit expert matrix of the layer (routed and shared) carries
+ * them (q4moe_matrix.codes_gm; the results are the same bits either way).
+ * Y fp32 or bf16 [T][hidden].  Needs Q4MOE_OP_FFN_PREFILL workspace (T).
  */
 int moe_ffn_prefill(const q4moe_layer* layer, const q4moe_bf16* X, int64_t T, void* Y,
                     int out_dtype, void* workspace, size_t workspace_bytes, q4moe_stream stream);

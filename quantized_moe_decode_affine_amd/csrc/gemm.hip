@@ -79,6 +79,10 @@ struct GemmParams {
   int64_t ldo;
   int vec_out;                // N and ldo multiples of 4, out aligned to 4 elements: 4-column stores
   int b_gm;                   // the 4-bit matrices' codes are read from their group-major copies
+  // store/scale with vec_out: when set, out holds fp16 values scaled by 2^-e, with one e
+  // per four consecutive columns of a row in out_exp[row][ldo/4] (the four values' largest
+  // magnitude lands in [2^14, 2^15))
+  int8_t* out_exp;
   // K-split extra segment (SwiGLU launch): its tiles leave the table's grid region and
   // take an appended region from main_blocks on, in which each (tile, slice) is ksplit
   // workgroups over consecutive K group ranges, each writing its raw gate and up sums
@@ -599,13 +603,27 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
           }
         }
         lds_sync();
+
         for (int c = threadIdx.x; c < 16 * cpr; c += 256) {
           const int rr = c / cpr, q = c - rr * cpr;
           const int r = rbase + rr, cc = colw + 4 * q;
           if (r < rows && cc < p.N) {
             const float4 v = *reinterpret_cast<const float4*>(so + rr * ostr + 4 * q);
             const int64_t o = (row0 + r) * p.ldo + cc;
-            if (p.out_bf16) {
+            if (p.out_exp) {
+              const float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+              int e = 0;
+              if (mx > 0.0f && mx <= 3.0e38f) {
+                int ex;
+                frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+                e = max(ex - 15, -127);
+              }
+              const f16x2_t lo = {(_Float16)ldexpf(v.x, -e), (_Float16)ldexpf(v.y, -e)};
+              const f16x2_t hi = {(_Float16)ldexpf(v.z, -e), (_Float16)ldexpf(v.w, -e)};
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
+                  make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+              p.out_exp[o >> 2] = (int8_t)e;
+            } else if (p.out_bf16) {
               const uint2 w = make_uint2(f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16),
                                          f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16));
               *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = w;
@@ -812,17 +830,26 @@ __global__ void shared_gate_kernel(const uint16_t* __restrict__ w, const uint16_
 }
 
 // Y[t] = Ys[P + t] (shared expert, weight already applied) + sum_slot Ys[inv[t*k + slot]], fixed slot order.
-__global__ void combine_kernel(const float* __restrict__ Ys, const int32_t* __restrict__ inv, int64_t T, int k,
-                               int H, int has_shared, int64_t P, void* __restrict__ Y, int out_bf16) {
+// Four columns 4c.. of per-position row r: fp16 values times their power of two.
+__device__ __forceinline__ float4 load_scaled4(const uint16_t* Ys, const int8_t* Ye, int64_t r, int c, int H) {
+  const uint2 w = reinterpret_cast<const uint2*>(Ys + r * H)[c];
+  const int e = Ye[r * (H >> 2) + c];
+  const f16x2_t lo = __builtin_bit_cast(f16x2_t, w.x), hi = __builtin_bit_cast(f16x2_t, w.y);
+  return make_float4(ldexpf((float)lo.x, e), ldexpf((float)lo.y, e), ldexpf((float)hi.x, e), ldexpf((float)hi.y, e));
+}
+
+__global__ void combine_kernel(const uint16_t* __restrict__ Ys, const int8_t* __restrict__ Ye,
+                               const int32_t* __restrict__ inv, int64_t T, int k, int H, int has_shared, int64_t P,
+                               void* __restrict__ Y, int out_bf16) {
   const int H4 = H >> 2;
   const int64_t total = T * H4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / H4;
     const int c = (int)(i - t * H4);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (has_shared) acc = reinterpret_cast<const float4*>(Ys + (P + t) * H)[c];
+    if (has_shared) acc = load_scaled4(Ys, Ye, P + t, c, H);
     for (int j = 0; j < k; ++j) {
-      const float4 v = reinterpret_cast<const float4*>(Ys + (int64_t)inv[t * k + j] * H)[c];
+      const float4 v = load_scaled4(Ys, Ye, inv[t * k + j], c, H);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     if (out_bf16) {
@@ -852,6 +879,7 @@ hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream, 
   // (the SwiGLU epilogue writes a quarter of the bytes per tile and measured no faster staged)
   p.vec_out = p.epi != EPI_SWIGLU && p.N % 4 == 0 && p.ldo % 4 == 0 &&
               (reinterpret_cast<uintptr_t>(p.out) & (p.out_bf16 ? 7u : 15u)) == 0;
+  if (p.out_exp && !p.vec_out) return hipErrorInvalidValue;  // the scaled fp16 form is a vec_out epilogue
 #ifdef Q4MOE_GEMM_STAMPS
   static int stamp_launches = 0;
   p.stamp_slot = stamp_launches++ & 3;
@@ -978,7 +1006,8 @@ struct PrefillWs {
   uint16_t* act;    // [R][I] fp16 activations (pair order)
   uint16_t* xs_act; // [R][2][Gp(I)]
   int32_t* xe_act;  // [R]
-  float* ys;        // [R][H] per-position outputs, weighted
+  uint16_t* ys;     // [R][H] per-position outputs, weighted: fp16 scaled by 2^-ye
+  int8_t* ye;       // [R][H/4] the powers of two of ys, one per four columns
   float* sh_gate;   // [T] shared-expert weight per token (with a shared-expert gate)
   float* part;      // [kSharedKSplit][T][2I] K-split gate and up sums of the 4-bit shared expert
   size_t total;
@@ -1008,7 +1037,8 @@ PrefillWs carve(void* base, int64_t T, int H, int I, int E, int k, int has_share
   w.act = reinterpret_cast<uint16_t*>(take((size_t)R * I * 2));
   w.xs_act = reinterpret_cast<uint16_t*>(take((size_t)R * 2 * pad16(I / 64) * 2));
   w.xe_act = reinterpret_cast<int32_t*>(take((size_t)R * 4));
-  w.ys = reinterpret_cast<float*>(take((size_t)R * H * 4));
+  w.ys = reinterpret_cast<uint16_t*>(take((size_t)R * H * 2));
+  w.ye = reinterpret_cast<int8_t*>(take((size_t)R * (H / 4)));
   w.sh_gate = reinterpret_cast<float*>(take((size_t)T * 4));
   w.part = reinterpret_cast<float*>(take(has_shared ? (size_t)kSharedKSplit * T * 2 * I * 4 : 0));
   w.total = off;
@@ -1108,6 +1138,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   d.n_slices = (H + BN - 1) / BN;
   d.epi = EPI_SCALE;
   d.out = w.ys;
+  d.out_exp = w.ye;
   d.out_bf16 = 0;
   d.ldo = H;
   if (L.has_shared && L.sh_gate_w) {
@@ -1121,8 +1152,8 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   e = launch_grouped(d, max_tiles, stream, sh_q8);
   if (e != hipSuccess) return e;
 
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * (H / 4), 256)), dim3(256), 0, stream, w.ys, w.inv, T, k, H,
-                     L.has_shared, P, Y, out_bf16);
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * (H / 4), 256)), dim3(256), 0, stream, w.ys, w.ye, w.inv, T,
+                     k, H, L.has_shared, P, Y, out_bf16);
   return hipGetLastError();
 }
 

@@ -327,3 +327,29 @@ def test_q8_shared_expert_layers(lib):
     assert lib.moe_ffn_decode_batch(ctypes.byref(L), A, 2, A2, 0, None, None, A, need_b - 1, None) == B.EWORKSPACE
     mixed = _layer(sh_gate=q8(I, H), sh_up=q8(I, H))
     assert d(ctypes.byref(mixed), A, A2, 0, None, None, A, need_d, None) == B.EUNSUPPORTED
+
+
+def test_binding_structs_match_header(tmp_path):
+    """The ctypes structures have the header's sizes and field offsets (gcc reads the header)."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    checks = []
+    for cname, cls in (("q4moe_matrix", B.q4moe_matrix), ("q4moe_layer", B.q4moe_layer)):
+        checks.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in cls._fields_:
+            checks.append(f'printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "q4moe.h"\nint main(void) {\n'
+                   + "\n".join(checks) + "\nreturn 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(line.split()[:2]): int(line.split()[2]) for line in out if line}
+    for cname, cls in (("q4moe_matrix", B.q4moe_matrix), ("q4moe_layer", B.q4moe_layer)):
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for field, _ in cls._fields_:
+            assert got[(cname, field)] == getattr(cls, field).offset, (cname, field)

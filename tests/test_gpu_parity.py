@@ -380,7 +380,10 @@ def _prefill_check(B, layer, dl, X, with_bf16=True):
 
 @pytest.mark.parametrize("T,H,I,E,k,shared", [(1, 128, 64, 4, 2, True), (100, 256, 128, 16, 4, True),
                                               (300, 512, 192, 16, 4, True), (257, 384, 128, 8, 3, False),
-                                              (520, 2048, 512, 32, 8, True)])
+                                              (520, 2048, 512, 32, 8, True),
+                                              # 3 and 1 K groups: the shared expert's gate/up split into
+                                              # uneven halves, or not at all; router quarters of unequal length
+                                              (97, 192, 64, 8, 2, True), (33, 64, 128, 4, 2, True)])
 def test_prefill_small(B, T, H, I, E, k, shared):
     say(f"prefill T={T} H={H} I={I} E={E} k={k} shared={shared}")
     layer = synth.moe_layer(90, 0, H, I, E, k, shared=shared)

@@ -572,7 +572,8 @@ def test_prefill_q8_router(B, T, H, I, E, k):
     assert worst <= 2 * REL_L2_TOL
 
 
-@pytest.mark.parametrize("T,H,E,k", [(300, 256, 16, 4), (2048, 2048, 256, 8), (777, 2048, 512, 10)])
+@pytest.mark.parametrize("T,H,E,k", [(300, 256, 16, 4), (2048, 2048, 256, 8), (777, 2048, 512, 10),
+                                     (61, 192, 70, 5), (9, 64, 8, 2)])  # 3 and 1 groups: unequal K quarters
 def test_route_topk_q8(B, T, H, E, k):
     """The standalone 8-bit router: ids bit-exact against the oracle outside the tie band,
     weights to 1e-4 (on the GPU's set where it differs within the band)."""

@@ -95,9 +95,22 @@ struct GroupTiles {
 };
 int group_max_tiles(int64_t rows, int n_experts, int64_t extra_rows, int tile_rows);
 
-// Stable counting sort of `rows` ids by expert (tiles may be null).
+// fp16 preparation of bf16 rows for the grouped GEMM (power-of-two exponents, pair-order
+// fp16 copy, two-part group sums), run by extra workgroups of the sort's rank launch.
+struct PrepRowsJob {
+  const uint16_t* A;  // bf16 [rows][K]
+  int64_t rows;
+  int K, Gp;
+  uint16_t* out;      // fp16 [rows][K]
+  uint16_t* sums;     // fp16 [rows][2][Gp]
+  int32_t* exps;      // [rows]
+};
+
+// Stable counting sort of `rows` ids by expert (tiles may be null); prep (optional)
+// prepares rows beside the rank step, in the same launch.
 hipError_t run_permute(const int32_t* ids, int64_t rows, int n_experts, int32_t* offsets, int32_t* sorted_rows,
-                       int32_t* inv_rows, void* ws, const GroupTiles* tiles, hipStream_t stream);
+                       int32_t* inv_rows, void* ws, const GroupTiles* tiles, hipStream_t stream,
+                       const PrepRowsJob* prep = nullptr);
 
 // ---- grouped MFMA GEMM and the prefill layer (gemm.hip)
 size_t gemm_workspace_bytes(int64_t m, int k);

@@ -2,9 +2,11 @@
 // and the stable counting sort that groups (token, slot) rows by expert for
 // the prefill expert GEMM (lily-qwen3.8-flash-next README, "How the speed was
 // achieved": prefill runs the expert GEMM over token-to-expert groups).
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
+#include "preprows.h"
 #include "topk.h"
 
 namespace q4moe {
@@ -173,10 +175,19 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const float* __restrict_
 constexpr int kRankThreads = 256;
 constexpr int kRankChunk = kMaxExperts;  // rows per chunk: one per thread of the scatter kernel
 
+// Workgroups from nchunks on prepare rows (PrepRowsJob) instead: work of their own that
+// only shares the launch, so that it runs beside the few rank workgroups.
 __global__ __launch_bounds__(kRankThreads) void chunk_rank_kernel(const int32_t* __restrict__ ids, int64_t rows, int E,
                                                                   int32_t* __restrict__ local_rank,
-                                                                  int32_t* __restrict__ hist) {
+                                                                  int32_t* __restrict__ hist, int nchunks,
+                                                                  PrepRowsJob prep) {
   __shared__ int32_t s_cnt[kMaxExperts];
+  if ((int)blockIdx.x >= nchunks) {
+    prep::prep_rows_body<uint16_t>(prep.A, prep.rows, prep.K, prep.Gp, prep.out, prep.sums, prep.exps,
+                                   prep::SplitRows{nullptr, INT64_MAX, 0, 1}, (int64_t)blockIdx.x - nchunks,
+                                   (int64_t)gridDim.x - nchunks);
+    return;
+  }
   for (int e = threadIdx.x; e < E; e += kRankThreads) s_cnt[e] = 0;
   __syncthreads();
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -507,18 +518,29 @@ int group_max_tiles(int64_t rows, int n_experts, int64_t extra_rows, int tile_ro
 }
 
 hipError_t run_permute(const int32_t* ids, int64_t rows, int E, int32_t* offsets, int32_t* sorted_rows,
-                       int32_t* inv_rows, void* ws, const GroupTiles* tiles, hipStream_t stream) {
+                       int32_t* inv_rows, void* ws, const GroupTiles* tiles, hipStream_t stream,
+                       const PrepRowsJob* prep) {
   char* w = static_cast<char*>(ws);
   const int nchunks = (int)((rows + kRankChunk - 1) / kRankChunk);
   int32_t* local_rank = reinterpret_cast<int32_t*>(w);
   int32_t* hist = reinterpret_cast<int32_t*>(w + align256((size_t)rows * 4));
   GroupTiles none{};
+  // the row preparation's workgroups (one wave per row) after the rank workgroups
+  const PrepRowsJob pj = prep ? *prep : PrepRowsJob{};
+  const int64_t prep_blocks = prep && prep->rows > 0 ? std::min<int64_t>((prep->rows + 3) / 4, 8192) : 0;
   if (nchunks == 0) {  // no rows: offsets and the tile table still get written
+    if (prep_blocks > 0) {
+      hipLaunchKernelGGL(chunk_rank_kernel, dim3((unsigned)prep_blocks), dim3(kRankThreads), 0, stream, ids, rows, E,
+                         local_rank, hist, 0, pj);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(expert_scatter_kernel, dim3(1), dim3(kMaxExperts), 0, stream, ids, rows, E, local_rank, hist,
                        0, offsets, sorted_rows, inv_rows, tiles ? *tiles : none);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(chunk_rank_kernel, dim3(nchunks), dim3(kRankThreads), 0, stream, ids, rows, E, local_rank, hist);
+  hipLaunchKernelGGL(chunk_rank_kernel, dim3((unsigned)(nchunks + prep_blocks)), dim3(kRankThreads), 0, stream, ids,
+                     rows, E, local_rank, hist, nchunks, pj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(expert_scatter_kernel, dim3(nchunks), dim3(kMaxExperts), 0, stream, ids, rows, E, local_rank,

@@ -26,7 +26,7 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 DECODE_SOURCES = ("decode.hip", "common.h", "vecstage.h", "topk.h", "kernels.h", "handoff.h")
 ALL_SOURCES = ("abi.hip", "decode.hip", "decode_batch.hip", "gemm.hip", "gemv.hip", "route.hip", "common.h", "kernels.h", "topk.h",
-               "vecstage.h", "handoff.h")
+               "vecstage.h", "handoff.h", "preprows.h")
 
 
 def _sha256(names) -> str:

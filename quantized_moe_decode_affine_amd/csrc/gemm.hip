@@ -261,10 +261,12 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
     seg = -1;
     rows = (int)min<int64_t>(BM, p.extra_rows - (int64_t)tile * BM);
   } else if (p.tiles) {
+    // (uniform: so that the weight pointers chosen by seg below come from scalar loads,
+    // and the prologue has no vector loads for the main loop's first wait to drain)
     const int4 ti = p.tiles[tile];
-    seg = ti.x;
-    row0 = ti.y;
-    rows = ti.z;
+    seg = __builtin_amdgcn_readfirstlane(ti.x);
+    row0 = __builtin_amdgcn_readfirstlane(ti.y);
+    rows = __builtin_amdgcn_readfirstlane(ti.z);
   } else {
     row0 = (int64_t)tile * BM;
     seg = row0 < p.extra_rows ? -1 : -2;
@@ -301,11 +303,11 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int ln = lane & 31, lh = lane >> 5;
-  const bool swiglu = p.epi == EPI_SWIGLU;
+  const bool swiglu = __builtin_amdgcn_readfirstlane(p.epi) == EPI_SWIGLU;
 
   // ---- weight rows (B columns) of this lane: nb = 0, 1
-  const Q4Mat& M0 = seg >= 0 ? p.W : p.X;
-  const Q4Mat& M1 = seg >= 0 ? (swiglu ? p.W2 : p.W) : (swiglu ? p.X2 : p.X);
+  const Q4Mat M0 = seg >= 0 ? p.W : p.X;  // (by value: selected in scalar registers)
+  const Q4Mat M1 = seg >= 0 ? (swiglu ? p.W2 : p.W) : (swiglu ? p.X2 : p.X);
   const int64_t oc = seg >= 0 ? seg * p.w_codes_stride : 0;
   const int64_t og = seg >= 0 ? seg * p.w_groups_stride : 0;
   // Group-major codes: one K group of 32 consecutive rows is 1 KB of contiguous bytes,
@@ -320,7 +322,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   for (int nb = 0; nb < 2; ++nb) {
     col[nb] = swiglu ? slice * 128 + wave * 32 + ln : slice * BN + wave * 64 + nb * 32 + ln;
     const int64_t wrow = min(col[nb], p.N - 1);
-    const Q4Mat& Mx = nb == 0 ? M0 : M1;
+    const Q4Mat Mx = nb == 0 ? M0 : M1;
     // this lane's half of a group: 32 codes = 16 bytes (4-bit) or 32 bytes (8-bit)
     bcodes[nb] = gm ? reinterpret_cast<const uint4*>(Mx.codes_gm + oc) + wrow * 2 + lh
                     : reinterpret_cast<const uint4*>(Mx.codes + oc + wrow * (p.K * kBits / 32)) + kBW * lh;
@@ -552,6 +554,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
 
   Q4MOE_GSTAMP(3);
   __syncthreads();  // every wave is past its last read of stage 0 (s_wgt below)
+  // The factor is formed only here: computed where its loads are issued, it would make
+  // the prologue wait for them before its barrier.
+  asm volatile("" : "+v"(row_wgt), "+v"(row_e));
   if (threadIdx.x < BM) s_wgt[threadIdx.x] = ldexpf(row_wgt, row_e);  // exact: a power of two
   __syncthreads();
 

@@ -379,8 +379,6 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   // Raw bf16 scale bits of the groups in flight, converted where they are used
   // (a conversion next to the load would make the wave wait for it there).
   uint32_t sc[kStages][2];
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) issue(st, st, sc[st]);
 
 
   // The main loop is specialised on the number of active row blocks so that a
@@ -388,6 +386,12 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmParams& p) {
   // use of the data, not at a join right after the look-ahead loads.
   auto main_loop = [&](auto nmb_c) __attribute__((always_inline)) {
     constexpr int NMB = decltype(nmb_c)::value;
+    // The first groups' loads, issued after the branch on NMB: issued before it, their
+    // scale words are widened there at once, which waits for every load.  (The marker,
+    // different in each specialisation, keeps the compiler from hoisting them back.)
+    asm volatile("; grouped GEMM main loop, %0 row blocks" ::"n"(NMB));
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st) issue(st, st, sc[st]);
     // One K group from stage ST (a compile-time stage, so each LDS access names one array).
     auto step = [&](int g, auto st_c) __attribute__((always_inline)) {
       constexpr int st = decltype(st_c)::value;

@@ -21,8 +21,10 @@
 // range, bf16 inputs convert exactly (8 significant bits fit in 11) unless they are
 // below 2^-23 of the row's largest, and a row's 64-wide group sums stay below 2^15.
 // The epilogue multiplies the power back in.  The SwiGLU activations are written
-// in fp32 and get the same treatment before the down GEMM, so they are rounded
-// once, to 11 significant bits.
+// as fp16 with a power of two per four columns (each value rounded to 11
+// significant bits) and get the per-row treatment before the down GEMM; that
+// rescaling is exact unless a value falls below fp16's normal range, so each
+// activation is rounded once, as if converted from fp32 directly.
 //
 // Tiling: a workgroup (4 waves) owns up to 96 rows of one group (expert) and 256
 // output columns (or 128 gate + 128 up columns for the SwiGLU epilogue); each
@@ -694,8 +696,9 @@ using prep::SplitRows;
 
 template <typename In>
 __global__ void prep_rows_kernel(const In* __restrict__ A, int64_t rows, int K, int Gp, uint16_t* __restrict__ out,
-                                 uint16_t* __restrict__ sums, int32_t* __restrict__ exps, SplitRows sp) {
-  prep::prep_rows_body<In>(A, rows, K, Gp, out, sums, exps, sp, blockIdx.x, gridDim.x);
+                                 uint16_t* __restrict__ sums, int32_t* __restrict__ exps, SplitRows sp,
+                                 const int8_t* __restrict__ in_exp) {
+  prep::prep_rows_body<In>(A, rows, K, Gp, out, sums, exps, sp, blockIdx.x, gridDim.x, in_exp);
 }
 
 // The shared expert's weight per token, sigmoid(w . X[t]) (the shared-expert gate), one wave
@@ -767,8 +770,9 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // extra_q8: the extra segment (shared expert) holds 8-bit codes; it then takes a launch
 // of its own after the routed tiles'.
 hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream, bool extra_q8 = false) {
-  // (the SwiGLU epilogue writes a quarter of the bytes per tile and measured no faster staged)
-  p.vec_out = p.epi != EPI_SWIGLU && p.N % 4 == 0 && p.ldo % 4 == 0 &&
+  // (the SwiGLU epilogue writes a quarter of the bytes per tile and measured no faster
+  // staged in fp32; it is staged for the scaled fp16 form, which needs 4 columns per thread)
+  p.vec_out = (p.epi != EPI_SWIGLU || p.out_exp) && p.N % 4 == 0 && p.ldo % 4 == 0 &&
               (reinterpret_cast<uintptr_t>(p.out) & (p.out_bf16 ? 7u : 15u)) == 0;
   if (p.out_exp && !p.vec_out) return hipErrorInvalidValue;  // the scaled fp16 form is a vec_out epilogue
 #ifdef Q4MOE_GEMM_STAMPS
@@ -797,12 +801,13 @@ hipError_t launch_grouped(GemmParams& p, int64_t max_tiles, hipStream_t stream, 
 // fp16 pair-order copy, row exponents and group-sum parts of `rows` rows of length K.
 template <typename In>
 hipError_t launch_prep_rows(const In* A, int64_t rows, int K, uint16_t* out, uint16_t* sums, int32_t* exps,
-                            hipStream_t stream, SplitRows sp = SplitRows{nullptr, INT64_MAX, 0, 1}) {
+                            hipStream_t stream, SplitRows sp = SplitRows{nullptr, INT64_MAX, 0, 1},
+                            const int8_t* in_exp = nullptr) {
   if (rows == 0) return hipSuccess;
   const int Gp = pad16(K >> 6);
   const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 8192);
   hipLaunchKernelGGL(prep_rows_kernel<In>, dim3((unsigned)blocks), dim3(256), 0, stream, A, rows, K, Gp, out, sums,
-                     exps, sp);
+                     exps, sp, in_exp);
   return hipGetLastError();
 }
 
@@ -893,7 +898,8 @@ struct PrefillWs {
   uint16_t* xs_x;   // [T][2][Gp(H)] fp16 group-sum parts of the rows
   int32_t* xe_x;    // [T] row exponents
   uint16_t* xp;     // [T][H] fp16 rows (pair order)
-  float* act32;     // [R][I] SwiGLU outputs, fp32
+  uint16_t* act16;  // [R][I] SwiGLU outputs: fp16 scaled by 2^-act_e
+  int8_t* act_e;    // [R][I/4] the powers of two of act16, one per four columns
   uint16_t* act;    // [R][I] fp16 activations (pair order)
   uint16_t* xs_act; // [R][2][Gp(I)]
   int32_t* xe_act;  // [R]
@@ -924,7 +930,8 @@ PrefillWs carve(void* base, int64_t T, int H, int I, int E, int k, int has_share
   w.xs_x = reinterpret_cast<uint16_t*>(take((size_t)T * 2 * pad16(H / 64) * 2));
   w.xe_x = reinterpret_cast<int32_t*>(take((size_t)T * 4));
   w.xp = reinterpret_cast<uint16_t*>(take((size_t)T * H * 2));
-  w.act32 = reinterpret_cast<float*>(take((size_t)R * I * 4));
+  w.act16 = reinterpret_cast<uint16_t*>(take((size_t)R * I * 2));
+  w.act_e = reinterpret_cast<int8_t*>(take((size_t)R * (I / 4)));
   w.act = reinterpret_cast<uint16_t*>(take((size_t)R * I * 2));
   w.xs_act = reinterpret_cast<uint16_t*>(take((size_t)R * 2 * pad16(I / 64) * 2));
   w.xe_act = reinterpret_cast<int32_t*>(take((size_t)R * 4));
@@ -964,7 +971,8 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   e = run_permute(w.ids, P, E, w.offsets, w.sorted_rows, w.inv, w.perm_ws, &gt, stream, &prep);
   if (e != hipSuccess) return e;
 
-  // gate/up with SwiGLU -> act32 (fp32, sorted positions; shared rows appended)
+  // gate/up with SwiGLU -> act16/act_e (fp16 with a power of two per four columns,
+  // sorted positions; shared rows appended)
   GemmParams p{};
   p.A = w.xp;
   p.xs = w.xs_x;
@@ -987,7 +995,8 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   p.extra_rows = extra;
   p.n_slices = (I + 127) / 128;
   p.epi = EPI_SWIGLU;
-  p.out = w.act32;
+  p.out = w.act16;
+  p.out_exp = w.act_e;
   p.out_bf16 = 0;
   p.ldo = I;
   const bool sh_q8 = L.has_shared && L.sh_q8;
@@ -1004,7 +1013,8 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
 
   const int64_t R = P + extra;
   const SplitRows sp = ksplit > 1 ? SplitRows{w.part, P, T * 2 * I, ksplit} : SplitRows{nullptr, INT64_MAX, 0, 1};
-  e = launch_prep_rows(w.act32, R, I, w.act, w.xs_act, w.xe_act, stream, sp);
+  e = launch_prep_rows(reinterpret_cast<const prep::f16x_t*>(w.act16), R, I, w.act, w.xs_act, w.xe_act, stream, sp,
+                       w.act_e);
   if (e != hipSuccess) return e;
 
   // down with the routing weight -> ys (fp32, sorted positions)

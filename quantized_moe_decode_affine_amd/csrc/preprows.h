@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace q4moe {
@@ -20,6 +22,23 @@ __device__ __forceinline__ void load8(const uint16_t* src, float (&v)[8]) {
   for (int j = 0; j < 4; ++j) {
     v[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
     v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+  }
+}
+// fp16 values stored with a power of two per four columns (value = fp16 * 2^e).
+struct f16x_t {
+  uint16_t bits;
+};
+__device__ __forceinline__ void load8(const f16x_t* src, const int8_t* ex, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  const uint32_t e2 = *reinterpret_cast<const uint16_t*>(ex);  // the exponents of columns 0-3 and 4-7
+  const int e0 = (int8_t)(e2 & 0xFFu), e1 = (int8_t)(e2 >> 8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const half2_t h = __builtin_bit_cast(half2_t, w[j]);
+    const int e = j < 2 ? e0 : e1;
+    v[2 * j] = ldexpf((float)h[0], e);
+    v[2 * j + 1] = ldexpf((float)h[1], e);
   }
 }
 __device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
@@ -42,11 +61,13 @@ struct SplitRows {
 // row is written as fp16(x * 2^-e) with each 8-element block in the pair order
 // (x0,x4),(x1,x5),(x2,x6),(x3,x7), e goes to exps[row], and the sums of each 64-wide
 // group of the fp16 values are split into two fp16 parts: sums[row][part][g], with
-// the groups padded with zeros to Gp.
+// the groups padded with zeros to Gp.  With In = f16x_t, in_exp holds the input's powers
+// of two, [rows][K/4].
 template <typename In>
 __device__ __forceinline__ void prep_rows_body(const In* __restrict__ A, int64_t rows, int K, int Gp,
                                                uint16_t* __restrict__ out, uint16_t* __restrict__ sums,
-                                               int32_t* __restrict__ exps, SplitRows sp, int64_t block, int64_t nblocks) {
+                                               int32_t* __restrict__ exps, SplitRows sp, int64_t block, int64_t nblocks,
+                                               const int8_t* __restrict__ in_exp = nullptr) {
   const int lane = lane_id();
   const int nblk = K >> 3, G = K >> 6;
   const int64_t wstride = nblocks * (blockDim.x / kWave);
@@ -69,6 +90,8 @@ __device__ __forceinline__ void prep_rows_body(const In* __restrict__ A, int64_t
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = silu(g[j]) * u[j];
+      } else if constexpr (std::is_same_v<In, f16x_t>) {
+        load8(row + b * 8, in_exp + (r * K + b * 8) / 4, v);
       } else {
         load8(row + b * 8, v);
       }

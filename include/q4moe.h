@@ -260,7 +260,9 @@ int moe_ffn_decode_batch(const q4moe_layer* layer, const q4moe_bf16* X, int64_t 
  * for down with the routing weight, then combine back in token order.  Row t
  * of Y equals moe_ffn_decode on X[t] up to rounding; the SwiGLU output is
  * computed in fp32 and rounded once to fp16 (after an exact power-of-two row
- * scaling) before the down GEMM, and each expert's weighted output is rounded
+ * scaling; a value that lands below fp16's normal range there, under 2^-22 of
+ * its row's largest, may round twice) before the down GEMM, and each expert's
+ * weighted output is rounded
  * once to fp16 precision (11 significant bits, kept in range by a power of two
  * per four columns) before the combine adds them in fp32.  The GEMMs read the experts' group-major
  * codes when every 4-bit expert matrix of the layer (routed and shared) carries

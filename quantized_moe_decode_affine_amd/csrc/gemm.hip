@@ -724,35 +724,51 @@ __global__ void shared_gate_kernel(const uint16_t* __restrict__ w, const uint16_
 }
 
 // Y[t] = Ys[P + t] (shared expert, weight already applied) + sum_slot Ys[inv[t*k + slot]], fixed slot order.
-// Four columns 4c.. of per-position row r: fp16 values times their power of two.
-__device__ __forceinline__ float4 load_scaled4(const uint16_t* Ys, const int8_t* Ye, int64_t r, int c, int H) {
-  const uint2 w = reinterpret_cast<const uint2*>(Ys + r * H)[c];
-  const int e = Ye[r * (H >> 2) + c];
-  const f16x2_t lo = __builtin_bit_cast(f16x2_t, w.x), hi = __builtin_bit_cast(f16x2_t, w.y);
-  return make_float4(ldexpf((float)lo.x, e), ldexpf((float)lo.y, e), ldexpf((float)hi.x, e), ldexpf((float)hi.y, e));
+// Eight columns 8c.. of per-position row r: fp16 values times their powers of two (one
+// per four columns).
+__device__ __forceinline__ void load_scaled8(const uint16_t* Ys, const int8_t* Ye, int64_t r, int c, int H,
+                                             float (&v)[8]) {
+  const uint4 w = reinterpret_cast<const uint4*>(Ys + r * H)[c];
+  const uint32_t e2 = reinterpret_cast<const uint16_t*>(Ye + r * (H >> 2))[c];  // columns 0-3, 4-7
+  const int e0 = (int8_t)(e2 & 0xFFu), e1 = (int8_t)(e2 >> 8);
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x2_t h = __builtin_bit_cast(f16x2_t, ww[j]);
+    const int e = j < 2 ? e0 : e1;
+    v[2 * j] = ldexpf((float)h.x, e);
+    v[2 * j + 1] = ldexpf((float)h.y, e);
+  }
 }
 
+// Each thread takes 8 columns of one token (16-byte loads of every row it adds).
 __global__ void combine_kernel(const uint16_t* __restrict__ Ys, const int8_t* __restrict__ Ye,
                                const int32_t* __restrict__ inv, int64_t T, int k, int H, int has_shared, int64_t P,
                                void* __restrict__ Y, int out_bf16) {
-  const int H4 = H >> 2;
-  const int64_t total = T * H4;
+  const int H8 = H >> 3;
+  const int64_t total = T * H8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / H4;
-    const int c = (int)(i - t * H4);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (has_shared) acc = load_scaled4(Ys, Ye, P + t, c, H);
+    const int64_t t = i / H8;
+    const int c = (int)(i - t * H8);
+    float acc[8] = {};
+    if (has_shared) load_scaled8(Ys, Ye, P + t, c, H, acc);
     for (int j = 0; j < k; ++j) {
-      const float4 v = load_scaled4(Ys, Ye, inv[t * k + j], c, H);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      float v[8];
+      load_scaled8(Ys, Ye, inv[t * k + j], c, H, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += v[q];
     }
     if (out_bf16) {
-      uint2 o;
-      o.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
-      o.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
-      reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + t * H)[c] = o;
+      uint4 o;
+      o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+      o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+      o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
+      o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+      reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + t * H)[c] = o;
     } else {
-      reinterpret_cast<float4*>(static_cast<float*>(Y) + t * H)[c] = acc;
+      float4* y = reinterpret_cast<float4*>(static_cast<float*>(Y) + t * H) + 2 * c;
+      y[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      y[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
   }
 }
@@ -1053,7 +1069,7 @@ hipError_t run_moe_ffn_prefill(const DecodeLayer& L, const uint16_t* X, int64_t 
   e = launch_grouped(d, max_tiles, stream, sh_q8);
   if (e != hipSuccess) return e;
 
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * (H / 4), 256)), dim3(256), 0, stream, w.ys, w.ye, w.inv, T,
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * (H / 8), 256)), dim3(256), 0, stream, w.ys, w.ye, w.inv, T,
                      k, H, L.has_shared, P, Y, out_bf16);
   return hipGetLastError();
 }
